@@ -1,0 +1,17 @@
+"""Shared pytest set-up: the ``gpu`` marker and import paths.
+
+Tests marked ``gpu`` need an MI355X (gfx950) and the built HIP library;
+everything else runs on the CPU.
+"""
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+for p in (HERE, ROOT):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD GPU (gfx950) and the built HIP library")
