@@ -1,0 +1,248 @@
+"""Benchmark: achieved HBM bandwidth of the fused skip-add + normalize ops.
+
+One step is one pass of the whole hot path over one batch of the large
+workloads (inputs resident in HBM before timing starts):
+
+  skip_rms_norm   ssln_f16_16x2048x4096        (Y and S outputs)
+  gated_rms_norm  gated_f16_8x4096x4096_c128
+  skip_group_norm sgn_f16_nhwc_2x64x64x320     (Y and S, bias, SiLU)
+  skip_group_norm sgn_f32_nchw_4x1280x32x32    (broadcast skip, Y)
+
+Bytes are algorithmic: every input read once plus every requested output
+written once.  ``value`` = bytes of K steps / wall time of the K steps
+(synchronized on both sides).  Per-op times come from HIP events recorded on
+the stream the kernels run on.  The two 0.8-1 GB workloads exceed the 256 MB
+last-level cache, and between two visits of any workload at least 1.8 GB of
+other traffic passes, so every op starts from a cold cache.
+
+Prints one JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (and % of MI355X peak) per norm op, fp16 large shapes"
+PEAK_GBPS = 8000.0  # MI355X HBM3E
+STEP_WORKLOADS = ["ssln_f16_16x2048x4096", "gated_f16_8x4096x4096_c128",
+                  "sgn_f16_nhwc_2x64x64x320", "sgn_f32_nchw_4x1280x32x32"]
+DOMINANT = "ssln_f16_16x2048x4096"
+DOMINANT_KERNEL = "ssln_wave_kernel<half, 8 per vector, 8 vectors per lane>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ssln_f16_16x2048x4096.json")
+KERNEL_SOURCES = ["group_normalization_amd/csrc/ssln.hip", "group_normalization_amd/csrc/device_common.h"]
+COPY_BYTES = 1 << 30
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is absent or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except FileNotFoundError:
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Op:
+    """One workload's device tensors and a closure that enqueues the op."""
+
+    def __init__(self, name, torch, gn, workloads):
+        w = workloads.WORKLOADS[name]
+        self.name = name
+        self.bytes = workloads.io_bytes(w)
+        host = workloads.generate(w)
+        d = {k: torch.from_numpy(v).cuda() for k, v in host.items()}
+        del host
+        a = w.attrs
+        if w.op == "skip_rms_norm":
+            want_sum = "input_skip_bias_sum" in w.outputs
+            want_inv = "inv_std_var" in w.outputs
+            self.run = lambda: gn.skip_rms_norm(d["input"], d["skip"], d["gamma"], d.get("bias"),
+                                                a["epsilon"], want_sum=want_sum,
+                                                want_inv_std_var=want_inv)
+        elif w.op == "gated_rms_norm":
+            self.run = lambda: gn.gated_rms_norm(d["X"], d["scale"], d["gate"], a["epsilon"])
+        else:
+            ws = torch.empty(gn.skip_group_norm_workspace_size(d["X"], a["groups"], a["channels_last"]),
+                             dtype=torch.uint8, device="cuda")
+            want_sum = "S" in w.outputs
+            self.run = lambda: gn.skip_group_norm(d["X"], d["gamma"], d["beta"], d["skip"], d.get("bias"),
+                                                  groups=a["groups"], activation=a["activation"],
+                                                  epsilon=a["epsilon"],
+                                                  channels_last=a["channels_last"],
+                                                  want_sum=want_sum, workspace=ws)
+        self.tensors = d
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (single thread) on a bounded sample of each step workload:
+    whole rows / whole images, as many as fit a per-op share of the budget."""
+    import oracle
+    from group_normalization_amd import workloads
+
+    share = budget_s / len(STEP_WORKLOADS)
+    total_bytes, total_s, parts = 0, 0.0, []
+    for name in STEP_WORKLOADS:
+        w = workloads.WORKLOADS[name]
+        x = workloads.generate(w)
+        a = w.attrs
+        if w.op == "skip_rms_norm":
+            inp, skp = x["input"].reshape(-1, x["input"].shape[-1]), x["skip"].reshape(-1, x["input"].shape[-1])
+            unit_rows, per_row = inp.shape[0], workloads.io_bytes(w) / inp.shape[0]
+            call = lambda lo, hi: oracle.skip_rms_norm(inp[lo:hi], skp[lo:hi], x["gamma"], x.get("bias"),
+                                                       a["epsilon"], want_sum=True)
+        elif w.op == "gated_rms_norm":
+            C = x["scale"].size
+            X, G = x["X"].reshape(-1, C), x["gate"].reshape(-1, C)
+            unit_rows, per_row = X.shape[0], workloads.io_bytes(w) / X.shape[0]
+            call = lambda lo, hi: oracle.gated_rms_norm(X[lo:hi], x["scale"], G[lo:hi], a["epsilon"])
+        else:
+            N = x["X"].shape[0]
+            unit_rows, per_row = N, workloads.io_bytes(w) / N
+            call = lambda lo, hi: oracle.skip_group_norm(
+                x["X"][lo:hi], x["gamma"], x["beta"], x["skip"][lo:hi], x.get("bias"),
+                groups=a["groups"], activation=a["activation"], epsilon=a["epsilon"],
+                channels_last=a["channels_last"], want_sum="S" in w.outputs)
+        done, t_op, chunk = 0, 0.0, 1
+        while done < unit_rows and t_op < share:
+            hi = min(unit_rows, done + chunk)
+            t0 = time.perf_counter()
+            call(done, hi)
+            t_op += time.perf_counter() - t0
+            done = hi
+            chunk = min(chunk * 2, 4096)
+        total_bytes += per_row * done
+        total_s += t_op
+        unit = "rows" if w.op != "skip_group_norm" else "images"
+        parts.append(f"{name}: {done}/{unit_rows} {unit}")
+        log(f"cpu oracle {name}: {done} {unit} in {t_op:.2f} s")
+    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": "; ".join(parts) + f" ({total_s:.1f} s single-thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the operators need no communication and this "
+              "build runs on a single MI355X; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import group_normalization_amd as gn
+    from group_normalization_amd import workloads
+
+    torch.cuda.set_device(0)
+    log("generating inputs")
+    ops = [Op(n, torch, gn, workloads) for n in STEP_WORKLOADS]
+    torch.cuda.synchronize()
+    step_bytes = sum(o.bytes for o in ops)
+
+    def step(events=None):
+        for i, o in enumerate(ops):
+            if events is not None:
+                events[i][0].record()
+            o.run()
+            if events is not None:
+                events[i][1].record()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region, with an event pair around every op of every step.
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in ops]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    per_op = {}
+    for i, o in enumerate(ops):
+        ms = [evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)]
+        avg = float(np.mean(ms))
+        per_op[o.name] = {"bytes": o.bytes, "avg_us": round(avg * 1e3, 3),
+                          "median_us": round(float(np.median(ms)) * 1e3, 3),
+                          "min_us": round(float(np.min(ms)) * 1e3, 3),
+                          "gbps": round(o.bytes / (avg * 1e-3) / 1e9, 1),
+                          "frac_of_peak": round(o.bytes / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)}
+
+    # Copy ceiling: the library's 16-byte copy kernel over 1 GiB (outside the
+    # timed region; also the calibration kernel for the byte counters).
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        gn.copy_(dst, src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        gn.copy_(dst, src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * COPY_BYTES * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    dom = per_op[DOMINANT]
+    achieved = dom["bytes"] / (dom["avg_us"] * 1e-6) / 1e9
+    traffic = load_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes * args.steps / elapsed / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64, seed 0; N(0,1), U(0.5,1.5), N(0,0.1) per tensor)",
+        "config": {"workload": " + ".join(STEP_WORKLOADS), "io_dtype": "f16 (f32 for the NCHW group norm)",
+                   "bytes_per_step": step_bytes, "cache": "cold (working set > last-level cache)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": DOMINANT_KERNEL, "workload": DOMINANT},
+        "ops": per_op,
+        "copy_ceiling_gbps": round(copy_gbps, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,71 @@
+"""ctypes declarations of the libskipnorm C ABI (``include/skipnorm.h``).
+
+The library is loaded on first use from ``group_normalization_amd/libskipnorm.so``
+(built in-tree by ``group_normalization_amd.build``).  There is no fallback:
+if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskipnorm.so")
+
+SN_F32, SN_F16, SN_BF16 = 0, 1, 2
+STATUS_NAMES = {0: "SN_OK", 1: "SN_ERR_NULL", 2: "SN_ERR_DTYPE", 3: "SN_ERR_SHAPE",
+                4: "SN_ERR_ATTR", 5: "SN_ERR_ALIAS", 6: "SN_ERR_WORKSPACE", 7: "SN_ERR_HIP"}
+
+#: Every symbol the header declares, with (restype, argtypes).
+_vp, _i64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                              ctypes.c_float, ctypes.c_size_t)
+_ci = ctypes.c_int
+SIGNATURES = {
+    "skip_rms_norm": (_ci, [_ci, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp]),
+    "gated_rms_norm": (_ci, [_ci, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp]),
+    "skip_group_norm_workspace_size": (_ci, [_ci, _i64, _i64, _i64, _i64, _i64, _i32,
+                                             ctypes.POINTER(_sz)]),
+    "skip_group_norm": (_ci, [_ci, _ci, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
+                              _f32, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "skipnorm_last_error": (ctypes.c_char_p, []),
+    "skipnorm_abi_version": (_ci, []),
+    "skipnorm_force_route": (_ci, [_ci]),
+    "skipnorm_last_route": (ctypes.c_char_p, []),
+    "skipnorm_copy": (_ci, [_vp, _vp, _sz, _vp]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class SkipNormError(ValueError):
+    """A libskipnorm call returned a status other than SN_OK."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+def lib():
+    """The loaded library (loads it on first use; raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(
+                        f"libskipnorm is not built ({LIB_PATH} missing); run "
+                        "`python -m group_normalization_amd.build` first")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise SkipNormError(status, lib().skipnorm_last_error().decode())

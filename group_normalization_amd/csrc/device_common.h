@@ -1,0 +1,168 @@
+// device_common.h -- device helpers shared by the libskipnorm kernels
+// (gfx950 / CDNA4, wave64).  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sn {
+
+typedef _Float16 half_t;
+
+// ---------------------------------------------------------------------------
+// Element vectors.  Vec<T, E> holds E elements of T; E * sizeof(T) == 16 is
+// the 16-byte vector that becomes one global_load/store_dwordx4 per lane,
+// E == 1 the scalar route.
+template <typename T, int E> struct Vec { T v[E]; };
+template <> struct alignas(16) Vec<float, 4> { float v[4]; };
+template <> struct alignas(16) Vec<half_t, 8> { half_t v[8]; };
+
+template <typename T> struct VecWidth { static constexpr int value = 16 / sizeof(T); };
+
+template <typename T, int E>
+__device__ __forceinline__ Vec<T, E> load_vec(const T* __restrict__ p, int64_t i) {
+    return reinterpret_cast<const Vec<T, E>*>(p)[i];
+}
+template <typename T, int E>
+__device__ __forceinline__ void store_vec(T* __restrict__ p, int64_t i, const Vec<T, E>& v) {
+    reinterpret_cast<Vec<T, E>*>(p)[i] = v;
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(half_t x) { return static_cast<float>(x); }
+
+// Round a float32 value to T (round to nearest even; v_cvt_f16_f32 keeps
+// binary16 subnormals) -- the single narrowing step of every output.
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ half_t from_f32<half_t>(float x) { return static_cast<half_t>(x); }
+
+// Residual sum of one element: float32 (x + skip), then + bias only when a
+// bias exists (adding +0 would turn -0 into +0), then one rounding to T.
+// Returns the T value widened back to float32, which is what the
+// statistics and the normalization use.
+template <typename T>
+__device__ __forceinline__ float residual_sum(float x, float skip, bool has_bias, float bias, T& rounded) {
+    float s = x + skip;
+    if (has_bias) s = s + bias;
+    rounded = from_f32<T>(s);
+    return to_f32(rounded);
+}
+
+__device__ __forceinline__ float fmaf_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+
+// SiLU(v) = v / (1 + e^-v) in float32: v_exp_f32 on -v*log2(e) and
+// v_rcp_f32 (about 1 ulp each).  For v << 0, e^-v overflows to +inf and the
+// reciprocal gives 0, the correct limit.
+__device__ __forceinline__ float silu_f32(float v) {
+    const float e = __builtin_amdgcn_exp2f(-v * 1.4426950408889634f);
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// 1 / sqrt(x) from a correctly rounded square root and an IEEE division:
+// once per row or group, so exactness is preferred over speed.
+__device__ __forceinline__ float inv_sqrt(float x) { return 1.0f / __builtin_sqrtf(x); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums.  Every step adds a lane's value to its partner's; IEEE
+// addition is commutative, so both partners hold bitwise the same sum and
+// after the last step every lane of the segment holds the same total.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+// DPP controls (GFX9 encoding).
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within each 8
+constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within each 16
+
+// Sum over aligned segments of L lanes (L a power of two, 1..64).
+template <int L>
+__device__ __forceinline__ float segment_sum(float v) {
+    if constexpr (L >= 2) v = v + dpp_mov<kQuadXor1>(v);
+    if constexpr (L >= 4) v = v + dpp_mov<kQuadXor2>(v);
+    // After the quad steps each quad is uniform, so mirroring inside 8 lanes
+    // pairs quad 0 with quad 1, and mirroring inside 16 pairs the halves.
+    if constexpr (L >= 8) v = v + dpp_mov<kRowHalfMirror>(v);
+    if constexpr (L >= 16) v = v + dpp_mov<kRowMirror>(v);
+    if constexpr (L >= 32) v = v + __shfl_xor(v, 16, 64);
+    if constexpr (L >= 64) v = v + __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Moments (count, mean, M2 = sum of squared deviations) and their pairwise
+// combination (Chan, Golub and LeVeque, "Updating formulae and a pairwise
+// algorithm for computing sample variances", 1979).
+struct Moments {
+    float n, mean, m2;
+};
+
+__device__ __forceinline__ Moments merge(const Moments& a, const Moments& b) {
+    if (b.n == 0.0f) return a;
+    if (a.n == 0.0f) return b;
+    const float n = a.n + b.n;
+    const float d = b.mean - a.mean;
+    const float wb = b.n / n;
+    Moments r;
+    r.n = n;
+    r.mean = fmaf_(d, wb, a.mean);
+    r.m2 = fmaf_(d * d, a.n * wb, a.m2 + b.m2);
+    return r;
+}
+
+// Per-thread accumulator with the shifted-data method: sums of (x - shift)
+// and (x - shift)^2, shift = the first value seen, so a group whose values
+// are all equal accumulates exact zeros.
+struct ShiftedSums {
+    float shift = 0.0f, s1 = 0.0f, s2 = 0.0f;
+    __device__ __forceinline__ void add(float x, bool first) {
+        if (first) shift = x;
+        const float d = x - shift;
+        s1 += d;
+        s2 = fmaf_(d, d, s2);
+    }
+    __device__ __forceinline__ Moments moments(float n) const {
+        Moments m;
+        m.n = n;
+        if (n == 0.0f) {
+            m.mean = 0.0f;
+            m.m2 = 0.0f;
+            return m;
+        }
+        const float q = s1 / n;
+        m.mean = shift + q;
+        m.m2 = fmaxf(fmaf_(-s1, q, s2), 0.0f);
+        return m;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Unsigned division by a run-time invariant d >= 1 with one multiply-high
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, unsigned case): exact for every 32-bit n.
+struct FastDiv {
+    uint32_t d, m, s1, s2;
+};
+
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;  // l = ceil(log2 d)
+    FastDiv f;
+    f.d = d;
+    f.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+    f.s1 = l > 0 ? 1u : 0u;
+    f.s2 = l > 0 ? l - 1 : 0u;
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+    const uint32_t t = __umulhi(n, f.m);
+    return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
+}  // namespace sn

@@ -1,0 +1,197 @@
+/*
+ * skipnorm.h -- C ABI of libskipnorm: fused skip-add + normalize operators on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Three operators, each defined on its ONNX Runtime contrib-op kernels-hub
+ * README:
+ *   skip_rms_norm   "com.microsoft.SkipSimplifiedLayerNormalization"
+ *   gated_rms_norm  "com.microsoft.GatedRMSNorm"
+ *   skip_group_norm "com.microsoft.SkipGroupNorm"
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers on the current HIP device, dense
+ *     and row-major (C-contiguous) in the layout stated per argument.  The
+ *     caller owns every buffer; the library never allocates, frees or
+ *     synchronizes device memory.
+ *   - Work is enqueued on `stream` (0 = the null stream) and returns
+ *     immediately, like a kernel launch.
+ *   - Optional inputs and outputs are passed as NULL when absent.
+ *   - Arithmetic: the residual sum is formed in float32 and rounded once to
+ *     the tensor type T; statistics and normalization are float32; every
+ *     output is rounded once to its type.
+ *   - Validation happens on the host before anything is enqueued: on any
+ *     status other than SN_OK and SN_ERR_HIP nothing was launched and no
+ *     output was written.  SN_ERR_HIP reports a failed launch.  The message
+ *     for the last non-OK status of the calling thread is returned by
+ *     skipnorm_last_error().
+ *   - Outputs may not overlap inputs or each other (SN_ERR_ALIAS).
+ *   - Pointers need no particular alignment; 16-byte aligned tensors whose
+ *     rows are whole 16-byte vectors take the vectorized kernels, the rest a
+ *     scalar route with the same results up to float32 summation order.
+ *   - Zero-sized leading dimensions are valid and launch nothing.  A row
+ *     (hidden, span) or one SkipGroupNorm image (C*H*W) may hold at most
+ *     2^30 elements.
+ *   - Results are deterministic: no floating-point atomics; every reduction
+ *     runs in a fixed order, and requesting an optional output never changes
+ *     the others.
+ */
+#ifndef SKIPNORM_H
+#define SKIPNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKIPNORM_ABI_VERSION 1
+
+/* Element types.  T (tensor data) and M (SkipGroupNorm gamma/beta) take
+ * float32 or float16 ("Type constraints" on each page); statistics outputs
+ * are always float32 (U).  bfloat16 is listed only to be rejected: the pages
+ * state that it is not implemented. */
+typedef enum sn_dtype {
+    SN_F32 = 0,
+    SN_F16 = 1,
+    SN_BF16 = 2
+} sn_dtype;
+
+typedef enum sn_status {
+    SN_OK = 0,
+    SN_ERR_NULL = 1,      /* a required pointer is NULL                       */
+    SN_ERR_DTYPE = 2,     /* unsupported element type                         */
+    SN_ERR_SHAPE = 3,     /* sizes inconsistent or out of range               */
+    SN_ERR_ATTR = 4,      /* attribute out of range (epsilon, groups, ...)    */
+    SN_ERR_ALIAS = 5,     /* an output overlaps an input or another output    */
+    SN_ERR_WORKSPACE = 6, /* workspace missing or smaller than required       */
+    SN_ERR_HIP = 7        /* a HIP launch failed                              */
+} sn_status;
+
+/* ------------------------------------------------------------------------
+ * SkipSimplifiedLayerNormalization ("com.microsoft.SkipSimplifiedLayer-
+ * Normalization": Description, Inputs, Outputs, Attributes).
+ *
+ * For each of `rows` rows of `hidden` elements (the input's leading axes
+ * folded; the page allows (token_count, hidden_size) and (batch, sequence,
+ * hidden_size)):
+ *   S[j]  = round_T((input[j] + skip[j]) + bias[j])   (bias term only if given)
+ *   r     = 1 / sqrt(sum_j S[j]^2 / hidden + epsilon)
+ *   output[j] = round_T(S[j] * r * gamma[j])
+ * Arguments:
+ *   T            SN_F32 or SN_F16, the type of every tensor except the stats.
+ *   rows         >= 0.   hidden: >= 1.
+ *   input, skip  [rows, hidden] T.        gamma: [hidden] T.
+ *   bias         [hidden] T or NULL.
+ *   epsilon      >= 0 and finite (the page's default is 9.999999960041972e-13).
+ *   output       [rows, hidden] T.
+ *   mean         [rows] float32 or NULL; written as 0 (the simplified form has
+ *                no mean).
+ *   inv_std_var  [rows] float32 or NULL; receives r.
+ *   input_skip_bias_sum  [rows, hidden] T or NULL; receives S.
+ * ------------------------------------------------------------------------ */
+sn_status skip_rms_norm(sn_dtype T, int64_t rows, int64_t hidden,
+                        const void* input, const void* skip, const void* gamma,
+                        const void* bias, float epsilon,
+                        void* output, float* mean, float* inv_std_var,
+                        void* input_skip_bias_sum, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * GatedRMSNorm ("com.microsoft.GatedRMSNorm": Description, Inputs, Outputs,
+ * Attributes).
+ *
+ * C = `span` = element count of scale.  X is read as numel / C flat rows of
+ * C contiguous elements (any rank >= 1 folds to this):
+ *   r    = 1 / sqrt(sum_j X[j]^2 / C + epsilon)
+ *   Y[j] = round_T(X[j] * r * scale[j] * SiLU(gate[j])),  SiLU(g) = g / (1 + e^-g)
+ * with every intermediate in float32.
+ * Arguments:
+ *   T        SN_F32 or SN_F16.
+ *   numel    >= 0, a multiple of span.   span: >= 1.
+ *   X, gate  [numel] T.   scale: [span] T.   Y: [numel] T.
+ *   epsilon  >= 0 and finite (the page's default is 1e-5).
+ * ------------------------------------------------------------------------ */
+sn_status gated_rms_norm(sn_dtype T, int64_t numel, int64_t span,
+                         const void* X, const void* scale, const void* gate,
+                         float epsilon, void* Y, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * SkipGroupNorm ("com.microsoft.SkipGroupNorm": Description, Inputs,
+ * Outputs, Attributes, Type constraints).
+ *
+ * X has logical shape (N, C, H, W), stored NHWC when channels_last != 0 and
+ * NCHW when channels_last == 0 (any non-zero value selects NHWC).
+ *   S = round_T((X + skip) + bias)        (bias term only if given)
+ *   per (n, group g of C/groups channels), over all H*W positions:
+ *     mean, var = population mean and variance of S
+ *   Y = round_T(act(gamma[c] * (S - mean) / sqrt(var + epsilon) + beta[c]))
+ *   act = identity (activation 0) or SiLU (activation 1).
+ * Arguments:
+ *   T              SN_F32 or SN_F16 for X, skip, bias, Y, S.
+ *   M              SN_F32 or SN_F16 for gamma, beta (independent of T).
+ *   N, H, W        >= 0.   C: >= 1.
+ *   X              X's layout as above, T.
+ *   gamma, beta    [C] M.
+ *   skip           T; X's shape and layout when skip_broadcast == 0, else
+ *                  [N, C] (one value per batch item and channel; the page's
+ *                  (N, C) and (N, 1, 1, C) spellings).
+ *   bias           [C] T or NULL.
+ *   epsilon        >= 0 and finite (the page's default is 1e-5).
+ *   groups         >= 1 and divides C.
+ *   activation     0 or 1.
+ *   Y              X's shape and layout, T.   S: same, or NULL.
+ *   workspace      device memory of at least the size that
+ *                  skip_group_norm_workspace_size returns for the same
+ *                  arguments (may be NULL when that size is 0).  Its
+ *                  contents on entry do not matter.  Calls that share a
+ *                  workspace must be ordered (same stream).
+ * ------------------------------------------------------------------------ */
+sn_status skip_group_norm_workspace_size(sn_dtype T, int64_t N, int64_t C,
+                                         int64_t H, int64_t W, int64_t groups,
+                                         int32_t channels_last, size_t* bytes);
+
+sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C,
+                          int64_t H, int64_t W,
+                          const void* X, const void* gamma, const void* beta,
+                          const void* skip, int32_t skip_broadcast,
+                          const void* bias, float epsilon, int64_t groups,
+                          int32_t channels_last, int32_t activation,
+                          void* Y, void* S, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Library information and test hooks.
+ * ------------------------------------------------------------------------ */
+
+/* Message for the calling thread's last non-OK status ("" if none).  The
+ * string stays valid until that thread's next call into the library. */
+const char* skipnorm_last_error(void);
+
+/* SKIPNORM_ABI_VERSION of the built library. */
+int skipnorm_abi_version(void);
+
+/* Route selection for every later call in the process: 0 = automatic (the
+ * default), 1 = force the scalar routes (16-byte vectors off), 2 = force the
+ * vectorized route where its preconditions hold (automatic otherwise),
+ * 3 = force the one-workgroup-per-row route for skip_rms_norm and
+ * gated_rms_norm (skip_group_norm treats 3 like 1).  Returns the previous
+ * value; an unknown value leaves the setting unchanged and returns the
+ * current one.  Lets tests cover each route on the same shapes. */
+int skipnorm_force_route(int route);
+
+/* Name of the route the calling thread's last successful op call took
+ * (e.g. "ssln.wave", "ssln.scalar", "gated.segment", "sgn.nhwc"). */
+const char* skipnorm_last_route(void);
+
+/* Measurement helper: copies `bytes` bytes from src to dst with one kernel
+ * of 16-byte loads and stores (both 16-byte aligned, bytes a multiple of
+ * 16).  Serves as the copy-bandwidth reference and as the calibration
+ * kernel of known traffic for hardware counters. */
+sn_status skipnorm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SKIPNORM_H */

@@ -1,0 +1,93 @@
+"""GatedRMSNorm: HIP path (through the C ABI) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import group_normalization_amd as gn
+import oracle
+from group_normalization_amd import workloads
+from parity import assert_bitwise, assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+F32, F16 = np.float32, np.float16
+
+CASES = [
+    # (X shape, span C, dtype): spans around 16-byte vectors, segment widths and rows per wave
+    ((3, 4), 1, F32),           # the page's example shape, C = 1
+    ((5, 12), 2, F16),
+    ((7, 21), 3, F32),
+    ((9, 8), 8, F16),            # one vector per row
+    ((11, 48), 16, F16),
+    ((13, 64), 64, F32),
+    ((3, 7, 100), 100, F16),     # not a whole number of vectors
+    ((4, 33, 128), 128, F16),    # C = 128: 16 lanes x 8 halves; ragged last block
+    ((2, 4096), 128, F32),
+    ((6, 1024), 1024, F16),      # 128 vectors: 64 lanes x 2
+    ((3, 8192), 8192, F16),      # 1024 vectors: 64 lanes x 16
+    ((2, 5000), 5000, F32),      # scalar segment limit exceeded: block route
+    ((2, 2, 9000), 9000, F16),
+    ((1000,), 10, F16),          # rank 1
+]
+
+
+@pytest.mark.parametrize("route", ["auto", "scalar", "block"])
+@pytest.mark.parametrize("shape,C,dt", CASES, ids=[f"{s}-C{c}-{np.dtype(d).name}" for s, c, d in CASES])
+def test_matches_oracle(shape, C, dt, route):
+    w = workloads.gated("t", shape, C, dt, epsilon=1e-5)
+    x = workloads.generate(w, seed=C + len(shape))
+    ref = oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5)
+    with gn.force_route(route):
+        y = gn.gated_rms_norm(to_dev(x["X"]), to_dev(x["scale"]), to_dev(x["gate"]), 1e-5)
+        used = gn.last_route()
+    assert_close(to_host(y), ref, f"Y via {used}")
+    vec = 16 // np.dtype(dt).itemsize
+    if route == "auto" and C % vec == 0 and C // vec <= 1024:
+        assert used == "gated.segment.vec16"
+
+
+@pytest.mark.parametrize("dt", [F32, F16])
+def test_zero_gate_gives_zero(dt):
+    w = workloads.gated("t", (64, 256), 128, dt, epsilon=1e-5)
+    x = workloads.generate(w, seed=1)
+    y = gn.gated_rms_norm(to_dev(x["X"]), to_dev(x["scale"]), torch.zeros(64, 256, dtype=to_dev(x["X"]).dtype,
+                                                                           device="cuda"))
+    assert torch.all(y == 0)
+
+
+def test_scale_spellings_and_packing_agree():
+    w = workloads.gated("t", (8, 4 * 128), 128, F16, epsilon=1e-5)
+    x = workloads.generate(w, seed=2)
+    X, g, s = to_dev(x["X"]), to_dev(x["gate"]), to_dev(x["scale"])
+    base = to_host(gn.gated_rms_norm(X, s, g))
+    for Xs, gs, ss in [(X.view(32, 128), g.view(32, 128), s.view(1, 128)),
+                       (X.view(8, 4, 128), g.view(8, 4, 128), s.view(128, 1)),
+                       (X.view(-1), g.view(-1), s)]:
+        assert_bitwise(to_host(gn.gated_rms_norm(Xs, ss, gs)).reshape(base.shape), base, "repacked")
+
+
+def test_deterministic_and_in_bounds():
+    from group_normalization_amd._lib import lib, check as ck
+    rows, C, pad = 1000, 128, 1024
+    w = workloads.gated("t", (rows, C), C, F16, epsilon=1e-5)
+    x = workloads.generate(w, seed=6)
+    d = {k: to_dev(v) for k, v in x.items()}
+    arena = torch.full((rows * C + 2 * pad,), 3.0, dtype=torch.float16, device="cuda")
+    Y = arena[pad: pad + rows * C]
+    for _ in range(2):
+        ck(lib().gated_rms_norm(1, rows * C, C, d["X"].data_ptr(), d["scale"].data_ptr(),
+                                d["gate"].data_ptr(), 1e-5, Y.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        if _ == 0:
+            first = to_host(Y).copy()
+    assert_bitwise(to_host(Y), first, "second run")
+    a = to_host(arena)
+    assert np.all(a[:pad] == 3.0) and np.all(a[pad + rows * C:] == 3.0)
+    assert_close(first.reshape(rows, C), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
+
+
+def test_empty():
+    e = torch.empty(0, 128, dtype=torch.float16, device="cuda")
+    s = torch.ones(128, dtype=torch.float16, device="cuda")
+    assert gn.gated_rms_norm(e, s, e).shape == (0, 128)

@@ -1,0 +1,161 @@
+"""SkipGroupNorm: HIP path (through the C ABI) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import group_normalization_amd as gn
+import oracle
+from group_normalization_amd import workloads
+from parity import assert_bitwise, assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+F32, F16 = np.float32, np.float16
+
+
+def run(x, w, route="auto", want_sum=True, skip_override=None):
+    a = w.attrs
+    skip = x["skip"] if skip_override is None else skip_override
+    ref_y, ref_s = oracle.skip_group_norm(x["X"], x["gamma"], x["beta"], skip, x.get("bias"),
+                                          groups=a["groups"], activation=a["activation"],
+                                          epsilon=a["epsilon"], channels_last=a["channels_last"],
+                                          want_sum=True)
+    with gn.force_route(route):
+        out = gn.skip_group_norm(to_dev(x["X"]), to_dev(x["gamma"]), to_dev(x["beta"]), to_dev(skip),
+                                 to_dev(x.get("bias")), groups=a["groups"],
+                                 activation=a["activation"], epsilon=a["epsilon"],
+                                 channels_last=a["channels_last"], want_sum=want_sum)
+        used = gn.last_route()
+    torch.cuda.synchronize()
+    return (ref_y, ref_s), out, used
+
+
+def check(ref, out, want_sum=True):
+    assert_close(to_host(out.Y), ref[0], "Y")
+    if want_sum:
+        assert_bitwise(to_host(out.S), ref[1], "S")
+
+
+# (N, C, H, W, T, M, channels_last, broadcast skip, bias, groups, activation)
+CASES = [
+    (2, 320, 16, 16, F16, F32, 1, False, True, 32, 1),    # the NHWC workload's channel layout
+    (2, 1280, 8, 8, F32, F16, 0, True, False, 32, 0),     # the NCHW workload's channel layout
+    (3, 64, 7, 9, F16, F16, 1, True, True, 8, 0),
+    (2, 96, 5, 5, F32, F32, 0, False, True, 4, 1),        # H*W = 25: not a whole vector
+    (1, 40, 13, 11, F16, F32, 1, False, False, 5, 1),
+    (2, 12, 6, 6, F16, F16, 1, False, True, 3, 0),        # C not a whole vector: scalar NHWC
+    (2, 16, 4, 4, F32, F32, 0, True, True, 16, 1),        # groups == C (instance norm)
+    (2, 24, 3, 5, F16, F32, 0, False, False, 1, 0),       # one group (layer norm)
+    (1, 4096, 2, 2, F16, F16, 1, False, True, 32, 0),     # 512 vectors per pixel: scalar NHWC
+    (3, 8, 1, 1, F32, F16, 1, True, False, 2, 1),         # H = W = 1
+    (2, 2560, 8, 8, F32, F32, 1, False, True, 32, 1),     # 640 vectors per pixel: scalar NHWC
+]
+
+
+def make(case, seed=0):
+    N, C, H, W, T, M, cl, bc, bias, groups, act = case
+    w = workloads.sgn("t", N, C, H, W, T, M, channels_last=bool(cl), broadcast_skip=bc, bias=bias,
+                      groups=groups, activation=act, epsilon=1e-5)
+    return w, workloads.generate(w, seed=seed + N * C + H)
+
+
+@pytest.mark.parametrize("route", ["auto", "scalar"])
+@pytest.mark.parametrize("case", CASES, ids=[f"N{c[0]}C{c[1]}H{c[2]}W{c[3]}-{np.dtype(c[4]).name}/"
+                                             f"{np.dtype(c[5]).name}-{'nhwc' if c[6] else 'nchw'}"
+                                             f"{'-bc' if c[7] else ''}{'-b' if c[8] else ''}-g{c[9]}"
+                                             f"-a{c[10]}" for c in CASES])
+def test_matches_oracle(case, route):
+    w, x = make(case)
+    ref, out, used = run(x, w, route)
+    check(ref, out)
+    if route == "scalar":
+        assert used.endswith(".scalar")
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[3]])
+def test_S_request_does_not_change_Y(case):
+    w, x = make(case, seed=1)
+    _, with_s, _ = run(x, w, want_sum=True)
+    _, without, _ = run(x, w, want_sum=False)
+    assert without.S is None
+    assert_bitwise(to_host(with_s.Y), to_host(without.Y), "Y with/without S")
+
+
+@pytest.mark.parametrize("cl", [0, 1])
+def test_broadcast_equals_expanded(cl):
+    N, C, H, W = 2, 64, 6, 6
+    w, x = make((N, C, H, W, F16, F32, cl, True, True, 8, 1), seed=2)
+    _, bc, _ = run(x, w)
+    full = np.broadcast_to(x["skip"].reshape((N, 1, 1, C) if cl else (N, C, 1, 1)),
+                           x["X"].shape).copy()
+    ref, ex, _ = run(x, w, skip_override=full)
+    assert_bitwise(to_host(bc.S), to_host(ex.S), "S broadcast vs expanded")
+    assert_close(to_host(bc.Y), ref[0], "Y broadcast")
+    # The (N, 1, 1, C) spelling is the same broadcast.
+    ref2, sp, _ = run(x, w, skip_override=x["skip"].reshape(N, 1, 1, C))
+    assert_bitwise(to_host(sp.Y), to_host(bc.Y), "(N,1,1,C) spelling")
+
+
+def test_layouts_agree():
+    N, C, H, W = 2, 64, 8, 8
+    w, x = make((N, C, H, W, F32, F32, 0, False, True, 8, 0), seed=3)
+    _, nchw, _ = run(x, w)
+    xh = {k: (np.ascontiguousarray(v.transpose(0, 2, 3, 1)) if v.ndim == 4 else v) for k, v in x.items()}
+    wh = workloads.sgn("t", N, C, H, W, F32, F32, channels_last=True, broadcast_skip=False, bias=True,
+                       groups=8, activation=0, epsilon=1e-5)
+    ref, nhwc, _ = run(xh, wh)
+    check(ref, nhwc)
+    assert_close(to_host(nhwc.Y), np.ascontiguousarray(to_host(nchw.Y).transpose(0, 2, 3, 1)), "layouts")
+
+
+@pytest.mark.parametrize("cl", [0, 1])
+def test_constant_group_gives_beta(cl):
+    N, C, H, W = 1, 32, 8, 8
+    shape = (N, H, W, C) if cl else (N, C, H, W)
+    X = np.full(shape, 0.75, F32)
+    skip = np.full(shape, 0.25, F32)
+    gamma = np.linspace(-2, 3, C).astype(F32)
+    beta = np.linspace(0.5, -1.5, C).astype(F32)
+    out = gn.skip_group_norm(to_dev(X), to_dev(gamma), to_dev(beta), to_dev(skip), groups=4,
+                             activation=0, channels_last=cl)
+    y = to_host(out.Y)
+    expect = np.broadcast_to(beta.reshape((1, 1, 1, C) if cl else (1, C, 1, 1)), shape)
+    assert np.array_equal(y, expect)
+
+
+def test_deterministic_and_in_bounds():
+    from group_normalization_amd._lib import lib, check as ck
+    N, C, H, W, pad = 2, 320, 16, 16, 2048
+    w, x = make((N, C, H, W, F16, F32, 1, False, True, 32, 1), seed=4)
+    d = {k: to_dev(v) for k, v in x.items()}
+    n = N * C * H * W
+    arena = torch.full((2 * (n + 2 * pad),), 5.0, dtype=torch.float16, device="cuda")
+    Y = arena[pad: pad + n]
+    S = arena[n + 3 * pad: 2 * n + 3 * pad]
+    need = gn.skip_group_norm_workspace_size(d["X"], 32, 1)
+    ws = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    results = []
+    for _ in range(2):
+        ck(lib().skip_group_norm(1, 0, N, C, H, W, d["X"].data_ptr(), d["gamma"].data_ptr(),
+                                 d["beta"].data_ptr(), d["skip"].data_ptr(), 0, d["bias"].data_ptr(),
+                                 1e-5, 32, 1, 1, Y.data_ptr(), S.data_ptr(), ws.data_ptr(), need,
+                                 torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        results.append((to_host(Y).copy(), to_host(S).copy()))
+    assert_bitwise(results[0][0], results[1][0], "Y second run")
+    a = to_host(arena)
+    assert np.all(a[:pad] == 5.0) and np.all(a[pad + n: n + 3 * pad] == 5.0)
+    assert np.all(a[2 * n + 3 * pad:] == 5.0)
+    assert torch.all(ws[need:] == 0x5A)
+    ref_y, ref_s = oracle.skip_group_norm(x["X"], x["gamma"], x["beta"], x["skip"], x["bias"],
+                                          groups=32, activation=1, epsilon=1e-5, channels_last=1,
+                                          want_sum=True)
+    assert_close(results[0][0].reshape(ref_y.shape), ref_y, "Y")
+    assert_bitwise(results[0][1].reshape(ref_s.shape), ref_s, "S")
+
+
+def test_empty():
+    X = torch.empty(0, 4, 4, 8, dtype=torch.float16, device="cuda")
+    g = torch.ones(8, dtype=torch.float32, device="cuda")
+    out = gn.skip_group_norm(X, g, g, X, groups=2, activation=0)
+    assert out.Y.shape == X.shape

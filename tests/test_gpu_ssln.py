@@ -1,0 +1,155 @@
+"""SkipSimplifiedLayerNormalization: HIP path (through the C ABI) against the
+oracle, element by element.  Every route, both dtypes, every optional
+input/output combination, ragged and unaligned shapes, edge values."""
+import numpy as np
+import pytest
+import torch
+
+import group_normalization_amd as gn
+import oracle
+from group_normalization_amd import workloads
+from parity import assert_bitwise, assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+F32, F16 = np.float32, np.float16
+
+
+def run_both(inp, skip, gamma, bias, eps, route="auto", want=("mean", "inv", "sum")):
+    ref = oracle.skip_rms_norm(inp, skip, gamma, bias, eps, want_mean=True,
+                               want_inv_std_var=True, want_sum=True)
+    with gn.force_route(route):
+        out = gn.skip_rms_norm(to_dev(inp), to_dev(skip), to_dev(gamma), to_dev(bias), eps,
+                               want_mean="mean" in want, want_inv_std_var="inv" in want,
+                               want_sum="sum" in want)
+        used = gn.last_route()
+    torch.cuda.synchronize()
+    return ref, out, used
+
+
+def check(ref, out, want=("mean", "inv", "sum")):
+    y_ref, mean_ref, inv_ref, s_ref = ref
+    assert_close(to_host(out.output), y_ref, "output")
+    if "sum" in want:
+        assert_bitwise(to_host(out.input_skip_bias_sum), s_ref, "input_skip_bias_sum")
+    if "inv" in want:
+        assert_close(to_host(out.inv_std_var), inv_ref, "inv_std_var")
+    if "mean" in want:
+        assert np.all(to_host(out.mean) == 0)
+
+
+SHAPES = [
+    # (shape, dtype, bias): ragged row counts, widths around vector and wave sizes
+    ((64, 768), F32, True),
+    ((13, 768), F16, False),
+    ((3, 5, 4096), F16, True),
+    ((7, 8192), F16, False),
+    ((5, 8192), F32, True),
+    ((9, 1000), F16, True),      # 125 vectors: ragged second pass over the wave
+    ((6, 33), F32, False),       # not a whole number of vectors
+    ((4, 1), F16, True),
+    ((2, 3, 10000), F16, False), # wider than the register-resident rows
+    ((257, 256), F32, False),
+]
+
+
+@pytest.mark.parametrize("route", ["auto", "scalar", "block"])
+@pytest.mark.parametrize("shape,dt,with_bias", SHAPES, ids=[f"{s}-{np.dtype(d).name}-{'b' if b else 'nb'}"
+                                                            for s, d, b in SHAPES])
+def test_matches_oracle(shape, dt, with_bias, route):
+    w = workloads.ssln("t", shape, dt, bias=with_bias, epsilon=1e-6)
+    x = workloads.generate(w, seed=sum(shape))
+    ref, out, used = run_both(x["input"], x["skip"], x["gamma"], x.get("bias"), 1e-6, route)
+    check(ref, out)
+    if route == "auto" and shape[-1] % (16 // np.dtype(dt).itemsize) == 0 and shape[-1] <= 8192:
+        assert used == "ssln.wave.vec16"
+
+
+@pytest.mark.parametrize("want", [(), ("sum",), ("inv",), ("mean",), ("sum", "inv"),
+                                  ("mean", "inv", "sum")])
+@pytest.mark.parametrize("dt", [F32, F16])
+def test_optional_outputs_do_not_change_output(dt, want):
+    w = workloads.ssln("t", (37, 2048), dt, bias=True, epsilon=1e-6)
+    x = workloads.generate(w, seed=5)
+    ref, out, _ = run_both(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6, want=want)
+    check(ref, out, want)
+    _, base, _ = run_both(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6, want=())
+    assert_bitwise(to_host(out.output), to_host(base.output), "output with/without optional outputs")
+
+
+def test_unaligned_tensors_take_scalar_route():
+    w = workloads.ssln("t", (8, 513), F16, bias=True, epsilon=1e-6)
+    x = workloads.generate(w, seed=3)
+    dev = {k: to_dev(v) for k, v in x.items()}
+    # A view one element into a larger buffer is not 16-byte aligned.
+    big = torch.empty(8 * 513 + 1, dtype=torch.float16, device="cuda")
+    big[1:].copy_(dev["input"].ravel())
+    inp = big[1:].view(8, 513)
+    out = gn.skip_rms_norm(inp, dev["skip"], dev["gamma"], dev["bias"], 1e-6, want_sum=True)
+    assert gn.last_route() == "ssln.wave.scalar"
+    ref = oracle.skip_rms_norm(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6, want_sum=True)
+    assert_close(to_host(out.output), ref[0], "output")
+    assert_bitwise(to_host(out.input_skip_bias_sum), ref[3], "S")
+
+
+def test_edge_values_f16():
+    # Residual sums that tie, overflow to inf, become subnormal or -0.
+    inp = np.array([[1, 1.0009765625, 65504, 65504, 2 ** -24, 2 ** -14, -0.0, 3]], F16)
+    skip = np.array([[2 ** -11, 2 ** -11, 16, 8, 2 ** -24, -(2 ** -24), -0.0, -3]], F16)
+    gamma = np.ones(8, F16)
+    for route in ("auto", "scalar", "block"):
+        ref, out, _ = run_both(inp, skip, gamma, None, 1e-6, route)
+        assert_bitwise(to_host(out.input_skip_bias_sum), ref[3], f"S ({route})")
+        # The row holds +inf: output is NaN/0 as in the oracle.
+        assert_close(to_host(out.output), ref[0], f"output ({route})")
+
+
+def test_zero_rows_and_zero_row():
+    g = np.ones(16, F32)
+    z = np.zeros((0, 16), F32)
+    out = gn.skip_rms_norm(to_dev(z), to_dev(z), to_dev(g))
+    assert out.output.shape == (0, 16)
+    zr = np.zeros((3, 16), F32)
+    ref, out, _ = run_both(zr, zr, g, None, 9.999999960041972e-13)
+    check(ref, out)
+    assert np.all(to_host(out.inv_std_var) == np.float32(1e6))
+
+
+def test_deterministic():
+    w = workloads.ssln("t", (64, 4096), F16, bias=True, epsilon=1e-6)
+    x = workloads.generate(w, seed=9)
+    a = run_both(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6)[1]
+    b = run_both(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6)[1]
+    for f in ("output", "inv_std_var", "input_skip_bias_sum"):
+        assert_bitwise(to_host(getattr(a, f)), to_host(getattr(b, f)), f)
+
+
+def test_outputs_leave_neighbouring_memory_untouched():
+    """Writes stay inside each output: canary regions around the outputs
+    (passed as raw pointers through the C ABI) keep their pattern."""
+    from group_normalization_amd._lib import lib, check as ck
+    rows, hidden, pad = 11, 768, 4096
+    w = workloads.ssln("t", (rows, hidden), F16, bias=True, epsilon=1e-6)
+    x = workloads.generate(w, seed=4)
+    d = {k: to_dev(v) for k, v in x.items()}
+    n = rows * hidden
+    arena = torch.full((3 * (n + 2 * pad),), -7.0, dtype=torch.float16, device="cuda")
+    slots = [arena[i * (n + 2 * pad) + pad: i * (n + 2 * pad) + pad + n] for i in range(3)]
+    stats = torch.full((2 * (rows + 2 * pad),), -7.0, dtype=torch.float32, device="cuda")
+    mean = stats[pad: pad + rows]
+    inv = stats[rows + 3 * pad: rows + 3 * pad + rows]
+    ck(lib().skip_rms_norm(1, rows, hidden, d["input"].data_ptr(), d["skip"].data_ptr(),
+                           d["gamma"].data_ptr(), d["bias"].data_ptr(), 1e-6, slots[0].data_ptr(),
+                           mean.data_ptr(), inv.data_ptr(), slots[1].data_ptr(),
+                           torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    ref = oracle.skip_rms_norm(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6,
+                               want_mean=True, want_inv_std_var=True, want_sum=True)
+    assert_close(to_host(slots[0]).reshape(rows, hidden), ref[0], "output")
+    assert_bitwise(to_host(slots[1]).reshape(rows, hidden), ref[3], "S")
+    assert torch.all(slots[2] == -7.0)
+    a = to_host(arena).reshape(3, -1)
+    assert np.all(a[:, :pad] == -7.0) and np.all(a[:, pad + n:] == -7.0)
+    s = to_host(stats)
+    assert np.all(s[:pad] == -7.0) and np.all(s[pad + rows: rows + 3 * pad] == -7.0)
+    assert np.all(s[2 * rows + 3 * pad:] == -7.0)
