@@ -28,6 +28,27 @@ __device__ __forceinline__ void store_vec(T* __restrict__ p, int64_t i, const Ve
     reinterpret_cast<Vec<T, E>*>(p)[i] = v;
 }
 
+// Streaming (nontemporal) accesses for data touched exactly once: the
+// access carries the nontemporal hint, so the caches do not keep lines that
+// will not be reused.  Values are moved as raw bits of the same size.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <int BYTES> struct RawBits;
+template <> struct RawBits<16> { using type = u32x4; };
+template <> struct RawBits<4> { using type = uint32_t; };
+template <> struct RawBits<2> { using type = uint16_t; };
+
+template <typename T, int E>
+__device__ __forceinline__ Vec<T, E> load_vec_stream(const T* __restrict__ p, int64_t i) {
+    using R = typename RawBits<sizeof(Vec<T, E>)>::type;
+    const R r = __builtin_nontemporal_load(reinterpret_cast<const R*>(p) + i);
+    return __builtin_bit_cast(Vec<T, E>, r);
+}
+template <typename T, int E>
+__device__ __forceinline__ void store_vec_stream(T* __restrict__ p, int64_t i, const Vec<T, E>& v) {
+    using R = typename RawBits<sizeof(Vec<T, E>)>::type;
+    __builtin_nontemporal_store(__builtin_bit_cast(R, v), reinterpret_cast<R*>(p) + i);
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(half_t x) { return static_cast<float>(x); }
 

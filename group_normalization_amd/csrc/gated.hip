@@ -15,7 +15,8 @@
 //            Each thread loads RPT rows before computing, to keep enough
 //            bytes in flight.  Vector (16-byte) or scalar element width.
 //   block    one 256-thread workgroup per row for wider rows; X is read twice.
-// scale is loaded once per thread and kept in registers as float32.
+// scale is loaded once per thread and kept in registers as float32.  X, gate
+// and Y are touched once and move with nontemporal loads and stores.
 #include "device_common.h"
 #include "skipnorm_internal.h"
 
@@ -51,8 +52,8 @@ gated_segment_kernel(const T* __restrict__ X, const T* __restrict__ scale,
         for (int v = 0; v < VPL; ++v) {
             const int idx = v * L + l;
             if (row < rows && idx < nvec) {
-                xs[k][v] = load_vec<T, E>(X, row * nvec + idx);
-                gs[k][v] = load_vec<T, E>(gate, row * nvec + idx);
+                xs[k][v] = load_vec_stream<T, E>(X, row * nvec + idx);
+                gs[k][v] = load_vec_stream<T, E>(gate, row * nvec + idx);
             }
         }
     }
@@ -86,7 +87,7 @@ gated_segment_kernel(const T* __restrict__ X, const T* __restrict__ scale,
                     const float g = to_f32(gs[k][v].v[e]);
                     out.v[e] = from_f32<T>(x * r * sc[v][e] * silu_f32(g));
                 }
-                store_vec<T, E>(Y, row * nvec + idx, out);
+                store_vec_stream<T, E>(Y, row * nvec + idx, out);
             }
         }
     }

@@ -262,7 +262,7 @@ const char* skipnorm_last_error(void) { return g_error.c_str(); }
 int skipnorm_abi_version(void) { return SKIPNORM_ABI_VERSION; }
 
 int skipnorm_force_route(int route) {
-    if (route < 0 || route > 3) return g_force_route.load();
+    if (route < 0 || route > 4) return g_force_route.load();
     return g_force_route.exchange(route);
 }
 
@@ -271,6 +271,8 @@ const char* skipnorm_last_route(void) { return g_route; }
 sn_status skipnorm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
     if (bytes == 0) return ok();
     if (!src || !dst) return fail(SN_ERR_NULL, "skipnorm_copy: NULL pointer");
+    if (bytes > (size_t(1) << 40))
+        return fail(SN_ERR_SHAPE, "skipnorm_copy: at most 2^40 bytes per call");
     if (!sn::aligned16(src) || !sn::aligned16(dst) || bytes % 16 != 0)
         return fail(SN_ERR_SHAPE, "skipnorm_copy: pointers and size must be multiples of 16 bytes");
     const Span ins[] = {span_of("src", src, bytes)};

@@ -8,7 +8,7 @@
 
 namespace sn {
 
-enum class Route { Auto = 0, Scalar = 1, Vector = 2, Block = 3 };
+enum class Route { Auto = 0, Scalar = 1, Vector = 2, Block = 3, Split = 4 };
 
 // ---------------------------------------------------------------- SSLN
 struct SslnArgs {

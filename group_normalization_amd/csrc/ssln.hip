@@ -8,8 +8,10 @@
 // Routes:
 //   wave   one wave64 per row; lane l holds the row's vectors l, l+64, ...
 //          in VGPRs as T (the rounded S is exactly representable in T), so
-//          the row is read once and written once.  E elements per access:
-//          16-byte vectors (4 x f32 / 8 x f16) or scalars.
+//          the row is read once and written once, with nontemporal loads
+//          and stores (gamma and bias, shared by every row, stay cached).
+//          E elements per access: 16-byte vectors (4 x f32 / 8 x f16) or
+//          scalars.
 //   block  one 256-thread workgroup per row for rows wider than a wave's
 //          register budget: S is formed twice (once for the statistic, once
 //          for the output), reading the inputs twice.
@@ -45,8 +47,8 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     for (int v = 0; v < NV; ++v) {
         const int idx = v * 64 + lane;
         if (FULL || idx < nvec) {
-            xs[v] = load_vec<T, E>(input, base + idx);
-            ks[v] = load_vec<T, E>(skip, base + idx);
+            xs[v] = load_vec_stream<T, E>(input, base + idx);
+            ks[v] = load_vec_stream<T, E>(skip, base + idx);
         }
     }
 
@@ -64,7 +66,7 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                                                 to_f32(bv.v[e]), ss[v].v[e]);
                 acc = fmaf_(s, s, acc);
             }
-            if (sum) store_vec<T, E>(sum, base + idx, ss[v]);
+            if (sum) store_vec_stream<T, E>(sum, base + idx, ss[v]);
         }
     }
 
@@ -84,7 +86,7 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 out.v[e] = from_f32<T>(to_f32(ss[v].v[e]) * r * to_f32(gv.v[e]));
-            store_vec<T, E>(output, base + idx, out);
+            store_vec_stream<T, E>(output, base + idx, out);
         }
     }
 }

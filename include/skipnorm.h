@@ -172,13 +172,18 @@ const char* skipnorm_last_error(void);
 /* SKIPNORM_ABI_VERSION of the built library. */
 int skipnorm_abi_version(void);
 
-/* Route selection for every later call in the process: 0 = automatic (the
- * default), 1 = force the scalar routes (16-byte vectors off), 2 = force the
- * vectorized route where its preconditions hold (automatic otherwise),
- * 3 = force the one-workgroup-per-row route for skip_rms_norm and
- * gated_rms_norm (skip_group_norm treats 3 like 1).  Returns the previous
- * value; an unknown value leaves the setting unchanged and returns the
- * current one.  Lets tests cover each route on the same shapes. */
+/* Route selection for every later call in the process, so that tests can
+ * cover each kernel family on the same shapes:
+ *   0 = automatic (the default);
+ *   1 = scalar accesses (16-byte vectors off);
+ *   2 = vectorized where the preconditions hold (same as automatic);
+ *   3 = skip_rms_norm / gated_rms_norm: one workgroup per row;
+ *       skip_group_norm: the three-launch split route with scalar accesses;
+ *   4 = skip_group_norm: the three-launch split route (vectorized where the
+ *       preconditions hold) even where one workgroup per group would apply;
+ *       others: automatic.
+ * Returns the previous value; an unknown value leaves the setting unchanged
+ * and returns the current one. */
 int skipnorm_force_route(int route);
 
 /* Name of the route the calling thread's last successful op call took

@@ -59,7 +59,7 @@ def make(case, seed=0):
     return w, workloads.generate(w, seed=seed + N * C + H)
 
 
-@pytest.mark.parametrize("route", ["auto", "scalar"])
+@pytest.mark.parametrize("route", ["auto", "split", "scalar", "block"])
 @pytest.mark.parametrize("case", CASES, ids=[f"N{c[0]}C{c[1]}H{c[2]}W{c[3]}-{np.dtype(c[4]).name}/"
                                              f"{np.dtype(c[5]).name}-{'nhwc' if c[6] else 'nchw'}"
                                              f"{'-bc' if c[7] else ''}{'-b' if c[8] else ''}-g{c[9]}"
@@ -68,16 +68,53 @@ def test_matches_oracle(case, route):
     w, x = make(case)
     ref, out, used = run(x, w, route)
     check(ref, out)
+    N, C, H, W, T, M, cl, bc, bias, groups, act = case
     if route == "scalar":
         assert used.endswith(".scalar")
+    if route == "split":
+        assert used.startswith("sgn.split")
+    if route == "block":
+        assert used.startswith("sgn.split") and used.endswith(".scalar")
+    if route == "auto" and not cl:
+        assert used.startswith("sgn.block")  # every NCHW case here fits one workgroup
 
 
+# NCHW groups around the one-workgroup limits (elements per (n, group)):
+# 16-byte vectors: 8 Ki vectors with a full skip, 12 Ki with a broadcast
+# skip; scalars: 16 Ki elements.
+LIMIT_CASES = [
+    # (N, C, H, W, T, groups, broadcast skip, expected auto route)
+    (1, 32, 32, 32, F32, 1, False, "sgn.block.nchw.vec16"),    # 8192 vectors, full skip
+    (1, 64, 32, 32, F32, 1, False, "sgn.split.nchw.vec16"),    # 16384 vectors, full skip
+    (2, 48, 32, 32, F32, 1, True, "sgn.block.nchw.vec16"),     # 12288 vectors, broadcast
+    (1, 52, 32, 32, F32, 1, True, "sgn.split.nchw.vec16"),     # 13312 vectors, broadcast
+    (1, 32, 64, 64, F16, 2, False, "sgn.block.nchw.vec16"),    # 8192 vectors of halves
+    (2, 16, 32, 32, F16, 1, True, "sgn.block.nchw.vec16"),     # 2048 vectors of halves
+    (1, 16, 31, 33, F32, 1, False, "sgn.block.nchw.scalar"),   # 16368 elements
+    (1, 17, 31, 33, F32, 1, False, "sgn.split.nchw.scalar"),   # 17391 elements
+    (3, 6, 7, 7, F16, 3, True, "sgn.block.nchw.scalar"),
+]
+
+
+@pytest.mark.parametrize("case", LIMIT_CASES, ids=[f"N{c[0]}C{c[1]}H{c[2]}W{c[3]}-{np.dtype(c[4]).name}"
+                                                   f"-g{c[5]}{'-bc' if c[6] else ''}" for c in LIMIT_CASES])
+def test_group_block_limits(case):
+    N, C, H, W, T, groups, bc, want_route = case
+    w = workloads.sgn("t", N, C, H, W, T, np.float32, channels_last=False, broadcast_skip=bc,
+                      bias=True, groups=groups, activation=1, epsilon=1e-5)
+    x = workloads.generate(w, seed=C + H)
+    ref, out, used = run(x, w)
+    assert used == want_route
+    check(ref, out)
+
+
+@pytest.mark.parametrize("route", ["auto", "split", "scalar", "block"])
 @pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[3]])
-def test_S_request_does_not_change_Y(case):
+def test_S_request_does_not_change_Y(case, route):
     w, x = make(case, seed=1)
-    _, with_s, _ = run(x, w, want_sum=True)
-    _, without, _ = run(x, w, want_sum=False)
-    assert without.S is None
+    _, with_s, used = run(x, w, route, want_sum=True)
+    _, without, used2 = run(x, w, route, want_sum=False)
+    assert without.S is None and used == used2
     assert_bitwise(to_host(with_s.Y), to_host(without.Y), "Y with/without S")
 
 
