@@ -48,9 +48,26 @@ SHAPES = [
     ((9, 1000), F16, True),      # 125 vectors: ragged second pass over the wave
     ((6, 33), F32, False),       # not a whole number of vectors
     ((4, 1), F16, True),
-    ((2, 3, 10000), F16, False), # wider than the register-resident rows
+    ((2, 3, 10000), F16, False), # four waves per row, ragged
     ((257, 256), F32, False),
+    ((3, 12288), F16, True),     # four waves per row, 6 vectors per lane
+    ((2, 32768), F16, False),    # four waves per row, 16 vectors per lane (widest)
+    ((2, 16384), F32, True),     # float32 four waves per row, 16 vectors per lane
+    ((2, 10000), F32, False),    # float32 four waves per row, ragged
+    ((2, 40000), F16, True),     # wider than any register-resident route: block route
 ]
+
+
+def expected_route(shape, dt):
+    vec = 16 // np.dtype(dt).itemsize
+    hidden = shape[-1]
+    if hidden % vec:
+        return "ssln.wave.scalar" if hidden <= 2048 else "ssln.block"
+    if hidden <= 8192:
+        return "ssln.wave.vec16"
+    if hidden // vec <= 256 * 16:
+        return "ssln.rowblock.vec16"
+    return "ssln.block"
 
 
 @pytest.mark.parametrize("route", ["auto", "scalar", "block"])
@@ -61,15 +78,15 @@ def test_matches_oracle(shape, dt, with_bias, route):
     x = workloads.generate(w, seed=sum(shape))
     ref, out, used = run_both(x["input"], x["skip"], x["gamma"], x.get("bias"), 1e-6, route)
     check(ref, out)
-    if route == "auto" and shape[-1] % (16 // np.dtype(dt).itemsize) == 0 and shape[-1] <= 8192:
-        assert used == "ssln.wave.vec16"
+    if route == "auto":
+        assert used == expected_route(shape, dt)
 
 
 @pytest.mark.parametrize("want", [(), ("sum",), ("inv",), ("mean",), ("sum", "inv"),
                                   ("mean", "inv", "sum")])
-@pytest.mark.parametrize("dt", [F32, F16])
-def test_optional_outputs_do_not_change_output(dt, want):
-    w = workloads.ssln("t", (37, 2048), dt, bias=True, epsilon=1e-6)
+@pytest.mark.parametrize("dt,hidden", [(F32, 2048), (F16, 2048), (F16, 16384)])
+def test_optional_outputs_do_not_change_output(dt, hidden, want):
+    w = workloads.ssln("t", (37, hidden), dt, bias=True, epsilon=1e-6)
     x = workloads.generate(w, seed=5)
     ref, out, _ = run_both(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6, want=want)
     check(ref, out, want)
