@@ -24,7 +24,7 @@ from ._lib import SN_BF16, SN_F16, SN_F32, SkipNormError, check, lib
 
 __all__ = ["skip_rms_norm", "gated_rms_norm", "skip_group_norm", "skip_group_norm_workspace_size",
            "SkipRmsNormOutputs", "SkipGroupNormOutputs", "SkipNormError", "force_route",
-           "last_route", "abi_version", "copy_"]
+           "last_route", "exchange_timeout_us", "abi_version", "copy_"]
 
 #: Attribute defaults from the pages' Attributes tables.
 SSLN_EPSILON = 9.999999960041972e-13
@@ -201,6 +201,17 @@ def force_route(route: str):
         yield
     finally:
         lib().skipnorm_force_route(prev)
+
+
+@contextlib.contextmanager
+def exchange_timeout_us(microseconds: int):
+    """Bounded wait of SkipGroupNorm's cluster route inside the ``with``
+    block (0 makes every workgroup recompute the other slices itself)."""
+    prev = lib().skipnorm_set_exchange_timeout_us(int(microseconds))
+    try:
+        yield
+    finally:
+        lib().skipnorm_set_exchange_timeout_us(prev)
 
 
 def last_route() -> str:

@@ -31,6 +31,7 @@ SIGNATURES = {
     "skipnorm_abi_version": (_ci, []),
     "skipnorm_force_route": (_ci, [_ci]),
     "skipnorm_last_route": (ctypes.c_char_p, []),
+    "skipnorm_set_exchange_timeout_us": (_ci, [_ci]),
     "skipnorm_copy": (_ci, [_vp, _vp, _sz, _vp]),
 }
 

@@ -10,12 +10,11 @@
 // microseconds: cross-XCD atomics) than a kernel boundary on one stream, so
 // no kernel here waits for another block.  Two routes:
 //
-// group-block (NCHW, one (n, group) of at most 8 x 16 KiB, 12 x 16 KiB with
-//   a broadcast skip, or 16 Ki elements on the scalar route): a group is
-//   contiguous in NCHW, so one 1024-thread
-//   workgroup reads it once, keeps S in VGPRs, reduces with wave butterflies
-//   and one LDS step, and writes S and Y.  One launch, no workspace, exactly
-//   the operator's own traffic.
+// group-cluster (NCHW, groups of at most 8 x 256 x 16 sixteen-byte vectors
+//   or 8 x 256 x 32 scalars): a group is contiguous in NCHW, so K workgroups
+//   (K <= 8) read it once, keep S in VGPRs, exchange their slices' moments
+//   with a bounded wait (see sgn_cluster_kernel) and write S and Y.  One
+//   launch, exactly the operator's own traffic.
 //
 // split (everything else; NHWC always), three launches on one stream: the
 //   pages' "partial group statistics / combine / normalize" structure,
@@ -83,6 +82,7 @@ __device__ __forceinline__ Moments block_merge(Moments m, Moments* sh) {
     Moments tot = sh[0];
 #pragma unroll
     for (int w = 1; w < W; ++w) tot = merge(tot, sh[w]);
+    __syncthreads();  // `sh` may be reused right away
     return tot;
 }
 
@@ -103,78 +103,186 @@ __device__ __forceinline__ Vec<T, E> load_in(const T* p, int64_t i, bool stream)
     return stream ? load_vec_stream<T, E>(p, i) : load_vec<T, E>(p, i);
 }
 
-// ------------------------------------------------------------------ group-block
+// ------------------------------------------------------------------ group-cluster
+// K workgroups of 256 threads per (n, group) of an NCHW tensor (a group is
+// contiguous there), K = 1..8 chosen so that the grid covers the CUs: one CU
+// streams only ~20-25 GB/s, so a group must be spread over several CUs to
+// approach the chip's bandwidth.  Each workgroup forms S for its slice and
+// keeps it in VGPRs, publishes its slice's moments with a per-call tag, reads
+// the other slices' moments, combines all K in slice order (every workgroup
+// of the group computes bitwise the same statistics) and writes Y from its
+// registers.  The waits are bounded: a slice whose moments are not published
+// in time is recomputed by the waiting workgroup from X and skip with the
+// same arithmetic, so results never depend on scheduling and no workgroup
+// can wait forever.
 template <typename T, typename M>
-struct GroupBlockArgs {
+struct ClusterArgs {
     const T *X, *skip, *bias;
     T *S, *Y;
     const M *gamma, *beta;
+    Partial* part;     // N*groups*K slice moments
+    uint64_t* flags;   // N*groups*K publication tags
+    uint64_t tag;      // unique per call
+    long long timeout_ticks;  // wall-clock ticks a workgroup waits for a slice
     int64_t HW;
-    int C, cpg, groups;
-    uint32_t Kv;  // vectors per group
-    FastDiv div;  // by H*W
+    int C, cpg, groups, K;
+    uint32_t Kv;   // vectors per group
+    uint32_t vps;  // vectors per slice
+    FastDiv div;   // by H*W
     bool skip_bcast, silu;
     float eps;
 };
 
-constexpr int kGroupBlockThreads = 1024;
+constexpr int kClusterThreads = 256;
+constexpr int kClusterMaxK = 8;
 
 template <typename T, typename M, int E, int R, bool BCAST>
-__global__ void __launch_bounds__(kGroupBlockThreads)
-sgn_group_block_kernel(GroupBlockArgs<T, M> a) {
+__global__ void __launch_bounds__(kClusterThreads)
+sgn_cluster_kernel(ClusterArgs<T, M> a) {
     using V = Vec<T, E>;
-    __shared__ Moments sh[kGroupBlockThreads / 64];
+    __shared__ Moments sh[kClusterThreads / 64];
+    __shared__ Moments slice_m[kClusterMaxK];
+    __shared__ int late[kClusterMaxK];
     const int t = threadIdx.x;
-    const int ng = blockIdx.x;
+    const int ng = blockIdx.x / a.K, k = blockIdx.x % a.K;
     const int n = ng / a.groups, g = ng % a.groups;
     const int64_t base = (int64_t(n) * a.C + int64_t(g) * a.cpg) * a.HW / E;  // in vectors
     const bool has_bias = a.bias != nullptr;
     // Channel of vector j of the group; with E > 1, H*W is a whole number of
     // vectors, so no vector straddles channels.
     auto channel = [&](uint32_t j) { return g * a.cpg + int(fastdiv(j * E, a.div)); };
+    auto vec_of = [&](int slice, int r) {
+        return uint32_t(slice) * a.vps + uint32_t(t) + uint32_t(r) * kClusterThreads;
+    };
+    auto end_of = [&](int slice) {
+        const uint32_t e = uint32_t(slice + 1) * a.vps;
+        return e < a.Kv ? e : a.Kv;
+    };
+    // S of one vector, rounded to T; the same arithmetic for the own slice
+    // and for a recomputed one.
+    auto form = [&](const V& x, const V& kv, uint32_t j, V& s) {
+        const int c = channel(j);
+        const float bb = has_bias ? to_f32(a.bias[c]) : 0.0f;
+        float kb = 0.0f;
+        if constexpr (BCAST) kb = to_f32(a.skip[int64_t(n) * a.C + c]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float kk = kb;
+            if constexpr (!BCAST) kk = to_f32(kv.v[e]);
+            residual_sum<T>(to_f32(x.v[e]), kk, has_bias, bb, s.v[e]);
+        }
+    };
+    auto accumulate = [&](ShiftedSums& acc, float& cnt, const V& s) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc.add(to_f32(s.v[e]), cnt == 0.0f && e == 0);
+        cnt += float(E);
+    };
 
+    // ---- own slice: S into registers, S stored, slice moments
+    const uint32_t end = end_of(k);
     V sv[R], xs[R];
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const uint32_t j = uint32_t(t) + uint32_t(k) * kGroupBlockThreads;
-        if (j < a.Kv) {
-            xs[k] = load_vec_stream<T, E>(a.X, base + j);
-            if constexpr (!BCAST) sv[k] = load_vec_stream<T, E>(a.skip, base + j);
+    for (int r = 0; r < R; ++r) {
+        const uint32_t j = vec_of(k, r);
+        if (j < end) {
+            xs[r] = load_vec_stream<T, E>(a.X, base + j);
+            if constexpr (!BCAST) sv[r] = load_vec_stream<T, E>(a.skip, base + j);
         }
     }
     ShiftedSums acc;
     float cnt = 0.0f;
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const uint32_t j = uint32_t(t) + uint32_t(k) * kGroupBlockThreads;
-        if (j < a.Kv) {
-            const int c = channel(j);
-            const float bb = has_bias ? to_f32(a.bias[c]) : 0.0f;
-            float kb = 0.0f;
-            if constexpr (BCAST) kb = to_f32(a.skip[int64_t(n) * a.C + c]);
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                float kk = kb;
-                if constexpr (!BCAST) kk = to_f32(sv[k].v[e]);
-                const float s = residual_sum<T>(to_f32(xs[k].v[e]), kk, has_bias, bb, sv[k].v[e]);
-                acc.add(s, cnt == 0.0f && e == 0);
-            }
-            if (a.S) store_vec_stream<T, E>(a.S, base + j, sv[k]);
-            cnt += float(E);
+    for (int r = 0; r < R; ++r) {
+        const uint32_t j = vec_of(k, r);
+        if (j < end) {
+            form(xs[r], sv[r], j, sv[r]);
+            if (a.S) store_vec_stream<T, E>(a.S, base + j, sv[r]);
+            accumulate(acc, cnt, sv[r]);
         }
     }
-    const float2 st = finalize(block_merge<kGroupBlockThreads / 64>(acc.moments(cnt), sh), a.eps);
+    const Moments mine = block_merge<kClusterThreads / 64>(acc.moments(cnt), sh);
+
+    // ---- exchange with the other K-1 slices of the group
+    Moments tot = mine;
+    if (a.K > 1) {
+        uint64_t* flags = a.flags + int64_t(ng) * a.K;
+        Partial* part = a.part + int64_t(ng) * a.K;
+        // Publication: the moments go out as agent-scope atomic stores, which
+        // are coherent across the XCDs' separate L2 caches; the vector-memory
+        // counter wait makes them complete before the tag is stored, and a
+        // reader that sees the tag (agent-scope atomic load) therefore reads
+        // this call's moments.  No data written with plain stores is
+        // exchanged, so no cache-wide release or acquire fence is needed.
+        if (t == 0) {
+            float* pp = reinterpret_cast<float*>(&part[k]);
+            __hip_atomic_store(pp + 0, mine.n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pp + 1, mine.mean, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pp + 2, mine.m2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0);
+            __hip_atomic_store(&flags[k], a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (t < a.K && t != k) {
+            const long long t0 = wall_clock64();
+            bool ok = false;
+            for (;;) {
+                if (__hip_atomic_load(&flags[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.tag) {
+                    ok = true;
+                    break;
+                }
+                if (wall_clock64() - t0 > a.timeout_ticks) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            late[t] = ok ? 0 : 1;
+            if (ok) {
+                float* pp = reinterpret_cast<float*>(&part[t]);
+                slice_m[t] = Moments{__hip_atomic_load(pp + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                     __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                     __hip_atomic_load(pp + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+            }
+        }
+        __syncthreads();
+        tot = Moments{0.0f, 0.0f, 0.0f};
+        for (int q = 0; q < a.K; ++q) {  // uniform over the workgroup
+            Moments m;
+            if (q == k) {
+                m = mine;
+            } else if (!late[q]) {
+                m = slice_m[q];
+            } else {
+                // Slice q was not published in time: recompute its moments
+                // exactly as its own workgroup does.
+                const uint32_t qend = end_of(q);
+                ShiftedSums qacc;
+                float qcnt = 0.0f;
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const uint32_t j = uint32_t(t) + uint32_t(k) * kGroupBlockThreads;
-        if (j < a.Kv) {
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t j = vec_of(q, r);
+                    if (j < qend) {
+                        V x = load_vec<T, E>(a.X, base + j), kv, sq;
+                        if constexpr (!BCAST) kv = load_vec<T, E>(a.skip, base + j);
+                        form(x, kv, j, sq);
+                        accumulate(qacc, qcnt, sq);
+                    }
+                }
+                m = block_merge<kClusterThreads / 64>(qacc.moments(qcnt), sh);
+            }
+            tot = merge(tot, m);
+        }
+    }
+
+    // ---- normalize the held S
+    const float2 st = finalize(tot, a.eps);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t j = vec_of(k, r);
+        if (j < end) {
             const int c = channel(j);
             const float scl = st.y * to_f32(a.gamma[c]);
             const float sft = to_f32(a.beta[c]);
             V out;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                float y = fmaf_(to_f32(sv[k].v[e]) - st.x, scl, sft);
+                float y = fmaf_(to_f32(sv[r].v[e]) - st.x, scl, sft);
                 if (a.silu) y = silu_f32(y);
                 out.v[e] = from_f32<T>(y);
             }
@@ -538,46 +646,53 @@ int64_t split_blocks(int dtype, int64_t C, int64_t HW, int64_t groups, bool chan
     return B;
 }
 
-// Vectors per thread the group-block route holds within the 128 registers a
-// 1024-thread workgroup leaves each thread: 12 sixteen-byte vectors with a
-// broadcast skip, 8 with a full skip in flight beside X; 16 scalars.
-constexpr int kGroupBlockMaxVecBcast = 12;
-constexpr int kGroupBlockMaxVecFull = 8;
-constexpr int kGroupBlockMaxScalar = 16;
-
-int group_block_max_r(int E, bool bcast) {
-    if (E > 1) return bcast ? kGroupBlockMaxVecBcast : kGroupBlockMaxVecFull;
-    return kGroupBlockMaxScalar;
-}
+// Vectors per thread a cluster workgroup holds: 16 sixteen-byte vectors or
+// 32 scalars; with K <= 8 workgroups per group that bounds the groups this
+// route takes (larger ones use the split route).
+constexpr int kClusterMaxVec = 16;
+constexpr int kClusterMaxScalar = 32;
+constexpr int64_t kClusterTargetBlocks = 512;  // two workgroups per CU
 
 template <typename T, typename M, int E, int R>
-hipError_t launch_group_block_r(const GroupBlockArgs<T, M>& ga, int64_t NG, hipStream_t stream) {
-    if (ga.skip_bcast) {
-        hipLaunchKernelGGL((sgn_group_block_kernel<T, M, E, R, true>), dim3(unsigned(NG)),
-                           dim3(kGroupBlockThreads), 0, stream, ga);
-    } else {
-        if constexpr (R <= (E > 1 ? kGroupBlockMaxVecFull : kGroupBlockMaxScalar))
-            hipLaunchKernelGGL((sgn_group_block_kernel<T, M, E, R, false>), dim3(unsigned(NG)),
-                               dim3(kGroupBlockThreads), 0, stream, ga);
-        else
-            return hipErrorInvalidValue;  // callers check the size first
-    }
+hipError_t launch_cluster_r(const ClusterArgs<T, M>& ca, int64_t blocks, hipStream_t stream) {
+    if (ca.skip_bcast)
+        hipLaunchKernelGGL((sgn_cluster_kernel<T, M, E, R, true>), dim3(unsigned(blocks)),
+                           dim3(kClusterThreads), 0, stream, ca);
+    else
+        hipLaunchKernelGGL((sgn_cluster_kernel<T, M, E, R, false>), dim3(unsigned(blocks)),
+                           dim3(kClusterThreads), 0, stream, ca);
     return hipGetLastError();
 }
 
 template <typename T, typename M, int E>
-hipError_t launch_group_block(const GroupBlockArgs<T, M>& ga, int64_t NG, hipStream_t stream) {
-    const uint32_t r = (ga.Kv + kGroupBlockThreads - 1) / kGroupBlockThreads;
+hipError_t launch_cluster(const ClusterArgs<T, M>& ca, int64_t blocks, hipStream_t stream) {
+    const uint32_t r = (ca.vps + kClusterThreads - 1) / kClusterThreads;
     if constexpr (E > 1) {
-        if (r <= 2) return launch_group_block_r<T, M, E, 2>(ga, NG, stream);
-        if (r <= 4) return launch_group_block_r<T, M, E, 4>(ga, NG, stream);
-        if (r <= 8) return launch_group_block_r<T, M, E, 8>(ga, NG, stream);
-        return launch_group_block_r<T, M, E, kGroupBlockMaxVecBcast>(ga, NG, stream);
+        if (r <= 1) return launch_cluster_r<T, M, E, 1>(ca, blocks, stream);
+        if (r <= 2) return launch_cluster_r<T, M, E, 2>(ca, blocks, stream);
+        if (r <= 4) return launch_cluster_r<T, M, E, 4>(ca, blocks, stream);
+        if (r <= 8) return launch_cluster_r<T, M, E, 8>(ca, blocks, stream);
+        if (r <= 12) return launch_cluster_r<T, M, E, 12>(ca, blocks, stream);
+        return launch_cluster_r<T, M, E, kClusterMaxVec>(ca, blocks, stream);
     } else {
-        if (r <= 4) return launch_group_block_r<T, M, E, 4>(ga, NG, stream);
-        if (r <= 8) return launch_group_block_r<T, M, E, 8>(ga, NG, stream);
-        return launch_group_block_r<T, M, E, kGroupBlockMaxScalar>(ga, NG, stream);
+        if (r <= 4) return launch_cluster_r<T, M, E, 4>(ca, blocks, stream);
+        if (r <= 8) return launch_cluster_r<T, M, E, 8>(ca, blocks, stream);
+        if (r <= 16) return launch_cluster_r<T, M, E, 16>(ca, blocks, stream);
+        return launch_cluster_r<T, M, E, kClusterMaxScalar>(ca, blocks, stream);
     }
+}
+
+// Workgroups per (n, group) of the cluster route for a group of Kv vectors
+// (0: the group is too large for it).
+int cluster_k(int64_t Kv, int64_t NG, int max_r) {
+    const int64_t cap = int64_t(kClusterThreads) * max_r;
+    const int64_t k_fit = (Kv + cap - 1) / cap;
+    if (k_fit > kClusterMaxK) return 0;
+    int64_t k = (kClusterTargetBlocks + NG - 1) / NG;
+    if (k < k_fit) k = k_fit;
+    if (k > kClusterMaxK) k = kClusterMaxK;
+    if (k > Kv) k = Kv > 0 ? Kv : 1;  // no empty slices
+    return int(k);
 }
 
 template <typename T, typename M>
@@ -606,28 +721,50 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
                           data_ok && aligned16(a.skip) && (!a.bias || aligned16(a.bias));
     const bool nchw_vec = vec_allowed && !a.channels_last && HW % EV == 0 && data_ok;
 
-    // ---- group-block route (NCHW)
-    const bool block_route = !a.channels_last && want != Route::Split && want != Route::Block;
-    if (block_route) {
-        GroupBlockArgs<T, M> ga{X, skip, bias, S, Y, gamma, beta, HW, C, cpg, groups, 0,
-                                make_fastdiv(uint32_t(HW)), a.skip_broadcast, silu, a.epsilon};
-        if (nchw_vec && K / EV <= int64_t(group_block_max_r(EV, a.skip_broadcast)) * kGroupBlockThreads) {
-            *route = "sgn.block.nchw.vec16";
-            ga.Kv = uint32_t(K / EV);
-            return launch_group_block<T, M, EV>(ga, NG, stream);
-        }
-        if (!nchw_vec && K <= int64_t(group_block_max_r(1, a.skip_broadcast)) * kGroupBlockThreads) {
-            *route = "sgn.block.nchw.scalar";
-            ga.Kv = uint32_t(K);
-            return launch_group_block<T, M, 1>(ga, NG, stream);
+    // ---- group-cluster route (NCHW)
+    const int64_t B_ws = sgn_partials_per_group(a.dtype, a.N, a.C, a.H, a.W, a.groups, a.channels_last);
+    Partial* part = static_cast<Partial*>(a.workspace);
+    float2* stat = reinterpret_cast<float2*>(part + NG * B_ws);
+    const bool cluster_route = !a.channels_last && want != Route::Split && want != Route::Block;
+    if (cluster_route) {
+        const int E = nchw_vec ? EV : 1;
+        const int64_t Kv = K / E;
+        const int Kc = cluster_k(Kv, NG, nchw_vec ? kClusterMaxVec : kClusterMaxScalar);
+        if (Kc > 0) {
+            ClusterArgs<T, M> ca;
+            ca.X = X;
+            ca.skip = skip;
+            ca.bias = bias;
+            ca.S = S;
+            ca.Y = Y;
+            ca.gamma = gamma;
+            ca.beta = beta;
+            ca.part = part;
+            ca.flags = reinterpret_cast<uint64_t*>(stat + NG);
+            ca.tag = a.tag;
+            ca.timeout_ticks = a.exchange_timeout_ticks;
+            ca.HW = HW;
+            ca.C = C;
+            ca.cpg = cpg;
+            ca.groups = groups;
+            ca.K = Kc;
+            ca.Kv = uint32_t(Kv);
+            ca.vps = uint32_t((Kv + Kc - 1) / Kc);
+            ca.div = make_fastdiv(uint32_t(HW));
+            ca.skip_bcast = a.skip_broadcast;
+            ca.silu = silu;
+            ca.eps = a.epsilon;
+            if (nchw_vec) {
+                *route = "sgn.cluster.nchw.vec16";
+                return launch_cluster<T, M, EV>(ca, NG * Kc, stream);
+            }
+            *route = "sgn.cluster.nchw.scalar";
+            return launch_cluster<T, M, 1>(ca, NG * Kc, stream);
         }
     }
 
     // ---- split route
-    const int64_t B_ws = sgn_partials_per_group(a.dtype, a.N, a.C, a.H, a.W, a.groups, a.channels_last);
     const int B = int(split_blocks(a.dtype, a.C, HW, a.groups, a.channels_last));
-    Partial* part = static_cast<Partial*>(a.workspace);
-    float2* stat = reinterpret_cast<float2*>(part + NG * B_ws);
     const dim3 fin_grid = dim3(unsigned(NG));
 
     if (nhwc_vec) {
@@ -696,14 +833,19 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
 int64_t sgn_partials_per_group(int dtype, int64_t N, int64_t C, int64_t H, int64_t W,
                                int64_t groups, bool channels_last) {
     (void)N;
-    return split_blocks(dtype, C, H * W, groups, channels_last);
+    const int64_t b = split_blocks(dtype, C, H * W, groups, channels_last);
+    return channels_last || b >= kClusterMaxK ? b : kClusterMaxK;
 }
 
+// Workspace: N*groups*B partials of 16 bytes, N*groups (mean, rstd) pairs,
+// then (NCHW) N*groups*8 publication tags of the cluster route.
 size_t sgn_workspace_bytes(int dtype, int64_t N, int64_t C, int64_t H, int64_t W, int64_t groups,
                            bool channels_last) {
     const int64_t B = sgn_partials_per_group(dtype, N, C, H, W, groups, channels_last);
     const int64_t NG = N * groups;
-    return size_t(NG * B) * sizeof(Partial) + size_t(NG) * sizeof(float2);
+    size_t bytes = size_t(NG * B) * sizeof(Partial) + size_t(NG) * sizeof(float2);
+    if (!channels_last) bytes += size_t(NG) * kClusterMaxK * sizeof(uint64_t);
+    return bytes;
 }
 
 hipError_t launch_sgn(const SgnArgs& a, Route want, hipStream_t stream, const char** route) {

@@ -2,6 +2,7 @@
 // (host only, before anything is enqueued), route selection hooks, error
 // reporting, and the calls into the kernel launchers.
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -15,6 +16,23 @@ namespace {
 thread_local std::string g_error;
 thread_local const char* g_route = "";
 std::atomic<int> g_force_route{0};
+
+// Wall-clock ticks (100 MHz device clock) a SkipGroupNorm workgroup waits for
+// another workgroup's published moments before recomputing them itself.
+constexpr long long kDefaultExchangeTimeoutUs = 100;
+std::atomic<long long> g_exchange_timeout_us{kDefaultExchangeTimeoutUs};
+
+// Per-call publication tags: a process-unique 64-bit sequence, so tags left
+// in a reused workspace by earlier calls (or other processes) never match.
+uint64_t initial_tag() {
+    const uint64_t now = uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
+    uint64_t x = now ^ (uint64_t(reinterpret_cast<uintptr_t>(&g_force_route)) << 17);
+    x ^= x >> 33;
+    x *= 0xff51afd7ed558ccdULL;  // a 64-bit finalizer mix
+    x ^= x >> 33;
+    return x | 1;
+}
+std::atomic<uint64_t> g_tag{initial_tag()};
 
 sn_status fail(sn_status st, const char* fmt, ...) {
     char buf[512];
@@ -253,6 +271,8 @@ sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t 
     a.Y = Y;
     a.S = S;
     a.workspace = workspace;
+    a.tag = g_tag.fetch_add(2) | 1;  // odd, never 0
+    a.exchange_timeout_ticks = g_exchange_timeout_us.load() * 100;
     const char* route = "";
     return finish_launch(sn::launch_sgn(a, current_route(), stream, &route), route, "skip_group_norm");
 }
@@ -267,6 +287,12 @@ int skipnorm_force_route(int route) {
 }
 
 const char* skipnorm_last_route(void) { return g_route; }
+
+int skipnorm_set_exchange_timeout_us(int microseconds) {
+    const long long prev = g_exchange_timeout_us.load();
+    g_exchange_timeout_us.store(microseconds < 0 ? kDefaultExchangeTimeoutUs : microseconds);
+    return int(prev);
+}
 
 sn_status skipnorm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
     if (bytes == 0) return ok();

@@ -44,6 +44,8 @@ struct SgnArgs {
     float epsilon;
     void *Y, *S;
     void* workspace;
+    uint64_t tag;                     // unique per call (publication tags)
+    long long exchange_timeout_ticks; // bounded wait of the cluster route
 };
 // Blocks of the statistics pass per (n, group) partial-sum row; a function
 // of the shapes and T only, so that the workspace size does not depend on

@@ -33,7 +33,7 @@
  *     2^30 elements.
  *   - Results are deterministic: no floating-point atomics; every reduction
  *     runs in a fixed order, and requesting an optional output never changes
- *     the others.
+ *     the others.  No kernel waits on another workgroup without a bound.
  */
 #ifndef SKIPNORM_H
 #define SKIPNORM_H
@@ -185,6 +185,14 @@ int skipnorm_abi_version(void);
  * Returns the previous value; an unknown value leaves the setting unchanged
  * and returns the current one. */
 int skipnorm_force_route(int route);
+
+/* SkipGroupNorm's cluster route (NCHW) spreads one (n, group) over up to 8
+ * workgroups that exchange partial moments; a workgroup waits at most this
+ * long for another's moments and otherwise recomputes them itself with the
+ * same arithmetic (results are identical either way).  Sets the wait for
+ * later calls in the process (negative: the default, 100 us) and returns the
+ * previous value.  A test hook: 0 forces every recomputation path. */
+int skipnorm_set_exchange_timeout_us(int microseconds);
 
 /* Name of the route the calling thread's last successful op call took
  * (e.g. "ssln.wave", "ssln.scalar", "gated.segment", "sgn.nhwc"). */

@@ -76,23 +76,21 @@ def test_matches_oracle(case, route):
     if route == "block":
         assert used.startswith("sgn.split") and used.endswith(".scalar")
     if route == "auto" and not cl:
-        assert used.startswith("sgn.block")  # every NCHW case here fits one workgroup
+        assert used.startswith("sgn.cluster")  # every NCHW case here fits the cluster route
 
 
-# NCHW groups around the one-workgroup limits (elements per (n, group)):
-# 16-byte vectors: 8 Ki vectors with a full skip, 12 Ki with a broadcast
-# skip; scalars: 16 Ki elements.
+# NCHW groups around the cluster route's limits (per (n, group), at most 8
+# workgroups of 256 threads): 16 sixteen-byte vectors or 32 scalars per thread.
 LIMIT_CASES = [
     # (N, C, H, W, T, groups, broadcast skip, expected auto route)
-    (1, 32, 32, 32, F32, 1, False, "sgn.block.nchw.vec16"),    # 8192 vectors, full skip
-    (1, 64, 32, 32, F32, 1, False, "sgn.split.nchw.vec16"),    # 16384 vectors, full skip
-    (2, 48, 32, 32, F32, 1, True, "sgn.block.nchw.vec16"),     # 12288 vectors, broadcast
-    (1, 52, 32, 32, F32, 1, True, "sgn.split.nchw.vec16"),     # 13312 vectors, broadcast
-    (1, 32, 64, 64, F16, 2, False, "sgn.block.nchw.vec16"),    # 8192 vectors of halves
-    (2, 16, 32, 32, F16, 1, True, "sgn.block.nchw.vec16"),     # 2048 vectors of halves
-    (1, 16, 31, 33, F32, 1, False, "sgn.block.nchw.scalar"),   # 16368 elements
-    (1, 17, 31, 33, F32, 1, False, "sgn.split.nchw.scalar"),   # 17391 elements
-    (3, 6, 7, 7, F16, 3, True, "sgn.block.nchw.scalar"),
+    (1, 32, 64, 64, F32, 1, False, "sgn.cluster.nchw.vec16"),  # 32768 vectors: 8 full workgroups
+    (1, 33, 64, 64, F32, 1, False, "sgn.split.nchw.vec16"),    # 33792 vectors
+    (1, 64, 64, 64, F16, 2, True, "sgn.cluster.nchw.vec16"),   # 16384 vectors of halves
+    (2, 16, 32, 32, F16, 1, True, "sgn.cluster.nchw.vec16"),   # 2048 vectors, 8 small slices
+    (1, 64, 31, 33, F32, 1, False, "sgn.cluster.nchw.scalar"), # 65472 elements
+    (1, 65, 31, 33, F32, 1, False, "sgn.split.nchw.scalar"),   # 66495 elements
+    (3, 6, 7, 7, F16, 3, True, "sgn.cluster.nchw.scalar"),     # 98 elements in 8 slices
+    (1, 2, 1, 3, F32, 2, False, "sgn.cluster.nchw.scalar"),    # 3 elements: 3 slices of 1
 ]
 
 
@@ -131,6 +129,48 @@ def test_broadcast_equals_expanded(cl):
     # The (N, 1, 1, C) spelling is the same broadcast.
     ref2, sp, _ = run(x, w, skip_override=x["skip"].reshape(N, 1, 1, C))
     assert_bitwise(to_host(sp.Y), to_host(bc.Y), "(N,1,1,C) spelling")
+
+
+FALLBACK_CASES = [
+    (2, 64, 16, 16, F32, F16, 0, True, False, 8, 0),
+    (1, 32, 24, 24, F16, F32, 0, False, True, 4, 1),
+    (2, 12, 7, 7, F32, F32, 0, True, True, 3, 1),   # scalar accesses
+]
+
+
+@pytest.mark.parametrize("case", FALLBACK_CASES, ids=lambda c: f"N{c[0]}C{c[1]}H{c[2]}W{c[3]}")
+def test_cluster_recompute_path_matches(case):
+    """With a zero wait every workgroup recomputes the other slices' moments
+    itself; the results must equal those of the published-moments path bit
+    for bit (and the oracle's within tolerance)."""
+    w, x = make(case, seed=6)
+    ref, normal, used = run(x, w)
+    assert used.startswith("sgn.cluster")
+    with gn.exchange_timeout_us(0):
+        _, forced, used2 = run(x, w)
+    assert used2 == used
+    assert_bitwise(to_host(forced.Y), to_host(normal.Y), "Y recomputed vs published")
+    assert_bitwise(to_host(forced.S), to_host(normal.S), "S")
+    check(ref, forced)
+
+
+def test_cluster_tags_ignore_stale_workspace():
+    """A workspace left over from earlier calls (stale tags and moments from
+    a different tensor) must not leak into the next call."""
+    N, C, H, W = 2, 64, 16, 16
+    w, x = make((N, C, H, W, F32, F32, 0, False, True, 8, 1), seed=7)
+    w2, x2 = make((N, C, H, W, F32, F32, 0, False, True, 8, 1), seed=8)
+    ws = torch.empty(gn.skip_group_norm_workspace_size(to_dev(x["X"]), 8, 0), dtype=torch.uint8,
+                     device="cuda")
+    kw = dict(groups=8, activation=1, channels_last=0, want_sum=True, workspace=ws)
+    gn.skip_group_norm(to_dev(x2["X"]), to_dev(x2["gamma"]), to_dev(x2["beta"]), to_dev(x2["skip"]),
+                       to_dev(x2["bias"]), **kw)
+    out = gn.skip_group_norm(to_dev(x["X"]), to_dev(x["gamma"]), to_dev(x["beta"]), to_dev(x["skip"]),
+                             to_dev(x["bias"]), **kw)
+    ref_y, ref_s = oracle.skip_group_norm(x["X"], x["gamma"], x["beta"], x["skip"], x["bias"],
+                                          groups=8, activation=1, channels_last=0, want_sum=True)
+    assert_close(to_host(out.Y), ref_y, "Y after a call with other data")
+    assert_bitwise(to_host(out.S), ref_s, "S")
 
 
 def test_layouts_agree():
