@@ -77,6 +77,12 @@ def test_matches_oracle(case, route):
         assert used.startswith("sgn.split") and used.endswith(".scalar")
     if route == "auto" and not cl:
         assert used.startswith("sgn.cluster")  # every NCHW case here fits the cluster route
+    if route == "auto" and cl:
+        # NHWC: the channel-block cluster needs whole 16-byte vectors per pixel
+        # and groups at least one vector wide.
+        ev = 16 // np.dtype(T).itemsize
+        fits = C % ev == 0 and C // groups >= ev
+        assert used == ("sgn.cluster.nhwc.vec16" if fits else "sgn.split.nhwc.scalar")
 
 
 # NCHW groups around the cluster route's limits (per (n, group), at most 8
@@ -101,6 +107,39 @@ def test_group_block_limits(case):
     w = workloads.sgn("t", N, C, H, W, T, np.float32, channels_last=False, broadcast_skip=bc,
                       bias=True, groups=groups, activation=1, epsilon=1e-5)
     x = workloads.generate(w, seed=C + H)
+    ref, out, used = run(x, w)
+    assert used == want_route
+    check(ref, out)
+
+
+# NHWC channel-block cluster around its limits: at most 64 slices per
+# (image, channel block), 16 pixels per thread, 16 groups per block, and
+# groups at least one 16-byte vector wide.
+NHWC_LIMIT_CASES = [
+    # (N, C, H, W, T, groups, broadcast skip, expected auto route)
+    (2, 320, 64, 64, F16, 32, False, "sgn.cluster.nhwc.vec16"),   # 51 pixel lanes (odd), 16 slices
+    (1, 320, 204, 256, F16, 32, False, "sgn.cluster.nhwc.vec16"), # 52224 pixels: 64 slices, 16 pixels/thread
+    (1, 320, 205, 256, F16, 32, True, "sgn.split.nhwc.vec16"),    # 52480 pixels: too many
+    (8, 40, 32, 32, F16, 5, False, "sgn.cluster.nhwc.vec16"),     # one vector per block
+    (2, 72, 16, 16, F16, 8, True, "sgn.cluster.nhwc.vec16"),      # 9 channels/group: 2 groups per wave
+    (16, 144, 8, 8, F16, 16, False, "sgn.cluster.nhwc.vec16"),    # 16 groups per block: 4 per wave
+    (2, 96, 9, 11, F16, 8, False, "sgn.cluster.nhwc.vec16"),      # 12 channels/group, ragged last slice
+    (2, 64, 8, 8, F16, 16, False, "sgn.split.nhwc.vec16"),        # 4 channels/group < one vector
+    (1, 16, 9, 7, F32, 4, True, "sgn.cluster.nhwc.vec16"),        # float32, 4 channels/group, 1 slice
+    (2, 2560, 8, 8, F32, 32, False, "sgn.cluster.nhwc.vec16"),    # 640 vectors per pixel, 3 pixel lanes
+    (600, 16, 2, 2, F32, 2, True, "sgn.cluster.nhwc.vec16"),      # one slice per image: no exchange
+]
+
+
+@pytest.mark.parametrize("case", NHWC_LIMIT_CASES, ids=[f"N{c[0]}C{c[1]}H{c[2]}W{c[3]}-"
+                                                        f"{np.dtype(c[4]).name}-g{c[5]}"
+                                                        f"{'-bc' if c[6] else ''}"
+                                                        for c in NHWC_LIMIT_CASES])
+def test_nhwc_cluster_limits(case):
+    N, C, H, W, T, groups, bc, want_route = case
+    w = workloads.sgn("t", N, C, H, W, T, np.float32, channels_last=True, broadcast_skip=bc,
+                      bias=True, groups=groups, activation=1, epsilon=1e-5)
+    x = workloads.generate(w, seed=C + H + N)
     ref, out, used = run(x, w)
     assert used == want_route
     check(ref, out)
@@ -135,6 +174,9 @@ FALLBACK_CASES = [
     (2, 64, 16, 16, F32, F16, 0, True, False, 8, 0),
     (1, 32, 24, 24, F16, F32, 0, False, True, 4, 1),
     (2, 12, 7, 7, F32, F32, 0, True, True, 3, 1),   # scalar accesses
+    (2, 320, 16, 16, F16, F32, 1, False, True, 32, 1),  # NHWC, 5 slices of 51 pixel lanes
+    (2, 72, 16, 16, F16, F16, 1, True, False, 8, 0),    # NHWC, 2 groups per wave, 9 slices
+    (1, 48, 32, 31, F32, F32, 1, False, True, 4, 1),    # NHWC float32, 46 slices, ragged last
 ]
 
 
@@ -154,21 +196,23 @@ def test_cluster_recompute_path_matches(case):
     check(ref, forced)
 
 
-def test_cluster_tags_ignore_stale_workspace():
+@pytest.mark.parametrize("cl", [0, 1])
+def test_cluster_tags_ignore_stale_workspace(cl):
     """A workspace left over from earlier calls (stale tags and moments from
     a different tensor) must not leak into the next call."""
     N, C, H, W = 2, 64, 16, 16
-    w, x = make((N, C, H, W, F32, F32, 0, False, True, 8, 1), seed=7)
-    w2, x2 = make((N, C, H, W, F32, F32, 0, False, True, 8, 1), seed=8)
-    ws = torch.empty(gn.skip_group_norm_workspace_size(to_dev(x["X"]), 8, 0), dtype=torch.uint8,
+    w, x = make((N, C, H, W, F32, F32, cl, False, True, 8, 1), seed=7)
+    w2, x2 = make((N, C, H, W, F32, F32, cl, False, True, 8, 1), seed=8)
+    ws = torch.empty(gn.skip_group_norm_workspace_size(to_dev(x["X"]), 8, cl), dtype=torch.uint8,
                      device="cuda")
-    kw = dict(groups=8, activation=1, channels_last=0, want_sum=True, workspace=ws)
+    kw = dict(groups=8, activation=1, channels_last=cl, want_sum=True, workspace=ws)
     gn.skip_group_norm(to_dev(x2["X"]), to_dev(x2["gamma"]), to_dev(x2["beta"]), to_dev(x2["skip"]),
                        to_dev(x2["bias"]), **kw)
     out = gn.skip_group_norm(to_dev(x["X"]), to_dev(x["gamma"]), to_dev(x["beta"]), to_dev(x["skip"]),
                              to_dev(x["bias"]), **kw)
+    assert gn.last_route() == ("sgn.cluster.nhwc.vec16" if cl else "sgn.cluster.nchw.vec16")
     ref_y, ref_s = oracle.skip_group_norm(x["X"], x["gamma"], x["beta"], x["skip"], x["bias"],
-                                          groups=8, activation=1, channels_last=0, want_sum=True)
+                                          groups=8, activation=1, channels_last=cl, want_sum=True)
     assert_close(to_host(out.Y), ref_y, "Y after a call with other data")
     assert_bitwise(to_host(out.S), ref_s, "S")
 

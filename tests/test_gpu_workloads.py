@@ -84,7 +84,7 @@ def test_sgn_full(name):
                              to_dev(x.get("bias")), groups=a["groups"], activation=a["activation"],
                              epsilon=a["epsilon"], channels_last=a["channels_last"],
                              want_sum=want_sum)
-    assert gn.last_route() == ("sgn.split.nhwc.vec16" if a["channels_last"] else "sgn.cluster.nchw.vec16")
+    assert gn.last_route() == ("sgn.cluster.nhwc.vec16" if a["channels_last"] else "sgn.cluster.nchw.vec16")
     ref_y, ref_s = oracle.skip_group_norm(x["X"], x["gamma"], x["beta"], x["skip"], x.get("bias"),
                                           groups=a["groups"], activation=a["activation"],
                                           epsilon=a["epsilon"], channels_last=a["channels_last"],
