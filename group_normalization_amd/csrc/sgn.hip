@@ -110,6 +110,61 @@ __device__ __forceinline__ Vec<T, E> load_in(const T* p, int64_t i, bool stream)
     return stream ? load_vec_stream<T, E>(p, i) : load_vec<T, E>(p, i);
 }
 
+// Pairwise combination without branches, the weight taken from the
+// hardware reciprocal (about 1 ulp) rather than an IEEE division: thousands
+// of these sit on the cluster route's critical path.  Empty moments are
+// (0, 0, 0); merging with one is exact either way (weight 0, or weight 1
+// when the other side is empty).  Every workgroup runs the same operations,
+// so the results stay bitwise reproducible.
+__device__ __forceinline__ Moments merge_rcp(const Moments& a, const Moments& b) {
+    const float n = a.n + b.n;
+    const float wb = b.n == n ? 1.0f : b.n * __builtin_amdgcn_rcpf(n);
+    const float d = b.mean - a.mean;
+    Moments r;
+    r.n = n;
+    r.mean = fmaf_(d, wb, a.mean);
+    r.m2 = fmaf_(d * d, a.n * wb, a.m2 + b.m2);
+    return r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ Moments dpp_merge_step(const Moments& m, bool upper) {
+    const Moments o{dpp_mov<CTRL>(m.n), dpp_mov<CTRL>(m.mean), dpp_mov<CTRL>(m.m2)};
+    return upper ? merge_rcp(o, m) : merge_rcp(m, o);
+}
+
+// Ordered butterfly over aligned segments of W lanes (W a power of two, at
+// most 64; uniform over the wave): every lane of a segment ends with bitwise
+// the same combination of the segment's values in lane order.  After the two
+// quad steps each quad is uniform, so mirroring inside 8 and 16 lanes pairs
+// the same quads and half-rows as an xor by 4 and by 8 would.
+__device__ __forceinline__ Moments segment_merge(Moments m, int W) {
+    const int lane = threadIdx.x & 63;
+    if (W >= 2) m = dpp_merge_step<kQuadXor1>(m, lane & 1);
+    if (W >= 4) m = dpp_merge_step<kQuadXor2>(m, lane & 2);
+    if (W >= 8) m = dpp_merge_step<kRowHalfMirror>(m, lane & 4);
+    if (W >= 16) m = dpp_merge_step<kRowMirror>(m, lane & 8);
+    for (int s = 16; s < W; s <<= 1) {
+        const Moments o{__shfl_xor(m.n, s, 64), __shfl_xor(m.mean, s, 64), __shfl_xor(m.m2, s, 64)};
+        m = (lane & s) ? merge_rcp(o, m) : merge_rcp(m, o);
+    }
+    return m;
+}
+
+// Block of 256 threads: each wave's ordered butterfly, then the four wave
+// totals in wave order through LDS; every thread returns the same value.
+// `sh` holds four entries.
+__device__ __forceinline__ Moments block_merge_rcp(Moments m, Moments* sh) {
+    m = segment_merge(m, 64);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+    __syncthreads();
+    Moments tot = sh[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) tot = merge_rcp(tot, sh[w]);
+    __syncthreads();  // `sh` may be reused right away
+    return tot;
+}
+
 // ------------------------------------------------------------------ group-cluster
 // K workgroups of 256 threads per (n, group) of an NCHW tensor (a group is
 // contiguous there), K = 1..8 chosen so that the grid covers the CUs: one CU
@@ -165,13 +220,9 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
         const uint32_t e = uint32_t(slice + 1) * a.vps;
         return e < a.Kv ? e : a.Kv;
     };
-    // S of one vector, rounded to T; the same arithmetic for the own slice
-    // and for a recomputed one.
-    auto form = [&](const V& x, const V& kv, uint32_t j, V& s) {
-        const int c = channel(j);
-        const float bb = has_bias ? to_f32(a.bias[c]) : 0.0f;
-        float kb = 0.0f;
-        if constexpr (BCAST) kb = to_f32(a.skip[int64_t(n) * a.C + c]);
+    // S of one vector, rounded to T, from its channel's bias and broadcast
+    // skip; the same arithmetic for the own slice and a recomputed one.
+    auto form = [&](const V& x, const V& kv, float bb, float kb, V& s) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             float kk = kb;
@@ -185,9 +236,12 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
         cnt += float(E);
     };
 
-    // ---- own slice: S into registers, S stored, slice moments
+    // ---- own slice: S into registers, slice moments.  The data loads go out
+    // first, then each vector's per-channel constants (all needed later).
     const uint32_t end = end_of(k);
     V sv[R], xs[R];
+    T bias_r[R], kb_r[R];
+    M gam_r[R], bet_r[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t j = vec_of(k, r);
@@ -196,37 +250,54 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
             if constexpr (!BCAST) sv[r] = load_vec_stream<T, E>(a.skip, base + j);
         }
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t j = vec_of(k, r);
+        if (j < end) {
+            const int c = channel(j);
+            if (has_bias) bias_r[r] = a.bias[c];
+            if constexpr (BCAST) kb_r[r] = a.skip[int64_t(n) * a.C + c];
+            gam_r[r] = a.gamma[c];
+            bet_r[r] = a.beta[c];
+        }
+    }
     ShiftedSums acc;
     float cnt = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t j = vec_of(k, r);
         if (j < end) {
-            form(xs[r], sv[r], j, sv[r]);
-            if (a.S) store_vec_stream<T, E>(a.S, base + j, sv[r]);
+            form(xs[r], sv[r], has_bias ? to_f32(bias_r[r]) : 0.0f, BCAST ? to_f32(kb_r[r]) : 0.0f, sv[r]);
             accumulate(acc, cnt, sv[r]);
         }
     }
-    const Moments mine = block_merge<kClusterThreads / 64>(acc.moments(cnt), sh);
+    const Moments mine = block_merge_rcp(acc.moments(cnt), sh);
 
     // ---- exchange with the other K-1 slices of the group
     Moments tot = mine;
     if (a.K > 1) {
         uint64_t* flags = a.flags + int64_t(ng) * a.K;
-        Partial* part = a.part + int64_t(ng) * a.K;
-        // Publication: the moments go out as agent-scope atomic stores, which
-        // are coherent across the XCDs' separate L2 caches; the vector-memory
-        // counter wait makes them complete before the tag is stored, and a
-        // reader that sees the tag (agent-scope atomic load) therefore reads
-        // this call's moments.  No data written with plain stores is
-        // exchanged, so no cache-wide release or acquire fence is needed.
+        uint64_t* part = reinterpret_cast<uint64_t*>(a.part) + int64_t(ng) * a.K;
+        // Publication: (mean, M2) as one 64-bit agent-scope store, which is
+        // coherent across the XCDs' separate L2 caches (the count is implied
+        // by the slice's size); the memory-counter wait completes it before
+        // the tag is stored, and a reader that sees the tag (agent-scope
+        // load) therefore reads this call's moments.  Nothing written with
+        // plain stores is exchanged, so no cache-wide fence is needed.
         if (t == 0) {
-            float* pp = reinterpret_cast<float*>(&part[k]);
-            __hip_atomic_store(pp + 0, mine.n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(pp + 1, mine.mean, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(pp + 2, mine.m2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t bits = uint64_t(__float_as_uint(mine.mean)) |
+                                  (uint64_t(__float_as_uint(mine.m2)) << 32);
+            __hip_atomic_store(&part[k], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __builtin_amdgcn_s_waitcnt(0);
             __hip_atomic_store(&flags[k], a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // S goes out after the publication's wait, which then waits for nothing else.
+        if (a.S) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t j = vec_of(k, r);
+                if (j < end) store_vec_stream<T, E>(a.S, base + j, sv[r]);
+            }
         }
         if (t < a.K && t != k) {
             const long long t0 = wall_clock64();
@@ -241,10 +312,9 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
             }
             late[t] = ok ? 0 : 1;
             if (ok) {
-                float* pp = reinterpret_cast<float*>(&part[t]);
-                slice_m[t] = Moments{__hip_atomic_load(pp + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                                     __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                                     __hip_atomic_load(pp + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+                const uint64_t bits = __hip_atomic_load(&part[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                slice_m[t] = Moments{float((end_of(t) - uint32_t(t) * a.vps) * E),
+                                     __uint_as_float(uint32_t(bits)), __uint_as_float(uint32_t(bits >> 32))};
             }
         }
         __syncthreads();
@@ -265,15 +335,23 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
                 for (int r = 0; r < R; ++r) {
                     const uint32_t j = vec_of(q, r);
                     if (j < qend) {
+                        const int c = channel(j);
                         V x = load_vec<T, E>(a.X, base + j), kv, sq;
                         if constexpr (!BCAST) kv = load_vec<T, E>(a.skip, base + j);
-                        form(x, kv, j, sq);
+                        form(x, kv, has_bias ? to_f32(a.bias[c]) : 0.0f,
+                             BCAST ? to_f32(a.skip[int64_t(n) * a.C + c]) : 0.0f, sq);
                         accumulate(qacc, qcnt, sq);
                     }
                 }
-                m = block_merge<kClusterThreads / 64>(qacc.moments(qcnt), sh);
+                m = block_merge_rcp(qacc.moments(qcnt), sh);
             }
-            tot = merge(tot, m);
+            tot = merge_rcp(tot, m);
+        }
+    } else if (a.S) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t j = vec_of(k, r);
+            if (j < end) store_vec_stream<T, E>(a.S, base + j, sv[r]);
         }
     }
 
@@ -283,9 +361,8 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
     for (int r = 0; r < R; ++r) {
         const uint32_t j = vec_of(k, r);
         if (j < end) {
-            const int c = channel(j);
-            const float scl = st.y * to_f32(a.gamma[c]);
-            const float sft = to_f32(a.beta[c]);
+            const float scl = st.y * to_f32(gam_r[r]);
+            const float sft = to_f32(bet_r[r]);
             V out;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
@@ -346,47 +423,6 @@ constexpr int kNhwcMaxCBg = 16;   // groups per channel block: four per wave
 constexpr int kNhwcMaxR = 16;     // pixels per thread
 constexpr int kWaves = kClusterThreads / 64;
 constexpr int kGroupsPerWave = kNhwcMaxCBg / kWaves;
-
-// Pairwise combination without branches, the weight taken from the
-// hardware reciprocal (about 1 ulp) rather than an IEEE division: thousands
-// of these sit on the cluster route's critical path.  Empty moments are
-// (0, 0, 0); merging with one is exact either way (weight 0, or weight 1
-// when the other side is empty).  Every workgroup runs the same operations,
-// so the results stay bitwise reproducible.
-__device__ __forceinline__ Moments merge_rcp(const Moments& a, const Moments& b) {
-    const float n = a.n + b.n;
-    const float wb = b.n == n ? 1.0f : b.n * __builtin_amdgcn_rcpf(n);
-    const float d = b.mean - a.mean;
-    Moments r;
-    r.n = n;
-    r.mean = fmaf_(d, wb, a.mean);
-    r.m2 = fmaf_(d * d, a.n * wb, a.m2 + b.m2);
-    return r;
-}
-
-template <int CTRL>
-__device__ __forceinline__ Moments dpp_merge_step(const Moments& m, bool upper) {
-    const Moments o{dpp_mov<CTRL>(m.n), dpp_mov<CTRL>(m.mean), dpp_mov<CTRL>(m.m2)};
-    return upper ? merge_rcp(o, m) : merge_rcp(m, o);
-}
-
-// Ordered butterfly over aligned segments of W lanes (W a power of two, at
-// most 64; uniform over the wave): every lane of a segment ends with bitwise
-// the same combination of the segment's values in lane order.  After the two
-// quad steps each quad is uniform, so mirroring inside 8 and 16 lanes pairs
-// the same quads and half-rows as an xor by 4 and by 8 would.
-__device__ __forceinline__ Moments segment_merge(Moments m, int W) {
-    const int lane = threadIdx.x & 63;
-    if (W >= 2) m = dpp_merge_step<kQuadXor1>(m, lane & 1);
-    if (W >= 4) m = dpp_merge_step<kQuadXor2>(m, lane & 2);
-    if (W >= 8) m = dpp_merge_step<kRowHalfMirror>(m, lane & 4);
-    if (W >= 16) m = dpp_merge_step<kRowMirror>(m, lane & 8);
-    for (int s = 16; s < W; s <<= 1) {
-        const Moments o{__shfl_xor(m.n, s, 64), __shfl_xor(m.mean, s, 64), __shfl_xor(m.m2, s, 64)};
-        m = (lane & s) ? merge_rcp(o, m) : merge_rcp(m, o);
-    }
-    return m;
-}
 
 template <typename T, typename M, int E, int R, bool BCAST>
 __global__ void __launch_bounds__(kClusterThreads)
