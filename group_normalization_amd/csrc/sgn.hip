@@ -399,7 +399,10 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
 // Block ids are laid out so that the NCB channel blocks of one (image,
 // slice) share the id's residue mod 8: consecutive ids are dispatched
 // round-robin over the 8 XCDs, so those workgroups, which touch the same
-// pixel rows and share their boundary cache lines, run under one L2.
+// pixel rows and share their boundary cache lines, run under one L2.  The
+// data accesses are ordinary (cached) ones so that this L2 merges the
+// blocks' pieces of a line: with nontemporal stores the partial lines
+// reached memory separately (1.3-1.5x the written bytes, measured).
 template <typename T, typename M>
 struct NhwcClusterArgs {
     const T *X, *skip, *bias;
@@ -565,8 +568,8 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
             if (r < nv_own) {
-                xs[r] = load_vec_stream<T, E>(a.X, vidx(q, r));
-                if constexpr (!BCAST) sv[r] = load_vec_stream<T, E>(a.skip, vidx(q, r));
+                xs[r] = load_vec<T, E>(a.X, vidx(q, r));
+                if constexpr (!BCAST) sv[r] = load_vec<T, E>(a.skip, vidx(q, r));
             }
         load_constants();
         SlotSums acc;
@@ -596,7 +599,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
     if (a.S) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            if (r < nv_own) store_vec_stream<T, E>(a.S, vidx(q, r), sv[r]);
+            if (r < nv_own) store_vec<T, E>(a.S, vidx(q, r), sv[r]);
     }
     __syncthreads();  // own_m visible to every wave
 
@@ -730,7 +733,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
                     if (a.silu) y = silu_f32(y);
                     out.v[e] = from_f32<T>(y);
                 }
-                store_vec_stream<T, E>(a.Y, vidx(q, r), out);
+                store_vec<T, E>(a.Y, vidx(q, r), out);
             }
     }
 }
@@ -1142,12 +1145,12 @@ int cluster_k(int64_t Kv, int64_t NG, int max_r) {
 // Channel-block cluster plan.  Channel blocks: the fewest (so the most
 // channels per workgroup, for coalescing) with at most one group per wave,
 // which keeps each wave's combine to one butterfly; among those, the first
-// whose grid reaches kNhwcTargetBlocks workgroups (one per CU: the route is
-// latency-bound, and more, smaller workgroups lengthen the exchange more
-// than they shorten the streaming).  Slices are as few as that target
-// allows, no more than leave each thread about one vector, and as many as
-// the register budget (kNhwcMaxR pixels per thread) needs.
-constexpr int64_t kNhwcTargetBlocks = 256;
+// whose grid reaches kNhwcTargetBlocks workgroups (two per CU: fewer leave
+// the loads short of bandwidth, more lengthen the exchange more than they
+// shorten the streaming).  Slices are as few as that target allows, no more
+// than leave each thread about one vector, and as many as the register
+// budget (kNhwcMaxR pixels per thread) needs.
+constexpr int64_t kNhwcTargetBlocks = 512;
 
 struct NhwcPlan {
     int CBv, NCB, CBg, P, sw_log, K, R;

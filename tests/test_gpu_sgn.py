@@ -117,7 +117,7 @@ def test_group_block_limits(case):
 # groups at least one 16-byte vector wide.
 NHWC_LIMIT_CASES = [
     # (N, C, H, W, T, groups, broadcast skip, expected auto route)
-    (2, 320, 64, 64, F16, 32, False, "sgn.cluster.nhwc.vec16"),   # 51 pixel lanes (odd), 16 slices
+    (2, 320, 64, 64, F16, 32, False, "sgn.cluster.nhwc.vec16"),   # 51 pixel lanes (odd), 32 slices
     (1, 320, 204, 256, F16, 32, False, "sgn.cluster.nhwc.vec16"), # 52224 pixels: 64 slices, 16 pixels/thread
     (1, 320, 205, 256, F16, 32, True, "sgn.split.nhwc.vec16"),    # 52480 pixels: too many
     (8, 40, 32, 32, F16, 5, False, "sgn.cluster.nhwc.vec16"),     # one vector per block
