@@ -280,3 +280,36 @@ def test_empty():
     g = torch.ones(8, dtype=torch.float32, device="cuda")
     out = gn.skip_group_norm(X, g, g, X, groups=2, activation=0)
     assert out.Y.shape == X.shape
+
+
+@pytest.mark.parametrize("route", ["auto", "split", "scalar", "block"])
+@pytest.mark.parametrize("cl", [0, 1])
+def test_non_finite_values_stay_in_their_group(cl, route):
+    """A residual sum that overflows binary16 (S = +inf) or a NaN input makes
+    its own group's Y NaN, as in the oracle, and leaves every other group
+    untouched; S keeps the infinity bit for bit."""
+    N, C, H, W, groups = 2, 64, 6, 6, 8
+    w, x = make((N, C, H, W, F16, F32, cl, False, True, groups, 1), seed=11)
+    X, skip = x["X"].copy(), x["skip"].copy()
+    def put(a, n, c, h, wv, v):
+        if cl:
+            a[n, h, wv, c] = v
+        else:
+            a[n, c, h, wv] = v
+    put(X, 0, 17, 2, 3, 65504.0)    # group 2 of image 0: 65504 + 65504 rounds to +inf
+    put(skip, 0, 17, 2, 3, 65504.0)
+    put(X, 1, 45, 5, 0, np.nan)     # group 5 of image 1
+    x = dict(x, X=X, skip=skip)
+    ref, out, used = run(x, w, route)
+    check(ref, out, want_sum=False)
+    # S: the same NaN positions (NaN payloads are not compared), the rest bit for bit.
+    s_got, s_ref = to_host(out.S), ref[1]
+    assert np.array_equal(np.isnan(s_got), np.isnan(s_ref))
+    fin = ~np.isnan(s_ref)
+    assert_bitwise(s_got[fin], s_ref[fin], "S")
+    assert np.isinf(s_ref).sum() == 1
+    y = to_host(out.Y).astype(np.float32)
+    y = y if not cl else y.transpose(0, 3, 1, 2)
+    nan_groups = {(n, g) for n in range(N) for g in range(groups)
+                  if np.isnan(y[n, g * 8:(g + 1) * 8]).all()}
+    assert nan_groups == {(0, 2), (1, 5)}, nan_groups
