@@ -258,6 +258,7 @@ def main():
         per_op[o.name] = {"bytes": o.bytes, "avg_us": round(avg * 1e3, 3),
                           "median_us": round(float(np.median(ms)) * 1e3, 3),
                           "min_us": round(float(np.min(ms)) * 1e3, 3),
+                          "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 3),
                           "gbps": round(o.bytes / (avg * 1e-3) / 1e9, 1),
                           "frac_of_peak": round(o.bytes / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)}
 
