@@ -152,7 +152,7 @@ def cpu_baseline(budget_s=14.0):
     import oracle
     from group_normalization_amd import workloads
 
-    total_bytes, total_s, parts = 0, 0.0, []
+    total_bytes, total_s, parts, per_op = 0, 0.0, [], {}
     order = sorted(STEP_WORKLOADS, key=lambda n: workloads.WORKLOADS[n].op != "skip_group_norm")
     n_large = sum(workloads.WORKLOADS[n].op != "skip_group_norm" for n in order)
     for name in order:
@@ -191,9 +191,26 @@ def cpu_baseline(budget_s=14.0):
         total_s += t_op
         unit = "rows" if w.op != "skip_group_norm" else "images"
         parts.append(f"{name}: {done}/{unit_rows} {unit}")
+        per_op[name] = {"seconds": round(t_op, 3), unit: done, "of": unit_rows,
+                        "gbps": round(per_row * done / t_op / 1e9, 4)}
         log(f"cpu oracle {name}: {done} {unit} in {t_op:.2f} s")
     return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "sample": "; ".join(parts) + f" ({total_s:.1f} s single-thread)"}
+            "kind": "oracle", "sample": "; ".join(parts) + f" ({total_s:.1f} s single-thread)",
+            "per_op": per_op, "host": host_cpu()}
+
+
+def host_cpu():
+    """Logical CPU count and model name of the machine the oracle ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "model": model}
 
 
 def main():
@@ -278,6 +295,9 @@ def main():
     del src, dst
     for ev in [e0, e1] + [e for per_step in evs for pair in per_step for e in pair]:
         hev.destroy(ev)
+
+    for v in per_op.values():
+        v["frac_of_copy"] = round(v["gbps"] / copy_gbps, 4)
 
     dom = per_op[DOMINANT]
     achieved = dom["bytes"] / (dom["avg_us"] * 1e-6) / 1e9
