@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libskipnorm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["skipnorm_api.cpp", "ssln.hip", "gated.hip", "sgn.hip", "copy.hip"]
+SOURCES = ["skipnorm_api.cpp", "ssln.hip", "gated.hip", "sgn.hip", "sgn_nhwc.hip", "copy.hip"]
 
 # -ffp-contract=off: no implicit FMA, so the float32 arithmetic is exactly the
 # operations written (explicit FMAs are spelled __builtin_fmaf).

@@ -5,19 +5,39 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 namespace sn {
 
 typedef _Float16 half_t;
 
 // ---------------------------------------------------------------------------
-// Element vectors.  Vec<T, E> holds E elements of T; E * sizeof(T) == 16 is
-// the 16-byte vector that becomes one global_load/store_dwordx4 per lane,
+// Element vectors.  Vec<T, E> holds E elements of T and is aligned to its
+// size: E * sizeof(T) == 16 is the 16-byte vector that becomes one
+// global_load/store_dwordx4 per lane, 8 and 4 bytes the narrower vectors of
+// rows whose length (or base) is not a whole number of 16-byte vectors, and
 // E == 1 the scalar route.
 template <typename T, int E> struct Vec { T v[E]; };
 template <> struct alignas(16) Vec<float, 4> { float v[4]; };
+template <> struct alignas(8) Vec<float, 2> { float v[2]; };
 template <> struct alignas(16) Vec<half_t, 8> { half_t v[8]; };
+template <> struct alignas(8) Vec<half_t, 4> { half_t v[4]; };
+template <> struct alignas(4) Vec<half_t, 2> { half_t v[2]; };
 
 template <typename T> struct VecWidth { static constexpr int value = 16 / sizeof(T); };
+
+// Widest access (16, 8 or 4 bytes, else one element) that divides a row of
+// `row_elems` elements and every base address in `ptrs` (null entries are
+// ignored): the vector width, in elements, a route can use for such rows.
+template <typename T>
+inline int widest_vector(int64_t row_elems, std::initializer_list<const void*> ptrs) {
+    for (int bytes = 16; bytes > int(sizeof(T)); bytes /= 2) {
+        bool ok = (row_elems * int64_t(sizeof(T))) % bytes == 0;
+        for (const void* p : ptrs) ok = ok && (reinterpret_cast<uintptr_t>(p) % bytes == 0);
+        if (ok) return bytes / int(sizeof(T));
+    }
+    return 1;
+}
 
 template <typename T, int E>
 __device__ __forceinline__ Vec<T, E> load_vec(const T* __restrict__ p, int64_t i) {
@@ -32,8 +52,10 @@ __device__ __forceinline__ void store_vec(T* __restrict__ p, int64_t i, const Ve
 // access carries the nontemporal hint, so the caches do not keep lines that
 // will not be reused.  Values are moved as raw bits of the same size.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 template <int BYTES> struct RawBits;
 template <> struct RawBits<16> { using type = u32x4; };
+template <> struct RawBits<8> { using type = u32x2; };
 template <> struct RawBits<4> { using type = uint32_t; };
 template <> struct RawBits<2> { using type = uint16_t; };
 

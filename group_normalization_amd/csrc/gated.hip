@@ -13,7 +13,9 @@
 //            16 lanes x one 16-byte vector: 4 rows per wave.  Rows wider
 //            than 64 vectors use all 64 lanes with up to 16 vectors each.
 //            Each thread loads RPT rows before computing, to keep enough
-//            bytes in flight.  Vector (16-byte) or scalar element width.
+//            bytes in flight.  Element width: the widest of 16-, 8- and
+//            4-byte vectors that divides the row and every base, else
+//            scalars.
 //   block    one 256-thread workgroup per row for wider rows; X is read twice.
 // scale is loaded once per thread and kept in registers as float32.  X, gate
 // and Y are touched once and move with nontemporal loads and stores.
@@ -34,12 +36,14 @@ gated_segment_kernel(const T* __restrict__ X, const T* __restrict__ scale,
     const int l = threadIdx.x % L;
     const int64_t tile = int64_t(blockIdx.x) * SEGS * RPT;
 
+    // No load sits behind a lane-dependent branch (the compiler would wait
+    // for each in turn): padding lanes and rows past the end re-read the
+    // last vector / row and discard the result.
     float sc[VPL][E];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         const int idx = v * L + l;
-        V s = {};
-        if (idx < nvec) s = load_vec<T, E>(scale, idx);
+        const V s = load_vec<T, E>(scale, idx < nvec ? idx : nvec - 1);
 #pragma unroll
         for (int e = 0; e < E; ++e) sc[v][e] = to_f32(s.v[e]);
     }
@@ -48,13 +52,13 @@ gated_segment_kernel(const T* __restrict__ X, const T* __restrict__ scale,
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
         const int64_t row = tile + int64_t(k) * SEGS + seg;
+        const int64_t rc = row < rows ? row : rows - 1;
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
             const int idx = v * L + l;
-            if (row < rows && idx < nvec) {
-                xs[k][v] = load_vec_stream<T, E>(X, row * nvec + idx);
-                gs[k][v] = load_vec_stream<T, E>(gate, row * nvec + idx);
-            }
+            const int ic = idx < nvec ? idx : nvec - 1;
+            xs[k][v] = load_vec_stream<T, E>(X, rc * nvec + ic);
+            gs[k][v] = load_vec_stream<T, E>(gate, rc * nvec + ic);
         }
     }
 
@@ -153,19 +157,27 @@ constexpr int64_t kMaxSegmentVectors = 1024;
 
 template <typename T>
 hipError_t launch_gated_t(const GatedArgs& a, Route want, hipStream_t stream, const char** route) {
-    constexpr int EV = VecWidth<T>::value;
-    const bool vec_ok = a.span % EV == 0 && a.span / EV <= kMaxSegmentVectors && aligned16(a.X) &&
-                        aligned16(a.scale) && aligned16(a.gate) && aligned16(a.Y);
-    Route r = want;
-    if (r == Route::Auto || r == Route::Vector) r = vec_ok ? Route::Vector : Route::Scalar;
-    if (r == Route::Scalar && a.span > kMaxSegmentVectors) r = Route::Block;
-    if (r == Route::Vector) {
-        *route = "gated.segment.vec16";
-        return launch_segment_for<T, EV>(a, int(a.span / EV), stream);
-    }
-    if (r == Route::Scalar) {
+    // Widest access that divides the row and every tensor's base.
+    int E = widest_vector<T>(a.span, {a.X, a.scale, a.gate, a.Y});
+    if (want == Route::Scalar) E = 1;
+    const int64_t nvec = a.span / E;
+    if (want != Route::Block && nvec <= kMaxSegmentVectors) {
+        if (E * sizeof(T) == 16) {
+            *route = "gated.segment.vec16";
+            return launch_segment_for<T, VecWidth<T>::value>(a, int(nvec), stream);
+        }
+        if (E * sizeof(T) == 8) {
+            *route = "gated.segment.vec8";
+            return launch_segment_for<T, 8 / sizeof(T)>(a, int(nvec), stream);
+        }
+        if constexpr (sizeof(T) == 2) {
+            if (E == 2) {
+                *route = "gated.segment.vec4";
+                return launch_segment_for<T, 2>(a, int(nvec), stream);
+            }
+        }
         *route = "gated.segment.scalar";
-        return launch_segment_for<T, 1>(a, int(a.span), stream);
+        return launch_segment_for<T, 1>(a, int(nvec), stream);
     }
     *route = "gated.block";
     const int64_t blocks = a.rows < 65536 * 16 ? a.rows : 65536 * 16;

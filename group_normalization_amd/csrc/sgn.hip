@@ -17,11 +17,12 @@
 //   with a bounded wait (see sgn_cluster_kernel) and write S and Y.  One
 //   launch, exactly the operator's own traffic.
 //
-// channel-block cluster (NHWC, whole 16-byte vectors per pixel, groups at
-//   least one vector wide, images of up to 64 x 16 x (256 / vectors per
-//   block) pixels): workgroups own (image, pixel slice, channel block)
-//   tiles, hold S in VGPRs and exchange per-group moments the same way (see
-//   sgn_nhwc_cluster_kernel).  One launch, exactly the operator's traffic.
+// channel-block cluster (NHWC, in sgn_nhwc.hip; pixels a whole number of
+//   16-, 8- or 4-byte vectors no wider than a group, images of up to
+//   64 x 16 x (256 / vectors per block) pixels): workgroups own (image,
+//   pixel slice, channel block) tiles, hold S in VGPRs and exchange
+//   per-group moments the same way.  One launch, exactly the operator's
+//   traffic.
 //
 // split (everything else), three launches on one stream: the
 //   pages' "partial group statistics / combine / normalize" structure,
@@ -33,7 +34,8 @@
 //   3. normalize: re-reads S (or re-forms it from X, skip and bias, bit for
 //      bit the same) and writes Y.
 //   Tilings of passes 1 and 3:
-//   nhwc   (NHWC, C a whole number of 16-byte vectors, at most 256 of them):
+//   nhwc   (NHWC, C a whole number of 16-, 8- or 4-byte vectors, at most
+//          256 of them):
 //          a block covers a run of pixels of one image and all channels.
 //          Thread t owns channel vector t % Cv at pixels t / Cv + k * P,
 //          P = 256 / Cv, so its channels (and their bias, gamma, beta and
@@ -49,121 +51,12 @@
 // Moments: each thread uses the shifted-data sums (shift = its first value)
 // and every combination uses the pairwise update (Chan et al.) in a fixed
 // order, so results are deterministic and a constant group has variance 0.
-#include "device_common.h"
-#include "skipnorm_internal.h"
+#include <type_traits>
+
+#include "sgn_common.h"
 
 namespace sn {
 namespace {
-
-constexpr int kUnroll = 4;
-
-struct alignas(16) Partial {
-    float n, mean, m2, pad;
-};
-
-__device__ __forceinline__ Moments as_moments(const Partial& p) { return Moments{p.n, p.mean, p.m2}; }
-
-// Combines the moments of the 64 lanes of a wave.  Partners always combine
-// as merge(lower lane, upper lane), so both compute bitwise the same value
-// and every lane ends with the same total.
-__device__ __forceinline__ Moments wave_merge(Moments m) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-        Moments o;
-        o.n = __shfl_xor(m.n, s, 64);
-        o.mean = __shfl_xor(m.mean, s, 64);
-        o.m2 = __shfl_xor(m.m2, s, 64);
-        m = (lane & s) ? merge(o, m) : merge(m, o);
-    }
-    return m;
-}
-
-// Block of W waves: wave totals through LDS, combined in wave order by every
-// thread (all threads return the same value).  `sh` holds W entries.
-template <int W>
-__device__ __forceinline__ Moments block_merge(Moments m, Moments* sh) {
-    m = wave_merge(m);
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
-    __syncthreads();
-    Moments tot = sh[0];
-#pragma unroll
-    for (int w = 1; w < W; ++w) tot = merge(tot, sh[w]);
-    __syncthreads();  // `sh` may be reused right away
-    return tot;
-}
-
-__device__ __forceinline__ float2 finalize(const Moments& m, float eps) {
-    const float var = m.n > 0.0f ? fmaxf(m.m2 / m.n, 0.0f) : 0.0f;
-    return make_float2(m.mean, inv_sqrt(var + eps));
-}
-
-template <typename T, int E>
-__device__ __forceinline__ void load_param_vec(const T* p, int64_t vi, float (&out)[E]) {
-    const Vec<T, E> v = load_vec<T, E>(p, vi);
-#pragma unroll
-    for (int e = 0; e < E; ++e) out[e] = to_f32(v.v[e]);
-}
-
-template <typename T, int E>
-__device__ __forceinline__ Vec<T, E> load_in(const T* p, int64_t i, bool stream) {
-    return stream ? load_vec_stream<T, E>(p, i) : load_vec<T, E>(p, i);
-}
-
-// Pairwise combination without branches, the weight taken from the
-// hardware reciprocal (about 1 ulp) rather than an IEEE division: thousands
-// of these sit on the cluster route's critical path.  Empty moments are
-// (0, 0, 0); merging with one is exact either way (weight 0, or weight 1
-// when the other side is empty).  Every workgroup runs the same operations,
-// so the results stay bitwise reproducible.
-__device__ __forceinline__ Moments merge_rcp(const Moments& a, const Moments& b) {
-    const float n = a.n + b.n;
-    const float wb = b.n == n ? 1.0f : b.n * __builtin_amdgcn_rcpf(n);
-    const float d = b.mean - a.mean;
-    Moments r;
-    r.n = n;
-    r.mean = fmaf_(d, wb, a.mean);
-    r.m2 = fmaf_(d * d, a.n * wb, a.m2 + b.m2);
-    return r;
-}
-
-template <int CTRL>
-__device__ __forceinline__ Moments dpp_merge_step(const Moments& m, bool upper) {
-    const Moments o{dpp_mov<CTRL>(m.n), dpp_mov<CTRL>(m.mean), dpp_mov<CTRL>(m.m2)};
-    return upper ? merge_rcp(o, m) : merge_rcp(m, o);
-}
-
-// Ordered butterfly over aligned segments of W lanes (W a power of two, at
-// most 64; uniform over the wave): every lane of a segment ends with bitwise
-// the same combination of the segment's values in lane order.  After the two
-// quad steps each quad is uniform, so mirroring inside 8 and 16 lanes pairs
-// the same quads and half-rows as an xor by 4 and by 8 would.
-__device__ __forceinline__ Moments segment_merge(Moments m, int W) {
-    const int lane = threadIdx.x & 63;
-    if (W >= 2) m = dpp_merge_step<kQuadXor1>(m, lane & 1);
-    if (W >= 4) m = dpp_merge_step<kQuadXor2>(m, lane & 2);
-    if (W >= 8) m = dpp_merge_step<kRowHalfMirror>(m, lane & 4);
-    if (W >= 16) m = dpp_merge_step<kRowMirror>(m, lane & 8);
-    for (int s = 16; s < W; s <<= 1) {
-        const Moments o{__shfl_xor(m.n, s, 64), __shfl_xor(m.mean, s, 64), __shfl_xor(m.m2, s, 64)};
-        m = (lane & s) ? merge_rcp(o, m) : merge_rcp(m, o);
-    }
-    return m;
-}
-
-// Block of 256 threads: each wave's ordered butterfly, then the four wave
-// totals in wave order through LDS; every thread returns the same value.
-// `sh` holds four entries.
-__device__ __forceinline__ Moments block_merge_rcp(Moments m, Moments* sh) {
-    m = segment_merge(m, 64);
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
-    __syncthreads();
-    Moments tot = sh[0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) tot = merge_rcp(tot, sh[w]);
-    __syncthreads();  // `sh` may be reused right away
-    return tot;
-}
 
 // ------------------------------------------------------------------ group-cluster
 // K workgroups of 256 threads per (n, group) of an NCHW tensor (a group is
@@ -195,8 +88,6 @@ struct ClusterArgs {
     float eps;
 };
 
-constexpr int kClusterThreads = 256;
-constexpr int kClusterMaxK = 8;
 
 template <typename T, typename M, int E, int R, bool BCAST>
 __global__ void __launch_bounds__(kClusterThreads)
@@ -237,29 +128,27 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
     };
 
     // ---- own slice: S into registers, slice moments.  The data loads go out
-    // first, then each vector's per-channel constants (all needed later).
+    // first, then each vector's per-channel constants (all needed later).  No
+    // load sits behind a lane-dependent branch (the compiler would wait for
+    // each in turn): vectors past the slice's end re-read its first vector.
     const uint32_t end = end_of(k);
+    auto clamp = [&](uint32_t j) { return j < end ? j : uint32_t(k) * a.vps; };
     V sv[R], xs[R];
     T bias_r[R], kb_r[R];
     M gam_r[R], bet_r[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const uint32_t j = vec_of(k, r);
-        if (j < end) {
-            xs[r] = load_vec_stream<T, E>(a.X, base + j);
-            if constexpr (!BCAST) sv[r] = load_vec_stream<T, E>(a.skip, base + j);
-        }
+        const uint32_t j = clamp(vec_of(k, r));
+        xs[r] = load_vec_stream<T, E>(a.X, base + j);
+        if constexpr (!BCAST) sv[r] = load_vec_stream<T, E>(a.skip, base + j);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const uint32_t j = vec_of(k, r);
-        if (j < end) {
-            const int c = channel(j);
-            if (has_bias) bias_r[r] = a.bias[c];
-            if constexpr (BCAST) kb_r[r] = a.skip[int64_t(n) * a.C + c];
-            gam_r[r] = a.gamma[c];
-            bet_r[r] = a.beta[c];
-        }
+        const int c = channel(clamp(vec_of(k, r)));
+        if (has_bias) bias_r[r] = a.bias[c];
+        if constexpr (BCAST) kb_r[r] = a.skip[int64_t(n) * a.C + c];
+        gam_r[r] = a.gamma[c];
+        bet_r[r] = a.beta[c];
     }
     ShiftedSums acc;
     float cnt = 0.0f;
@@ -375,369 +264,6 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
     }
 }
 
-// ------------------------------------------------------------------ channel-block cluster (NHWC)
-// In NHWC a group's channels are a short run inside every pixel, so a group
-// is not contiguous.  The channels are cut into NCB blocks, each a whole
-// number of groups and of 16-byte vectors (a multiple of lcm(cpg, E)
-// channels), and an image's pixels into K slices; one workgroup of 256
-// threads owns one (image, slice, channel block).  Thread t owns channel
-// vector v = t % CBv of the block at pixels t / CBv + r * P (P = 256 / CBv
-// pixel lanes), so its channels never change, and holds S for those pixels
-// in VGPRs.
-//
-// A slice's per-group moments: each thread keeps shifted sums for the (at
-// most two, as cpg >= E) groups its vector touches; the pixel lanes of each
-// (vector, group) column are merged in LDS, chunk by chunk and then by an
-// ordered DPP butterfly; each group merges its columns in channel order.
-// The K slices of an (image, block) exchange these moments as the
-// group-cluster route does (per-call tags, bounded waits, a late slice
-// recomputed with the same code) and each wave combines its groups over the
-// K slices with an ordered butterfly in slice order, so every workgroup of
-// the cluster holds bitwise the same statistics.  One launch: X and skip are
-// read once, S and Y written once.
-//
-// Block ids are laid out so that the NCB channel blocks of one (image,
-// slice) share the id's residue mod 8: consecutive ids are dispatched
-// round-robin over the 8 XCDs, so those workgroups, which touch the same
-// pixel rows and share their boundary cache lines, run under one L2.  The
-// data accesses are ordinary (cached) ones so that this L2 merges the
-// blocks' pieces of a line: with nontemporal stores the partial lines
-// reached memory separately (1.3-1.5x the written bytes, measured).
-template <typename T, typename M>
-struct NhwcClusterArgs {
-    const T *X, *skip, *bias;
-    T *S, *Y;
-    const M *gamma, *beta;
-    Partial* part;     // N * NCB * K * CBg slice moments (mean, M2)
-    uint64_t* flags;   // N * NCB * K * CBg publication tags
-    uint64_t tag;
-    long long timeout_ticks;
-    int64_t HW, pps;   // pixels per image and per slice
-    int Cv, cpg;       // vectors per pixel, channels per group
-    int CBv, NCB, CBg; // vectors per channel block, blocks per pixel, groups per block
-    int P, sw_log;     // pixel lanes per workgroup (256 / CBv); log2 of the chunks per column
-    int K, units;      // slices per image, N * K
-    bool skip_bcast, silu;
-    float eps;
-};
-
-constexpr int kNhwcMaxK = 64;     // slices per (image, block): one per lane in the combine
-constexpr int kNhwcMaxCBg = 16;   // groups per channel block: four per wave
-constexpr int kNhwcMaxR = 16;     // pixels per thread
-constexpr int kWaves = kClusterThreads / 64;
-constexpr int kGroupsPerWave = kNhwcMaxCBg / kWaves;
-
-template <typename T, typename M, int E, int R, bool BCAST>
-__global__ void __launch_bounds__(kClusterThreads)
-sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
-    using V = Vec<T, E>;
-    __shared__ Moments lane_m[2 * kClusterThreads];  // [pixel lane][column = 2 * vector + slot]
-    __shared__ Moments col_m[2 * kClusterThreads];   // column totals
-    __shared__ Moments own_m[kNhwcMaxCBg];           // this slice's group moments
-    __shared__ Moments slice_m[kNhwcMaxK][kNhwcMaxCBg];  // recomputed slices
-    __shared__ float2 stat[kNhwcMaxCBg];
-    __shared__ int late[kNhwcMaxK];
-    __shared__ int any_late;
-
-    const int bid = int(blockIdx.x);
-    const int xcd = bid & 7, rest = bid >> 3;
-    const int cb = rest % a.NCB;
-    const int u = (rest / a.NCB) * 8 + xcd;
-    if (u >= a.units) return;  // grid padding; not part of any cluster
-    const int n = u / a.K, q = u % a.K;
-    const int t = threadIdx.x;
-    const int wave = t >> 6, lane = t & 63;
-    const bool active = t < a.P * a.CBv;
-    const int v = active ? t % a.CBv : 0;
-    const int pl = active ? t / a.CBv : 0;
-    const int cvec = cb * a.CBv + v;  // channel vector within the pixel
-    const int glo = (v * E) / a.cpg;  // block-local group of the vector's first channel
-    const int split = (glo + 1) * a.cpg - v * E;  // channels [0, split) are in glo, the rest in glo + 1
-    const int ncol = 2 * a.CBv;
-    const int SW = 1 << a.sw_log;
-    const int64_t img = int64_t(n) * a.HW;
-    const bool has_bias = a.bias != nullptr;
-    if (t < kNhwcMaxK) late[t] = 0;
-    if (t == 0) any_late = 0;
-
-    // Pixels of slice s this thread holds (they are consecutive in r).
-    auto slice_len = [&](int s) {
-        const int64_t rem = a.HW - int64_t(s) * a.pps;
-        return rem < a.pps ? rem : a.pps;
-    };
-    auto nvalid = [&](int s) {
-        const int64_t len = slice_len(s);
-        if (!active || len <= pl) return 0;
-        const int64_t nv = (len - pl + a.P - 1) / a.P;
-        return nv < R ? int(nv) : R;
-    };
-    auto vidx = [&](int s, int r) {
-        return (img + int64_t(s) * a.pps + pl + int64_t(r) * a.P) * a.Cv + cvec;
-    };
-    // Per-channel constants: bias and broadcast skip (as T), gamma, beta.
-    V bvec, kvec;
-    M gam[E], bet[E];
-    auto load_constants = [&]() {
-        if (has_bias) bvec = load_vec<T, E>(a.bias, cvec);
-        if constexpr (BCAST) kvec = load_vec<T, E>(a.skip, int64_t(n) * a.Cv + cvec);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            gam[e] = a.gamma[cvec * E + e];
-            bet[e] = a.beta[cvec * E + e];
-        }
-    };
-    auto form = [&](const V& x, const V& kv, V& s) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float kk = BCAST ? to_f32(kvec.v[e]) : to_f32(kv.v[e]);
-            const float bb = has_bias ? to_f32(bvec.v[e]) : 0.0f;
-            residual_sum<T>(to_f32(x.v[e]), kk, has_bias, bb, s.v[e]);
-        }
-    };
-    // Shifted sums of the thread's two groups over its pixels of a slice, in
-    // pixel then channel order; the shifts are the first pixel's first and
-    // last channels (the last channel is in the upper group when it exists).
-    struct SlotSums {
-        ShiftedSums lo, hi;
-    };
-    auto accumulate = [&](SlotSums& acc, const V& s, int r) {
-        if (r == 0) {
-            acc.lo.shift = to_f32(s.v[0]);
-            acc.hi.shift = to_f32(s.v[E - 1]);
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float x = to_f32(s.v[e]);
-            const bool in_lo = e < split;
-            const float d = x - (in_lo ? acc.lo.shift : acc.hi.shift);
-            const float dl = in_lo ? d : 0.0f, dh = in_lo ? 0.0f : d;
-            acc.lo.s1 += dl;
-            acc.lo.s2 = fmaf_(dl, dl, acc.lo.s2);
-            acc.hi.s1 += dh;
-            acc.hi.s2 = fmaf_(dh, dh, acc.hi.s2);
-        }
-    };
-    // Group moments of a slice from every thread's sums over its nv pixels,
-    // into dst[0 .. CBg).  The same code and thread mapping run wherever a
-    // slice is reduced.  Ends with dst written but not yet visible.
-    auto reduce_slice = [&](const SlotSums& acc, int nv, Moments* dst) {
-        if (active) {
-            const int nlo = split < E ? split : E;
-            lane_m[pl * ncol + 2 * v] = acc.lo.moments(float(nv * nlo));
-            lane_m[pl * ncol + 2 * v + 1] = acc.hi.moments(float(nv * (E - nlo)));
-        }
-        __syncthreads();
-        // Column c, chunk j: pixel lanes j, j + SW, ... in order; then the SW
-        // chunks (adjacent lanes of one DPP row) in an ordered butterfly.
-        for (int i0 = 0; i0 < ncol * SW; i0 += kClusterThreads) {
-            const int i = i0 + t;
-            const bool on = i < ncol * SW;
-            const int c = i >> a.sw_log, j = i & (SW - 1);
-            Moments m{0.0f, 0.0f, 0.0f};
-            if (on) {
-                // Up to four lanes' loads in flight per step.
-                for (int l0 = j; l0 < a.P; l0 += 4 * SW) {
-                    Moments x[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int l = l0 + k * SW;
-                        x[k] = l < a.P ? lane_m[l * ncol + c] : Moments{0.0f, 0.0f, 0.0f};
-                    }
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) m = merge_rcp(m, x[k]);
-                }
-            }
-            m = segment_merge(m, SW);
-            if (on && j == 0) col_m[c] = m;
-        }
-        __syncthreads();
-        if (t < a.CBg) {  // group t over its columns, in channel order
-            const int vf = (t * a.cpg) / E, vl = ((t + 1) * a.cpg - 1) / E;
-            Moments m{0.0f, 0.0f, 0.0f};
-            for (int w = vf; w <= vl; ++w) m = merge_rcp(m, col_m[2 * w + ((w * E) / a.cpg == t ? 0 : 1)]);
-            dst[t] = m;
-        }
-    };
-
-    // ---- own slice: S into registers, slice moments.  The data loads go out
-    // before the per-channel constants'.
-    const int nv_own = nvalid(q);
-    V sv[R];
-    {
-        V xs[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (r < nv_own) {
-                xs[r] = load_vec<T, E>(a.X, vidx(q, r));
-                if constexpr (!BCAST) sv[r] = load_vec<T, E>(a.skip, vidx(q, r));
-            }
-        load_constants();
-        SlotSums acc;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (r < nv_own) {
-                form(xs[r], sv[r], sv[r]);
-                accumulate(acc, sv[r], r);
-            }
-        reduce_slice(acc, nv_own, own_m);
-    }
-
-    // ---- publication: per group, (mean, M2) as one 64-bit agent-scope store
-    // (coherent across the XCDs' L2 caches; the count is implied by the
-    // slice's size), completed before that group's tag goes out.
-    const int64_t first = (int64_t(n) * a.NCB + cb) * a.K * a.CBg;  // slice 0 of this (image, block)
-    uint64_t* part = reinterpret_cast<uint64_t*>(a.part) + first;
-    uint64_t* flags = a.flags + first;
-    if (a.K > 1 && t < a.CBg) {
-        const Moments m = own_m[t];
-        const uint64_t bits = uint64_t(__float_as_uint(m.mean)) | (uint64_t(__float_as_uint(m.m2)) << 32);
-        __hip_atomic_store(&part[q * a.CBg + t], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        __hip_atomic_store(&flags[q * a.CBg + t], a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // S goes out after the publication's wait, which then waits for nothing else.
-    if (a.S) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (r < nv_own) store_vec<T, E>(a.S, vidx(q, r), sv[r]);
-    }
-    __syncthreads();  // own_m visible to every wave
-
-    // ---- statistics: wave w combines groups w, w + 4, ... over the K slices,
-    // lane s holding slice s (butterfly over the smallest power of two >= K
-    // lanes; the lanes beyond K hold empty moments).
-    int kw = 1;
-    while (kw < a.K) kw <<= 1;
-    auto slice_moments = [&](int s, uint64_t bits) {
-        return Moments{float(slice_len(s) * a.cpg), __uint_as_float(uint32_t(bits)),
-                       __uint_as_float(uint32_t(bits >> 32))};
-    };
-    auto combine = [&](const Moments (&m)[kGroupsPerWave]) {
-#pragma unroll
-        for (int i = 0; i < kGroupsPerWave; ++i) {
-            const int g = wave + i * kWaves;
-            if (g < a.CBg) {  // uniform over the wave
-                const Moments tot = segment_merge(m[i], kw);
-                if (lane == 0) stat[g] = finalize(tot, a.eps);
-            }
-        }
-    };
-    bool wave_late = false;
-    if (wave < a.CBg) {
-        Moments m[kGroupsPerWave];
-        bool ok = true;
-        if (lane == q) {
-#pragma unroll
-            for (int i = 0; i < kGroupsPerWave; ++i) {
-                const int g = wave + i * kWaves;
-                m[i] = g < a.CBg ? own_m[g] : Moments{0.0f, 0.0f, 0.0f};
-            }
-        } else if (lane < a.K) {
-            const long long t0 = wall_clock64();
-            for (;;) {
-                uint64_t seen[kGroupsPerWave];
-#pragma unroll
-                for (int i = 0; i < kGroupsPerWave; ++i) {
-                    const int g = wave + i * kWaves;
-                    seen[i] = g < a.CBg ? __hip_atomic_load(&flags[lane * a.CBg + g], __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT)
-                                        : a.tag;
-                }
-                bool ready = true;
-#pragma unroll
-                for (int i = 0; i < kGroupsPerWave; ++i) ready &= seen[i] == a.tag;
-                if (ready) break;
-                if (wall_clock64() - t0 > a.timeout_ticks) {
-                    ok = false;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-            uint64_t bits[kGroupsPerWave] = {};
-#pragma unroll
-            for (int i = 0; i < kGroupsPerWave; ++i) {
-                const int g = wave + i * kWaves;
-                if (ok && g < a.CBg)
-                    bits[i] = __hip_atomic_load(&part[lane * a.CBg + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-#pragma unroll
-            for (int i = 0; i < kGroupsPerWave; ++i) m[i] = slice_moments(lane, bits[i]);
-            if (!ok) late[lane] = 1;
-        } else {
-#pragma unroll
-            for (int i = 0; i < kGroupsPerWave; ++i) m[i] = Moments{0.0f, 0.0f, 0.0f};
-        }
-        wave_late = __any(!ok);
-        if (!wave_late) combine(m);
-        else if (lane == 0) any_late = 1;
-    }
-    __syncthreads();
-
-    // ---- slow path: some slice was not published in time.  Every slice some
-    // wave found late is reduced here with the code its owner runs; the waves
-    // that found one combine their groups again.
-    if (any_late) {  // uniform: written before the barrier
-        for (int s = 0; s < a.K; ++s) {
-            if (!late[s]) continue;  // uniform
-            const int nv = nvalid(s);
-            SlotSums acc;
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                if (r < nv) {
-                    V xv = load_vec<T, E>(a.X, vidx(s, r)), kv, sr;
-                    if constexpr (!BCAST) kv = load_vec<T, E>(a.skip, vidx(s, r));
-                    form(xv, kv, sr);
-                    accumulate(acc, sr, r);
-                }
-            reduce_slice(acc, nv, slice_m[s]);
-            __syncthreads();
-        }
-        if (wave_late) {
-            Moments m[kGroupsPerWave];
-#pragma unroll
-            for (int i = 0; i < kGroupsPerWave; ++i) {
-                const int g = wave + i * kWaves;
-                m[i] = Moments{0.0f, 0.0f, 0.0f};
-                if (g < a.CBg) {
-                    if (lane == q) m[i] = own_m[g];
-                    else if (lane < a.K && late[lane]) m[i] = slice_m[lane][g];
-                    else if (lane < a.K)  // this wave saw its tag
-                        m[i] = slice_moments(lane, __hip_atomic_load(&part[lane * a.CBg + g], __ATOMIC_RELAXED,
-                                                                     __HIP_MEMORY_SCOPE_AGENT));
-                }
-            }
-            combine(m);
-        }
-        __syncthreads();
-    }
-
-    // ---- normalize the held S
-    if (nv_own > 0) {
-        const float2 slo = stat[glo];
-        const float2 shi = stat[glo + 1 < a.CBg ? glo + 1 : glo];
-        float mean[E], scl[E], sft[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float2 st = e < split ? slo : shi;
-            mean[e] = st.x;
-            scl[e] = st.y * to_f32(gam[e]);
-            sft[e] = to_f32(bet[e]);
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (r < nv_own) {
-                V out;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    float y = fmaf_(to_f32(sv[r].v[e]) - mean[e], scl[e], sft[e]);
-                    if (a.silu) y = silu_f32(y);
-                    out.v[e] = from_f32<T>(y);
-                }
-                store_vec<T, E>(a.Y, vidx(q, r), out);
-            }
-    }
-}
-
 // ------------------------------------------------------------------ split: nhwc
 template <typename T, int E>
 __global__ void __launch_bounds__(256)
@@ -766,14 +292,15 @@ sgn_stats_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
     float cnt = 0.0f;
     if (active) {
         for (int64_t p = pb + p0; p < pe; p += kUnroll * P) {
+            // Pixels past the block's end re-read pixel p (loads stay out of
+            // lane-dependent branches); their values are discarded.
             V xs[kUnroll], ks[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t pp = p + int64_t(u) * P;
-                if (pp < pe) {
-                    xs[u] = load_in<T, E>(X, img + pp * Cv + cv, stream_in);
-                    if (!skip_bcast) ks[u] = load_in<T, E>(skip, img + pp * Cv + cv, stream_in);
-                }
+                const int64_t pc = pp < pe ? pp : p;
+                xs[u] = load_in<T, E>(X, img + pc * Cv + cv, stream_in);
+                if (!skip_bcast) ks[u] = load_in<T, E>(skip, img + pc * Cv + cv, stream_in);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
@@ -848,13 +375,12 @@ sgn_norm_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t pp = p + int64_t(u) * P;
-            if (pp < pe) {
-                if (S_in) {
-                    ss[u] = load_vec_stream<T, E>(S_in, img + pp * Cv + cv);
-                } else {
-                    ss[u] = load_vec_stream<T, E>(X, img + pp * Cv + cv);
-                    if (!skip_bcast) ks[u] = load_vec_stream<T, E>(skip, img + pp * Cv + cv);
-                }
+            const int64_t pc = pp < pe ? pp : p;  // discarded past the block's end
+            if (S_in) {
+                ss[u] = load_vec_stream<T, E>(S_in, img + pc * Cv + cv);
+            } else {
+                ss[u] = load_vec_stream<T, E>(X, img + pc * Cv + cv);
+                if (!skip_bcast) ks[u] = load_vec_stream<T, E>(skip, img + pc * Cv + cv);
             }
         }
         if (first) {
@@ -939,25 +465,31 @@ sgn_stats_group_kernel(const T* __restrict__ X, const T* __restrict__ skip,
     ShiftedSums acc;
     float cnt = 0.0f;
     for (uint32_t iv = vb + t; iv < ve; iv += kUnroll * 256) {
+        // Vectors past the block's end re-read vector iv (loads stay out of
+        // lane-dependent branches); their values are discarded.
         V xs[kUnroll], ks[kUnroll];
+        T bias_u[kUnroll], kb_u[kUnroll];
         int64_t addr[kUnroll];
         int ch[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t j = iv + uint32_t(u) * 256;
-            if (j < ve) {
-                // With E > 1 (NCHW only) a vector never straddles channels.
-                group_element<NCHW>(geo, n, g, j * E, addr[u], ch[u]);
-                xs[u] = load_in<T, E>(X, addr[u] / E, stream_in);
-                if (!skip_bcast) ks[u] = load_in<T, E>(skip, addr[u] / E, stream_in);
-            }
+            // With E > 1 (NCHW only) a vector never straddles channels.
+            group_element<NCHW>(geo, n, g, (j < ve ? j : iv) * E, addr[u], ch[u]);
+            xs[u] = load_in<T, E>(X, addr[u] / E, stream_in);
+            if (!skip_bcast) ks[u] = load_in<T, E>(skip, addr[u] / E, stream_in);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (has_bias) bias_u[u] = bias[ch[u]];
+            if (skip_bcast) kb_u[u] = skip[int64_t(n) * geo.C + ch[u]];
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t j = iv + uint32_t(u) * 256;
             if (j < ve) {
-                const float bb = has_bias ? to_f32(bias[ch[u]]) : 0.0f;
-                const float kb = skip_bcast ? to_f32(skip[int64_t(n) * geo.C + ch[u]]) : 0.0f;
+                const float bb = has_bias ? to_f32(bias_u[u]) : 0.0f;
+                const float kb = skip_bcast ? to_f32(kb_u[u]) : 0.0f;
                 V sv;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
@@ -991,33 +523,41 @@ sgn_norm_group_kernel(const T* __restrict__ X, const T* __restrict__ skip,
     const float2 st = stat[ng];
 
     for (uint32_t iv = vb + t; iv < ve; iv += kUnroll * 256) {
+        // Vectors past the block's end re-read vector iv (loads stay out of
+        // lane-dependent branches); their values are discarded.
         V ss[kUnroll], ks[kUnroll];
+        T bias_u[kUnroll], kb_u[kUnroll];
+        M gam_u[kUnroll], bet_u[kUnroll];
         int64_t addr[kUnroll];
         int ch[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t j = iv + uint32_t(u) * 256;
-            if (j < ve) {
-                group_element<NCHW>(geo, n, g, j * E, addr[u], ch[u]);
-                if (S_in) {
-                    ss[u] = load_vec_stream<T, E>(S_in, addr[u] / E);
-                } else {
-                    ss[u] = load_vec_stream<T, E>(X, addr[u] / E);
-                    if (!skip_bcast) ks[u] = load_vec_stream<T, E>(skip, addr[u] / E);
-                }
+            group_element<NCHW>(geo, n, g, (j < ve ? j : iv) * E, addr[u], ch[u]);
+            if (S_in) {
+                ss[u] = load_vec_stream<T, E>(S_in, addr[u] / E);
+            } else {
+                ss[u] = load_vec_stream<T, E>(X, addr[u] / E);
+                if (!skip_bcast) ks[u] = load_vec_stream<T, E>(skip, addr[u] / E);
             }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            gam_u[u] = gamma[ch[u]];
+            bet_u[u] = beta[ch[u]];
+            if (!S_in && has_bias) bias_u[u] = bias[ch[u]];
+            if (!S_in && skip_bcast) kb_u[u] = skip[int64_t(n) * geo.C + ch[u]];
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t j = iv + uint32_t(u) * 256;
             if (j < ve) {
-                const int c = ch[u];
-                const float scl = st.y * to_f32(gamma[c]);
-                const float sft = to_f32(beta[c]);
+                const float scl = st.y * to_f32(gam_u[u]);
+                const float sft = to_f32(bet_u[u]);
                 float bb = 0.0f, kb = 0.0f;
                 if (!S_in) {
-                    bb = has_bias ? to_f32(bias[c]) : 0.0f;
-                    kb = skip_bcast ? to_f32(skip[int64_t(n) * geo.C + c]) : 0.0f;
+                    bb = has_bias ? to_f32(bias_u[u]) : 0.0f;
+                    kb = skip_bcast ? to_f32(kb_u[u]) : 0.0f;
                 }
                 V out;
 #pragma unroll
@@ -1142,96 +682,6 @@ int cluster_k(int64_t Kv, int64_t NG, int max_r) {
     return int(k);
 }
 
-// Channel-block cluster plan.  Channel blocks: the fewest (so the most
-// channels per workgroup, for coalescing) with at most one group per wave,
-// which keeps each wave's combine to one butterfly; among those, the first
-// whose grid reaches kNhwcTargetBlocks workgroups (two per CU: fewer leave
-// the loads short of bandwidth, more lengthen the exchange more than they
-// shorten the streaming).  Slices are as few as that target allows, no more
-// than leave each thread about one vector, and as many as the register
-// budget (kNhwcMaxR pixels per thread) needs.
-constexpr int64_t kNhwcTargetBlocks = 512;
-
-struct NhwcPlan {
-    int CBv, NCB, CBg, P, sw_log, K, R;
-    int64_t pps;
-};
-
-bool nhwc_cluster_plan(int E, int64_t N, int64_t C, int64_t HW, int64_t groups, NhwcPlan* out) {
-    const int64_t cpg = C / groups;
-    if (N < 1 || HW < 1 || C % E != 0 || cpg < E) return false;
-    int64_t x = cpg, y = E;
-    while (y) {
-        const int64_t r = x % y;
-        x = y;
-        y = r;
-    }
-    const int64_t nb0 = C / (cpg / x * E);  // blocks of lcm(cpg, E) channels
-    for (int pass = 0; pass < 2; ++pass) {  // pass 0: at most one group per wave
-        bool found = false;
-        int64_t best_grid = 0;
-        for (int64_t ncb = 1; ncb <= nb0; ++ncb) {
-            if (nb0 % ncb) continue;
-            const int64_t cbv = C / ncb / E, cbg = C / ncb / cpg;
-            if (cbv > kClusterThreads || cbg > (pass == 0 ? kWaves : kNhwcMaxCBg)) continue;
-            const int64_t P = kClusterThreads / cbv;
-            const int64_t k_fit = (HW + P * kNhwcMaxR - 1) / (P * kNhwcMaxR);
-            if (k_fit > kNhwcMaxK) continue;
-            int64_t K = (kNhwcTargetBlocks + N * ncb - 1) / (N * ncb);
-            const int64_t k_work = HW * cbv / kClusterThreads;  // at least one vector per thread
-            if (K > k_work) K = k_work;
-            if (K < k_fit) K = k_fit;
-            if (K > kNhwcMaxK) K = kNhwcMaxK;
-            if (K > HW) K = HW;
-            const int64_t pps = (HW + K - 1) / K;
-            K = (HW + pps - 1) / pps;  // no empty slices
-            const int64_t grid = N * ncb * K;
-            if (!found || grid > best_grid) {
-                found = true;
-                best_grid = grid;
-                out->CBv = int(cbv);
-                out->NCB = int(ncb);
-                out->CBg = int(cbg);
-                out->P = int(P);
-                // Chunks per column in the pixel-lane reduction: a power of
-                // two, at most 16 (one DPP row), 2 * cbv columns * chunks <= 256.
-                int sw = 16;
-                while (sw > 1 && (2 * cbv * sw > kClusterThreads || sw / 2 >= P)) sw >>= 1;
-                int sw_log = 0;
-                while ((1 << sw_log) < sw) ++sw_log;
-                out->sw_log = sw_log;
-                out->K = int(K);
-                out->pps = pps;
-                out->R = int((pps + P - 1) / P);
-            }
-            if (grid >= kNhwcTargetBlocks) break;
-        }
-        if (found) return true;
-    }
-    return false;
-}
-
-template <typename T, typename M, int E, int R>
-hipError_t launch_nhwc_cluster_r(const NhwcClusterArgs<T, M>& ca, int64_t blocks, hipStream_t stream) {
-    if (ca.skip_bcast)
-        hipLaunchKernelGGL((sgn_nhwc_cluster_kernel<T, M, E, R, true>), dim3(unsigned(blocks)),
-                           dim3(kClusterThreads), 0, stream, ca);
-    else
-        hipLaunchKernelGGL((sgn_nhwc_cluster_kernel<T, M, E, R, false>), dim3(unsigned(blocks)),
-                           dim3(kClusterThreads), 0, stream, ca);
-    return hipGetLastError();
-}
-
-template <typename T, typename M, int E>
-hipError_t launch_nhwc_cluster(const NhwcClusterArgs<T, M>& ca, int r, int64_t blocks,
-                               hipStream_t stream) {
-    if (r <= 1) return launch_nhwc_cluster_r<T, M, E, 1>(ca, blocks, stream);
-    if (r <= 2) return launch_nhwc_cluster_r<T, M, E, 2>(ca, blocks, stream);
-    if (r <= 4) return launch_nhwc_cluster_r<T, M, E, 4>(ca, blocks, stream);
-    if (r <= 8) return launch_nhwc_cluster_r<T, M, E, 8>(ca, blocks, stream);
-    return launch_nhwc_cluster_r<T, M, E, kNhwcMaxR>(ca, blocks, stream);
-}
-
 template <typename T, typename M>
 hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const char** route) {
     constexpr int EV = VecWidth<T>::value;
@@ -1254,8 +704,13 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
     const bool data_ok = aligned16(a.X) && aligned16(a.Y) && (!a.S || aligned16(a.S)) &&
                          (a.skip_broadcast || aligned16(a.skip));
     const bool vec_allowed = want != Route::Scalar && want != Route::Block;
-    const bool nhwc_vec = vec_allowed && a.channels_last && a.C % EV == 0 && a.C / EV <= 256 &&
-                          data_ok && aligned16(a.skip) && (!a.bias || aligned16(a.bias));
+    // NHWC: the widest access that divides a pixel's channels and every base,
+    // with at most 256 vectors per pixel (one per thread).
+    int nhwc_e = 1;
+    if (vec_allowed && a.channels_last) {
+        nhwc_e = widest_vector<T>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
+        if (a.C / nhwc_e > 256) nhwc_e = 1;
+    }
     const bool nchw_vec = vec_allowed && !a.channels_last && HW % EV == 0 && data_ok;
 
     // ---- group-cluster route (NCHW)
@@ -1301,58 +756,35 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
     }
 
     // ---- channel-block cluster route (NHWC)
-    NhwcPlan plan;
-    if (a.channels_last && vec_allowed && want != Route::Split && a.C % EV == 0 && data_ok &&
-        aligned16(a.skip) && (!a.bias || aligned16(a.bias)) &&
-        nhwc_cluster_plan(EV, a.N, a.C, HW, a.groups, &plan)) {
-        NhwcClusterArgs<T, M> ca;
-        ca.X = X;
-        ca.skip = skip;
-        ca.bias = bias;
-        ca.S = S;
-        ca.Y = Y;
-        ca.gamma = gamma;
-        ca.beta = beta;
-        ca.part = part;
-        ca.flags = reinterpret_cast<uint64_t*>(stat + NG);
-        ca.tag = a.tag;
-        ca.timeout_ticks = a.exchange_timeout_ticks;
-        ca.HW = HW;
-        ca.pps = plan.pps;
-        ca.Cv = C / EV;
-        ca.cpg = cpg;
-        ca.CBv = plan.CBv;
-        ca.NCB = plan.NCB;
-        ca.CBg = plan.CBg;
-        ca.P = plan.P;
-        ca.sw_log = plan.sw_log;
-        ca.K = plan.K;
-        ca.units = int(a.N * plan.K);
-        ca.skip_bcast = a.skip_broadcast;
-        ca.silu = silu;
-        ca.eps = a.epsilon;
-        const int64_t blocks = (a.N * plan.K + 7) / 8 * 8 * plan.NCB;
-        *route = "sgn.cluster.nhwc.vec16";
-        return launch_nhwc_cluster<T, M, EV>(ca, plan.R, blocks, stream);
-    }
+    hipError_t err = hipSuccess;
+    if (launch_sgn_nhwc_cluster(a, want, part, reinterpret_cast<uint64_t*>(stat + NG), stream, route, &err))
+        return err;
 
     // ---- split route
     const int B = int(split_blocks(a.dtype, a.C, HW, a.groups, a.channels_last));
     const dim3 fin_grid = dim3(unsigned(NG));
 
-    if (nhwc_vec) {
-        *route = "sgn.split.nhwc.vec16";
-        const int Cv = C / EV, P = 256 / Cv;
+    if (nhwc_e > 1) {
+        // Blocks cover ppb pixels of one image whatever the access width.
         const int64_t ppb = (HW + B - 1) / B;
         const dim3 grid(unsigned(a.N * B));
-        hipLaunchKernelGGL((sgn_stats_nhwc_kernel<T, EV>), grid, dim3(256), 0, stream, X, skip, bias,
-                           S, part, HW, C, Cv, P, cpg, groups, B, ppb, a.skip_broadcast);
-        hipLaunchKernelGGL(sgn_finalize_kernel, fin_grid, dim3(256), 0, stream, part, stat, B,
-                           a.epsilon);
-        hipLaunchKernelGGL((sgn_norm_nhwc_kernel<T, M, EV>), grid, dim3(256), 0, stream, X, skip,
-                           bias, static_cast<const T*>(S), gamma, beta, stat, Y, HW, Cv, P, cpg,
-                           groups, B, ppb, a.skip_broadcast, silu);
-        return hipGetLastError();
+        auto launch = [&](auto tag, const char* name) {
+            constexpr int E = decltype(tag)::value;
+            const int Cv = C / E, P = 256 / Cv;
+            *route = name;
+            hipLaunchKernelGGL((sgn_stats_nhwc_kernel<T, E>), grid, dim3(256), 0, stream, X, skip, bias,
+                               S, part, HW, C, Cv, P, cpg, groups, B, ppb, a.skip_broadcast);
+            hipLaunchKernelGGL(sgn_finalize_kernel, fin_grid, dim3(256), 0, stream, part, stat, B,
+                               a.epsilon);
+            hipLaunchKernelGGL((sgn_norm_nhwc_kernel<T, M, E>), grid, dim3(256), 0, stream, X, skip,
+                               bias, static_cast<const T*>(S), gamma, beta, stat, Y, HW, Cv, P, cpg,
+                               groups, B, ppb, a.skip_broadcast, silu);
+            return hipGetLastError();
+        };
+        if (nhwc_e == EV) return launch(std::integral_constant<int, EV>(), "sgn.split.nhwc.vec16");
+        if (nhwc_e == EV / 2) return launch(std::integral_constant<int, EV / 2>(), "sgn.split.nhwc.vec8");
+        if constexpr (EV >= 8)
+            if (nhwc_e == EV / 4) return launch(std::integral_constant<int, EV / 4>(), "sgn.split.nhwc.vec4");
     }
 
     GroupGeom geo;

@@ -1,0 +1,133 @@
+// sgn_common.h -- device helpers and workspace constants shared by the
+// SkipGroupNorm sources (sgn.hip, sgn_nhwc.hip).  Internal to the library.
+#pragma once
+
+#include "device_common.h"
+#include "skipnorm_internal.h"
+
+namespace sn {
+
+constexpr int kClusterThreads = 256;  // threads per workgroup of the cluster routes
+constexpr int kClusterMaxK = 8;       // workgroups per (n, group), NCHW cluster route
+constexpr int kNhwcMaxK = 64;         // slices per (image, channel block), NHWC cluster route
+
+// Launches the NHWC channel-block cluster route when the shapes, alignments
+// and `want` allow it (returns false, having launched nothing, otherwise).
+// `part` and `flags` are the workspace's partial and tag areas.
+bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, uint64_t* flags,
+                             hipStream_t stream, const char** route, hipError_t* err);
+
+namespace {
+
+constexpr int kUnroll = 4;
+
+struct alignas(16) Partial {
+    float n, mean, m2, pad;
+};
+
+__device__ __forceinline__ Moments as_moments(const Partial& p) { return Moments{p.n, p.mean, p.m2}; }
+
+// Combines the moments of the 64 lanes of a wave.  Partners always combine
+// as merge(lower lane, upper lane), so both compute bitwise the same value
+// and every lane ends with the same total.
+__device__ __forceinline__ Moments wave_merge(Moments m) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        Moments o;
+        o.n = __shfl_xor(m.n, s, 64);
+        o.mean = __shfl_xor(m.mean, s, 64);
+        o.m2 = __shfl_xor(m.m2, s, 64);
+        m = (lane & s) ? merge(o, m) : merge(m, o);
+    }
+    return m;
+}
+
+// Block of W waves: wave totals through LDS, combined in wave order by every
+// thread (all threads return the same value).  `sh` holds W entries.
+template <int W>
+__device__ __forceinline__ Moments block_merge(Moments m, Moments* sh) {
+    m = wave_merge(m);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+    __syncthreads();
+    Moments tot = sh[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) tot = merge(tot, sh[w]);
+    __syncthreads();  // `sh` may be reused right away
+    return tot;
+}
+
+__device__ __forceinline__ float2 finalize(const Moments& m, float eps) {
+    const float var = m.n > 0.0f ? fmaxf(m.m2 / m.n, 0.0f) : 0.0f;
+    return make_float2(m.mean, inv_sqrt(var + eps));
+}
+
+template <typename T, int E>
+__device__ __forceinline__ void load_param_vec(const T* p, int64_t vi, float (&out)[E]) {
+    const Vec<T, E> v = load_vec<T, E>(p, vi);
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[e] = to_f32(v.v[e]);
+}
+
+template <typename T, int E>
+__device__ __forceinline__ Vec<T, E> load_in(const T* p, int64_t i, bool stream) {
+    return stream ? load_vec_stream<T, E>(p, i) : load_vec<T, E>(p, i);
+}
+
+// Pairwise combination without branches, the weight taken from the
+// hardware reciprocal (about 1 ulp) rather than an IEEE division: thousands
+// of these sit on the cluster route's critical path.  Empty moments are
+// (0, 0, 0); merging with one is exact either way (weight 0, or weight 1
+// when the other side is empty).  Every workgroup runs the same operations,
+// so the results stay bitwise reproducible.
+__device__ __forceinline__ Moments merge_rcp(const Moments& a, const Moments& b) {
+    const float n = a.n + b.n;
+    const float wb = b.n == n ? 1.0f : b.n * __builtin_amdgcn_rcpf(n);
+    const float d = b.mean - a.mean;
+    Moments r;
+    r.n = n;
+    r.mean = fmaf_(d, wb, a.mean);
+    r.m2 = fmaf_(d * d, a.n * wb, a.m2 + b.m2);
+    return r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ Moments dpp_merge_step(const Moments& m, bool upper) {
+    const Moments o{dpp_mov<CTRL>(m.n), dpp_mov<CTRL>(m.mean), dpp_mov<CTRL>(m.m2)};
+    return upper ? merge_rcp(o, m) : merge_rcp(m, o);
+}
+
+// Ordered butterfly over aligned segments of W lanes (W a power of two, at
+// most 64; uniform over the wave): every lane of a segment ends with bitwise
+// the same combination of the segment's values in lane order.  After the two
+// quad steps each quad is uniform, so mirroring inside 8 and 16 lanes pairs
+// the same quads and half-rows as an xor by 4 and by 8 would.
+__device__ __forceinline__ Moments segment_merge(Moments m, int W) {
+    const int lane = threadIdx.x & 63;
+    if (W >= 2) m = dpp_merge_step<kQuadXor1>(m, lane & 1);
+    if (W >= 4) m = dpp_merge_step<kQuadXor2>(m, lane & 2);
+    if (W >= 8) m = dpp_merge_step<kRowHalfMirror>(m, lane & 4);
+    if (W >= 16) m = dpp_merge_step<kRowMirror>(m, lane & 8);
+    for (int s = 16; s < W; s <<= 1) {
+        const Moments o{__shfl_xor(m.n, s, 64), __shfl_xor(m.mean, s, 64), __shfl_xor(m.m2, s, 64)};
+        m = (lane & s) ? merge_rcp(o, m) : merge_rcp(m, o);
+    }
+    return m;
+}
+
+// Block of 256 threads: each wave's ordered butterfly, then the four wave
+// totals in wave order through LDS; every thread returns the same value.
+// `sh` holds four entries.
+__device__ __forceinline__ Moments block_merge_rcp(Moments m, Moments* sh) {
+    m = segment_merge(m, 64);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+    __syncthreads();
+    Moments tot = sh[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) tot = merge_rcp(tot, sh[w]);
+    __syncthreads();  // `sh` may be reused right away
+    return tot;
+}
+
+}  // namespace
+}  // namespace sn

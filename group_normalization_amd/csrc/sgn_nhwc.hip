@@ -1,0 +1,531 @@
+// sgn_nhwc.hip -- SkipGroupNorm, NHWC channel-block cluster route (gfx950).
+// The operator and the other routes are described in sgn.hip.
+#include "sgn_common.h"
+
+namespace sn {
+namespace {
+
+// ------------------------------------------------------------------ channel-block cluster (NHWC)
+// In NHWC a group's channels are a short run inside every pixel, so a group
+// is not contiguous.  The channels are cut into NCB blocks, each a whole
+// number of groups and of 16-byte vectors (a multiple of lcm(cpg, E)
+// channels), and an image's pixels into K slices; one workgroup of 256
+// threads owns one (image, slice, channel block).  Thread t owns channel
+// vector v = t % CBv of the block at pixels t / CBv + r * P (P = 256 / CBv
+// pixel lanes), so its channels never change, and holds S for those pixels
+// in VGPRs.
+//
+// A slice's per-group moments: each thread keeps shifted sums for the (at
+// most two, as cpg >= E) groups its vector touches; the pixel lanes of each
+// (vector, group) column are merged in LDS, chunk by chunk and then by an
+// ordered DPP butterfly; each group merges its columns in channel order.
+// The K slices of an (image, block) exchange these moments as the
+// group-cluster route does (per-call tags, bounded waits, a late slice
+// recomputed with the same code) and each wave combines its groups over the
+// K slices with an ordered butterfly in slice order, so every workgroup of
+// the cluster holds bitwise the same statistics.  One launch: X and skip are
+// read once, S and Y written once.
+//
+// Block ids are laid out so that the NCB channel blocks of one (image,
+// slice) share the id's residue mod 8: consecutive ids are dispatched
+// round-robin over the 8 XCDs, so those workgroups, which touch the same
+// pixel rows and share their boundary cache lines, run under one L2.  The
+// data accesses are ordinary (cached) ones so that this L2 merges the
+// blocks' pieces of a line: with nontemporal stores the partial lines
+// reached memory separately (1.3-1.5x the written bytes, measured).
+template <typename T, typename M>
+struct NhwcClusterArgs {
+    const T *X, *skip, *bias;
+    T *S, *Y;
+    const M *gamma, *beta;
+    Partial* part;     // N * NCB * K * CBg slice moments (mean, M2)
+    uint64_t* flags;   // N * NCB * K * CBg publication tags
+    uint64_t tag;
+    long long timeout_ticks;
+    int64_t HW, pps;   // pixels per image and per slice
+    int Cv, cpg;       // vectors per pixel, channels per group
+    int CBv, NCB, CBg; // vectors per channel block, blocks per pixel, groups per block
+    int P, sw_log;     // pixel lanes per workgroup (256 / CBv); log2 of the chunks per column
+    int K, units;      // slices per image, N * K
+    bool skip_bcast, silu;
+    float eps;
+};
+
+constexpr int kNhwcMaxCBg = 16;   // groups per channel block: four per wave
+constexpr int kNhwcMaxR = 16;     // pixels per thread
+constexpr int kWaves = kClusterThreads / 64;
+constexpr int kGroupsPerWave = kNhwcMaxCBg / kWaves;
+
+template <typename T, typename M, int E, int R, bool BCAST>
+__global__ void __launch_bounds__(kClusterThreads)
+sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
+    using V = Vec<T, E>;
+    __shared__ Moments lane_m[2 * kClusterThreads];  // [pixel lane][column = 2 * vector + slot]
+    __shared__ Moments col_m[2 * kClusterThreads];   // column totals
+    __shared__ Moments own_m[kNhwcMaxCBg];           // this slice's group moments
+    __shared__ Moments slice_m[kNhwcMaxK][kNhwcMaxCBg];  // recomputed slices
+    __shared__ float2 stat[kNhwcMaxCBg];
+    __shared__ int late[kNhwcMaxK];
+    __shared__ int any_late;
+
+    const int bid = int(blockIdx.x);
+    const int xcd = bid & 7, rest = bid >> 3;
+    const int cb = rest % a.NCB;
+    const int u = (rest / a.NCB) * 8 + xcd;
+    if (u >= a.units) return;  // grid padding; not part of any cluster
+    const int n = u / a.K, q = u % a.K;
+    const int t = threadIdx.x;
+    const int wave = t >> 6, lane = t & 63;
+    const bool active = t < a.P * a.CBv;
+    const int v = active ? t % a.CBv : 0;
+    const int pl = active ? t / a.CBv : 0;
+    const int cvec = cb * a.CBv + v;  // channel vector within the pixel
+    const int glo = (v * E) / a.cpg;  // block-local group of the vector's first channel
+    const int split = (glo + 1) * a.cpg - v * E;  // channels [0, split) are in glo, the rest in glo + 1
+    const int ncol = 2 * a.CBv;
+    const int SW = 1 << a.sw_log;
+    const int64_t img = int64_t(n) * a.HW;
+    const bool has_bias = a.bias != nullptr;
+    if (t < kNhwcMaxK) late[t] = 0;
+    if (t == 0) any_late = 0;
+
+    // Pixels of slice s this thread holds (they are consecutive in r).
+    auto slice_len = [&](int s) {
+        const int64_t rem = a.HW - int64_t(s) * a.pps;
+        return rem < a.pps ? rem : a.pps;
+    };
+    auto nvalid = [&](int s) {
+        const int64_t len = slice_len(s);
+        if (!active || len <= pl) return 0;
+        const int64_t nv = (len - pl + a.P - 1) / a.P;
+        return nv < R ? int(nv) : R;
+    };
+    auto vidx = [&](int s, int r) {
+        return (img + int64_t(s) * a.pps + pl + int64_t(r) * a.P) * a.Cv + cvec;
+    };
+    // Per-channel constants: bias and broadcast skip (as T), gamma, beta.
+    V bvec, kvec;
+    M gam[E], bet[E];
+    auto load_constants = [&]() {
+        if (has_bias) bvec = load_vec<T, E>(a.bias, cvec);
+        if constexpr (BCAST) kvec = load_vec<T, E>(a.skip, int64_t(n) * a.Cv + cvec);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            gam[e] = a.gamma[cvec * E + e];
+            bet[e] = a.beta[cvec * E + e];
+        }
+    };
+    auto form = [&](const V& x, const V& kv, V& s) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float kk = BCAST ? to_f32(kvec.v[e]) : to_f32(kv.v[e]);
+            const float bb = has_bias ? to_f32(bvec.v[e]) : 0.0f;
+            residual_sum<T>(to_f32(x.v[e]), kk, has_bias, bb, s.v[e]);
+        }
+    };
+    // Shifted sums of the thread's two groups over its pixels of a slice, in
+    // pixel then channel order; the shifts are the first pixel's first and
+    // last channels (the last channel is in the upper group when it exists).
+    struct SlotSums {
+        ShiftedSums lo, hi;
+    };
+    auto accumulate = [&](SlotSums& acc, const V& s, int r) {
+        if (r == 0) {
+            acc.lo.shift = to_f32(s.v[0]);
+            acc.hi.shift = to_f32(s.v[E - 1]);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float x = to_f32(s.v[e]);
+            const bool in_lo = e < split;
+            const float d = x - (in_lo ? acc.lo.shift : acc.hi.shift);
+            const float dl = in_lo ? d : 0.0f, dh = in_lo ? 0.0f : d;
+            acc.lo.s1 += dl;
+            acc.lo.s2 = fmaf_(dl, dl, acc.lo.s2);
+            acc.hi.s1 += dh;
+            acc.hi.s2 = fmaf_(dh, dh, acc.hi.s2);
+        }
+    };
+    // Group moments of a slice from every thread's sums over its nv pixels,
+    // into dst[0 .. CBg).  The same code and thread mapping run wherever a
+    // slice is reduced.  Ends with dst written but not yet visible.
+    auto reduce_slice = [&](const SlotSums& acc, int nv, Moments* dst) {
+        if (active) {
+            const int nlo = split < E ? split : E;
+            lane_m[pl * ncol + 2 * v] = acc.lo.moments(float(nv * nlo));
+            lane_m[pl * ncol + 2 * v + 1] = acc.hi.moments(float(nv * (E - nlo)));
+        }
+        __syncthreads();
+        // Column c, chunk j: pixel lanes j, j + SW, ... in order; then the SW
+        // chunks (adjacent lanes of one DPP row) in an ordered butterfly.
+        for (int i0 = 0; i0 < ncol * SW; i0 += kClusterThreads) {
+            const int i = i0 + t;
+            const bool on = i < ncol * SW;
+            const int c = i >> a.sw_log, j = i & (SW - 1);
+            Moments m{0.0f, 0.0f, 0.0f};
+            if (on) {
+                // Up to four lanes' loads in flight per step.
+                for (int l0 = j; l0 < a.P; l0 += 4 * SW) {
+                    Moments x[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int l = l0 + k * SW;
+                        x[k] = l < a.P ? lane_m[l * ncol + c] : Moments{0.0f, 0.0f, 0.0f};
+                    }
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) m = merge_rcp(m, x[k]);
+                }
+            }
+            m = segment_merge(m, SW);
+            if (on && j == 0) col_m[c] = m;
+        }
+        __syncthreads();
+        if (t < a.CBg) {  // group t over its columns, in channel order
+            const int vf = (t * a.cpg) / E, vl = ((t + 1) * a.cpg - 1) / E;
+            Moments m{0.0f, 0.0f, 0.0f};
+            for (int w = vf; w <= vl; ++w) m = merge_rcp(m, col_m[2 * w + ((w * E) / a.cpg == t ? 0 : 1)]);
+            dst[t] = m;
+        }
+    };
+
+    // ---- own slice: S into registers, slice moments.  The data loads go out
+    // before the per-channel constants'.  No load sits behind a lane-dependent
+    // branch (the compiler would wait for each in turn): a thread's accesses
+    // past its pixels re-read the slice's first pixel and are discarded.
+    const int nv_own = nvalid(q);
+    const int64_t first_px = (img + int64_t(q) * a.pps) * a.Cv + cvec;
+    auto own_idx = [&](int r) { return r < nv_own ? vidx(q, r) : first_px; };
+    V sv[R];
+    {
+        V xs[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            xs[r] = load_vec<T, E>(a.X, own_idx(r));
+            if constexpr (!BCAST) sv[r] = load_vec<T, E>(a.skip, own_idx(r));
+        }
+        load_constants();
+        SlotSums acc;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < nv_own) {
+                form(xs[r], sv[r], sv[r]);
+                accumulate(acc, sv[r], r);
+            }
+        reduce_slice(acc, nv_own, own_m);
+    }
+
+    // ---- publication: per group, (mean, M2) as one 64-bit agent-scope store
+    // (coherent across the XCDs' L2 caches; the count is implied by the
+    // slice's size), completed before that group's tag goes out.
+    const int64_t first = (int64_t(n) * a.NCB + cb) * a.K * a.CBg;  // slice 0 of this (image, block)
+    uint64_t* part = reinterpret_cast<uint64_t*>(a.part) + first;
+    uint64_t* flags = a.flags + first;
+    if (a.K > 1 && t < a.CBg) {
+        const Moments m = own_m[t];
+        const uint64_t bits = uint64_t(__float_as_uint(m.mean)) | (uint64_t(__float_as_uint(m.m2)) << 32);
+        __hip_atomic_store(&part[q * a.CBg + t], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __hip_atomic_store(&flags[q * a.CBg + t], a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // S goes out after the publication's wait, which then waits for nothing else.
+    if (a.S) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < nv_own) store_vec<T, E>(a.S, vidx(q, r), sv[r]);
+    }
+    __syncthreads();  // own_m visible to every wave
+
+    // ---- statistics: wave w combines groups w, w + 4, ... over the K slices,
+    // lane s holding slice s (butterfly over the smallest power of two >= K
+    // lanes; the lanes beyond K hold empty moments).
+    int kw = 1;
+    while (kw < a.K) kw <<= 1;
+    auto slice_moments = [&](int s, uint64_t bits) {
+        return Moments{float(slice_len(s) * a.cpg), __uint_as_float(uint32_t(bits)),
+                       __uint_as_float(uint32_t(bits >> 32))};
+    };
+    auto combine = [&](const Moments (&m)[kGroupsPerWave]) {
+#pragma unroll
+        for (int i = 0; i < kGroupsPerWave; ++i) {
+            const int g = wave + i * kWaves;
+            if (g < a.CBg) {  // uniform over the wave
+                const Moments tot = segment_merge(m[i], kw);
+                if (lane == 0) stat[g] = finalize(tot, a.eps);
+            }
+        }
+    };
+    bool wave_late = false;
+    if (wave < a.CBg) {
+        Moments m[kGroupsPerWave];
+        bool ok = true;
+        if (lane == q) {
+#pragma unroll
+            for (int i = 0; i < kGroupsPerWave; ++i) {
+                const int g = wave + i * kWaves;
+                m[i] = g < a.CBg ? own_m[g] : Moments{0.0f, 0.0f, 0.0f};
+            }
+        } else if (lane < a.K) {
+            const long long t0 = wall_clock64();
+            for (;;) {
+                uint64_t seen[kGroupsPerWave];
+#pragma unroll
+                for (int i = 0; i < kGroupsPerWave; ++i) {
+                    const int g = wave + i * kWaves;
+                    seen[i] = g < a.CBg ? __hip_atomic_load(&flags[lane * a.CBg + g], __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                        : a.tag;
+                }
+                bool ready = true;
+#pragma unroll
+                for (int i = 0; i < kGroupsPerWave; ++i) ready &= seen[i] == a.tag;
+                if (ready) break;
+                if (wall_clock64() - t0 > a.timeout_ticks) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            uint64_t bits[kGroupsPerWave] = {};
+#pragma unroll
+            for (int i = 0; i < kGroupsPerWave; ++i) {
+                const int g = wave + i * kWaves;
+                if (ok && g < a.CBg)
+                    bits[i] = __hip_atomic_load(&part[lane * a.CBg + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int i = 0; i < kGroupsPerWave; ++i) m[i] = slice_moments(lane, bits[i]);
+            if (!ok) late[lane] = 1;
+        } else {
+#pragma unroll
+            for (int i = 0; i < kGroupsPerWave; ++i) m[i] = Moments{0.0f, 0.0f, 0.0f};
+        }
+        wave_late = __any(!ok);
+        if (!wave_late) combine(m);
+        else if (lane == 0) any_late = 1;
+    }
+    __syncthreads();
+
+    // ---- slow path: some slice was not published in time.  Every slice some
+    // wave found late is reduced here with the code its owner runs; the waves
+    // that found one combine their groups again.
+    if (any_late) {  // uniform: written before the barrier
+        for (int s = 0; s < a.K; ++s) {
+            if (!late[s]) continue;  // uniform
+            const int nv = nvalid(s);
+            SlotSums acc;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (r < nv) {
+                    V xv = load_vec<T, E>(a.X, vidx(s, r)), kv, sr;
+                    if constexpr (!BCAST) kv = load_vec<T, E>(a.skip, vidx(s, r));
+                    form(xv, kv, sr);
+                    accumulate(acc, sr, r);
+                }
+            reduce_slice(acc, nv, slice_m[s]);
+            __syncthreads();
+        }
+        if (wave_late) {
+            Moments m[kGroupsPerWave];
+#pragma unroll
+            for (int i = 0; i < kGroupsPerWave; ++i) {
+                const int g = wave + i * kWaves;
+                m[i] = Moments{0.0f, 0.0f, 0.0f};
+                if (g < a.CBg) {
+                    if (lane == q) m[i] = own_m[g];
+                    else if (lane < a.K && late[lane]) m[i] = slice_m[lane][g];
+                    else if (lane < a.K)  // this wave saw its tag
+                        m[i] = slice_moments(lane, __hip_atomic_load(&part[lane * a.CBg + g], __ATOMIC_RELAXED,
+                                                                     __HIP_MEMORY_SCOPE_AGENT));
+                }
+            }
+            combine(m);
+        }
+        __syncthreads();
+    }
+
+    // ---- normalize the held S
+    if (nv_own > 0) {
+        const float2 slo = stat[glo];
+        const float2 shi = stat[glo + 1 < a.CBg ? glo + 1 : glo];
+        float mean[E], scl[E], sft[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float2 st = e < split ? slo : shi;
+            mean[e] = st.x;
+            scl[e] = st.y * to_f32(gam[e]);
+            sft[e] = to_f32(bet[e]);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < nv_own) {
+                V out;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    float y = fmaf_(to_f32(sv[r].v[e]) - mean[e], scl[e], sft[e]);
+                    if (a.silu) y = silu_f32(y);
+                    out.v[e] = from_f32<T>(y);
+                }
+                store_vec<T, E>(a.Y, vidx(q, r), out);
+            }
+    }
+}
+
+// Channel-block cluster plan.  Channel blocks: the fewest (so the most
+// channels per workgroup, for coalescing) with at most one group per wave,
+// which keeps each wave's combine to one butterfly; among those, the first
+// whose grid reaches kNhwcTargetBlocks workgroups (two per CU: fewer leave
+// the loads short of bandwidth, more lengthen the exchange more than they
+// shorten the streaming).  Slices are as few as that target allows, no more
+// than leave each thread about one vector, and as many as the register
+// budget (kNhwcMaxR pixels per thread) needs.
+constexpr int64_t kNhwcTargetBlocks = 512;
+
+struct NhwcPlan {
+    int CBv, NCB, CBg, P, sw_log, K, R;
+    int64_t pps;
+};
+
+bool nhwc_cluster_plan(int E, int64_t N, int64_t C, int64_t HW, int64_t groups, NhwcPlan* out) {
+    const int64_t cpg = C / groups;
+    if (N < 1 || HW < 1 || C % E != 0 || cpg < E) return false;
+    int64_t x = cpg, y = E;
+    while (y) {
+        const int64_t r = x % y;
+        x = y;
+        y = r;
+    }
+    const int64_t nb0 = C / (cpg / x * E);  // blocks of lcm(cpg, E) channels
+    for (int pass = 0; pass < 2; ++pass) {  // pass 0: at most one group per wave
+        bool found = false;
+        int64_t best_grid = 0;
+        for (int64_t ncb = 1; ncb <= nb0; ++ncb) {
+            if (nb0 % ncb) continue;
+            const int64_t cbv = C / ncb / E, cbg = C / ncb / cpg;
+            if (cbv > kClusterThreads || cbg > (pass == 0 ? kWaves : kNhwcMaxCBg)) continue;
+            const int64_t P = kClusterThreads / cbv;
+            const int64_t k_fit = (HW + P * kNhwcMaxR - 1) / (P * kNhwcMaxR);
+            if (k_fit > kNhwcMaxK) continue;
+            int64_t K = (kNhwcTargetBlocks + N * ncb - 1) / (N * ncb);
+            const int64_t k_work = HW * cbv / kClusterThreads;  // at least one vector per thread
+            if (K > k_work) K = k_work;
+            if (K < k_fit) K = k_fit;
+            if (K > kNhwcMaxK) K = kNhwcMaxK;
+            if (K > HW) K = HW;
+            const int64_t pps = (HW + K - 1) / K;
+            K = (HW + pps - 1) / pps;  // no empty slices
+            const int64_t grid = N * ncb * K;
+            if (!found || grid > best_grid) {
+                found = true;
+                best_grid = grid;
+                out->CBv = int(cbv);
+                out->NCB = int(ncb);
+                out->CBg = int(cbg);
+                out->P = int(P);
+                // Chunks per column in the pixel-lane reduction: a power of
+                // two, at most 16 (one DPP row), 2 * cbv columns * chunks <= 256.
+                int sw = 16;
+                while (sw > 1 && (2 * cbv * sw > kClusterThreads || sw / 2 >= P)) sw >>= 1;
+                int sw_log = 0;
+                while ((1 << sw_log) < sw) ++sw_log;
+                out->sw_log = sw_log;
+                out->K = int(K);
+                out->pps = pps;
+                out->R = int((pps + P - 1) / P);
+            }
+            if (grid >= kNhwcTargetBlocks) break;
+        }
+        if (found) return true;
+    }
+    return false;
+}
+
+template <typename T, typename M, int E, int R>
+hipError_t launch_nhwc_cluster_r(const NhwcClusterArgs<T, M>& ca, int64_t blocks, hipStream_t stream) {
+    if (ca.skip_bcast)
+        hipLaunchKernelGGL((sgn_nhwc_cluster_kernel<T, M, E, R, true>), dim3(unsigned(blocks)),
+                           dim3(kClusterThreads), 0, stream, ca);
+    else
+        hipLaunchKernelGGL((sgn_nhwc_cluster_kernel<T, M, E, R, false>), dim3(unsigned(blocks)),
+                           dim3(kClusterThreads), 0, stream, ca);
+    return hipGetLastError();
+}
+
+template <typename T, typename M, int E>
+hipError_t launch_nhwc_cluster(const NhwcClusterArgs<T, M>& ca, int r, int64_t blocks,
+                               hipStream_t stream) {
+    if (r <= 1) return launch_nhwc_cluster_r<T, M, E, 1>(ca, blocks, stream);
+    if (r <= 2) return launch_nhwc_cluster_r<T, M, E, 2>(ca, blocks, stream);
+    if (r <= 4) return launch_nhwc_cluster_r<T, M, E, 4>(ca, blocks, stream);
+    if (r <= 8) return launch_nhwc_cluster_r<T, M, E, 8>(ca, blocks, stream);
+    return launch_nhwc_cluster_r<T, M, E, kNhwcMaxR>(ca, blocks, stream);
+}
+
+template <typename T, typename M>
+hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, int E, void* part,
+                             uint64_t* flags, hipStream_t stream) {
+    NhwcClusterArgs<T, M> ca;
+    ca.X = static_cast<const T*>(a.X);
+    ca.skip = static_cast<const T*>(a.skip);
+    ca.bias = static_cast<const T*>(a.bias);
+    ca.S = static_cast<T*>(a.S);
+    ca.Y = static_cast<T*>(a.Y);
+    ca.gamma = static_cast<const M*>(a.gamma);
+    ca.beta = static_cast<const M*>(a.beta);
+    ca.part = static_cast<Partial*>(part);
+    ca.flags = flags;
+    ca.tag = a.tag;
+    ca.timeout_ticks = a.exchange_timeout_ticks;
+    ca.HW = a.H * a.W;
+    ca.pps = plan.pps;
+    ca.Cv = int(a.C / E);
+    ca.cpg = int(a.C / a.groups);
+    ca.CBv = plan.CBv;
+    ca.NCB = plan.NCB;
+    ca.CBg = plan.CBg;
+    ca.P = plan.P;
+    ca.sw_log = plan.sw_log;
+    ca.K = plan.K;
+    ca.units = int(a.N * plan.K);
+    ca.skip_bcast = a.skip_broadcast;
+    ca.silu = a.activation == 1;
+    ca.eps = a.epsilon;
+    const int64_t blocks = (a.N * plan.K + 7) / 8 * 8 * plan.NCB;
+    constexpr int EV = VecWidth<T>::value;
+    if (E == EV) return launch_nhwc_cluster<T, M, EV>(ca, plan.R, blocks, stream);
+    if (E == EV / 2) return launch_nhwc_cluster<T, M, EV / 2>(ca, plan.R, blocks, stream);
+    if constexpr (EV >= 8)
+        if (E == EV / 4) return launch_nhwc_cluster<T, M, EV / 4>(ca, plan.R, blocks, stream);
+    return hipErrorInvalidValue;  // the caller picks E from the same widths
+}
+
+}  // namespace
+
+bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, uint64_t* flags,
+                             hipStream_t stream, const char** route, hipError_t* err) {
+    if (!a.channels_last || want == Route::Scalar || want == Route::Block || want == Route::Split)
+        return false;
+    const int size = a.dtype == 0 ? 4 : 2;
+    const int64_t HW = a.H * a.W;
+    // The widest access that divides a pixel's channels and every base (the
+    // broadcast skip's rows are C elements apart, like the pixels) and is
+    // no wider than a group: groups narrower than a 16-byte vector take
+    // 8- or 4-byte vectors here rather than three launches.
+    int E = a.dtype == 0 ? widest_vector<float>(a.C, {a.X, a.Y, a.S, a.skip, a.bias})
+                         : widest_vector<half_t>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
+    while (E > 1 && a.C / a.groups < E) E /= 2;
+    NhwcPlan plan;
+    if (E == 1 || !nhwc_cluster_plan(E, a.N, a.C, HW, a.groups, &plan)) return false;
+    static const char* const kNames[] = {"sgn.cluster.nhwc.vec4", "sgn.cluster.nhwc.vec8",
+                                         "sgn.cluster.nhwc.vec16"};
+    *route = kNames[E * size == 16 ? 2 : E * size == 8 ? 1 : 0];
+    if (a.dtype == 0) {
+        if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, E, part, flags, stream);
+        else *err = launch_nhwc_typed<float, half_t>(a, plan, E, part, flags, stream);
+    } else {
+        if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, plan, E, part, flags, stream);
+        else *err = launch_nhwc_typed<half_t, half_t>(a, plan, E, part, flags, stream);
+    }
+    return true;
+}
+
+}  // namespace sn

@@ -11,14 +11,16 @@
 //          in VGPRs as T (the rounded S is exactly representable in T), so
 //          the row is read once and written once, with nontemporal loads
 //          and stores (gamma and bias, shared by every row, stay cached).
-//          E elements per access: 16-byte vectors (4 x f32 / 8 x f16) or
-//          scalars.
+//          E elements per access: the widest of 16-, 8- and 4-byte vectors
+//          that divides the row and every base address, else scalars.
 //   rowblock  the same with four waves (one 256-thread workgroup) per row
-//          for wider rows (up to 32768 float16 / 16384 float32 elements): the
-//          wave sums meet in LDS and are added in wave order.
-//   block  one 256-thread workgroup per row for any other row (scalar
-//          accesses, wider rows): S is formed twice (once for the statistic,
-//          once for the output), reading the inputs twice.
+//          for wider rows (up to 16 vectors per lane: 32768 float16 /
+//          16384 float32 elements with 16-byte vectors; 32 scalars per lane:
+//          8192 elements): the wave sums meet in LDS and are added in wave
+//          order.
+//   block  one 256-thread workgroup per row for any wider row: S is formed
+//          twice (once for the statistic, once for the output), reading the
+//          inputs twice.
 // Statistic: each lane accumulates its own squares in float32 (FMA), then a
 // fixed butterfly sums the 64 lanes (DPP inside 16-lane rows, then two
 // cross-row exchanges), so every lane holds the same total and the result
@@ -50,25 +52,25 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     const int64_t base = row * nvec;
     const bool has_bias = bias != nullptr;
 
-    // Issue every load of the row before any arithmetic.
+    // Issue every load of the row before any arithmetic.  No load sits behind
+    // a lane-dependent branch (that makes the compiler wait for each one in
+    // turn): lanes past the row's end re-read its last vector and discard it.
+    auto clamp = [&](int idx) { return FULL || idx < nvec ? idx : nvec - 1; };
     V xs[NV], ks[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-        const int idx = v * LANES + lane;
-        if (FULL || idx < nvec) {
-            xs[v] = load_vec_stream<T, E>(input, base + idx);
-            ks[v] = load_vec_stream<T, E>(skip, base + idx);
-        }
+        const int idx = clamp(v * LANES + lane);
+        xs[v] = load_vec_stream<T, E>(input, base + idx);
+        ks[v] = load_vec_stream<T, E>(skip, base + idx);
     }
-
     V ss[NV];
     float acc = 0.0f;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int idx = v * LANES + lane;
+        V bv = {};
+        if (has_bias) bv = load_vec<T, E>(bias, clamp(idx));  // cached; outside the lane branch
         if (FULL || idx < nvec) {
-            V bv = {};
-            if (has_bias) bv = load_vec<T, E>(bias, idx);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const float s = residual_sum<T>(to_f32(xs[v].v[e]), to_f32(ks[v].v[e]), has_bias,
@@ -96,14 +98,12 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int idx = v * LANES + lane;
-        if (FULL || idx < nvec) {
-            const V gv = load_vec<T, E>(gamma, idx);
-            V out;
+        const V gv = load_vec<T, E>(gamma, clamp(idx));
+        V out;
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                out.v[e] = from_f32<T>(to_f32(ss[v].v[e]) * r * to_f32(gv.v[e]));
-            store_vec_stream<T, E>(output, base + idx, out);
-        }
+        for (int e = 0; e < E; ++e)
+            out.v[e] = from_f32<T>(to_f32(ss[v].v[e]) * r * to_f32(gv.v[e]));
+        if (FULL || idx < nvec) store_vec_stream<T, E>(output, base + idx, out);
     }
 }
 
@@ -172,10 +172,8 @@ hipError_t launch_wave(const SslnArgs& a, int nvec, hipStream_t stream) {
     if (need <= 4) return launch_wave_nv<T, E, 4, WPR>(a, nvec, stream);
     if (need <= 6) return launch_wave_nv<T, E, 6, WPR>(a, nvec, stream);
     if (need <= 8) return launch_wave_nv<T, E, 8, WPR>(a, nvec, stream);
-    if constexpr (MAXNV >= 16) {
-        if (need <= 12) return launch_wave_nv<T, E, 12, WPR>(a, nvec, stream);
-        if (need <= 16) return launch_wave_nv<T, E, 16, WPR>(a, nvec, stream);
-    }
+    if (need <= 12) return launch_wave_nv<T, E, 12, WPR>(a, nvec, stream);
+    if (need <= 16) return launch_wave_nv<T, E, 16, WPR>(a, nvec, stream);
     if constexpr (MAXNV >= 32) {
         if (need <= 24) return launch_wave_nv<T, E, 24, WPR>(a, nvec, stream);
         if (need <= 32) return launch_wave_nv<T, E, 32, WPR>(a, nvec, stream);
@@ -183,36 +181,46 @@ hipError_t launch_wave(const SslnArgs& a, int nvec, hipStream_t stream) {
     return hipErrorInvalidValue;  // callers check the width first
 }
 
-// Widest row (in vectors per lane) each instantiation keeps in registers:
-// one wave per row up to 8192 elements; four waves per row up to 16 vectors
-// per lane (32768 float16 or 16384 float32 elements).
-template <typename T> constexpr int kMaxNvVector = sizeof(T) == 2 ? 16 : 32;
-constexpr int kMaxNvRowBlock = 16;
-constexpr int kMaxNvScalar = 32;                                           // 2048 elements
+// Widest row (in accesses per lane) each route keeps in registers: 16 per
+// lane for vectors (32 for 16-byte float32 vectors and for scalars, whose
+// registers hold less) with one wave per row; 16 (32 for scalars) with four
+// waves per row.
+template <typename T, int E>
+constexpr int kMaxNvWave = E == 1 || (E * sizeof(T) == 16 && sizeof(T) == 4) ? 32 : 16;
+template <int E> constexpr int kMaxNvRowBlock = E == 1 ? 32 : 16;
+
+// Rows of E-element accesses: one wave per row, else four waves per row.
+template <typename T, int E>
+hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char** route) {
+    static const char* const kNames[2][4] = {
+        {"ssln.wave.scalar", "ssln.wave.vec4", "ssln.wave.vec8", "ssln.wave.vec16"},
+        {"ssln.rowblock.scalar", "ssln.rowblock.vec4", "ssln.rowblock.vec8", "ssln.rowblock.vec16"}};
+    constexpr int kName = E == 1 ? 0 : E * sizeof(T) == 16 ? 3 : E * sizeof(T) == 8 ? 2 : 1;
+    const int64_t nvec = a.hidden / E;
+    if (nvec <= 64 * kMaxNvWave<T, E>) {
+        *route = kNames[0][kName];
+        return launch_wave<T, E, kMaxNvWave<T, E>, 1>(a, int(nvec), stream);
+    }
+    *route = kNames[1][kName];
+    return launch_wave<T, E, kMaxNvRowBlock<E>, 4>(a, int(nvec), stream);
+}
 
 template <typename T>
 hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, const char** route) {
-    constexpr int EV = VecWidth<T>::value;
-    const int64_t nvec = a.hidden / EV;
-    const bool vec_ok = a.hidden % EV == 0 && nvec <= 256 * kMaxNvRowBlock &&
-                        aligned16(a.input) && aligned16(a.skip) && aligned16(a.gamma) &&
-                        (!a.bias || aligned16(a.bias)) && aligned16(a.output) &&
-                        (!a.sum || aligned16(a.sum));
-    Route r = want;
-    if (r == Route::Auto || r == Route::Vector || r == Route::Split) r = vec_ok ? Route::Vector : Route::Scalar;
-    if (r == Route::Scalar && a.hidden > 64 * kMaxNvScalar) r = Route::Block;
-
-    if (r == Route::Vector) {
-        if (nvec <= 64 * kMaxNvVector<T>) {
-            *route = "ssln.wave.vec16";
-            return launch_wave<T, EV, kMaxNvVector<T>, 1>(a, int(nvec), stream);
+    // Widest access that divides the row and every tensor's base.
+    int E = widest_vector<T>(a.hidden, {a.input, a.skip, a.gamma, a.bias, a.output, a.sum});
+    if (want == Route::Scalar) E = 1;
+    const int64_t max_regs = 256 * int64_t(E) * (E == 1 ? kMaxNvRowBlock<1> : kMaxNvRowBlock<2>);
+    if (want != Route::Block && a.hidden <= max_regs) {
+        if constexpr (sizeof(T) == 2) {
+            if (E == 8) return launch_ssln_width<T, 8>(a, stream, route);
+            if (E == 4) return launch_ssln_width<T, 4>(a, stream, route);
+            if (E == 2) return launch_ssln_width<T, 2>(a, stream, route);
+        } else {
+            if (E == 4) return launch_ssln_width<T, 4>(a, stream, route);
+            if (E == 2) return launch_ssln_width<T, 2>(a, stream, route);
         }
-        *route = "ssln.rowblock.vec16";
-        return launch_wave<T, EV, kMaxNvRowBlock, 4>(a, int(nvec), stream);
-    }
-    if (r == Route::Scalar) {
-        *route = "ssln.wave.scalar";
-        return launch_wave<T, 1, kMaxNvScalar, 1>(a, int(a.hidden), stream);
+        return launch_ssln_width<T, 1>(a, stream, route);
     }
     *route = "ssln.block";
     const int64_t blocks = a.rows < 65536 * 16 ? a.rows : 65536 * 16;

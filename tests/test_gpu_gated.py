@@ -28,7 +28,20 @@ CASES = [
     ((2, 5000), 5000, F32),      # scalar segment limit exceeded: block route
     ((2, 2, 9000), 9000, F16),
     ((1000,), 10, F16),          # rank 1
+    ((4, 396), 132, F16),        # 8-byte vectors: 33 per row
+    ((3, 650), 130, F16),        # 4-byte vectors: 65 per row, two per lane
+    ((5, 129), 129, F16),        # odd span: scalars
+    ((4, 6), 6, F32),            # float32 8-byte vectors: 3 per row
+    ((2, 8200), 4100, F16),      # 1025 eight-byte vectors: block route
 ]
+
+
+def expected_route(C, dt):
+    size = np.dtype(dt).itemsize
+    width = next((b for b in (16, 8, 4) if b > size and C * size % b == 0), size)
+    E = width // size
+    name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
+    return f"gated.segment.{name}" if C // E <= 1024 else "gated.block"
 
 
 @pytest.mark.parametrize("route", ["auto", "scalar", "block"])
@@ -41,9 +54,8 @@ def test_matches_oracle(shape, C, dt, route):
         y = gn.gated_rms_norm(to_dev(x["X"]), to_dev(x["scale"]), to_dev(x["gate"]), 1e-5)
         used = gn.last_route()
     assert_close(to_host(y), ref, f"Y via {used}")
-    vec = 16 // np.dtype(dt).itemsize
-    if route == "auto" and C % vec == 0 and C // vec <= 1024:
-        assert used == "gated.segment.vec16"
+    if route == "auto":
+        assert used == expected_route(C, dt)
 
 
 @pytest.mark.parametrize("dt", [F32, F16])

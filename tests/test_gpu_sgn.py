@@ -52,6 +52,24 @@ CASES = [
 ]
 
 
+def nhwc_route(C, groups, T):
+    """The NHWC route the library picks for aligned tensors of these
+    channels: the channel-block cluster with the widest of 16-, 8- and
+    4-byte accesses that divides a pixel and is no wider than a group;
+    otherwise the split route with the widest access (or scalars)."""
+    size = np.dtype(T).itemsize
+    width = next((b for b in (16, 8, 4) if b > size and C * size % b == 0), size)
+    names = {16: "vec16", 8: "vec8", 4: "vec4"}
+    w = width
+    while w > size and C // groups < w // size:
+        w //= 2
+    if w > size:
+        return f"sgn.cluster.nhwc.{names[w]}"
+    if width > size and C // (width // size) <= 256:
+        return f"sgn.split.nhwc.{names[width]}"
+    return "sgn.split.nhwc.scalar"
+
+
 def make(case, seed=0):
     N, C, H, W, T, M, cl, bc, bias, groups, act = case
     w = workloads.sgn("t", N, C, H, W, T, M, channels_last=bool(cl), broadcast_skip=bc, bias=bias,
@@ -78,11 +96,7 @@ def test_matches_oracle(case, route):
     if route == "auto" and not cl:
         assert used.startswith("sgn.cluster")  # every NCHW case here fits the cluster route
     if route == "auto" and cl:
-        # NHWC: the channel-block cluster needs whole 16-byte vectors per pixel
-        # and groups at least one vector wide.
-        ev = 16 // np.dtype(T).itemsize
-        fits = C % ev == 0 and C // groups >= ev
-        assert used == ("sgn.cluster.nhwc.vec16" if fits else "sgn.split.nhwc.scalar")
+        assert used == nhwc_route(C, groups, T)
 
 
 # NCHW groups around the cluster route's limits (per (n, group), at most 8
@@ -124,7 +138,12 @@ NHWC_LIMIT_CASES = [
     (2, 72, 16, 16, F16, 8, True, "sgn.cluster.nhwc.vec16"),      # 9 channels/group: 2 groups per wave
     (16, 144, 8, 8, F16, 16, False, "sgn.cluster.nhwc.vec16"),    # 16 groups per block: 4 per wave
     (2, 96, 9, 11, F16, 8, False, "sgn.cluster.nhwc.vec16"),      # 12 channels/group, ragged last slice
-    (2, 64, 8, 8, F16, 16, False, "sgn.split.nhwc.vec16"),        # 4 channels/group < one vector
+    (2, 64, 8, 8, F16, 16, False, "sgn.cluster.nhwc.vec8"),       # 4 channels/group: 8-byte vectors
+    (2, 64, 8, 8, F16, 32, True, "sgn.cluster.nhwc.vec4"),        # 2 channels/group: 4-byte vectors
+    (2, 64, 8, 8, F16, 64, False, "sgn.split.nhwc.vec16"),        # 1 channel/group: split route
+    (2, 324, 16, 16, F16, 36, False, "sgn.cluster.nhwc.vec8"),    # 648-byte pixels: 8-byte vectors
+    (2, 162, 8, 8, F16, 18, True, "sgn.cluster.nhwc.vec4"),       # 324-byte pixels: 4-byte vectors
+    (2, 90, 8, 8, F32, 9, False, "sgn.cluster.nhwc.vec8"),        # float32 360-byte pixels
     (1, 16, 9, 7, F32, 4, True, "sgn.cluster.nhwc.vec16"),        # float32, 4 channels/group, 1 slice
     (2, 2560, 8, 8, F32, 32, False, "sgn.cluster.nhwc.vec16"),    # 640 vectors per pixel, 3 pixel lanes
     (600, 16, 2, 2, F32, 2, True, "sgn.cluster.nhwc.vec16"),      # one slice per image: no exchange

@@ -55,18 +55,27 @@ SHAPES = [
     ((2, 16384), F32, True),     # float32 four waves per row, 16 vectors per lane
     ((2, 10000), F32, False),    # float32 four waves per row, ragged
     ((2, 40000), F16, True),     # wider than any register-resident route: block route
+    ((7, 4100), F16, True),      # 8-byte vectors, 1025 of them: four waves per row
+    ((5, 4092), F16, True),      # 8-byte vectors, one wave per row
+    ((5, 4098), F16, False),     # 4-byte vectors, 2049 of them: four waves per row
+    ((3, 2046), F16, True),      # 4-byte vectors, one wave per row
+    ((4, 4097), F16, False),     # odd width: scalars, four waves per row
+    ((3, 6002), F32, True),      # float32 8-byte vectors, four waves per row
+    ((2, 8193), F16, True),      # odd and wider than the scalar registers: block route
 ]
 
 
 def expected_route(shape, dt):
-    vec = 16 // np.dtype(dt).itemsize
+    size = np.dtype(dt).itemsize
     hidden = shape[-1]
-    if hidden % vec:
-        return "ssln.wave.scalar" if hidden <= 2048 else "ssln.block"
-    if hidden <= 8192:
-        return "ssln.wave.vec16"
-    if hidden // vec <= 256 * 16:
-        return "ssln.rowblock.vec16"
+    width = next((b for b in (16, 8, 4) if b > size and hidden * size % b == 0), size)
+    E = width // size
+    name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
+    nvec = hidden // E
+    if nvec <= 64 * (32 if E == 1 or (width == 16 and size == 4) else 16):
+        return f"ssln.wave.{name}"
+    if nvec <= 256 * (32 if E == 1 else 16):
+        return f"ssln.rowblock.{name}"
     return "ssln.block"
 
 
@@ -92,6 +101,29 @@ def test_optional_outputs_do_not_change_output(dt, hidden, want):
     check(ref, out, want)
     _, base, _ = run_both(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6, want=())
     assert_bitwise(to_host(out.output), to_host(base.output), "output with/without optional outputs")
+
+
+@pytest.mark.parametrize("offset,route", [(1, "ssln.rowblock.scalar"), (2, "ssln.rowblock.vec4"),
+                                          (4, "ssln.wave.vec8")])
+def test_base_alignment_picks_the_vector_width(offset, route):
+    """Views `offset` halves into their buffers: 2-, 4- and 8-byte aligned
+    bases take scalar, 4-byte and 8-byte accesses, with the same results."""
+    rows, hidden = 6, 4096
+    w = workloads.ssln("t", (rows, hidden), F16, bias=True, epsilon=1e-6)
+    x = workloads.generate(w, seed=12)
+    def view(a):
+        buf = torch.empty(rows * hidden + 8, dtype=torch.float16, device="cuda")
+        v = buf[offset: offset + rows * hidden].view(rows, hidden)
+        v.copy_(to_dev(a))
+        return v
+    out = gn.skip_rms_norm(view(x["input"]), view(x["skip"]), to_dev(x["gamma"]), to_dev(x["bias"]),
+                           1e-6, want_sum=True, want_inv_std_var=True)
+    assert gn.last_route() == route
+    ref = oracle.skip_rms_norm(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6,
+                               want_inv_std_var=True, want_sum=True)
+    assert_close(to_host(out.output), ref[0], "output")
+    assert_close(to_host(out.inv_std_var), ref[2], "inv_std_var")
+    assert_bitwise(to_host(out.input_skip_bias_sum), ref[3], "S")
 
 
 def test_unaligned_tensors_take_scalar_route():
