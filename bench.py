@@ -38,7 +38,7 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E
 STEP_WORKLOADS = ["ssln_f16_16x2048x4096", "gated_f16_8x4096x4096_c128",
                   "sgn_f16_nhwc_2x64x64x320", "sgn_f32_nchw_4x1280x32x32"]
 DOMINANT = "ssln_f16_16x2048x4096"
-DOMINANT_KERNEL = "ssln_wave_kernel<half, 8 per vector, 8 vectors per lane>"
+DOMINANT_KERNEL = "ssln_wave_kernel<half, 8 per vector, 4 vectors per lane, 2 waves per row>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ssln_f16_16x2048x4096.json")
 KERNEL_SOURCES = ["group_normalization_amd/csrc/ssln.hip", "group_normalization_amd/csrc/device_common.h"]
 COPY_BYTES = 1 << 30

@@ -6,7 +6,8 @@
 // S, mean (zero for the simplified form) and inv_std_var (r).
 //
 // Routes:
-//   wave   one wave64 per row (rows up to 8192 elements); lane l holds the
+//   wave   one wave64 per row (wave2: two; rows of up to 4 sixteen-byte,
+//          8 eight-byte or 16 narrower accesses per lane); lane l holds the
 //          row's vectors l, l+64, ...
 //          in VGPRs as T (the rounded S is exactly representable in T), so
 //          the row is read once and written once, with nontemporal loads
@@ -33,9 +34,8 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-// WPR waves per row: 1 (four rows per 256-thread block) or 4 (one row per
-// block, for rows wider than one wave's registers).  Lane l of the row's
-// 64*WPR lanes holds vectors l, l + 64*WPR, ...
+// WPR waves per row: 1, 2 or 4 (four, two or one rows per 256-thread
+// block).  Lane l of the row's 64*WPR lanes holds vectors l, l + 64*WPR, ...
 template <typename T, int E, int NV, bool FULL, int WPR>
 __global__ void __launch_bounds__(256)
 ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
@@ -45,10 +45,15 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                  int64_t rows, int nvec, float hidden_f, float eps) {
     using V = Vec<T, E>;
     constexpr int LANES = 64 * WPR;
-    __shared__ float wave_part[WPR > 1 ? WPR : 1];
+    __shared__ float wave_part[kWavesPerBlock];
     const int lane = threadIdx.x % LANES;
-    const int64_t row = int64_t(blockIdx.x) * (kWavesPerBlock / WPR) + threadIdx.x / LANES;
-    if (row >= rows) return;  // whole wave (WPR = 1) or whole block (WPR = 4)
+    const int64_t my_row = int64_t(blockIdx.x) * (kWavesPerBlock / WPR) + threadIdx.x / LANES;
+    // A whole wave (WPR = 1) or block (WPR = 4) leaves; with two rows per
+    // block the waves of a missing second row stay for the barrier and
+    // store nothing.
+    if (WPR != 2 && my_row >= rows) return;
+    const bool live = my_row < rows;
+    const int64_t row = live ? my_row : rows - 1;
     const int64_t base = row * nvec;
     const bool has_bias = bias != nullptr;
 
@@ -77,7 +82,7 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                                                 to_f32(bv.v[e]), ss[v].v[e]);
                 acc = fmaf_(s, s, acc);
             }
-            if (sum) store_vec_stream<T, E>(sum, base + idx, ss[v]);
+            if (sum && live) store_vec_stream<T, E>(sum, base + idx, ss[v]);
         }
     }
 
@@ -85,12 +90,13 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     if constexpr (WPR > 1) {
         if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = total;
         __syncthreads();
-        total = wave_part[0];
+        const int w0 = (threadIdx.x / LANES) * WPR;  // the row's first wave
+        total = wave_part[w0];
 #pragma unroll
-        for (int w = 1; w < WPR; ++w) total += wave_part[w];
+        for (int w = 1; w < WPR; ++w) total += wave_part[w0 + w];
     }
     const float r = inv_sqrt(total / hidden_f + eps);
-    if (lane == 0) {
+    if (live && lane == 0) {
         if (inv_std_var) inv_std_var[row] = r;
         if (mean) mean[row] = 0.0f;
     }
@@ -103,7 +109,7 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
 #pragma unroll
         for (int e = 0; e < E; ++e)
             out.v[e] = from_f32<T>(to_f32(ss[v].v[e]) * r * to_f32(gv.v[e]));
-        if (FULL || idx < nvec) store_vec_stream<T, E>(output, base + idx, out);
+        if ((FULL || idx < nvec) && live) store_vec_stream<T, E>(output, base + idx, out);
     }
 }
 
@@ -170,10 +176,14 @@ hipError_t launch_wave(const SslnArgs& a, int nvec, hipStream_t stream) {
     if (need <= 2) return launch_wave_nv<T, E, 2, WPR>(a, nvec, stream);
     if (need <= 3) return launch_wave_nv<T, E, 3, WPR>(a, nvec, stream);
     if (need <= 4) return launch_wave_nv<T, E, 4, WPR>(a, nvec, stream);
-    if (need <= 6) return launch_wave_nv<T, E, 6, WPR>(a, nvec, stream);
-    if (need <= 8) return launch_wave_nv<T, E, 8, WPR>(a, nvec, stream);
-    if (need <= 12) return launch_wave_nv<T, E, 12, WPR>(a, nvec, stream);
-    if (need <= 16) return launch_wave_nv<T, E, 16, WPR>(a, nvec, stream);
+    if constexpr (MAXNV >= 8) {
+        if (need <= 6) return launch_wave_nv<T, E, 6, WPR>(a, nvec, stream);
+        if (need <= 8) return launch_wave_nv<T, E, 8, WPR>(a, nvec, stream);
+    }
+    if constexpr (MAXNV >= 16) {
+        if (need <= 12) return launch_wave_nv<T, E, 12, WPR>(a, nvec, stream);
+        if (need <= 16) return launch_wave_nv<T, E, 16, WPR>(a, nvec, stream);
+    }
     if constexpr (MAXNV >= 32) {
         if (need <= 24) return launch_wave_nv<T, E, 24, WPR>(a, nvec, stream);
         if (need <= 32) return launch_wave_nv<T, E, 32, WPR>(a, nvec, stream);
@@ -181,27 +191,33 @@ hipError_t launch_wave(const SslnArgs& a, int nvec, hipStream_t stream) {
     return hipErrorInvalidValue;  // callers check the width first
 }
 
-// Widest row (in accesses per lane) each route keeps in registers: 16 per
-// lane for vectors (32 for 16-byte float32 vectors and for scalars, whose
-// registers hold less) with one wave per row; 16 (32 for scalars) with four
-// waves per row.
-template <typename T, int E>
-constexpr int kMaxNvWave = E == 1 || (E * sizeof(T) == 16 && sizeof(T) == 4) ? 32 : 16;
+// Accesses per lane: a row goes to the fewest waves (1, 2 or 4) that keep
+// it within kNvLane<T, E> accesses per lane -- about 64 VGPRs of row data,
+// which leaves room for 8 waves per SIMD (measured on 4096-wide float16
+// rows: two waves of 4 vectors per lane 6.1 TB/s, one wave of 8 vectors
+// 5.7 TB/s) -- and rows wider than four waves' worth go to four waves with
+// up to 16 accesses per lane (32 for scalars).
+template <typename T, int E> constexpr int kNvLane = E * sizeof(T) >= 16 ? 4 : E * sizeof(T) == 8 ? 8 : 16;
 template <int E> constexpr int kMaxNvRowBlock = E == 1 ? 32 : 16;
 
-// Rows of E-element accesses: one wave per row, else four waves per row.
 template <typename T, int E>
 hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char** route) {
-    static const char* const kNames[2][4] = {
+    static const char* const kNames[3][4] = {
         {"ssln.wave.scalar", "ssln.wave.vec4", "ssln.wave.vec8", "ssln.wave.vec16"},
+        {"ssln.wave2.scalar", "ssln.wave2.vec4", "ssln.wave2.vec8", "ssln.wave2.vec16"},
         {"ssln.rowblock.scalar", "ssln.rowblock.vec4", "ssln.rowblock.vec8", "ssln.rowblock.vec16"}};
     constexpr int kName = E == 1 ? 0 : E * sizeof(T) == 16 ? 3 : E * sizeof(T) == 8 ? 2 : 1;
+    constexpr int NVL = kNvLane<T, E>;
     const int64_t nvec = a.hidden / E;
-    if (nvec <= 64 * kMaxNvWave<T, E>) {
+    if (nvec <= 64 * NVL) {
         *route = kNames[0][kName];
-        return launch_wave<T, E, kMaxNvWave<T, E>, 1>(a, int(nvec), stream);
+        return launch_wave<T, E, NVL, 1>(a, int(nvec), stream);
     }
-    *route = kNames[1][kName];
+    if (nvec <= 128 * NVL) {
+        *route = kNames[1][kName];
+        return launch_wave<T, E, NVL, 2>(a, int(nvec), stream);
+    }
+    *route = kNames[2][kName];
     return launch_wave<T, E, kMaxNvRowBlock<E>, 4>(a, int(nvec), stream);
 }
 

@@ -39,7 +39,7 @@ def test_ssln_beyond_2_31_elements():
     k = gen((rows, hidden), torch.float16, 2)
     gamma = (torch.rand(hidden, device="cuda", generator=torch.Generator(device="cuda").manual_seed(3)) + 0.5).half()
     out = gn.skip_rms_norm(x, k, gamma, None, 1e-6, want_inv_std_var=True, want_sum=True)
-    assert gn.last_route() == "ssln.wave.vec16"
+    assert gn.last_route() == "ssln.wave2.vec16"
     torch.cuda.synchronize()
     sample = np.array([0, 1, TWO31 // hidden - 1, TWO31 // hidden, rows - 2, rows - 1])
     idx = torch.from_numpy(sample).cuda()

@@ -56,7 +56,7 @@ SHAPES = [
     ((2, 10000), F32, False),    # float32 four waves per row, ragged
     ((2, 40000), F16, True),     # wider than any register-resident route: block route
     ((7, 4100), F16, True),      # 8-byte vectors, 1025 of them: four waves per row
-    ((5, 4092), F16, True),      # 8-byte vectors, one wave per row
+    ((5, 4092), F16, True),      # 8-byte vectors, two waves per row (odd row count)
     ((5, 4098), F16, False),     # 4-byte vectors, 2049 of them: four waves per row
     ((3, 2046), F16, True),      # 4-byte vectors, one wave per row
     ((4, 4097), F16, False),     # odd width: scalars, four waves per row
@@ -72,8 +72,11 @@ def expected_route(shape, dt):
     E = width // size
     name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
     nvec = hidden // E
-    if nvec <= 64 * (32 if E == 1 or (width == 16 and size == 4) else 16):
+    per_lane = 4 if E > 1 and width == 16 else 8 if E > 1 and width == 8 else 16
+    if nvec <= 64 * per_lane:
         return f"ssln.wave.{name}"
+    if nvec <= 128 * per_lane:
+        return f"ssln.wave2.{name}"
     if nvec <= 256 * (32 if E == 1 else 16):
         return f"ssln.rowblock.{name}"
     return "ssln.block"
@@ -103,8 +106,8 @@ def test_optional_outputs_do_not_change_output(dt, hidden, want):
     assert_bitwise(to_host(out.output), to_host(base.output), "output with/without optional outputs")
 
 
-@pytest.mark.parametrize("offset,route", [(1, "ssln.rowblock.scalar"), (2, "ssln.rowblock.vec4"),
-                                          (4, "ssln.wave.vec8")])
+@pytest.mark.parametrize("offset,route", [(1, "ssln.rowblock.scalar"), (2, "ssln.wave2.vec4"),
+                                          (4, "ssln.wave2.vec8")])
 def test_base_alignment_picks_the_vector_width(offset, route):
     """Views `offset` halves into their buffers: 2-, 4- and 8-byte aligned
     bases take scalar, 4-byte and 8-byte accesses, with the same results."""

@@ -45,7 +45,7 @@ def test_ssln_f16_16x2048x4096_sampled():
     eps = w.attrs["epsilon"]
     out = gn.skip_rms_norm(to_dev(x["input"]), to_dev(x["skip"]), to_dev(x["gamma"]), None, eps,
                            want_sum=True)
-    assert gn.last_route() == "ssln.wave.vec16"
+    assert gn.last_route() == "ssln.wave2.vec16"
     y = to_host(out.output).reshape(-1, 4096)
     s = to_host(out.input_skip_bias_sum).reshape(-1, 4096)
     inp, skp = x["input"].reshape(-1, 4096), x["skip"].reshape(-1, 4096)
