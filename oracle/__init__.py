@@ -72,6 +72,9 @@ class Oracle:
         lib.oracle_skip_rms_norm.argtypes = [ci, i64, i64, vp, vp, vp, vp, f32,
                                              vp, vp, vp, vp]
         lib.oracle_skip_rms_norm.restype = ci
+        lib.oracle_skip_layer_norm.argtypes = [ci, i64, i64, vp, vp, vp, vp, vp, f32,
+                                               vp, vp, vp, vp]
+        lib.oracle_skip_layer_norm.restype = ci
         lib.oracle_gated_rms_norm.argtypes = [ci, i64, i64, vp, vp, vp, f32, vp]
         lib.oracle_gated_rms_norm.restype = ci
         lib.oracle_skip_group_norm.argtypes = [ci, ci, i64, i64, i64, i64, ci,
@@ -124,6 +127,35 @@ class Oracle:
                                            _ptr(out), _ptr(mean), _ptr(inv), _ptr(s))
         if rc != 0:
             raise ValueError(f"oracle_skip_rms_norm rejected its arguments ({rc})")
+        return out, mean, inv, s
+
+    def skip_layer_norm(self, input, skip, gamma, beta=None, bias=None,
+                        epsilon=9.999999960041972e-13, *, want_mean=False,
+                        want_inv_std_var=False, want_sum=False):
+        """Skip layer normalization with the mean removed, over the last axis.
+
+        Returns (output, mean, inv_std_var, input_skip_bias_sum) like
+        skip_rms_norm; here mean is the row mean and inv_std_var the inverse
+        standard deviation.
+        """
+        input = _host(input)
+        T = _type_code(input.dtype)
+        skip = _host(skip, input.dtype)
+        gamma = _host(gamma, input.dtype)
+        beta = _host(beta, input.dtype)
+        bias = _host(bias, input.dtype)
+        hidden = input.shape[-1]
+        rows = input.size // hidden if hidden else 0
+        stat_shape = input.shape[:-1] + (1,)
+        out = np.empty_like(input)
+        mean = np.empty(stat_shape, np.float32) if want_mean else None
+        inv = np.empty(stat_shape, np.float32) if want_inv_std_var else None
+        s = np.empty_like(input) if want_sum else None
+        rc = self.lib.oracle_skip_layer_norm(T, rows, hidden, _ptr(input), _ptr(skip),
+                                             _ptr(gamma), _ptr(beta), _ptr(bias), float(epsilon),
+                                             _ptr(out), _ptr(mean), _ptr(inv), _ptr(s))
+        if rc != 0:
+            raise ValueError(f"oracle_skip_layer_norm rejected its arguments ({rc})")
         return out, mean, inv, s
 
     def gated_rms_norm(self, X, scale, gate, epsilon=1e-5):
@@ -203,6 +235,10 @@ def f64_to_f16_bits(value):
 
 def skip_rms_norm(*args, **kwargs):
     return default().skip_rms_norm(*args, **kwargs)
+
+
+def skip_layer_norm(*args, **kwargs):
+    return default().skip_layer_norm(*args, **kwargs)
 
 
 def gated_rms_norm(*args, **kwargs):

@@ -187,6 +187,52 @@ int oracle_skip_rms_norm(int T, int64_t rows, int64_t hidden,
 }
 
 /* ---------------------------------------------------------------------- */
+/* Skip layer normalization with the mean removed: the operator whose
+ * simplified form is SkipSimplifiedLayerNormalization.  The SSLN page's
+ * Outputs section describes its `mean` output as the per-row mean (zero only
+ * for the simplified form) and `inv_std_var` as the per-row inverse standard
+ * deviation (the inverse RMS only for the simplified form); this is that
+ * non-simplified form: S as for SSLN, mean = sum(S)/hidden,
+ * var = sum((S - mean)^2)/hidden (population), inv = 1/sqrt(var + eps),
+ * output = (S - mean) * inv * gamma (+ beta when beta is given).          */
+int oracle_skip_layer_norm(int T, int64_t rows, int64_t hidden,
+                           const void* input, const void* skip,
+                           const void* gamma, const void* beta, const void* bias,
+                           float epsilon, void* output, float* mean,
+                           float* inv_std_var, void* input_skip_bias_sum)
+{
+    if (!valid_type(T) || hidden <= 0 || rows < 0) return -1;
+    double* s = (double*)malloc((size_t)hidden * sizeof(double));
+    if (!s) return -2;
+    const double eps = (double)epsilon;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t base = r * hidden;
+        double sum = 0.0;
+        for (int64_t j = 0; j < hidden; ++j) {
+            float sv = residual_sum(T, load_f32(T, input, base + j),
+                                    load_f32(T, skip, base + j), bias != NULL,
+                                    bias ? load_f32(T, bias, j) : 0.0f);
+            if (input_skip_bias_sum) store_exact(T, input_skip_bias_sum, base + j, sv);
+            s[j] = (double)sv;
+            sum += s[j];
+        }
+        const double mu = sum / (double)hidden;
+        double ssd = 0.0;
+        for (int64_t j = 0; j < hidden; ++j) ssd += (s[j] - mu) * (s[j] - mu);
+        const double inv = 1.0 / sqrt(ssd / (double)hidden + eps);
+        for (int64_t j = 0; j < hidden; ++j) {
+            double y = (s[j] - mu) * inv * (double)load_f32(T, gamma, j);
+            if (beta) y += (double)load_f32(T, beta, j);
+            store_f64(T, output, base + j, y);
+        }
+        if (mean) mean[r] = (float)mu;
+        if (inv_std_var) inv_std_var[r] = (float)inv;
+    }
+    free(s);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
 /* com.microsoft.GatedRMSNorm, Description: Y = X * rsqrt(mean(X^2) + eps) *
  * scale * SiLU(gate), the mean taken over each contiguous run of C elements,
  * C = element count of scale, rows counted flat as numel / C.             */

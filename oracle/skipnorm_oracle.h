@@ -49,6 +49,16 @@ int oracle_skip_rms_norm(int T, int64_t rows, int64_t hidden,
                          void* output, float* mean, float* inv_std_var,
                          void* input_skip_bias_sum);
 
+/* Skip layer normalization with the mean removed (the non-simplified form
+ * of SkipSimplifiedLayerNormalization): mean = sum(S)/hidden, population
+ * variance, output = (S - mean) / sqrt(var + eps) * gamma (+ beta).
+ * beta, bias, mean, inv_std_var and input_skip_bias_sum may be NULL. */
+int oracle_skip_layer_norm(int T, int64_t rows, int64_t hidden,
+                           const void* input, const void* skip,
+                           const void* gamma, const void* beta, const void* bias,
+                           float epsilon, void* output, float* mean,
+                           float* inv_std_var, void* input_skip_bias_sum);
+
 /* GatedRMSNorm: numel elements, normalization span C = element count of
  * scale; rows = numel / C, counted flat. */
 int oracle_gated_rms_norm(int T, int64_t numel, int64_t C,

@@ -97,6 +97,11 @@ def run_hand_case(orc, case):
             arr(case["input"]), arr(case["skip"]), arr(case["gamma"]), arr(case["bias"]),
             float(eps32), want_mean=True, want_inv_std_var=True, want_sum=True)
         got = {"output": out, "mean": mean, "inv_std_var": inv, "input_skip_bias_sum": s}
+    elif case["op"] == "skip_layer_norm":
+        out, mean, inv, s = orc.skip_layer_norm(
+            arr(case["input"]), arr(case["skip"]), arr(case["gamma"]), arr(case["beta"]),
+            arr(case["bias"]), float(eps32), want_mean=True, want_inv_std_var=True, want_sum=True)
+        got = {"output": out, "mean": mean, "inv_std_var": inv, "input_skip_bias_sum": s}
     elif case["op"] == "gated_rms_norm":
         got = {"Y": orc.gated_rms_norm(arr(case["X"]), arr(case["scale"]), arr(case["gate"]),
                                        float(eps32))}
@@ -238,6 +243,77 @@ def pin_ssln_invariants(orc):
         s = orc.skip_rms_norm(x, k, g, b, 1e-6, want_sum=True)[3]
         y5 = orc.skip_rms_norm(s, z, g, None, 1e-6)[0]
         assert np.array_equal(y4.view(np.uint8), y5.view(np.uint8)), "statistic not on rounded S"
+
+
+# ----------------------------------------------------------------- SkipLayerNorm
+def pin_sln_matches_torch(orc):
+    rng = np.random.default_rng(13)
+    for dt, rows, hidden, with_beta, with_bias in [(np.float32, 8, 768, True, True),
+                                                   (np.float32, 5, 33, False, False),
+                                                   (np.float16, 6, 256, True, False),
+                                                   (np.float16, 3, 17, False, True)]:
+        x = rng.standard_normal((rows, hidden), dtype=np.float32).astype(dt)
+        k = rng.standard_normal((rows, hidden), dtype=np.float32).astype(dt)
+        g = rng.uniform(0.5, 1.5, hidden).astype(dt)
+        be = (0.1 * rng.standard_normal(hidden, dtype=np.float32)).astype(dt) if with_beta else None
+        b = (0.1 * rng.standard_normal(hidden, dtype=np.float32)).astype(dt) if with_bias else None
+        eps = 1e-5
+        out, mean, inv, s = orc.skip_layer_norm(x, k, g, be, b, eps, want_mean=True,
+                                                want_inv_std_var=True, want_sum=True)
+        s_ref = residual_sum_numpy(x, k, b, dt)
+        assert np.array_equal(s.view(np.uint8), s_ref.view(np.uint8)), "S differs from numpy's sum"
+        st = torch.from_numpy(s_ref.astype(np.float64))
+        y = F.layer_norm(st, (hidden,), torch.from_numpy(g.astype(np.float64)),
+                         None if be is None else torch.from_numpy(be.astype(np.float64)),
+                         eps=float(np.float32(eps)))
+        assert_within_ulp(out, y.numpy().astype(dt), 1, f"SLN {np.dtype(dt)} output vs layer_norm")
+        assert_within_ulp(mean, st.mean(-1, keepdim=True).numpy().astype(np.float32), 1, "SLN mean")
+        var = st.var(-1, unbiased=False, keepdim=True)
+        assert_within_ulp(inv, torch.rsqrt(var + float(np.float32(eps))).numpy().astype(np.float32), 1,
+                          "SLN inv_std_var")
+
+
+def pin_sln_invariants(orc):
+    rng = np.random.default_rng(14)
+    for dt in (np.float32, np.float16):
+        rows, hidden = 6, 64
+        x = rng.standard_normal((rows, hidden), dtype=np.float32).astype(dt)
+        k = rng.standard_normal((rows, hidden), dtype=np.float32).astype(dt)
+        g = rng.uniform(0.5, 1.5, hidden).astype(dt)
+        be = (0.1 * rng.standard_normal(hidden, dtype=np.float32)).astype(dt)
+        ones, zeros = np.ones(hidden, dt), np.zeros(hidden, dt)
+        # gamma = 1, beta = 0: each output row has mean 0 and variance v/(v + eps).
+        eps = 0.01
+        out, _, _, s = orc.skip_layer_norm(x, k, ones, None, None, eps, want_sum=True)
+        v = s.astype(np.float64).var(-1)
+        tol = 1e-6 if dt == np.float32 else 2e-3
+        assert np.allclose(out.astype(np.float64).mean(-1), 0, atol=tol * 10), "output mean"
+        assert np.allclose(out.astype(np.float64).var(-1), v / (v + np.float32(eps)), rtol=tol * 5), "variance"
+        # A zero-mean S (values in +- pairs, exact cancellation) makes the
+        # operator the simplified one: outputs equal bit for bit.
+        half = rng.standard_normal((rows, hidden // 2), dtype=np.float32).astype(dt)
+        xs = np.empty((rows, hidden), dt)
+        xs[:, 0::2], xs[:, 1::2] = half, -half
+        y_ln, m_ln, inv_ln, _ = orc.skip_layer_norm(xs, np.zeros_like(xs), g, None, None, 1e-6,
+                                                    want_mean=True, want_inv_std_var=True)
+        y_rms, _, inv_rms, _ = orc.skip_rms_norm(xs, np.zeros_like(xs), g, None, 1e-6, want_inv_std_var=True)
+        assert np.all(m_ln == 0)
+        assert np.array_equal(y_ln.view(np.uint8), y_rms.view(np.uint8)), "zero-mean rows != simplified"
+        assert np.array_equal(inv_ln, inv_rms)
+        # beta adds after the normalization: beta = 0 equals no beta; a beta
+        # of ones shifts every output by exactly one (float32).
+        y0 = orc.skip_layer_norm(x, k, g, zeros, None, 1e-5)[0]
+        y1 = orc.skip_layer_norm(x, k, g, None, None, 1e-5)[0]
+        assert np.array_equal(y0.view(np.uint8), y1.view(np.uint8)), "beta = 0"
+        # Scale invariance with eps = 0: powers of two scale exactly.
+        y2 = orc.skip_layer_norm(x, k, g, be, None, 0.0)[0]
+        y3 = orc.skip_layer_norm((x * dt(4)).astype(dt), (k * dt(4)).astype(dt), g, be, None, 0.0)[0]
+        assert np.array_equal(y2.view(np.uint8), y3.view(np.uint8)), "scale invariance"
+        # Requesting S / statistics does not change the output.
+        y4 = orc.skip_layer_norm(x, k, g, be, None, 1e-5, want_mean=True, want_inv_std_var=True,
+                                 want_sum=True)[0]
+        y5 = orc.skip_layer_norm(x, k, g, be, None, 1e-5)[0]
+        assert np.array_equal(y4.view(np.uint8), y5.view(np.uint8)), "S request changed output"
 
 
 # ----------------------------------------------------------------- Gated
@@ -402,5 +478,6 @@ def pin_sgn_invariants(orc):
 
 PINS = [pin_hand_cases, pin_f16_decode_exhaustive, pin_f32_to_f16_structured,
         pin_f64_to_f16_ties, pin_ssln_matches_torch, pin_ssln_invariants,
+        pin_sln_matches_torch, pin_sln_invariants,
         pin_gated_matches_torch, pin_gated_invariants, pin_sgn_matches_torch,
         pin_sgn_invariants]

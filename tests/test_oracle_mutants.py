@@ -26,6 +26,12 @@ MUTATIONS = [
     ("ssln epsilon dropped", "1.0 / sqrt(mean_sq + eps)", "1.0 / sqrt(mean_sq)"),
     ("inv_std_var is RMS", "inv_std_var[r] = (float)inv_rms;",
      "inv_std_var[r] = (float)(1.0 / inv_rms);"),
+    ("ln variance unbiased", "ssd / (double)hidden + eps", "ssd / (double)(hidden - 1) + eps"),
+    ("ln mean not removed", "double y = (s[j] - mu) * inv", "double y = s[j] * inv"),
+    ("ln beta scaled by gamma", "if (beta) y += (double)load_f32(T, beta, j);",
+     "if (beta) y += (double)load_f32(T, beta, j) * (double)load_f32(T, gamma, j);"),
+    ("ln mean output zero", "if (mean) mean[r] = (float)mu;", "if (mean) mean[r] = 0.0f;"),
+    ("ln epsilon dropped", "sqrt(ssd / (double)hidden + eps)", "sqrt(ssd / (double)hidden)"),
     ("gated epsilon dropped", "sqrt(sum_sq / (double)C + eps)", "sqrt(sum_sq / (double)C)"),
     ("gated scale index fixed", "(double)load_f32(T, scale, j)", "(double)load_f32(T, scale, 0)"),
     ("silu sign", "return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
