@@ -117,7 +117,7 @@ class Op:
     """One workload's device tensors and a closure that enqueues the op."""
 
     def __init__(self, name, torch, gn, workloads):
-        w = workloads.WORKLOADS[name]
+        w = workloads.WORKLOADS.get(name) or workloads.EXTRA_WORKLOADS[name]
         self.name = name
         self.bytes = workloads.io_bytes(w)
         host = workloads.generate(w)
@@ -130,6 +130,10 @@ class Op:
             self.run = lambda: gn.skip_rms_norm(d["input"], d["skip"], d["gamma"], d.get("bias"),
                                                 a["epsilon"], want_sum=want_sum,
                                                 want_inv_std_var=want_inv)
+        elif w.op == "skip_layer_norm":
+            want_sum = "input_skip_bias_sum" in w.outputs
+            self.run = lambda: gn.skip_layer_norm(d["input"], d["skip"], d["gamma"], d.get("beta"),
+                                                  d.get("bias"), a["epsilon"], want_sum=want_sum)
         elif w.op == "gated_rms_norm":
             self.run = lambda: gn.gated_rms_norm(d["X"], d["scale"], d["gate"], a["epsilon"])
         else:
@@ -299,6 +303,33 @@ def main():
     for v in per_op.values():
         v["frac_of_copy"] = round(v["gbps"] / copy_gbps, 4)
 
+    # Beyond the step: the non-simplified skip layer normalization at the
+    # large SSLN shape, timed alone (its 1 GB per call keeps it cold).
+    next_ops = {}
+    for name in workloads.EXTRA_WORKLOADS:
+        o = Op(name, torch, gn, workloads)
+        for _ in range(args.warmup):
+            o.run()
+        pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+        for e0, e1 in pairs:
+            hev.record(e0, stream)
+            o.run()
+            hev.record(e1, stream)
+        torch.cuda.synchronize()
+        ms = [hev.elapsed_ms(e0, e1) for e0, e1 in pairs]
+        for e0, e1 in pairs:
+            hev.destroy(e0)
+            hev.destroy(e1)
+        avg = float(np.mean(ms))
+        gbps = o.bytes / (avg * 1e-3) / 1e9
+        next_ops[name] = {"bytes": o.bytes, "avg_us": round(avg * 1e3, 3),
+                          "median_us": round(float(np.median(ms)) * 1e3, 3),
+                          "min_us": round(float(np.min(ms)) * 1e3, 3),
+                          "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 3),
+                          "gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4),
+                          "frac_of_copy": round(gbps / copy_gbps, 4)}
+        del o
+
     dom = per_op[DOMINANT]
     achieved = dom["bytes"] / (dom["avg_us"] * 1e-6) / 1e9
     traffic = load_traffic()
@@ -321,6 +352,7 @@ def main():
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": DOMINANT_KERNEL, "workload": DOMINANT},
         "ops": per_op,
+        "next_ops": next_ops,
         "copy_ceiling_gbps": round(copy_gbps, 1),
     }
     if not args.no_cpu_baseline:

@@ -22,7 +22,7 @@ import torch
 
 from ._lib import SN_BF16, SN_F16, SN_F32, SkipNormError, check, lib
 
-__all__ = ["skip_rms_norm", "gated_rms_norm", "skip_group_norm", "skip_group_norm_workspace_size",
+__all__ = ["skip_layer_norm", "skip_rms_norm", "gated_rms_norm", "skip_group_norm", "skip_group_norm_workspace_size",
            "SkipRmsNormOutputs", "SkipGroupNormOutputs", "SkipNormError", "force_route",
            "last_route", "exchange_timeout_us", "abi_version", "copy_"]
 
@@ -111,6 +111,39 @@ def skip_rms_norm(input: torch.Tensor, skip: torch.Tensor, gamma: torch.Tensor,
         check(lib().skip_rms_norm(T, rows, hidden, _ptr(input), _ptr(skip), _ptr(gamma),
                                   _ptr(bias), float(epsilon), _ptr(output), _ptr(mean),
                                   _ptr(inv), _ptr(s), _stream(dev)))
+    return SkipRmsNormOutputs(output, mean, inv, s)
+
+
+def skip_layer_norm(input: torch.Tensor, skip: torch.Tensor, gamma: torch.Tensor,
+                    beta: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                    epsilon: float = SSLN_EPSILON, *, want_mean: bool = False,
+                    want_inv_std_var: bool = False, want_sum: bool = False) -> SkipRmsNormOutputs:
+    """Skip layer normalization with the row mean removed (the non-simplified
+    form of SkipSimplifiedLayerNormalization): output = (S - mean) *
+    inv_std_var * gamma (+ beta).  Arguments and outputs as skip_rms_norm,
+    plus beta (hidden,); mean and inv_std_var are the row mean and inverse
+    standard deviation."""
+    if input.dim() not in (2, 3):
+        raise ValueError(f"input must have rank 2 or 3, got shape {tuple(input.shape)}")
+    if skip.shape != input.shape:
+        raise ValueError(f"skip shape {tuple(skip.shape)} != input shape {tuple(input.shape)}")
+    hidden = input.shape[-1]
+    for name, t in (("gamma", gamma), ("beta", beta), ("bias", bias)):
+        if t is not None and tuple(t.shape) != (hidden,):
+            raise ValueError(f"{name} must have shape ({hidden},), got {tuple(t.shape)}")
+    _same_dtype(input, "skip_layer_norm", skip, gamma, beta, bias)
+    dev = _device_of(input, skip, gamma, beta, bias)
+    T = _code(input, "skip_layer_norm")
+    rows = input.numel() // hidden if hidden else 0
+    output = torch.empty_like(input)
+    stat_shape = tuple(input.shape[:-1]) + (1,)
+    mean = torch.empty(stat_shape, dtype=torch.float32, device=dev) if want_mean else None
+    inv = torch.empty(stat_shape, dtype=torch.float32, device=dev) if want_inv_std_var else None
+    s = torch.empty_like(input) if want_sum else None
+    with torch.cuda.device(dev):
+        check(lib().skip_layer_norm(T, rows, hidden, _ptr(input), _ptr(skip), _ptr(gamma),
+                                    _ptr(beta), _ptr(bias), float(epsilon), _ptr(output),
+                                    _ptr(mean), _ptr(inv), _ptr(s), _stream(dev)))
     return SkipRmsNormOutputs(output, mean, inv, s)
 
 

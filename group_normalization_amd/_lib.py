@@ -22,6 +22,8 @@ _vp, _i64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
 _ci = ctypes.c_int
 SIGNATURES = {
     "skip_rms_norm": (_ci, [_ci, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp]),
+    "skip_layer_norm": (_ci, [_ci, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp,
+                              _vp]),
     "gated_rms_norm": (_ci, [_ci, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp]),
     "skip_group_norm_workspace_size": (_ci, [_ci, _i64, _i64, _i64, _i64, _i64, _i32,
                                              ctypes.POINTER(_sz)]),

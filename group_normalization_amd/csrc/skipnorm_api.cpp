@@ -117,37 +117,64 @@ constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1; // rows; blocks of one laun
 
 extern "C" {
 
-sn_status skip_rms_norm(sn_dtype T, int64_t rows, int64_t hidden, const void* input,
-                        const void* skip, const void* gamma, const void* bias, float epsilon,
-                        void* output, float* mean, float* inv_std_var,
-                        void* input_skip_bias_sum, hipStream_t stream) {
-    SN_TRY(check_dtype(T, "skip_rms_norm T"));
+}  // extern "C"
+
+namespace {
+
+// Both row normalizations share validation and kernels; `center` removes the
+// row mean (skip_layer_norm).
+sn_status row_norm(const char* op, bool center, sn_dtype T, int64_t rows, int64_t hidden,
+                   const void* input, const void* skip, const void* gamma, const void* beta,
+                   const void* bias, float epsilon, void* output, float* mean,
+                   float* inv_std_var, void* input_skip_bias_sum, hipStream_t stream) {
+    SN_TRY(check_dtype(T, op));
     if (rows < 0 || hidden < 1 || hidden > kMaxRowElems)
-        return fail(SN_ERR_SHAPE, "skip_rms_norm: need rows >= 0 and 1 <= hidden <= 2^30 (got %lld, %lld)",
+        return fail(SN_ERR_SHAPE, "%s: need rows >= 0 and 1 <= hidden <= 2^30 (got %lld, %lld)", op,
                     (long long)rows, (long long)hidden);
     int64_t numel;
     if (mul_overflows(rows, hidden, &numel) || numel > kMaxElems || rows > kMaxRows)
-        return fail(SN_ERR_SHAPE, "skip_rms_norm: rows * hidden too large (rows < 2^31, elements <= 2^46)");
+        return fail(SN_ERR_SHAPE, "%s: rows * hidden too large (rows < 2^31, elements <= 2^46)", op);
     SN_TRY(check_epsilon(epsilon));
-    if (!gamma) return fail(SN_ERR_NULL, "skip_rms_norm: gamma is required");
+    if (!gamma) return fail(SN_ERR_NULL, "%s: gamma is required", op);
     if (numel > 0 && (!input || !skip || !output))
-        return fail(SN_ERR_NULL, "skip_rms_norm: input, skip and output are required");
+        return fail(SN_ERR_NULL, "%s: input, skip and output are required", op);
 
     const size_t es = elem_size(T);
     const size_t tb = size_t(numel) * es;
     const Span ins[] = {span_of("input", input, tb), span_of("skip", skip, tb),
                         span_of("gamma", gamma, size_t(hidden) * es),
-                        span_of("bias", bias, size_t(hidden) * es)};
+                        span_of("bias", bias, size_t(hidden) * es),
+                        span_of("beta", beta, size_t(hidden) * es)};
     const Span outs[] = {span_of("output", output, tb),
                          span_of("mean", mean, size_t(rows) * 4),
                          span_of("inv_std_var", inv_std_var, size_t(rows) * 4),
                          span_of("input_skip_bias_sum", input_skip_bias_sum, tb)};
-    SN_TRY(check_alias(outs, 4, ins, 4));
+    SN_TRY(check_alias(outs, 4, ins, 5));
 
-    sn::SslnArgs a{T == SN_F32 ? 0 : 1, rows, hidden, input, skip, gamma, bias, epsilon,
-                   output, mean, inv_std_var, input_skip_bias_sum};
+    sn::SslnArgs a{T == SN_F32 ? 0 : 1, rows, hidden, input, skip, gamma, beta, bias, epsilon,
+                   output, mean, inv_std_var, input_skip_bias_sum, center};
     const char* route = "";
-    return finish_launch(sn::launch_ssln(a, current_route(), stream, &route), route, "skip_rms_norm");
+    return finish_launch(sn::launch_ssln(a, current_route(), stream, &route), route, op);
+}
+
+}  // namespace
+
+extern "C" {
+
+sn_status skip_rms_norm(sn_dtype T, int64_t rows, int64_t hidden, const void* input,
+                        const void* skip, const void* gamma, const void* bias, float epsilon,
+                        void* output, float* mean, float* inv_std_var,
+                        void* input_skip_bias_sum, hipStream_t stream) {
+    return row_norm("skip_rms_norm", false, T, rows, hidden, input, skip, gamma, nullptr, bias,
+                    epsilon, output, mean, inv_std_var, input_skip_bias_sum, stream);
+}
+
+sn_status skip_layer_norm(sn_dtype T, int64_t rows, int64_t hidden, const void* input,
+                          const void* skip, const void* gamma, const void* beta, const void* bias,
+                          float epsilon, void* output, float* mean, float* inv_std_var,
+                          void* input_skip_bias_sum, hipStream_t stream) {
+    return row_norm("skip_layer_norm", true, T, rows, hidden, input, skip, gamma, beta, bias,
+                    epsilon, output, mean, inv_std_var, input_skip_bias_sum, stream);
 }
 
 sn_status gated_rms_norm(sn_dtype T, int64_t numel, int64_t span, const void* X,

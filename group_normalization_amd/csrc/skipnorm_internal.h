@@ -11,14 +11,17 @@ namespace sn {
 enum class Route { Auto = 0, Scalar = 1, Vector = 2, Block = 3, Split = 4 };
 
 // ---------------------------------------------------------------- SSLN
+// Also the non-simplified form (center = true: the row mean is removed and
+// beta, if given, added).
 struct SslnArgs {
     int dtype;  // 0 = float32, 1 = float16
     int64_t rows, hidden;
-    const void *input, *skip, *gamma, *bias;
+    const void *input, *skip, *gamma, *beta, *bias;
     float epsilon;
     void* output;
     float *mean, *inv_std_var;
     void* sum;
+    bool center;
 };
 // Enqueues the op; *route receives the name of the kernel family used.
 hipError_t launch_ssln(const SslnArgs& a, Route want, hipStream_t stream, const char** route);

@@ -36,11 +36,13 @@ constexpr int kWavesPerBlock = 4;
 
 // WPR waves per row: 1, 2 or 4 (four, two or one rows per 256-thread
 // block).  Lane l of the row's 64*WPR lanes holds vectors l, l + 64*WPR, ...
-template <typename T, int E, int NV, bool FULL, int WPR>
+// CENTER: remove the row mean (skip layer normalization) instead of the
+// simplified root-mean-square form.
+template <typename T, int E, int NV, bool FULL, int WPR, bool CENTER>
 __global__ void __launch_bounds__(256)
 ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
-                 const T* __restrict__ gamma, const T* __restrict__ bias,
-                 T* __restrict__ output, float* __restrict__ mean,
+                 const T* __restrict__ gamma, const T* __restrict__ beta,
+                 const T* __restrict__ bias, T* __restrict__ output, float* __restrict__ mean,
                  float* __restrict__ inv_std_var, T* __restrict__ sum,
                  int64_t rows, int nvec, float hidden_f, float eps) {
     using V = Vec<T, E>;
@@ -56,6 +58,17 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     const int64_t row = live ? my_row : rows - 1;
     const int64_t base = row * nvec;
     const bool has_bias = bias != nullptr;
+
+    // With the mean removed, everything is taken about the row's first
+    // element S[0] (every lane forms it from the same inputs, bit for bit):
+    // S - S[0] is exact for nearby values and the mean of the differences is
+    // small, so rows far from zero keep their accuracy in float32.
+    float shift = 0.0f;
+    if constexpr (CENTER) {
+        T rounded;
+        shift = residual_sum<T>(to_f32(input[row * nvec * E]), to_f32(skip[row * nvec * E]), has_bias,
+                                has_bias ? to_f32(bias[0]) : 0.0f, rounded);
+    }
 
     // Issue every load of the row before any arithmetic.  No load sits behind
     // a lane-dependent branch (that makes the compiler wait for each one in
@@ -80,74 +93,138 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
             for (int e = 0; e < E; ++e) {
                 const float s = residual_sum<T>(to_f32(xs[v].v[e]), to_f32(ks[v].v[e]), has_bias,
                                                 to_f32(bv.v[e]), ss[v].v[e]);
-                acc = fmaf_(s, s, acc);
+                if constexpr (CENTER) acc += s - shift;
+                else acc = fmaf_(s, s, acc);
             }
             if (sum && live) store_vec_stream<T, E>(sum, base + idx, ss[v]);
         }
     }
 
-    float total = segment_sum<64>(acc);
-    if constexpr (WPR > 1) {
-        if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = total;
-        __syncthreads();
-        const int w0 = (threadIdx.x / LANES) * WPR;  // the row's first wave
-        total = wave_part[w0];
+    // Row total of the lanes' partial sums: butterfly inside the wave, then
+    // the row's waves in order through LDS.
+    auto row_total = [&](float part) {
+        float total = segment_sum<64>(part);
+        if constexpr (WPR > 1) {
+            __syncthreads();  // earlier readers of wave_part are done
+            if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = total;
+            __syncthreads();
+            const int w0 = (threadIdx.x / LANES) * WPR;  // the row's first wave
+            total = wave_part[w0];
 #pragma unroll
-        for (int w = 1; w < WPR; ++w) total += wave_part[w0 + w];
+            for (int w = 1; w < WPR; ++w) total += wave_part[w0 + w];
+        }
+        return total;
+    };
+    // Simplified: r = 1/sqrt(mean(S^2) + eps), no centre.  With the mean
+    // removed: md = mean(S - S[0]) (the mean is S[0] + md), then the squared
+    // deviations from the S held in registers (a second pass over registers,
+    // not memory).
+    float md = 0.0f, r;
+    if constexpr (!CENTER) {
+        r = inv_sqrt(row_total(acc) / hidden_f + eps);
+    } else {
+        md = row_total(acc) / hidden_f;
+        float dev = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int idx = v * LANES + lane;
+            if (FULL || idx < nvec) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = (to_f32(ss[v].v[e]) - shift) - md;
+                    dev = fmaf_(d, d, dev);
+                }
+            }
+        }
+        r = inv_sqrt(row_total(dev) / hidden_f + eps);
     }
-    const float r = inv_sqrt(total / hidden_f + eps);
     if (live && lane == 0) {
         if (inv_std_var) inv_std_var[row] = r;
-        if (mean) mean[row] = 0.0f;
+        if (mean) mean[row] = shift + md;
     }
 
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int idx = v * LANES + lane;
         const V gv = load_vec<T, E>(gamma, clamp(idx));
+        V bt = {};
+        if (CENTER && beta) bt = load_vec<T, E>(beta, clamp(idx));
         V out;
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            out.v[e] = from_f32<T>(to_f32(ss[v].v[e]) * r * to_f32(gv.v[e]));
+        for (int e = 0; e < E; ++e) {
+            if constexpr (CENTER) {
+                float y = ((to_f32(ss[v].v[e]) - shift) - md) * r * to_f32(gv.v[e]);
+                if (beta) y = y + to_f32(bt.v[e]);
+                out.v[e] = from_f32<T>(y);
+            } else {
+                out.v[e] = from_f32<T>(to_f32(ss[v].v[e]) * r * to_f32(gv.v[e]));
+            }
+        }
         if ((FULL || idx < nvec) && live) store_vec_stream<T, E>(output, base + idx, out);
     }
 }
 
-template <typename T>
+template <typename T, bool CENTER>
 __global__ void __launch_bounds__(256)
 ssln_block_kernel(const T* __restrict__ input, const T* __restrict__ skip,
-                  const T* __restrict__ gamma, const T* __restrict__ bias,
-                  T* __restrict__ output, float* __restrict__ mean,
+                  const T* __restrict__ gamma, const T* __restrict__ beta,
+                  const T* __restrict__ bias, T* __restrict__ output, float* __restrict__ mean,
                   float* __restrict__ inv_std_var, T* __restrict__ sum,
                   int64_t rows, int64_t hidden, float hidden_f, float eps) {
     __shared__ float wave_part[kWavesPerBlock];
     const bool has_bias = bias != nullptr;
     const int t = threadIdx.x;
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const int64_t base = row * hidden;
-        float acc = 0.0f;
-        for (int64_t j = t; j < hidden; j += 256) {
-            T rounded;
-            const float s = residual_sum<T>(to_f32(input[base + j]), to_f32(skip[base + j]), has_bias,
-                                            has_bias ? to_f32(bias[j]) : 0.0f, rounded);
-            if (sum) sum[base + j] = rounded;
-            acc = fmaf_(s, s, acc);
-        }
+    auto block_total = [&](float acc) {
         acc = segment_sum<64>(acc);
         if ((t & 63) == 0) wave_part[t >> 6] = acc;
         __syncthreads();
         const float total = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
-        __syncthreads();  // wave_part is rewritten by the next row
-        const float r = inv_sqrt(total / hidden_f + eps);
+        __syncthreads();  // wave_part is rewritten next
+        return total;
+    };
+    auto form = [&](int64_t base, int64_t j, T& rounded) {
+        return residual_sum<T>(to_f32(input[base + j]), to_f32(skip[base + j]), has_bias,
+                               has_bias ? to_f32(bias[j]) : 0.0f, rounded);
+    };
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const int64_t base = row * hidden;
+        T r0;
+        const float shift = CENTER ? form(base, 0, r0) : 0.0f;  // sums about S[0], as above
+        float acc = 0.0f;
+        for (int64_t j = t; j < hidden; j += 256) {
+            T rounded;
+            const float s = form(base, j, rounded);
+            if (sum) sum[base + j] = rounded;
+            if constexpr (CENTER) acc += s - shift;
+            else acc = fmaf_(s, s, acc);
+        }
+        float md = 0.0f, r;
+        if constexpr (!CENTER) {
+            r = inv_sqrt(block_total(acc) / hidden_f + eps);
+        } else {
+            md = block_total(acc) / hidden_f;
+            float dev = 0.0f;
+            for (int64_t j = t; j < hidden; j += 256) {
+                T rounded;
+                const float d = (form(base, j, rounded) - shift) - md;
+                dev = fmaf_(d, d, dev);
+            }
+            r = inv_sqrt(block_total(dev) / hidden_f + eps);
+        }
         if (t == 0) {
             if (inv_std_var) inv_std_var[row] = r;
-            if (mean) mean[row] = 0.0f;
+            if (mean) mean[row] = shift + md;
         }
         for (int64_t j = t; j < hidden; j += 256) {
             T rounded;
-            const float s = residual_sum<T>(to_f32(input[base + j]), to_f32(skip[base + j]), has_bias,
-                                            has_bias ? to_f32(bias[j]) : 0.0f, rounded);
-            output[base + j] = from_f32<T>(s * r * to_f32(gamma[j]));
+            const float s = form(base, j, rounded);
+            if constexpr (CENTER) {
+                float y = ((s - shift) - md) * r * to_f32(gamma[j]);
+                if (beta) y = y + to_f32(beta[j]);
+                output[base + j] = from_f32<T>(y);
+            } else {
+                output[base + j] = from_f32<T>(s * r * to_f32(gamma[j]));
+            }
         }
     }
 }
@@ -160,12 +237,18 @@ hipError_t launch_wave_nv(const SslnArgs& a, int nvec, hipStream_t stream) {
     auto args = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), 0, stream,
                            static_cast<const T*>(a.input), static_cast<const T*>(a.skip),
-                           static_cast<const T*>(a.gamma), static_cast<const T*>(a.bias),
-                           static_cast<T*>(a.output), a.mean, a.inv_std_var,
-                           static_cast<T*>(a.sum), a.rows, nvec, hidden_f, a.epsilon);
+                           static_cast<const T*>(a.gamma), static_cast<const T*>(a.beta),
+                           static_cast<const T*>(a.bias), static_cast<T*>(a.output), a.mean,
+                           a.inv_std_var, static_cast<T*>(a.sum), a.rows, nvec, hidden_f, a.epsilon);
     };
-    if (nvec == 64 * WPR * NV) args(ssln_wave_kernel<T, E, NV, true, WPR>);
-    else args(ssln_wave_kernel<T, E, NV, false, WPR>);
+    const bool full = nvec == 64 * WPR * NV;
+    if (a.center) {
+        if (full) args(ssln_wave_kernel<T, E, NV, true, WPR, true>);
+        else args(ssln_wave_kernel<T, E, NV, false, WPR, true>);
+    } else {
+        if (full) args(ssln_wave_kernel<T, E, NV, true, WPR, false>);
+        else args(ssln_wave_kernel<T, E, NV, false, WPR, false>);
+    }
     return hipGetLastError();
 }
 
@@ -224,7 +307,7 @@ hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char**
 template <typename T>
 hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, const char** route) {
     // Widest access that divides the row and every tensor's base.
-    int E = widest_vector<T>(a.hidden, {a.input, a.skip, a.gamma, a.bias, a.output, a.sum});
+    int E = widest_vector<T>(a.hidden, {a.input, a.skip, a.gamma, a.beta, a.bias, a.output, a.sum});
     if (want == Route::Scalar) E = 1;
     const int64_t max_regs = 256 * int64_t(E) * (E == 1 ? kMaxNvRowBlock<1> : kMaxNvRowBlock<2>);
     if (want != Route::Block && a.hidden <= max_regs) {
@@ -240,11 +323,16 @@ hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, cons
     }
     *route = "ssln.block";
     const int64_t blocks = a.rows < 65536 * 16 ? a.rows : 65536 * 16;
-    hipLaunchKernelGGL(ssln_block_kernel<T>, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                       static_cast<const T*>(a.input), static_cast<const T*>(a.skip),
-                       static_cast<const T*>(a.gamma), static_cast<const T*>(a.bias),
-                       static_cast<T*>(a.output), a.mean, a.inv_std_var, static_cast<T*>(a.sum),
-                       a.rows, a.hidden, float(a.hidden), a.epsilon);
+    auto block = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                           static_cast<const T*>(a.input), static_cast<const T*>(a.skip),
+                           static_cast<const T*>(a.gamma), static_cast<const T*>(a.beta),
+                           static_cast<const T*>(a.bias), static_cast<T*>(a.output), a.mean,
+                           a.inv_std_var, static_cast<T*>(a.sum), a.rows, a.hidden, float(a.hidden),
+                           a.epsilon);
+    };
+    if (a.center) block(ssln_block_kernel<T, true>);
+    else block(ssln_block_kernel<T, false>);
     return hipGetLastError();
 }
 

@@ -76,6 +76,18 @@ def ssln(name, shape, dtype, bias: bool, epsilon, outputs=("output",)) -> Worklo
     return Workload(name, "skip_rms_norm", tuple(ts), {"epsilon": epsilon}, tuple(outputs))
 
 
+def sln(name, shape, dtype, beta: bool, bias: bool, epsilon, outputs=("output",)) -> Workload:
+    """Skip layer normalization with the mean removed (non-simplified form)."""
+    hidden = shape[-1]
+    ts = [Tensor("input", shape, "normal", dtype), Tensor("skip", shape, "normal", dtype),
+          Tensor("gamma", (hidden,), "uniform", dtype)]
+    if beta:
+        ts.append(Tensor("beta", (hidden,), "normal01", dtype))
+    if bias:
+        ts.append(Tensor("bias", (hidden,), "normal01", dtype))
+    return Workload(name, "skip_layer_norm", tuple(ts), {"epsilon": epsilon}, tuple(outputs))
+
+
 def gated(name, shape, span, dtype, epsilon) -> Workload:
     ts = (Tensor("X", shape, "normal", dtype), Tensor("gate", shape, "normal", dtype),
           Tensor("scale", (span,), "uniform", dtype))
@@ -110,6 +122,13 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
 ]}
 
 ORDER: List[str] = list(WORKLOADS)
+
+# Beyond the five: the non-simplified skip layer normalization at the large
+# SSLN workload's shape (rows of 4096 float16, S requested), with beta.
+EXTRA_WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
+    sln("sln_f16_16x2048x4096", (16, 2048, 4096), F16, beta=True, bias=False, epsilon=1e-5,
+        outputs=("output", "input_skip_bias_sum")),
+]}
 
 
 def io_bytes(w: Workload) -> int:

@@ -3,8 +3,9 @@
  * AMD Instinct MI355X (gfx950).
  *
  * Three operators, each defined on its ONNX Runtime contrib-op kernels-hub
- * README:
+ * README, and the non-simplified form of the first:
  *   skip_rms_norm   "com.microsoft.SkipSimplifiedLayerNormalization"
+ *   skip_layer_norm its form with the row mean removed (see below)
  *   gated_rms_norm  "com.microsoft.GatedRMSNorm"
  *   skip_group_norm "com.microsoft.SkipGroupNorm"
  *
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SKIPNORM_ABI_VERSION 1
+#define SKIPNORM_ABI_VERSION 2
 
 /* Element types.  T (tensor data) and M (SkipGroupNorm gamma/beta) take
  * float32 or float16 ("Type constraints" on each page); statistics outputs
@@ -97,6 +98,28 @@ sn_status skip_rms_norm(sn_dtype T, int64_t rows, int64_t hidden,
                         const void* bias, float epsilon,
                         void* output, float* mean, float* inv_std_var,
                         void* input_skip_bias_sum, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Skip layer normalization with the row mean removed: the non-simplified
+ * form of SkipSimplifiedLayerNormalization, whose page describes the `mean`
+ * output as the per-row mean (zero only for the simplified form) and
+ * `inv_std_var` as the inverse standard deviation (the inverse RMS only for
+ * the simplified form); the optional `beta` is added after the scaling, as
+ * in the ONNX Runtime operator of that form.
+ *   S[j]  = round_T((input[j] + skip[j]) + bias[j])   (bias term only if given)
+ *   mu    = sum_j S[j] / hidden
+ *   r     = 1 / sqrt(sum_j (S[j] - mu)^2 / hidden + epsilon)
+ *   output[j] = round_T((S[j] - mu) * r * gamma[j] + beta[j])   (beta only if given)
+ * Arguments as for skip_rms_norm, plus:
+ *   beta         [hidden] T or NULL.
+ *   mean         [rows] float32 or NULL; receives mu.
+ *   inv_std_var  [rows] float32 or NULL; receives r.
+ * ------------------------------------------------------------------------ */
+sn_status skip_layer_norm(sn_dtype T, int64_t rows, int64_t hidden,
+                          const void* input, const void* skip, const void* gamma,
+                          const void* beta, const void* bias, float epsilon,
+                          void* output, float* mean, float* inv_std_var,
+                          void* input_skip_bias_sum, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * GatedRMSNorm ("com.microsoft.GatedRMSNorm": Description, Inputs, Outputs,

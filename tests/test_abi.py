@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.skipnorm_abi_version() == 1
+    assert lib.skipnorm_abi_version() == 2
 
 
 def err(lib):
@@ -89,6 +89,33 @@ def test_ssln_rejects(lib, kw, status, text):
 
 def test_ssln_zero_rows_is_a_no_op(lib):
     assert ssln(lib, rows=0, inp=None, skip=None, out=None) == OK
+    assert err(lib) == ""
+    assert lib.skipnorm_last_route() == b"ssln.empty"
+
+
+# ------------------------------------------------------------------ SkipLayerNorm
+def sln(lib, T=SN_F32, rows=4, hidden=8, inp=A, skip=A + MB, gamma=A + 2 * MB, beta=None, bias=None,
+        eps=1e-6, out=A + 3 * MB, mean=None, inv=None, s=None):
+    return lib.skip_layer_norm(T, rows, hidden, inp, skip, gamma, beta, bias, eps, out, mean, inv, s,
+                               None)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(T=SN_BF16), DTYPE, "bfloat16"),
+    (dict(hidden=0), SHAPE, "skip_layer_norm: need rows >= 0"),
+    (dict(eps=-1e-6), ATTR, "epsilon"),
+    (dict(gamma=None), NULL, "skip_layer_norm: gamma"),
+    (dict(inp=None), NULL, "required"),
+    (dict(beta=A + 3 * MB + 8), ALIAS, "output overlaps input beta"),
+    (dict(s=A + 3 * MB + 16), ALIAS, "overlaps output"),
+])
+def test_sln_rejects(lib, kw, status, text):
+    assert sln(lib, **kw) == status
+    assert text in err(lib)
+
+
+def test_sln_zero_rows_is_a_no_op(lib):
+    assert sln(lib, rows=0, inp=None, skip=None, out=None) == OK
     assert err(lib) == ""
     assert lib.skipnorm_last_route() == b"ssln.empty"
 
