@@ -34,6 +34,14 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
+// v with its raw bits ANDed with m (all ones keeps v, zero makes every
+// element +0).
+template <typename T, int E>
+__device__ __forceinline__ Vec<T, E> mask_bits(const Vec<T, E>& v, uint32_t m) {
+    using R = typename RawBits<sizeof(Vec<T, E>)>::type;
+    return __builtin_bit_cast(Vec<T, E>, R(__builtin_bit_cast(R, v) & R(m)));
+}
+
 // WPR waves per row: 1, 2 or 4 (four, two or one rows per 256-thread
 // block).  Lane l of the row's 64*WPR lanes holds vectors l, l + 64*WPR, ...
 // CENTER: remove the row mean (skip layer normalization) instead of the
@@ -44,7 +52,7 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                  const T* __restrict__ gamma, const T* __restrict__ beta,
                  const T* __restrict__ bias, T* __restrict__ output, float* __restrict__ mean,
                  float* __restrict__ inv_std_var, T* __restrict__ sum,
-                 int64_t rows, int nvec, float hidden_f, float eps) {
+                 int64_t rows, int nvec, float hidden_f, float eps, uint32_t beta_mask) {
     using V = Vec<T, E>;
     constexpr int LANES = 64 * WPR;
     __shared__ float wave_part[kWavesPerBlock];
@@ -59,17 +67,6 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     const int64_t base = row * nvec;
     const bool has_bias = bias != nullptr;
 
-    // With the mean removed, everything is taken about the row's first
-    // element S[0] (every lane forms it from the same inputs, bit for bit):
-    // S - S[0] is exact for nearby values and the mean of the differences is
-    // small, so rows far from zero keep their accuracy in float32.
-    float shift = 0.0f;
-    if constexpr (CENTER) {
-        T rounded;
-        shift = residual_sum<T>(to_f32(input[row * nvec * E]), to_f32(skip[row * nvec * E]), has_bias,
-                                has_bias ? to_f32(bias[0]) : 0.0f, rounded);
-    }
-
     // Issue every load of the row before any arithmetic.  No load sits behind
     // a lane-dependent branch (that makes the compiler wait for each one in
     // turn): lanes past the row's end re-read its last vector and discard it.
@@ -81,6 +78,18 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
         xs[v] = load_vec_stream<T, E>(input, base + idx);
         ks[v] = load_vec_stream<T, E>(skip, base + idx);
     }
+    // With the mean removed, everything is taken about the row's first
+    // element S[0] (every lane forms it from the same inputs, bit for bit,
+    // after the row's loads are out): S - S[0] is exact for nearby values
+    // and the mean of the differences is small, so rows far from zero keep
+    // their accuracy in float32.
+    float shift = 0.0f;
+    if constexpr (CENTER) {
+        T rounded;
+        shift = residual_sum<T>(to_f32(input[row * nvec * E]), to_f32(skip[row * nvec * E]), has_bias,
+                                has_bias ? to_f32(bias[0]) : 0.0f, rounded);
+    }
+
     V ss[NV];
     float acc = 0.0f;
 #pragma unroll
@@ -147,14 +156,18 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     for (int v = 0; v < NV; ++v) {
         const int idx = v * LANES + lane;
         const V gv = load_vec<T, E>(gamma, clamp(idx));
+        // beta's load and add are unconditional: without a beta the host
+        // passes gamma's address and a zero mask, so the added value is +0.
+        // (A load whose use sits behind a branch, even a uniform one, is
+        // moved into it and waited for on the spot.)
         V bt = {};
-        if (CENTER && beta) bt = load_vec<T, E>(beta, clamp(idx));
+        if constexpr (CENTER) bt = mask_bits(load_vec<T, E>(beta, clamp(idx)), beta_mask);
         V out;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             if constexpr (CENTER) {
                 float y = ((to_f32(ss[v].v[e]) - shift) - md) * r * to_f32(gv.v[e]);
-                if (beta) y = y + to_f32(bt.v[e]);
+                y = y + to_f32(bt.v[e]);
                 out.v[e] = from_f32<T>(y);
             } else {
                 out.v[e] = from_f32<T>(to_f32(ss[v].v[e]) * r * to_f32(gv.v[e]));
@@ -237,9 +250,11 @@ hipError_t launch_wave_nv(const SslnArgs& a, int nvec, hipStream_t stream) {
     auto args = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), 0, stream,
                            static_cast<const T*>(a.input), static_cast<const T*>(a.skip),
-                           static_cast<const T*>(a.gamma), static_cast<const T*>(a.beta),
+                           static_cast<const T*>(a.gamma),
+                           static_cast<const T*>(a.beta ? a.beta : a.gamma),
                            static_cast<const T*>(a.bias), static_cast<T*>(a.output), a.mean,
-                           a.inv_std_var, static_cast<T*>(a.sum), a.rows, nvec, hidden_f, a.epsilon);
+                           a.inv_std_var, static_cast<T*>(a.sum), a.rows, nvec, hidden_f, a.epsilon,
+                           a.beta ? ~0u : 0u);
     };
     const bool full = nvec == 64 * WPR * NV;
     if (a.center) {
