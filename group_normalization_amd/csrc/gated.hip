@@ -16,6 +16,17 @@
 //            bytes in flight.  Element width: the widest of 16-, 8- and
 //            4-byte vectors that divides the row and every base, else
 //            scalars.
+//   tile     float16 rows of 33 to 128 vectors of 8 or 4 bytes of which the
+//            segment route would leave more than 40 % of the lanes idle (it
+//            gives such a row 64 or 128 lane slots): each wave takes RT whole rows
+//            packed back to back into its 64 * VPT vector slots
+//            (RT = floor(64 * VPT / vectors per row)), so nearly every slot
+//            carries data; per-vector sums of squares meet in LDS and each
+//            row is summed by a power-of-two group of lanes, in order, then
+//            by a butterfly over the group.  Elsewhere (and for float32) the
+//            segment route measured as fast or faster: its idle lanes
+//            re-read cached vectors, which costs issue slots but no HBM
+//            traffic.
 //   block    one 256-thread workgroup per row for wider rows; X is read twice.
 // scale is loaded once per thread and kept in registers as float32.  X, gate
 // and Y are touched once and move with nontemporal loads and stores.
@@ -97,6 +108,100 @@ gated_segment_kernel(const T* __restrict__ X, const T* __restrict__ scale,
     }
 }
 
+// Orders a wave's LDS writes before its later LDS reads from other lanes of
+// the same wave: the LDS executes one wave's instructions in issue order, so
+// only the compiler must be kept from moving accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Tile route.  Wave w of the grid takes rows [w * rt, w * rt + rt) (fewer at
+// the end), i.e. vectors [0, cnt) from the first of them; lane l holds the
+// vectors l, l + 64, ... of that run.  A vector's row within the tile is
+// j / nvec, taken as (j * magic) >> 32 with magic = floor(2^32 / nvec) + 1,
+// exact because j < 64 * VPT <= 1024 and nvec <= 1024 (j * nvec < 2^32).
+// Rows are summed by lpr = 2^lpr_log lanes each (rt * lpr <= 64).
+template <typename T, int E, int VPT>
+__global__ void __launch_bounds__(256)
+gated_tile_kernel(const T* __restrict__ X, const T* __restrict__ scale,
+                  const T* __restrict__ gate, T* __restrict__ Y, int64_t rows, int nvec,
+                  int rt, int lpr_log, uint32_t magic, float span_f, float eps) {
+    using V = Vec<T, E>;
+    constexpr int SLOTS = 64 * VPT;
+    __shared__ float part[4][SLOTS];
+    __shared__ float row_r[4][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r0 = (int64_t(blockIdx.x) * 4 + wave) * rt;
+    const int64_t left = rows - r0;
+    const int nr = left <= 0 ? 0 : (left < rt ? int(left) : rt);
+    // Each wave works on its own LDS rows, so the waves of a block never wait
+    // for one another; a wave past the last row has nothing to do.
+    if (nr == 0) return;
+    const int cnt = nr * nvec;
+    const int64_t base = r0 * nvec;
+    auto clamp = [&](int j) { return j < cnt ? j : cnt - 1; };
+    auto row_of = [&](int j) { return int((uint64_t(uint32_t(j)) * magic) >> 32); };
+
+    V xs[VPT], gs[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int jc = clamp(v * 64 + lane);
+        xs[v] = load_vec_stream<T, E>(X, base + jc);
+        gs[v] = load_vec_stream<T, E>(gate, base + jc);
+    }
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int j = v * 64 + lane;
+        float p = 0.0f;
+        if (j < cnt) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float x = to_f32(xs[v].v[e]);
+                p = fmaf_(x, x, p);
+            }
+        }
+        part[wave][j] = p;
+    }
+    wave_lds_sync();
+    // Row rr of the tile: lanes rr * lpr + k add its vectors k, k + lpr, ...
+    // in order; then the lpr lanes meet in a butterfly (every lane of the
+    // group ends with the same total).  A lane adds at most 2 * VPT + 1
+    // vectors (lpr = 64 / rtp with rtp < 2 * rt and rt * nvec <= 64 * VPT),
+    // read unconditionally from clamped slots so that the reads go out
+    // together; the terms past the row add zero.
+    const int lpr = 1 << lpr_log;
+    const int rr = lane >> lpr_log, k = lane & (lpr - 1);
+    const int row0 = (rr < nr ? rr : 0) * nvec;  // lanes past the last row read row 0
+    float acc = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 2 * VPT + 1; ++s) {
+        const int i = k + s * lpr;
+        const float pv = part[wave][row0 + (i < nvec ? i : nvec - 1)];
+        acc += (i < nvec && rr < nr) ? pv : 0.0f;
+    }
+    for (int m = 1; m < lpr; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (rr < nr && k == 0) row_r[wave][rr] = inv_sqrt(acc / span_f + eps);
+    wave_lds_sync();
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int j = v * 64 + lane;
+        const int jc = clamp(j);
+        const int row = row_of(jc);
+        const V sv = load_vec<T, E>(scale, jc - row * nvec);
+        const float r = row_r[wave][row];
+        V out;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float x = to_f32(xs[v].v[e]);
+            const float g = to_f32(gs[v].v[e]);
+            out.v[e] = from_f32<T>(x * r * to_f32(sv.v[e]) * silu_f32(g));
+        }
+        if (j < cnt) store_vec_stream<T, E>(Y, base + j, out);
+    }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 gated_block_kernel(const T* __restrict__ X, const T* __restrict__ scale,
@@ -127,7 +232,13 @@ gated_block_kernel(const T* __restrict__ X, const T* __restrict__ scale,
 
 template <typename T, int E, int L, int VPL>
 hipError_t launch_segment(const GatedArgs& a, int nvec, hipStream_t stream) {
-    constexpr int RPT = VPL >= 4 ? 1 : 4 / VPL;
+    // Vectors of X (and of gate) per thread in flight: 4 of 16 bytes; 16 of
+    // 4 or 2 bytes (measured 1.1-1.6x faster than 4 where a row takes all
+    // 64 lanes, the same elsewhere); 8 of 8 bytes where a row takes 64
+    // lanes, else 4 (8 measured 2-3 % slower there).
+    constexpr int VB = E * int(sizeof(T));
+    constexpr int WANT = VB >= 16 ? 4 : VB == 8 ? (L == 64 ? 8 : 4) : 16;
+    constexpr int RPT = VPL >= WANT ? 1 : WANT / VPL;
     constexpr int rows_per_block = (256 / L) * RPT;
     const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL((gated_segment_kernel<T, E, L, VPL, RPT>), dim3(unsigned(blocks)), dim3(256),
@@ -155,12 +266,86 @@ hipError_t launch_segment_for(const GatedArgs& a, int nvec, hipStream_t stream) 
 
 constexpr int64_t kMaxSegmentVectors = 1024;
 
+// Tile plan for rows of nvec vectors of vec_bytes each: taken for rows of
+// 33 to 128 vectors of 8 or 4 bytes that fill less than 60 % of the segment
+// route's lane slots (beyond that the segment route measured as fast), with
+// the vectors per lane (4, 8 or 16, and no more than 64 bytes of each tensor
+// per lane beyond 4 vectors, which keeps the held data at 32 VGPRs or less)
+// that leave the fewest idle slots.
+struct TilePlan {
+    int vpt, rt, lpr_log;
+    uint32_t magic;
+};
+
+bool gated_tile_plan(int64_t nvec, int vec_bytes, TilePlan* p) {
+    if (vec_bytes != 8 && vec_bytes != 4) return false;
+    if (nvec <= 32 || nvec > 128 || (nvec & (nvec - 1)) == 0) return false;
+    int64_t lanes = 1;
+    while (lanes < nvec && lanes < 64) lanes <<= 1;
+    int64_t vpl = 1;
+    while (lanes * vpl < nvec) vpl <<= 1;
+    const double seg_eff = double(nvec) / double(lanes * vpl);
+    if (seg_eff >= 0.6) return false;
+    double best = 0.0;
+    for (int vpt : {4, 8, 16}) {
+        if (vpt > 4 && vpt * vec_bytes > 64) continue;
+        const int64_t rt = 64 * vpt / nvec;
+        if (rt < 1 || rt > 64) continue;
+        const double eff = double(rt * nvec) / double(64 * vpt);
+        if (eff > best + 1e-9) {
+            best = eff;
+            p->vpt = vpt;
+            p->rt = int(rt);
+        }
+    }
+    if (best <= seg_eff) return false;
+    int rtp = 1;
+    while (rtp < p->rt) rtp <<= 1;
+    int lpr_log = 0;
+    while ((1 << lpr_log) * rtp < 64) ++lpr_log;
+    p->lpr_log = lpr_log;
+    p->magic = uint32_t((uint64_t(1) << 32) / uint64_t(nvec) + 1);
+    return true;
+}
+
+template <typename T, int E, int VPT>
+hipError_t launch_tile(const GatedArgs& a, int nvec, const TilePlan& p, hipStream_t stream) {
+    const int64_t tiles = (a.rows + p.rt - 1) / p.rt;
+    const int64_t blocks = (tiles + 3) / 4;
+    hipLaunchKernelGGL((gated_tile_kernel<T, E, VPT>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<const T*>(a.X), static_cast<const T*>(a.scale),
+                       static_cast<const T*>(a.gate), static_cast<T*>(a.Y), a.rows, nvec, p.rt,
+                       p.lpr_log, p.magic, float(a.span), a.epsilon);
+    return hipGetLastError();
+}
+
+template <typename T, int E>
+hipError_t launch_tile_for(const GatedArgs& a, int nvec, const TilePlan& p, hipStream_t stream) {
+    if (p.vpt == 4) return launch_tile<T, E, 4>(a, nvec, p, stream);
+    if constexpr (E * sizeof(T) <= 8)
+        if (p.vpt == 8) return launch_tile<T, E, 8>(a, nvec, p, stream);
+    if constexpr (E * sizeof(T) <= 4)
+        if (p.vpt == 16) return launch_tile<T, E, 16>(a, nvec, p, stream);
+    return hipErrorInvalidValue;  // the plan only picks the widths above
+}
+
 template <typename T>
 hipError_t launch_gated_t(const GatedArgs& a, Route want, hipStream_t stream, const char** route) {
     // Widest access that divides the row and every tensor's base.
     int E = widest_vector<T>(a.span, {a.X, a.scale, a.gate, a.Y});
     if (want == Route::Scalar) E = 1;
     const int64_t nvec = a.span / E;
+    if constexpr (sizeof(T) == 2) {
+        TilePlan tp;
+        if (want == Route::Auto && E > 1 && gated_tile_plan(nvec, int(E * sizeof(T)), &tp)) {
+            if (E == 4) {
+                *route = "gated.tile.vec8";
+                return launch_tile_for<T, 4>(a, int(nvec), tp, stream);
+            }
+            *route = "gated.tile.vec4";
+            return launch_tile_for<T, 2>(a, int(nvec), tp, stream);
+        }
+    }
     if (want != Route::Block && nvec <= kMaxSegmentVectors) {
         if (E * sizeof(T) == 16) {
             *route = "gated.segment.vec16";

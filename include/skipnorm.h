@@ -199,7 +199,10 @@ int skipnorm_abi_version(void);
  * cover each kernel family on the same shapes:
  *   0 = automatic (the default);
  *   1 = scalar accesses (16-byte vectors off);
- *   2 = vectorized where the preconditions hold (same as automatic);
+ *   2 = vectorized where the preconditions hold (same as automatic, except
+ *       that gated_rms_norm keeps one power-of-two lane group per row for
+ *       every row length, where automatic packs rows that are not a power
+ *       of two of vectors back to back);
  *   3 = skip_rms_norm / gated_rms_norm: one workgroup per row;
  *       skip_group_norm: the three-launch split route with scalar accesses;
  *   4 = skip_group_norm: the three-launch split route (vectorized where the

@@ -33,18 +33,62 @@ CASES = [
     ((5, 129), 129, F16),        # odd span: scalars
     ((4, 6), 6, F32),            # float32 8-byte vectors: 3 per row
     ((2, 8200), 4100, F16),      # 1025 eight-byte vectors: block route
+    # tile route (float16 rows of 33-128 vectors of 8 or 4 bytes that fill
+    # < 60 % of the segment route's lanes, packed back to back): several
+    # tiles, a ragged last tile and waves past the last row
+    ((1000, 132), 132, F16),     # 33 eight-byte vectors: 15 rows per wave of 8 per lane
+    ((257, 3, 130), 130, F16),   # 65 four-byte vectors: 15 rows per wave of 16 per lane
+    ((211, 130), 130, F32),      # 65 eight-byte float32 vectors: segment (float32 never tiles)
+    ((77, 2, 148), 148, F16),    # 37 eight-byte vectors: 13 rows per wave
+    ((93, 150), 150, F16),       # 75 four-byte vectors: 13 rows per wave of 16 per lane
+    # around the tile route's bounds: segment
+    ((99, 264), 264, F16),       # 33 sixteen-byte vectors
+    ((41, 124), 124, F16),       # 31 eight-byte vectors
+    ((43, 156), 156, F16),       # 39 eight-byte vectors: 61 % of the lanes busy
+    ((37, 516), 516, F16),       # 129 eight-byte vectors
+    ((301, 254), 254, F16),      # 127 four-byte vectors: 2 x 64 lanes nearly full
+    ((53, 129), 129, F32),       # scalars
 ]
 
 
-def expected_route(C, dt):
+def tile_plan(nvec, vec_bytes):
+    """The host's choice between the two lane layouts, restated: (vectors per
+    lane, rows per wave) of the tile route, or None for the segment route."""
+    if vec_bytes not in (8, 4) or nvec <= 32 or nvec > 128 or nvec & (nvec - 1) == 0:
+        return None
+    lanes = 1
+    while lanes < nvec and lanes < 64:
+        lanes *= 2
+    vpl = 1
+    while lanes * vpl < nvec:
+        vpl *= 2
+    if nvec / (lanes * vpl) >= 0.6:
+        return None
+    best, plan = 0.0, None
+    for vpt in (4, 8, 16):
+        if vpt > 4 and vpt * vec_bytes > 64:
+            continue
+        rt = 64 * vpt // nvec
+        if 1 <= rt <= 64 and rt * nvec / (64 * vpt) > best + 1e-9:
+            best, plan = rt * nvec / (64 * vpt), (vpt, rt)
+    return plan if best > nvec / (lanes * vpl) else None
+
+
+def expected_route(C, dt, route="auto"):
     size = np.dtype(dt).itemsize
     width = next((b for b in (16, 8, 4) if b > size and C * size % b == 0), size)
+    if route == "scalar":
+        width = size
     E = width // size
     name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
-    return f"gated.segment.{name}" if C // E <= 1024 else "gated.block"
+    if route == "block" or C // E > 1024:
+        return "gated.block"
+    if route == "auto" and size == 2 and E > 1 and tile_plan(C // E, width):
+        return f"gated.tile.{name}"
+    return f"gated.segment.{name}"
 
 
-@pytest.mark.parametrize("route", ["auto", "scalar", "block"])
+@pytest.mark.parametrize("route", ["auto", "scalar", "vector", "block"])
 @pytest.mark.parametrize("shape,C,dt", CASES, ids=[f"{s}-C{c}-{np.dtype(d).name}" for s, c, d in CASES])
 def test_matches_oracle(shape, C, dt, route):
     w = workloads.gated("t", shape, C, dt, epsilon=1e-5)
@@ -54,8 +98,44 @@ def test_matches_oracle(shape, C, dt, route):
         y = gn.gated_rms_norm(to_dev(x["X"]), to_dev(x["scale"]), to_dev(x["gate"]), 1e-5)
         used = gn.last_route()
     assert_close(to_host(y), ref, f"Y via {used}")
-    if route == "auto":
-        assert used == expected_route(C, dt)
+    assert used == expected_route(C, dt, route)
+
+
+def test_tile_plan_examples():
+    """Spot values of the restated plan (vectors per lane, rows per wave)."""
+    assert tile_plan(33, 8) == (8, 15)
+    assert tile_plan(65, 4) == (16, 15)
+    assert tile_plan(37, 8) == (8, 13) and tile_plan(38, 8) == (8, 13)
+    assert tile_plan(39, 8) is None and tile_plan(50, 8) is None
+    assert tile_plan(127, 4) is None and tile_plan(33, 16) is None and tile_plan(31, 8) is None and tile_plan(129, 8) is None
+    assert tile_plan(64, 8) is None and tile_plan(65, 2) is None
+
+
+@pytest.mark.parametrize("C,dt", [(132, F16), (130, F16), (148, F16), (150, F16), (68 * 2 + 2, F16)])
+def test_tile_route_stays_in_bounds(C, dt):
+    """Tile route through raw pointers: guard elements on both sides of Y are
+    untouched, two runs agree bit for bit, and the rows match the oracle."""
+    from group_normalization_amd._lib import lib, check as ck
+    rows, pad = 211, 4096
+    w = workloads.gated("t", (rows, C), C, dt, epsilon=1e-5)
+    x = workloads.generate(w, seed=C)
+    d = {k: to_dev(v) for k, v in x.items()}
+    tdt = torch.float16 if dt == F16 else torch.float32
+    arena = torch.full((rows * C + 2 * pad,), 3.0, dtype=tdt, device="cuda")
+    Y = arena[pad: pad + rows * C]
+    code = 1 if dt == F16 else 0
+    for i in range(2):
+        ck(lib().gated_rms_norm(code, rows * C, C, d["X"].data_ptr(), d["scale"].data_ptr(),
+                                d["gate"].data_ptr(), 1e-5, Y.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        assert gn.last_route().startswith("gated.tile")
+        if i == 0:
+            first = to_host(Y).copy()
+    assert_bitwise(to_host(Y), first, "second run")
+    a = to_host(arena)
+    assert np.all(a[:pad] == 3.0) and np.all(a[pad + rows * C:] == 3.0)
+    assert_close(first.reshape(rows, C), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
 
 
 @pytest.mark.parametrize("dt", [F32, F16])
