@@ -27,7 +27,11 @@
 //            segment route measured as fast or faster: its idle lanes
 //            re-read cached vectors, which costs issue slots but no HBM
 //            traffic.
-//   block    one 256-thread workgroup per row for wider rows; X is read twice.
+//   row      rows of 1025 to 4096 vectors: one 256-thread workgroup per row
+//            holding it in registers (up to 16 vectors per thread); the
+//            four waves' sums meet in LDS in wave order.
+//   block    one 256-thread workgroup per row for wider rows; X is read
+//            twice, four vectors per thread in flight per pass.
 // scale is loaded once per thread and kept in registers as float32.  X, gate
 // and Y are touched once and move with nontemporal loads and stores.
 #include "device_common.h"
@@ -202,30 +206,114 @@ gated_tile_kernel(const T* __restrict__ X, const T* __restrict__ scale,
     }
 }
 
-template <typename T>
+// Row route: thread t holds vectors t, t + 256, ... (NV of them) of the
+// block's row; lanes past the row re-read its last vector and discard it.
+template <typename T, int E, int NV>
+__global__ void __launch_bounds__(256)
+gated_row_kernel(const T* __restrict__ X, const T* __restrict__ scale,
+                 const T* __restrict__ gate, T* __restrict__ Y, int64_t rows, int nvec,
+                 float span_f, float eps) {
+    using V = Vec<T, E>;
+    __shared__ float wave_part[4];
+    const int t = threadIdx.x;
+    auto clamp = [&](int j) { return j < nvec ? j : nvec - 1; };
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const int64_t base = row * nvec;
+        V xs[NV], gs[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int jc = clamp(v * 256 + t);
+            xs[v] = load_vec_stream<T, E>(X, base + jc);
+            gs[v] = load_vec_stream<T, E>(gate, base + jc);
+        }
+        float acc = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            if (v * 256 + t < nvec) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float x = to_f32(xs[v].v[e]);
+                    acc = fmaf_(x, x, acc);
+                }
+            }
+        acc = segment_sum<64>(acc);
+        if ((t & 63) == 0) wave_part[t >> 6] = acc;
+        __syncthreads();
+        const float total = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
+        __syncthreads();  // wave_part is rewritten for the next row
+        const float r = inv_sqrt(total / span_f + eps);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int j = v * 256 + t;
+            const V sv = load_vec<T, E>(scale, clamp(j));
+            V out;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float x = to_f32(xs[v].v[e]);
+                const float g = to_f32(gs[v].v[e]);
+                out.v[e] = from_f32<T>(x * r * to_f32(sv.v[e]) * silu_f32(g));
+            }
+            if (j < nvec) store_vec_stream<T, E>(Y, base + j, out);
+        }
+    }
+}
+
+// Block route: two passes over X, four vectors per thread per step (the
+// loads of a step go out together; lanes past the row re-read its last
+// vector).  E == 1 is the scalar route.
+template <typename T, int E>
 __global__ void __launch_bounds__(256)
 gated_block_kernel(const T* __restrict__ X, const T* __restrict__ scale,
                    const T* __restrict__ gate, T* __restrict__ Y, int64_t rows,
-                   int64_t span, float span_f, float eps) {
+                   int64_t nvec, float span_f, float eps) {
+    using V = Vec<T, E>;
+    constexpr int U = 4;
     __shared__ float wave_part[4];
     const int t = threadIdx.x;
+    auto clamp = [&](int64_t j) { return j < nvec ? j : nvec - 1; };
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const int64_t base = row * span;
+        const int64_t base = row * nvec;
         float acc = 0.0f;
-        for (int64_t j = t; j < span; j += 256) {
-            const float x = to_f32(X[base + j]);
-            acc = fmaf_(x, x, acc);
+        for (int64_t j0 = t; j0 < nvec; j0 += 256 * U) {
+            V xs[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) xs[u] = load_vec<T, E>(X, base + clamp(j0 + u * 256));
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (j0 + u * 256 < nvec) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float x = to_f32(xs[u].v[e]);
+                        acc = fmaf_(x, x, acc);
+                    }
+                }
         }
         acc = segment_sum<64>(acc);
         if ((t & 63) == 0) wave_part[t >> 6] = acc;
         __syncthreads();
         const float total = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
-        __syncthreads();
+        __syncthreads();  // wave_part is rewritten for the next row
         const float r = inv_sqrt(total / span_f + eps);
-        for (int64_t j = t; j < span; j += 256) {
-            const float x = to_f32(X[base + j]);
-            const float g = to_f32(gate[base + j]);
-            Y[base + j] = from_f32<T>(x * r * to_f32(scale[j]) * silu_f32(g));
+        for (int64_t j0 = t; j0 < nvec; j0 += 256 * U) {
+            V xs[U], gs[U], ss[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t jc = clamp(j0 + u * 256);
+                xs[u] = load_vec_stream<T, E>(X, base + jc);
+                gs[u] = load_vec_stream<T, E>(gate, base + jc);
+                ss[u] = load_vec<T, E>(scale, jc);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                V out;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float x = to_f32(xs[u].v[e]);
+                    const float g = to_f32(gs[u].v[e]);
+                    out.v[e] = from_f32<T>(x * r * to_f32(ss[u].v[e]) * silu_f32(g));
+                }
+                if (j0 + u * 256 < nvec) store_vec_stream<T, E>(Y, base + j0 + u * 256, out);
+            }
         }
     }
 }
@@ -265,6 +353,35 @@ hipError_t launch_segment_for(const GatedArgs& a, int nvec, hipStream_t stream) 
 }
 
 constexpr int64_t kMaxSegmentVectors = 1024;
+constexpr int64_t kMaxRowVectors = 256 * 16;
+
+template <typename T, int E, int NV>
+hipError_t launch_row(const GatedArgs& a, int nvec, hipStream_t stream) {
+    const int64_t blocks = a.rows < (int64_t(1) << 20) ? a.rows : (int64_t(1) << 20);
+    hipLaunchKernelGGL((gated_row_kernel<T, E, NV>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<const T*>(a.X), static_cast<const T*>(a.scale),
+                       static_cast<const T*>(a.gate), static_cast<T*>(a.Y), a.rows, nvec,
+                       float(a.span), a.epsilon);
+    return hipGetLastError();
+}
+
+// The fewest of 8, 12 or 16 vectors per thread that hold the row.
+template <typename T, int E>
+hipError_t launch_row_for(const GatedArgs& a, int nvec, hipStream_t stream) {
+    if (nvec <= 256 * 8) return launch_row<T, E, 8>(a, nvec, stream);
+    if (nvec <= 256 * 12) return launch_row<T, E, 12>(a, nvec, stream);
+    return launch_row<T, E, 16>(a, nvec, stream);
+}
+
+template <typename T, int E>
+hipError_t launch_block(const GatedArgs& a, int64_t nvec, hipStream_t stream) {
+    const int64_t blocks = a.rows < (int64_t(1) << 20) ? a.rows : (int64_t(1) << 20);
+    hipLaunchKernelGGL((gated_block_kernel<T, E>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<const T*>(a.X), static_cast<const T*>(a.scale),
+                       static_cast<const T*>(a.gate), static_cast<T*>(a.Y), a.rows, nvec,
+                       float(a.span), a.epsilon);
+    return hipGetLastError();
+}
 
 // Tile plan for rows of nvec vectors of vec_bytes each: taken for rows of
 // 33 to 128 vectors of 8 or 4 bytes that fill less than 60 % of the segment
@@ -364,13 +481,43 @@ hipError_t launch_gated_t(const GatedArgs& a, Route want, hipStream_t stream, co
         *route = "gated.segment.scalar";
         return launch_segment_for<T, 1>(a, int(nvec), stream);
     }
+    if (want != Route::Block && nvec <= kMaxRowVectors) {
+        if (E * sizeof(T) == 16) {
+            *route = "gated.row.vec16";
+            return launch_row_for<T, VecWidth<T>::value>(a, int(nvec), stream);
+        }
+        if (E * sizeof(T) == 8) {
+            *route = "gated.row.vec8";
+            return launch_row_for<T, 8 / sizeof(T)>(a, int(nvec), stream);
+        }
+        if constexpr (sizeof(T) == 2) {
+            if (E == 2) {
+                *route = "gated.row.vec4";
+                return launch_row_for<T, 2>(a, int(nvec), stream);
+            }
+        }
+        *route = "gated.row.scalar";
+        return launch_row_for<T, 1>(a, int(nvec), stream);
+    }
+    // The block route: wider rows, or forced (then with scalar accesses).
+    if (want == Route::Block) E = 1;
+    const int64_t bvec = a.span / E;
+    if (E * sizeof(T) == 16) {
+        *route = "gated.block.vec16";
+        return launch_block<T, VecWidth<T>::value>(a, bvec, stream);
+    }
+    if (E * sizeof(T) == 8) {
+        *route = "gated.block.vec8";
+        return launch_block<T, 8 / sizeof(T)>(a, bvec, stream);
+    }
+    if constexpr (sizeof(T) == 2) {
+        if (E == 2) {
+            *route = "gated.block.vec4";
+            return launch_block<T, 2>(a, bvec, stream);
+        }
+    }
     *route = "gated.block";
-    const int64_t blocks = a.rows < 65536 * 16 ? a.rows : 65536 * 16;
-    hipLaunchKernelGGL(gated_block_kernel<T>, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                       static_cast<const T*>(a.X), static_cast<const T*>(a.scale),
-                       static_cast<const T*>(a.gate), static_cast<T*>(a.Y), a.rows, a.span,
-                       float(a.span), a.epsilon);
-    return hipGetLastError();
+    return launch_block<T, 1>(a, bvec, stream);
 }
 
 }  // namespace
