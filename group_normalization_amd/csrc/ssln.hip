@@ -26,6 +26,8 @@
 // fixed butterfly sums the 64 lanes (DPP inside 16-lane rows, then two
 // cross-row exchanges), so every lane holds the same total and the result
 // does not depend on which optional outputs were requested.
+#include <type_traits>
+
 #include "device_common.h"
 #include "skipnorm_internal.h"
 
@@ -177,16 +179,25 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     }
 }
 
-template <typename T, bool CENTER>
+// Rows too wide for the register-resident routes: one workgroup per row,
+// S formed again in every pass (two passes; three with the mean removed),
+// four accesses per thread per step whose loads go out together (lanes past
+// the row re-read its last access).  E == 1 is the scalar route.  bias and
+// beta are read unconditionally: the host passes gamma's address for an
+// absent one and the flags say whether to use the value.
+template <typename T, int E, bool CENTER>
 __global__ void __launch_bounds__(256)
 ssln_block_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                   const T* __restrict__ gamma, const T* __restrict__ beta,
                   const T* __restrict__ bias, T* __restrict__ output, float* __restrict__ mean,
                   float* __restrict__ inv_std_var, T* __restrict__ sum,
-                  int64_t rows, int64_t hidden, float hidden_f, float eps) {
+                  int64_t rows, int64_t nvec, float hidden_f, float eps, bool has_bias,
+                  bool has_beta) {
+    using V = Vec<T, E>;
+    constexpr int U = 4;
     __shared__ float wave_part[kWavesPerBlock];
-    const bool has_bias = bias != nullptr;
     const int t = threadIdx.x;
+    auto clamp = [&](int64_t j) { return j < nvec ? j : nvec - 1; };
     auto block_total = [&](float acc) {
         acc = segment_sum<64>(acc);
         if ((t & 63) == 0) wave_part[t >> 6] = acc;
@@ -195,21 +206,46 @@ ssln_block_kernel(const T* __restrict__ input, const T* __restrict__ skip,
         __syncthreads();  // wave_part is rewritten next
         return total;
     };
-    auto form = [&](int64_t base, int64_t j, T& rounded) {
-        return residual_sum<T>(to_f32(input[base + j]), to_f32(skip[base + j]), has_bias,
-                               has_bias ? to_f32(bias[j]) : 0.0f, rounded);
+    // S (rounded to T) of the U accesses j0, j0 + 256, ... of the row.
+    auto form = [&](int64_t base, int64_t j0, V (&ss)[U]) {
+        V xs[U], ks[U], bs[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t jc = clamp(j0 + u * 256);
+            xs[u] = load_vec_stream<T, E>(input, base + jc);
+            ks[u] = load_vec_stream<T, E>(skip, base + jc);
+            bs[u] = load_vec<T, E>(bias, jc);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                residual_sum<T>(to_f32(xs[u].v[e]), to_f32(ks[u].v[e]), has_bias, to_f32(bs[u].v[e]),
+                                ss[u].v[e]);
     };
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const int64_t base = row * hidden;
-        T r0;
-        const float shift = CENTER ? form(base, 0, r0) : 0.0f;  // sums about S[0], as above
+        const int64_t base = row * nvec;
+        float shift = 0.0f;  // sums about S[0], as in the register routes
+        if constexpr (CENTER) {
+            T r0;
+            shift = residual_sum<T>(to_f32(input[base * E]), to_f32(skip[base * E]), has_bias,
+                                    to_f32(bias[0]), r0);
+        }
         float acc = 0.0f;
-        for (int64_t j = t; j < hidden; j += 256) {
-            T rounded;
-            const float s = form(base, j, rounded);
-            if (sum) sum[base + j] = rounded;
-            if constexpr (CENTER) acc += s - shift;
-            else acc = fmaf_(s, s, acc);
+        for (int64_t j0 = t; j0 < nvec; j0 += 256 * U) {
+            V ss[U];
+            form(base, j0, ss);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j0 + u * 256 >= nvec) continue;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float sv = to_f32(ss[u].v[e]);
+                    if constexpr (CENTER) acc += sv - shift;
+                    else acc = fmaf_(sv, sv, acc);
+                }
+                if (sum) store_vec_stream<T, E>(sum, base + j0 + u * 256, ss[u]);
+            }
         }
         float md = 0.0f, r;
         if constexpr (!CENTER) {
@@ -217,10 +253,18 @@ ssln_block_kernel(const T* __restrict__ input, const T* __restrict__ skip,
         } else {
             md = block_total(acc) / hidden_f;
             float dev = 0.0f;
-            for (int64_t j = t; j < hidden; j += 256) {
-                T rounded;
-                const float d = (form(base, j, rounded) - shift) - md;
-                dev = fmaf_(d, d, dev);
+            for (int64_t j0 = t; j0 < nvec; j0 += 256 * U) {
+                V ss[U];
+                form(base, j0, ss);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (j0 + u * 256 >= nvec) continue;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float d = (to_f32(ss[u].v[e]) - shift) - md;
+                        dev = fmaf_(d, d, dev);
+                    }
+                }
             }
             r = inv_sqrt(block_total(dev) / hidden_f + eps);
         }
@@ -228,15 +272,30 @@ ssln_block_kernel(const T* __restrict__ input, const T* __restrict__ skip,
             if (inv_std_var) inv_std_var[row] = r;
             if (mean) mean[row] = shift + md;
         }
-        for (int64_t j = t; j < hidden; j += 256) {
-            T rounded;
-            const float s = form(base, j, rounded);
-            if constexpr (CENTER) {
-                float y = ((s - shift) - md) * r * to_f32(gamma[j]);
-                if (beta) y = y + to_f32(beta[j]);
-                output[base + j] = from_f32<T>(y);
-            } else {
-                output[base + j] = from_f32<T>(s * r * to_f32(gamma[j]));
+        for (int64_t j0 = t; j0 < nvec; j0 += 256 * U) {
+            V ss[U], gs[U], bt[U];
+            form(base, j0, ss);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t jc = clamp(j0 + u * 256);
+                gs[u] = load_vec<T, E>(gamma, jc);
+                bt[u] = load_vec<T, E>(beta, jc);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                V out;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float sv = to_f32(ss[u].v[e]);
+                    if constexpr (CENTER) {
+                        float y = ((sv - shift) - md) * r * to_f32(gs[u].v[e]);
+                        if (has_beta) y = y + to_f32(bt[u].v[e]);
+                        out.v[e] = from_f32<T>(y);
+                    } else {
+                        out.v[e] = from_f32<T>(sv * r * to_f32(gs[u].v[e]));
+                    }
+                }
+                if (j0 + u * 256 < nvec) store_vec_stream<T, E>(output, base + j0 + u * 256, out);
             }
         }
     }
@@ -336,19 +395,36 @@ hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, cons
         }
         return launch_ssln_width<T, 1>(a, stream, route);
     }
-    *route = "ssln.block";
+    // Wider rows (or forced, then with scalar accesses): the block route.
+    if (want == Route::Block) E = 1;
+    static const char* const kBlockNames[4] = {"ssln.block", "ssln.block.vec4", "ssln.block.vec8",
+                                               "ssln.block.vec16"};
+    *route = kBlockNames[E == 1 ? 0 : E * sizeof(T) == 16 ? 3 : E * sizeof(T) == 8 ? 2 : 1];
     const int64_t blocks = a.rows < 65536 * 16 ? a.rows : 65536 * 16;
     auto block = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), 0, stream,
                            static_cast<const T*>(a.input), static_cast<const T*>(a.skip),
-                           static_cast<const T*>(a.gamma), static_cast<const T*>(a.beta),
-                           static_cast<const T*>(a.bias), static_cast<T*>(a.output), a.mean,
-                           a.inv_std_var, static_cast<T*>(a.sum), a.rows, a.hidden, float(a.hidden),
-                           a.epsilon);
+                           static_cast<const T*>(a.gamma),
+                           static_cast<const T*>(a.beta ? a.beta : a.gamma),
+                           static_cast<const T*>(a.bias ? a.bias : a.gamma), static_cast<T*>(a.output),
+                           a.mean, a.inv_std_var, static_cast<T*>(a.sum), a.rows, a.hidden / E,
+                           float(a.hidden), a.epsilon, a.bias != nullptr, a.beta != nullptr);
+        return hipGetLastError();
     };
-    if (a.center) block(ssln_block_kernel<T, true>);
-    else block(ssln_block_kernel<T, false>);
-    return hipGetLastError();
+    auto by_width = [&](auto center) {
+        constexpr bool C = decltype(center)::value;
+        if constexpr (sizeof(T) == 2) {
+            if (E == 8) return block(ssln_block_kernel<T, 8, C>);
+            if (E == 4) return block(ssln_block_kernel<T, 4, C>);
+            if (E == 2) return block(ssln_block_kernel<T, 2, C>);
+        } else {
+            if (E == 4) return block(ssln_block_kernel<T, 4, C>);
+            if (E == 2) return block(ssln_block_kernel<T, 2, C>);
+        }
+        return block(ssln_block_kernel<T, 1, C>);
+    };
+    if (a.center) return by_width(std::true_type{});
+    return by_width(std::false_type{});
 }
 
 }  // namespace

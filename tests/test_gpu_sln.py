@@ -52,7 +52,9 @@ SHAPES = [
     ((3, 4100), F16, True, False),      # 8-byte vectors
     ((3, 4098), F16, False, True),      # 4-byte vectors
     ((2, 4097), F16, True, False),      # odd width: scalars, four waves
-    ((2, 40000), F16, True, True),      # block route (three passes)
+    ((2, 40000), F16, True, True),      # block route (three passes), 16-byte vectors
+    ((3, 20002), F32, True, False),     # block route, 8-byte vectors, ragged step
+    ((2, 8193), F16, False, True),      # block route, scalars
 ]
 
 
@@ -67,6 +69,8 @@ def test_matches_oracle(shape, dt, beta, bias, route):
     check(ref, out)
     if route == "block":
         assert used == "ssln.block"
+    elif route == "auto" and shape[-1] * np.dtype(dt).itemsize > 65536:
+        assert used.startswith("ssln.block")  # wider than 256 lanes x 16 x 16 bytes
 
 
 @pytest.mark.parametrize("want", [(), ("sum",), ("mean",), ("inv",), ("mean", "inv", "sum")])

@@ -55,6 +55,9 @@ SHAPES = [
     ((2, 16384), F32, True),     # float32 four waves per row, 16 vectors per lane
     ((2, 10000), F32, False),    # float32 four waves per row, ragged
     ((2, 40000), F16, True),     # wider than any register-resident route: block route
+    ((3, 65536), F16, False),    # block route, 16-byte vectors, whole steps
+    ((2, 20002), F32, True),     # float32 block route, 8-byte vectors, ragged step
+    ((2, 32770), F16, True),     # block route, 4-byte vectors
     ((7, 4100), F16, True),      # 8-byte vectors, 1025 of them: four waves per row
     ((5, 4092), F16, True),      # 8-byte vectors, two waves per row (odd row count)
     ((5, 4098), F16, False),     # 4-byte vectors, 2049 of them: four waves per row
@@ -79,7 +82,7 @@ def expected_route(shape, dt):
         return f"ssln.wave2.{name}"
     if nvec <= 256 * (32 if E == 1 else 16):
         return f"ssln.rowblock.{name}"
-    return "ssln.block"
+    return "ssln.block" if E == 1 else f"ssln.block.{name}"
 
 
 @pytest.mark.parametrize("route", ["auto", "scalar", "block"])
