@@ -66,6 +66,41 @@ def test_gated_beyond_2_31_elements():
     assert_close(Y[idx].cpu().numpy(), ref, "Y")
 
 
+def test_skip_layer_norm_beyond_2_31_elements():
+    hidden = 4096
+    rows = TWO31 // hidden + 8
+    x = gen((rows, hidden), torch.float16, 11)
+    k = gen((rows, hidden), torch.float16, 12)
+    g = torch.Generator(device="cuda").manual_seed(13)
+    gamma = (torch.rand(hidden, device="cuda", generator=g) + 0.5).half()
+    beta = (0.1 * torch.randn(hidden, device="cuda", generator=g)).half()
+    out = gn.skip_layer_norm(x, k, gamma, beta, None, 1e-5, want_mean=True, want_sum=True)
+    assert gn.last_route() == "ssln.wave2.vec16"
+    torch.cuda.synchronize()
+    sample = np.array([0, TWO31 // hidden - 1, TWO31 // hidden, rows - 1])
+    idx = torch.from_numpy(sample).cuda()
+    ref = oracle.skip_layer_norm(x[idx].cpu().numpy(), k[idx].cpu().numpy(), gamma.cpu().numpy(),
+                                 beta.cpu().numpy(), None, 1e-5, want_mean=True, want_sum=True)
+    assert_close(out.output[idx].cpu().numpy(), ref[0], "output")
+    assert_close(out.mean[idx].cpu().numpy(), ref[1], "mean")
+    assert_bitwise(out.input_skip_bias_sum[idx].cpu().numpy(), ref[3], "S")
+
+
+@pytest.mark.parametrize("C,route", [(16384, "gated.row.vec16"), (132, "gated.tile.vec8")])
+def test_gated_wide_and_tiled_rows_beyond_2_31_elements(C, route):
+    rows = TWO31 // C + 64
+    X = gen((rows, C), torch.float16, 14)
+    G = gen((rows, C), torch.float16, 15)
+    scale = (torch.rand(C, device="cuda", generator=torch.Generator(device="cuda").manual_seed(16)) + 0.5).half()
+    Y = gn.gated_rms_norm(X, scale, G, 1e-5)
+    assert gn.last_route() == route
+    torch.cuda.synchronize()
+    sample = np.array([0, TWO31 // C - 1, TWO31 // C, TWO31 // C + 1, rows - 1])
+    idx = torch.from_numpy(sample).cuda()
+    ref = oracle.gated_rms_norm(X[idx].cpu().numpy(), scale.cpu().numpy(), G[idx].cpu().numpy(), 1e-5)
+    assert_close(Y[idx].cpu().numpy(), ref, "Y")
+
+
 @pytest.mark.parametrize("channels_last", [1, 0])
 def test_sgn_beyond_2_31_elements(channels_last):
     C, H, W, groups = 256, 16, 16, 32
