@@ -733,6 +733,8 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
             ca.beta = beta;
             ca.part = part;
             ca.flags = reinterpret_cast<uint64_t*>(stat + NG);
+            if (hipError_t e = clear_publication_tags(a, ca.flags, NG * Kc, stream); e != hipSuccess)
+                return e;
             ca.tag = a.tag;
             ca.timeout_ticks = a.exchange_timeout_ticks;
             ca.HW = HW;
@@ -853,6 +855,20 @@ size_t sgn_workspace_bytes(int dtype, int64_t N, int64_t C, int64_t H, int64_t W
     size_t bytes = size_t(NG * B) * sizeof(Partial) + size_t(NG) * sizeof(float2);
     bytes += size_t(NG) * (channels_last ? kNhwcMaxK : kClusterMaxK) * sizeof(uint64_t);
     return bytes;
+}
+
+namespace {
+__global__ void __launch_bounds__(256) sgn_clear_tags_kernel(uint64_t* __restrict__ flags, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+        flags[i] = 0;
+}
+}  // namespace
+
+hipError_t clear_publication_tags(const SgnArgs& a, uint64_t* flags, int64_t n, hipStream_t stream) {
+    if (!a.clear_tags || n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    hipLaunchKernelGGL(sgn_clear_tags_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, flags, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_sgn(const SgnArgs& a, Route want, hipStream_t stream, const char** route) {

@@ -17,6 +17,11 @@ constexpr int kNhwcMaxK = 64;         // slices per (image, channel block), NHWC
 bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, uint64_t* flags,
                              hipStream_t stream, const char** route, hipError_t* err);
 
+// Zeroes the cluster routes' n publication tags on `stream` when a.clear_tags
+// is set (a kernel of plain stores, not a memset, so that graph replays
+// rerun it faithfully); nothing otherwise.
+hipError_t clear_publication_tags(const SgnArgs& a, uint64_t* flags, int64_t n, hipStream_t stream);
+
 namespace {
 
 constexpr int kUnroll = 4;

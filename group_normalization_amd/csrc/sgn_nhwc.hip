@@ -473,6 +473,8 @@ hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, int E, void
     ca.beta = static_cast<const M*>(a.beta);
     ca.part = static_cast<Partial*>(part);
     ca.flags = flags;
+    if (hipError_t e = clear_publication_tags(a, flags, a.N * a.groups * plan.K, stream); e != hipSuccess)
+        return e;
     ca.tag = a.tag;
     ca.timeout_ticks = a.exchange_timeout_ticks;
     ca.HW = a.H * a.W;

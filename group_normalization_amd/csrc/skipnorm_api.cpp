@@ -301,16 +301,19 @@ sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t 
     a.tag = g_tag.fetch_add(2) | 1;  // odd, never 0
     a.exchange_timeout_ticks = g_exchange_timeout_us.load() * 100;
     // A captured graph replays its kernels with the arguments of the
-    // capture, so the cluster routes' per-call tag would repeat on every
-    // replay and a workgroup could take the moments a slice left in the
-    // previous replay.  Under capture the split route runs instead: its
-    // launches exchange nothing within a launch, only through stream order.
-    sn::Route want = current_route();
+    // capture, so a per-call tag would repeat on every replay and a
+    // workgroup could take the moments a slice left in the previous replay.
+    // Under capture the cluster routes' tags are zeroed by a kernel ahead of
+    // each cluster launch instead, and the tag is a constant: only this
+    // launch's publications can carry it.
+    a.clear_tags = false;
     hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &capture) == hipSuccess && capture != hipStreamCaptureStatusNone)
-        want = (want == sn::Route::Scalar || want == sn::Route::Block) ? sn::Route::Block : sn::Route::Split;
+    if (hipStreamIsCapturing(stream, &capture) == hipSuccess && capture != hipStreamCaptureStatusNone) {
+        a.clear_tags = true;
+        a.tag = 1;
+    }
     const char* route = "";
-    return finish_launch(sn::launch_sgn(a, want, stream, &route), route, "skip_group_norm");
+    return finish_launch(sn::launch_sgn(a, current_route(), stream, &route), route, "skip_group_norm");
 }
 
 const char* skipnorm_last_error(void) { return g_error.c_str(); }

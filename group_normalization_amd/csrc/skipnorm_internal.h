@@ -49,6 +49,9 @@ struct SgnArgs {
     void* workspace;
     uint64_t tag;                     // unique per call (publication tags)
     long long exchange_timeout_ticks; // bounded wait of the cluster route
+    // Clear the publication tags before a cluster launch (the call is being
+    // captured into a graph, whose replays repeat `tag`).
+    bool clear_tags;
 };
 // Blocks of the statistics pass per (n, group) partial-sum row; a function
 // of the shapes and T only, so that the workspace size does not depend on

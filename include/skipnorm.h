@@ -170,11 +170,11 @@ sn_status gated_rms_norm(sn_dtype T, int64_t numel, int64_t span,
  *                  arguments (may be NULL when that size is 0).  Its
  *                  contents on entry do not matter.  Calls that share a
  *                  workspace must be ordered (same stream).
- * On a stream that is being captured into a HIP graph the call records the
- * three-launch route (partial statistics, combine, normalize), whose
- * launches share data only through stream order, so every replay is
- * correct; the single-launch routes identify their exchanges by a per-call
- * value that a replay would repeat.
+ * The single-launch routes tell a call's exchanged partial moments from
+ * earlier ones by a per-call value.  On a stream that is being captured into
+ * a HIP graph (whose replays repeat every argument) the call records, ahead
+ * of such a launch, a small kernel that clears those values in the
+ * workspace, so that every replay is correct.
  * ------------------------------------------------------------------------ */
 sn_status skip_group_norm_workspace_size(sn_dtype T, int64_t N, int64_t C,
                                          int64_t H, int64_t W, int64_t groups,

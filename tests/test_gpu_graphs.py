@@ -1,11 +1,11 @@
 """HIP graph capture and replay (torch.cuda.CUDAGraph): every operator is
 captured once and replayed with new inputs written in place; each replay's
 outputs must equal, bit for bit, the same calls made eagerly on the same
-inputs, with eager work between the replays.  Under capture SkipGroupNorm
-records its three-launch route (the single-launch routes identify their
-exchanges by a per-call value that a replay would repeat), so the eager
-reference forces that route ("split"; it leaves the other operators on their
-automatic routes)."""
+inputs, with eager work between the replays.  SkipGroupNorm's single-launch
+routes tell a call's exchanged moments from earlier ones by a per-call value
+that a replay repeats; under capture they record a kernel that clears those
+values ahead of the launch, which these replays (with changed inputs)
+exercise."""
 import pytest
 import torch
 
@@ -71,10 +71,7 @@ def test_graph_replays_match_eager():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         captured, routes = run(t)
-    assert routes[0].startswith("sgn.split.nhwc") and routes[1].startswith("sgn.split.nchw"), routes
-    # Outside capture the same calls take the single-launch routes.
-    _, eager_routes = run(t)
-    assert eager_routes[0].startswith("sgn.cluster") and eager_routes[1].startswith("sgn.cluster")
+    assert routes[0].startswith("sgn.cluster.nhwc") and routes[1].startswith("sgn.cluster.nchw"), routes
     torch.cuda.synchronize()
 
     names = ["ssln output", "ssln inv_std_var", "ssln S", "sln output", "sln mean", "sln inv_std_var",
@@ -84,8 +81,7 @@ def test_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         got = [to_host(o).copy() for o in captured]
-        with gn.force_route("split"):
-            ref, _ = run(t)
+        ref, _ = run(t)
         torch.cuda.synchronize()
         for n, gv, rv in zip(names, got, ref):
             assert_bitwise(gv, to_host(rv), f"replay {rep}: {n}")
