@@ -1,5 +1,9 @@
 // sgn_nhwc.hip -- SkipGroupNorm, NHWC channel-block cluster route (gfx950).
 // The operator and the other routes are described in sgn.hip.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "sgn_common.h"
 
 namespace sn {
@@ -439,6 +443,68 @@ bool nhwc_cluster_plan(int E, int64_t N, int64_t C, int64_t HW, int64_t groups, 
     return false;
 }
 
+// Workgroups of `kernel` (256 threads) that the current device holds at once:
+// its occupancy per CU times the CUs, queried once per device and kernel.
+int resident_workgroups(const void* kernel) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, kernel);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kClusterThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;  // unknown: the caller takes another route
+    return cache[key] = per_cu * cus;
+}
+
+template <typename T, typename M, int E, int R>
+const void* nhwc_kernel_r(bool bcast) {
+    return bcast ? reinterpret_cast<const void*>(&sgn_nhwc_cluster_kernel<T, M, E, R, true>)
+                 : reinterpret_cast<const void*>(&sgn_nhwc_cluster_kernel<T, M, E, R, false>);
+}
+
+// The kernel launch_nhwc_cluster runs for r pixels per thread.
+template <typename T, typename M, int E>
+const void* nhwc_kernel(int r, bool bcast) {
+    if (r <= 1) return nhwc_kernel_r<T, M, E, 1>(bcast);
+    if (r <= 2) return nhwc_kernel_r<T, M, E, 2>(bcast);
+    if (r <= 4) return nhwc_kernel_r<T, M, E, 4>(bcast);
+    if (r <= 8) return nhwc_kernel_r<T, M, E, 8>(bcast);
+    return nhwc_kernel_r<T, M, E, kNhwcMaxR>(bcast);
+}
+
+template <typename T, typename M>
+const void* nhwc_kernel_for(int E, int r, bool bcast) {
+    constexpr int EV = VecWidth<T>::value;
+    if (E == EV) return nhwc_kernel<T, M, EV>(r, bcast);
+    if (E == EV / 2) return nhwc_kernel<T, M, EV / 2>(r, bcast);
+    if constexpr (EV >= 8)
+        if (E == EV / 4) return nhwc_kernel<T, M, EV / 4>(r, bcast);
+    return nullptr;
+}
+
+// The widest block-id range one exchange cluster (an image's K slices of one
+// channel block) occupies under the block-id layout of the kernel.  The
+// dispatcher starts workgroups in block-id order, so when every cluster's
+// range fits in the workgroups the device holds at once, the lowest
+// unfinished cluster can always become wholly resident and the launch never
+// waits on a workgroup that cannot start; beyond that, waits run into their
+// bound and slices are recomputed (correct, but far slower).
+int64_t nhwc_cluster_span(int64_t N, const NhwcPlan& p) {
+    int64_t span = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t u0 = n * p.K, u1 = n * p.K + p.K - 1;
+        const int64_t lo = ((u0 >> 3) * p.NCB) * 8 + (u0 & 7);
+        const int64_t hi = ((u1 >> 3) * p.NCB) * 8 + (u1 & 7);
+        if (hi - lo + 1 > span) span = hi - lo + 1;
+    }
+    return span;
+}
+
 template <typename T, typename M, int E, int R>
 hipError_t launch_nhwc_cluster_r(const NhwcClusterArgs<T, M>& ca, int64_t blocks, hipStream_t stream) {
     if (ca.skip_bcast)
@@ -517,6 +583,12 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, uint64_t*
     while (E > 1 && a.C / a.groups < E) E /= 2;
     NhwcPlan plan;
     if (E == 1 || !nhwc_cluster_plan(E, a.N, a.C, HW, a.groups, &plan)) return false;
+    const void* kernel = a.dtype == 0
+        ? (a.param_dtype == 0 ? nhwc_kernel_for<float, float>(E, plan.R, a.skip_broadcast)
+                              : nhwc_kernel_for<float, half_t>(E, plan.R, a.skip_broadcast))
+        : (a.param_dtype == 0 ? nhwc_kernel_for<half_t, float>(E, plan.R, a.skip_broadcast)
+                              : nhwc_kernel_for<half_t, half_t>(E, plan.R, a.skip_broadcast));
+    if (!kernel || nhwc_cluster_span(a.N, plan) > resident_workgroups(kernel)) return false;
     static const char* const kNames[] = {"sgn.cluster.nhwc.vec4", "sgn.cluster.nhwc.vec8",
                                          "sgn.cluster.nhwc.vec16"};
     *route = kNames[E * size == 16 ? 2 : E * size == 8 ? 1 : 0];

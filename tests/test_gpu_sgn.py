@@ -147,6 +147,13 @@ NHWC_LIMIT_CASES = [
     (1, 16, 9, 7, F32, 4, True, "sgn.cluster.nhwc.vec16"),        # float32, 4 channels/group, 1 slice
     (2, 2560, 8, 8, F32, 32, False, "sgn.cluster.nhwc.vec16"),    # 640 vectors per pixel, 3 pixel lanes
     (600, 16, 2, 2, F32, 2, True, "sgn.cluster.nhwc.vec16"),      # one slice per image: no exchange
+    # Residency (MI355X: 256 CUs, two workgroups each at 16 pixels per
+    # thread): 704 workgroups, more than are resident at once, but each
+    # image's 88 within reach of one another: one launch in two rounds.
+    (8, 640, 64, 64, F16, 32, False, "sgn.cluster.nhwc.vec16"),
+    # One image of 1024 workgroups spread over 904 block ids, more than the
+    # device holds at once: the split route.
+    (1, 512, 256, 256, F16, 32, False, "sgn.split.nhwc.vec16"),
 ]
 
 
