@@ -610,19 +610,25 @@ sgn_finalize_kernel(const Partial* __restrict__ part, float2* __restrict__ stat,
 // ------------------------------------------------------------------ host side
 constexpr int64_t kVectorsPerBlock = 256 * kUnroll;  // one unrolled pass of a 256-thread block
 
-constexpr int kNhwcRowsPerThread = 2;                // pixel rows per thread in the nhwc tiling
+constexpr int kNhwcRowsPerThread = 2;                // least pixel rows per thread in the nhwc tiling
+constexpr int64_t kSplitTargetBlocks = 2048;         // nhwc tiling: about 8 workgroups per CU in all
 
 // Blocks per image (nhwc) or per (n, group) (group tiling) of the split
-// route.  The nhwc tiling gives each thread kNhwcRowsPerThread pixels, so a
-// small image still spreads over many CUs; the group tiling gives each block
-// one unrolled pass of vectors.
-int64_t split_blocks(int dtype, int64_t C, int64_t HW, int64_t groups, bool channels_last) {
+// route.  The nhwc tiling gives each thread at least kNhwcRowsPerThread
+// pixels, so a small image still spreads over many CUs, and large images
+// more, so that the N images together take about kSplitTargetBlocks blocks
+// (thousands of blocks of two pixels per thread spent their time in each
+// block's reduction: 2.4 TB/s on a 256x256x512 float16 image); the group
+// tiling gives each block one unrolled pass of vectors.
+int64_t split_blocks(int dtype, int64_t N, int64_t C, int64_t HW, int64_t groups, bool channels_last) {
     const int64_t ev = dtype == 0 ? 4 : 8;
     int64_t B;
     if (channels_last && C % ev == 0 && C / ev <= 256) {
         const int64_t P = 256 / (C / ev);
         const int64_t ppb = P * kNhwcRowsPerThread;
         B = (HW + ppb - 1) / ppb;
+        const int64_t target = (kSplitTargetBlocks + N - 1) / (N > 0 ? N : 1);
+        if (B > target) B = target;
     } else {
         const int64_t per_unit = channels_last ? HW * C : (C / groups) * HW;  // image / group
         B = (per_unit + ev * kVectorsPerBlock - 1) / (ev * kVectorsPerBlock);
@@ -763,7 +769,7 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
         return err;
 
     // ---- split route
-    const int B = int(split_blocks(a.dtype, a.C, HW, a.groups, a.channels_last));
+    const int B = int(split_blocks(a.dtype, a.N, a.C, HW, a.groups, a.channels_last));
     const dim3 fin_grid = dim3(unsigned(NG));
 
     if (nhwc_e > 1) {
@@ -839,8 +845,7 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
 
 int64_t sgn_partials_per_group(int dtype, int64_t N, int64_t C, int64_t H, int64_t W,
                                int64_t groups, bool channels_last) {
-    (void)N;
-    const int64_t b = split_blocks(dtype, C, H * W, groups, channels_last);
+    const int64_t b = split_blocks(dtype, N, C, H * W, groups, channels_last);
     const int64_t k = channels_last ? kNhwcMaxK : kClusterMaxK;
     return b >= k ? b : k;
 }
