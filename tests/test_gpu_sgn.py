@@ -154,6 +154,8 @@ NHWC_LIMIT_CASES = [
     # One image of 1024 workgroups spread over 904 block ids, more than the
     # device holds at once: the split route.
     (1, 512, 256, 256, F16, 32, False, "sgn.split.nhwc.vec16"),
+    # 1344 workgroups, more than two rounds of the 512 resident: split.
+    (8, 320, 128, 128, F16, 32, False, "sgn.split.nhwc.vec16"),
 ]
 
 
