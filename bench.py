@@ -18,6 +18,12 @@ last-level cache, and between two visits of any workload at least 1.8 GB of
 other traffic passes, so every op starts from a cold cache.
 
 Prints one JSON line on stdout (progress goes to stderr).
+
+``--configs`` instead times each of the five reference workloads on its own:
+every invocation is preceded by a 1 GiB copy (so it starts from a cold
+cache) and bracketed by HIP events; the oracle is timed on one thread on the
+same inputs (median of 3 runs for the small workloads, one run for the two
+large ones).  It prints one JSON object and a markdown table (stderr).
 """
 from __future__ import annotations
 
@@ -203,6 +209,100 @@ def cpu_baseline(budget_s=14.0):
             "per_op": per_op, "host": host_cpu()}
 
 
+def oracle_runner(w, x):
+    """A call of the oracle over the whole workload, with its outputs."""
+    import oracle
+
+    a = w.attrs
+    if w.op in ("skip_rms_norm", "skip_layer_norm"):
+        hidden = x["input"].shape[-1]
+        inp, skp = x["input"].reshape(-1, hidden), x["skip"].reshape(-1, hidden)
+        return lambda: oracle.skip_rms_norm(inp, skp, x["gamma"], x.get("bias"), a["epsilon"],
+                                            want_inv_std_var="inv_std_var" in w.outputs,
+                                            want_sum="input_skip_bias_sum" in w.outputs)
+    if w.op == "gated_rms_norm":
+        return lambda: oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], a["epsilon"])
+    return lambda: oracle.skip_group_norm(x["X"], x["gamma"], x["beta"], x["skip"], x.get("bias"),
+                                          groups=a["groups"], activation=a["activation"],
+                                          epsilon=a["epsilon"], channels_last=a["channels_last"],
+                                          want_sum="S" in w.outputs)
+
+
+def config_table(args):
+    """Each reference workload alone, cold, K timed invocations (see the
+    module docstring)."""
+    import torch
+    import group_normalization_amd as gn
+    from group_normalization_amd import workloads
+
+    torch.cuda.set_device(0)
+    hev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        gn.copy_(dst, src)
+    e0, e1 = hev.create(), hev.create()
+    hev.record(e0, stream)
+    for _ in range(10):
+        gn.copy_(dst, src)
+    hev.record(e1, stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * COPY_BYTES * 10 / (hev.elapsed_ms(e0, e1) * 1e-3) / 1e9
+    rows = []
+    for name in workloads.ORDER:
+        w = workloads.WORKLOADS[name]
+        o = Op(name, torch, gn, workloads)
+        for _ in range(args.warmup):
+            gn.copy_(dst, src)
+            o.run()
+        pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+        for a, b in pairs:
+            gn.copy_(dst, src)  # evicts the last-level cache
+            hev.record(a, stream)
+            o.run()
+            hev.record(b, stream)
+        torch.cuda.synchronize()
+        us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b in pairs])
+        for a, b in pairs:
+            hev.destroy(a)
+            hev.destroy(b)
+        med = float(np.median(us))
+        row = {"workload": name, "bytes": o.bytes, "invocations": args.steps,
+               "median_us": round(med, 3), "min_us": round(float(us.min()), 3),
+               "p90_us": round(float(np.percentile(us, 90)), 3),
+               "gbps": round(o.bytes / med / 1e3, 1), "frac_of_peak": round(o.bytes / med / 1e3 / PEAK_GBPS, 4),
+               "frac_of_copy": round(o.bytes / med / 1e3 / copy_gbps, 4)}
+        del o
+        if not args.no_cpu_baseline:
+            x = workloads.generate(w)
+            run = oracle_runner(w, x)
+            reps = 3 if workloads.io_bytes(w) < 100e6 else 1
+            secs = []
+            for _ in range(reps):
+                t0 = time.perf_counter_ns()
+                run()
+                secs.append((time.perf_counter_ns() - t0) * 1e-9)
+            row["oracle_s"] = round(float(np.median(secs)), 4)
+            row["oracle_runs"] = reps
+            row["oracle_gbps"] = round(workloads.io_bytes(w) / float(np.median(secs)) / 1e9, 4)
+            del x
+        rows.append(row)
+        log(f"{name}: median {med:.2f} us ({row['gbps']} GB/s)")
+    for e in (e0, e1):
+        hev.destroy(e)
+    out = {"configs": rows, "copy_ceiling_gbps": round(copy_gbps, 1), "oracle_threads": 1,
+           "host": host_cpu()}
+    lines = ["| workload | median us | min us | p90 us | GB/s | % of 8 TB/s | % of copy | oracle s | oracle GB/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['workload']} | {r['median_us']} | {r['min_us']} | {r['p90_us']} | {r['gbps']} | "
+                     f"{100 * r['frac_of_peak']:.1f} | {100 * r['frac_of_copy']:.1f} | "
+                     f"{r.get('oracle_s', '')} | {r.get('oracle_gbps', '')} |")
+    print("\n".join(lines), file=sys.stderr)
+    print(json.dumps(out), flush=True)
+
+
 def host_cpu():
     """Logical CPU count and model name of the machine the oracle ran on."""
     model = None
@@ -223,11 +323,16 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--configs", action="store_true",
+                    help="time each reference workload alone (cold), and the oracle on it")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the operators need no communication and this "
               "build runs on a single MI355X; use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.configs:
+        config_table(args)
+        return
 
     import torch
     import group_normalization_amd as gn
