@@ -49,6 +49,10 @@ CASES = [
     ((211, 130), 130, F32),      # 65 eight-byte float32 vectors: segment (float32 never tiles)
     ((77, 2, 148), 148, F16),    # 37 eight-byte vectors: 13 rows per wave
     ((93, 150), 150, F16),       # 75 four-byte vectors: 13 rows per wave of 16 per lane
+    ((1, 132), 132, F16),        # one row: one tile, one row in it
+    ((3, 2, 130), 130, F16),     # six rows: fewer than one tile
+    ((1, 16384), 16384, F16),    # one row through the row route
+    ((1, 40000), 40000, F32),    # one row through the two-pass route
     # around the tile route's bounds: segment
     ((99, 264), 264, F16),       # 33 sixteen-byte vectors
     ((41, 124), 124, F16),       # 31 eight-byte vectors
