@@ -301,6 +301,128 @@ ssln_block_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     }
 }
 
+// Rows of at most 48 accesses: L lanes per row (the row's access count
+// rounded up to a power of two), 64 / L rows per wave and RPT rows per
+// thread in flight; each lane holds one access of each of its rows, and a
+// row's sums are a butterfly inside its L-lane segment (no LDS, no
+// barrier).  Lanes past the row's end re-read its last access and discard
+// it; rows past the last re-read the last row and store nothing.
+template <typename T, int E, int L, int RPT, bool CENTER>
+__global__ void __launch_bounds__(256)
+ssln_segment_kernel(const T* __restrict__ input, const T* __restrict__ skip,
+                    const T* __restrict__ gamma, const T* __restrict__ beta,
+                    const T* __restrict__ bias, T* __restrict__ output, float* __restrict__ mean,
+                    float* __restrict__ inv_std_var, T* __restrict__ sum,
+                    int64_t rows, int nvec, float hidden_f, float eps, uint32_t beta_mask) {
+    using V = Vec<T, E>;
+    constexpr int SEGS = 256 / L;  // rows per block per step
+    const int seg = threadIdx.x / L, l = threadIdx.x % L;
+    const int first_lane = (threadIdx.x & 63) & ~(L - 1);  // the segment's lane 0 in the wave
+    const int64_t tile = int64_t(blockIdx.x) * SEGS * RPT;
+    const int ic = l < nvec ? l : nvec - 1;
+    const bool has_bias = bias != nullptr;
+
+    V xs[RPT], ks[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        const int64_t row = tile + int64_t(k) * SEGS + seg;
+        const int64_t rc = row < rows ? row : rows - 1;
+        xs[k] = load_vec_stream<T, E>(input, rc * nvec + ic);
+        ks[k] = load_vec_stream<T, E>(skip, rc * nvec + ic);
+    }
+    const V gv = load_vec<T, E>(gamma, ic);
+    V bt = {};
+    if constexpr (CENTER) bt = mask_bits(load_vec<T, E>(beta, ic), beta_mask);
+    V bv = {};
+    if (has_bias) bv = load_vec<T, E>(bias, ic);
+
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        const int64_t row = tile + int64_t(k) * SEGS + seg;
+        const bool store = row < rows && l < nvec;
+        V ss;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            residual_sum<T>(to_f32(xs[k].v[e]), to_f32(ks[k].v[e]), has_bias, to_f32(bv.v[e]), ss.v[e]);
+        // With the mean removed, sums are taken about the row's first element
+        // S[0], which the segment's lane 0 holds.
+        float shift = 0.0f, md = 0.0f, r;
+        if constexpr (CENTER) shift = __shfl(to_f32(ss.v[0]), first_lane, 64);
+        float part = 0.0f;
+        if (l < nvec) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float sv = to_f32(ss.v[e]);
+                if constexpr (CENTER) part += sv - shift;
+                else part = fmaf_(sv, sv, part);
+            }
+        }
+        if constexpr (!CENTER) {
+            r = inv_sqrt(segment_sum<L>(part) / hidden_f + eps);
+        } else {
+            md = segment_sum<L>(part) / hidden_f;
+            float dev = 0.0f;
+            if (l < nvec) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = (to_f32(ss.v[e]) - shift) - md;
+                    dev = fmaf_(d, d, dev);
+                }
+            }
+            r = inv_sqrt(segment_sum<L>(dev) / hidden_f + eps);
+        }
+        V out;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if constexpr (CENTER)
+                out.v[e] = from_f32<T>(((to_f32(ss.v[e]) - shift) - md) * r * to_f32(gv.v[e]) +
+                                       to_f32(bt.v[e]));
+            else
+                out.v[e] = from_f32<T>(to_f32(ss.v[e]) * r * to_f32(gv.v[e]));
+        }
+        if (store) {
+            store_vec_stream<T, E>(output, row * nvec + l, out);
+            if (sum) store_vec_stream<T, E>(sum, row * nvec + l, ss);
+        }
+        if (row < rows && l == 0) {
+            if (inv_std_var) inv_std_var[row] = r;
+            if (mean) mean[row] = shift + md;
+        }
+    }
+}
+
+template <typename T, int E, int L>
+hipError_t launch_segment(const SslnArgs& a, int nvec, hipStream_t stream) {
+    // About 64 bytes of each input per thread in flight, at most 16 rows.
+    constexpr int VB = E * int(sizeof(T));
+    constexpr int RPT = 64 / VB < 16 ? 64 / VB : 16;
+    constexpr int rows_per_block = (256 / L) * RPT;
+    const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+    auto args = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                           static_cast<const T*>(a.input), static_cast<const T*>(a.skip),
+                           static_cast<const T*>(a.gamma),
+                           static_cast<const T*>(a.beta ? a.beta : a.gamma),
+                           static_cast<const T*>(a.bias), static_cast<T*>(a.output), a.mean,
+                           a.inv_std_var, static_cast<T*>(a.sum), a.rows, nvec, float(a.hidden),
+                           a.epsilon, a.beta ? ~0u : 0u);
+    };
+    if (a.center) args(ssln_segment_kernel<T, E, L, RPT, true>);
+    else args(ssln_segment_kernel<T, E, L, RPT, false>);
+    return hipGetLastError();
+}
+
+template <typename T, int E>
+hipError_t launch_segment_for(const SslnArgs& a, int nvec, hipStream_t stream) {
+    if (nvec <= 1) return launch_segment<T, E, 1>(a, nvec, stream);
+    if (nvec <= 2) return launch_segment<T, E, 2>(a, nvec, stream);
+    if (nvec <= 4) return launch_segment<T, E, 4>(a, nvec, stream);
+    if (nvec <= 8) return launch_segment<T, E, 8>(a, nvec, stream);
+    if (nvec <= 16) return launch_segment<T, E, 16>(a, nvec, stream);
+    if (nvec <= 32) return launch_segment<T, E, 32>(a, nvec, stream);
+    return launch_segment<T, E, 64>(a, nvec, stream);
+}
+
 template <typename T, int E, int NV, int WPR>
 hipError_t launch_wave_nv(const SslnArgs& a, int nvec, hipStream_t stream) {
     constexpr int rows_per_block = kWavesPerBlock / WPR;
@@ -359,13 +481,21 @@ template <int E> constexpr int kMaxNvRowBlock = E == 1 ? 32 : 16;
 
 template <typename T, int E>
 hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char** route) {
-    static const char* const kNames[3][4] = {
+    static const char* const kNames[4][4] = {
         {"ssln.wave.scalar", "ssln.wave.vec4", "ssln.wave.vec8", "ssln.wave.vec16"},
         {"ssln.wave2.scalar", "ssln.wave2.vec4", "ssln.wave2.vec8", "ssln.wave2.vec16"},
-        {"ssln.rowblock.scalar", "ssln.rowblock.vec4", "ssln.rowblock.vec8", "ssln.rowblock.vec16"}};
+        {"ssln.rowblock.scalar", "ssln.rowblock.vec4", "ssln.rowblock.vec8", "ssln.rowblock.vec16"},
+        {"ssln.segment.scalar", "ssln.segment.vec4", "ssln.segment.vec8", "ssln.segment.vec16"}};
     constexpr int kName = E == 1 ? 0 : E * sizeof(T) == 16 ? 3 : E * sizeof(T) == 8 ? 2 : 1;
     constexpr int NVL = kNvLane<T, E>;
     const int64_t nvec = a.hidden / E;
+    // Lane groups for rows of up to 48 accesses (64 lanes for 33-48: 1.01-1.11x
+    // the one-wave route on float16 rows of 264-384; from 63 accesses on the
+    // one-wave route measured faster, 1.1-1.15x at 504 and 512).
+    if (nvec <= 48) {
+        *route = kNames[3][kName];
+        return launch_segment_for<T, E>(a, int(nvec), stream);
+    }
     if (nvec <= 64 * NVL) {
         *route = kNames[0][kName];
         return launch_wave<T, E, NVL, 1>(a, int(nvec), stream);

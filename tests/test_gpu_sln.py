@@ -55,6 +55,9 @@ SHAPES = [
     ((2, 40000), F16, True, True),      # block route (three passes), 16-byte vectors
     ((3, 20002), F32, True, False),     # block route, 8-byte vectors, ragged step
     ((2, 8193), F16, False, True),      # block route, scalars
+    ((1000, 128), F16, True, True),     # lane groups: 16 lanes per row
+    ((64, 6), F32, True, False),        # lane groups of 4
+    ((31, 7), F16, True, True),         # scalars in lane groups of 8
 ]
 
 

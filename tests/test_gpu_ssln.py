@@ -65,6 +65,19 @@ SHAPES = [
     ((4, 4097), F16, False),     # odd width: scalars, four waves per row
     ((3, 6002), F32, True),      # float32 8-byte vectors, four waves per row
     ((2, 8193), F16, True),      # odd and wider than the scalar registers: block route
+    # rows of at most 32 accesses: lane groups, several rows per wave
+    ((1000, 128), F16, True),    # 16 sixteen-byte vectors: 16 lanes per row, 4 rows per thread
+    ((777, 256), F16, False),    # 32 vectors: 32 lanes per row
+    ((333, 40), F16, True),      # 5 vectors in 8 lanes
+    ((64, 6), F32, False),       # 3 eight-byte vectors in 4 lanes
+    ((129, 100), F16, True),     # 25 eight-byte vectors in 32 lanes
+    ((50, 30), F16, False),      # 15 four-byte vectors in 16 lanes, 16 rows per thread
+    ((31, 7), F16, True),        # 7 scalars in 8 lanes
+    ((5, 32), F32, True),        # 8 vectors
+    ((3, 5, 24), F32, False),    # rank 3, 6 sixteen-byte vectors
+    ((200, 320), F16, True),     # 40 vectors: 64-lane groups, 4 rows per thread
+    ((97, 384), F16, False),     # 48 vectors: the last lane-group width
+    ((33, 392), F16, True),      # 49 vectors: one wave per row
 ]
 
 
@@ -75,6 +88,8 @@ def expected_route(shape, dt):
     E = width // size
     name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
     nvec = hidden // E
+    if nvec <= 48:
+        return f"ssln.segment.{name}"
     per_lane = 4 if E > 1 and width == 16 else 8 if E > 1 and width == 8 else 16
     if nvec <= 64 * per_lane:
         return f"ssln.wave.{name}"
