@@ -19,10 +19,15 @@
 //
 // channel-block cluster (NHWC, in sgn_nhwc.hip; pixels a whole number of
 //   16-, 8- or 4-byte vectors no wider than a group, images of up to
-//   64 x 16 x (256 / vectors per block) pixels): workgroups own (image,
-//   pixel slice, channel block) tiles, hold S in VGPRs and exchange
-//   per-group moments the same way.  One launch, exactly the operator's
-//   traffic.
+//   64 x 16 x (256 / vectors per block) pixels, and only while each
+//   exchange cluster fits in the workgroups the device holds at once and
+//   the grid is at most two rounds of them): workgroups own (image, pixel
+//   slice, channel block) tiles, hold S in VGPRs and exchange per-group
+//   moments the same way.  One launch, exactly the operator's traffic.
+//
+// Under HIP graph capture the cluster routes' tags are cleared by a store
+// kernel ahead of each launch and the tag is constant (a replay repeats the
+// arguments of the capture).
 //
 // split (everything else), three launches on one stream: the
 //   pages' "partial group statistics / combine / normalize" structure,
@@ -36,10 +41,11 @@
 //   Tilings of passes 1 and 3:
 //   nhwc   (NHWC, C a whole number of 16-, 8- or 4-byte vectors, at most
 //          256 of them):
-//          a block covers a run of pixels of one image and all channels.
-//          Thread t owns channel vector t % Cv at pixels t / Cv + k * P,
-//          P = 256 / Cv, so its channels (and their bias, gamma, beta and
-//          group) never change.  Per-channel moments are merged over the
+//          a block covers a run of pixels of one image and all channels
+//          (at least two pixels per thread, more where the grid would
+//          exceed about 2048 blocks).  Thread t owns channel vector t % Cv
+//          at pixels t / Cv + k * P, P = 256 / Cv, so its channels (and
+//          their bias, gamma, beta and group) never change.  Per-channel moments are merged over the
 //          pixel lanes, then over each group's channels, through LDS.
 //   group  (NCHW groups too large for one workgroup; the scalar route of
 //          both layouts): a block covers a slice of one (n, group)'s
