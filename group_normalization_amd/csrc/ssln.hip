@@ -5,7 +5,13 @@
 // r = 1/sqrt(mean(S^2) + epsilon), output = S * r * gamma; optional outputs
 // S, mean (zero for the simplified form) and inv_std_var (r).
 //
+// The same kernels with the mean removed (CENTER) give the non-simplified
+// skip layer normalization: mean = mean(S), r = 1/sqrt(mean((S - mean)^2) +
+// epsilon), output = (S - mean) * r * gamma (+ beta).
+//
 // Routes:
+//   segment  rows of at most 48 accesses: a power-of-two group of lanes per
+//          row, several rows per wave and per thread (ssln_segment_kernel).
 //   wave   one wave64 per row (wave2: two; rows of up to 4 sixteen-byte,
 //          8 eight-byte or 16 narrower accesses per lane); lane l holds the
 //          row's vectors l, l+64, ...
@@ -20,8 +26,8 @@
 //          8192 elements): the wave sums meet in LDS and are added in wave
 //          order.
 //   block  one 256-thread workgroup per row for any wider row: S is formed
-//          twice (once for the statistic, once for the output), reading the
-//          inputs twice.
+//          twice (once for the statistic, once for the output; three times
+//          with the mean removed), reading the inputs again each time.
 // Statistic: each lane accumulates its own squares in float32 (FMA), then a
 // fixed butterfly sums the 64 lanes (DPP inside 16-lane rows, then two
 // cross-row exchanges), so every lane holds the same total and the result
