@@ -1,0 +1,133 @@
+"""Seeded random parity: shapes, dtypes, optional inputs and outputs and
+unaligned base addresses drawn at random (fixed seeds, so every run checks
+the same cases) for every operator, each compared with the oracle element by
+element (S bitwise).  The draws cover the length buckets that select the
+different routes and access widths, so that combinations the hand-written
+cases miss are still exercised."""
+import numpy as np
+import pytest
+import torch
+
+import group_normalization_amd as gn
+import oracle
+from parity import assert_bitwise, assert_close, to_host
+
+pytestmark = pytest.mark.gpu
+
+F32, F16 = np.float32, np.float16
+MAX_ELEMS = 1 << 21
+N_CASES = 64
+
+
+def dev(a, offset=0):
+    """a on the GPU, starting `offset` elements into a fresh buffer (a
+    contiguous view whose base address is shifted)."""
+    if a is None:
+        return None
+    flat = torch.empty(a.size + offset, dtype=torch.float16 if a.dtype == F16 else torch.float32,
+                       device="cuda")
+    view = flat[offset:]
+    view.copy_(torch.from_numpy(np.ascontiguousarray(a).ravel()))
+    return view.view(a.shape)
+
+
+def draw_length(rng, buckets):
+    los, his, ps = zip(*buckets)
+    i = rng.choice(len(buckets), p=np.array(ps) / sum(ps))
+    return int(rng.integers(los[i], his[i] + 1))
+
+
+def normal(rng, shape, dtype, scale=1.0):
+    return (scale * rng.standard_normal(shape)).astype(dtype)
+
+
+def uniform(rng, shape, dtype):
+    return rng.uniform(0.5, 1.5, shape).astype(dtype)
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+@pytest.mark.parametrize("center", [False, True], ids=["ssln", "sln"])
+def test_row_norms(center, case):
+    rng = np.random.default_rng(1000 + case + (500 if center else 0))
+    dt = F16 if rng.random() < 0.6 else F32
+    hidden = draw_length(rng, [(1, 64, 4), (65, 2048, 3), (2049, 12000, 2), (12001, 40000, 1)])
+    rows = int(rng.integers(1, max(2, min(300, MAX_ELEMS // hidden)) + 1))
+    shape = (rows, hidden) if rng.random() < 0.7 else (1, rows, hidden)
+    x, k = normal(rng, shape, dt), normal(rng, shape, dt)
+    gamma = uniform(rng, hidden, dt)
+    bias = normal(rng, hidden, dt, 0.1) if rng.random() < 0.5 else None
+    beta = normal(rng, hidden, dt, 0.1) if center and rng.random() < 0.6 else None
+    off = int(rng.choice([0, 0, 0, 1, 2, 4]))
+    eps = float(rng.choice([1e-6, 1e-5]))
+    want = {w: bool(rng.random() < 0.5) for w in ("mean", "inv", "sum")}
+    if center:
+        ref = oracle.skip_layer_norm(x.reshape(-1, hidden), k.reshape(-1, hidden), gamma, beta, bias, eps,
+                                     want_mean=True, want_inv_std_var=True, want_sum=True)
+        out = gn.skip_layer_norm(dev(x, off), dev(k, off), dev(gamma), dev(beta), dev(bias), eps,
+                                 want_mean=want["mean"], want_inv_std_var=want["inv"], want_sum=want["sum"])
+    else:
+        ref = oracle.skip_rms_norm(x.reshape(-1, hidden), k.reshape(-1, hidden), gamma, bias, eps,
+                                   want_mean=True, want_inv_std_var=True, want_sum=True)
+        out = gn.skip_rms_norm(dev(x, off), dev(k, off), dev(gamma), dev(bias), eps,
+                               want_mean=want["mean"], want_inv_std_var=want["inv"], want_sum=want["sum"])
+    route = gn.last_route()
+    torch.cuda.synchronize()
+    what = f"{route} {dt.__name__} {shape} bias={bias is not None} beta={beta is not None} off={off}"
+    assert_close(to_host(out.output).reshape(-1, hidden), ref[0], f"output ({what})")
+    if want["sum"]:
+        assert_bitwise(to_host(out.input_skip_bias_sum).reshape(-1, hidden), ref[3], f"S ({what})")
+    if want["inv"]:
+        assert_close(to_host(out.inv_std_var).reshape(-1), ref[2].reshape(-1), f"inv_std_var ({what})")
+    if want["mean"]:
+        assert_close(to_host(out.mean).reshape(-1), ref[1].reshape(-1), f"mean ({what})")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_gated(case):
+    rng = np.random.default_rng(2000 + case)
+    dt = F16 if rng.random() < 0.6 else F32
+    C = draw_length(rng, [(1, 64, 3), (65, 1024, 4), (1025, 9000, 2), (9001, 40000, 1)])
+    rows = int(rng.integers(1, max(2, min(400, MAX_ELEMS // C)) + 1))
+    X, G = normal(rng, (rows, C), dt), normal(rng, (rows, C), dt)
+    scale = uniform(rng, C, dt)
+    off = int(rng.choice([0, 0, 0, 1, 2, 4]))
+    ref = oracle.gated_rms_norm(X, scale, G, 1e-5)
+    Y = gn.gated_rms_norm(dev(X, off), dev(scale), dev(G, off), 1e-5)
+    route = gn.last_route()
+    torch.cuda.synchronize()
+    assert_close(to_host(Y), ref, f"Y ({route} {dt.__name__} rows={rows} C={C} off={off})")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_skip_group_norm(case):
+    rng = np.random.default_rng(3000 + case)
+    T = F16 if rng.random() < 0.6 else F32
+    M = F16 if rng.random() < 0.5 else F32
+    groups = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    cpg = draw_length(rng, [(1, 8, 2), (9, 48, 3)])
+    C = groups * cpg
+    N = int(rng.integers(1, 4))
+    H, W = int(rng.integers(1, 25)), int(rng.integers(1, 25))
+    while N * C * H * W > MAX_ELEMS:
+        H = max(1, H // 2)
+    cl = int(rng.random() < 0.6)
+    shape = (N, H, W, C) if cl else (N, C, H, W)
+    X = normal(rng, shape, T)
+    bcast = bool(rng.random() < 0.3)
+    skip = normal(rng, (N, C), T) if bcast else normal(rng, shape, T)
+    gamma, beta = uniform(rng, C, M), normal(rng, C, M, 0.1)
+    bias = normal(rng, C, T, 0.1) if rng.random() < 0.5 else None
+    act = int(rng.random() < 0.5)
+    want_sum = bool(rng.random() < 0.5)
+    off = int(rng.choice([0, 0, 0, 1, 4]))
+    ref_y, ref_s = oracle.skip_group_norm(X, gamma, beta, skip, bias, groups=groups, activation=act,
+                                          epsilon=1e-5, channels_last=cl, want_sum=True)
+    out = gn.skip_group_norm(dev(X, off), dev(gamma), dev(beta), dev(skip), dev(bias), groups=groups,
+                             activation=act, epsilon=1e-5, channels_last=cl, want_sum=want_sum)
+    route = gn.last_route()
+    torch.cuda.synchronize()
+    what = (f"{route} {T.__name__}/{M.__name__} {'nhwc' if cl else 'nchw'} {shape} g={groups} "
+            f"bcast={bcast} bias={bias is not None} act={act} off={off}")
+    assert_close(to_host(out.Y), ref_y, f"Y ({what})")
+    if want_sum:
+        assert_bitwise(to_host(out.S), ref_s, f"S ({what})")
