@@ -26,9 +26,10 @@
  *     for the last non-OK status of the calling thread is returned by
  *     skipnorm_last_error().
  *   - Outputs may not overlap inputs or each other (SN_ERR_ALIAS).
- *   - Pointers need no particular alignment; 16-byte aligned tensors whose
- *     rows are whole 16-byte vectors take the vectorized kernels, the rest a
- *     scalar route with the same results up to float32 summation order.
+ *   - Pointers need no particular alignment: each call reads and writes in
+ *     the widest of 16-, 8- and 4-byte vectors that divides a row (pixel,
+ *     image plane) and every base address, else element by element, with
+ *     the same results up to float32 summation order.
  *   - Zero-sized leading dimensions are valid and launch nothing.  A row
  *     (hidden, span) or one SkipGroupNorm image (C*H*W) may hold at most
  *     2^30 elements.
@@ -104,8 +105,8 @@ sn_status skip_rms_norm(sn_dtype T, int64_t rows, int64_t hidden,
  * form of SkipSimplifiedLayerNormalization, whose page describes the `mean`
  * output as the per-row mean (zero only for the simplified form) and
  * `inv_std_var` as the inverse standard deviation (the inverse RMS only for
- * the simplified form); the optional `beta` is added after the scaling, as
- * in the ONNX Runtime operator of that form.
+ * the simplified form); the optional `beta` is added after the scaling
+ * (layer normalization's affine form).
  *   S[j]  = round_T((input[j] + skip[j]) + bias[j])   (bias term only if given)
  *   mu    = sum_j S[j] / hidden
  *   r     = 1 / sqrt(sum_j (S[j] - mu)^2 / hidden + epsilon)
@@ -203,12 +204,13 @@ int skipnorm_abi_version(void);
 /* Route selection for every later call in the process, so that tests can
  * cover each kernel family on the same shapes:
  *   0 = automatic (the default);
- *   1 = scalar accesses (16-byte vectors off);
+ *   1 = element-by-element accesses (vectors off);
  *   2 = vectorized where the preconditions hold (same as automatic, except
  *       that gated_rms_norm keeps one power-of-two lane group per row for
  *       every row length, where automatic packs rows that are not a power
  *       of two of vectors back to back);
- *   3 = skip_rms_norm / gated_rms_norm: one workgroup per row;
+ *   3 = skip_rms_norm / skip_layer_norm / gated_rms_norm: one workgroup per
+ *       row, two passes, element by element;
  *       skip_group_norm: the three-launch split route with scalar accesses;
  *   4 = skip_group_norm: the three-launch split route (vectorized where the
  *       preconditions hold) even where one workgroup per group would apply;
@@ -217,16 +219,18 @@ int skipnorm_abi_version(void);
  * and returns the current one. */
 int skipnorm_force_route(int route);
 
-/* SkipGroupNorm's cluster route (NCHW) spreads one (n, group) over up to 8
- * workgroups that exchange partial moments; a workgroup waits at most this
- * long for another's moments and otherwise recomputes them itself with the
- * same arithmetic (results are identical either way).  Sets the wait for
+/* SkipGroupNorm's single-launch routes spread each (n, group) over several
+ * workgroups (NCHW: up to 8; NHWC: up to 64 pixel slices of an image) that
+ * exchange partial moments; a workgroup waits at most this long for
+ * another's moments and otherwise recomputes them itself with the same
+ * arithmetic (results are identical either way).  Sets the wait for
  * later calls in the process (negative: the default, 100 us) and returns the
  * previous value.  A test hook: 0 forces every recomputation path. */
 int skipnorm_set_exchange_timeout_us(int microseconds);
 
 /* Name of the route the calling thread's last successful op call took
- * (e.g. "ssln.wave", "ssln.scalar", "gated.segment", "sgn.nhwc"). */
+ * (e.g. "ssln.wave2.vec16", "ssln.segment.vec8", "gated.tile.vec8",
+ * "sgn.cluster.nhwc.vec16", "sgn.split.nchw.scalar"). */
 const char* skipnorm_last_route(void);
 
 /* Measurement helper: copies `bytes` bytes from src to dst with one kernel
