@@ -213,7 +213,7 @@ int skipnorm_abi_version(void);
  *       row, two passes, element by element;
  *       skip_group_norm: the three-launch split route with scalar accesses;
  *   4 = skip_group_norm: the three-launch split route (vectorized where the
- *       preconditions hold) even where one workgroup per group would apply;
+ *       preconditions hold) even where a single-launch route would apply;
  *       others: automatic.
  * Returns the previous value; an unknown value leaves the setting unchanged
  * and returns the current one. */
