@@ -684,6 +684,7 @@ hipError_t launch_cluster(const ClusterArgs<T, M>& ca, int64_t blocks, hipStream
 // Workgroups per (n, group) of the cluster route for a group of Kv vectors
 // (0: the group is too large for it).
 int cluster_k(int64_t Kv, int64_t NG, int max_r) {
+    if (Kv <= int64_t(kClusterThreads) * kSingleSliceMaxR) return 1;  // one slice, no exchange
     const int64_t cap = int64_t(kClusterThreads) * max_r;
     const int64_t k_fit = (Kv + cap - 1) / cap;
     if (k_fit > kClusterMaxK) return 0;
@@ -745,8 +746,9 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
             ca.beta = beta;
             ca.part = part;
             ca.flags = reinterpret_cast<uint64_t*>(stat + NG);
-            if (hipError_t e = clear_publication_tags(a, ca.flags, NG * Kc, stream); e != hipSuccess)
-                return e;
+            if (Kc > 1)
+                if (hipError_t e = clear_publication_tags(a, ca.flags, NG * Kc, stream); e != hipSuccess)
+                    return e;
             ca.tag = a.tag;
             ca.timeout_ticks = a.exchange_timeout_ticks;
             ca.HW = HW;

@@ -415,6 +415,7 @@ bool nhwc_cluster_plan(int E, int64_t N, int64_t C, int64_t HW, int64_t groups, 
             if (K < k_fit) K = k_fit;
             if (K > kNhwcMaxK) K = kNhwcMaxK;
             if (K > HW) K = HW;
+            if ((HW + P - 1) / P <= kSingleSliceMaxR) K = 1;  // one slice, no exchange
             const int64_t pps = (HW + K - 1) / K;
             K = (HW + pps - 1) / pps;  // no empty slices
             const int64_t grid = N * ncb * K;
@@ -539,8 +540,9 @@ hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, int E, void
     ca.beta = static_cast<const M*>(a.beta);
     ca.part = static_cast<Partial*>(part);
     ca.flags = flags;
-    if (hipError_t e = clear_publication_tags(a, flags, a.N * a.groups * plan.K, stream); e != hipSuccess)
-        return e;
+    if (plan.K > 1)
+        if (hipError_t e = clear_publication_tags(a, flags, a.N * a.groups * plan.K, stream); e != hipSuccess)
+            return e;
     ca.tag = a.tag;
     ca.timeout_ticks = a.exchange_timeout_ticks;
     ca.HW = a.H * a.W;

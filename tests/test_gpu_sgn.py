@@ -198,11 +198,13 @@ def test_broadcast_equals_expanded(cl):
     assert_bitwise(to_host(sp.Y), to_host(bc.Y), "(N,1,1,C) spelling")
 
 
+# Groups (NCHW) and channel blocks (NHWC) larger than one workgroup holds at
+# six accesses per thread, so that every case exchanges moments.
 FALLBACK_CASES = [
-    (2, 64, 16, 16, F32, F16, 0, True, False, 8, 0),
-    (1, 32, 24, 24, F16, F32, 0, False, True, 4, 1),
-    (2, 12, 7, 7, F32, F32, 0, True, True, 3, 1),   # scalar accesses
-    (2, 320, 16, 16, F16, F32, 1, False, True, 32, 1),  # NHWC, 5 slices of 51 pixel lanes
+    (2, 64, 32, 32, F32, F16, 0, True, False, 8, 0),
+    (1, 32, 48, 48, F16, F32, 0, False, True, 4, 1),
+    (2, 12, 23, 23, F32, F32, 0, True, True, 3, 1),   # scalar accesses
+    (2, 320, 24, 24, F16, F32, 1, False, True, 32, 1),  # NHWC, 11 slices of 51 pixel lanes
     (2, 72, 16, 16, F16, F16, 1, True, False, 8, 0),    # NHWC, 2 groups per wave, 9 slices
     (1, 48, 32, 31, F32, F32, 1, False, True, 4, 1),    # NHWC float32, 46 slices, ragged last
 ]
@@ -228,7 +230,7 @@ def test_cluster_recompute_path_matches(case):
 def test_cluster_tags_ignore_stale_workspace(cl):
     """A workspace left over from earlier calls (stale tags and moments from
     a different tensor) must not leak into the next call."""
-    N, C, H, W = 2, 64, 16, 16
+    N, C, H, W = 2, 64, 32, 32  # groups spread over several workgroups in both layouts
     w, x = make((N, C, H, W, F32, F32, cl, False, True, 8, 1), seed=7)
     w2, x2 = make((N, C, H, W, F32, F32, cl, False, True, 8, 1), seed=8)
     ws = torch.empty(gn.skip_group_norm_workspace_size(to_dev(x["X"]), 8, cl), dtype=torch.uint8,
