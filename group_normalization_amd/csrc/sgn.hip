@@ -39,14 +39,17 @@
 //   3. normalize: re-reads S (or re-forms it from X, skip and bias, bit for
 //      bit the same) and writes Y.
 //   Tilings of passes 1 and 3:
-//   nhwc   (NHWC, C a whole number of 16-, 8- or 4-byte vectors, at most
-//          256 of them):
-//          a block covers a run of pixels of one image and all channels
-//          (at least two pixels per thread, more where the grid would
-//          exceed about 2048 blocks).  Thread t owns channel vector t % Cv
-//          at pixels t / Cv + k * P, P = 256 / Cv, so its channels (and
-//          their bias, gamma, beta and group) never change.  Per-channel moments are merged over the
-//          pixel lanes, then over each group's channels, through LDS.
+//   nhwc   (NHWC, C a whole number of 16-, 8- or 4-byte vectors that
+//          splits into equal channel blocks of whole groups, at most 256
+//          vectors each):
+//          a block covers a run of pixels of one image and one channel
+//          block (every thread the same number of pixels: at least two,
+//          more where the grid would exceed about 2048 blocks).  Thread t
+//          owns the block's channel vector t % CBv at pixels t / CBv + k * P,
+//          P = 256 / CBv, so its channels (and their bias, gamma, beta and
+//          group) never change.  Per-channel moments are merged over the
+//          pixel lanes, then over each group's channels, through LDS, by
+//          segments of lanes in a fixed order.
 //   group  (NCHW groups too large for one workgroup; the scalar route of
 //          both layouts): a block covers a slice of one (n, group)'s
 //          elements.
@@ -271,19 +274,53 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
 }
 
 // ------------------------------------------------------------------ split: nhwc
+// Block (n, b, cb) covers pixels [b*ppb, (b+1)*ppb) of image n and channel
+// block cb: vectors [cb*CBv, (cb+1)*CBv) of each pixel's Cv, a whole number
+// of groups.  Thread t owns vector cb*CBv + t % CBv at pixels t / CBv + k*P,
+// P = 256 / CBv.
+struct NhwcTile {
+    int n, b, cv0, cvl, p0;
+    bool active;
+};
+
+__device__ __forceinline__ NhwcTile nhwc_tile(int B, int NCB, int CBv, int P) {
+    NhwcTile tl;
+    const int cb = blockIdx.x % NCB, nb = blockIdx.x / NCB;
+    tl.n = nb / B;
+    tl.b = nb % B;
+    tl.cv0 = cb * CBv;
+    const int t = threadIdx.x;
+    tl.active = t < P * CBv;
+    tl.cvl = tl.active ? t % CBv : 0;
+    tl.p0 = tl.active ? t / CBv : 0;
+    return tl;
+}
+
+// Lanes (a power of two, at most 64) that combine each of `items` runs of
+// `len` moments in the block's reductions: as many as keep all items within
+// one pass of 256 threads, and no more than a run has values.  Each lane
+// merges every w-th value of its run, then the w lanes combine in order
+// (segment_merge), a fixed order for a given shape.
+__device__ __forceinline__ int merge_lanes(int items, int len) {
+    int w = 1;
+    while (w < 64 && 2 * w * items <= 256 && w < len) w <<= 1;
+    return w;
+}
+
 template <typename T, int E>
 __global__ void __launch_bounds__(256)
 sgn_stats_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
                       const T* __restrict__ bias, T* __restrict__ S, Partial* __restrict__ part,
-                      int64_t HW, int C, int Cv, int P, int cpg, int groups, int B, int64_t ppb,
-                      bool skip_bcast) {
+                      int64_t HW, int Cv, int CBv, int NCB, int P, int cpg, int groups, int B,
+                      int64_t ppb, bool skip_bcast) {
     using V = Vec<T, E>;
     __shared__ float sh_n[256 * E], sh_mean[256 * E], sh_m2[256 * E];
-    const int n = blockIdx.x / B, b = blockIdx.x % B;
+    const NhwcTile tl = nhwc_tile(B, NCB, CBv, P);
+    const int n = tl.n, b = tl.b, p0 = tl.p0;
+    const int cv = tl.cv0 + tl.cvl;
+    const int Cw = CBv * E;  // channels of the block
     const int t = threadIdx.x;
-    const bool active = t < P * Cv;
-    const int cv = active ? t % Cv : 0;
-    const int p0 = active ? t / Cv : 0;
+    const bool active = tl.active;
     const int64_t pb = int64_t(b) * ppb;
     const int64_t pe = pb + ppb < HW ? pb + ppb : HW;
     const int64_t img = int64_t(n) * HW * Cv;
@@ -327,31 +364,50 @@ sgn_stats_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const Moments m = acc[e].moments(cnt);
-            const int slot = p0 * C + cv * E + e;
+            const int slot = p0 * Cw + tl.cvl * E + e;
             sh_n[slot] = m.n;
             sh_mean[slot] = m.mean;
             sh_m2[slot] = m.m2;
         }
     }
     __syncthreads();
-    // Per channel over the P pixel lanes; the totals go to row 0.
-    for (int c = t; c < C; c += 256) {
-        Moments m{sh_n[c], sh_mean[c], sh_m2[c]};
-        for (int q = 1; q < P; ++q) {
-            const int slot = q * C + c;
-            m = merge(m, Moments{sh_n[slot], sh_mean[slot], sh_m2[slot]});
+    // Per channel over the P pixel lanes (slots c, Cw + c, ...); the totals
+    // go to row 0.
+    {
+        const int w = merge_lanes(Cw, P);
+        const int lane = t & (w - 1);
+        for (int c0 = 0; c0 < Cw; c0 += 256 / w) {
+            const int c = c0 + t / w;
+            Moments m{0.0f, 0.0f, 0.0f};
+            if (c < Cw)
+                for (int q = lane; q < P; q += w) {
+                    const int slot = q * Cw + c;
+                    m = merge(m, Moments{sh_n[slot], sh_mean[slot], sh_m2[slot]});
+                }
+            m = segment_merge(m, w);
+            if (c < Cw && lane == 0) {
+                sh_n[c] = m.n;
+                sh_mean[c] = m.mean;
+                sh_m2[c] = m.m2;
+            }
         }
-        sh_n[c] = m.n;
-        sh_mean[c] = m.mean;
-        sh_m2[c] = m.m2;
     }
     __syncthreads();
-    // Per group over its channels.
-    for (int g = t; g < groups; g += 256) {
-        const int c0 = g * cpg;
-        Moments m{sh_n[c0], sh_mean[c0], sh_m2[c0]};
-        for (int c = c0 + 1; c < c0 + cpg; ++c) m = merge(m, Moments{sh_n[c], sh_mean[c], sh_m2[c]});
-        part[(int64_t(n) * groups + g) * B + b] = Partial{m.n, m.mean, m.m2, 0.0f};
+    // Per group of the block over its channels.
+    {
+        const int g0 = tl.cv0 * E / cpg, gpb = Cw / cpg;
+        const int w = merge_lanes(gpb, cpg);
+        const int lane = t & (w - 1);
+        for (int gl0 = 0; gl0 < gpb; gl0 += 256 / w) {
+            const int gl = gl0 + t / w;
+            Moments m{0.0f, 0.0f, 0.0f};
+            if (gl < gpb)
+                for (int c = gl * cpg + lane; c < (gl + 1) * cpg; c += w)
+                    m = merge(m, Moments{sh_n[c], sh_mean[c], sh_m2[c]});
+            m = segment_merge(m, w);
+            if (gl < gpb && lane == 0)
+                part[(int64_t(n) * groups + g0 + gl) * B + b] = Partial{m.n, m.mean, m.m2, 0.0f};
+        }
     }
 }
 
@@ -360,14 +416,14 @@ __global__ void __launch_bounds__(256)
 sgn_norm_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
                      const T* __restrict__ bias, const T* __restrict__ S_in,
                      const M* __restrict__ gamma, const M* __restrict__ beta,
-                     const float2* __restrict__ stat, T* __restrict__ Y, int64_t HW, int Cv, int P,
-                     int cpg, int groups, int B, int64_t ppb, bool skip_bcast, bool silu) {
+                     const float2* __restrict__ stat, T* __restrict__ Y, int64_t HW, int Cv,
+                     int CBv, int NCB, int P, int cpg, int groups, int B, int64_t ppb,
+                     bool skip_bcast, bool silu) {
     using V = Vec<T, E>;
-    const int n = blockIdx.x / B, b = blockIdx.x % B;
-    const int t = threadIdx.x;
-    if (t >= P * Cv) return;  // no barrier below
-    const int cv = t % Cv;
-    const int p0 = t / Cv;
+    const NhwcTile tl = nhwc_tile(B, NCB, CBv, P);
+    if (!tl.active) return;  // no barrier below
+    const int n = tl.n, b = tl.b, p0 = tl.p0;
+    const int cv = tl.cv0 + tl.cvl;
     const int64_t pb = int64_t(b) * ppb;
     const int64_t pe = pb + ppb < HW ? pb + ppb : HW;
     const int64_t img = int64_t(n) * HW * Cv;
@@ -616,25 +672,84 @@ sgn_finalize_kernel(const Partial* __restrict__ part, float2* __restrict__ stat,
 // ------------------------------------------------------------------ host side
 constexpr int64_t kVectorsPerBlock = 256 * kUnroll;  // one unrolled pass of a 256-thread block
 
+}  // namespace
+
+// Channel blocks of the nhwc tiling for pixels of C channels read as vectors
+// of E: NCB equal blocks of at most 256 vectors, each a whole number of
+// groups and of vectors (so a multiple of lcm(cpg, E) channels).  The fewest
+// blocks that keep at least 90 % of a block's threads busy (one block of
+// 160 vectors would leave 96 of 256 idle; two of 80 leave 16), else the
+// busiest.  False when no such block exists (a group wider than 256 vectors
+// that is not a whole number of them, or C not a whole number of vectors).
+bool nhwc_split_channel_blocks(int64_t C, int64_t cpg, int E, int* ncb_out) {
+    if (E < 1 || C % E != 0 || cpg < 1 || C % cpg != 0) return false;
+    int64_t x = cpg, y = E;
+    while (y) {
+        const int64_t r = x % y;
+        x = y;
+        y = r;
+    }
+    const int64_t unit = cpg / x * E;  // lcm(cpg, E) channels
+    const int64_t nb0 = C / unit;
+    int64_t best = 0, best_busy = -1;
+    for (int64_t ncb = 1; ncb <= nb0; ++ncb) {
+        if (nb0 % ncb) continue;
+        const int64_t cbv = C / E / ncb;
+        if (cbv > 256) continue;
+        const int64_t busy = 256 / cbv * cbv;
+        if (busy > best_busy) {
+            best_busy = busy;
+            best = ncb;
+        }
+        if (busy * 10 >= 256 * 9) break;  // always reached once cbv <= 25
+    }
+    if (best == 0) return false;
+    *ncb_out = int(best);
+    return true;
+}
+
+namespace {
+
 constexpr int kNhwcRowsPerThread = 2;                // least pixel rows per thread in the nhwc tiling
 constexpr int64_t kSplitTargetBlocks = 2048;         // nhwc tiling: about 8 workgroups per CU in all
 
-// Blocks per image (nhwc) or per (n, group) (group tiling) of the split
-// route.  The nhwc tiling gives each thread at least kNhwcRowsPerThread
-// pixels, so a small image still spreads over many CUs, and large images
-// more, so that the N images together take about kSplitTargetBlocks blocks
-// (thousands of blocks of two pixels per thread spent their time in each
-// block's reduction: 2.4 TB/s on a 256x256x512 float16 image); the group
-// tiling gives each block one unrolled pass of vectors.
+// The nhwc tiling for vectors of E channels: ncb channel blocks of CBv
+// vectors, P = 256 / CBv pixel lanes, and runs of ppb = P * R pixels, so
+// that every thread of a full run holds R pixels: at least
+// kNhwcRowsPerThread, so that a small image still spreads over many CUs;
+// more where the N images would take more than about kSplitTargetBlocks
+// blocks (thousands of blocks of two pixels per thread spent their time in
+// each block's reduction: 2.4 TB/s on a 256x256x512 float16 image); and,
+// beyond one unrolled step, a whole number of them (a ragged last step
+// issues loads whose values are discarded).
+struct NhwcSplit {
+    int ncb, P;
+    int64_t ppb, B;
+};
+
+bool nhwc_split_plan(int64_t N, int64_t C, int64_t HW, int64_t groups, int E, NhwcSplit* sp) {
+    int ncb = 0;
+    if (N < 1 || HW < 1 || !nhwc_split_channel_blocks(C, C / groups, E, &ncb)) return false;
+    const int64_t P = 256 / (C / E / ncb);
+    int64_t R = (N * ncb * HW + P * kSplitTargetBlocks - 1) / (P * kSplitTargetBlocks);
+    if (R < kNhwcRowsPerThread) R = kNhwcRowsPerThread;
+    if (R > kUnroll) R = (R + kUnroll - 1) / kUnroll * kUnroll;
+    sp->ncb = ncb;
+    sp->P = int(P);
+    sp->ppb = P * R;
+    sp->B = (HW + sp->ppb - 1) / sp->ppb;
+    return true;
+}
+
+// Blocks per image (nhwc: pixel runs) or per (n, group) (group tiling: one
+// unrolled pass of vectors each) of the split route, planned for 16-byte
+// vectors; the partials per (n, group) the workspace holds.
 int64_t split_blocks(int dtype, int64_t N, int64_t C, int64_t HW, int64_t groups, bool channels_last) {
     const int64_t ev = dtype == 0 ? 4 : 8;
     int64_t B;
-    if (channels_last && C % ev == 0 && C / ev <= 256) {
-        const int64_t P = 256 / (C / ev);
-        const int64_t ppb = P * kNhwcRowsPerThread;
-        B = (HW + ppb - 1) / ppb;
-        const int64_t target = (kSplitTargetBlocks + N - 1) / (N > 0 ? N : 1);
-        if (B > target) B = target;
+    NhwcSplit sp;
+    if (channels_last && nhwc_split_plan(N, C, HW, groups, int(ev), &sp)) {
+        B = sp.B;
     } else {
         const int64_t per_unit = channels_last ? HW * C : (C / groups) * HW;  // image / group
         B = (per_unit + ev * kVectorsPerBlock - 1) / (ev * kVectorsPerBlock);
@@ -717,12 +832,13 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
     const bool data_ok = aligned16(a.X) && aligned16(a.Y) && (!a.S || aligned16(a.S)) &&
                          (a.skip_broadcast || aligned16(a.skip));
     const bool vec_allowed = want != Route::Scalar && want != Route::Block;
-    // NHWC: the widest access that divides a pixel's channels and every base,
-    // with at most 256 vectors per pixel (one per thread).
+    // NHWC: the widest access that divides a pixel's channels and every base
+    // and splits the pixel into channel blocks of whole groups and vectors.
     int nhwc_e = 1;
     if (vec_allowed && a.channels_last) {
         nhwc_e = widest_vector<T>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
-        if (a.C / nhwc_e > 256) nhwc_e = 1;
+        int ncb = 0;
+        if (nhwc_e > 1 && !nhwc_split_channel_blocks(a.C, cpg, nhwc_e, &ncb)) nhwc_e = 1;
     }
     const bool nchw_vec = vec_allowed && !a.channels_last && HW % EV == 0 && data_ok;
 
@@ -781,20 +897,29 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
     const dim3 fin_grid = dim3(unsigned(NG));
 
     if (nhwc_e > 1) {
-        // Blocks cover ppb pixels of one image whatever the access width.
-        const int64_t ppb = (HW + B - 1) / B;
-        const dim3 grid(unsigned(a.N * B));
+        // The plan for this access width; its pixel runs must fit the B
+        // partials per (n, group) the workspace holds (planned for 16-byte
+        // vectors), else the runs are stretched to B.
+        NhwcSplit sp;
+        nhwc_split_plan(a.N, a.C, HW, a.groups, nhwc_e, &sp);  // nhwc_e was checked above
+        if (sp.B > B) {
+            sp.ppb = ((HW + B - 1) / B + sp.P - 1) / sp.P * sp.P;
+            sp.B = (HW + sp.ppb - 1) / sp.ppb;
+        }
+        const int Bn = int(sp.B), ncb = sp.ncb, P = sp.P;
+        const int64_t ppb = sp.ppb;
+        const dim3 grid(unsigned(a.N * Bn * ncb));
         auto launch = [&](auto tag, const char* name) {
             constexpr int E = decltype(tag)::value;
-            const int Cv = C / E, P = 256 / Cv;
+            const int Cv = C / E, CBv = Cv / ncb;
             *route = name;
             hipLaunchKernelGGL((sgn_stats_nhwc_kernel<T, E>), grid, dim3(256), 0, stream, X, skip, bias,
-                               S, part, HW, C, Cv, P, cpg, groups, B, ppb, a.skip_broadcast);
-            hipLaunchKernelGGL(sgn_finalize_kernel, fin_grid, dim3(256), 0, stream, part, stat, B,
+                               S, part, HW, Cv, CBv, ncb, P, cpg, groups, Bn, ppb, a.skip_broadcast);
+            hipLaunchKernelGGL(sgn_finalize_kernel, fin_grid, dim3(256), 0, stream, part, stat, Bn,
                                a.epsilon);
             hipLaunchKernelGGL((sgn_norm_nhwc_kernel<T, M, E>), grid, dim3(256), 0, stream, X, skip,
-                               bias, static_cast<const T*>(S), gamma, beta, stat, Y, HW, Cv, P, cpg,
-                               groups, B, ppb, a.skip_broadcast, silu);
+                               bias, static_cast<const T*>(S), gamma, beta, stat, Y, HW, Cv, CBv, ncb,
+                               P, cpg, groups, Bn, ppb, a.skip_broadcast, silu);
             return hipGetLastError();
         };
         if (nhwc_e == EV) return launch(std::integral_constant<int, EV>(), "sgn.split.nhwc.vec16");

@@ -21,6 +21,11 @@ constexpr int kSingleSliceMaxR = 6;
 bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, uint64_t* flags,
                              hipStream_t stream, const char** route, hipError_t* err);
 
+// Channel blocks (*ncb equal blocks of whole groups, at most 256 vectors of E
+// channels each) of the split route's NHWC tiling for pixels of C channels in
+// groups of cpg; false when no such blocking exists.
+bool nhwc_split_channel_blocks(int64_t C, int64_t cpg, int E, int* ncb);
+
 // Zeroes the cluster routes' n publication tags on `stream` when a.clear_tags
 // is set (a kernel of plain stores, not a memset, so that graph replays
 // rerun it faithfully); nothing otherwise.

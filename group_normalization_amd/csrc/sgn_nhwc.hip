@@ -593,14 +593,14 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, uint64_t*
     const int64_t resident = resident_workgroups(kernel);
     if (!kernel || nhwc_cluster_span(a.N, plan) > resident) return false;
     // Beyond two rounds of resident workgroups the split route measured
-    // faster (10-30 %, e.g. 8 x 128 x 128 x 320 float16: 86 against 112 us),
-    // unless it would fall to scalar accesses (more than 256 vectors per
-    // pixel), which costs more than the extra rounds.
+    // faster (10-30 %, e.g. 8 x 128 x 128 x 320 float16: 86 against 112 us)
+    // where its blocks hold whole pixels; wider pixels stay here (8 x 64 x 64
+    // x 1280 float32: 148 us, against 162 us split over channel blocks).
     const int split_e = a.dtype == 0 ? widest_vector<float>(a.C, {a.X, a.Y, a.S, a.skip, a.bias})
                                      : widest_vector<half_t>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
-    const bool split_vectorized = split_e > 1 && a.C / split_e <= 256;
+    const bool split_whole_pixels = split_e > 1 && a.C / split_e <= 256;
     const int64_t grid = (a.N * plan.K + 7) / 8 * 8 * plan.NCB;
-    if (split_vectorized && grid > 2 * resident) return false;
+    if (split_whole_pixels && grid > 2 * resident) return false;
     static const char* const kNames[] = {"sgn.cluster.nhwc.vec4", "sgn.cluster.nhwc.vec8",
                                          "sgn.cluster.nhwc.vec16"};
     *route = kNames[E * size == 16 ? 2 : E * size == 8 ? 1 : 0];

@@ -1,4 +1,6 @@
 """SkipGroupNorm: HIP path (through the C ABI) against the oracle."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -46,10 +48,34 @@ CASES = [
     (2, 12, 6, 6, F16, F16, 1, False, True, 3, 0),        # C not a whole vector: scalar NHWC
     (2, 16, 4, 4, F32, F32, 0, True, True, 16, 1),        # groups == C (instance norm)
     (2, 24, 3, 5, F16, F32, 0, False, False, 1, 0),       # one group (layer norm)
-    (1, 4096, 2, 2, F16, F16, 1, False, True, 32, 0),     # 512 vectors per pixel: scalar NHWC
+    (1, 4096, 2, 2, F16, F16, 1, False, True, 32, 0),     # 512 vectors per pixel: 2 channel blocks
     (3, 8, 1, 1, F32, F16, 1, True, False, 2, 1),         # H = W = 1
-    (2, 2560, 8, 8, F32, F32, 1, False, True, 32, 1),     # 640 vectors per pixel: scalar NHWC
+    (2, 2560, 8, 8, F32, F32, 1, False, True, 32, 1),     # 640 vectors per pixel: 8 channel blocks
 ]
+
+
+def split_channel_blocks(C, cpg, e):
+    """Channel blocks of the split route's NHWC tiling for vectors of e
+    channels: the fewest equal blocks of whole groups and vectors, at most
+    256 vectors each, that keep 90 % of a block's 256 threads busy, else the
+    busiest; 0 when there is none (the library's rule, restated)."""
+    if C % e or C % cpg:
+        return 0
+    unit = cpg // math.gcd(cpg, e) * e
+    nb0 = C // unit
+    best, best_busy = 0, -1
+    for ncb in range(1, nb0 + 1):
+        if nb0 % ncb:
+            continue
+        cbv = C // e // ncb
+        if cbv > 256:
+            continue
+        busy = 256 // cbv * cbv
+        if busy > best_busy:
+            best, best_busy = ncb, busy
+        if busy * 10 >= 256 * 9:
+            break
+    return best
 
 
 def nhwc_route(C, groups, T):
@@ -65,7 +91,7 @@ def nhwc_route(C, groups, T):
         w //= 2
     if w > size:
         return f"sgn.cluster.nhwc.{names[w]}"
-    if width > size and C // (width // size) <= 256:
+    if width > size and split_channel_blocks(C, C // groups, width // size):
         return f"sgn.split.nhwc.{names[width]}"
     return "sgn.split.nhwc.scalar"
 
@@ -97,6 +123,39 @@ def test_matches_oracle(case, route):
         assert used.startswith("sgn.cluster")  # every NCHW case here fits the cluster route
     if route == "auto" and cl:
         assert used == nhwc_route(C, groups, T)
+
+
+# The split route's NHWC tiling over channel blocks: pixels wider than 256
+# vectors, or whose 256-thread blocks would leave over a tenth of the
+# threads idle, are cut into equal blocks of whole groups and vectors.
+SPLIT_BLOCK_CASES = [
+    # (case, channel blocks, route)
+    ((2, 1280, 9, 7, F16, F32, 1, False, True, 32, 1), 2, "sgn.split.nhwc.vec16"),   # 160 vectors: 2 x 80
+    ((2, 1280, 40, 40, F16, F32, 1, True, True, 32, 1), 2, "sgn.split.nhwc.vec16"),  # 267 pixel runs
+    ((1, 2560, 5, 6, F32, F16, 1, True, False, 32, 0), 8, "sgn.split.nhwc.vec16"),   # 640 vectors: 8 x 80
+    ((2, 4096, 3, 3, F16, F16, 1, False, True, 32, 1), 2, "sgn.split.nhwc.vec16"),   # 512 vectors: 2 x 256
+    ((1, 1200, 4, 5, F16, F32, 1, False, True, 30, 1), 3, "sgn.split.nhwc.vec16"),   # 150 vectors: 3 x 50
+    # 10-channel groups straddle 16-byte vectors: blocks of 5 vectors (4 groups) each.
+    ((2, 1040, 4, 4, F16, F32, 1, True, True, 104, 1), 13, "sgn.split.nhwc.vec16"),
+    ((2, 40, 8, 8, F32, F32, 1, False, True, 4, 0), 1, "sgn.split.nhwc.vec16"),      # one block
+    # One group of 257 sixteen-byte vectors: no channel blocks, scalar accesses.
+    ((1, 2056, 3, 3, F16, F32, 1, False, True, 1, 1), 0, "sgn.split.nhwc.scalar"),
+]
+
+
+@pytest.mark.parametrize("case,ncb,want_route", SPLIT_BLOCK_CASES,
+                         ids=[f"N{c[0][0]}C{c[0][1]}H{c[0][2]}W{c[0][3]}-{np.dtype(c[0][4]).name}-g{c[0][9]}"
+                              for c in SPLIT_BLOCK_CASES])
+def test_split_channel_blocks(case, ncb, want_route):
+    N, C, H, W, T, M, cl, bc, bias, groups, act = case
+    size = np.dtype(T).itemsize
+    assert split_channel_blocks(C, C // groups, 16 // size) == ncb
+    w, x = make(case, seed=9)
+    ref, out, used = run(x, w, "split")
+    assert used == want_route
+    check(ref, out)
+    _, no_s, _ = run(x, w, "split", want_sum=False)  # pass 3 re-forms S from X and skip
+    assert_bitwise(to_host(no_s.Y), to_host(out.Y), "Y without S")
 
 
 # NCHW groups around the cluster route's limits (per (n, group), at most 8
