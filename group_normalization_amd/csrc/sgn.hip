@@ -84,9 +84,8 @@ struct ClusterArgs {
     const T *X, *skip, *bias;
     T *S, *Y;
     const M *gamma, *beta;
-    Partial* part;     // N*groups*K slice moments
-    uint64_t* flags;   // N*groups*K publication tags
-    uint64_t tag;      // unique per call
+    Partial* part;     // N*groups*K publication slots
+    PubTags tags;      // this call's publication tags
     long long timeout_ticks;  // wall-clock ticks a workgroup waits for a slice
     int64_t HW;
     int C, cpg, groups, K;
@@ -174,22 +173,11 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
     // ---- exchange with the other K-1 slices of the group
     Moments tot = mine;
     if (a.K > 1) {
-        uint64_t* flags = a.flags + int64_t(ng) * a.K;
-        uint64_t* part = reinterpret_cast<uint64_t*>(a.part) + int64_t(ng) * a.K;
-        // Publication: (mean, M2) as one 64-bit agent-scope store, which is
-        // coherent across the XCDs' separate L2 caches (the count is implied
-        // by the slice's size); the memory-counter wait completes it before
-        // the tag is stored, and a reader that sees the tag (agent-scope
-        // load) therefore reads this call's moments.  Nothing written with
-        // plain stores is exchanged, so no cache-wide fence is needed.
-        if (t == 0) {
-            const uint64_t bits = uint64_t(__float_as_uint(mine.mean)) |
-                                  (uint64_t(__float_as_uint(mine.m2)) << 32);
-            __hip_atomic_store(&part[k], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_s_waitcnt(0);
-            __hip_atomic_store(&flags[k], a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // S goes out after the publication's wait, which then waits for nothing else.
+        // Publication: this slice's (mean, M2) in its self-tagged slot;
+        // nothing written with plain stores is exchanged, so no cache-wide
+        // fence is needed.
+        uint64_t* slots = reinterpret_cast<uint64_t*>(a.part) + 2 * (int64_t(ng) * a.K);
+        if (t == 0) publish_moments(&slots[2 * k], mine, a.tags);
         if (a.S) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -200,8 +188,9 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
         if (t < a.K && t != k) {
             const long long t0 = wall_clock64();
             bool ok = false;
+            float mean = 0.0f, m2 = 0.0f;
             for (;;) {
-                if (__hip_atomic_load(&flags[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.tag) {
+                if (read_moments(&slots[2 * t], a.tags, &mean, &m2)) {
                     ok = true;
                     break;
                 }
@@ -209,11 +198,7 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
                 __builtin_amdgcn_s_sleep(2);
             }
             late[t] = ok ? 0 : 1;
-            if (ok) {
-                const uint64_t bits = __hip_atomic_load(&part[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                slice_m[t] = Moments{float((end_of(t) - uint32_t(t) * a.vps) * E),
-                                     __uint_as_float(uint32_t(bits)), __uint_as_float(uint32_t(bits >> 32))};
-            }
+            if (ok) slice_m[t] = Moments{float((end_of(t) - uint32_t(t) * a.vps) * E), mean, m2};
         }
         __syncthreads();
         tot = Moments{0.0f, 0.0f, 0.0f};
@@ -692,7 +677,7 @@ bool nhwc_split_channel_blocks(int64_t C, int64_t cpg, int E, int* ncb_out) {
     const int64_t unit = cpg / x * E;  // lcm(cpg, E) channels
     const int64_t nb0 = C / unit;
     int64_t best = 0, best_busy = -1;
-    for (int64_t ncb = 1; ncb <= nb0; ++ncb) {
+    for (int64_t ncb = (C / E + 255) / 256; ncb <= nb0; ++ncb) {  // from the fewest of <= 256 vectors
         if (nb0 % ncb) continue;
         const int64_t cbv = C / E / ncb;
         if (cbv > 256) continue;
@@ -861,11 +846,10 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
             ca.gamma = gamma;
             ca.beta = beta;
             ca.part = part;
-            ca.flags = reinterpret_cast<uint64_t*>(stat + NG);
             if (Kc > 1)
-                if (hipError_t e = clear_publication_tags(a, ca.flags, NG * Kc, stream); e != hipSuccess)
+                if (hipError_t e = clear_publication_tags(a, part, NG * Kc, stream); e != hipSuccess)
                     return e;
-            ca.tag = a.tag;
+            ca.tags = publication_tags(a.tag);
             ca.timeout_ticks = a.exchange_timeout_ticks;
             ca.HW = HW;
             ca.C = C;
@@ -889,7 +873,7 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
 
     // ---- channel-block cluster route (NHWC)
     hipError_t err = hipSuccess;
-    if (launch_sgn_nhwc_cluster(a, want, part, reinterpret_cast<uint64_t*>(stat + NG), stream, route, &err))
+    if (launch_sgn_nhwc_cluster(a, want, part, stream, route, &err))
         return err;
 
     // ---- split route
@@ -983,29 +967,29 @@ int64_t sgn_partials_per_group(int dtype, int64_t N, int64_t C, int64_t H, int64
     return b >= k ? b : k;
 }
 
-// Workspace: N*groups*B partials of 16 bytes, N*groups (mean, rstd) pairs,
-// then the cluster routes' publication tags: N*groups*8 (NCHW) or
-// N*groups*64 (NHWC: one per (image, slice, group), at most 64 slices).
+// Workspace: N*groups*B partials of 16 bytes (the split route's partials, or
+// the cluster routes' publication slots: at most 8 (NCHW) or 64 (NHWC) per
+// (n, group)), then N*groups (mean, rstd) pairs.
 size_t sgn_workspace_bytes(int dtype, int64_t N, int64_t C, int64_t H, int64_t W, int64_t groups,
                            bool channels_last) {
     const int64_t B = sgn_partials_per_group(dtype, N, C, H, W, groups, channels_last);
     const int64_t NG = N * groups;
-    size_t bytes = size_t(NG * B) * sizeof(Partial) + size_t(NG) * sizeof(float2);
-    bytes += size_t(NG) * (channels_last ? kNhwcMaxK : kClusterMaxK) * sizeof(uint64_t);
-    return bytes;
+    return size_t(NG * B) * sizeof(Partial) + size_t(NG) * sizeof(float2);
 }
 
 namespace {
-__global__ void __launch_bounds__(256) sgn_clear_tags_kernel(uint64_t* __restrict__ flags, int64_t n) {
+__global__ void __launch_bounds__(256) sgn_clear_tags_kernel(uint64_t* __restrict__ words, int64_t n) {
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
-        flags[i] = 0;
+        words[i] = 0;
 }
 }  // namespace
 
-hipError_t clear_publication_tags(const SgnArgs& a, uint64_t* flags, int64_t n, hipStream_t stream) {
+hipError_t clear_publication_tags(const SgnArgs& a, void* slots, int64_t n, hipStream_t stream) {
     if (!a.clear_tags || n <= 0) return hipSuccess;
-    const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
-    hipLaunchKernelGGL(sgn_clear_tags_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, flags, n);
+    const int64_t words = 2 * n;
+    const int64_t blocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
+    hipLaunchKernelGGL(sgn_clear_tags_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<uint64_t*>(slots), words);
     return hipGetLastError();
 }
 

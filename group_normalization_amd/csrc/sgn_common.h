@@ -17,19 +17,42 @@ constexpr int kSingleSliceMaxR = 6;
 
 // Launches the NHWC channel-block cluster route when the shapes, alignments
 // and `want` allow it (returns false, having launched nothing, otherwise).
-// `part` and `flags` are the workspace's partial and tag areas.
-bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, uint64_t* flags,
-                             hipStream_t stream, const char** route, hipError_t* err);
+// `part` is the workspace's partial area (the publication slots).
+bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream_t stream,
+                             const char** route, hipError_t* err);
 
 // Channel blocks (*ncb equal blocks of whole groups, at most 256 vectors of E
 // channels each) of the split route's NHWC tiling for pixels of C channels in
 // groups of cpg; false when no such blocking exists.
 bool nhwc_split_channel_blocks(int64_t C, int64_t cpg, int E, int* ncb);
 
-// Zeroes the cluster routes' n publication tags on `stream` when a.clear_tags
-// is set (a kernel of plain stores, not a memset, so that graph replays
-// rerun it faithfully); nothing otherwise.
-hipError_t clear_publication_tags(const SgnArgs& a, uint64_t* flags, int64_t n, hipStream_t stream);
+// Zeroes n publication slots of the cluster routes on `stream` when
+// a.clear_tags is set (a kernel of plain stores, not a memset, so that graph
+// replays rerun it faithfully); nothing otherwise.
+hipError_t clear_publication_tags(const SgnArgs& a, void* slots, int64_t n, hipStream_t stream);
+
+// Publication of one slice's moments in the cluster routes: a 16-byte slot
+// of two 64-bit words holding the mean and M2 in their low halves and, in
+// their high halves, two 32-bit tags taken from a 64-bit mix of the call's
+// tag.  Each word is one 64-bit agent-scope store (single-copy atomic, and
+// coherent across the XCDs' separate L2 caches), so a reader that finds
+// both words carrying this call's tags has this call's values: no fence,
+// no separate flag, and no second round trip to fetch the data after the
+// flag.  The count is implied by the slice's size.  A stale slot would have
+// to match the tags in 62 bits; zeroed slots (tags are odd) never match.
+struct PubTags {
+    uint32_t lo, hi;
+};
+
+inline PubTags publication_tags(uint64_t tag) {
+    uint64_t z = tag;  // MurmurHash3's 64-bit finalizer
+    z ^= z >> 33;
+    z *= 0xff51afd7ed558ccdULL;
+    z ^= z >> 33;
+    z *= 0xc4ceb9fe1a85ec53ULL;
+    z ^= z >> 33;
+    return PubTags{uint32_t(z) | 1u, uint32_t(z >> 32) | 1u};
+}
 
 namespace {
 
@@ -40,6 +63,24 @@ struct alignas(16) Partial {
 };
 
 __device__ __forceinline__ Moments as_moments(const Partial& p) { return Moments{p.n, p.mean, p.m2}; }
+
+// The two words of a publication slot (see publication_tags).
+__device__ __forceinline__ void publish_moments(uint64_t* slot, const Moments& m, PubTags tg) {
+    __hip_atomic_store(&slot[0], uint64_t(__float_as_uint(m.mean)) | (uint64_t(tg.lo) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&slot[1], uint64_t(__float_as_uint(m.m2)) | (uint64_t(tg.hi) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Reads a publication slot: true when both words carry this call's tags,
+// and then *mean and *m2 are the published values.
+__device__ __forceinline__ bool read_moments(uint64_t* slot, PubTags tg, float* mean, float* m2) {
+    const uint64_t w0 = __hip_atomic_load(&slot[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t w1 = __hip_atomic_load(&slot[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *mean = __uint_as_float(uint32_t(w0));
+    *m2 = __uint_as_float(uint32_t(w1));
+    return uint32_t(w0 >> 32) == tg.lo && uint32_t(w1 >> 32) == tg.hi;
+}
 
 // Combines the moments of the 64 lanes of a wave.  Partners always combine
 // as merge(lower lane, upper lane), so both compute bitwise the same value

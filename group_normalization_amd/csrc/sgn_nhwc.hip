@@ -42,9 +42,8 @@ struct NhwcClusterArgs {
     const T *X, *skip, *bias;
     T *S, *Y;
     const M *gamma, *beta;
-    Partial* part;     // N * NCB * K * CBg slice moments (mean, M2)
-    uint64_t* flags;   // N * NCB * K * CBg publication tags
-    uint64_t tag;
+    Partial* part;     // N * NCB * K * CBg publication slots
+    PubTags tags;      // this call's publication tags
     long long timeout_ticks;
     int64_t HW, pps;   // pixels per image and per slice
     int Cv, cpg;       // vectors per pixel, channels per group
@@ -218,20 +217,11 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
         reduce_slice(acc, nv_own, own_m);
     }
 
-    // ---- publication: per group, (mean, M2) as one 64-bit agent-scope store
-    // (coherent across the XCDs' L2 caches; the count is implied by the
-    // slice's size), completed before that group's tag goes out.
+    // ---- publication: per group, (mean, M2) in its self-tagged slot.
     const int64_t first = (int64_t(n) * a.NCB + cb) * a.K * a.CBg;  // slice 0 of this (image, block)
-    uint64_t* part = reinterpret_cast<uint64_t*>(a.part) + first;
-    uint64_t* flags = a.flags + first;
-    if (a.K > 1 && t < a.CBg) {
-        const Moments m = own_m[t];
-        const uint64_t bits = uint64_t(__float_as_uint(m.mean)) | (uint64_t(__float_as_uint(m.m2)) << 32);
-        __hip_atomic_store(&part[q * a.CBg + t], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        __hip_atomic_store(&flags[q * a.CBg + t], a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // S goes out after the publication's wait, which then waits for nothing else.
+    uint64_t* slots = reinterpret_cast<uint64_t*>(a.part) + 2 * first;  // two words per (slice, group)
+    auto slot = [&](int s, int g) { return &slots[2 * (s * a.CBg + g)]; };
+    if (a.K > 1 && t < a.CBg) publish_moments(slot(q, t), own_m[t], a.tags);
     if (a.S) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -244,10 +234,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
     // lanes; the lanes beyond K hold empty moments).
     int kw = 1;
     while (kw < a.K) kw <<= 1;
-    auto slice_moments = [&](int s, uint64_t bits) {
-        return Moments{float(slice_len(s) * a.cpg), __uint_as_float(uint32_t(bits)),
-                       __uint_as_float(uint32_t(bits >> 32))};
-    };
+    auto slice_count = [&](int s) { return float(slice_len(s) * a.cpg); };
     auto combine = [&](const Moments (&m)[kGroupsPerWave]) {
 #pragma unroll
         for (int i = 0; i < kGroupsPerWave; ++i) {
@@ -270,18 +257,15 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
             }
         } else if (lane < a.K) {
             const long long t0 = wall_clock64();
+            float mean[kGroupsPerWave], m2[kGroupsPerWave];
             for (;;) {
-                uint64_t seen[kGroupsPerWave];
+                bool ready = true;
 #pragma unroll
                 for (int i = 0; i < kGroupsPerWave; ++i) {
                     const int g = wave + i * kWaves;
-                    seen[i] = g < a.CBg ? __hip_atomic_load(&flags[lane * a.CBg + g], __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT)
-                                        : a.tag;
+                    mean[i] = m2[i] = 0.0f;
+                    if (g < a.CBg) ready &= read_moments(slot(lane, g), a.tags, &mean[i], &m2[i]);
                 }
-                bool ready = true;
-#pragma unroll
-                for (int i = 0; i < kGroupsPerWave; ++i) ready &= seen[i] == a.tag;
                 if (ready) break;
                 if (wall_clock64() - t0 > a.timeout_ticks) {
                     ok = false;
@@ -289,15 +273,9 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
                 }
                 __builtin_amdgcn_s_sleep(2);
             }
-            uint64_t bits[kGroupsPerWave] = {};
 #pragma unroll
-            for (int i = 0; i < kGroupsPerWave; ++i) {
-                const int g = wave + i * kWaves;
-                if (ok && g < a.CBg)
-                    bits[i] = __hip_atomic_load(&part[lane * a.CBg + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-#pragma unroll
-            for (int i = 0; i < kGroupsPerWave; ++i) m[i] = slice_moments(lane, bits[i]);
+            for (int i = 0; i < kGroupsPerWave; ++i)
+                m[i] = ok ? Moments{slice_count(lane), mean[i], m2[i]} : Moments{0.0f, 0.0f, 0.0f};
             if (!ok) late[lane] = 1;
         } else {
 #pragma unroll
@@ -337,9 +315,11 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
                 if (g < a.CBg) {
                     if (lane == q) m[i] = own_m[g];
                     else if (lane < a.K && late[lane]) m[i] = slice_m[lane][g];
-                    else if (lane < a.K)  // this wave saw its tag
-                        m[i] = slice_moments(lane, __hip_atomic_load(&part[lane * a.CBg + g], __ATOMIC_RELAXED,
-                                                                     __HIP_MEMORY_SCOPE_AGENT));
+                    else if (lane < a.K) {  // this wave saw its tags: the slot holds this call's values
+                        float mean = 0.0f, m2 = 0.0f;
+                        read_moments(slot(lane, g), a.tags, &mean, &m2);
+                        m[i] = Moments{slice_count(lane), mean, m2};
+                    }
                 }
             }
             combine(m);
@@ -383,6 +363,11 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
 // than leave each thread about one vector, and as many as the register
 // budget (kNhwcMaxR pixels per thread) needs.
 constexpr int64_t kNhwcTargetBlocks = 512;
+// Slices per cluster where the register budget allows: every slice's
+// moments are polled by every other slice's waves (two words per group),
+// and beyond 32 slices that traffic cost more than the added workgroups
+// bought (1 x 64 x 64 x 320 float16: 64 slices 13.3 us, 32 slices 10.9 us).
+constexpr int64_t kNhwcExchangeK = 32;
 
 struct NhwcPlan {
     int CBv, NCB, CBg, P, sw_log, K, R;
@@ -412,6 +397,7 @@ bool nhwc_cluster_plan(int E, int64_t N, int64_t C, int64_t HW, int64_t groups, 
             int64_t K = (kNhwcTargetBlocks + N * ncb - 1) / (N * ncb);
             const int64_t k_work = HW * cbv / kClusterThreads;  // at least one vector per thread
             if (K > k_work) K = k_work;
+            if (K > kNhwcExchangeK) K = kNhwcExchangeK;
             if (K < k_fit) K = k_fit;
             if (K > kNhwcMaxK) K = kNhwcMaxK;
             if (K > HW) K = HW;
@@ -529,7 +515,7 @@ hipError_t launch_nhwc_cluster(const NhwcClusterArgs<T, M>& ca, int r, int64_t b
 
 template <typename T, typename M>
 hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, int E, void* part,
-                             uint64_t* flags, hipStream_t stream) {
+                             hipStream_t stream) {
     NhwcClusterArgs<T, M> ca;
     ca.X = static_cast<const T*>(a.X);
     ca.skip = static_cast<const T*>(a.skip);
@@ -539,11 +525,10 @@ hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, int E, void
     ca.gamma = static_cast<const M*>(a.gamma);
     ca.beta = static_cast<const M*>(a.beta);
     ca.part = static_cast<Partial*>(part);
-    ca.flags = flags;
     if (plan.K > 1)
-        if (hipError_t e = clear_publication_tags(a, flags, a.N * a.groups * plan.K, stream); e != hipSuccess)
+        if (hipError_t e = clear_publication_tags(a, part, a.N * a.groups * plan.K, stream); e != hipSuccess)
             return e;
-    ca.tag = a.tag;
+    ca.tags = publication_tags(a.tag);
     ca.timeout_ticks = a.exchange_timeout_ticks;
     ca.HW = a.H * a.W;
     ca.pps = plan.pps;
@@ -570,8 +555,8 @@ hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, int E, void
 
 }  // namespace
 
-bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, uint64_t* flags,
-                             hipStream_t stream, const char** route, hipError_t* err) {
+bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream_t stream,
+                             const char** route, hipError_t* err) {
     if (!a.channels_last || want == Route::Scalar || want == Route::Block || want == Route::Split)
         return false;
     const int size = a.dtype == 0 ? 4 : 2;
@@ -605,11 +590,11 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, uint64_t*
                                          "sgn.cluster.nhwc.vec16"};
     *route = kNames[E * size == 16 ? 2 : E * size == 8 ? 1 : 0];
     if (a.dtype == 0) {
-        if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, E, part, flags, stream);
-        else *err = launch_nhwc_typed<float, half_t>(a, plan, E, part, flags, stream);
+        if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, E, part, stream);
+        else *err = launch_nhwc_typed<float, half_t>(a, plan, E, part, stream);
     } else {
-        if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, plan, E, part, flags, stream);
-        else *err = launch_nhwc_typed<half_t, half_t>(a, plan, E, part, flags, stream);
+        if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, plan, E, part, stream);
+        else *err = launch_nhwc_typed<half_t, half_t>(a, plan, E, part, stream);
     }
     return true;
 }
