@@ -25,9 +25,9 @@
 //   slice, channel block) tiles, hold S in VGPRs and exchange per-group
 //   moments the same way.  One launch, exactly the operator's traffic.
 //
-// Under HIP graph capture the cluster routes' tags are cleared by a store
-// kernel ahead of each launch and the tag is constant (a replay repeats the
-// arguments of the capture).
+// Under HIP graph capture the cluster routes' publication slots are cleared
+// by a store kernel ahead of each launch and the tag is constant (a replay
+// repeats the arguments of the capture).
 //
 // split (everything else), three launches on one stream: the
 //   pages' "partial group statistics / combine / normalize" structure,

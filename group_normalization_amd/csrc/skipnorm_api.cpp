@@ -303,9 +303,9 @@ sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t 
     // A captured graph replays its kernels with the arguments of the
     // capture, so a per-call tag would repeat on every replay and a
     // workgroup could take the moments a slice left in the previous replay.
-    // Under capture the cluster routes' tags are zeroed by a kernel ahead of
-    // each cluster launch instead, and the tag is a constant: only this
-    // launch's publications can carry it.
+    // Under capture the cluster routes' publication slots are zeroed by a
+    // kernel ahead of each cluster launch instead, and the tag is a
+    // constant: only this launch's publications can carry it.
     a.clear_tags = false;
     hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &capture) == hipSuccess && capture != hipStreamCaptureStatusNone) {

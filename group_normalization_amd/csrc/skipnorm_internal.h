@@ -49,7 +49,7 @@ struct SgnArgs {
     void* workspace;
     uint64_t tag;                     // unique per call (publication tags)
     long long exchange_timeout_ticks; // bounded wait of the cluster route
-    // Clear the publication tags before a cluster launch (the call is being
+    // Clear the publication slots before a cluster launch (the call is being
     // captured into a graph, whose replays repeat `tag`).
     bool clear_tags;
 };
