@@ -51,11 +51,12 @@ __device__ __forceinline__ Vec<T, E> mask_bits(const Vec<T, E>& v, uint32_t m) {
 }
 
 // WPR waves per row: 1, 2 or 4 (four, two or one rows per 256-thread
-// block).  Lane l of the row's 64*WPR lanes holds vectors l, l + 64*WPR, ...
+// block), or 8 and 16 (one row per block of WPB = WPR waves).  Lane l of the
+// row's 64*WPR lanes holds vectors l, l + 64*WPR, ...
 // CENTER: remove the row mean (skip layer normalization) instead of the
 // simplified root-mean-square form.
-template <typename T, int E, int NV, bool FULL, int WPR, bool CENTER>
-__global__ void __launch_bounds__(256)
+template <typename T, int E, int NV, bool FULL, int WPR, bool CENTER, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
 ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                  const T* __restrict__ gamma, const T* __restrict__ beta,
                  const T* __restrict__ bias, T* __restrict__ output, float* __restrict__ mean,
@@ -63,9 +64,10 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                  int64_t rows, int nvec, float hidden_f, float eps, uint32_t beta_mask) {
     using V = Vec<T, E>;
     constexpr int LANES = 64 * WPR;
-    __shared__ float wave_part[kWavesPerBlock];
+    static_assert(WPB % WPR == 0, "whole rows per block");
+    __shared__ float wave_part[WPB];
     const int lane = threadIdx.x % LANES;
-    const int64_t my_row = int64_t(blockIdx.x) * (kWavesPerBlock / WPR) + threadIdx.x / LANES;
+    const int64_t my_row = int64_t(blockIdx.x) * (WPB / WPR) + threadIdx.x / LANES;
     // A whole wave (WPR = 1) or block (WPR = 4) leaves; with two rows per
     // block the waves of a missing second row stay for the barrier and
     // store nothing.
@@ -429,13 +431,13 @@ hipError_t launch_segment_for(const SslnArgs& a, int nvec, hipStream_t stream) {
     return launch_segment<T, E, 64>(a, nvec, stream);
 }
 
-template <typename T, int E, int NV, int WPR>
+template <typename T, int E, int NV, int WPR, int WPB>
 hipError_t launch_wave_nv(const SslnArgs& a, int nvec, hipStream_t stream) {
-    constexpr int rows_per_block = kWavesPerBlock / WPR;
+    constexpr int rows_per_block = WPB / WPR;
     const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
     const float hidden_f = float(a.hidden);
     auto args = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), 0, stream,
+        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * WPB), 0, stream,
                            static_cast<const T*>(a.input), static_cast<const T*>(a.skip),
                            static_cast<const T*>(a.gamma),
                            static_cast<const T*>(a.beta ? a.beta : a.gamma),
@@ -445,53 +447,55 @@ hipError_t launch_wave_nv(const SslnArgs& a, int nvec, hipStream_t stream) {
     };
     const bool full = nvec == 64 * WPR * NV;
     if (a.center) {
-        if (full) args(ssln_wave_kernel<T, E, NV, true, WPR, true>);
-        else args(ssln_wave_kernel<T, E, NV, false, WPR, true>);
+        if (full) args(ssln_wave_kernel<T, E, NV, true, WPR, true, WPB>);
+        else args(ssln_wave_kernel<T, E, NV, false, WPR, true, WPB>);
     } else {
-        if (full) args(ssln_wave_kernel<T, E, NV, true, WPR, false>);
-        else args(ssln_wave_kernel<T, E, NV, false, WPR, false>);
+        if (full) args(ssln_wave_kernel<T, E, NV, true, WPR, false, WPB>);
+        else args(ssln_wave_kernel<T, E, NV, false, WPR, false, WPB>);
     }
     return hipGetLastError();
 }
 
-template <typename T, int E, int MAXNV, int WPR>
+template <typename T, int E, int MAXNV, int WPR, int WPB = kWavesPerBlock>
 hipError_t launch_wave(const SslnArgs& a, int nvec, hipStream_t stream) {
     const int need = (nvec + 64 * WPR - 1) / (64 * WPR);
-    if (need <= 1) return launch_wave_nv<T, E, 1, WPR>(a, nvec, stream);
-    if (need <= 2) return launch_wave_nv<T, E, 2, WPR>(a, nvec, stream);
-    if (need <= 3) return launch_wave_nv<T, E, 3, WPR>(a, nvec, stream);
-    if (need <= 4) return launch_wave_nv<T, E, 4, WPR>(a, nvec, stream);
+    if (need <= 1) return launch_wave_nv<T, E, 1, WPR, WPB>(a, nvec, stream);
+    if (need <= 2) return launch_wave_nv<T, E, 2, WPR, WPB>(a, nvec, stream);
+    if (need <= 3) return launch_wave_nv<T, E, 3, WPR, WPB>(a, nvec, stream);
+    if (need <= 4) return launch_wave_nv<T, E, 4, WPR, WPB>(a, nvec, stream);
     if constexpr (MAXNV >= 8) {
-        if (need <= 6) return launch_wave_nv<T, E, 6, WPR>(a, nvec, stream);
-        if (need <= 8) return launch_wave_nv<T, E, 8, WPR>(a, nvec, stream);
+        if (need <= 6) return launch_wave_nv<T, E, 6, WPR, WPB>(a, nvec, stream);
+        if (need <= 8) return launch_wave_nv<T, E, 8, WPR, WPB>(a, nvec, stream);
     }
     if constexpr (MAXNV >= 16) {
-        if (need <= 12) return launch_wave_nv<T, E, 12, WPR>(a, nvec, stream);
-        if (need <= 16) return launch_wave_nv<T, E, 16, WPR>(a, nvec, stream);
+        if (need <= 12) return launch_wave_nv<T, E, 12, WPR, WPB>(a, nvec, stream);
+        if (need <= 16) return launch_wave_nv<T, E, 16, WPR, WPB>(a, nvec, stream);
     }
     if constexpr (MAXNV >= 32) {
-        if (need <= 24) return launch_wave_nv<T, E, 24, WPR>(a, nvec, stream);
-        if (need <= 32) return launch_wave_nv<T, E, 32, WPR>(a, nvec, stream);
+        if (need <= 24) return launch_wave_nv<T, E, 24, WPR, WPB>(a, nvec, stream);
+        if (need <= 32) return launch_wave_nv<T, E, 32, WPR, WPB>(a, nvec, stream);
     }
     return hipErrorInvalidValue;  // callers check the width first
 }
 
-// Accesses per lane: a row goes to the fewest waves (1, 2 or 4) that keep
-// it within kNvLane<T, E> accesses per lane -- about 64 VGPRs of row data,
-// which leaves room for 8 waves per SIMD (measured on 4096-wide float16
-// rows: two waves of 4 vectors per lane 6.1 TB/s, one wave of 8 vectors
-// 5.7 TB/s) -- and rows wider than four waves' worth go to four waves with
-// up to 16 accesses per lane (32 for scalars).
+// Accesses per lane: a row goes to the fewest waves (1, 2, 4, 8 or 16) that
+// keep it within kNvLane<T, E> accesses per lane -- about 64 VGPRs of row
+// data, which leaves room for 8 waves per SIMD (measured on 4096-wide
+// float16 rows: two waves of 4 vectors per lane 6.1 TB/s, one wave of 8
+// vectors 5.7 TB/s; float32 rows of 8192: eight waves of 4 vectors 5.9 TB/s,
+// four waves of 8 vectors 5.4 TB/s).
 template <typename T, int E> constexpr int kNvLane = E * sizeof(T) >= 16 ? 4 : E * sizeof(T) == 8 ? 8 : 16;
 template <int E> constexpr int kMaxNvRowBlock = E == 1 ? 32 : 16;
 
 template <typename T, int E>
 hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char** route) {
-    static const char* const kNames[4][4] = {
+    static const char* const kNames[6][4] = {
         {"ssln.wave.scalar", "ssln.wave.vec4", "ssln.wave.vec8", "ssln.wave.vec16"},
         {"ssln.wave2.scalar", "ssln.wave2.vec4", "ssln.wave2.vec8", "ssln.wave2.vec16"},
         {"ssln.rowblock.scalar", "ssln.rowblock.vec4", "ssln.rowblock.vec8", "ssln.rowblock.vec16"},
-        {"ssln.segment.scalar", "ssln.segment.vec4", "ssln.segment.vec8", "ssln.segment.vec16"}};
+        {"ssln.segment.scalar", "ssln.segment.vec4", "ssln.segment.vec8", "ssln.segment.vec16"},
+        {"ssln.row8.scalar", "ssln.row8.vec4", "ssln.row8.vec8", "ssln.row8.vec16"},
+        {"ssln.row16.scalar", "ssln.row16.vec4", "ssln.row16.vec8", "ssln.row16.vec16"}};
     constexpr int kName = E == 1 ? 0 : E * sizeof(T) == 16 ? 3 : E * sizeof(T) == 8 ? 2 : 1;
     constexpr int NVL = kNvLane<T, E>;
     const int64_t nvec = a.hidden / E;
@@ -509,6 +513,18 @@ hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char**
     if (nvec <= 128 * NVL) {
         *route = kNames[1][kName];
         return launch_wave<T, E, NVL, 2>(a, int(nvec), stream);
+    }
+    if (nvec <= 256 * NVL) {
+        *route = kNames[2][kName];
+        return launch_wave<T, E, NVL, 4>(a, int(nvec), stream);
+    }
+    if (nvec <= 512 * NVL) {
+        *route = kNames[4][kName];
+        return launch_wave<T, E, NVL, 8, 8>(a, int(nvec), stream);
+    }
+    if (nvec <= 1024 * NVL) {
+        *route = kNames[5][kName];
+        return launch_wave<T, E, NVL, 16, 16>(a, int(nvec), stream);
     }
     *route = kNames[2][kName];
     return launch_wave<T, E, kMaxNvRowBlock<E>, 4>(a, int(nvec), stream);

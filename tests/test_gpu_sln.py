@@ -45,13 +45,15 @@ SHAPES = [
     ((13, 768), F16, False, False),
     ((3, 5, 4096), F16, True, False),   # two waves per row, odd row count
     ((7, 8192), F16, True, True),       # four waves per row
-    ((5, 8192), F32, False, True),
+    ((5, 8192), F32, False, True),      # eight waves per row
+    ((3, 20480), F16, True, False),     # sixteen waves per row, ragged
+    ((2, 16384), F32, True, True),      # float32, sixteen waves per row
     ((9, 1000), F16, True, False),      # ragged lanes
     ((6, 33), F32, True, False),        # scalars
     ((4, 1), F16, True, True),          # one element: variance 0
     ((3, 4100), F16, True, False),      # 8-byte vectors
     ((3, 4098), F16, False, True),      # 4-byte vectors
-    ((2, 4097), F16, True, False),      # odd width: scalars, four waves
+    ((2, 4097), F16, True, False),      # odd width: scalars, eight waves
     ((2, 40000), F16, True, True),      # block route (three passes), 16-byte vectors
     ((3, 20002), F32, True, False),     # block route, 8-byte vectors, ragged step
     ((2, 8193), F16, False, True),      # block route, scalars

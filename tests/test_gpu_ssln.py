@@ -44,16 +44,17 @@ SHAPES = [
     ((13, 768), F16, False),
     ((3, 5, 4096), F16, True),
     ((7, 8192), F16, False),
-    ((5, 8192), F32, True),
+    ((5, 8192), F32, True),      # float32, eight waves per row
     ((9, 1000), F16, True),      # 125 vectors: ragged second pass over the wave
     ((6, 33), F32, False),       # not a whole number of vectors
     ((4, 1), F16, True),
-    ((2, 3, 10000), F16, False), # four waves per row, ragged
+    ((2, 3, 10000), F16, False), # eight waves per row, ragged
     ((257, 256), F32, False),
-    ((3, 12288), F16, True),     # four waves per row, 6 vectors per lane
-    ((2, 32768), F16, False),    # four waves per row, 16 vectors per lane (widest)
-    ((2, 16384), F32, True),     # float32 four waves per row, 16 vectors per lane
-    ((2, 10000), F32, False),    # float32 four waves per row, ragged
+    ((3, 12288), F16, True),     # eight waves per row, 3 vectors per lane
+    ((2, 32768), F16, False),    # sixteen waves per row, 4 vectors per lane (widest)
+    ((3, 20480), F16, True),     # sixteen waves per row, ragged
+    ((2, 16384), F32, True),     # float32 sixteen waves per row
+    ((2, 10000), F32, False),    # float32 sixteen waves per row, ragged
     ((2, 40000), F16, True),     # wider than any register-resident route: block route
     ((3, 65536), F16, False),    # block route, 16-byte vectors, whole steps
     ((2, 20002), F32, True),     # float32 block route, 8-byte vectors, ragged step
@@ -62,8 +63,9 @@ SHAPES = [
     ((5, 4092), F16, True),      # 8-byte vectors, two waves per row (odd row count)
     ((5, 4098), F16, False),     # 4-byte vectors, 2049 of them: four waves per row
     ((3, 2046), F16, True),      # 4-byte vectors, one wave per row
-    ((4, 4097), F16, False),     # odd width: scalars, four waves per row
-    ((3, 6002), F32, True),      # float32 8-byte vectors, four waves per row
+    ((4, 4097), F16, False),     # odd width: scalars, eight waves per row
+    ((3, 6000), F16, True),      # 750 sixteen-byte vectors: four waves per row, ragged
+    ((3, 6002), F32, True),      # float32 8-byte vectors, eight waves per row
     ((2, 8193), F16, True),      # odd and wider than the scalar registers: block route
     # rows of at most 32 accesses: lane groups, several rows per wave
     ((1000, 128), F16, True),    # 16 sixteen-byte vectors: 16 lanes per row, 4 rows per thread
@@ -95,9 +97,16 @@ def expected_route(shape, dt):
         return f"ssln.wave.{name}"
     if nvec <= 128 * per_lane:
         return f"ssln.wave2.{name}"
-    if nvec <= 256 * (32 if E == 1 else 16):
+    max_regs = 256 * (32 if E == 1 else 16)  # vectors the register routes hold
+    if nvec > max_regs:
+        return "ssln.block" if E == 1 else f"ssln.block.{name}"
+    if nvec <= 256 * per_lane:
         return f"ssln.rowblock.{name}"
-    return "ssln.block" if E == 1 else f"ssln.block.{name}"
+    if nvec <= 512 * per_lane:
+        return f"ssln.row8.{name}"
+    if nvec <= 1024 * per_lane:
+        return f"ssln.row16.{name}"
+    return f"ssln.rowblock.{name}"
 
 
 @pytest.mark.parametrize("route", ["auto", "scalar", "block"])
