@@ -485,7 +485,12 @@ hipError_t launch_wave(const SslnArgs& a, int nvec, hipStream_t stream) {
 // vectors 5.7 TB/s; float32 rows of 8192: eight waves of 4 vectors 5.9 TB/s,
 // four waves of 8 vectors 5.4 TB/s).
 template <typename T, int E> constexpr int kNvLane = E * sizeof(T) >= 16 ? 4 : E * sizeof(T) == 8 ? 8 : 16;
-template <int E> constexpr int kMaxNvRowBlock = E == 1 ? 32 : 16;
+// Accesses per lane of the widest register rows (sixteen waves): twice
+// kNvLane for 16-byte vectors (8, about 100 VGPRs: 128 KB rows), kNvLane for
+// narrower accesses (deeper ones spill under the 1024-thread block's
+// 128-VGPR limit).
+template <typename T, int E> constexpr int kNvWidest = E * sizeof(T) >= 16 ? 2 * kNvLane<T, E> : kNvLane<T, E>;
+template <typename T, int E> constexpr int64_t kMaxRegisterRow = int64_t(1024) * kNvWidest<T, E> * E;
 
 template <typename T, int E>
 hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char** route) {
@@ -522,12 +527,9 @@ hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char**
         *route = kNames[4][kName];
         return launch_wave<T, E, NVL, 8, 8>(a, int(nvec), stream);
     }
-    if (nvec <= 1024 * NVL) {
-        *route = kNames[5][kName];
-        return launch_wave<T, E, NVL, 16, 16>(a, int(nvec), stream);
-    }
-    *route = kNames[2][kName];
-    return launch_wave<T, E, kMaxNvRowBlock<E>, 4>(a, int(nvec), stream);
+    *route = kNames[5][kName];
+    if (nvec <= 1024 * NVL) return launch_wave<T, E, NVL, 16, 16>(a, int(nvec), stream);
+    return launch_wave<T, E, kNvWidest<T, E>, 16, 16>(a, int(nvec), stream);  // up to kMaxRegisterRow
 }
 
 template <typename T>
@@ -535,7 +537,15 @@ hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, cons
     // Widest access that divides the row and every tensor's base.
     int E = widest_vector<T>(a.hidden, {a.input, a.skip, a.gamma, a.beta, a.bias, a.output, a.sum});
     if (want == Route::Scalar) E = 1;
-    const int64_t max_regs = 256 * int64_t(E) * (E == 1 ? kMaxNvRowBlock<1> : kMaxNvRowBlock<2>);
+    int64_t max_regs = kMaxRegisterRow<T, 1>;
+    if constexpr (sizeof(T) == 2) {
+        if (E == 8) max_regs = kMaxRegisterRow<T, 8>;
+        if (E == 4) max_regs = kMaxRegisterRow<T, 4>;
+        if (E == 2) max_regs = kMaxRegisterRow<T, 2>;
+    } else {
+        if (E == 4) max_regs = kMaxRegisterRow<T, 4>;
+        if (E == 2) max_regs = kMaxRegisterRow<T, 2>;
+    }
     if (want != Route::Block && a.hidden <= max_regs) {
         if constexpr (sizeof(T) == 2) {
             if (E == 8) return launch_ssln_width<T, 8>(a, stream, route);

@@ -54,9 +54,12 @@ SHAPES = [
     ((3, 4100), F16, True, False),      # 8-byte vectors
     ((3, 4098), F16, False, True),      # 4-byte vectors
     ((2, 4097), F16, True, False),      # odd width: scalars, eight waves
-    ((2, 40000), F16, True, True),      # block route (three passes), 16-byte vectors
+    ((2, 40000), F16, True, True),      # sixteen waves, 5 vectors per lane
+    ((2, 65544), F16, True, True),      # block route (three passes), 16-byte vectors
+    ((2, 40000), F32, False, True),     # float32 block route
     ((3, 20002), F32, True, False),     # block route, 8-byte vectors, ragged step
-    ((2, 8193), F16, False, True),      # block route, scalars
+    ((2, 8193), F16, False, True),      # scalars, sixteen waves
+    ((2, 16385), F16, False, True),     # block route, scalars
     ((1000, 128), F16, True, True),     # lane groups: 16 lanes per row
     ((64, 6), F32, True, False),        # lane groups of 4
     ((31, 7), F16, True, True),         # scalars in lane groups of 8
@@ -74,8 +77,8 @@ def test_matches_oracle(shape, dt, beta, bias, route):
     check(ref, out)
     if route == "block":
         assert used == "ssln.block"
-    elif route == "auto" and shape[-1] * np.dtype(dt).itemsize > 65536:
-        assert used.startswith("ssln.block")  # wider than 256 lanes x 16 x 16 bytes
+    elif route == "auto" and shape[-1] * np.dtype(dt).itemsize > 131072:
+        assert used.startswith("ssln.block")  # wider than 1024 lanes x 8 x 16 bytes
 
 
 @pytest.mark.parametrize("want", [(), ("sum",), ("mean",), ("inv",), ("mean", "inv", "sum")])

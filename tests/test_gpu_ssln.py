@@ -55,8 +55,13 @@ SHAPES = [
     ((3, 20480), F16, True),     # sixteen waves per row, ragged
     ((2, 16384), F32, True),     # float32 sixteen waves per row
     ((2, 10000), F32, False),    # float32 sixteen waves per row, ragged
-    ((2, 40000), F16, True),     # wider than any register-resident route: block route
-    ((3, 65536), F16, False),    # block route, 16-byte vectors, whole steps
+    ((2, 40000), F16, True),     # sixteen waves, 5 vectors per lane
+    ((2, 65544), F16, True),     # wider than any register-resident route: block route
+    ((2, 40000), F32, False),    # float32 block route
+    ((2, 30000), F32, True),     # float32 sixteen waves, 8 vectors per lane, ragged
+    ((2, 20004), F16, False),    # 8-byte vectors, sixteen waves
+    ((3, 65536), F16, False),    # sixteen waves, 8 vectors per lane (widest register row)
+    ((2, 131072), F16, False),   # block route, 16-byte vectors, whole steps
     ((2, 20002), F32, True),     # float32 block route, 8-byte vectors, ragged step
     ((2, 32770), F16, True),     # block route, 4-byte vectors
     ((7, 4100), F16, True),      # 8-byte vectors, 1025 of them: four waves per row
@@ -66,7 +71,8 @@ SHAPES = [
     ((4, 4097), F16, False),     # odd width: scalars, eight waves per row
     ((3, 6000), F16, True),      # 750 sixteen-byte vectors: four waves per row, ragged
     ((3, 6002), F32, True),      # float32 8-byte vectors, eight waves per row
-    ((2, 8193), F16, True),      # odd and wider than the scalar registers: block route
+    ((2, 8193), F16, True),      # odd: scalars, sixteen waves
+    ((2, 16385), F16, True),     # odd and wider than the scalar registers: block route
     # rows of at most 32 accesses: lane groups, several rows per wave
     ((1000, 128), F16, True),    # 16 sixteen-byte vectors: 16 lanes per row, 4 rows per thread
     ((777, 256), F16, False),    # 32 vectors: 32 lanes per row
@@ -97,16 +103,14 @@ def expected_route(shape, dt):
         return f"ssln.wave.{name}"
     if nvec <= 128 * per_lane:
         return f"ssln.wave2.{name}"
-    max_regs = 256 * (32 if E == 1 else 16)  # vectors the register routes hold
-    if nvec > max_regs:
+    widest = 2 * per_lane if width == 16 else per_lane  # accesses per lane of 16-wave rows
+    if nvec > 1024 * widest:
         return "ssln.block" if E == 1 else f"ssln.block.{name}"
     if nvec <= 256 * per_lane:
         return f"ssln.rowblock.{name}"
     if nvec <= 512 * per_lane:
         return f"ssln.row8.{name}"
-    if nvec <= 1024 * per_lane:
-        return f"ssln.row16.{name}"
-    return f"ssln.rowblock.{name}"
+    return f"ssln.row16.{name}"
 
 
 @pytest.mark.parametrize("route", ["auto", "scalar", "block"])
