@@ -206,15 +206,18 @@ gated_tile_kernel(const T* __restrict__ X, const T* __restrict__ scale,
     }
 }
 
-// Row route: thread t holds vectors t, t + 256, ... (NV of them) of the
-// block's row; lanes past the row re-read its last vector and discard it.
-template <typename T, int E, int NV>
-__global__ void __launch_bounds__(256)
+// Row route: a block of TPB threads (4, 8 or 16 waves) per row; thread t
+// holds vectors t, t + TPB, ... (NV of them); lanes past the row re-read
+// its last vector and discard it.  The wave sums are added as a pairwise
+// tree in wave order.
+template <typename T, int E, int NV, int TPB>
+__global__ void __launch_bounds__(TPB)
 gated_row_kernel(const T* __restrict__ X, const T* __restrict__ scale,
                  const T* __restrict__ gate, T* __restrict__ Y, int64_t rows, int nvec,
                  float span_f, float eps) {
     using V = Vec<T, E>;
-    __shared__ float wave_part[4];
+    constexpr int W = TPB / 64;
+    __shared__ float wave_part[W];
     const int t = threadIdx.x;
     auto clamp = [&](int j) { return j < nvec ? j : nvec - 1; };
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
@@ -222,14 +225,14 @@ gated_row_kernel(const T* __restrict__ X, const T* __restrict__ scale,
         V xs[NV], gs[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int jc = clamp(v * 256 + t);
+            const int jc = clamp(v * TPB + t);
             xs[v] = load_vec_stream<T, E>(X, base + jc);
             gs[v] = load_vec_stream<T, E>(gate, base + jc);
         }
         float acc = 0.0f;
 #pragma unroll
         for (int v = 0; v < NV; ++v)
-            if (v * 256 + t < nvec) {
+            if (v * TPB + t < nvec) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const float x = to_f32(xs[v].v[e]);
@@ -239,12 +242,19 @@ gated_row_kernel(const T* __restrict__ X, const T* __restrict__ scale,
         acc = segment_sum<64>(acc);
         if ((t & 63) == 0) wave_part[t >> 6] = acc;
         __syncthreads();
-        const float total = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
+        float part[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) part[w] = wave_part[w];
+#pragma unroll
+        for (int s = 1; s < W; s *= 2)
+#pragma unroll
+            for (int w = 0; w + s < W; w += 2 * s) part[w] += part[w + s];
+        const float total = part[0];
         __syncthreads();  // wave_part is rewritten for the next row
         const float r = inv_sqrt(total / span_f + eps);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int j = v * 256 + t;
+            const int j = v * TPB + t;
             const V sv = load_vec<T, E>(scale, clamp(j));
             V out;
 #pragma unroll
@@ -353,24 +363,57 @@ hipError_t launch_segment_for(const GatedArgs& a, int nvec, hipStream_t stream) 
 }
 
 constexpr int64_t kMaxSegmentVectors = 1024;
-constexpr int64_t kMaxRowVectors = 256 * 16;
+// Widest rows of the row route: 16 waves of four 16-byte vectors per thread,
+// or of eight narrower accesses (eight 16-byte ones would spill under the
+// 1024-thread block's 128-VGPR limit).
+constexpr int64_t kMaxRowVectors16 = 1024 * 4;
+constexpr int64_t kMaxRowVectors = 1024 * 8;
 
-template <typename T, int E, int NV>
+template <typename T, int E, int NV, int TPB>
 hipError_t launch_row(const GatedArgs& a, int nvec, hipStream_t stream) {
     const int64_t blocks = a.rows < (int64_t(1) << 20) ? a.rows : (int64_t(1) << 20);
-    hipLaunchKernelGGL((gated_row_kernel<T, E, NV>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((gated_row_kernel<T, E, NV, TPB>), dim3(unsigned(blocks)), dim3(TPB), 0, stream,
                        static_cast<const T*>(a.X), static_cast<const T*>(a.scale),
                        static_cast<const T*>(a.gate), static_cast<T*>(a.Y), a.rows, nvec,
                        float(a.span), a.epsilon);
     return hipGetLastError();
 }
 
-// The fewest of 8, 12 or 16 vectors per thread that hold the row.
+template <typename T, int E, int TPB>
+hipError_t launch_row_nv(const GatedArgs& a, int nvec, int nv, hipStream_t stream) {
+    switch (nv) {
+        case 2: return launch_row<T, E, 2, TPB>(a, nvec, stream);
+        case 3: return launch_row<T, E, 3, TPB>(a, nvec, stream);
+        case 4: return launch_row<T, E, 4, TPB>(a, nvec, stream);
+        default: break;
+    }
+    if constexpr (E * sizeof(T) < 16) {
+        switch (nv) {
+            case 5: return launch_row<T, E, 5, TPB>(a, nvec, stream);
+            case 6: return launch_row<T, E, 6, TPB>(a, nvec, stream);
+            case 7: return launch_row<T, E, 7, TPB>(a, nvec, stream);
+            case 8: return launch_row<T, E, 8, TPB>(a, nvec, stream);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;  // callers check the width first
+}
+
+// Rows of more than 1024 vectors: 8 or 16 waves (512 or 1024 threads) of
+// ceil(nvec / threads) vectors per thread, at most four 16-byte vectors or
+// eight narrower accesses, whichever of the two leaves fewer lanes re-reading
+// past the row's end; on a tie 512 threads, which hold more rows' bytes in
+// flight per CU.  One 256-thread block of 8-16 vectors per thread ran
+// float32 C = 16384 at 5.4 TB/s, 16 waves of four run it at 6.1; 3072
+// vectors as 16 waves of four (a quarter of the loads discarded) ran at
+// 5.0 TB/s against 5.4 on one 256-thread block of twelve.
 template <typename T, int E>
 hipError_t launch_row_for(const GatedArgs& a, int nvec, hipStream_t stream) {
-    if (nvec <= 256 * 8) return launch_row<T, E, 8>(a, nvec, stream);
-    if (nvec <= 256 * 12) return launch_row<T, E, 12>(a, nvec, stream);
-    return launch_row<T, E, 16>(a, nvec, stream);
+    constexpr int kNvMax = E * sizeof(T) >= 16 ? 4 : 8;
+    const int nv512 = (nvec + 511) / 512, nv1024 = (nvec + 1023) / 1024;
+    if (nv512 <= kNvMax && 512 * nv512 <= 1024 * nv1024)
+        return launch_row_nv<T, E, 512>(a, nvec, nv512, stream);
+    return launch_row_nv<T, E, 1024>(a, nvec, nv1024, stream);
 }
 
 template <typename T, int E>
@@ -481,7 +524,7 @@ hipError_t launch_gated_t(const GatedArgs& a, Route want, hipStream_t stream, co
         *route = "gated.segment.scalar";
         return launch_segment_for<T, 1>(a, int(nvec), stream);
     }
-    if (want != Route::Block && nvec <= kMaxRowVectors) {
+    if (want != Route::Block && nvec <= (E * sizeof(T) == 16 ? kMaxRowVectors16 : kMaxRowVectors)) {
         if (E * sizeof(T) == 16) {
             *route = "gated.row.vec16";
             return launch_row_for<T, VecWidth<T>::value>(a, int(nvec), stream);

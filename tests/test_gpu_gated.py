@@ -25,22 +25,25 @@ CASES = [
     ((2, 4096), 128, F32),
     ((6, 1024), 1024, F16),      # 128 vectors: 64 lanes x 2
     ((3, 8192), 8192, F16),      # 1024 vectors: 64 lanes x 16
-    ((2, 5000), 5000, F32),      # 1250 sixteen-byte vectors: one workgroup per row in registers
-    ((2, 2, 9000), 9000, F16),   # 1125 vectors (8 per thread)
+    ((2, 5000), 5000, F32),      # 1250 sixteen-byte vectors: one 512-thread workgroup per row in registers
+    ((2, 2, 9000), 9000, F16),   # 1125 vectors: 8 waves, ragged
     ((1000,), 10, F16),          # rank 1
     ((4, 396), 132, F16),        # 8-byte vectors: 33 per row
     ((3, 650), 130, F16),        # 4-byte vectors: 65 per row, two per lane
     ((5, 129), 129, F16),        # odd span: scalars
     ((4, 6), 6, F32),            # float32 8-byte vectors: 3 per row
     ((2, 8200), 4100, F16),      # 1025 eight-byte vectors: row route
-    ((3, 24576), 24576, F16),    # 3072 vectors: 12 per thread
-    ((2, 32768), 32768, F16),    # 4096 vectors: 16 per thread
+    ((3, 24576), 24576, F16),    # 3072 vectors: 16 waves, ragged
+    ((2, 32768), 32768, F16),    # 4096 vectors: 16 waves of 4 per thread
     ((3, 32776), 32776, F16),    # 4097 vectors: two-pass block route, vectorized
+    ((2, 12000), 12000, F16),    # 1500 vectors: 8 waves, ragged
     ((2, 16386), 16386, F32),    # 8193 eight-byte vectors: block route
-    ((3, 4099), 4099, F16),      # 4099 scalars: scalar block route
-    ((3, 4095), 4095, F16),      # 4095 scalars: row route, 16 per thread
-    ((4, 2049), 2049, F32),      # 2049 scalars: row route, 12 per thread
-    ((2, 5003), 5003, F32),      # 5003 scalars: scalar block route
+    ((2, 16382), 16382, F32),    # 8191 eight-byte vectors: 16 waves of 8 per thread
+    ((3, 4099), 4099, F16),      # 4099 scalars: 16 waves of 8 per thread
+    ((2, 8195), 8195, F16),      # 8195 scalars: scalar block route
+    ((3, 4095), 4095, F16),      # 4095 scalars: 16 waves of 4 per thread
+    ((4, 2049), 2049, F32),      # 2049 scalars: 16 waves, ragged
+    ((2, 5003), 5003, F32),      # 5003 scalars: 16 waves of 8 per thread
     # tile route (float16 rows of 33-128 vectors of 8 or 4 bytes that fill
     # < 60 % of the segment route's lanes, packed back to back): several
     # tiles, a ragged last tile and waves past the last row
@@ -95,7 +98,7 @@ def expected_route(C, dt, route="auto"):
     name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
     if route == "block":
         return "gated.block"
-    if C // E > 4096:
+    if C // E > (4096 if width == 16 else 8192):  # the row route's widest rows
         return "gated.block" if E == 1 else f"gated.block.{name}"
     if C // E > 1024:
         return f"gated.row.{name}"
