@@ -20,11 +20,16 @@
 //          and stores (gamma and bias, shared by every row, stay cached).
 //          E elements per access: the widest of 16-, 8- and 4-byte vectors
 //          that divides the row and every base address, else scalars.
-//   rowblock  the same with four waves (one 256-thread workgroup) per row
-//          for wider rows (up to 16 vectors per lane: 32768 float16 /
-//          16384 float32 elements with 16-byte vectors; 32 scalars per lane:
-//          8192 elements): the wave sums meet in LDS and are added in wave
-//          order.
+//   rowblock, row8, row16  the same with 4, 8 or 16 waves (a 256-, 512-
+//          or 1024-thread workgroup) per row for wider rows, at the same
+//          accesses per lane, and 16 waves of up to 8 sixteen-byte vectors
+//          per lane for the widest (128 KB rows: 65536 float16 / 32768
+//          float32 elements): the wave sums meet in LDS and are added in
+//          wave order.
+//   phase  rows that would otherwise be read element by element (an odd
+//          row length, or data tensors sharing a base 2 or 6 bytes off a
+//          16-byte boundary): aligned 16-byte vectors read across row
+//          boundaries, boundary elements masked (ssln_phase_kernel).
 //   block  one 256-thread workgroup per row for any wider row: S is formed
 //          twice (once for the statistic, once for the output; three times
 //          with the mean removed), reading the inputs again each time.
@@ -184,6 +189,191 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
             }
         }
         if ((FULL || idx < nvec) && live) store_vec_stream<T, E>(output, base + idx, out);
+    }
+}
+
+// Elements k .. k + E - 1 of the 2E-element concatenation [lo, hi] of two
+// 16-byte vectors (0 <= k < E): byte funnel shifts of their eight dwords.
+// The dword offset is applied with value selects, not branches: an
+// if / else-if chain on it, which the compiler could not prove uniform,
+// was lowered into exec-masked blocks that left the last case's values
+// unassigned (seen in the generated code and as wrong rows on the GPU).
+template <typename T, int E>
+__device__ __forceinline__ Vec<T, E> funnel16(const Vec<T, E>& lo, const Vec<T, E>& hi, int k) {
+    static_assert(sizeof(Vec<T, E>) == 16, "16-byte vectors");
+    const u32x4 a = __builtin_bit_cast(u32x4, lo), b = __builtin_bit_cast(u32x4, hi);
+    const uint32_t c[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const int byte = k * int(sizeof(T));
+    const int q = byte >> 2;
+    const uint32_t r = uint32_t(byte & 3);
+    uint32_t w[5];  // dwords q .. q + 4 of [a, b]
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const uint32_t x01 = q == 0 ? c[j] : c[j + 1];
+        const uint32_t x23 = q == 2 ? c[j + 2] : c[j + 3 < 8 ? j + 3 : 7];
+        w[j] = q < 2 ? x01 : x23;
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], r);
+    return __builtin_bit_cast(Vec<T, E>, o);
+}
+
+// Rows off the 16-byte grid: a row length that is not a whole number of
+// 16-byte vectors, or data tensors (input, skip, output, S) whose common
+// base address sits off a 16-byte boundary.  Counted from the boundary at
+// or below that base, row r holds elements [a, a + hidden), a = r * hidden +
+// phase; its lanes read the aligned 16-byte vectors that cover them (the
+// first and last may hold a neighbouring row's elements, read and left
+// unused, never outside the 16-byte chunks that hold the tensors' own
+// elements), write the interior vectors whole and the two boundary vectors
+// element by element.  gamma, beta and bias are 16-byte aligned: a lane
+// takes its elements' values from the two aligned vectors around them,
+// funnel-shifted by the row's offset p = a mod E (uniform over the row).
+// Without a bias or beta the host passes gamma's address and a zero mask
+// (the loads stay unconditional).  Otherwise the arithmetic, its order and
+// the row reduction are those of ssln_wave_kernel.
+template <typename T, int E, int NV, int WPR, bool CENTER, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
+ssln_phase_kernel(const T* __restrict__ input, const T* __restrict__ skip,
+                  const T* __restrict__ gamma, const T* __restrict__ beta,
+                  const T* __restrict__ bias, T* __restrict__ output, float* __restrict__ mean,
+                  float* __restrict__ inv_std_var, T* __restrict__ sum,
+                  int64_t rows, int hidden, int phase, int nvg, float hidden_f, float eps,
+                  uint32_t beta_mask, uint32_t bias_mask) {
+    using V = Vec<T, E>;
+    constexpr int LANES = 64 * WPR;
+    static_assert(WPB % WPR == 0, "whole rows per block");
+    __shared__ float wave_part[WPB];
+    const int lane = threadIdx.x % LANES;
+    const int64_t my_row = int64_t(blockIdx.x) * (WPB / WPR) + threadIdx.x / LANES;
+    if (WPR != 2 && my_row >= rows) return;
+    const bool live = my_row < rows;
+    const int64_t row = live ? my_row : rows - 1;
+    const bool has_bias = bias_mask != 0;
+
+    const int64_t a = row * hidden + phase;
+    const int64_t v0 = a / E;                              // the row's first vector
+    const int p = int(a - v0 * E);                         // its first element's place in it
+    const int nvr = int((a + hidden + E - 1) / E - v0);    // vectors the row touches
+    const T* in_a = input - phase;                         // 16-byte aligned bases
+    const T* sk_a = skip - phase;
+    T* out_a = output - phase;
+    T* sum_a = sum ? sum - phase : nullptr;
+    const int k_shift = (E - p) % E;
+    const int pv = p > 0 ? 1 : 0;
+    // The parameter values of vector i's elements (row positions i*E - p + e).
+    auto param = [&](const T* base, int i) {
+        int lo = i - pv, hi = i - pv + 1;
+        lo = lo < 0 ? 0 : (lo < nvg ? lo : nvg - 1);
+        hi = hi < 0 ? 0 : (hi < nvg ? hi : nvg - 1);
+        return funnel16<T, E>(load_vec<T, E>(base, lo), load_vec<T, E>(base, hi), k_shift);
+    };
+
+    auto clamp = [&](int i) { return i < nvr ? i : nvr - 1; };
+    V xs[NV], ks[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int i = clamp(v * LANES + lane);
+        xs[v] = load_vec_stream<T, E>(in_a, v0 + i);
+        ks[v] = load_vec_stream<T, E>(sk_a, v0 + i);
+    }
+    float shift = 0.0f;
+    if constexpr (CENTER) {
+        T rounded;
+        shift = residual_sum<T>(to_f32(input[row * hidden]), to_f32(skip[row * hidden]), has_bias,
+                                has_bias ? to_f32(bias[0]) : 0.0f, rounded);
+    }
+    // Element e of vector i lies in the row when lo_e <= e < hi_e.
+    auto in_row = [&](int i, int e) { return i < nvr && e >= p - i * E && e < hidden + p - i * E; };
+    auto whole = [&](int i) { return i < nvr && p - i * E <= 0 && hidden + p - i * E >= E; };
+
+    V ss[NV];
+    float acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int i = v * LANES + lane;
+        const V bv = mask_bits(param(bias, i), bias_mask);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float s = residual_sum<T>(to_f32(xs[v].v[e]), to_f32(ks[v].v[e]), has_bias,
+                                            to_f32(bv.v[e]), ss[v].v[e]);
+            const bool ok = in_row(i, e);
+            if constexpr (CENTER) acc += ok ? s - shift : 0.0f;
+            else acc = ok ? fmaf_(s, s, acc) : acc;
+        }
+        if (sum_a && live) {
+            if (whole(i)) {
+                store_vec_stream<T, E>(sum_a, v0 + i, ss[v]);
+            } else if (i < nvr) {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (in_row(i, e)) sum_a[(v0 + i) * E + e] = ss[v].v[e];
+            }
+        }
+    }
+
+    auto row_total = [&](float part) {
+        float total = segment_sum<64>(part);
+        if constexpr (WPR > 1) {
+            __syncthreads();
+            if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = total;
+            __syncthreads();
+            const int w0 = (threadIdx.x / LANES) * WPR;
+            total = wave_part[w0];
+#pragma unroll
+            for (int w = 1; w < WPR; ++w) total += wave_part[w0 + w];
+        }
+        return total;
+    };
+    float md = 0.0f, r;
+    if constexpr (!CENTER) {
+        r = inv_sqrt(row_total(acc) / hidden_f + eps);
+    } else {
+        md = row_total(acc) / hidden_f;
+        float dev = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int i = v * LANES + lane;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float d = (to_f32(ss[v].v[e]) - shift) - md;
+                dev = in_row(i, e) ? fmaf_(d, d, dev) : dev;
+            }
+        }
+        r = inv_sqrt(row_total(dev) / hidden_f + eps);
+    }
+    if (live && lane == 0) {
+        if (inv_std_var) inv_std_var[row] = r;
+        if (mean) mean[row] = shift + md;
+    }
+
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int i = v * LANES + lane;
+        const V gv = param(gamma, i);
+        V bt = {};
+        if constexpr (CENTER) bt = mask_bits(param(beta, i), beta_mask);
+        V out;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if constexpr (CENTER) {
+                float y = ((to_f32(ss[v].v[e]) - shift) - md) * r * to_f32(gv.v[e]);
+                y = y + to_f32(bt.v[e]);
+                out.v[e] = from_f32<T>(y);
+            } else {
+                out.v[e] = from_f32<T>(to_f32(ss[v].v[e]) * r * to_f32(gv.v[e]));
+            }
+        }
+        if (live) {
+            if (whole(i)) {
+                store_vec_stream<T, E>(out_a, v0 + i, out);
+            } else if (i < nvr) {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (in_row(i, e)) out_a[(v0 + i) * E + e] = out.v[e];
+            }
+        }
     }
 }
 
@@ -532,11 +722,82 @@ hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char**
     return launch_wave<T, E, kNvWidest<T, E>, 16, 16>(a, int(nvec), stream);  // up to kMaxRegisterRow
 }
 
+template <typename T, int NV, int WPR, int WPB>
+hipError_t launch_phase_nv(const SslnArgs& a, int phase, int nvg, hipStream_t stream) {
+    constexpr int E = VecWidth<T>::value;
+    constexpr int rows_per_block = WPB / WPR;
+    const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+    const T* g = static_cast<const T*>(a.gamma);
+    auto args = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * WPB), 0, stream,
+                           static_cast<const T*>(a.input), static_cast<const T*>(a.skip), g,
+                           a.beta ? static_cast<const T*>(a.beta) : g,
+                           a.bias ? static_cast<const T*>(a.bias) : g, static_cast<T*>(a.output), a.mean,
+                           a.inv_std_var, static_cast<T*>(a.sum), a.rows, int(a.hidden), phase, nvg,
+                           float(a.hidden), a.epsilon, a.beta ? ~0u : 0u, a.bias ? ~0u : 0u);
+    };
+    if (a.center) args(ssln_phase_kernel<T, E, NV, WPR, true, WPB>);
+    else args(ssln_phase_kernel<T, E, NV, WPR, false, WPB>);
+    return hipGetLastError();
+}
+
+template <typename T, int MAXNV, int WPR, int WPB = kWavesPerBlock>
+hipError_t launch_phase(const SslnArgs& a, int nmax, int phase, int nvg, hipStream_t stream) {
+    const int need = (nmax + 64 * WPR - 1) / (64 * WPR);
+    if (need <= 1) return launch_phase_nv<T, 1, WPR, WPB>(a, phase, nvg, stream);
+    if (need <= 2) return launch_phase_nv<T, 2, WPR, WPB>(a, phase, nvg, stream);
+    if (need <= 3) return launch_phase_nv<T, 3, WPR, WPB>(a, phase, nvg, stream);
+    if (need <= 4) return launch_phase_nv<T, 4, WPR, WPB>(a, phase, nvg, stream);
+    if constexpr (MAXNV >= 8) {
+        if (need <= 6) return launch_phase_nv<T, 6, WPR, WPB>(a, phase, nvg, stream);
+        if (need <= 8) return launch_phase_nv<T, 8, WPR, WPB>(a, phase, nvg, stream);
+    }
+    return hipErrorInvalidValue;  // the caller checks the width first
+}
+
+// The phased route for rows off the 16-byte grid (see ssln_phase_kernel):
+// taken when the data tensors share their offset from a 16-byte boundary,
+// gamma, beta and bias are 16-byte aligned, and the row needs more than
+// lane groups' 48 vectors and at most sixteen waves of four.  Returns
+// false, having launched nothing, otherwise.
+template <typename T>
+bool launch_ssln_phase(const SslnArgs& a, hipStream_t stream, const char** route, hipError_t* err) {
+    constexpr int E = VecWidth<T>::value;
+    constexpr int NVL = kNvLane<T, E>;
+    const uintptr_t ph = reinterpret_cast<uintptr_t>(a.input) % 16;
+    auto same = [&](const void* q) { return !q || reinterpret_cast<uintptr_t>(q) % 16 == ph; };
+    if (ph % sizeof(T) != 0 || !same(a.skip) || !same(a.output) || !same(a.sum)) return false;
+    if (!aligned16(a.gamma) || (a.beta && !aligned16(a.beta)) || (a.bias && !aligned16(a.bias)))
+        return false;
+    const int64_t nmax = a.hidden / E + 2;  // vectors a row can touch
+    // Deeper than four vectors per lane its parameter funnels spill under
+    // the 1024-thread block's 128-VGPR limit.
+    if (nmax <= 48 || nmax > 1024 * NVL) return false;
+    const int phase = int(ph / sizeof(T));
+    const int nvg = int((a.hidden + E - 1) / E);
+    const int n = int(nmax);
+    *route = "ssln.phase.vec16";
+    if (nmax <= 64 * NVL) *err = launch_phase<T, NVL, 1>(a, n, phase, nvg, stream);
+    else if (nmax <= 128 * NVL) *err = launch_phase<T, NVL, 2>(a, n, phase, nvg, stream);
+    else if (nmax <= 256 * NVL) *err = launch_phase<T, NVL, 4>(a, n, phase, nvg, stream);
+    else if (nmax <= 512 * NVL) *err = launch_phase<T, NVL, 8, 8>(a, n, phase, nvg, stream);
+    else *err = launch_phase<T, NVL, 16, 16>(a, n, phase, nvg, stream);
+    return true;
+}
+
 template <typename T>
 hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, const char** route) {
     // Widest access that divides the row and every tensor's base.
     int E = widest_vector<T>(a.hidden, {a.input, a.skip, a.gamma, a.beta, a.bias, a.output, a.sum});
     if (want == Route::Scalar) E = 1;
+    // Rows that would otherwise be read element by element take the phased
+    // route (1.2-2.3x: float16 hidden 4097 / 8193 at 5.3 / 5.1 TB/s against
+    // 3.6 / 3.0); against 4- and 8-byte vectors it measured within -7 / +14 %,
+    // so those keep them.
+    if ((want == Route::Auto || want == Route::Vector) && E == 1) {
+        hipError_t err = hipSuccess;
+        if (launch_ssln_phase<T>(a, stream, route, &err)) return err;
+    }
     int64_t max_regs = kMaxRegisterRow<T, 1>;
     if constexpr (sizeof(T) == 2) {
         if (E == 8) max_regs = kMaxRegisterRow<T, 8>;

@@ -53,13 +53,14 @@ SHAPES = [
     ((4, 1), F16, True, True),          # one element: variance 0
     ((3, 4100), F16, True, False),      # 8-byte vectors
     ((3, 4098), F16, False, True),      # 4-byte vectors
-    ((2, 4097), F16, True, False),      # odd width: scalars, eight waves
+    ((2, 4097), F16, True, False),      # odd width: phased route
     ((2, 40000), F16, True, True),      # sixteen waves, 5 vectors per lane
     ((2, 65544), F16, True, True),      # block route (three passes), 16-byte vectors
     ((2, 40000), F32, False, True),     # float32 block route
-    ((3, 20002), F32, True, False),     # block route, 8-byte vectors, ragged step
-    ((2, 8193), F16, False, True),      # scalars, sixteen waves
-    ((2, 16385), F16, False, True),     # block route, scalars
+    ((3, 20002), F32, True, False),     # rows off the 16-byte grid: phased route
+    ((2, 8193), F16, False, True),      # odd: phased route
+    ((2, 16385), F16, False, True),     # odd: phased route, sixteen waves
+    ((2, 32769), F16, True, True),      # block route, scalars
     ((1000, 128), F16, True, True),     # lane groups: 16 lanes per row
     ((64, 6), F32, True, False),        # lane groups of 4
     ((31, 7), F16, True, True),         # scalars in lane groups of 8

@@ -68,11 +68,12 @@ SHAPES = [
     ((5, 4092), F16, True),      # 8-byte vectors, two waves per row (odd row count)
     ((5, 4098), F16, False),     # 4-byte vectors, 2049 of them: four waves per row
     ((3, 2046), F16, True),      # 4-byte vectors, one wave per row
-    ((4, 4097), F16, False),     # odd width: scalars, eight waves per row
+    ((4, 4097), F16, False),     # odd width: phased route (aligned 16-byte vectors across rows)
     ((3, 6000), F16, True),      # 750 sixteen-byte vectors: four waves per row, ragged
     ((3, 6002), F32, True),      # float32 8-byte vectors, eight waves per row
-    ((2, 8193), F16, True),      # odd: scalars, sixteen waves
-    ((2, 16385), F16, True),     # odd and wider than the scalar registers: block route
+    ((2, 8193), F16, True),      # odd: phased route, eight waves
+    ((2, 16385), F16, True),     # odd: phased route, sixteen waves
+    ((2, 32769), F16, True),     # odd and wider than the phased route: scalar block route
     # rows of at most 32 accesses: lane groups, several rows per wave
     ((1000, 128), F16, True),    # 16 sixteen-byte vectors: 16 lanes per row, 4 rows per thread
     ((777, 256), F16, False),    # 32 vectors: 32 lanes per row
@@ -96,6 +97,11 @@ def expected_route(shape, dt):
     E = width // size
     name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
     nvec = hidden // E
+    # Rows that would be read element by element (all bases here are 16-byte
+    # aligned): the phased route reads whole aligned 16-byte vectors when a
+    # row needs more than 48 and at most 1024 x 4 of them.
+    if E == 1 and 48 < hidden // (16 // size) + 2 <= 1024 * 4:
+        return "ssln.phase.vec16"
     if nvec <= 48:
         return f"ssln.segment.{name}"
     per_lane = 4 if E > 1 and width == 16 else 8 if E > 1 and width == 8 else 16
@@ -236,3 +242,63 @@ def test_outputs_leave_neighbouring_memory_untouched():
     s = to_host(stats)
     assert np.all(s[:pad] == -7.0) and np.all(s[pad + rows: rows + 3 * pad] == -7.0)
     assert np.all(s[2 * rows + 3 * pad:] == -7.0)
+
+
+@pytest.mark.parametrize("dt,hidden,offset,center", [
+    (F16, 4096, 1, False), (F16, 4096, 3, True), (F16, 4095, 0, False), (F16, 4097, 5, True),
+    (F16, 1000, 7, False), (F16, 20003, 2, True), (F16, 32753, 6, False), (F16, 391, 4, True),
+    (F32, 4097, 1, False), (F32, 6002, 1, True), (F32, 8191, 3, False), (F32, 4096, 3, True),
+])
+def test_phased_rows(dt, hidden, offset, center):
+    """Rows that would be read element by element, through the C ABI:
+    input, skip, output and S all `offset` elements past a 16-byte boundary
+    (2-byte aligned for float16, 4-byte for float32), or rows of an odd
+    length, take the phased route, which reads whole aligned 16-byte vectors
+    across row boundaries.  Results match
+    the oracle, and nothing outside the outputs is written (canaries around
+    them keep their pattern)."""
+    from group_normalization_amd._lib import lib, check as ck
+    rows, pad = 7, 64
+    if center:
+        w = workloads.sln("t", (rows, hidden), dt, beta=True, bias=True, epsilon=1e-5)
+    else:
+        w = workloads.ssln("t", (rows, hidden), dt, bias=True, epsilon=1e-5)
+    x = workloads.generate(w, seed=hidden + offset)
+    tdt = torch.float16 if dt == F16 else torch.float32
+    n = rows * hidden
+
+    def arena(fill):
+        return torch.full((n + 2 * pad,), fill, dtype=tdt, device="cuda")
+
+    bufs = {k: arena(-7.0) for k in ("input", "skip", "output", "sum")}
+    views = {k: b[pad + offset: pad + offset + n] for k, b in bufs.items()}
+    views["input"].copy_(to_dev(x["input"]).ravel())
+    views["skip"].copy_(to_dev(x["skip"]).ravel())
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    inv = torch.empty(rows, dtype=torch.float32, device="cuda")
+    d = {k: to_dev(x[k]) for k in ("gamma", "bias", "beta") if x.get(k) is not None}
+    code = 1 if dt == F16 else 0
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        if center:
+            ck(lib().skip_layer_norm(code, rows, hidden, views["input"].data_ptr(), views["skip"].data_ptr(),
+                                     d["gamma"].data_ptr(), d["beta"].data_ptr(), d["bias"].data_ptr(), 1e-5,
+                                     views["output"].data_ptr(), mean.data_ptr(), inv.data_ptr(),
+                                     views["sum"].data_ptr(), stream))
+            ref = oracle.skip_layer_norm(x["input"], x["skip"], x["gamma"], x["beta"], x["bias"], 1e-5,
+                                         want_mean=True, want_inv_std_var=True, want_sum=True)
+        else:
+            ck(lib().skip_rms_norm(code, rows, hidden, views["input"].data_ptr(), views["skip"].data_ptr(),
+                                   d["gamma"].data_ptr(), d["bias"].data_ptr(), 1e-5, views["output"].data_ptr(),
+                                   mean.data_ptr(), inv.data_ptr(), views["sum"].data_ptr(), stream))
+            ref = oracle.skip_rms_norm(x["input"], x["skip"], x["gamma"], x["bias"], 1e-5,
+                                       want_mean=True, want_inv_std_var=True, want_sum=True)
+        assert gn.last_route() == "ssln.phase.vec16"
+        torch.cuda.synchronize()
+        assert_close(to_host(views["output"]).reshape(rows, hidden), ref[0], "output")
+        assert_close(to_host(mean), ref[1].reshape(-1), "mean")
+        assert_close(to_host(inv), ref[2].reshape(-1), "inv_std_var")
+        assert_bitwise(to_host(views["sum"]).reshape(rows, hidden), ref[3], "S")
+        for k in ("output", "sum"):
+            b = to_host(bufs[k])
+            assert np.all(b[:pad + offset] == -7.0) and np.all(b[pad + offset + n:] == -7.0), k
