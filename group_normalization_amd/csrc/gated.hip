@@ -27,9 +27,11 @@
 //            segment route measured as fast or faster: its idle lanes
 //            re-read cached vectors, which costs issue slots but no HBM
 //            traffic.
-//   row      rows of 1025 to 4096 vectors: one 256-thread workgroup per row
-//            holding it in registers (up to 16 vectors per thread); the
-//            four waves' sums meet in LDS in wave order.
+//   row      rows of 1025 to 4096 sixteen-byte vectors (8192 narrower
+//            accesses): one 512- or 1024-thread workgroup per row holding
+//            it in registers (at most four 16-byte vectors or eight
+//            narrower accesses per thread); the waves' sums meet in LDS and
+//            are added as a pairwise tree in wave order.
 //   block    one 256-thread workgroup per row for wider rows; X is read
 //            twice, four vectors per thread in flight per pass.
 // scale is loaded once per thread and kept in registers as float32.  X, gate
