@@ -26,10 +26,17 @@
  *     for the last non-OK status of the calling thread is returned by
  *     skipnorm_last_error().
  *   - Outputs may not overlap inputs or each other (SN_ERR_ALIAS).
- *   - Pointers need no particular alignment: each call reads and writes in
- *     the widest of 16-, 8- and 4-byte vectors that divides a row (pixel,
- *     image plane) and every base address, else element by element, with
- *     the same results up to float32 summation order.
+ *   - Pointers need no particular alignment (beyond their element type's):
+ *     each call reads and writes in the widest of 16-, 8- and 4-byte vectors
+ *     that divides a row (pixel, image plane) and every base address, else
+ *     element by element -- except that skip_rms_norm / skip_layer_norm rows
+ *     left with element-by-element accesses read aligned 16-byte vectors
+ *     across row boundaries when input, skip, output and S share their
+ *     offset from a 16-byte boundary and gamma, beta and bias are 16-byte
+ *     aligned (reads then touch the up to 15 bytes beside a tensor's first
+ *     and last element that share their 16-byte block; nothing outside a
+ *     tensor is written) -- with the same results up to float32 summation
+ *     order.
  *   - Zero-sized leading dimensions are valid and launch nothing.  A row
  *     (hidden, span) or one SkipGroupNorm image (C*H*W) may hold at most
  *     2^30 elements.
