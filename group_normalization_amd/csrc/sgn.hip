@@ -15,7 +15,9 @@
 //   or 8 x 256 x 32 scalars): a group is contiguous in NCHW, so K workgroups
 //   (K <= 8) read it once, keep S in VGPRs, exchange their slices' moments
 //   with a bounded wait (see sgn_cluster_kernel) and write S and Y.  One
-//   launch, exactly the operator's own traffic.
+//   launch, exactly the operator's own traffic.  Groups off the 16-byte
+//   grid (odd H*W, or data bases sharing an offset from it) read aligned
+//   16-byte vectors across group boundaries (sgn_cluster_phase_kernel).
 //
 // channel-block cluster (NHWC, in sgn_nhwc.hip; pixels a whole number of
 //   16-, 8- or 4-byte vectors no wider than a group, images of up to
@@ -94,6 +96,7 @@ struct ClusterArgs {
     FastDiv div;   // by H*W
     bool skip_bcast, silu;
     float eps;
+    int phase;     // phased route: elements from the 16-byte boundary below the data bases
 };
 
 
@@ -254,6 +257,222 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
                 out.v[e] = from_f32<T>(y);
             }
             store_vec_stream<T, E>(a.Y, base + j, out);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ group-cluster, phased
+// NCHW groups whose span does not start on the 16-byte grid (H*W not a
+// whole number of 16-byte vectors; X, skip, S and Y sharing a base off the
+// grid): the same cluster, but each workgroup reads the aligned 16-byte
+// vectors that cover its part of the group's span [s0, s0 + cpg*H*W)
+// (counted from the boundary at or below the data bases; the span's first
+// and last vector may hold the neighbouring groups' elements, read and
+// masked), writes whole vectors where they lie inside the span and the two
+// boundary vectors element by element.  With H*W >= E a vector holds at most
+// two channels; their constants (bias, broadcast skip, gamma, beta) come
+// from a per-workgroup LDS table of the group's channels.  The slices, the
+// exchange and the recomputation of late slices are those of
+// sgn_cluster_kernel, with each slice's element count in closed form.
+constexpr int kPhaseMaxCpg = 512;  // channels per group the LDS table holds
+constexpr int kPhaseMaxR = 8;      // vectors per thread
+
+template <typename T, typename M, int E, int R, bool BCAST>
+__global__ void __launch_bounds__(kClusterThreads)
+sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
+    using V = Vec<T, E>;
+    __shared__ Moments sh[kClusterThreads / 64];
+    __shared__ Moments slice_m[kClusterMaxK];
+    __shared__ int late[kClusterMaxK];
+    __shared__ float4 cst[kPhaseMaxCpg];  // per channel: bias, broadcast skip, gamma, beta
+    const int t = threadIdx.x;
+    const int ng = blockIdx.x / a.K, k = blockIdx.x % a.K;
+    const int n = ng / a.groups, g = ng % a.groups;
+    const int64_t span = int64_t(a.cpg) * a.HW;
+    const int64_t s0 = (int64_t(n) * a.C + int64_t(g) * a.cpg) * a.HW + a.phase;
+    const int64_t v0 = s0 / E;                                     // the span's first vector
+    const int p = int(s0 - v0 * E);                                // its first element's place
+    const uint32_t nvr = uint32_t((s0 + span + E - 1) / E - v0);   // vectors the span touches
+    const T* xa = a.X - a.phase;
+    const T* ka = a.skip - a.phase;  // full skip only
+    T* sa = a.S ? a.S - a.phase : nullptr;
+    T* ya = a.Y - a.phase;
+    const bool has_bias = a.bias != nullptr;
+    const int64_t HW = a.HW;
+
+    auto slice_begin = [&](int s) { return uint32_t(s) * a.vps; };
+    auto slice_end = [&](int s) {
+        const uint32_t e = uint32_t(s + 1) * a.vps;
+        return e < nvr ? e : nvr;
+    };
+    auto slice_count = [&](int s) {
+        const int64_t lo = int64_t(slice_begin(s)) * E - p, hi = int64_t(slice_end(s)) * E - p;
+        const int64_t l = lo > 0 ? lo : 0, h = hi < span ? hi : span;
+        return h > l ? float(h - l) : 0.0f;
+    };
+    auto vec_of = [&](int s, int r) { return slice_begin(s) + uint32_t(t) + uint32_t(r) * kClusterThreads; };
+    // Span position of vector i's element 0 (negative before the span).
+    auto first_pos = [&](uint32_t i) { return int64_t(i) * E - p; };
+    // The two channels (within the group) a vector can hold, and the first
+    // span position of the second.
+    struct Chan {
+        int lo, hi;
+        int64_t edge;
+    };
+    auto chans = [&](uint32_t i) {
+        const int64_t j0 = first_pos(i);
+        const uint32_t c = fastdiv(uint32_t(j0 > 0 ? j0 : 0), a.div);
+        Chan ch;
+        ch.lo = c < uint32_t(a.cpg) ? int(c) : a.cpg - 1;
+        ch.hi = ch.lo + 1 < a.cpg ? ch.lo + 1 : ch.lo;
+        ch.edge = int64_t(c + 1) * HW;
+        return ch;
+    };
+    auto form = [&](const V& x, const V& kv, uint32_t i, V& s) {
+        const Chan ch = chans(i);
+        const float4 c0 = cst[ch.lo], c1 = cst[ch.hi];
+        const int64_t j0 = first_pos(i);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool up = j0 + e >= ch.edge;
+            const float bb = up ? c1.x : c0.x;
+            const float kk = BCAST ? (up ? c1.y : c0.y) : to_f32(kv.v[e]);
+            residual_sum<T>(to_f32(x.v[e]), kk, has_bias, bb, s.v[e]);
+        }
+    };
+    auto accumulate = [&](ShiftedSums& acc, float& cnt, const V& s, uint32_t i) {
+        const int64_t j0 = first_pos(i);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (j0 + e >= 0 && j0 + e < span) {
+                acc.add(to_f32(s.v[e]), cnt == 0.0f);
+                cnt += 1.0f;
+            }
+    };
+    // Vector i of the span into `dst` (aligned base): whole when it lies
+    // inside the span, else the span's elements one by one.
+    auto put = [&](T* dst, uint32_t i, const V& v) {
+        const int64_t j0 = first_pos(i);
+        if (j0 >= 0 && j0 + E <= span) {
+            store_vec_stream<T, E>(dst, v0 + i, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (j0 + e >= 0 && j0 + e < span) dst[(v0 + i) * E + e] = v.v[e];
+        }
+    };
+
+    // ---- own slice: data loads first, then the group's channel table.
+    const uint32_t end = slice_end(k);
+    auto clamp = [&](uint32_t j) { return j < end ? j : (slice_begin(k) < nvr ? slice_begin(k) : nvr - 1); };
+    V sv[R], xs[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t j = clamp(vec_of(k, r));
+        xs[r] = load_vec_stream<T, E>(xa, v0 + j);
+        if constexpr (!BCAST) sv[r] = load_vec_stream<T, E>(ka, v0 + j);
+    }
+    for (int c = t; c < a.cpg; c += kClusterThreads) {
+        const int ch = g * a.cpg + c;
+        cst[c] = make_float4(has_bias ? to_f32(a.bias[ch]) : 0.0f,
+                             BCAST ? to_f32(a.skip[int64_t(n) * a.C + ch]) : 0.0f, to_f32(a.gamma[ch]),
+                             to_f32(a.beta[ch]));
+    }
+    __syncthreads();
+    ShiftedSums acc;
+    float cnt = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t j = vec_of(k, r);
+        if (j < end) {
+            form(xs[r], sv[r], j, sv[r]);
+            accumulate(acc, cnt, sv[r], j);
+        }
+    }
+    const Moments mine = block_merge_rcp(acc.moments(cnt), sh);
+
+    // ---- exchange with the other K-1 slices of the group (as sgn_cluster_kernel)
+    Moments tot = mine;
+    if (a.K > 1) {
+        uint64_t* slots = reinterpret_cast<uint64_t*>(a.part) + 2 * (int64_t(ng) * a.K);
+        if (t == 0) publish_moments(&slots[2 * k], mine, a.tags);
+        if (sa) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t j = vec_of(k, r);
+                if (j < end) put(sa, j, sv[r]);
+            }
+        }
+        if (t < a.K && t != k) {
+            const long long t0 = wall_clock64();
+            bool ok = false;
+            float mean = 0.0f, m2 = 0.0f;
+            for (;;) {
+                if (read_moments(&slots[2 * t], a.tags, &mean, &m2)) {
+                    ok = true;
+                    break;
+                }
+                if (wall_clock64() - t0 > a.timeout_ticks) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            late[t] = ok ? 0 : 1;
+            if (ok) slice_m[t] = Moments{slice_count(t), mean, m2};
+        }
+        __syncthreads();
+        tot = Moments{0.0f, 0.0f, 0.0f};
+        for (int q = 0; q < a.K; ++q) {  // uniform over the workgroup
+            Moments m;
+            if (q == k) {
+                m = mine;
+            } else if (!late[q]) {
+                m = slice_m[q];
+            } else {
+                // Slice q was not published in time: recompute its moments
+                // exactly as its own workgroup does.
+                const uint32_t qend = slice_end(q);
+                ShiftedSums qacc;
+                float qcnt = 0.0f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t j = vec_of(q, r);
+                    if (j < qend) {
+                        V x = load_vec<T, E>(xa, v0 + j), kv, sq;
+                        if constexpr (!BCAST) kv = load_vec<T, E>(ka, v0 + j);
+                        form(x, kv, j, sq);
+                        accumulate(qacc, qcnt, sq, j);
+                    }
+                }
+                m = block_merge_rcp(qacc.moments(qcnt), sh);
+            }
+            tot = merge_rcp(tot, m);
+        }
+    } else if (sa) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t j = vec_of(k, r);
+            if (j < end) put(sa, j, sv[r]);
+        }
+    }
+
+    // ---- normalize the held S
+    const float2 st = finalize(tot, a.eps);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t j = vec_of(k, r);
+        if (j < end) {
+            const Chan ch = chans(j);
+            const float4 c0 = cst[ch.lo], c1 = cst[ch.hi];
+            const float scl0 = st.y * c0.z, scl1 = st.y * c1.z;
+            const int64_t j0 = first_pos(j);
+            V out;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool up = j0 + e >= ch.edge;
+                float y = fmaf_(to_f32(sv[r].v[e]) - st.x, up ? scl1 : scl0, up ? c1.w : c0.w);
+                if (a.silu) y = silu_f32(y);
+                out.v[e] = from_f32<T>(y);
+            }
+            put(ya, j, out);
         }
     }
 }
@@ -764,6 +983,25 @@ hipError_t launch_cluster_r(const ClusterArgs<T, M>& ca, int64_t blocks, hipStre
 }
 
 template <typename T, typename M, int E>
+hipError_t launch_cluster_phase(const ClusterArgs<T, M>& ca, int64_t blocks, hipStream_t stream) {
+    const uint32_t r = (ca.vps + kClusterThreads - 1) / kClusterThreads;
+    auto go = [&](auto rt) {
+        constexpr int R = decltype(rt)::value;
+        if (ca.skip_bcast)
+            hipLaunchKernelGGL((sgn_cluster_phase_kernel<T, M, E, R, true>), dim3(unsigned(blocks)),
+                               dim3(kClusterThreads), 0, stream, ca);
+        else
+            hipLaunchKernelGGL((sgn_cluster_phase_kernel<T, M, E, R, false>), dim3(unsigned(blocks)),
+                               dim3(kClusterThreads), 0, stream, ca);
+        return hipGetLastError();
+    };
+    if (r <= 1) return go(std::integral_constant<int, 1>());
+    if (r <= 2) return go(std::integral_constant<int, 2>());
+    if (r <= 4) return go(std::integral_constant<int, 4>());
+    return go(std::integral_constant<int, kPhaseMaxR>());
+}
+
+template <typename T, typename M, int E>
 hipError_t launch_cluster(const ClusterArgs<T, M>& ca, int64_t blocks, hipStream_t stream) {
     const uint32_t r = (ca.vps + kClusterThreads - 1) / kClusterThreads;
     if constexpr (E > 1) {
@@ -783,8 +1021,8 @@ hipError_t launch_cluster(const ClusterArgs<T, M>& ca, int64_t blocks, hipStream
 
 // Workgroups per (n, group) of the cluster route for a group of Kv vectors
 // (0: the group is too large for it).
-int cluster_k(int64_t Kv, int64_t NG, int max_r) {
-    if (Kv <= int64_t(kClusterThreads) * kSingleSliceMaxR) return 1;  // one slice, no exchange
+int cluster_k(int64_t Kv, int64_t NG, int max_r, int single_max_r = kSingleSliceMaxR) {
+    if (Kv <= int64_t(kClusterThreads) * single_max_r) return 1;  // one slice, no exchange
     const int64_t cap = int64_t(kClusterThreads) * max_r;
     const int64_t k_fit = (Kv + cap - 1) / cap;
     if (k_fit > kClusterMaxK) return 0;
@@ -826,6 +1064,18 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
         if (nhwc_e > 1 && !nhwc_split_channel_blocks(a.C, cpg, nhwc_e, &ncb)) nhwc_e = 1;
     }
     const bool nchw_vec = vec_allowed && !a.channels_last && HW % EV == 0 && data_ok;
+    // NCHW groups off the 16-byte grid (odd H*W, or data bases sharing an
+    // offset from it): the phased cluster reads aligned 16-byte vectors
+    // across the group boundaries, when H*W holds a vector, the group's
+    // channel table fits, and X, skip, S and Y share their offset.
+    bool nchw_phase = false;
+    int phase = 0;
+    if (vec_allowed && !a.channels_last && !nchw_vec && HW >= EV && cpg <= kPhaseMaxCpg) {
+        const uintptr_t ph = reinterpret_cast<uintptr_t>(a.X) % 16;
+        auto same = [&](const void* q) { return !q || reinterpret_cast<uintptr_t>(q) % 16 == ph; };
+        nchw_phase = ph % sizeof(T) == 0 && same(a.Y) && same(a.S) && (a.skip_broadcast || same(a.skip));
+        phase = int(ph / sizeof(T));
+    }
 
     // ---- group-cluster route (NCHW)
     const int64_t B_ws = sgn_partials_per_group(a.dtype, a.N, a.C, a.H, a.W, a.groups, a.channels_last);
@@ -834,8 +1084,12 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
     const bool cluster_route = !a.channels_last && want != Route::Split && want != Route::Block;
     if (cluster_route) {
         const int E = nchw_vec ? EV : 1;
-        const int64_t Kv = K / E;
-        const int Kc = cluster_k(Kv, NG, nchw_vec ? kClusterMaxVec : kClusterMaxScalar);
+        const int64_t Kv = nchw_phase ? K / EV + 2 : K / E;  // phased: vectors a group's span can touch
+        // The phased route keeps one slice only up to two vectors per thread
+        // (2 x 1280 x 15 x 15 float16, 1127 vectors a group: one slice
+        // 11.5 us, eight 10.4 us).
+        const int Kc = nchw_phase ? cluster_k(Kv, NG, kPhaseMaxR, 2)
+                                  : cluster_k(Kv, NG, nchw_vec ? kClusterMaxVec : kClusterMaxScalar);
         if (Kc > 0) {
             ClusterArgs<T, M> ca;
             ca.X = X;
@@ -862,6 +1116,11 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
             ca.skip_bcast = a.skip_broadcast;
             ca.silu = silu;
             ca.eps = a.epsilon;
+            ca.phase = phase;
+            if (nchw_phase) {
+                *route = "sgn.cluster.nchw.phase";
+                return launch_cluster_phase<T, M, EV>(ca, NG * Kc, stream);
+            }
             if (nchw_vec) {
                 *route = "sgn.cluster.nchw.vec16";
                 return launch_cluster<T, M, EV>(ca, NG * Kc, stream);

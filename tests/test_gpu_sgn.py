@@ -166,9 +166,10 @@ LIMIT_CASES = [
     (1, 33, 64, 64, F32, 1, False, "sgn.split.nchw.vec16"),    # 33792 vectors
     (1, 64, 64, 64, F16, 2, True, "sgn.cluster.nchw.vec16"),   # 16384 vectors of halves
     (2, 16, 32, 32, F16, 1, True, "sgn.cluster.nchw.vec16"),   # 2048 vectors, 8 small slices
-    (1, 64, 31, 33, F32, 1, False, "sgn.cluster.nchw.scalar"), # 65472 elements
+    (1, 64, 31, 33, F32, 1, False, "sgn.cluster.nchw.phase"),  # odd H*W: 16370 phased vectors, 8 slices
     (1, 65, 31, 33, F32, 1, False, "sgn.split.nchw.scalar"),   # 66495 elements
-    (3, 6, 7, 7, F16, 3, True, "sgn.cluster.nchw.scalar"),     # 98 elements in 8 slices
+    (3, 6, 7, 7, F16, 3, True, "sgn.cluster.nchw.phase"),      # 7 x 7: phased, one slice
+    (1, 600, 1, 3, F32, 1, False, "sgn.cluster.nchw.scalar"),  # H*W = 3 < one vector: scalars, 8 slices
     (1, 2, 1, 3, F32, 2, False, "sgn.cluster.nchw.scalar"),    # 3 elements: 3 slices of 1
 ]
 
@@ -262,7 +263,9 @@ def test_broadcast_equals_expanded(cl):
 FALLBACK_CASES = [
     (2, 64, 32, 32, F32, F16, 0, True, False, 8, 0),
     (1, 32, 48, 48, F16, F32, 0, False, True, 4, 1),
-    (2, 12, 23, 23, F32, F32, 0, True, True, 3, 1),   # scalar accesses
+    (2, 12, 45, 45, F32, F32, 0, True, True, 3, 1),   # odd H*W: phased vectors, 8 slices
+    (1, 64, 31, 31, F16, F32, 0, False, True, 2, 1),  # float16 phased, 8 slices
+    (1, 1024, 1, 3, F32, F16, 0, False, True, 1, 0),  # H*W = 3: scalar accesses, 8 slices
     (2, 320, 24, 24, F16, F32, 1, False, True, 32, 1),  # NHWC, 11 slices of 51 pixel lanes
     (2, 72, 16, 16, F16, F16, 1, True, False, 8, 0),    # NHWC, 2 groups per wave, 9 slices
     (1, 48, 33, 31, F32, F32, 1, False, True, 4, 1),    # NHWC float32, 32 slices, ragged last
@@ -402,3 +405,53 @@ def test_non_finite_values_stay_in_their_group(cl, route):
     nan_groups = {(n, g) for n in range(N) for g in range(groups)
                   if np.isnan(y[n, g * 8:(g + 1) * 8]).all()}
     assert nan_groups == {(0, 2), (1, 5)}, nan_groups
+
+
+@pytest.mark.parametrize("dt,N,C,H,W,groups,offset,bc", [
+    (F16, 2, 64, 8, 8, 8, 1, False),     # whole vectors per plane, bases off the grid
+    (F16, 2, 40, 7, 7, 4, 0, True),      # 7 x 7 planes
+    (F16, 1, 64, 31, 31, 2, 5, False),   # several slices
+    (F32, 2, 48, 5, 5, 6, 3, True),
+    (F32, 1, 32, 33, 31, 4, 2, False),
+])
+def test_nchw_phased_groups(dt, N, C, H, W, groups, offset, bc):
+    """NCHW groups off the 16-byte grid, through the C ABI: X, skip, Y and S
+    all `offset` elements past a 16-byte boundary (or planes that are not a
+    whole number of 16-byte vectors) take the phased cluster route, which
+    reads aligned vectors across group boundaries.  Results match the oracle
+    and nothing outside Y and S is written."""
+    from group_normalization_amd._lib import lib, check as ck
+    w = workloads.sgn("t", N, C, H, W, dt, F32, channels_last=False, broadcast_skip=bc, bias=True,
+                      groups=groups, activation=1, epsilon=1e-5)
+    x = workloads.generate(w, seed=C + H + offset)
+    tdt = torch.float16 if dt == F16 else torch.float32
+    n, pad = N * C * H * W, 64
+
+    def arena():
+        return torch.full((n + 2 * pad,), -7.0, dtype=tdt, device="cuda")
+
+    bufs = {k: arena() for k in ("X", "skip", "Y", "S")}
+    views = {k: b[pad + offset: pad + offset + n] for k, b in bufs.items()}
+    views["X"].copy_(to_dev(x["X"]).ravel())
+    skip = to_dev(x["skip"]) if bc else views["skip"]
+    if not bc:
+        views["skip"].copy_(to_dev(x["skip"]).ravel())
+    d = {k: to_dev(x[k]) for k in ("gamma", "beta", "bias")}
+    ws = torch.empty(gn.skip_group_norm_workspace_size(views["X"].view(N, C, H, W), groups, 0),
+                     dtype=torch.uint8, device="cuda")
+    code = 1 if dt == F16 else 0
+    for _ in range(2):
+        ck(lib().skip_group_norm(code, 0, N, C, H, W, views["X"].data_ptr(), d["gamma"].data_ptr(),
+                                 d["beta"].data_ptr(), skip.data_ptr(), 1 if bc else 0, d["bias"].data_ptr(),
+                                 1e-5, groups, 0, 1, views["Y"].data_ptr(), views["S"].data_ptr(),
+                                 ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream))
+        assert gn.last_route() == "sgn.cluster.nchw.phase"
+        torch.cuda.synchronize()
+        ref_y, ref_s = oracle.skip_group_norm(x["X"], x["gamma"], x["beta"], x["skip"], x["bias"],
+                                              groups=groups, activation=1, epsilon=1e-5, channels_last=0,
+                                              want_sum=True)
+        assert_close(to_host(views["Y"]).reshape(ref_y.shape), ref_y, "Y")
+        assert_bitwise(to_host(views["S"]).reshape(ref_s.shape), ref_s, "S")
+        for k in ("Y", "S"):
+            b = to_host(bufs[k])
+            assert np.all(b[:pad + offset] == -7.0) and np.all(b[pad + offset + n:] == -7.0), k
