@@ -33,10 +33,12 @@
  *     left with element-by-element accesses read aligned 16-byte vectors
  *     across row boundaries when input, skip, output and S share their
  *     offset from a 16-byte boundary and gamma, beta and bias are 16-byte
- *     aligned (reads then touch the up to 15 bytes beside a tensor's first
- *     and last element that share their 16-byte block; nothing outside a
- *     tensor is written) -- with the same results up to float32 summation
- *     order.
+ *     aligned, and skip_group_norm NCHW groups likewise across group
+ *     boundaries when X, skip, Y and S share their offset and H*W holds a
+ *     16-byte vector (reads then touch the up to 15 bytes beside a tensor's
+ *     first and last element that share their 16-byte block; nothing
+ *     outside a tensor is written) -- with the same results up to float32
+ *     summation order.
  *   - Zero-sized leading dimensions are valid and launch nothing.  A row
  *     (hidden, span) or one SkipGroupNorm image (C*H*W) may hold at most
  *     2^30 elements.
