@@ -24,14 +24,22 @@ def make_inputs():
     t = {
         "x": rn(24, 4096), "k": rn(24, 4096), "gamma": rn(4096), "beta": rn(4096),
         "X": rn(64, 4 * 128), "gate": rn(64, 4 * 128), "scale": rn(128),
-        "Xh": rn(2, 16, 16, 320), "kh": rn(2, 16, 16, 320), "bh": rn(320),
+        # SkipGroupNorm shapes whose groups span several workgroups, so that
+        # every replay exchanges moments: NHWC 32 slices per channel block,
+        # NCHW 16-byte vectors, and NCHW groups off the 16-byte grid (31 x 31
+        # planes, the phased route).
+        "Xh": rn(2, 64, 64, 320), "kh": rn(2, 64, 64, 320), "bh": rn(320),
         "gh": rn(320, dtype=torch.float32), "eh": rn(320, dtype=torch.float32),
-        "Xc": rn(2, 640, 8, 8, dtype=torch.float32), "kc": rn(2, 640, dtype=torch.float32),
+        "Xc": rn(2, 640, 32, 32, dtype=torch.float32), "kc": rn(2, 640, dtype=torch.float32),
         "gc": rn(640), "ec": rn(640),
+        "Xp": rn(2, 640, 31, 31), "kp": rn(2, 640, 31, 31), "bp": rn(640),
+        "gp": rn(640, dtype=torch.float32), "ep": rn(640, dtype=torch.float32),
     }
     t["ws_h"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xh"], 32, 1), dtype=torch.uint8,
                             device="cuda")
     t["ws_c"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xc"], 32, 0), dtype=torch.uint8,
+                            device="cuda")
+    t["ws_p"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xp"], 32, 0), dtype=torch.uint8,
                             device="cuda")
     return t
 
@@ -47,14 +55,17 @@ def run(t):
     e = gn.skip_group_norm(t["Xc"], t["gc"], t["ec"], t["kc"], None, groups=32, activation=0,
                            channels_last=0, workspace=t["ws_c"])
     route_c = gn.last_route()
+    f = gn.skip_group_norm(t["Xp"], t["gp"], t["ep"], t["kp"], t["bp"], groups=32, activation=1,
+                           channels_last=0, want_sum=True, workspace=t["ws_p"])
+    route_p = gn.last_route()
     outs = [a.output, a.inv_std_var, a.input_skip_bias_sum, b.output, b.mean, b.inv_std_var, c,
-            d.Y, d.S, e.Y]
-    return outs, (route_h, route_c)
+            d.Y, d.S, e.Y, f.Y, f.S]
+    return outs, (route_h, route_c, route_p)
 
 
 def refill(t, seed):
     g = torch.Generator(device="cuda").manual_seed(seed)
-    for name in ("x", "k", "X", "gate", "Xh", "kh", "Xc", "kc"):
+    for name in ("x", "k", "X", "gate", "Xh", "kh", "Xc", "kc", "Xp", "kp"):
         v = t[name]
         v.copy_(torch.randn(v.shape, generator=g, device="cuda", dtype=torch.float32).to(v.dtype))
 
@@ -71,11 +82,11 @@ def test_graph_replays_match_eager():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         captured, routes = run(t)
-    assert routes[0].startswith("sgn.cluster.nhwc") and routes[1].startswith("sgn.cluster.nchw"), routes
+    assert routes == ("sgn.cluster.nhwc.vec16", "sgn.cluster.nchw.vec16", "sgn.cluster.nchw.phase"), routes
     torch.cuda.synchronize()
 
     names = ["ssln output", "ssln inv_std_var", "ssln S", "sln output", "sln mean", "sln inv_std_var",
-             "gated Y", "sgn nhwc Y", "sgn nhwc S", "sgn nchw Y"]
+             "gated Y", "sgn nhwc Y", "sgn nhwc S", "sgn nchw Y", "sgn nchw phased Y", "sgn nchw phased S"]
     for rep in range(4):
         refill(t, seed=100 + rep)
         graph.replay()
