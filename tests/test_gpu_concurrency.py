@@ -27,11 +27,17 @@ def make_inputs(seed):
          "X": rn(256, 512), "gate": rn(256, 512), "scale": rn(128),
          "Xh": rn(2, 32, 32, 320), "kh": rn(2, 32, 32, 320), "bh": rn(320),
          "gh": rn(320, dtype=torch.float32), "eh": rn(320, dtype=torch.float32),
-         "Xc": rn(2, 640, 16, 16, dtype=torch.float32), "kc": rn(2, 640, dtype=torch.float32),
-         "gc": rn(640), "ec": rn(640)}
+         # NCHW groups spread over several workgroups (moments exchanged):
+         # 16-byte vectors, and 31 x 31 planes off the 16-byte grid (phased).
+         "Xc": rn(2, 640, 32, 32, dtype=torch.float32), "kc": rn(2, 640, dtype=torch.float32),
+         "gc": rn(640), "ec": rn(640),
+         "Xp": rn(2, 320, 31, 31), "kp": rn(2, 320, 31, 31), "bp": rn(320),
+         "gp": rn(320, dtype=torch.float32), "ep": rn(320, dtype=torch.float32)}
     t["ws_h"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xh"], 32, 1), dtype=torch.uint8,
                             device="cuda")
     t["ws_c"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xc"], 32, 0), dtype=torch.uint8,
+                            device="cuda")
+    t["ws_p"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xp"], 32, 0), dtype=torch.uint8,
                             device="cuda")
     return t
 
@@ -44,7 +50,9 @@ def run(t):
                            channels_last=1, want_sum=True, workspace=t["ws_h"])
     e = gn.skip_group_norm(t["Xc"], t["gc"], t["ec"], t["kc"], None, groups=32, activation=0,
                            channels_last=0, workspace=t["ws_c"])
-    return [a.output, a.input_skip_bias_sum, b.output, b.mean, c, d.Y, d.S, e.Y]
+    f = gn.skip_group_norm(t["Xp"], t["gp"], t["ep"], t["kp"], t["bp"], groups=32, activation=1,
+                           channels_last=0, want_sum=True, workspace=t["ws_p"])
+    return [a.output, a.input_skip_bias_sum, b.output, b.mean, c, d.Y, d.S, e.Y, f.Y, f.S]
 
 
 def host(outs):
