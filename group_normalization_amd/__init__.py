@@ -226,9 +226,10 @@ def skip_group_norm(X: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, sk
 
 @contextlib.contextmanager
 def force_route(route: str):
-    """Force "auto", "scalar", "vector", "block" or "split" routes inside the
-    ``with`` block (codes 0-4 of skipnorm_force_route in include/skipnorm.h)."""
-    code = {"auto": 0, "scalar": 1, "vector": 2, "block": 3, "split": 4}[route]
+    """Force "auto", "scalar", "vector", "block", "split" or "flat" routes
+    inside the ``with`` block (codes 0-5 of skipnorm_force_route in
+    include/skipnorm.h)."""
+    code = {"auto": 0, "scalar": 1, "vector": 2, "block": 3, "split": 4, "flat": 5}[route]
     prev = lib().skipnorm_force_route(code)
     try:
         yield

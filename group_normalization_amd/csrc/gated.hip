@@ -27,6 +27,14 @@
 //            segment route measured as fast or faster: its idle lanes
 //            re-read cached vectors, which costs issue slots but no HBM
 //            traffic.
+//   flat     rows of at most 1024 elements read with accesses narrower than
+//            16 bytes (odd spans, narrow rows), where X, gate and Y share
+//            their offset from the 16-byte grid and the tile is at least 3/4
+//            full: the rows are read as one stream of aligned 16-byte
+//            vectors, each wave taking whole rows packed back to back; the
+//            squares meet in LDS, each row is summed by a power-of-two group
+//            of lanes, and every element takes its row's r and its column's
+//            scale from LDS (where exactly: flat_preferred below).
 //   row      rows of 1025 to 4096 sixteen-byte vectors (8192 narrower
 //            accesses): one 512- or 1024-thread workgroup per row holding
 //            it in registers (at most four 16-byte vectors or eight
@@ -34,8 +42,8 @@
 //            are added as a pairwise tree in wave order.
 //   block    one 256-thread workgroup per row for wider rows; X is read
 //            twice, four vectors per thread in flight per pass.
-// scale is loaded once per thread and kept in registers as float32.  X, gate
-// and Y are touched once and move with nontemporal loads and stores.
+// scale is loaded once per thread and kept in registers as float32 (flat: an
+// LDS table per workgroup).  X, gate and Y are touched once and move with nontemporal loads and stores.
 #include "device_common.h"
 #include "skipnorm_internal.h"
 
@@ -205,6 +213,132 @@ gated_tile_kernel(const T* __restrict__ X, const T* __restrict__ scale,
             out.v[e] = from_f32<T>(x * r * to_f32(sv.v[e]) * silu_f32(g));
         }
         if (j < cnt) store_vec_stream<T, E>(Y, base + j, out);
+    }
+}
+
+// Flat route: the rows are one stream of elements.  Wave w takes the rt
+// whole rows from r0 = w * rt on, elements [r0 * C, (r0 + rt) * C) (plus the
+// offset `phase` of the data bases from the 16-byte grid, which X, gate and
+// Y share), and reads the aligned 16-byte vectors that cover them; the first
+// and last may hold a neighbouring wave's elements, which are read and left
+// unused (never outside the 16-byte chunks that hold the tensors' own
+// elements), and they are written element by element, the rest whole.  The
+// squares go to LDS element by element; each row is summed by a power-of-two
+// group of lanes (lane k of the group adds elements k, k + lpr, ... in
+// order, then a butterfly over the group), and its r overwrites its first
+// square.  Each element then takes r from its row and scale from an LDS
+// table of C float32 values by its column.  NARROW (C < elements per
+// vector): a vector spans several rows, so every element finds its own row;
+// otherwise a vector spans at most two and the row changes once.
+constexpr int kFlatMaxSpan = 1024;
+
+template <typename T, int VPT, bool NARROW>
+__global__ void __launch_bounds__(256)
+gated_flat_kernel(const T* __restrict__ X, const T* __restrict__ scale,
+                  const T* __restrict__ gate, T* __restrict__ Y, int64_t rows, int C, int rt,
+                  int lpr_log, int phase, FastDiv cdiv, float span_f, float eps) {
+    constexpr int E = VecWidth<T>::value;
+    constexpr int TE = 64 * VPT * E;  // element slots of a wave's tile
+    using V = Vec<T, E>;
+    __shared__ float sq[4][TE];
+    __shared__ float sc_tab[kFlatMaxSpan];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r0 = (int64_t(blockIdx.x) * 4 + wave) * rt;
+    const int64_t left = rows - r0;
+    const int nr = left <= 0 ? 0 : (left < rt ? int(left) : rt);
+    // A wave past the last row loads the last row (and discards it), so that
+    // every wave reaches the barrier below with nothing out of bounds.
+    const int64_t rl = nr > 0 ? r0 : rows - 1;
+    const int span = (nr > 0 ? nr : 1) * C;
+    const int64_t f0 = phase + rl * C;  // the tile's first element from the aligned base
+    const int64_t v0 = f0 / E;
+    const int off0 = int(f0 - v0 * E);
+    const int nvt = (off0 + span + E - 1) / E;  // vectors the tile touches
+    const T* xa = X - phase;
+    const T* ga = gate - phase;
+    T* ya = Y - phase;
+
+    V xs[VPT], gs[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int i = v * 64 + lane;
+        const int ic = i < nvt ? i : nvt - 1;
+        xs[v] = load_vec_stream<T, E>(xa, v0 + ic);
+        gs[v] = load_vec_stream<T, E>(ga, v0 + ic);
+    }
+    for (int c = threadIdx.x; c < C; c += 256) sc_tab[c] = to_f32(scale[c]);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int i = v * 64 + lane;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float x = to_f32(xs[v].v[e]);
+            sq[wave][i * E + e] = x * x;
+        }
+    }
+    __syncthreads();  // the scale table, and this wave's squares
+    if (nr == 0) return;
+
+    const int lpr = 1 << lpr_log;
+    const int k = lane & (lpr - 1);
+    for (int rb = 0; rb < nr; rb += 64 >> lpr_log) {
+        const int rr = rb + (lane >> lpr_log);
+        const bool has = rr < nr;
+        const int first = off0 + (has ? rr : 0) * C;
+        float acc = 0.0f;
+        if (has)
+            for (int c = k; c < C; c += lpr) acc += sq[wave][first + c];
+        for (int m = 1; m < lpr; m <<= 1) acc += __shfl_xor(acc, m, 64);
+        // The group's reads of this row are done (the butterfly used them).
+        if (has && k == 0) sq[wave][first] = inv_sqrt(acc / span_f + eps);
+    }
+    wave_lds_sync();
+
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int i = v * 64 + lane;
+        const int t0 = i * E - off0;  // the vector's first element, from the tile's first
+        float rv[E], sv[E];
+        if constexpr (NARROW) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                int t = t0 + e;
+                t = t < 0 ? 0 : (t < span ? t : span - 1);
+                const int row = int(fastdiv(uint32_t(t), cdiv));
+                rv[e] = sq[wave][off0 + row * C];
+                sv[e] = sc_tab[t - row * C];
+            }
+        } else {
+            const int tc = t0 < 0 ? 0 : (t0 < span ? t0 : span - 1);
+            const int row0 = int(fastdiv(uint32_t(tc), cdiv));
+            const int row1 = row0 + 1 < nr ? row0 + 1 : row0;
+            const float ra = sq[wave][off0 + row0 * C];
+            const float rb = sq[wave][off0 + row1 * C];
+            const int c0 = t0 - row0 * C;  // column of element 0 (negative before the tile)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int c = c0 + e;
+                const bool next = c >= C;
+                int col = next ? c - C : c;
+                col = col < 0 ? 0 : (col < C ? col : C - 1);
+                rv[e] = next ? rb : ra;
+                sv[e] = sc_tab[col];
+            }
+        }
+        V out;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float x = to_f32(xs[v].v[e]);
+            const float g = to_f32(gs[v].v[e]);
+            out.v[e] = from_f32<T>(x * rv[e] * sv[e] * silu_f32(g));
+        }
+        if (t0 >= 0 && t0 + E <= span) {
+            store_vec_stream<T, E>(ya, v0 + i, out);
+        } else if (i < nvt) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (t0 + e >= 0 && t0 + e < span) ya[(v0 + i) * E + e] = out.v[e];
+        }
     }
 }
 
@@ -491,15 +625,110 @@ hipError_t launch_tile_for(const GatedArgs& a, int nvec, const TilePlan& p, hipS
     return hipErrorInvalidValue;  // the plan only picks the widths above
 }
 
+// Flat plan for rows of C <= kFlatMaxSpan elements: rt whole rows per wave
+// such that the vectors they touch (at any offset from the grid) fit the
+// wave's 64 * VPT vector slots, in the smaller tile (VPT = 2 for float16, 4
+// for float32: 1024 element slots) unless `large` allows twice that and the
+// smaller leaves over a quarter of its slots idle while the larger fills
+// more; lpr = the largest power of two with lpr * rt <= 64 (1 beyond 64
+// rows, which the lanes then take in turns).
+struct FlatPlan {
+    int vpt, rt, lpr_log;
+    double fill;  // share of the tile's element slots that carry data
+};
+
+bool gated_flat_plan(int64_t C, int vec_elems, bool large, FlatPlan* p) {
+    if (C < 1 || C > kFlatMaxSpan) return false;
+    const int small = 16 / vec_elems;
+    p->fill = -1.0;
+    for (int vpt : {small, 2 * small}) {
+        if (vpt != small && !large) break;
+        const int64_t te = int64_t(64) * vpt * vec_elems;
+        const int64_t rt = (te - vec_elems + 1) / C;
+        if (rt < 1) continue;
+        const double fill = double(rt * C) / double(te);
+        if (p->fill >= 0.75 || fill <= p->fill) continue;
+        p->fill = fill;
+        p->vpt = vpt;
+        p->rt = int(rt);
+    }
+    if (p->fill < 0.0) return false;
+    int lpr_log = 0;
+    while ((int64_t(2) << lpr_log) * p->rt <= 64) ++lpr_log;
+    p->lpr_log = lpr_log;
+    return true;
+}
+
+// Where the automatic choice takes the flat route, for rows whose widest
+// access (E elements of T) is narrower than 16 bytes, as measured on
+// 2^27-element tensors against the segment and tile routes: tiles at least
+// 3/4 full, and element-by-element rows of two elements or more (float32:
+// from 8 elements on; the segment route's coalesced 4-byte loads win below),
+// float16 pairs unless a row is one pair, and 8-byte rows whose segment lane
+// group would be less than 3/4 full (float32: 0.6).  Float16 C = 3 to 301:
+// 4.4-5.8 TB/s against 2.1-5.3 before; float32 C = 9 to 602: 5.3-5.6 against
+// 4.3-5.2.
+template <typename T>
+bool flat_preferred(int64_t C, int E, const FlatPlan& p) {
+    if (p.fill < 0.75) return false;
+    const int64_t nvec = C / E;
+    if (E == 1) return C >= (sizeof(T) == 2 ? 2 : 8);
+    if (E * sizeof(T) == 4) return nvec >= 2;
+    int64_t lanes = 1;
+    while (lanes < nvec && lanes < 64) lanes <<= 1;
+    int64_t vpl = 1;
+    while (lanes * vpl < nvec) vpl <<= 1;
+    return double(nvec) / double(lanes * vpl) < (sizeof(T) == 2 ? 0.75 : 0.6);
+}
+
+template <typename T, int VPT>
+hipError_t launch_flat(const GatedArgs& a, const FlatPlan& p, int phase, hipStream_t stream) {
+    const int C = int(a.span);
+    const int64_t tiles = (a.rows + p.rt - 1) / p.rt;
+    const int64_t blocks = (tiles + 3) / 4;
+    const FastDiv cdiv = make_fastdiv(uint32_t(C));
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                           static_cast<const T*>(a.X), static_cast<const T*>(a.scale),
+                           static_cast<const T*>(a.gate), static_cast<T*>(a.Y), a.rows, C, p.rt,
+                           p.lpr_log, phase, cdiv, float(a.span), a.epsilon);
+        return hipGetLastError();
+    };
+    if (C < VecWidth<T>::value) return go(gated_flat_kernel<T, VPT, true>);
+    return go(gated_flat_kernel<T, VPT, false>);
+}
+
+template <typename T>
+hipError_t launch_flat_for(const GatedArgs& a, const FlatPlan& p, int phase, hipStream_t stream) {
+    constexpr int small = 16 / VecWidth<T>::value;
+    if (p.vpt == small) return launch_flat<T, small>(a, p, phase, stream);
+    return launch_flat<T, 2 * small>(a, p, phase, stream);
+}
+
 template <typename T>
 hipError_t launch_gated_t(const GatedArgs& a, Route want, hipStream_t stream, const char** route) {
     // Widest access that divides the row and every tensor's base.
     int E = widest_vector<T>(a.span, {a.X, a.scale, a.gate, a.Y});
     if (want == Route::Scalar) E = 1;
     const int64_t nvec = a.span / E;
+    // The flat route, forced or (rows read with accesses narrower than 16
+    // bytes) where it measured faster, when X, gate and Y share their offset
+    // from the 16-byte grid.
+    if (want == Route::Flat || (want == Route::Auto && E * sizeof(T) < 16)) {
+        const uintptr_t ph = reinterpret_cast<uintptr_t>(a.X) % 16;
+        FlatPlan fp;
+        if (ph % sizeof(T) == 0 && reinterpret_cast<uintptr_t>(a.gate) % 16 == ph &&
+            reinterpret_cast<uintptr_t>(a.Y) % 16 == ph &&
+            gated_flat_plan(a.span, VecWidth<T>::value, want == Route::Flat || sizeof(T) == 4, &fp) &&
+            (want == Route::Flat || flat_preferred<T>(a.span, E, fp))) {
+            *route = "gated.flat.vec16";
+            return launch_flat_for<T>(a, fp, int(ph / sizeof(T)), stream);
+        }
+    }
     if constexpr (sizeof(T) == 2) {
         TilePlan tp;
-        if (want == Route::Auto && E > 1 && gated_tile_plan(nvec, int(E * sizeof(T)), &tp)) {
+        if ((want == Route::Auto || want == Route::Flat) && E > 1 &&
+            gated_tile_plan(nvec, int(E * sizeof(T)), &tp)) {
             if (E == 4) {
                 *route = "gated.tile.vec8";
                 return launch_tile_for<T, 4>(a, int(nvec), tp, stream);

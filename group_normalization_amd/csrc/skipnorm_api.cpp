@@ -95,6 +95,11 @@ sn_status check_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
 bool mul_overflows(int64_t a, int64_t b, int64_t* out) { return __builtin_mul_overflow(a, b, out); }
 
 sn::Route current_route() { return static_cast<sn::Route>(g_force_route.load(std::memory_order_relaxed)); }
+// The flat route is GatedRMSNorm's; the other operators run it as automatic.
+sn::Route current_route_not_flat() {
+    const sn::Route r = current_route();
+    return r == sn::Route::Flat ? sn::Route::Auto : r;
+}
 
 sn_status finish_launch(hipError_t err, const char* route, const char* op) {
     if (err != hipSuccess)
@@ -154,7 +159,7 @@ sn_status row_norm(const char* op, bool center, sn_dtype T, int64_t rows, int64_
     sn::SslnArgs a{T == SN_F32 ? 0 : 1, rows, hidden, input, skip, gamma, beta, bias, epsilon,
                    output, mean, inv_std_var, input_skip_bias_sum, center};
     const char* route = "";
-    return finish_launch(sn::launch_ssln(a, current_route(), stream, &route), route, op);
+    return finish_launch(sn::launch_ssln(a, current_route_not_flat(), stream, &route), route, op);
 }
 
 }  // namespace
@@ -313,7 +318,7 @@ sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t 
         a.tag = 1;
     }
     const char* route = "";
-    return finish_launch(sn::launch_sgn(a, current_route(), stream, &route), route, "skip_group_norm");
+    return finish_launch(sn::launch_sgn(a, current_route_not_flat(), stream, &route), route, "skip_group_norm");
 }
 
 const char* skipnorm_last_error(void) { return g_error.c_str(); }
@@ -321,7 +326,7 @@ const char* skipnorm_last_error(void) { return g_error.c_str(); }
 int skipnorm_abi_version(void) { return SKIPNORM_ABI_VERSION; }
 
 int skipnorm_force_route(int route) {
-    if (route < 0 || route > 4) return g_force_route.load();
+    if (route < 0 || route > 5) return g_force_route.load();
     return g_force_route.exchange(route);
 }
 

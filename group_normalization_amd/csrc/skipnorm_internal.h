@@ -8,7 +8,7 @@
 
 namespace sn {
 
-enum class Route { Auto = 0, Scalar = 1, Vector = 2, Block = 3, Split = 4 };
+enum class Route { Auto = 0, Scalar = 1, Vector = 2, Block = 3, Split = 4, Flat = 5 };
 
 // ---------------------------------------------------------------- SSLN
 // Also the non-simplified form (center = true: the row mean is removed and

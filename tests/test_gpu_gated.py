@@ -63,6 +63,13 @@ CASES = [
     ((37, 516), 516, F16),       # 129 eight-byte vectors
     ((301, 254), 254, F16),      # 127 four-byte vectors: 2 x 64 lanes nearly full
     ((53, 129), 129, F32),       # scalars
+    # flat route (rows as one stream of 16-byte vectors): chosen automatically
+    ((5000, 3), 3, F16),         # rows narrower than a vector: 339 rows per wave
+    ((4000, 25), 25, F16),       # 40 rows per wave, lanes take rows in turns
+    ((700, 301), 301, F32),      # 3 rows per wave, 16 lanes per row
+    ((123, 602), 602, F32),      # the 2048-slot tile: 3 rows per wave
+    ((77, 9), 9, F32),           # odd float32 rows from 9 elements on
+    ((6, 1, 150), 150, F32),     # 8-byte float32 vectors filling 59 % of the segment lanes
 ]
 
 
@@ -89,7 +96,48 @@ def tile_plan(nvec, vec_bytes):
     return plan if best > nvec / (lanes * vpl) else None
 
 
+def flat_plan(C, vec_elems, large):
+    """The flat route's tile, restated: (vectors per lane, rows per wave,
+    share of the element slots filled), or None."""
+    if not 1 <= C <= 1024:
+        return None
+    small, best = 16 // vec_elems, None
+    for vpt in (small, 2 * small):
+        if vpt != small and not large:
+            break
+        te = 64 * vpt * vec_elems
+        rt = (te - vec_elems + 1) // C
+        if rt < 1:
+            continue
+        fill = rt * C / te
+        if best is not None and (best[2] >= 0.75 or fill <= best[2]):
+            continue
+        best = (vpt, rt, fill)
+    return best
+
+
+def flat_preferred(C, size, E):
+    """Whether the automatic choice takes the flat route (rows read with
+    E-element accesses narrower than 16 bytes), restated."""
+    plan = flat_plan(C, 16 // size, size == 4)
+    if plan is None or plan[2] < 0.75:
+        return False
+    nvec = C // E
+    if E == 1:
+        return C >= (2 if size == 2 else 8)
+    if E * size == 4:
+        return nvec >= 2
+    lanes = 1
+    while lanes < nvec and lanes < 64:
+        lanes *= 2
+    vpl = 1
+    while lanes * vpl < nvec:
+        vpl *= 2
+    return nvec / (lanes * vpl) < (0.75 if size == 2 else 0.6)
+
+
 def expected_route(C, dt, route="auto"):
+    """Route for tensors from to_dev (every base 16-byte aligned)."""
     size = np.dtype(dt).itemsize
     width = next((b for b in (16, 8, 4) if b > size and C * size % b == 0), size)
     if route == "scalar":
@@ -98,16 +146,20 @@ def expected_route(C, dt, route="auto"):
     name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
     if route == "block":
         return "gated.block"
+    if route == "flat" and C <= 1024:
+        return "gated.flat.vec16"
+    if route == "auto" and width < 16 and flat_preferred(C, size, E):
+        return "gated.flat.vec16"
     if C // E > (4096 if width == 16 else 8192):  # the row route's widest rows
         return "gated.block" if E == 1 else f"gated.block.{name}"
     if C // E > 1024:
         return f"gated.row.{name}"
-    if route == "auto" and size == 2 and E > 1 and tile_plan(C // E, width):
+    if route in ("auto", "flat") and size == 2 and E > 1 and tile_plan(C // E, width):
         return f"gated.tile.{name}"
     return f"gated.segment.{name}"
 
 
-@pytest.mark.parametrize("route", ["auto", "scalar", "vector", "block"])
+@pytest.mark.parametrize("route", ["auto", "scalar", "vector", "block", "flat"])
 @pytest.mark.parametrize("shape,C,dt", CASES, ids=[f"{s}-C{c}-{np.dtype(d).name}" for s, c, d in CASES])
 def test_matches_oracle(shape, C, dt, route):
     w = workloads.gated("t", shape, C, dt, epsilon=1e-5)
@@ -132,7 +184,8 @@ def test_tile_plan_examples():
 
 @pytest.mark.parametrize("C,dt", [(132, F16), (130, F16), (148, F16), (150, F16), (68 * 2 + 2, F16)])
 def test_tile_route_stays_in_bounds(C, dt):
-    """Tile route through raw pointers: guard elements on both sides of Y are
+    """Tile route through raw pointers (gate off X's 16-byte grid, so the flat
+    route does not apply): guard elements on both sides of Y are
     untouched, two runs agree bit for bit, and the rows match the oracle."""
     from group_normalization_amd._lib import lib, check as ck
     rows, pad = 211, 4096
@@ -140,6 +193,9 @@ def test_tile_route_stays_in_bounds(C, dt):
     x = workloads.generate(w, seed=C)
     d = {k: to_dev(v) for k, v in x.items()}
     tdt = torch.float16 if dt == F16 else torch.float32
+    gbuf = torch.empty(rows * C + 4, dtype=tdt, device="cuda")
+    d["gate"] = gbuf[4:].view(rows, C)  # 8 bytes off the grid X lies on: no flat route
+    d["gate"].copy_(torch.from_numpy(x["gate"]))
     arena = torch.full((rows * C + 2 * pad,), 3.0, dtype=tdt, device="cuda")
     Y = arena[pad: pad + rows * C]
     code = 1 if dt == F16 else 0
@@ -155,6 +211,65 @@ def test_tile_route_stays_in_bounds(C, dt):
     a = to_host(arena)
     assert np.all(a[:pad] == 3.0) and np.all(a[pad + rows * C:] == 3.0)
     assert_close(first.reshape(rows, C), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
+
+
+FLAT_CASES = [(c, F16) for c in (1, 2, 3, 5, 7, 10, 20, 25, 50, 100, 129, 130, 301, 602, 1002, 1017, 1023)] + \
+    [(c, F32) for c in (1, 3, 5, 10, 25, 129, 130, 301, 683, 1021, 1023)]
+
+
+@pytest.mark.parametrize("off", [0, 1, 3])
+@pytest.mark.parametrize("C,dt", FLAT_CASES, ids=[f"C{c}-{np.dtype(d).name}" for c, d in FLAT_CASES])
+def test_flat_route(C, dt, off):
+    """Flat route (forced): X, gate and Y start `off` elements past a 16-byte
+    boundary, so tiles begin and end inside vectors; guard elements on both
+    sides of Y stay untouched, two runs agree bit for bit, and the rows
+    (several tiles, a ragged last one, waves past the last row) match the
+    oracle."""
+    from group_normalization_amd._lib import lib, check as ck
+    rows, pad = 4000 // C + 7, 64
+    w = workloads.gated("t", (rows, C), C, dt, epsilon=1e-5)
+    x = workloads.generate(w, seed=C + off)
+    tdt = torch.float16 if dt == F16 else torch.float32
+
+    def placed(a, fill=None):
+        buf = torch.full((a.size + 2 * pad,), 3.0, dtype=tdt, device="cuda")
+        view = buf[pad + off: pad + off + a.size]  # buf is 256-byte aligned
+        if fill is None:
+            view.copy_(torch.from_numpy(np.ascontiguousarray(a).ravel()))
+        return buf, view
+
+    _, X = placed(x["X"])
+    _, G = placed(x["gate"])
+    arena, Y = placed(x["X"], fill=3.0)
+    S = to_dev(x["scale"])
+    code = 1 if dt == F16 else 0
+    for i in range(2):
+        with gn.force_route("flat"):
+            ck(lib().gated_rms_norm(code, rows * C, C, X.data_ptr(), S.data_ptr(), G.data_ptr(), 1e-5,
+                                    Y.data_ptr(), torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        assert gn.last_route() == "gated.flat.vec16"
+        if i == 0:
+            first = to_host(Y).copy()
+    assert_bitwise(to_host(Y), first, "second run")
+    a = to_host(arena)
+    assert np.all(a[:pad + off] == 3.0) and np.all(a[pad + off + rows * C:] == 3.0)
+    assert_close(first.reshape(rows, C), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
+
+
+def test_flat_needs_a_shared_offset():
+    """X and gate at different offsets from the 16-byte grid: not the flat
+    route, even forced, and the same values."""
+    w = workloads.gated("t", (300, 10), 10, F16, epsilon=1e-5)
+    x = workloads.generate(w, seed=5)
+    buf = torch.empty(3000 + 8, dtype=torch.float16, device="cuda")
+    X = buf[1:3001].view(300, 10)
+    X.copy_(torch.from_numpy(x["X"]))
+    for route in ("auto", "flat"):
+        with gn.force_route(route):
+            y = gn.gated_rms_norm(X, to_dev(x["scale"]), to_dev(x["gate"]), 1e-5)
+        assert gn.last_route() == "gated.segment.scalar"
+        assert_close(to_host(y), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
 
 
 @pytest.mark.parametrize("dt", [F32, F16])

@@ -86,8 +86,9 @@ def test_skip_layer_norm_beyond_2_31_elements():
     assert_bitwise(out.input_skip_bias_sum[idx].cpu().numpy(), ref[3], "S")
 
 
-@pytest.mark.parametrize("C,route", [(16384, "gated.row.vec16"), (132, "gated.tile.vec8")])
-def test_gated_wide_and_tiled_rows_beyond_2_31_elements(C, route):
+@pytest.mark.parametrize("C,route", [(16384, "gated.row.vec16"), (132, "gated.flat.vec16"),
+                                     (301, "gated.flat.vec16")])
+def test_gated_wide_and_flat_rows_beyond_2_31_elements(C, route):
     rows = TWO31 // C + 64
     X = gen((rows, C), torch.float16, 14)
     G = gen((rows, C), torch.float16, 15)
