@@ -52,6 +52,21 @@ MUTATIONS = [
      "                        y = gm * y + bt;"),
     ("group mean off by one", "const double mean = sum / count;",
      "const double mean = sum / (count + 1.0);"),
+    ("gated squares dropped", "sum_sq += x * x;", "sum_sq += x;"),
+    ("gated rms from the gate", "double x = (double)load_f32(T, X, base + j);\n            sum_sq",
+     "double x = (double)load_f32(T, gate, base + j);\n            sum_sq"),
+    ("group bias fixed channel", "bias ? load_f32(T, bias, c) : 0.0f", "bias ? load_f32(T, bias, 0) : 0.0f"),
+    ("group activation ignored", "if (activation == 1) y = silu(y);\n                        store_f64",
+     "if (activation == 2) y = silu(y);\n                        store_f64"),
+    ("group mean over one channel",
+     "for (int64_t c = g * cpg; c < (g + 1) * cpg; ++c)\n                for (int64_t h = 0; h < H; ++h)\n"
+     "                    for (int64_t w = 0; w < W; ++w)\n                        sum +=",
+     "for (int64_t c = g * cpg; c < g * cpg + 1; ++c)\n                for (int64_t h = 0; h < H; ++h)\n"
+     "                    for (int64_t w = 0; w < W; ++w)\n                        sum +="),
+    ("gamma by group", "const double gm = (double)load_f32(M, gamma, c);",
+     "const double gm = (double)load_f32(M, gamma, g);"),
+    ("skip added twice", "float sv = residual_sum(T, load_f32(T, X, i), load_f32(T, skip, k),",
+     "float sv = residual_sum(T, load_f32(T, X, i) + load_f32(T, skip, k), load_f32(T, skip, k),"),
     ("rounding ties away", "if (frac < 0.5) return fl;\n    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;",
      "if (frac < 0.5) return fl;\n    return fl + 1.0;"),
     ("overflow threshold", "if (a >= 65520.0)", "if (a >= 131072.0)"),
