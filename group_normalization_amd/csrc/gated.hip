@@ -241,7 +241,10 @@ gated_flat_kernel(const T* __restrict__ X, const T* __restrict__ scale,
     constexpr int TE = 64 * VPT * E;  // element slots of a wave's tile
     using V = Vec<T, E>;
     __shared__ float sq[4][TE];
-    __shared__ float sc_tab[kFlatMaxSpan];
+    // scale by column at sc[c]; E slots ahead of it keep the reads of
+    // elements before a tile (columns down to 1 - E) inside the array.
+    __shared__ float sc_tab[E + kFlatMaxSpan];
+    float* sc = sc_tab + E;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t r0 = (int64_t(blockIdx.x) * 4 + wave) * rt;
     const int64_t left = rows - r0;
@@ -266,7 +269,7 @@ gated_flat_kernel(const T* __restrict__ X, const T* __restrict__ scale,
         xs[v] = load_vec_stream<T, E>(xa, v0 + ic);
         gs[v] = load_vec_stream<T, E>(ga, v0 + ic);
     }
-    for (int c = threadIdx.x; c < C; c += 256) sc_tab[c] = to_f32(scale[c]);
+    for (int c = threadIdx.x; c < C; c += 256) sc[c] = to_f32(scale[c]);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int i = v * 64 + lane;
@@ -306,7 +309,7 @@ gated_flat_kernel(const T* __restrict__ X, const T* __restrict__ scale,
                 t = t < 0 ? 0 : (t < span ? t : span - 1);
                 const int row = int(fastdiv(uint32_t(t), cdiv));
                 rv[e] = sq[wave][off0 + row * C];
-                sv[e] = sc_tab[t - row * C];
+                sv[e] = sc[t - row * C];
             }
         } else {
             const int tc = t0 < 0 ? 0 : (t0 < span ? t0 : span - 1);
@@ -314,15 +317,19 @@ gated_flat_kernel(const T* __restrict__ X, const T* __restrict__ scale,
             const int row1 = row0 + 1 < nr ? row0 + 1 : row0;
             const float ra = sq[wave][off0 + row0 * C];
             const float rb = sq[wave][off0 + row1 * C];
-            const int c0 = t0 - row0 * C;  // column of element 0 (negative before the tile)
+            // Column of element 0: 1 - E to -1 for the vector that starts
+            // before the tile, 0 to C - 1 for the others with elements in it
+            // (clamped for the vectors past it, whose results are dropped).
+            int c0 = t0 - row0 * C;
+            c0 = c0 > C - 1 ? C - 1 : c0;
+            const int b = C - c0;  // elements e >= b lie in the next row
+            const float* sa = sc + c0;
+            const float* sb = sc + (c0 - C);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const int c = c0 + e;
-                const bool next = c >= C;
-                int col = next ? c - C : c;
-                col = col < 0 ? 0 : (col < C ? col : C - 1);
+                const bool next = e >= b;
                 rv[e] = next ? rb : ra;
-                sv[e] = sc_tab[col];
+                sv[e] = (next ? sb : sa)[e];
             }
         }
         V out;
