@@ -27,7 +27,8 @@
 //            segment route measured as fast or faster: its idle lanes
 //            re-read cached vectors, which costs issue slots but no HBM
 //            traffic.
-//   flat     rows of at most 1024 elements read with accesses narrower than
+//   flat     rows of at most 1016 (float16) or 1020 (float32) elements read with
+//            accesses narrower than
 //            16 bytes (odd spans, narrow rows), where X, gate and Y share
 //            their offset from the 16-byte grid and the tile is at least 3/4
 //            full: the rows are read as one stream of aligned 16-byte
@@ -229,8 +230,10 @@ gated_tile_kernel(const T* __restrict__ X, const T* __restrict__ scale,
 // square.  Each element then takes r from its row and scale from an LDS
 // table of C float32 values by its column.  NARROW (C < elements per
 // vector): a vector spans several rows, so every element finds its own row;
-// otherwise a vector spans at most two and the row changes once.
-constexpr int kFlatMaxSpan = 1024;
+// otherwise a vector spans at most two and the row changes once.  The scale
+// table holds 1024 float32 slots, E of them ahead of column 0, so rows hold
+// at most 1024 - E elements.
+constexpr int kFlatTable = 1024;
 
 template <typename T, int VPT, bool NARROW>
 __global__ void __launch_bounds__(256)
@@ -243,7 +246,7 @@ gated_flat_kernel(const T* __restrict__ X, const T* __restrict__ scale,
     __shared__ float sq[4][TE];
     // scale by column at sc[c]; E slots ahead of it keep the reads of
     // elements before a tile (columns down to 1 - E) inside the array.
-    __shared__ float sc_tab[E + kFlatMaxSpan];
+    __shared__ float sc_tab[kFlatTable];
     float* sc = sc_tab + E;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t r0 = (int64_t(blockIdx.x) * 4 + wave) * rt;
@@ -297,6 +300,9 @@ gated_flat_kernel(const T* __restrict__ X, const T* __restrict__ scale,
     }
     wave_lds_sync();
 
+    // The tile's ends fall inside 128-byte lines shared with the neighbouring
+    // tiles: the vectors there are stored through L2.
+    const LineRun run = line_run<T, E>(ya + v0 * E, nvt);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int i = v * 64 + lane;
@@ -340,7 +346,7 @@ gated_flat_kernel(const T* __restrict__ X, const T* __restrict__ scale,
             out.v[e] = from_f32<T>(x * rv[e] * sv[e] * silu_f32(g));
         }
         if (t0 >= 0 && t0 + E <= span) {
-            store_vec_stream<T, E>(ya, v0 + i, out);
+            store_vec_run<T, E>(ya + v0 * E, i, out, run);
         } else if (i < nvt) {
 #pragma unroll
             for (int e = 0; e < E; ++e)
@@ -632,7 +638,7 @@ hipError_t launch_tile_for(const GatedArgs& a, int nvec, const TilePlan& p, hipS
     return hipErrorInvalidValue;  // the plan only picks the widths above
 }
 
-// Flat plan for rows of C <= kFlatMaxSpan elements: rt whole rows per wave
+// Flat plan for rows of C <= kFlatTable - E elements: rt whole rows per wave
 // such that the vectors they touch (at any offset from the grid) fit the
 // wave's 64 * VPT vector slots, in the smaller tile (VPT = 2 for float16, 4
 // for float32: 1024 element slots) unless `large` allows twice that and the
@@ -645,7 +651,7 @@ struct FlatPlan {
 };
 
 bool gated_flat_plan(int64_t C, int vec_elems, bool large, FlatPlan* p) {
-    if (C < 1 || C > kFlatMaxSpan) return false;
+    if (C < 1 || C > kFlatTable - vec_elems) return false;
     const int small = 16 / vec_elems;
     p->fill = -1.0;
     for (int vpt : {small, 2 * small}) {

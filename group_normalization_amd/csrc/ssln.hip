@@ -66,7 +66,8 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                  const T* __restrict__ gamma, const T* __restrict__ beta,
                  const T* __restrict__ bias, T* __restrict__ output, float* __restrict__ mean,
                  float* __restrict__ inv_std_var, T* __restrict__ sum,
-                 int64_t rows, int nvec, float hidden_f, float eps, uint32_t beta_mask) {
+                 int64_t rows, int nvec, float hidden_f, float eps, uint32_t beta_mask,
+                 int lines) {
     using V = Vec<T, E>;
     constexpr int LANES = 64 * WPR;
     static_assert(WPB % WPR == 0, "whole rows per block");
@@ -81,6 +82,14 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     const int64_t row = live ? my_row : rows - 1;
     const int64_t base = row * nvec;
     const bool has_bias = bias != nullptr;
+    // lines: rows that do not all start on 128-byte lines (a uniform
+    // argument): the vectors in lines shared with the neighbouring rows are
+    // stored through L2.  Rows that fill the lanes exactly (FULL) keep plain
+    // streaming stores: their widths are whole lines, and the check alone
+    // cost 2-4 % there.
+    const bool use_lines = !FULL && lines;
+    const LineRun out_run = line_run<T, E>(output + base * E, nvec);
+    const LineRun sum_run = line_run<T, E>(sum ? sum + base * E : output, nvec);
 
     // Issue every load of the row before any arithmetic.  No load sits behind
     // a lane-dependent branch (that makes the compiler wait for each one in
@@ -120,7 +129,10 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                 if constexpr (CENTER) acc += s - shift;
                 else acc = fmaf_(s, s, acc);
             }
-            if (sum && live) store_vec_stream<T, E>(sum, base + idx, ss[v]);
+            if (sum && live) {
+                if (use_lines) store_vec_run<T, E>(sum + base * E, idx, ss[v], sum_run);
+                else store_vec_stream<T, E>(sum, base + idx, ss[v]);
+            }
         }
     }
 
@@ -188,7 +200,10 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
                 out.v[e] = from_f32<T>(to_f32(ss[v].v[e]) * r * to_f32(gv.v[e]));
             }
         }
-        if ((FULL || idx < nvec) && live) store_vec_stream<T, E>(output, base + idx, out);
+        if ((FULL || idx < nvec) && live) {
+            if (use_lines) store_vec_run<T, E>(output + base * E, idx, out, out_run);
+            else store_vec_stream<T, E>(output, base + idx, out);
+        }
     }
 }
 
@@ -626,6 +641,7 @@ hipError_t launch_wave_nv(const SslnArgs& a, int nvec, hipStream_t stream) {
     constexpr int rows_per_block = WPB / WPR;
     const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
     const float hidden_f = float(a.hidden);
+    const int lines = rows_off_lines(a.hidden * int64_t(sizeof(T)), {a.output, a.sum});
     auto args = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * WPB), 0, stream,
                            static_cast<const T*>(a.input), static_cast<const T*>(a.skip),
@@ -633,7 +649,7 @@ hipError_t launch_wave_nv(const SslnArgs& a, int nvec, hipStream_t stream) {
                            static_cast<const T*>(a.beta ? a.beta : a.gamma),
                            static_cast<const T*>(a.bias), static_cast<T*>(a.output), a.mean,
                            a.inv_std_var, static_cast<T*>(a.sum), a.rows, nvec, hidden_f, a.epsilon,
-                           a.beta ? ~0u : 0u);
+                           a.beta ? ~0u : 0u, lines);
     };
     const bool full = nvec == 64 * WPR * NV;
     if (a.center) {

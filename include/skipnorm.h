@@ -225,8 +225,9 @@ int skipnorm_abi_version(void);
  *       preconditions hold) even where a single-launch route would apply;
  *       others: automatic.
  *   5 = gated_rms_norm: the flat route (rows read as one stream of aligned
- *       16-byte vectors) wherever it applies -- rows of at most 1024
- *       elements, X, gate and Y at one offset from a 16-byte boundary --
+ *       16-byte vectors) wherever it applies -- rows of at most 1016
+ *       (float16) or 1020 (float32) elements, X, gate and Y at one offset
+ *       from a 16-byte boundary --
  *       where automatic takes it only for the row lengths it measured
  *       faster on; others: automatic.
  * Returns the previous value; an unknown value leaves the setting unchanged

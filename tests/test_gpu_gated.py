@@ -99,7 +99,7 @@ def tile_plan(nvec, vec_bytes):
 def flat_plan(C, vec_elems, large):
     """The flat route's tile, restated: (vectors per lane, rows per wave,
     share of the element slots filled), or None."""
-    if not 1 <= C <= 1024:
+    if not 1 <= C <= 1024 - vec_elems:  # the scale table's 1024 slots, E of them ahead
         return None
     small, best = 16 // vec_elems, None
     for vpt in (small, 2 * small):
@@ -146,7 +146,7 @@ def expected_route(C, dt, route="auto"):
     name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
     if route == "block":
         return "gated.block"
-    if route == "flat" and C <= 1024:
+    if route == "flat" and C <= 1024 - 16 // size:
         return "gated.flat.vec16"
     if route == "auto" and width < 16 and flat_preferred(C, size, E):
         return "gated.flat.vec16"
@@ -213,8 +213,8 @@ def test_tile_route_stays_in_bounds(C, dt):
     assert_close(first.reshape(rows, C), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
 
 
-FLAT_CASES = [(c, F16) for c in (1, 2, 3, 5, 7, 10, 20, 25, 50, 100, 129, 130, 301, 602, 1002, 1017, 1023)] + \
-    [(c, F32) for c in (1, 3, 5, 10, 25, 129, 130, 301, 683, 1021, 1023)]
+FLAT_CASES = [(c, F16) for c in (1, 2, 3, 5, 7, 10, 20, 25, 50, 100, 129, 130, 301, 602, 1002, 1015, 1016)] + \
+    [(c, F32) for c in (1, 3, 5, 10, 25, 129, 130, 301, 683, 1019, 1020)]
 
 
 @pytest.mark.parametrize("off", [0, 1, 3])
@@ -255,6 +255,18 @@ def test_flat_route(C, dt, off):
     a = to_host(arena)
     assert np.all(a[:pad + off] == 3.0) and np.all(a[pad + off + rows * C:] == 3.0)
     assert_close(first.reshape(rows, C), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
+
+
+@pytest.mark.parametrize("C,dt", [(1017, F16), (1021, F32)])
+def test_flat_longest_rows(C, dt):
+    """One element past the flat route's longest rows: forced flat, the
+    route falls back to the others with the same values."""
+    w = workloads.gated("t", (40, C), C, dt, epsilon=1e-5)
+    x = workloads.generate(w, seed=C)
+    with gn.force_route("flat"):
+        y = gn.gated_rms_norm(to_dev(x["X"]), to_dev(x["scale"]), to_dev(x["gate"]), 1e-5)
+    assert gn.last_route() == "gated.segment.scalar"
+    assert_close(to_host(y), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
 
 
 def test_flat_needs_a_shared_offset():
