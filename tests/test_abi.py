@@ -208,7 +208,10 @@ def test_sgn_empty_is_a_no_op(lib):
 def test_force_route_round_trip(lib):
     assert lib.skipnorm_force_route(1) == 0
     assert lib.skipnorm_force_route(7) == 1   # unknown: unchanged, reports current
-    assert lib.skipnorm_force_route(0) == 1
+    assert lib.skipnorm_force_route(-1) == 1
+    assert lib.skipnorm_force_route(5) == 1   # the flat GatedRMSNorm route
+    assert lib.skipnorm_force_route(6) == 5
+    assert lib.skipnorm_force_route(0) == 5
 
 
 def test_last_error_is_per_thread(lib):
