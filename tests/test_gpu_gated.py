@@ -70,6 +70,10 @@ CASES = [
     ((123, 602), 602, F32),      # the 2048-slot tile: 3 rows per wave
     ((77, 9), 9, F32),           # odd float32 rows from 9 elements on
     ((6, 1, 150), 150, F32),     # 8-byte float32 vectors filling 59 % of the segment lanes
+    # segment rows of more than 64 vectors off the 128-byte grid: the lines
+    # shared between rows are stored through L2
+    ((50, 1000), 1000, F16),     # 125 sixteen-byte vectors, rows of 2000 bytes
+    ((41, 264), 264, F32),       # 66 sixteen-byte vectors, rows of 1056 bytes
 ]
 
 
