@@ -786,9 +786,13 @@ bool launch_ssln_phase(const SslnArgs& a, hipStream_t stream, const char** route
     if (!aligned16(a.gamma) || (a.beta && !aligned16(a.beta)) || (a.bias && !aligned16(a.bias)))
         return false;
     const int64_t nmax = a.hidden / E + 2;  // vectors a row can touch
-    // Deeper than four vectors per lane its parameter funnels spill under
-    // the 1024-thread block's 128-VGPR limit.
-    if (nmax <= 48 || nmax > 1024 * NVL) return false;
+    // From 33 vectors on (f16 rows of 248 elements, f32 of 124) a wave of
+    // 16-byte vectors beats the one-wave-per-row element route (f16 hidden
+    // 255 / 301 / 375 +14 / +30 / +37 %, f32 187 +13 %); below that it leaves
+    // too many lanes idle (f16 57-127: 17-44 % slower).  Deeper than four
+    // vectors per lane its parameter funnels spill under the 1024-thread
+    // block's 128-VGPR limit.
+    if (nmax <= 32 || nmax > 1024 * NVL) return false;
     const int phase = int(ph / sizeof(T));
     const int nvg = int((a.hidden + E - 1) / E);
     const int n = int(nmax);

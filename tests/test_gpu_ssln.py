@@ -87,6 +87,11 @@ SHAPES = [
     ((200, 320), F16, True),     # 40 vectors: 64-lane groups, 4 rows per thread
     ((97, 384), F16, False),     # 48 vectors: the last lane-group width
     ((33, 392), F16, True),      # 49 vectors: one wave per row
+    # odd rows around the phased route's shortest: 33 vectors phased, 32 not
+    ((41, 255), F16, False),     # 33 sixteen-byte vectors touched: phased
+    ((41, 247), F16, True),      # 32: one wave of scalars per row
+    ((37, 127), F32, True),      # 33: phased
+    ((37, 123), F32, False),     # 32: one wave of scalars per row
 ]
 
 
@@ -99,8 +104,8 @@ def expected_route(shape, dt):
     nvec = hidden // E
     # Rows that would be read element by element (all bases here are 16-byte
     # aligned): the phased route reads whole aligned 16-byte vectors when a
-    # row needs more than 48 and at most 1024 x 4 of them.
-    if E == 1 and 48 < hidden // (16 // size) + 2 <= 1024 * 4:
+    # row needs more than 32 and at most 1024 x 4 of them.
+    if E == 1 and 32 < hidden // (16 // size) + 2 <= 1024 * 4:
         return "ssln.phase.vec16"
     if nvec <= 48:
         return f"ssln.segment.{name}"
@@ -248,6 +253,7 @@ def test_outputs_leave_neighbouring_memory_untouched():
     (F16, 4096, 1, False), (F16, 4096, 3, True), (F16, 4095, 0, False), (F16, 4097, 5, True),
     (F16, 1000, 7, False), (F16, 20003, 2, True), (F16, 32753, 6, False), (F16, 391, 4, True),
     (F32, 4097, 1, False), (F32, 6002, 1, True), (F32, 8191, 3, False), (F32, 4096, 3, True),
+    (F16, 255, 0, True), (F16, 301, 3, False), (F32, 127, 2, False), (F32, 187, 0, True),
 ])
 def test_phased_rows(dt, hidden, offset, center):
     """Rows that would be read element by element, through the C ABI:
