@@ -712,8 +712,12 @@ hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char**
     const int64_t nvec = a.hidden / E;
     // Lane groups for rows of up to 48 accesses (64 lanes for 33-48: 1.01-1.11x
     // the one-wave route on float16 rows of 264-384; from 63 accesses on the
-    // one-wave route measured faster, 1.1-1.15x at 504 and 512).
-    if (nvec <= 48) {
+    // one-wave route measured faster, 1.1-1.15x at 504 and 512), and for
+    // rows of up to 64 accesses narrower than 16 bytes, where the one-wave
+    // route holds one small access per lane (49-63 accesses: f16 elements
+    // 2.0-2.1x, f16 pairs 1.7-2.0x, f32 elements 1.3-1.6x, 8-byte accesses
+    // 0.96-1.28x).
+    if (nvec <= (E * int(sizeof(T)) < 16 ? 64 : 48)) {
         *route = kNames[3][kName];
         return launch_segment_for<T, E>(a, int(nvec), stream);
     }

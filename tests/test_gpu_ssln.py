@@ -92,6 +92,13 @@ SHAPES = [
     ((41, 247), F16, True),      # 32: one wave of scalars per row
     ((37, 127), F32, True),      # 33: phased
     ((37, 123), F32, False),     # 32: one wave of scalars per row
+    ((300, 63), F16, True),      # 63 scalars: 64-lane groups
+    ((90, 65), F32, False),      # 65 scalars: one wave per row
+    ((120, 49), F32, True),      # 49 scalars: 64-lane groups
+    ((200, 126), F16, False),    # 63 four-byte pairs: 64-lane groups
+    ((70, 252), F16, True),      # 63 eight-byte vectors: 64-lane groups
+    ((60, 130), F16, False),     # 65 four-byte pairs: one wave per row
+    ((80, 102), F32, True),      # 51 eight-byte vectors: 64-lane groups
 ]
 
 
@@ -107,7 +114,7 @@ def expected_route(shape, dt):
     # row needs more than 32 and at most 1024 x 4 of them.
     if E == 1 and 32 < hidden // (16 // size) + 2 <= 1024 * 4:
         return "ssln.phase.vec16"
-    if nvec <= 48:
+    if nvec <= (64 if width < 16 else 48):
         return f"ssln.segment.{name}"
     per_lane = 4 if E > 1 and width == 16 else 8 if E > 1 and width == 8 else 16
     if nvec <= 64 * per_lane:
