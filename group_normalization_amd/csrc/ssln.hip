@@ -711,8 +711,9 @@ hipError_t launch_ssln_width(const SslnArgs& a, hipStream_t stream, const char**
     constexpr int NVL = kNvLane<T, E>;
     const int64_t nvec = a.hidden / E;
     // Lane groups for rows of up to 48 accesses (64 lanes for 33-48: 1.01-1.11x
-    // the one-wave route on float16 rows of 264-384; from 63 accesses on the
-    // one-wave route measured faster, 1.1-1.15x at 504 and 512), and for
+    // the one-wave route on float16 rows of 264-384; from 49 sixteen-byte
+    // accesses on the one-wave route measured faster, 1.09-1.16x on float16
+    // rows of 392-512), and for
     // rows of up to 64 accesses narrower than 16 bytes, where the one-wave
     // route holds one small access per lane (49-63 accesses: f16 elements
     // 2.0-2.1x, f16 pairs 1.7-2.0x, f32 elements 1.3-1.6x, 8-byte accesses
