@@ -23,6 +23,7 @@ import torch
 from ._lib import SN_BF16, SN_F16, SN_F32, SkipNormError, check, lib
 
 __all__ = ["skip_layer_norm", "skip_rms_norm", "gated_rms_norm", "skip_group_norm", "skip_group_norm_workspace_size",
+           "skip_group_norm_noalloc",
            "SkipRmsNormOutputs", "SkipGroupNormOutputs", "SkipNormError", "force_route",
            "last_route", "exchange_timeout_us", "abi_version", "copy_"]
 
@@ -221,6 +222,42 @@ def skip_group_norm(X: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, sk
                                     bcast, _ptr(bias), float(epsilon), int(groups),
                                     1 if channels_last else 0, int(activation), _ptr(Y), _ptr(S),
                                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    return SkipGroupNormOutputs(Y, S)
+
+
+def skip_group_norm_noalloc(X: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
+                            skip: torch.Tensor, bias: Optional[torch.Tensor] = None, *, groups: int,
+                            activation: int, Y: torch.Tensor, S: Optional[torch.Tensor] = None,
+                            epsilon: float = SGN_EPSILON, channels_last: int = 1) -> SkipGroupNormOutputs:
+    """skip_group_norm for callers that cannot allocate device memory: the
+    caller passes the outputs Y (and S, if wanted), and the library keeps its
+    partial moments in its own static scratch (shapes needing more than
+    SKIPNORM_NOALLOC_SCRATCH_BYTES are rejected).  Calls that overlap in
+    time on one device race on that scratch."""
+    N, C, H, W = _sgn_dims(X, channels_last)
+    if tuple(skip.shape) == tuple(X.shape):
+        bcast = 0
+    elif tuple(skip.shape) in ((N, C), (N, 1, 1, C)):
+        bcast = 1
+    else:
+        raise ValueError(f"skip shape {tuple(skip.shape)} is neither X's shape {tuple(X.shape)} "
+                         f"nor ({N}, {C}) / ({N}, 1, 1, {C})")
+    for name, t in (("gamma", gamma), ("beta", beta), ("bias", bias)):
+        if t is not None and tuple(t.shape) != (C,):
+            raise ValueError(f"{name} must have shape ({C},), got {tuple(t.shape)}")
+    for name, t in (("Y", Y), ("S", S)):
+        if t is not None and (tuple(t.shape) != tuple(X.shape) or t.dtype != X.dtype):
+            raise ValueError(f"{name} must match X's shape and dtype")
+    _same_dtype(X, "skip_group_norm_noalloc", skip, bias)
+    if beta.dtype != gamma.dtype:
+        raise TypeError("gamma and beta must share one dtype (M)")
+    dev = _device_of(X, gamma, beta, skip, bias, Y, S)
+    T, M = _code(X, "skip_group_norm_noalloc"), _code(gamma, "skip_group_norm_noalloc gamma")
+    with torch.cuda.device(dev):
+        check(lib().skip_group_norm_noalloc(T, M, N, C, H, W, _ptr(X), _ptr(gamma), _ptr(beta),
+                                            _ptr(skip), bcast, _ptr(bias), float(epsilon),
+                                            int(groups), 1 if channels_last else 0, int(activation),
+                                            _ptr(Y), _ptr(S), _stream(dev)))
     return SkipGroupNormOutputs(Y, S)
 
 

@@ -29,6 +29,8 @@ SIGNATURES = {
                                              ctypes.POINTER(_sz)]),
     "skip_group_norm": (_ci, [_ci, _ci, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                               _f32, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "skip_group_norm_noalloc": (_ci, [_ci, _ci, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i32,
+                                      _vp, _f32, _i64, _i32, _i32, _vp, _vp, _vp]),
     "skipnorm_last_error": (ctypes.c_char_p, []),
     "skipnorm_abi_version": (_ci, []),
     "skipnorm_force_route": (_ci, [_ci]),

@@ -62,6 +62,7 @@
 // Moments: each thread uses the shifted-data sums (shift = its first value)
 // and every combination uses the pairwise update (Chan et al.) in a fixed
 // order, so results are deterministic and a constant group has variance 0.
+#include <atomic>
 #include <type_traits>
 
 #include "sgn_common.h"
@@ -1263,6 +1264,43 @@ hipError_t launch_sgn(const SgnArgs& a, Route want, hipStream_t stream, const ch
     }
     if (a.param_dtype == 0) return launch_sgn_tm<half_t, float>(a, want, stream, route);
     return launch_sgn_tm<half_t, half_t>(a, want, stream, route);
+}
+
+}  // namespace sn
+
+// ---------------------------------------------------------------------------
+// Static scratch for skip_group_norm_noalloc: the workspace of callers that
+// cannot allocate device memory (code being captured into a HIP graph, tight
+// serving loops, hosts that forbid allocation).  Each device that runs the
+// library holds its own copy of this array until the process ends.  Host
+// code never passes `scratch` itself (on the host that name is a stand-in,
+// not a device address): static_scratch() looks up the array's device
+// address once per device, with that device current, and every launch takes
+// that address.  Every call on one device shares the array; calls that
+// overlap in time on one device (different streams, or host threads without
+// ordering) race on it.  Its contents on entry never matter: each call writes
+// every partial before reading it, and the single-launch routes accept only
+// moments that carry the current call's tags (under graph capture the slots
+// are cleared by a kernel ahead of the launch, as for a caller's workspace).
+static __device__ __align__(256) unsigned char scratch[sn::kStaticScratchBytes];
+
+namespace sn {
+
+hipError_t static_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void*> by_device[kMaxDevices];
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = by_device[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // Idempotent: two threads that race here store the same address.
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        by_device[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace sn

@@ -117,12 +117,10 @@ sn_status finish_launch(hipError_t err, const char* route, const char* op) {
 constexpr int64_t kMaxRowElems = int64_t(1) << 30;   // hidden / span / image size
 constexpr int64_t kMaxElems = int64_t(1) << 46;      // whole tensor
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1; // rows; blocks of one launch
+static_assert(sn::kStaticScratchBytes == SKIPNORM_NOALLOC_SCRATCH_BYTES,
+              "the header states the static scratch size");
 
 }  // namespace
-
-extern "C" {
-
-}  // extern "C"
 
 namespace {
 
@@ -249,11 +247,17 @@ sn_status skip_group_norm_workspace_size(sn_dtype T, int64_t N, int64_t C, int64
     return ok();
 }
 
-sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t H, int64_t W,
-                          const void* X, const void* gamma, const void* beta, const void* skip,
-                          int32_t skip_broadcast, const void* bias, float epsilon, int64_t groups,
-                          int32_t channels_last, int32_t activation, void* Y, void* S,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// skip_group_norm with the caller's workspace, or (noalloc) with the
+// library's static scratch on the current device.
+sn_status group_norm(const char* op, sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t H,
+                     int64_t W, const void* X, const void* gamma, const void* beta,
+                     const void* skip, int32_t skip_broadcast, const void* bias, float epsilon,
+                     int64_t groups, int32_t channels_last, int32_t activation, void* Y, void* S,
+                     void* workspace, size_t workspace_bytes, bool noalloc, hipStream_t stream) {
     SN_TRY(check_sgn_geometry(T, N, C, H, W, groups));
     SN_TRY(check_dtype(M, "skip_group_norm M (gamma/beta)"));
     SN_TRY(check_epsilon(epsilon));
@@ -267,11 +271,21 @@ sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t 
     size_t need = 0;
     if (numel > 0)
         need = sn::sgn_workspace_bytes(T == SN_F32 ? 0 : 1, N, C, H, W, groups, channels_last != 0);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(SN_ERR_WORKSPACE, "skip_group_norm: workspace of %zu bytes required, got %zu%s",
-                    need, workspace_bytes, workspace ? "" : " (NULL)");
-    if (need > 0 && !sn::aligned16(workspace))
-        return fail(SN_ERR_WORKSPACE, "skip_group_norm: workspace must be 16-byte aligned");
+    if (noalloc) {
+        if (need > sn::kStaticScratchBytes)
+            return fail(SN_ERR_WORKSPACE,
+                        "%s: this shape needs %zu bytes of scratch; the static scratch holds %zu "
+                        "(use skip_group_norm with a workspace)",
+                        op, need, size_t(sn::kStaticScratchBytes));
+        workspace = nullptr;  // looked up after validation
+        workspace_bytes = 0;
+    } else {
+        if (need > 0 && (!workspace || workspace_bytes < need))
+            return fail(SN_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", op,
+                        need, workspace_bytes, workspace ? "" : " (NULL)");
+        if (need > 0 && !sn::aligned16(workspace))
+            return fail(SN_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", op);
+    }
 
     const size_t es = elem_size(T), ms = elem_size(M);
     const size_t tb = size_t(numel) * es;
@@ -282,6 +296,11 @@ sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t 
     const Span outs[] = {span_of("Y", Y, tb), span_of("S", S, tb),
                          span_of("workspace", workspace, need)};
     SN_TRY(check_alias(outs, 3, ins, 5));
+    if (noalloc && need > 0) {
+        if (hipError_t e = sn::static_scratch(&workspace); e != hipSuccess)
+            return fail(SN_ERR_HIP, "%s: static scratch lookup failed: %s", op, hipGetErrorString(e));
+        workspace_bytes = sn::kStaticScratchBytes;
+    }
 
     sn::SgnArgs a;
     a.dtype = T == SN_F32 ? 0 : 1;
@@ -318,7 +337,31 @@ sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t 
         a.tag = 1;
     }
     const char* route = "";
-    return finish_launch(sn::launch_sgn(a, current_route_not_flat(), stream, &route), route, "skip_group_norm");
+    return finish_launch(sn::launch_sgn(a, current_route_not_flat(), stream, &route), route, op);
+}
+
+}  // namespace
+
+extern "C" {
+
+sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t H, int64_t W,
+                          const void* X, const void* gamma, const void* beta, const void* skip,
+                          int32_t skip_broadcast, const void* bias, float epsilon, int64_t groups,
+                          int32_t channels_last, int32_t activation, void* Y, void* S,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return group_norm("skip_group_norm", T, M, N, C, H, W, X, gamma, beta, skip, skip_broadcast,
+                      bias, epsilon, groups, channels_last, activation, Y, S, workspace,
+                      workspace_bytes, false, stream);
+}
+
+sn_status skip_group_norm_noalloc(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t H,
+                                  int64_t W, const void* X, const void* gamma, const void* beta,
+                                  const void* skip, int32_t skip_broadcast, const void* bias,
+                                  float epsilon, int64_t groups, int32_t channels_last,
+                                  int32_t activation, void* Y, void* S, hipStream_t stream) {
+    return group_norm("skip_group_norm_noalloc", T, M, N, C, H, W, X, gamma, beta, skip,
+                      skip_broadcast, bias, epsilon, groups, channels_last, activation, Y, S,
+                      nullptr, 0, true, stream);
 }
 
 const char* skipnorm_last_error(void) { return g_error.c_str(); }

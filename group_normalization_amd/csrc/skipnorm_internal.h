@@ -62,6 +62,12 @@ size_t sgn_workspace_bytes(int dtype, int64_t N, int64_t C, int64_t H, int64_t W
                            int64_t groups, bool channels_last);
 hipError_t launch_sgn(const SgnArgs& a, Route want, hipStream_t stream, const char** route);
 
+// The device address of the library's static SkipGroupNorm scratch on the
+// current device (kStaticScratchBytes, 256-byte aligned), looked up on the
+// first call on each device.  Allocates nothing.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+hipError_t static_scratch(void** ptr);
+
 // ---------------------------------------------------------------- copy
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 

@@ -200,6 +200,33 @@ sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C,
                           size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * skip_group_norm without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, hosts that forbid hipMalloc.  It allocates nothing (no
+ * hipMalloc, hipFree or allocating library call); its partial moments live
+ * in a static device array of SKIPNORM_NOALLOC_SCRATCH_BYTES inside the
+ * library, one copy on each device it runs on, held until the process ends.
+ * Arguments, results and routes are skip_group_norm's (the caller still
+ * passes every input and output).  Errors as skip_group_norm, plus
+ * SN_ERR_WORKSPACE when the shape needs more scratch than the array holds
+ * (skip_group_norm_workspace_size tells how much it needs) and SN_ERR_HIP
+ * when the array's device address cannot be obtained.
+ * Every call on one device shares that device's array and leaves its
+ * contents behind (no call depends on them): calls that overlap in time on
+ * one device -- on different streams, or from host threads without
+ * ordering -- race on it and must not be issued.
+ * ------------------------------------------------------------------------ */
+#define SKIPNORM_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+sn_status skip_group_norm_noalloc(sn_dtype T, sn_dtype M, int64_t N, int64_t C,
+                                  int64_t H, int64_t W,
+                                  const void* X, const void* gamma, const void* beta,
+                                  const void* skip, int32_t skip_broadcast,
+                                  const void* bias, float epsilon, int64_t groups,
+                                  int32_t channels_last, int32_t activation,
+                                  void* Y, void* S, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Library information and test hooks.
  * ------------------------------------------------------------------------ */
 

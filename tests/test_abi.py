@@ -204,6 +204,36 @@ def test_sgn_empty_is_a_no_op(lib):
     assert sgn(lib, H=0, X=None, skip=None, Y=None, ws=None, ws_bytes=0) == OK
 
 
+def sgn_noalloc(lib, T=SN_F16, M=SN_F32, N=2, C=32, H=4, W=4, X=A, gamma=A + MB, beta=A + 2 * MB,
+                skip=A + 3 * MB, bcast=0, bias=None, eps=1e-5, groups=8, cl=1, act=0, Y=A + 4 * MB,
+                S=None):
+    return lib.skip_group_norm_noalloc(T, M, N, C, H, W, X, gamma, beta, skip, bcast, bias, eps,
+                                       groups, cl, act, Y, S, None)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(T=SN_BF16), DTYPE, "bfloat16"),
+    (dict(groups=7), ATTR, "divide C"),
+    (dict(act=2), ATTR, "activation"),
+    (dict(gamma=None), NULL, "gamma and beta"),
+    (dict(Y=None), NULL, "required"),
+    (dict(Y=A + 64), ALIAS, "Y overlaps input X"),
+    # 32 x 1280 x 512 x 512 float32 NCHW needs ~42 MB of partials: more than
+    # the static scratch's 8 MiB.
+    (dict(T=SN_F32, N=32, C=1280, H=512, W=512, groups=32, cl=0, gamma=A + (1 << 36),
+          beta=A + (1 << 36) + MB, skip=A + (1 << 37), bcast=1, Y=A + (1 << 38)),
+     WORKSPACE, "static scratch holds 8388608"),
+])
+def test_sgn_noalloc_rejects(lib, kw, status, text):
+    assert sgn_noalloc(lib, **kw) == status
+    assert text in err(lib)
+
+
+def test_sgn_noalloc_empty_is_a_no_op(lib):
+    assert sgn_noalloc(lib, N=0, X=None, skip=None, Y=None) == OK
+    assert sgn_noalloc(lib, H=0, X=None, skip=None, Y=None) == OK
+
+
 # ------------------------------------------------------------------ hooks
 def test_force_route_round_trip(lib):
     assert lib.skipnorm_force_route(1) == 0

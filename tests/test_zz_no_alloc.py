@@ -1,0 +1,147 @@
+"""skip_group_norm_noalloc (the entry point for callers that cannot allocate
+device memory) against skip_group_norm with a caller's workspace, called
+through the C ABI with raw pointers.
+
+Both entry points run the same kernels with the same arithmetic, so their
+outputs must agree bit for bit (stricter than the oracle tolerance); the
+oracle is checked as well.  Each test makes consecutive calls into the one
+static scratch array, the later ones on smaller inputs, so a call that read
+what the previous call left behind would show."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import group_normalization_amd as gn
+import oracle
+from group_normalization_amd import _lib, workloads
+from parity import assert_bitwise, assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+SCRATCH_BYTES = 8 << 20
+WORKSPACE = 6
+
+
+def vp(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def code(t):
+    return {torch.float32: _lib.SN_F32, torch.float16: _lib.SN_F16}[t.dtype]
+
+
+def noalloc_call(x, a, want_sum):
+    """skip_group_norm_noalloc through ctypes; outputs allocated here, the
+    library allocates nothing."""
+    X = x["X"]
+    cl = a["channels_last"]
+    N, C = X.shape[0], (X.shape[3] if cl else X.shape[1])
+    H, W = (X.shape[1], X.shape[2]) if cl else (X.shape[2], X.shape[3])
+    bcast = 0 if tuple(x["skip"].shape) == tuple(X.shape) else 1
+    Y = torch.empty_like(X)
+    S = torch.empty_like(X) if want_sum else None
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    st = _lib.lib().skip_group_norm_noalloc(
+        code(X), code(x["gamma"]), N, C, H, W, vp(X), vp(x["gamma"]), vp(x["beta"]), vp(x["skip"]),
+        bcast, vp(x.get("bias")), float(a["epsilon"]), int(a["groups"]), 1 if cl else 0,
+        int(a["activation"]), vp(Y), vp(S), stream)
+    _lib.check(st)
+    return Y, S
+
+
+def workspace_call(x, a, want_sum):
+    out = gn.skip_group_norm(x["X"], x["gamma"], x["beta"], x["skip"], x.get("bias"),
+                             groups=a["groups"], activation=a["activation"], epsilon=a["epsilon"],
+                             channels_last=a["channels_last"], want_sum=want_sum)
+    return out.Y, out.S
+
+
+CASES = [
+    # (N, C, H, W, T, M, channels_last, broadcast, bias, groups, activation, want_sum)
+    (2, 320, 64, 64, np.float16, np.float32, 1, False, True, 32, 1, True),   # the NHWC workload
+    (4, 1280, 32, 32, np.float32, np.float16, 0, True, False, 32, 0, False),  # the NCHW workload
+    (2, 640, 16, 16, np.float16, np.float16, 0, False, True, 32, 1, True),
+    (1, 320, 8, 8, np.float32, np.float32, 1, True, False, 16, 0, True),
+    (1, 64, 7, 9, np.float16, np.float32, 0, False, True, 8, 1, True),        # odd plane: phased
+]
+
+
+def inputs(case, seed):
+    N, C, H, W, T, M, cl, bc, bias, groups, act, want_sum = case
+    w = workloads.sgn("noalloc", N, C, H, W, T, M, channels_last=bool(cl), broadcast_skip=bc,
+                      bias=bias, groups=groups, activation=act, epsilon=1e-5)
+    host = workloads.generate(w, seed)
+    return host, {k: to_dev(v) for k, v in host.items()}, w.attrs, want_sum
+
+
+def check_pair(case, seed):
+    host, dev, a, want_sum = inputs(case, seed)
+    y0, s0 = noalloc_call(dev, a, want_sum)
+    route = gn.last_route()
+    y1, s1 = workspace_call(dev, a, want_sum)
+    assert gn.last_route() == route
+    assert_bitwise(to_host(y0), to_host(y1), f"Y {case}")
+    if want_sum:
+        assert_bitwise(to_host(s0), to_host(s1), f"S {case}")
+    ry, rs = oracle.skip_group_norm(host["X"], host["gamma"], host["beta"], host["skip"],
+                                    host.get("bias"), groups=a["groups"], activation=a["activation"],
+                                    epsilon=a["epsilon"], channels_last=a["channels_last"],
+                                    want_sum=want_sum)
+    assert_close(to_host(y0), ry, f"Y vs oracle {case}")
+    if want_sum:
+        assert_bitwise(to_host(s0), rs, f"S vs oracle {case}")
+    return route
+
+
+def test_noalloc_two_calls_second_smaller():
+    # The NHWC workload, then a much smaller NCHW one into the same scratch.
+    r0 = check_pair(CASES[0], seed=0)
+    r1 = check_pair(CASES[3], seed=1)
+    assert r0.startswith("sgn.cluster.nhwc") and r1.startswith("sgn.")
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c[:4])) + ("nhwc" if c[6] else "nchw"))
+def test_noalloc_matches_workspace_entry_point(case):
+    check_pair(case, seed=2)
+    check_pair(case, seed=3)  # again: the scratch now holds this shape's last call
+
+
+@pytest.mark.parametrize("route", ["split", "block"])
+def test_noalloc_split_routes(route):
+    # The three-launch routes keep their partials and (mean, rstd) in the scratch.
+    with gn.force_route(route):
+        r0 = check_pair(CASES[2], seed=4)
+        r1 = check_pair(CASES[4], seed=5)
+    assert r0.startswith("sgn.split") and r1.startswith("sgn.split")
+
+
+def test_noalloc_rejects_shapes_beyond_the_scratch():
+    # NCHW float32 32 x 1280 x 512 x 512 with 32 groups needs ~42 MB of
+    # partials; the call is rejected during validation, before anything is
+    # enqueued (the small tensors passed are never dereferenced).
+    dims = (32, 1280, 512, 512)
+    need = ctypes.c_size_t()
+    _lib.check(_lib.lib().skip_group_norm_workspace_size(_lib.SN_F32, *dims, 32, 0, ctypes.byref(need)))
+    assert need.value > SCRATCH_BYTES
+    x = torch.empty(16, device="cuda")
+    y = torch.empty(16, device="cuda")
+    st = _lib.lib().skip_group_norm_noalloc(_lib.SN_F32, _lib.SN_F32, *dims, vp(x), vp(x), vp(x), vp(x), 1,
+                                            None, 1e-5, 32, 0, 0, vp(y), None, None)
+    assert st == WORKSPACE
+    assert "static scratch" in _lib.lib().skipnorm_last_error().decode()
+
+
+def test_noalloc_binding_matches():
+    # The Python binding of the same entry point, with caller-provided outputs.
+    host, dev, a, want_sum = inputs(CASES[0], seed=6)
+    Y = torch.empty_like(dev["X"])
+    S = torch.empty_like(dev["X"])
+    out = gn.skip_group_norm_noalloc(dev["X"], dev["gamma"], dev["beta"], dev["skip"], dev["bias"],
+                                     groups=a["groups"], activation=a["activation"], Y=Y, S=S,
+                                     epsilon=a["epsilon"], channels_last=a["channels_last"])
+    assert out.Y is Y and out.S is S
+    y1, s1 = workspace_call(dev, a, True)
+    assert_bitwise(to_host(Y), to_host(y1), "Y")
+    assert_bitwise(to_host(S), to_host(s1), "S")
