@@ -98,6 +98,8 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_int, ctypes.c_void_p]
 
     def create(self):
         ev = self.ct.c_void_p()
@@ -117,6 +119,37 @@ class HipEvents:
 
     def destroy(self, ev):
         self.hip.hipEventDestroy(ev)
+
+    def memcpy_dtod(self, dst_ptr, src_ptr, nbytes, stream_handle):
+        """hipMemcpyAsync(..., hipMemcpyDeviceToDevice) on the given stream."""
+        if self.hip.hipMemcpyAsync(self.ct.c_void_p(dst_ptr), self.ct.c_void_p(src_ptr), nbytes, 3,
+                                   self.ct.c_void_p(stream_handle)) != 0:
+            raise RuntimeError("hipMemcpyAsync failed")
+
+
+def copy_ceilings(torch, gn, hev, stream, reps=10):
+    """Practical bandwidth ceilings over COPY_BYTES (read + written bytes per
+    second): the library's 16-byte copy kernel, and hipMemcpyDtoD (the
+    runtime's device-to-device copy) as a second reference."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    out = {}
+    for name, run in (("copy_kernel", lambda: gn.copy_(dst, src)),
+                      ("hipMemcpyDtoD", lambda: hev.memcpy_dtod(dst.data_ptr(), src.data_ptr(),
+                                                                COPY_BYTES, stream))):
+        for _ in range(3):
+            run()
+        e0, e1 = hev.create(), hev.create()
+        hev.record(e0, stream)
+        for _ in range(reps):
+            run()
+        hev.record(e1, stream)
+        torch.cuda.synchronize()
+        out[name] = 2 * COPY_BYTES * reps / (hev.elapsed_ms(e0, e1) * 1e-3) / 1e9
+        hev.destroy(e0)
+        hev.destroy(e1)
+    del src, dst
+    return out
 
 
 class Op:
@@ -238,41 +271,50 @@ def config_table(args):
     torch.cuda.set_device(0)
     hev = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
+    ceilings = copy_ceilings(torch, gn, hev, stream)
+    copy_gbps = ceilings["copy_kernel"]
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        gn.copy_(dst, src)
-    e0, e1 = hev.create(), hev.create()
-    hev.record(e0, stream)
-    for _ in range(10):
-        gn.copy_(dst, src)
-    hev.record(e1, stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * COPY_BYTES * 10 / (hev.elapsed_ms(e0, e1) * 1e-3) / 1e9
-    rows = []
-    for name in workloads.ORDER:
-        w = workloads.WORKLOADS[name]
-        o = Op(name, torch, gn, workloads)
+
+    def cold_times(run):
+        """Event-timed invocations of run(), each after a 1 GiB copy that
+        evicts the last-level cache."""
         for _ in range(args.warmup):
             gn.copy_(dst, src)
-            o.run()
+            run()
         pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
         for a, b in pairs:
-            gn.copy_(dst, src)  # evicts the last-level cache
+            gn.copy_(dst, src)
             hev.record(a, stream)
-            o.run()
+            run()
             hev.record(b, stream)
         torch.cuda.synchronize()
         us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b in pairs])
         for a, b in pairs:
             hev.destroy(a)
             hev.destroy(b)
-        med = float(np.median(us))
+        return us
+
+    rows = []
+    for name in workloads.ORDER:
+        w = workloads.WORKLOADS[name]
+        o = Op(name, torch, gn, workloads)
+        us = cold_times(o.run)
+        # The same byte volume moved by the copy kernel (half read, half
+        # written), cold: what streaming those bytes costs at this size,
+        # launch included.
+        half = (o.bytes // 2 + 15) // 16 * 16
+        csrc = torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1)
+        cdst = torch.empty_like(csrc)
+        cus = cold_times(lambda: gn.copy_(cdst, csrc))
+        del csrc, cdst
+        med, cmed = float(np.median(us)), float(np.median(cus))
         row = {"workload": name, "bytes": o.bytes, "invocations": args.steps,
                "median_us": round(med, 3), "min_us": round(float(us.min()), 3),
                "p90_us": round(float(np.percentile(us, 90)), 3),
                "gbps": round(o.bytes / med / 1e3, 1), "frac_of_peak": round(o.bytes / med / 1e3 / PEAK_GBPS, 4),
-               "frac_of_copy": round(o.bytes / med / 1e3 / copy_gbps, 4)}
+               "frac_of_copy": round(o.bytes / med / 1e3 / copy_gbps, 4),
+               "same_bytes_copy_us": round(cmed, 3), "frac_of_same_bytes_copy": round(cmed / med, 4)}
         del o
         if not args.no_cpu_baseline:
             x = workloads.generate(w)
@@ -289,15 +331,16 @@ def config_table(args):
             del x
         rows.append(row)
         log(f"{name}: median {med:.2f} us ({row['gbps']} GB/s)")
-    for e in (e0, e1):
-        hev.destroy(e)
-    out = {"configs": rows, "copy_ceiling_gbps": round(copy_gbps, 1), "oracle_threads": 1,
+    out = {"configs": rows, "copy_ceiling_gbps": round(copy_gbps, 1),
+           "memcpy_dtod_ceiling_gbps": round(ceilings["hipMemcpyDtoD"], 1), "oracle_threads": 1,
            "host": host_cpu()}
-    lines = ["| workload | median us | min us | p90 us | GB/s | % of 8 TB/s | % of copy | oracle s | oracle GB/s |",
-             "|---|---|---|---|---|---|---|---|---|"]
+    lines = ["| workload | median us | min us | p90 us | GB/s | % of 8 TB/s | % of copy | same-bytes copy us | "
+             "% of same-bytes copy | oracle s | oracle GB/s |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| {r['workload']} | {r['median_us']} | {r['min_us']} | {r['p90_us']} | {r['gbps']} | "
                      f"{100 * r['frac_of_peak']:.1f} | {100 * r['frac_of_copy']:.1f} | "
+                     f"{r['same_bytes_copy_us']} | {100 * r['frac_of_same_bytes_copy']:.1f} | "
                      f"{r.get('oracle_s', '')} | {r.get('oracle_gbps', '')} |")
     print("\n".join(lines), file=sys.stderr)
     print(json.dumps(out), flush=True)
@@ -388,22 +431,13 @@ def main():
                           "gbps": round(o.bytes / (avg * 1e-3) / 1e9, 1),
                           "frac_of_peak": round(o.bytes / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)}
 
-    # Copy ceiling: the library's 16-byte copy kernel over 1 GiB (outside the
-    # timed region; also the calibration kernel for the byte counters).
-    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        gn.copy_(dst, src)
-    e0, e1 = hev.create(), hev.create()
-    hev.record(e0, stream)
-    for _ in range(10):
-        gn.copy_(dst, src)
-    hev.record(e1, stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * COPY_BYTES * 10 / (hev.elapsed_ms(e0, e1) * 1e-3) / 1e9
-    del src, dst
-    for ev in [e0, e1] + [e for per_step in evs for pair in per_step for e in pair]:
+    # Copy ceilings over 1 GiB, outside the timed region: the library's
+    # 16-byte copy kernel (also the calibration kernel for the byte counters)
+    # and hipMemcpyDtoD.
+    for ev in [e for per_step in evs for pair in per_step for e in pair]:
         hev.destroy(ev)
+    ceilings = copy_ceilings(torch, gn, hev, stream)
+    copy_gbps = ceilings["copy_kernel"]
 
     for v in per_op.values():
         v["frac_of_copy"] = round(v["gbps"] / copy_gbps, 4)
@@ -459,6 +493,7 @@ def main():
         "ops": per_op,
         "next_ops": next_ops,
         "copy_ceiling_gbps": round(copy_gbps, 1),
+        "memcpy_dtod_ceiling_gbps": round(ceilings["hipMemcpyDtoD"], 1),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
