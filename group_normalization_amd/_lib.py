@@ -1,4 +1,5 @@
-"""ctypes declarations of the libskipnorm C ABI (``include/skipnorm.h``).
+"""ctypes declarations of the libskipnorm C ABI (``include/skipnorm.h``, and
+the test hooks of ``include/skipnorm_testing.h``).
 
 The library is loaded on first use from ``group_normalization_amd/libskipnorm.so``
 (built in-tree by ``group_normalization_amd.build``).  There is no fallback:
@@ -16,21 +17,46 @@ SN_F32, SN_F16, SN_BF16 = 0, 1, 2
 STATUS_NAMES = {0: "SN_OK", 1: "SN_ERR_NULL", 2: "SN_ERR_DTYPE", 3: "SN_ERR_SHAPE",
                 4: "SN_ERR_ATTR", 5: "SN_ERR_ALIAS", 6: "SN_ERR_WORKSPACE", 7: "SN_ERR_HIP"}
 
-#: Every symbol the header declares, with (restype, argtypes).
+SN_MAX_RANK = 8
+
+
+class TensorDesc(ctypes.Structure):
+    """sn_tensor_in / sn_tensor_out: device data, element type, rank, shape."""
+
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("rank", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * SN_MAX_RANK)]
+
+
+def tensor_desc(data_ptr, dtype_code: int, shape) -> TensorDesc:
+    """A descriptor for ``shape`` elements of type ``dtype_code`` at the
+    device address ``data_ptr`` (an int or None)."""
+    shape = tuple(int(x) for x in shape)
+    if len(shape) > SN_MAX_RANK:
+        raise ValueError(f"rank {len(shape)} exceeds the ABI's {SN_MAX_RANK}")
+    d = TensorDesc()
+    d.data = data_ptr
+    d.dtype = dtype_code
+    d.rank = len(shape)
+    for i, x in enumerate(shape):
+        d.shape[i] = x
+    return d
+
+
+#: Every symbol the headers (skipnorm.h and skipnorm_testing.h) declare,
+#: with (restype, argtypes).
 _vp, _i64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                               ctypes.c_float, ctypes.c_size_t)
 _ci = ctypes.c_int
+_td = ctypes.POINTER(TensorDesc)
 SIGNATURES = {
-    "skip_rms_norm": (_ci, [_ci, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp]),
-    "skip_layer_norm": (_ci, [_ci, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp,
+    "skip_rms_norm": (_ci, [_td, _td, _td, _td, _f32, _td, _td, _td, _td, _vp]),
+    "skip_layer_norm": (_ci, [_td, _td, _td, _td, _td, _f32, _td, _td, _td, _td, _vp]),
+    "gated_rms_norm": (_ci, [_td, _td, _td, _f32, _td, _vp]),
+    "skip_group_norm_workspace_size": (_ci, [_td, _i64, _i32, ctypes.POINTER(_sz)]),
+    "skip_group_norm": (_ci, [_td, _td, _td, _td, _td, _f32, _i64, _i32, _i32, _td, _td, _vp, _sz,
                               _vp]),
-    "gated_rms_norm": (_ci, [_ci, _i64, _i64, _vp, _vp, _vp, _f32, _vp, _vp]),
-    "skip_group_norm_workspace_size": (_ci, [_ci, _i64, _i64, _i64, _i64, _i64, _i32,
-                                             ctypes.POINTER(_sz)]),
-    "skip_group_norm": (_ci, [_ci, _ci, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
-                              _f32, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
-    "skip_group_norm_noalloc": (_ci, [_ci, _ci, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i32,
-                                      _vp, _f32, _i64, _i32, _i32, _vp, _vp, _vp]),
+    "skip_group_norm_noalloc": (_ci, [_td, _td, _td, _td, _td, _f32, _i64, _i32, _i32, _td, _td,
+                                      _vp]),
     "skipnorm_last_error": (ctypes.c_char_p, []),
     "skipnorm_abi_version": (_ci, []),
     "skipnorm_force_route": (_ci, [_ci]),

@@ -1,5 +1,6 @@
-// skipnorm_api.cpp -- C-ABI front end of libskipnorm: argument validation
-// (host only, before anything is enqueued), route selection hooks, error
+// skipnorm_api.cpp -- C-ABI front end of libskipnorm: validation of every
+// tensor descriptor and attribute against the operators' contracts (host
+// only, before anything is enqueued), route selection hooks, error
 // reporting, and the calls into the kernel launchers.
 #include <atomic>
 #include <chrono>
@@ -9,6 +10,7 @@
 #include <string>
 
 #include "../../include/skipnorm.h"
+#include "../../include/skipnorm_testing.h"
 #include "skipnorm_internal.h"
 
 namespace {
@@ -49,21 +51,117 @@ sn_status ok() {
     return SN_OK;
 }
 
-size_t elem_size(sn_dtype t) { return t == SN_F32 ? 4 : 2; }
+#define SN_TRY(expr)                     \
+    do {                                 \
+        sn_status st_ = (expr);          \
+        if (st_ != SN_OK) return st_;    \
+    } while (0)
 
-sn_status check_dtype(sn_dtype t, const char* what) {
+constexpr int64_t kMaxRowElems = int64_t(1) << 30;   // hidden / span / image size
+constexpr int64_t kMaxElems = int64_t(1) << 46;      // whole tensor
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1; // rows; blocks of one launch
+static_assert(sn::kStaticScratchBytes == SKIPNORM_NOALLOC_SCRATCH_BYTES,
+              "the header states the static scratch size");
+
+size_t elem_size(sn_dtype t) { return t == SN_F32 ? 4 : 2; }
+int kernel_dtype(sn_dtype t) { return t == SN_F32 ? 0 : 1; }
+
+sn_status check_dtype(sn_dtype t, const char* op, const char* what) {
     if (t == SN_F32 || t == SN_F16) return SN_OK;
-    if (t == SN_BF16) return fail(SN_ERR_DTYPE, "%s: bfloat16 is not implemented", what);
-    return fail(SN_ERR_DTYPE, "%s: unknown dtype code %d", what, int(t));
+    if (t == SN_BF16) return fail(SN_ERR_DTYPE, "%s: %s: bfloat16 is not implemented", op, what);
+    return fail(SN_ERR_DTYPE, "%s: %s: unknown dtype code %d", op, what, int(t));
 }
 
-sn_status check_epsilon(float eps) {
+sn_status check_epsilon(const char* op, float eps) {
     if (!std::isfinite(eps) || eps < 0.0f)
-        return fail(SN_ERR_ATTR, "epsilon must be finite and non-negative (got %g)", double(eps));
+        return fail(SN_ERR_ATTR, "%s: epsilon must be finite and non-negative (got %g)", op,
+                    double(eps));
     return SN_OK;
 }
 
-// A byte range of a tensor; empty when the pointer is NULL or size is 0.
+bool mul_overflows(int64_t a, int64_t b, int64_t* out) { return __builtin_mul_overflow(a, b, out); }
+
+// ---------------------------------------------------------------- descriptors
+// A descriptor read and checked for internal consistency: rank within
+// 0..SN_MAX_RANK, every extent >= 0, element count without overflow.
+struct Tensor {
+    const char* name = "";
+    bool present = false;
+    void* data = nullptr;
+    sn_dtype dtype = SN_F32;
+    int rank = 0;
+    int64_t shape[SN_MAX_RANK] = {};
+    int64_t numel = 0;
+};
+
+template <typename D>
+sn_status read_tensor(const char* op, const char* name, const D* d, bool required, Tensor* out) {
+    out->name = name;
+    if (!d) {
+        if (required) return fail(SN_ERR_NULL, "%s: %s is required", op, name);
+        return SN_OK;
+    }
+    out->present = true;
+    out->data = const_cast<void*>(static_cast<const void*>(d->data));
+    out->dtype = d->dtype;
+    if (d->rank < 0 || d->rank > SN_MAX_RANK)
+        return fail(SN_ERR_SHAPE, "%s: %s: rank %d outside 0..%d", op, name, int(d->rank), SN_MAX_RANK);
+    out->rank = d->rank;
+    int64_t n = 1;
+    for (int i = 0; i < d->rank; ++i) {
+        if (d->shape[i] < 0)
+            return fail(SN_ERR_SHAPE, "%s: %s: negative extent %lld", op, name, (long long)d->shape[i]);
+        out->shape[i] = d->shape[i];
+        if (mul_overflows(n, d->shape[i], &n) || n > kMaxElems)
+            return fail(SN_ERR_SHAPE, "%s: %s: more than 2^46 elements", op, name);
+    }
+    out->numel = n;
+    return SN_OK;
+}
+
+std::string shape_str(const int64_t* shape, int rank) {
+    std::string s = "(";
+    for (int i = 0; i < rank; ++i) {
+        if (i) s += ", ";
+        s += std::to_string(shape[i]);
+    }
+    if (rank == 1) s += ",";
+    return s + ")";
+}
+std::string shape_str(const Tensor& t) { return shape_str(t.shape, t.rank); }
+
+bool same_shape(const Tensor& a, const int64_t* shape, int rank) {
+    if (a.rank != rank) return false;
+    for (int i = 0; i < rank; ++i)
+        if (a.shape[i] != shape[i]) return false;
+    return true;
+}
+
+// t (if present) has exactly this shape.
+sn_status expect_shape(const char* op, const Tensor& t, const int64_t* shape, int rank,
+                       const char* what) {
+    if (!t.present || same_shape(t, shape, rank)) return SN_OK;
+    return fail(SN_ERR_SHAPE, "%s: %s must have shape %s (%s), got %s", op, t.name,
+                shape_str(shape, rank).c_str(), what, shape_str(t).c_str());
+}
+
+// t (if present) has element type `want`.
+sn_status expect_dtype(const char* op, const Tensor& t, sn_dtype want, const char* what) {
+    if (!t.present || t.dtype == want) return SN_OK;
+    if (t.dtype != SN_F32 && t.dtype != SN_F16) SN_TRY(check_dtype(t.dtype, op, t.name));
+    return fail(SN_ERR_DTYPE, "%s: %s must be %s (%s)", op, t.name,
+                want == SN_F32 ? "float32" : "float16", what);
+}
+
+// Present tensors holding elements need a data pointer.
+sn_status expect_data(const char* op, const Tensor& t) {
+    if (t.present && t.numel > 0 && !t.data)
+        return fail(SN_ERR_NULL, "%s: %s has %lld elements and a NULL data pointer", op, t.name,
+                    (long long)t.numel);
+    return SN_OK;
+}
+
+// A byte range of a tensor; empty when absent, NULL or without elements.
 struct Span {
     const char* name;
     uintptr_t lo, hi;
@@ -73,6 +171,10 @@ struct Span {
 Span span_of(const char* name, const void* p, size_t bytes) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
     return Span{name, lo, p ? lo + bytes : lo};
+}
+Span span_of(const Tensor& t) {
+    if (!t.present) return Span{t.name, 0, 0};
+    return span_of(t.name, t.data, size_t(t.numel) * elem_size(t.dtype));
 }
 
 bool overlap(const Span& a, const Span& b) {
@@ -92,8 +194,6 @@ sn_status check_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
     return SN_OK;
 }
 
-bool mul_overflows(int64_t a, int64_t b, int64_t* out) { return __builtin_mul_overflow(a, b, out); }
-
 sn::Route current_route() { return static_cast<sn::Route>(g_force_route.load(std::memory_order_relaxed)); }
 // The flat route is GatedRMSNorm's; the other operators run it as automatic.
 sn::Route current_route_not_flat() {
@@ -108,169 +208,162 @@ sn_status finish_launch(hipError_t err, const char* route, const char* op) {
     return ok();
 }
 
-#define SN_TRY(expr)                     \
-    do {                                 \
-        sn_status st_ = (expr);          \
-        if (st_ != SN_OK) return st_;    \
-    } while (0)
+// ---------------------------------------------------------------- row norms
+// SkipSimplifiedLayerNormalization and its mean-removing form share
+// validation and kernels; `center` removes the row mean (skip_layer_norm).
+sn_status row_norm(const char* op, bool center, const sn_tensor_in* input_d,
+                   const sn_tensor_in* skip_d, const sn_tensor_in* gamma_d,
+                   const sn_tensor_in* beta_d, const sn_tensor_in* bias_d, float epsilon,
+                   const sn_tensor_out* output_d, const sn_tensor_out* mean_d,
+                   const sn_tensor_out* inv_d, const sn_tensor_out* sum_d, hipStream_t stream) {
+    Tensor input, skip, gamma, beta, bias, output, mean, inv, sum;
+    SN_TRY(read_tensor(op, "input", input_d, true, &input));
+    SN_TRY(read_tensor(op, "skip", skip_d, true, &skip));
+    SN_TRY(read_tensor(op, "gamma", gamma_d, true, &gamma));
+    SN_TRY(read_tensor(op, "beta", beta_d, false, &beta));
+    SN_TRY(read_tensor(op, "bias", bias_d, false, &bias));
+    SN_TRY(read_tensor(op, "output", output_d, true, &output));
+    SN_TRY(read_tensor(op, "mean", mean_d, false, &mean));
+    SN_TRY(read_tensor(op, "inv_std_var", inv_d, false, &inv));
+    SN_TRY(read_tensor(op, "input_skip_bias_sum", sum_d, false, &sum));
 
-constexpr int64_t kMaxRowElems = int64_t(1) << 30;   // hidden / span / image size
-constexpr int64_t kMaxElems = int64_t(1) << 46;      // whole tensor
-constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1; // rows; blocks of one launch
-static_assert(sn::kStaticScratchBytes == SKIPNORM_NOALLOC_SCRATCH_BYTES,
-              "the header states the static scratch size");
+    // Element types: one T for every tensor but the statistics (float32).
+    const sn_dtype T = input.dtype;
+    SN_TRY(check_dtype(T, op, "input"));
+    for (const Tensor* t : {&skip, &gamma, &beta, &bias, &output, &sum})
+        SN_TRY(expect_dtype(op, *t, T, "the input's type"));
+    for (const Tensor* t : {&mean, &inv}) SN_TRY(expect_dtype(op, *t, SN_F32, "statistics"));
 
-}  // namespace
+    // Shapes: input (token_count, hidden) or (batch, sequence, hidden).
+    if (input.rank != 2 && input.rank != 3)
+        return fail(SN_ERR_SHAPE,
+                    "%s: input must have rank 2 (token_count, hidden) or 3 (batch, sequence, hidden), "
+                    "got %s", op, shape_str(input).c_str());
+    const int64_t hidden = input.shape[input.rank - 1];
+    if (hidden < 1 || hidden > kMaxRowElems)
+        return fail(SN_ERR_SHAPE, "%s: hidden (the last extent) must be in 1..2^30, got %lld", op,
+                    (long long)hidden);
+    const int64_t rows = input.numel / hidden;
+    if (rows > kMaxRows) return fail(SN_ERR_SHAPE, "%s: more than 2^31 - 1 rows", op);
+    int64_t stat_shape[SN_MAX_RANK];
+    for (int i = 0; i < input.rank; ++i) stat_shape[i] = input.shape[i];
+    stat_shape[input.rank - 1] = 1;
+    SN_TRY(expect_shape(op, skip, input.shape, input.rank, "the input's shape"));
+    for (const Tensor* t : {&gamma, &beta, &bias}) SN_TRY(expect_shape(op, *t, &hidden, 1, "hidden"));
+    for (const Tensor* t : {&output, &sum})
+        SN_TRY(expect_shape(op, *t, input.shape, input.rank, "the input's shape"));
+    for (const Tensor* t : {&mean, &inv})
+        SN_TRY(expect_shape(op, *t, stat_shape, input.rank, "the input's shape, last extent 1"));
 
-namespace {
+    SN_TRY(check_epsilon(op, epsilon));
+    for (const Tensor* t : {&input, &skip, &gamma, &beta, &bias, &output, &mean, &inv, &sum})
+        SN_TRY(expect_data(op, *t));
 
-// Both row normalizations share validation and kernels; `center` removes the
-// row mean (skip_layer_norm).
-sn_status row_norm(const char* op, bool center, sn_dtype T, int64_t rows, int64_t hidden,
-                   const void* input, const void* skip, const void* gamma, const void* beta,
-                   const void* bias, float epsilon, void* output, float* mean,
-                   float* inv_std_var, void* input_skip_bias_sum, hipStream_t stream) {
-    SN_TRY(check_dtype(T, op));
-    if (rows < 0 || hidden < 1 || hidden > kMaxRowElems)
-        return fail(SN_ERR_SHAPE, "%s: need rows >= 0 and 1 <= hidden <= 2^30 (got %lld, %lld)", op,
-                    (long long)rows, (long long)hidden);
-    int64_t numel;
-    if (mul_overflows(rows, hidden, &numel) || numel > kMaxElems || rows > kMaxRows)
-        return fail(SN_ERR_SHAPE, "%s: rows * hidden too large (rows < 2^31, elements <= 2^46)", op);
-    SN_TRY(check_epsilon(epsilon));
-    if (!gamma) return fail(SN_ERR_NULL, "%s: gamma is required", op);
-    if (numel > 0 && (!input || !skip || !output))
-        return fail(SN_ERR_NULL, "%s: input, skip and output are required", op);
-
-    const size_t es = elem_size(T);
-    const size_t tb = size_t(numel) * es;
-    const Span ins[] = {span_of("input", input, tb), span_of("skip", skip, tb),
-                        span_of("gamma", gamma, size_t(hidden) * es),
-                        span_of("bias", bias, size_t(hidden) * es),
-                        span_of("beta", beta, size_t(hidden) * es)};
-    const Span outs[] = {span_of("output", output, tb),
-                         span_of("mean", mean, size_t(rows) * 4),
-                         span_of("inv_std_var", inv_std_var, size_t(rows) * 4),
-                         span_of("input_skip_bias_sum", input_skip_bias_sum, tb)};
+    const Span ins[] = {span_of(input), span_of(skip), span_of(gamma), span_of(bias), span_of(beta)};
+    const Span outs[] = {span_of(output), span_of(mean), span_of(inv), span_of(sum)};
     SN_TRY(check_alias(outs, 4, ins, 5));
 
-    sn::SslnArgs a{T == SN_F32 ? 0 : 1, rows, hidden, input, skip, gamma, beta, bias, epsilon,
-                   output, mean, inv_std_var, input_skip_bias_sum, center};
+    sn::SslnArgs a{kernel_dtype(T), rows, hidden, input.data, skip.data, gamma.data,
+                   beta.present ? beta.data : nullptr, bias.present ? bias.data : nullptr, epsilon,
+                   output.data, static_cast<float*>(mean.present ? mean.data : nullptr),
+                   static_cast<float*>(inv.present ? inv.data : nullptr),
+                   sum.present ? sum.data : nullptr, center};
     const char* route = "";
     return finish_launch(sn::launch_ssln(a, current_route_not_flat(), stream, &route), route, op);
 }
 
-}  // namespace
-
-extern "C" {
-
-sn_status skip_rms_norm(sn_dtype T, int64_t rows, int64_t hidden, const void* input,
-                        const void* skip, const void* gamma, const void* bias, float epsilon,
-                        void* output, float* mean, float* inv_std_var,
-                        void* input_skip_bias_sum, hipStream_t stream) {
-    return row_norm("skip_rms_norm", false, T, rows, hidden, input, skip, gamma, nullptr, bias,
-                    epsilon, output, mean, inv_std_var, input_skip_bias_sum, stream);
-}
-
-sn_status skip_layer_norm(sn_dtype T, int64_t rows, int64_t hidden, const void* input,
-                          const void* skip, const void* gamma, const void* beta, const void* bias,
-                          float epsilon, void* output, float* mean, float* inv_std_var,
-                          void* input_skip_bias_sum, hipStream_t stream) {
-    return row_norm("skip_layer_norm", true, T, rows, hidden, input, skip, gamma, beta, bias,
-                    epsilon, output, mean, inv_std_var, input_skip_bias_sum, stream);
-}
-
-sn_status gated_rms_norm(sn_dtype T, int64_t numel, int64_t span, const void* X,
-                         const void* scale, const void* gate, float epsilon, void* Y,
-                         hipStream_t stream) {
-    SN_TRY(check_dtype(T, "gated_rms_norm T"));
-    if (numel < 0 || span < 1 || span > kMaxRowElems || numel > kMaxElems)
-        return fail(SN_ERR_SHAPE, "gated_rms_norm: need numel >= 0 and 1 <= span <= 2^30 (got %lld, %lld)",
-                    (long long)numel, (long long)span);
-    if (numel / span > kMaxRows)
-        return fail(SN_ERR_SHAPE, "gated_rms_norm: more than 2^31 - 1 rows");
-    if (numel % span != 0)
-        return fail(SN_ERR_SHAPE,
-                    "gated_rms_norm: element count %lld is not a multiple of the span C = %lld",
-                    (long long)numel, (long long)span);
-    SN_TRY(check_epsilon(epsilon));
-    if (!scale) return fail(SN_ERR_NULL, "gated_rms_norm: scale is required");
-    if (numel > 0 && (!X || !gate || !Y))
-        return fail(SN_ERR_NULL, "gated_rms_norm: X, gate and Y are required");
-
-    const size_t es = elem_size(T);
-    const size_t tb = size_t(numel) * es;
-    const Span ins[] = {span_of("X", X, tb), span_of("gate", gate, tb),
-                        span_of("scale", scale, size_t(span) * es)};
-    const Span outs[] = {span_of("Y", Y, tb)};
-    SN_TRY(check_alias(outs, 1, ins, 3));
-
-    sn::GatedArgs a{T == SN_F32 ? 0 : 1, numel / span, span, X, scale, gate, epsilon, Y};
-    const char* route = "";
-    return finish_launch(sn::launch_gated(a, current_route(), stream, &route), route, "gated_rms_norm");
-}
-
-namespace {
-
-sn_status check_sgn_geometry(sn_dtype T, int64_t N, int64_t C, int64_t H, int64_t W,
-                             int64_t groups) {
-    SN_TRY(check_dtype(T, "skip_group_norm T"));
-    if (N < 0 || H < 0 || W < 0 || C < 1)
-        return fail(SN_ERR_SHAPE, "skip_group_norm: need N, H, W >= 0 and C >= 1");
+// ---------------------------------------------------------------- SkipGroupNorm
+sn_status check_sgn_geometry(const char* op, sn_dtype T, int64_t N, int64_t C, int64_t H,
+                             int64_t W, int64_t groups) {
+    if (C < 1) return fail(SN_ERR_SHAPE, "%s: X must have C >= 1 channels", op);
     int64_t hw, image;
     if (mul_overflows(H, W, &hw) || mul_overflows(hw, C, &image) || image > kMaxRowElems)
-        return fail(SN_ERR_SHAPE, "skip_group_norm: C * H * W must not exceed 2^30");
-    int64_t numel;
-    if (mul_overflows(image, N, &numel) || numel > kMaxElems)
-        return fail(SN_ERR_SHAPE, "skip_group_norm: tensor too large");
+        return fail(SN_ERR_SHAPE, "%s: C * H * W must not exceed 2^30", op);
     if (groups < 1 || C % groups != 0)
-        return fail(SN_ERR_ATTR, "skip_group_norm: groups (%lld) must be >= 1 and divide C (%lld)",
+        return fail(SN_ERR_ATTR, "%s: groups (%lld) must be >= 1 and divide C (%lld)", op,
                     (long long)groups, (long long)C);
     // Launch grids: N * groups * B blocks, B blocks per (n, group) partial row.
-    const int64_t B = sn::sgn_partials_per_group(T == SN_F32 ? 0 : 1, N, C, H, W, groups, true);
-    const int64_t B2 = sn::sgn_partials_per_group(T == SN_F32 ? 0 : 1, N, C, H, W, groups, false);
+    const int64_t B = sn::sgn_partials_per_group(kernel_dtype(T), N, C, H, W, groups, true);
+    const int64_t B2 = sn::sgn_partials_per_group(kernel_dtype(T), N, C, H, W, groups, false);
     int64_t blocks;
     if (mul_overflows(N * groups, B > B2 ? B : B2, &blocks) || blocks > kMaxRows)
-        return fail(SN_ERR_SHAPE, "skip_group_norm: too many (n, group) pairs for one launch");
+        return fail(SN_ERR_SHAPE, "%s: too many (n, group) pairs for one launch", op);
     return SN_OK;
 }
 
-}  // namespace
-
-sn_status skip_group_norm_workspace_size(sn_dtype T, int64_t N, int64_t C, int64_t H, int64_t W,
-                                         int64_t groups, int32_t channels_last, size_t* bytes) {
-    if (!bytes) return fail(SN_ERR_NULL, "skip_group_norm_workspace_size: bytes is NULL");
-    SN_TRY(check_sgn_geometry(T, N, C, H, W, groups));
-    *bytes = (N == 0 || H * W == 0)
-                 ? 0
-                 : sn::sgn_workspace_bytes(T == SN_F32 ? 0 : 1, N, C, H, W, groups, channels_last != 0);
-    return ok();
+// X's logical (N, C, H, W) from its rank-4 shape and layout.
+struct Nchw {
+    int64_t N, C, H, W;
+};
+sn_status sgn_dims(const char* op, const Tensor& X, int32_t channels_last, Nchw* d) {
+    if (X.rank != 4)
+        return fail(SN_ERR_SHAPE, "%s: X must have rank 4 (%s), got %s", op,
+                    channels_last ? "N, H, W, C" : "N, C, H, W", shape_str(X).c_str());
+    d->N = X.shape[0];
+    if (channels_last) {
+        d->H = X.shape[1];
+        d->W = X.shape[2];
+        d->C = X.shape[3];
+    } else {
+        d->C = X.shape[1];
+        d->H = X.shape[2];
+        d->W = X.shape[3];
+    }
+    return SN_OK;
 }
-
-}  // extern "C"
-
-namespace {
 
 // skip_group_norm with the caller's workspace, or (noalloc) with the
 // library's static scratch on the current device.
-sn_status group_norm(const char* op, sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t H,
-                     int64_t W, const void* X, const void* gamma, const void* beta,
-                     const void* skip, int32_t skip_broadcast, const void* bias, float epsilon,
-                     int64_t groups, int32_t channels_last, int32_t activation, void* Y, void* S,
-                     void* workspace, size_t workspace_bytes, bool noalloc, hipStream_t stream) {
-    SN_TRY(check_sgn_geometry(T, N, C, H, W, groups));
-    SN_TRY(check_dtype(M, "skip_group_norm M (gamma/beta)"));
-    SN_TRY(check_epsilon(epsilon));
+sn_status group_norm(const char* op, const sn_tensor_in* X_d, const sn_tensor_in* gamma_d,
+                     const sn_tensor_in* beta_d, const sn_tensor_in* skip_d,
+                     const sn_tensor_in* bias_d, float epsilon, int64_t groups,
+                     int32_t channels_last, int32_t activation, const sn_tensor_out* Y_d,
+                     const sn_tensor_out* S_d, void* workspace, size_t workspace_bytes,
+                     bool noalloc, hipStream_t stream) {
+    Tensor X, gamma, beta, skip, bias, Y, S;
+    SN_TRY(read_tensor(op, "X", X_d, true, &X));
+    SN_TRY(read_tensor(op, "gamma", gamma_d, true, &gamma));
+    SN_TRY(read_tensor(op, "beta", beta_d, true, &beta));
+    SN_TRY(read_tensor(op, "skip", skip_d, true, &skip));
+    SN_TRY(read_tensor(op, "bias", bias_d, false, &bias));
+    SN_TRY(read_tensor(op, "Y", Y_d, true, &Y));
+    SN_TRY(read_tensor(op, "S", S_d, false, &S));
+
+    // Element types: T for X, skip, bias, Y, S; M for gamma and beta.
+    const sn_dtype T = X.dtype, M = gamma.dtype;
+    SN_TRY(check_dtype(T, op, "X"));
+    SN_TRY(check_dtype(M, op, "gamma"));
+    for (const Tensor* t : {&skip, &bias, &Y, &S}) SN_TRY(expect_dtype(op, *t, T, "X's type"));
+    SN_TRY(expect_dtype(op, beta, M, "gamma's type"));
+
+    // Shapes.
+    Nchw d;
+    SN_TRY(sgn_dims(op, X, channels_last, &d));
+    SN_TRY(check_sgn_geometry(op, T, d.N, d.C, d.H, d.W, groups));
+    for (const Tensor* t : {&gamma, &beta, &bias}) SN_TRY(expect_shape(op, *t, &d.C, 1, "C"));
+    for (const Tensor* t : {&Y, &S}) SN_TRY(expect_shape(op, *t, X.shape, 4, "X's shape"));
+    // skip: X's exact shape first, then the broadcast spellings (N, C) and
+    // (N, 1, 1, C).
+    bool broadcast = false;
+    if (!same_shape(skip, X.shape, 4)) {
+        const int64_t nc[2] = {d.N, d.C}, n11c[4] = {d.N, 1, 1, d.C};
+        if (!same_shape(skip, nc, 2) && !same_shape(skip, n11c, 4))
+            return fail(SN_ERR_SHAPE, "%s: skip must have X's shape %s, or %s or %s; got %s", op,
+                        shape_str(X).c_str(), shape_str(nc, 2).c_str(), shape_str(n11c, 4).c_str(),
+                        shape_str(skip).c_str());
+        broadcast = true;
+    }
+
+    SN_TRY(check_epsilon(op, epsilon));
     if (activation != 0 && activation != 1)
-        return fail(SN_ERR_ATTR, "skip_group_norm: activation must be 0 (none) or 1 (SiLU), got %d",
+        return fail(SN_ERR_ATTR, "%s: activation must be 0 (none) or 1 (SiLU), got %d", op,
                     int(activation));
-    const int64_t numel = N * C * H * W;
-    if (!gamma || !beta) return fail(SN_ERR_NULL, "skip_group_norm: gamma and beta are required");
-    if (numel > 0 && (!X || !skip || !Y))
-        return fail(SN_ERR_NULL, "skip_group_norm: X, skip and Y are required");
+    for (const Tensor* t : {&X, &gamma, &beta, &skip, &bias, &Y, &S}) SN_TRY(expect_data(op, *t));
+
+    const int64_t numel = X.numel;
     size_t need = 0;
     if (numel > 0)
-        need = sn::sgn_workspace_bytes(T == SN_F32 ? 0 : 1, N, C, H, W, groups, channels_last != 0);
+        need = sn::sgn_workspace_bytes(kernel_dtype(T), d.N, d.C, d.H, d.W, groups, channels_last != 0);
     if (noalloc) {
         if (need > sn::kStaticScratchBytes)
             return fail(SN_ERR_WORKSPACE,
@@ -287,14 +380,8 @@ sn_status group_norm(const char* op, sn_dtype T, sn_dtype M, int64_t N, int64_t 
             return fail(SN_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", op);
     }
 
-    const size_t es = elem_size(T), ms = elem_size(M);
-    const size_t tb = size_t(numel) * es;
-    const size_t skip_bytes = skip_broadcast ? size_t(N * C) * es : tb;
-    const Span ins[] = {span_of("X", X, tb), span_of("skip", skip, skip_bytes),
-                        span_of("bias", bias, size_t(C) * es),
-                        span_of("gamma", gamma, size_t(C) * ms), span_of("beta", beta, size_t(C) * ms)};
-    const Span outs[] = {span_of("Y", Y, tb), span_of("S", S, tb),
-                         span_of("workspace", workspace, need)};
+    const Span ins[] = {span_of(X), span_of(skip), span_of(bias), span_of(gamma), span_of(beta)};
+    const Span outs[] = {span_of(Y), span_of(S), span_of("workspace", workspace, need)};
     SN_TRY(check_alias(outs, 3, ins, 5));
     if (noalloc && need > 0) {
         if (hipError_t e = sn::static_scratch(&workspace); e != hipSuccess)
@@ -303,24 +390,24 @@ sn_status group_norm(const char* op, sn_dtype T, sn_dtype M, int64_t N, int64_t 
     }
 
     sn::SgnArgs a;
-    a.dtype = T == SN_F32 ? 0 : 1;
-    a.param_dtype = M == SN_F32 ? 0 : 1;
-    a.N = N;
-    a.C = C;
-    a.H = H;
-    a.W = W;
+    a.dtype = kernel_dtype(T);
+    a.param_dtype = kernel_dtype(M);
+    a.N = d.N;
+    a.C = d.C;
+    a.H = d.H;
+    a.W = d.W;
     a.groups = groups;
     a.channels_last = channels_last != 0;
     a.activation = activation;
-    a.X = X;
-    a.gamma = gamma;
-    a.beta = beta;
-    a.skip = skip;
-    a.bias = bias;
-    a.skip_broadcast = skip_broadcast != 0;
+    a.X = X.data;
+    a.gamma = gamma.data;
+    a.beta = beta.data;
+    a.skip = skip.data;
+    a.bias = bias.present ? bias.data : nullptr;
+    a.skip_broadcast = broadcast;
     a.epsilon = epsilon;
-    a.Y = Y;
-    a.S = S;
+    a.Y = Y.data;
+    a.S = S.present ? S.data : nullptr;
     a.workspace = workspace;
     a.tag = g_tag.fetch_add(2) | 1;  // odd, never 0
     a.exchange_timeout_ticks = g_exchange_timeout_us.load() * 100;
@@ -344,24 +431,102 @@ sn_status group_norm(const char* op, sn_dtype T, sn_dtype M, int64_t N, int64_t 
 
 extern "C" {
 
-sn_status skip_group_norm(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t H, int64_t W,
-                          const void* X, const void* gamma, const void* beta, const void* skip,
-                          int32_t skip_broadcast, const void* bias, float epsilon, int64_t groups,
-                          int32_t channels_last, int32_t activation, void* Y, void* S,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return group_norm("skip_group_norm", T, M, N, C, H, W, X, gamma, beta, skip, skip_broadcast,
-                      bias, epsilon, groups, channels_last, activation, Y, S, workspace,
-                      workspace_bytes, false, stream);
+sn_status skip_rms_norm(const sn_tensor_in* input, const sn_tensor_in* skip,
+                        const sn_tensor_in* gamma, const sn_tensor_in* bias, float epsilon,
+                        const sn_tensor_out* output, const sn_tensor_out* mean,
+                        const sn_tensor_out* inv_std_var,
+                        const sn_tensor_out* input_skip_bias_sum, hipStream_t stream) {
+    return row_norm("skip_rms_norm", false, input, skip, gamma, nullptr, bias, epsilon, output,
+                    mean, inv_std_var, input_skip_bias_sum, stream);
 }
 
-sn_status skip_group_norm_noalloc(sn_dtype T, sn_dtype M, int64_t N, int64_t C, int64_t H,
-                                  int64_t W, const void* X, const void* gamma, const void* beta,
-                                  const void* skip, int32_t skip_broadcast, const void* bias,
-                                  float epsilon, int64_t groups, int32_t channels_last,
-                                  int32_t activation, void* Y, void* S, hipStream_t stream) {
-    return group_norm("skip_group_norm_noalloc", T, M, N, C, H, W, X, gamma, beta, skip,
-                      skip_broadcast, bias, epsilon, groups, channels_last, activation, Y, S,
-                      nullptr, 0, true, stream);
+sn_status skip_layer_norm(const sn_tensor_in* input, const sn_tensor_in* skip,
+                          const sn_tensor_in* gamma, const sn_tensor_in* beta,
+                          const sn_tensor_in* bias, float epsilon, const sn_tensor_out* output,
+                          const sn_tensor_out* mean, const sn_tensor_out* inv_std_var,
+                          const sn_tensor_out* input_skip_bias_sum, hipStream_t stream) {
+    return row_norm("skip_layer_norm", true, input, skip, gamma, beta, bias, epsilon, output, mean,
+                    inv_std_var, input_skip_bias_sum, stream);
+}
+
+sn_status gated_rms_norm(const sn_tensor_in* X_d, const sn_tensor_in* scale_d,
+                         const sn_tensor_in* gate_d, float epsilon, const sn_tensor_out* Y_d,
+                         hipStream_t stream) {
+    const char* op = "gated_rms_norm";
+    Tensor X, scale, gate, Y;
+    SN_TRY(read_tensor(op, "X", X_d, true, &X));
+    SN_TRY(read_tensor(op, "scale", scale_d, true, &scale));
+    SN_TRY(read_tensor(op, "gate", gate_d, true, &gate));
+    SN_TRY(read_tensor(op, "Y", Y_d, true, &Y));
+
+    const sn_dtype T = X.dtype;
+    SN_TRY(check_dtype(T, op, "X"));
+    for (const Tensor* t : {&scale, &gate, &Y}) SN_TRY(expect_dtype(op, *t, T, "X's type"));
+
+    if (X.rank < 1) return fail(SN_ERR_SHAPE, "%s: X must have rank >= 1", op);
+    // scale: a vector in any spelling -- at most one extent differs from 1.
+    int non_unit = 0;
+    for (int i = 0; i < scale.rank; ++i) non_unit += scale.shape[i] != 1;
+    if (scale.rank < 1 || non_unit > 1)
+        return fail(SN_ERR_SHAPE, "%s: scale must be a vector ((C), (1, C), (C, 1), ...), got %s", op,
+                    shape_str(scale).c_str());
+    const int64_t span = scale.numel;
+    if (span < 1 || span > kMaxRowElems)
+        return fail(SN_ERR_SHAPE, "%s: the span C = numel(scale) must be in 1..2^30, got %lld", op,
+                    (long long)span);
+    if (X.numel % span != 0)
+        return fail(SN_ERR_SHAPE, "%s: numel(X) = %lld is not a multiple of the span C = %lld", op,
+                    (long long)X.numel, (long long)span);
+    if (X.numel / span > kMaxRows) return fail(SN_ERR_SHAPE, "%s: more than 2^31 - 1 rows", op);
+    SN_TRY(expect_shape(op, gate, X.shape, X.rank, "X's shape"));
+    SN_TRY(expect_shape(op, Y, X.shape, X.rank, "X's shape"));
+
+    SN_TRY(check_epsilon(op, epsilon));
+    for (const Tensor* t : {&X, &scale, &gate, &Y}) SN_TRY(expect_data(op, *t));
+
+    const Span ins[] = {span_of(X), span_of(gate), span_of(scale)};
+    const Span outs[] = {span_of(Y)};
+    SN_TRY(check_alias(outs, 1, ins, 3));
+
+    sn::GatedArgs a{kernel_dtype(T), X.numel / span, span, X.data, scale.data, gate.data, epsilon, Y.data};
+    const char* route = "";
+    return finish_launch(sn::launch_gated(a, current_route(), stream, &route), route, op);
+}
+
+sn_status skip_group_norm_workspace_size(const sn_tensor_in* X_d, int64_t groups,
+                                         int32_t channels_last, size_t* bytes) {
+    const char* op = "skip_group_norm_workspace_size";
+    if (!bytes) return fail(SN_ERR_NULL, "%s: bytes is NULL", op);
+    Tensor X;
+    SN_TRY(read_tensor(op, "X", X_d, true, &X));
+    SN_TRY(check_dtype(X.dtype, op, "X"));
+    Nchw d;
+    SN_TRY(sgn_dims(op, X, channels_last, &d));
+    SN_TRY(check_sgn_geometry(op, X.dtype, d.N, d.C, d.H, d.W, groups));
+    *bytes = X.numel == 0 ? 0
+                          : sn::sgn_workspace_bytes(kernel_dtype(X.dtype), d.N, d.C, d.H, d.W, groups,
+                                                    channels_last != 0);
+    return ok();
+}
+
+sn_status skip_group_norm(const sn_tensor_in* X, const sn_tensor_in* gamma,
+                          const sn_tensor_in* beta, const sn_tensor_in* skip,
+                          const sn_tensor_in* bias, float epsilon, int64_t groups,
+                          int32_t channels_last, int32_t activation, const sn_tensor_out* Y,
+                          const sn_tensor_out* S, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    return group_norm("skip_group_norm", X, gamma, beta, skip, bias, epsilon, groups,
+                      channels_last, activation, Y, S, workspace, workspace_bytes, false, stream);
+}
+
+sn_status skip_group_norm_noalloc(const sn_tensor_in* X, const sn_tensor_in* gamma,
+                                  const sn_tensor_in* beta, const sn_tensor_in* skip,
+                                  const sn_tensor_in* bias, float epsilon, int64_t groups,
+                                  int32_t channels_last, int32_t activation,
+                                  const sn_tensor_out* Y, const sn_tensor_out* S,
+                                  hipStream_t stream) {
+    return group_norm("skip_group_norm_noalloc", X, gamma, beta, skip, bias, epsilon, groups,
+                      channels_last, activation, Y, S, nullptr, 0, true, stream);
 }
 
 const char* skipnorm_last_error(void) { return g_error.c_str(); }

@@ -18,6 +18,17 @@ F16_REL, F16_ABS = 2e-3, 2.0 ** -14
 F32_TOL = 1e-5
 
 
+def desc(t, shape=None):
+    """The C ABI's tensor descriptor for a torch tensor (None for None), with
+    the tensor's own shape or the given one (same element count)."""
+    if t is None:
+        return None
+    from group_normalization_amd._lib import SN_F16, SN_F32, tensor_desc
+    shape = tuple(t.shape) if shape is None else tuple(shape)
+    assert int(np.prod(shape)) == t.numel()
+    return tensor_desc(t.data_ptr(), {torch.float32: SN_F32, torch.float16: SN_F16}[t.dtype], shape)
+
+
 def to_dev(a, device="cuda"):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
 

@@ -1,9 +1,11 @@
-"""The C-ABI library on the CPU: it loads, exports every symbol the header
-declares, and rejects every invalid call during host validation, before any
-HIP call.  Pointers here are fake addresses that are never dereferenced: each
-call is built to fail validation (or to have zero elements, which launches
-nothing).  Skipped when a GPU is visible, so that no bug in validation could
-ever launch a kernel on a fake address."""
+"""The C-ABI library on the CPU: it loads, exports every symbol the headers
+declare, and rejects every invalid call during host validation, before any
+HIP call: ranks, shapes and element types of every tensor descriptor against
+the operator contracts, attributes, pointers, aliasing and workspace sizes.
+Pointers here are fake addresses that are never dereferenced: each call is
+built to fail validation (or to have zero elements, which launches nothing).
+Skipped when a GPU is visible, so that no bug in validation could ever launch
+a kernel on a fake address."""
 import ctypes
 import os
 import re
@@ -14,10 +16,10 @@ import pytest
 import torch
 
 from group_normalization_amd import _lib
-from group_normalization_amd._lib import SN_BF16, SN_F16, SN_F32
+from group_normalization_amd._lib import SN_BF16, SN_F16, SN_F32, tensor_desc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "skipnorm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("skipnorm.h", "skipnorm_testing.h")]
 
 pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
                                 reason="fake-pointer validation tests run only without a GPU")
@@ -25,6 +27,8 @@ pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
 OK, NULL, DTYPE, SHAPE, ATTR, ALIAS, WORKSPACE, HIP = range(8)
 A = 0x10000000  # fake, 16-byte aligned, never dereferenced
 MB = 1 << 20
+GB = 1 << 30
+ABSENT = object()
 
 
 @pytest.fixture(scope="module")
@@ -33,12 +37,14 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text))
+    return sorted(names)
 
 
-def test_header_declares_the_abi():
+def test_headers_declare_the_abi():
     assert declared_functions() == sorted(_lib.SIGNATURES)
 
 
@@ -52,35 +58,90 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.skipnorm_abi_version() == 2
+    assert lib.skipnorm_abi_version() == 3
+
+
+def test_descriptor_layout_matches_the_header():
+    # sn_tensor_in / sn_tensor_out: pointer, enum, int32 rank, int64 shape[8].
+    assert ctypes.sizeof(_lib.TensorDesc) == 8 + 4 + 4 + 8 * 8
+    assert _lib.TensorDesc.shape.offset == 16
 
 
 def err(lib):
     return lib.skipnorm_last_error().decode()
 
 
+def T(ptr, dtype, shape):
+    return tensor_desc(ptr, dtype, shape)
+
+
+def pick(value, default):
+    """A keyword's value: ABSENT -> None (no descriptor), None -> default."""
+    if value is ABSENT:
+        return None
+    return default if value is None else value
+
+
 # ------------------------------------------------------------------ SSLN
-def ssln(lib, T=SN_F32, rows=4, hidden=8, inp=A, skip=A + MB, gamma=A + 2 * MB, bias=None,
-         eps=1e-6, out=A + 3 * MB, mean=None, inv=None, s=None):
-    return lib.skip_rms_norm(T, rows, hidden, inp, skip, gamma, bias, eps, out, mean, inv, s, None)
+def ssln(lib, dt=SN_F32, shape=(4, 8), inp=None, skip=None, gamma=None, bias=ABSENT, eps=1e-6,
+         out=None, mean=ABSENT, inv=ABSENT, s=ABSENT, layer=False, beta=ABSENT):
+    hidden = shape[-1]
+    stat = tuple(shape[:-1]) + (1,)
+    args = [pick(inp, T(A, dt, shape)), pick(skip, T(A + GB, dt, shape)),
+            pick(gamma, T(A + 2 * GB, dt, (hidden,)))]
+    if layer:
+        args.append(pick(beta, T(A + 2 * GB + MB, dt, (hidden,))) if beta is not ABSENT else None)
+    args += [pick(bias, T(A + 2 * GB + 2 * MB, dt, (hidden,))) if bias is not ABSENT else None, eps,
+             pick(out, T(A + 3 * GB, dt, shape)),
+             pick(mean, T(A + 4 * GB, SN_F32, stat)) if mean is not ABSENT else None,
+             pick(inv, T(A + 4 * GB + MB, SN_F32, stat)) if inv is not ABSENT else None,
+             pick(s, T(A + 5 * GB, dt, shape)) if s is not ABSENT else None, None]
+    return (lib.skip_layer_norm if layer else lib.skip_rms_norm)(*args)
 
 
 @pytest.mark.parametrize("kw,status,text", [
-    (dict(T=SN_BF16), DTYPE, "bfloat16"),
-    (dict(T=9), DTYPE, "unknown dtype"),
-    (dict(hidden=0), SHAPE, "hidden"),
-    (dict(rows=-1), SHAPE, "rows"),
-    (dict(hidden=(1 << 30) + 1), SHAPE, "hidden"),
+    # element types
+    (dict(dt=SN_BF16), DTYPE, "input: bfloat16"),
+    (dict(dt=9), DTYPE, "unknown dtype"),
+    (dict(skip=T(A + GB, SN_F16, (4, 8))), DTYPE, "skip must be float32"),
+    (dict(gamma=T(A + 2 * GB, SN_F16, (8,))), DTYPE, "gamma must be float32"),
+    (dict(bias=T(A + 2 * GB, SN_BF16, (8,))), DTYPE, "bias: bfloat16"),
+    (dict(out=T(A + 3 * GB, SN_F16, (4, 8))), DTYPE, "output must be float32"),
+    (dict(dt=SN_F16, inv=T(A + 4 * GB, SN_F16, (4, 1))), DTYPE, "inv_std_var must be float32"),
+    (dict(s=T(A + 5 * GB, SN_F16, (4, 8))), DTYPE, "input_skip_bias_sum must be float32"),
+    # ranks and shapes
+    (dict(shape=(32,)), SHAPE, "input must have rank 2"),
+    (dict(shape=(2, 2, 2, 8)), SHAPE, "input must have rank 2"),
+    (dict(shape=(4, 0)), SHAPE, "hidden"),
+    (dict(shape=(4, (1 << 30) + 1)), SHAPE, "hidden"),
+    (dict(inp=T(A, SN_F32, (4, -8))), SHAPE, "negative extent"),
+    (dict(inp=T(A, SN_F32, (1 << 24, 1 << 24))), SHAPE, "2^46"),
+    (dict(skip=T(A + GB, SN_F32, (4, 9))), SHAPE, "skip must have shape (4, 8)"),
+    (dict(skip=T(A + GB, SN_F32, (32,))), SHAPE, "skip must have shape (4, 8)"),
+    (dict(gamma=T(A + 2 * GB, SN_F32, (9,))), SHAPE, "gamma must have shape (8,)"),
+    (dict(gamma=T(A + 2 * GB, SN_F32, (1, 8))), SHAPE, "gamma must have shape (8,)"),
+    (dict(bias=T(A + 2 * GB, SN_F32, (4,))), SHAPE, "bias must have shape (8,)"),
+    (dict(out=T(A + 3 * GB, SN_F32, (8, 4))), SHAPE, "output must have shape (4, 8)"),
+    (dict(s=T(A + 5 * GB, SN_F32, (4, 8, 1))), SHAPE, "input_skip_bias_sum must have shape"),
+    (dict(mean=T(A + 4 * GB, SN_F32, (4,))), SHAPE, "mean must have shape (4, 1)"),
+    (dict(shape=(2, 3, 8), inv=T(A + 4 * GB, SN_F32, (6, 1))), SHAPE, "inv_std_var must have shape (2, 3, 1)"),
+    # attributes
     (dict(eps=-1e-6), ATTR, "epsilon"),
     (dict(eps=float("nan")), ATTR, "epsilon"),
     (dict(eps=float("inf")), ATTR, "epsilon"),
-    (dict(gamma=None), NULL, "gamma"),
-    (dict(inp=None), NULL, "required"),
-    (dict(out=None), NULL, "required"),
-    (dict(out=A + 8), ALIAS, "output overlaps input input"),
-    (dict(s=A + 3 * MB + 16), ALIAS, "overlaps output"),
-    (dict(mean=A + 5 * MB, inv=A + 5 * MB + 4), ALIAS, "mean overlaps output inv_std_var"),
-    (dict(bias=A + 3 * MB + 4), ALIAS, "overlaps input bias"),
+    # required tensors and pointers
+    (dict(gamma=ABSENT), NULL, "gamma is required"),
+    (dict(inp=ABSENT), NULL, "input is required"),
+    (dict(out=ABSENT), NULL, "output is required"),
+    (dict(inp=T(None, SN_F32, (4, 8))), NULL, "input has 32 elements and a NULL data pointer"),
+    (dict(gamma=T(None, SN_F32, (8,))), NULL, "gamma has 8 elements"),
+    # aliasing
+    (dict(out=T(A + 8, SN_F32, (4, 8))), ALIAS, "output output overlaps input input"),
+    (dict(s=T(A + 3 * GB + 16, SN_F32, (4, 8))), ALIAS, "overlaps output"),
+    (dict(mean=T(A + 8, SN_F32, (4, 1))), ALIAS, "output mean overlaps input input"),
+    (dict(mean=T(A + 6 * GB, SN_F32, (4, 1)), inv=T(A + 6 * GB + 4, SN_F32, (4, 1))), ALIAS,
+     "mean overlaps output inv_std_var"),
+    (dict(bias=T(A + 3 * GB + 4, SN_F32, (8,))), ALIAS, "overlaps input bias"),
 ])
 def test_ssln_rejects(lib, kw, status, text):
     assert ssln(lib, **kw) == status
@@ -88,54 +149,63 @@ def test_ssln_rejects(lib, kw, status, text):
 
 
 def test_ssln_zero_rows_is_a_no_op(lib):
-    assert ssln(lib, rows=0, inp=None, skip=None, out=None) == OK
-    assert err(lib) == ""
-    assert lib.skipnorm_last_route() == b"ssln.empty"
+    for shape in ((0, 8), (0, 5, 8), (3, 0, 8)):
+        assert ssln(lib, shape=shape, inp=T(None, SN_F32, shape), skip=T(None, SN_F32, shape),
+                    out=T(None, SN_F32, shape)) == OK
+        assert err(lib) == ""
+        assert lib.skipnorm_last_route() == b"ssln.empty"
 
 
 # ------------------------------------------------------------------ SkipLayerNorm
-def sln(lib, T=SN_F32, rows=4, hidden=8, inp=A, skip=A + MB, gamma=A + 2 * MB, beta=None, bias=None,
-        eps=1e-6, out=A + 3 * MB, mean=None, inv=None, s=None):
-    return lib.skip_layer_norm(T, rows, hidden, inp, skip, gamma, beta, bias, eps, out, mean, inv, s,
-                               None)
-
-
 @pytest.mark.parametrize("kw,status,text", [
-    (dict(T=SN_BF16), DTYPE, "bfloat16"),
-    (dict(hidden=0), SHAPE, "skip_layer_norm: need rows >= 0"),
+    (dict(dt=SN_BF16), DTYPE, "bfloat16"),
+    (dict(shape=(4, 0)), SHAPE, "skip_layer_norm: hidden"),
+    (dict(beta=T(A + 2 * GB + MB, SN_F32, (7,))), SHAPE, "beta must have shape (8,)"),
+    (dict(beta=T(A + 2 * GB + MB, SN_F16, (8,))), DTYPE, "beta must be float32"),
     (dict(eps=-1e-6), ATTR, "epsilon"),
-    (dict(gamma=None), NULL, "skip_layer_norm: gamma"),
-    (dict(inp=None), NULL, "required"),
-    (dict(beta=A + 3 * MB + 8), ALIAS, "output overlaps input beta"),
-    (dict(s=A + 3 * MB + 16), ALIAS, "overlaps output"),
+    (dict(gamma=ABSENT), NULL, "skip_layer_norm: gamma is required"),
+    (dict(inp=ABSENT), NULL, "required"),
+    (dict(beta=T(A + 3 * GB + 8, SN_F32, (8,))), ALIAS, "output output overlaps input beta"),
+    (dict(s=T(A + 3 * GB + 16, SN_F32, (4, 8))), ALIAS, "overlaps output"),
 ])
 def test_sln_rejects(lib, kw, status, text):
-    assert sln(lib, **kw) == status
+    assert ssln(lib, layer=True, **kw) == status
     assert text in err(lib)
 
 
 def test_sln_zero_rows_is_a_no_op(lib):
-    assert sln(lib, rows=0, inp=None, skip=None, out=None) == OK
+    assert ssln(lib, layer=True, shape=(0, 8), inp=T(None, SN_F32, (0, 8)), skip=T(None, SN_F32, (0, 8)),
+                out=T(None, SN_F32, (0, 8))) == OK
     assert err(lib) == ""
     assert lib.skipnorm_last_route() == b"ssln.empty"
 
 
 # ------------------------------------------------------------------ Gated
-def gated(lib, T=SN_F16, numel=64, span=16, X=A, scale=A + MB, gate=A + 2 * MB, eps=1e-5,
-          Y=A + 3 * MB):
-    return lib.gated_rms_norm(T, numel, span, X, scale, gate, eps, Y, None)
+def gated(lib, dt=SN_F16, shape=(4, 16), C=16, X=None, scale=None, gate=None, eps=1e-5, Y=None):
+    return lib.gated_rms_norm(pick(X, T(A, dt, shape)), pick(scale, T(A + GB, dt, (C,))),
+                              pick(gate, T(A + 2 * GB, dt, shape)), eps,
+                              pick(Y, T(A + 3 * GB, dt, shape)), None)
 
 
 @pytest.mark.parametrize("kw,status,text", [
-    (dict(T=SN_BF16), DTYPE, "bfloat16"),
-    (dict(numel=60, span=16), SHAPE, "not a multiple of the span"),
-    (dict(span=0), SHAPE, "span"),
-    (dict(numel=-16), SHAPE, "numel"),
+    (dict(dt=SN_BF16), DTYPE, "bfloat16"),
+    (dict(gate=T(A + 2 * GB, SN_F32, (4, 16))), DTYPE, "gate must be float16"),
+    (dict(scale=T(A + GB, SN_F32, (16,))), DTYPE, "scale must be float16"),
+    (dict(Y=T(A + 3 * GB, SN_F32, (4, 16))), DTYPE, "Y must be float16"),
+    (dict(shape=(60,), C=16), SHAPE, "not a multiple of the span"),
+    (dict(shape=()), SHAPE, "X must have rank >= 1"),
+    (dict(C=0), SHAPE, "span"),
+    (dict(scale=T(A + GB, SN_F16, (2, 8))), SHAPE, "scale must be a vector"),
+    (dict(scale=T(A + GB, SN_F16, ())), SHAPE, "scale must be a vector"),
+    (dict(X=T(A, SN_F16, (4, -16))), SHAPE, "negative extent"),
+    (dict(gate=T(A + 2 * GB, SN_F16, (64,))), SHAPE, "gate must have shape (4, 16)"),
+    (dict(Y=T(A + 3 * GB, SN_F16, (16, 4))), SHAPE, "Y must have shape (4, 16)"),
     (dict(eps=-1.0), ATTR, "epsilon"),
-    (dict(scale=None), NULL, "scale"),
-    (dict(gate=None), NULL, "required"),
-    (dict(Y=A + 2 * MB + 64), ALIAS, "Y overlaps input gate"),
-    (dict(Y=A + MB), ALIAS, "Y overlaps input scale"),
+    (dict(scale=ABSENT), NULL, "scale is required"),
+    (dict(gate=ABSENT), NULL, "gate is required"),
+    (dict(X=T(None, SN_F16, (4, 16))), NULL, "NULL data pointer"),
+    (dict(Y=T(A + 2 * GB + 64, SN_F16, (4, 16))), ALIAS, "Y overlaps input gate"),
+    (dict(Y=T(A + GB, SN_F16, (4, 16))), ALIAS, "Y overlaps input scale"),
 ])
 def test_gated_rejects(lib, kw, status, text):
     assert gated(lib, **kw) == status
@@ -143,86 +213,128 @@ def test_gated_rejects(lib, kw, status, text):
 
 
 def test_gated_zero_rows_is_a_no_op(lib):
-    assert gated(lib, numel=0, X=None, gate=None, Y=None) == OK
+    # Every spelling of a vector scale is accepted.
+    for sshape in ((16,), (1, 16), (16, 1), (1, 16, 1)):
+        e = T(None, SN_F16, (0, 16))
+        assert gated(lib, X=e, gate=e, Y=e, scale=T(A + GB, SN_F16, sshape)) == OK, err(lib)
 
 
 # ------------------------------------------------------------------ SGN
-def ws_size(lib, T=SN_F16, N=2, C=320, H=64, W=64, groups=32, cl=1):
+def x_desc(dt=SN_F16, N=2, C=32, H=4, W=4, cl=1, ptr=A):
+    return T(ptr, dt, (N, H, W, C) if cl else (N, C, H, W))
+
+
+def ws_size(lib, dt=SN_F16, N=2, C=320, H=64, W=64, groups=32, cl=1):
     out = ctypes.c_size_t(0)
-    st = lib.skip_group_norm_workspace_size(T, N, C, H, W, groups, cl, ctypes.byref(out))
+    st = lib.skip_group_norm_workspace_size(x_desc(dt, N, C, H, W, cl, ptr=None), groups, cl,
+                                            ctypes.byref(out))
     return st, out.value
 
 
-def sgn(lib, T=SN_F16, M=SN_F32, N=2, C=32, H=4, W=4, X=A, gamma=A + MB, beta=A + 2 * MB,
-        skip=A + 3 * MB, bcast=0, bias=None, eps=1e-5, groups=8, cl=1, act=0, Y=A + 4 * MB,
-        S=None, ws=A + 6 * MB, ws_bytes=1 << 20):
-    return lib.skip_group_norm(T, M, N, C, H, W, X, gamma, beta, skip, bcast, bias, eps, groups, cl,
-                               act, Y, S, ws, ws_bytes, None)
+def sgn_args(dt=SN_F16, M=SN_F32, N=2, C=32, H=4, W=4, cl=1, X=None, gamma=None, beta=None,
+             skip=None, bias=ABSENT, eps=1e-5, groups=8, act=0, Y=None, S=ABSENT):
+    xs = (N, H, W, C) if cl else (N, C, H, W)
+    return [pick(X, T(A, dt, xs)), pick(gamma, T(A + GB, M, (C,))), pick(beta, T(A + GB + MB, M, (C,))),
+            pick(skip, T(A + 2 * GB, dt, xs)),
+            pick(bias, T(A + GB + 2 * MB, dt, (C,))) if bias is not ABSENT else None, eps, groups, cl,
+            act, pick(Y, T(A + 3 * GB, dt, xs)), pick(S, T(A + 4 * GB, dt, xs)) if S is not ABSENT else None]
+
+
+def sgn(lib, ws=A + 6 * GB, ws_bytes=1 << 20, **kw):
+    return lib.skip_group_norm(*sgn_args(**kw), ws, ws_bytes, None)
+
+
+def sgn_noalloc(lib, **kw):
+    return lib.skip_group_norm_noalloc(*sgn_args(**kw), None)
 
 
 def test_workspace_size(lib):
     st, n4 = ws_size(lib)
     assert st == OK and n4 > 0
-    st, n5 = ws_size(lib, T=SN_F32, N=4, C=1280, H=32, W=32, cl=0)
+    st, n5 = ws_size(lib, dt=SN_F32, N=4, C=1280, H=32, W=32, cl=0)
     assert st == OK and n5 > 0
     assert ws_size(lib, N=0) == (OK, 0)
     assert ws_size(lib, H=0) == (OK, 0)
     assert ws_size(lib, groups=7)[0] == ATTR
-    assert ws_size(lib, T=SN_BF16)[0] == DTYPE
-    assert lib.skip_group_norm_workspace_size(SN_F16, 1, 8, 1, 1, 2, 1, None) == NULL
+    assert ws_size(lib, dt=SN_BF16)[0] == DTYPE
+    out = ctypes.c_size_t(0)
+    assert lib.skip_group_norm_workspace_size(T(None, SN_F16, (1, 8, 8)), 2, 1, ctypes.byref(out)) == SHAPE
+    assert "X must have rank 4" in err(lib)
+    assert lib.skip_group_norm_workspace_size(None, 2, 1, ctypes.byref(out)) == NULL
+    assert lib.skip_group_norm_workspace_size(x_desc(), 2, 1, None) == NULL
 
 
-@pytest.mark.parametrize("kw,status,text", [
-    (dict(T=SN_BF16), DTYPE, "bfloat16"),
-    (dict(M=SN_BF16), DTYPE, "gamma/beta"),
+SGN_REJECTS = [
+    # element types
+    (dict(dt=SN_BF16), DTYPE, "X: bfloat16"),
+    (dict(M=SN_BF16), DTYPE, "gamma: bfloat16"),
+    (dict(beta=T(A + GB + MB, SN_F16, (32,))), DTYPE, "beta must be float32 (gamma's type)"),
+    (dict(skip=T(A + 2 * GB, SN_F32, (2, 4, 4, 32))), DTYPE, "skip must be float16"),
+    (dict(bias=T(A + GB + 2 * MB, SN_F32, (32,))), DTYPE, "bias must be float16"),
+    (dict(S=T(A + 4 * GB, SN_F32, (2, 4, 4, 32))), DTYPE, "S must be float16"),
+    # ranks and shapes
+    (dict(X=T(A, SN_F16, (2, 16, 32))), SHAPE, "X must have rank 4"),
+    (dict(C=0, groups=1), SHAPE, "C >= 1"),
+    (dict(X=T(A, SN_F16, (-2, 4, 4, 32))), SHAPE, "negative extent"),
+    (dict(C=1 << 12, H=1 << 10, W=1 << 9, groups=1), SHAPE, "2^30"),
+    (dict(gamma=T(A + GB, SN_F32, (16,))), SHAPE, "gamma must have shape (32,)"),
+    (dict(beta=T(A + GB + MB, SN_F32, (1, 32))), SHAPE, "beta must have shape (32,)"),
+    (dict(bias=T(A + GB + 2 * MB, SN_F16, (31,))), SHAPE, "bias must have shape (32,)"),
+    (dict(Y=T(A + 3 * GB, SN_F16, (2, 32, 4, 4))), SHAPE, "Y must have shape (2, 4, 4, 32)"),
+    (dict(skip=T(A + 2 * GB, SN_F16, (2, 33))), SHAPE, "skip must have X's shape"),
+    (dict(skip=T(A + 2 * GB, SN_F16, (2, 32, 1, 1))), SHAPE, "skip must have X's shape"),
+    (dict(skip=T(A + 2 * GB, SN_F16, (1, 32))), SHAPE, "skip must have X's shape"),
+    (dict(skip=T(A + 2 * GB, SN_F16, (64,))), SHAPE, "skip must have X's shape"),
+    # attributes
     (dict(groups=7), ATTR, "divide C"),
     (dict(groups=0), ATTR, "groups"),
     (dict(act=2), ATTR, "activation"),
     (dict(act=-1), ATTR, "activation"),
     (dict(eps=-1e-5), ATTR, "epsilon"),
-    (dict(C=0), SHAPE, "C >= 1"),
-    (dict(N=-1), SHAPE, "N, H, W"),
-    (dict(C=1 << 12, H=1 << 10, W=1 << 9, groups=1), SHAPE, "2^30"),
-    (dict(gamma=None), NULL, "gamma and beta"),
-    (dict(skip=None), NULL, "required"),
-    (dict(Y=None), NULL, "required"),
+    # required tensors and pointers
+    (dict(gamma=ABSENT), NULL, "gamma is required"),
+    (dict(beta=ABSENT), NULL, "beta is required"),
+    (dict(skip=ABSENT), NULL, "skip is required"),
+    (dict(Y=ABSENT), NULL, "Y is required"),
+    (dict(X=T(None, SN_F16, (2, 4, 4, 32))), NULL, "X has 1024 elements and a NULL data pointer"),
+    # aliasing
+    (dict(Y=T(A + 64, SN_F16, (2, 4, 4, 32))), ALIAS, "Y overlaps input X"),
+    (dict(S=T(A + 3 * GB + 2, SN_F16, (2, 4, 4, 32))), ALIAS, "Y overlaps output S"),
+    (dict(bias=T(A + 3 * GB, SN_F16, (32,))), ALIAS, "Y overlaps input bias"),
+]
+
+
+@pytest.mark.parametrize("kw,status,text", SGN_REJECTS + [
     (dict(ws=None), WORKSPACE, "NULL"),
     (dict(ws_bytes=16), WORKSPACE, "required"),
-    (dict(ws=A + 6 * MB + 4), WORKSPACE, "aligned"),
-    (dict(Y=A + 64), ALIAS, "Y overlaps input X"),
-    (dict(S=A + 4 * MB + 2), ALIAS, "Y overlaps output S"),
-    (dict(ws=A + 3 * MB), ALIAS, "workspace overlaps input skip"),
-    (dict(bias=A + 4 * MB), ALIAS, "Y overlaps input bias"),
+    (dict(ws=A + 6 * GB + 4), WORKSPACE, "aligned"),
+    (dict(ws=A + 2 * GB), ALIAS, "workspace overlaps input skip"),
 ])
 def test_sgn_rejects(lib, kw, status, text):
     assert sgn(lib, **kw) == status
     assert text in err(lib)
 
 
+@pytest.mark.parametrize("skip_shape", [(2, 32), (2, 1, 1, 32)])
+@pytest.mark.parametrize("cl", [0, 1])
+def test_sgn_accepts_broadcast_skip_spellings(lib, skip_shape, cl):
+    # Both broadcast spellings pass shape validation in both layouts: the
+    # call gets as far as the (deliberately missing) workspace.
+    assert sgn(lib, cl=cl, skip=T(A + 2 * GB, SN_F16, skip_shape), ws=None) == WORKSPACE
+    assert "workspace of" in err(lib)
+
+
 def test_sgn_empty_is_a_no_op(lib):
-    assert sgn(lib, N=0, X=None, skip=None, Y=None, ws=None, ws_bytes=0) == OK
-    assert sgn(lib, H=0, X=None, skip=None, Y=None, ws=None, ws_bytes=0) == OK
+    for dims in (dict(N=0), dict(H=0)):
+        xs = x_desc(ptr=None, **dims)
+        assert sgn(lib, X=xs, skip=xs, Y=xs, ws=None, ws_bytes=0, **dims) == OK, err(lib)
 
 
-def sgn_noalloc(lib, T=SN_F16, M=SN_F32, N=2, C=32, H=4, W=4, X=A, gamma=A + MB, beta=A + 2 * MB,
-                skip=A + 3 * MB, bcast=0, bias=None, eps=1e-5, groups=8, cl=1, act=0, Y=A + 4 * MB,
-                S=None):
-    return lib.skip_group_norm_noalloc(T, M, N, C, H, W, X, gamma, beta, skip, bcast, bias, eps,
-                                       groups, cl, act, Y, S, None)
-
-
-@pytest.mark.parametrize("kw,status,text", [
-    (dict(T=SN_BF16), DTYPE, "bfloat16"),
-    (dict(groups=7), ATTR, "divide C"),
-    (dict(act=2), ATTR, "activation"),
-    (dict(gamma=None), NULL, "gamma and beta"),
-    (dict(Y=None), NULL, "required"),
-    (dict(Y=A + 64), ALIAS, "Y overlaps input X"),
+@pytest.mark.parametrize("kw,status,text", SGN_REJECTS[:10] + [
     # 32 x 1280 x 512 x 512 float32 NCHW needs ~42 MB of partials: more than
     # the static scratch's 8 MiB.
-    (dict(T=SN_F32, N=32, C=1280, H=512, W=512, groups=32, cl=0, gamma=A + (1 << 36),
-          beta=A + (1 << 36) + MB, skip=A + (1 << 37), bcast=1, Y=A + (1 << 38)),
-     WORKSPACE, "static scratch holds 8388608"),
+    (dict(dt=SN_F32, N=32, C=1280, H=512, W=512, groups=32, cl=0,
+          skip=T(A + 2 * GB, SN_F32, (32, 1280))), WORKSPACE, "static scratch holds 8388608"),
 ])
 def test_sgn_noalloc_rejects(lib, kw, status, text):
     assert sgn_noalloc(lib, **kw) == status
@@ -230,8 +342,9 @@ def test_sgn_noalloc_rejects(lib, kw, status, text):
 
 
 def test_sgn_noalloc_empty_is_a_no_op(lib):
-    assert sgn_noalloc(lib, N=0, X=None, skip=None, Y=None) == OK
-    assert sgn_noalloc(lib, H=0, X=None, skip=None, Y=None) == OK
+    for dims in (dict(N=0), dict(H=0)):
+        xs = x_desc(ptr=None, **dims)
+        assert sgn_noalloc(lib, X=xs, skip=xs, Y=xs, **dims) == OK, err(lib)
 
 
 # ------------------------------------------------------------------ hooks
@@ -245,7 +358,7 @@ def test_force_route_round_trip(lib):
 
 
 def test_last_error_is_per_thread(lib):
-    assert ssln(lib, hidden=0) == SHAPE
+    assert ssln(lib, shape=(4, 0)) == SHAPE
     seen = {}
 
     def other():

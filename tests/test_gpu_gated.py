@@ -6,7 +6,7 @@ import torch
 import group_normalization_amd as gn
 import oracle
 from group_normalization_amd import workloads
-from parity import assert_bitwise, assert_close, to_dev, to_host
+from parity import assert_bitwise, assert_close, desc, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -202,11 +202,9 @@ def test_tile_route_stays_in_bounds(C, dt):
     d["gate"].copy_(torch.from_numpy(x["gate"]))
     arena = torch.full((rows * C + 2 * pad,), 3.0, dtype=tdt, device="cuda")
     Y = arena[pad: pad + rows * C]
-    code = 1 if dt == F16 else 0
     for i in range(2):
-        ck(lib().gated_rms_norm(code, rows * C, C, d["X"].data_ptr(), d["scale"].data_ptr(),
-                                d["gate"].data_ptr(), 1e-5, Y.data_ptr(),
-                                torch.cuda.current_stream().cuda_stream))
+        ck(lib().gated_rms_norm(desc(d["X"]), desc(d["scale"]), desc(d["gate"]), 1e-5,
+                                desc(Y, (rows, C)), torch.cuda.current_stream().cuda_stream))
         torch.cuda.synchronize()
         assert gn.last_route().startswith("gated.tile")
         if i == 0:
@@ -246,11 +244,10 @@ def test_flat_route(C, dt, off):
     _, G = placed(x["gate"])
     arena, Y = placed(x["X"], fill=3.0)
     S = to_dev(x["scale"])
-    code = 1 if dt == F16 else 0
     for i in range(2):
         with gn.force_route("flat"):
-            ck(lib().gated_rms_norm(code, rows * C, C, X.data_ptr(), S.data_ptr(), G.data_ptr(), 1e-5,
-                                    Y.data_ptr(), torch.cuda.current_stream().cuda_stream))
+            ck(lib().gated_rms_norm(desc(X), desc(S), desc(G), 1e-5, desc(Y),
+                                    torch.cuda.current_stream().cuda_stream))
         torch.cuda.synchronize()
         assert gn.last_route() == "gated.flat.vec16"
         if i == 0:
@@ -317,9 +314,8 @@ def test_deterministic_and_in_bounds():
     arena = torch.full((rows * C + 2 * pad,), 3.0, dtype=torch.float16, device="cuda")
     Y = arena[pad: pad + rows * C]
     for _ in range(2):
-        ck(lib().gated_rms_norm(1, rows * C, C, d["X"].data_ptr(), d["scale"].data_ptr(),
-                                d["gate"].data_ptr(), 1e-5, Y.data_ptr(),
-                                torch.cuda.current_stream().cuda_stream))
+        ck(lib().gated_rms_norm(desc(d["X"]), desc(d["scale"]), desc(d["gate"]), 1e-5,
+                                desc(Y, (rows, C)), torch.cuda.current_stream().cuda_stream))
         torch.cuda.synchronize()
         if _ == 0:
             first = to_host(Y).copy()

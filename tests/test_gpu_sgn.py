@@ -8,7 +8,7 @@ import torch
 import group_normalization_amd as gn
 import oracle
 from group_normalization_amd import workloads
-from parity import assert_bitwise, assert_close, to_dev, to_host
+from parity import assert_bitwise, assert_close, desc, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -349,9 +349,9 @@ def test_deterministic_and_in_bounds():
     ws = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
     results = []
     for _ in range(2):
-        ck(lib().skip_group_norm(1, 0, N, C, H, W, d["X"].data_ptr(), d["gamma"].data_ptr(),
-                                 d["beta"].data_ptr(), d["skip"].data_ptr(), 0, d["bias"].data_ptr(),
-                                 1e-5, 32, 1, 1, Y.data_ptr(), S.data_ptr(), ws.data_ptr(), need,
+        ck(lib().skip_group_norm(desc(d["X"]), desc(d["gamma"]), desc(d["beta"]), desc(d["skip"]),
+                                 desc(d["bias"]), 1e-5, 32, 1, 1, desc(Y, (N, H, W, C)),
+                                 desc(S, (N, H, W, C)), ws.data_ptr(), need,
                                  torch.cuda.current_stream().cuda_stream))
         torch.cuda.synchronize()
         results.append((to_host(Y).copy(), to_host(S).copy()))
@@ -439,12 +439,12 @@ def test_nchw_phased_groups(dt, N, C, H, W, groups, offset, bc):
     d = {k: to_dev(x[k]) for k in ("gamma", "beta", "bias")}
     ws = torch.empty(gn.skip_group_norm_workspace_size(views["X"].view(N, C, H, W), groups, 0),
                      dtype=torch.uint8, device="cuda")
-    code = 1 if dt == F16 else 0
     for _ in range(2):
-        ck(lib().skip_group_norm(code, 0, N, C, H, W, views["X"].data_ptr(), d["gamma"].data_ptr(),
-                                 d["beta"].data_ptr(), skip.data_ptr(), 1 if bc else 0, d["bias"].data_ptr(),
-                                 1e-5, groups, 0, 1, views["Y"].data_ptr(), views["S"].data_ptr(),
-                                 ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream))
+        xs = (N, C, H, W)
+        ck(lib().skip_group_norm(desc(views["X"], xs), desc(d["gamma"]), desc(d["beta"]),
+                                 desc(skip) if bc else desc(skip, xs), desc(d["bias"]), 1e-5, groups, 0, 1,
+                                 desc(views["Y"], xs), desc(views["S"], xs), ws.data_ptr(), ws.numel(),
+                                 torch.cuda.current_stream().cuda_stream))
         assert gn.last_route() == "sgn.cluster.nchw.phase"
         torch.cuda.synchronize()
         ref_y, ref_s = oracle.skip_group_norm(x["X"], x["gamma"], x["beta"], x["skip"], x["bias"],

@@ -8,7 +8,7 @@ import torch
 import group_normalization_amd as gn
 import oracle
 from group_normalization_amd import workloads
-from parity import assert_bitwise, assert_close, to_dev, to_host
+from parity import assert_bitwise, assert_close, desc, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -239,10 +239,9 @@ def test_outputs_leave_neighbouring_memory_untouched():
     stats = torch.full((2 * (rows + 2 * pad),), -7.0, dtype=torch.float32, device="cuda")
     mean = stats[pad: pad + rows]
     inv = stats[rows + 3 * pad: rows + 3 * pad + rows]
-    ck(lib().skip_rms_norm(1, rows, hidden, d["input"].data_ptr(), d["skip"].data_ptr(),
-                           d["gamma"].data_ptr(), d["bias"].data_ptr(), 1e-6, slots[0].data_ptr(),
-                           mean.data_ptr(), inv.data_ptr(), slots[1].data_ptr(),
-                           torch.cuda.current_stream().cuda_stream))
+    ck(lib().skip_rms_norm(desc(d["input"]), desc(d["skip"]), desc(d["gamma"]), desc(d["bias"]), 1e-6,
+                           desc(slots[0], (rows, hidden)), desc(mean, (rows, 1)), desc(inv, (rows, 1)),
+                           desc(slots[1], (rows, hidden)), torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     ref = oracle.skip_rms_norm(x["input"], x["skip"], x["gamma"], x["bias"], 1e-6,
                                want_mean=True, want_inv_std_var=True, want_sum=True)
@@ -290,20 +289,20 @@ def test_phased_rows(dt, hidden, offset, center):
     mean = torch.empty(rows, dtype=torch.float32, device="cuda")
     inv = torch.empty(rows, dtype=torch.float32, device="cuda")
     d = {k: to_dev(x[k]) for k in ("gamma", "bias", "beta") if x.get(k) is not None}
-    code = 1 if dt == F16 else 0
+    shp = (rows, hidden)
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(2):
         if center:
-            ck(lib().skip_layer_norm(code, rows, hidden, views["input"].data_ptr(), views["skip"].data_ptr(),
-                                     d["gamma"].data_ptr(), d["beta"].data_ptr(), d["bias"].data_ptr(), 1e-5,
-                                     views["output"].data_ptr(), mean.data_ptr(), inv.data_ptr(),
-                                     views["sum"].data_ptr(), stream))
+            ck(lib().skip_layer_norm(desc(views["input"], shp), desc(views["skip"], shp), desc(d["gamma"]),
+                                     desc(d["beta"]), desc(d["bias"]), 1e-5, desc(views["output"], shp),
+                                     desc(mean, (rows, 1)), desc(inv, (rows, 1)), desc(views["sum"], shp),
+                                     stream))
             ref = oracle.skip_layer_norm(x["input"], x["skip"], x["gamma"], x["beta"], x["bias"], 1e-5,
                                          want_mean=True, want_inv_std_var=True, want_sum=True)
         else:
-            ck(lib().skip_rms_norm(code, rows, hidden, views["input"].data_ptr(), views["skip"].data_ptr(),
-                                   d["gamma"].data_ptr(), d["bias"].data_ptr(), 1e-5, views["output"].data_ptr(),
-                                   mean.data_ptr(), inv.data_ptr(), views["sum"].data_ptr(), stream))
+            ck(lib().skip_rms_norm(desc(views["input"], shp), desc(views["skip"], shp), desc(d["gamma"]),
+                                   desc(d["bias"]), 1e-5, desc(views["output"], shp), desc(mean, (rows, 1)),
+                                   desc(inv, (rows, 1)), desc(views["sum"], shp), stream))
             ref = oracle.skip_rms_norm(x["input"], x["skip"], x["gamma"], x["bias"], 1e-5,
                                        want_mean=True, want_inv_std_var=True, want_sum=True)
         assert gn.last_route() == "ssln.phase.vec16"

@@ -16,7 +16,7 @@ import torch
 import group_normalization_amd as gn
 import oracle
 from group_normalization_amd import _lib, workloads
-from parity import assert_bitwise, assert_close, to_dev, to_host
+from parity import assert_bitwise, assert_close, desc, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -24,29 +24,17 @@ SCRATCH_BYTES = 8 << 20
 WORKSPACE = 6
 
 
-def vp(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
-
-
-def code(t):
-    return {torch.float32: _lib.SN_F32, torch.float16: _lib.SN_F16}[t.dtype]
-
-
 def noalloc_call(x, a, want_sum):
     """skip_group_norm_noalloc through ctypes; outputs allocated here, the
     library allocates nothing."""
     X = x["X"]
-    cl = a["channels_last"]
-    N, C = X.shape[0], (X.shape[3] if cl else X.shape[1])
-    H, W = (X.shape[1], X.shape[2]) if cl else (X.shape[2], X.shape[3])
-    bcast = 0 if tuple(x["skip"].shape) == tuple(X.shape) else 1
     Y = torch.empty_like(X)
     S = torch.empty_like(X) if want_sum else None
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     st = _lib.lib().skip_group_norm_noalloc(
-        code(X), code(x["gamma"]), N, C, H, W, vp(X), vp(x["gamma"]), vp(x["beta"]), vp(x["skip"]),
-        bcast, vp(x.get("bias")), float(a["epsilon"]), int(a["groups"]), 1 if cl else 0,
-        int(a["activation"]), vp(Y), vp(S), stream)
+        desc(X), desc(x["gamma"]), desc(x["beta"]), desc(x["skip"]), desc(x.get("bias")),
+        float(a["epsilon"]), int(a["groups"]), 1 if a["channels_last"] else 0, int(a["activation"]),
+        desc(Y), desc(S), stream)
     _lib.check(st)
     return Y, S
 
@@ -120,15 +108,19 @@ def test_noalloc_split_routes(route):
 def test_noalloc_rejects_shapes_beyond_the_scratch():
     # NCHW float32 32 x 1280 x 512 x 512 with 32 groups needs ~42 MB of
     # partials; the call is rejected during validation, before anything is
-    # enqueued (the small tensors passed are never dereferenced).
-    dims = (32, 1280, 512, 512)
+    # enqueued (the small tensors behind the descriptors are never touched).
+    xs = (32, 1280, 512, 512)
     need = ctypes.c_size_t()
-    _lib.check(_lib.lib().skip_group_norm_workspace_size(_lib.SN_F32, *dims, 32, 0, ctypes.byref(need)))
+    _lib.check(_lib.lib().skip_group_norm_workspace_size(_lib.tensor_desc(None, _lib.SN_F32, xs), 32, 0,
+                                                         ctypes.byref(need)))
     assert need.value > SCRATCH_BYTES
     x = torch.empty(16, device="cuda")
     y = torch.empty(16, device="cuda")
-    st = _lib.lib().skip_group_norm_noalloc(_lib.SN_F32, _lib.SN_F32, *dims, vp(x), vp(x), vp(x), vp(x), 1,
-                                            None, 1e-5, 32, 0, 0, vp(y), None, None)
+    big = _lib.tensor_desc(x.data_ptr(), _lib.SN_F32, xs)
+    out = _lib.tensor_desc(y.data_ptr(), _lib.SN_F32, xs)
+    par = _lib.tensor_desc(x.data_ptr(), _lib.SN_F32, (1280,))
+    skp = _lib.tensor_desc(x.data_ptr(), _lib.SN_F32, (32, 1280))
+    st = _lib.lib().skip_group_norm_noalloc(big, par, par, skp, None, 1e-5, 32, 0, 0, out, None, None)
     assert st == WORKSPACE
     assert "static scratch" in _lib.lib().skipnorm_last_error().decode()
 
