@@ -38,6 +38,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))  # workloads: the seeded input generator
 
 METRIC = "achieved HBM GB/s (and % of MI355X peak) per norm op, fp16 large shapes"
 PEAK_GBPS = 8000.0  # MI355X HBM3E
@@ -193,7 +194,7 @@ def cpu_baseline(budget_s=14.0):
     large workloads, as many as fit an equal share of what remains of the
     budget."""
     import oracle
-    from group_normalization_amd import workloads
+    import workloads
 
     total_bytes, total_s, parts, per_op = 0, 0.0, [], {}
     order = sorted(STEP_WORKLOADS, key=lambda n: workloads.WORKLOADS[n].op != "skip_group_norm")
@@ -266,7 +267,7 @@ def config_table(args):
     module docstring)."""
     import torch
     import group_normalization_amd as gn
-    from group_normalization_amd import workloads
+    import workloads
 
     torch.cuda.set_device(0)
     hev = HipEvents()
@@ -379,7 +380,7 @@ def main():
 
     import torch
     import group_normalization_amd as gn
-    from group_normalization_amd import workloads
+    import workloads
 
     torch.cuda.set_device(0)
     log("generating inputs")

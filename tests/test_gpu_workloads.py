@@ -16,7 +16,7 @@ import pytest
 
 import group_normalization_amd as gn
 import oracle
-from group_normalization_amd import workloads
+import workloads
 from parity import assert_bitwise, assert_close, to_dev, to_host
 
 pytestmark = pytest.mark.gpu

@@ -15,7 +15,8 @@ import torch
 
 import group_normalization_amd as gn
 import oracle
-from group_normalization_amd import _lib, workloads
+import workloads
+from group_normalization_amd import _lib
 from parity import assert_bitwise, assert_close, desc, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
