@@ -36,7 +36,12 @@ namespace {
 // pixel rows and share their boundary cache lines, run under one L2.  The
 // data accesses are ordinary (cached) ones so that this L2 merges the
 // blocks' pieces of a line: with nontemporal stores the partial lines
-// reached memory separately (1.3-1.5x the written bytes, measured).
+// reached memory separately (1.3-1.5x the written bytes, measured).  Two
+// orders (NhwcLayout): slice-major, where the channel blocks of eight
+// (image, slice) units follow one another, so that what starts together
+// reads contiguous pixel rows; and cluster-major, where a cluster's slices
+// are consecutive ids, for grids whose clusters would otherwise spread
+// over more ids than the device holds at once.
 template <typename T, typename M>
 struct NhwcClusterArgs {
     const T *X, *skip, *bias;
@@ -49,7 +54,11 @@ struct NhwcClusterArgs {
     int Cv, cpg;       // vectors per pixel, channels per group
     int CBv, NCB, CBg; // vectors per channel block, blocks per pixel, groups per block
     int P, sw_log;     // pixel lanes per workgroup (256 / CBv); log2 of the chunks per column
-    int K, units;      // slices per image, N * K
+    int K;             // slices per image
+    int N, Kp, G;      // images; block-id layout (NhwcLayout)
+    // Invariant divisors (one multiply-high each instead of a division in
+    // the set-up every load address waits for).
+    FastDiv div_G, div_NCB, div_K, div_CBv, div_cpg, div_P;
     bool skip_bcast, silu;
     float eps;
 };
@@ -71,19 +80,32 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
     __shared__ int late[kNhwcMaxK];
     __shared__ int any_late;
 
-    const int bid = int(blockIdx.x);
-    const int xcd = bid & 7, rest = bid >> 3;
-    const int cb = rest % a.NCB;
-    const int u = (rest / a.NCB) * 8 + xcd;
-    if (u >= a.units) return;  // grid padding; not part of any cluster
-    const int n = u / a.K, q = u % a.K;
+    // Block id = ((item / m * NCB + cb) * G + (item % m) * Kp + j), m = G / Kp
+    // (see NhwcLayout): an item is an (image, slice) unit when Kp == 1, else
+    // an image whose slices j take Kp consecutive ids.
+    // Slice-major: G = 8, Kp = 1, item = (image, slice) unit; cluster-major:
+    // G = Kp, item = image.
+    const uint32_t bid = blockIdx.x;
+    const uint32_t rest = fastdiv(bid, a.div_G), r = bid - rest * uint32_t(a.G);
+    const uint32_t hi = fastdiv(rest, a.div_NCB);
+    const int cb = int(rest - hi * uint32_t(a.NCB));
+    int n, q;
+    if (a.Kp == 1) {  // uniform
+        const uint32_t unit = hi * 8 + r;
+        n = int(fastdiv(unit, a.div_K));
+        q = int(unit - uint32_t(n) * uint32_t(a.K));
+    } else {
+        n = int(hi);
+        q = int(r);
+    }
+    if (q >= a.K || n >= a.N) return;  // padding; not part of any cluster
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const bool active = t < a.P * a.CBv;
-    const int v = active ? t % a.CBv : 0;
-    const int pl = active ? t / a.CBv : 0;
+    const int pl = active ? int(fastdiv(uint32_t(t), a.div_CBv)) : 0;
+    const int v = active ? t - pl * a.CBv : 0;
     const int cvec = cb * a.CBv + v;  // channel vector within the pixel
-    const int glo = (v * E) / a.cpg;  // block-local group of the vector's first channel
+    const int glo = int(fastdiv(uint32_t(v * E), a.div_cpg));  // block-local group of the vector's first channel
     const int split = (glo + 1) * a.cpg - v * E;  // channels [0, split) are in glo, the rest in glo + 1
     const int ncol = 2 * a.CBv;
     const int SW = 1 << a.sw_log;
@@ -100,7 +122,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
     auto nvalid = [&](int s) {
         const int64_t len = slice_len(s);
         if (!active || len <= pl) return 0;
-        const int64_t nv = (len - pl + a.P - 1) / a.P;
+        const int64_t nv = fastdiv(uint32_t(len - pl + a.P - 1), a.div_P);  // len <= pps < 2^31
         return nv < R ? int(nv) : R;
     };
     auto vidx = [&](int s, int r) {
@@ -186,7 +208,8 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
         if (t < a.CBg) {  // group t over its columns, in channel order
             const int vf = (t * a.cpg) / E, vl = ((t + 1) * a.cpg - 1) / E;
             Moments m{0.0f, 0.0f, 0.0f};
-            for (int w = vf; w <= vl; ++w) m = merge_rcp(m, col_m[2 * w + ((w * E) / a.cpg == t ? 0 : 1)]);
+            for (int w = vf; w <= vl; ++w)
+                m = merge_rcp(m, col_m[2 * w + (int(fastdiv(uint32_t(w * E), a.div_cpg)) == t ? 0 : 1)]);
             dst[t] = m;
         }
     };
@@ -481,15 +504,42 @@ const void* nhwc_kernel_for(int E, int r, bool bcast) {
 // unfinished cluster can always become wholly resident and the launch never
 // waits on a workgroup that cannot start; beyond that, waits run into their
 // bound and slices are recomputed (correct, but far slower).
-int64_t nhwc_cluster_span(int64_t N, const NhwcPlan& p) {
-    int64_t span = 0;
-    for (int64_t n = 0; n < N; ++n) {
-        const int64_t u0 = n * p.K, u1 = n * p.K + p.K - 1;
-        const int64_t lo = ((u0 >> 3) * p.NCB) * 8 + (u0 & 7);
-        const int64_t hi = ((u1 >> 3) * p.NCB) * 8 + (u1 & 7);
-        if (hi - lo + 1 > span) span = hi - lo + 1;
+// Block-id layout: id = (v / m * NCB + cb) * G + (v % m) * Kp + j with
+// m = G / Kp, for items v with Kp ids each.
+//   slice-major (Kp = 1, G = 8): the items are the N * K (image, slice)
+//     units u = n * K + q; eight units' NCB channel blocks follow one
+//     another.  Measured faster wherever it fits (below): the workgroups
+//     that start together read contiguous pixel rows (8 x 64 x 64 x 640
+//     float16, two rounds of resident workgroups: 45 us, against 53 us
+//     cluster-major).  A cluster spans about K * NCB ids.
+//   cluster-major (G = Kp = K rounded up to a multiple of 8): the items are
+//     images, and a cluster's slices j = q take Kp consecutive ids.  A
+//     cluster spans Kp ids.
+// In both, slice q of image n sits at the same residue mod 8 in every
+// channel block.  Ids with q >= K or n >= N are padding.  The dispatcher starts workgroups in id order, so when a
+// cluster's span fits in the workgroups the device holds at once, the
+// lowest unfinished cluster can always become wholly resident and no
+// workgroup waits on one that cannot start; beyond that, waits would run
+// into their bound and recompute (correct, but far slower: one 512 x 512 x
+// 256 float16 image took 2.5 ms that way).
+struct NhwcLayout {
+    int Kp, G;
+    int64_t grid, span;
+};
+NhwcLayout nhwc_layout(int64_t N, const NhwcPlan& p, bool cluster_major) {
+    if (!cluster_major) {
+        const int64_t units = N * p.K;
+        int64_t span = 0;  // widest id range of one cluster
+        for (int64_t n = 0; n < N; ++n) {
+            const int64_t u0 = n * p.K, u1 = n * p.K + p.K - 1;
+            const int64_t lo = ((u0 >> 3) * p.NCB) * 8 + (u0 & 7);
+            const int64_t hi = ((u1 >> 3) * p.NCB) * 8 + (u1 & 7);
+            if (hi - lo + 1 > span) span = hi - lo + 1;
+        }
+        return NhwcLayout{1, 8, (units + 7) / 8 * p.NCB * 8, span};
     }
-    return span;
+    const int Kp = (p.K + 7) / 8 * 8;
+    return NhwcLayout{Kp, Kp, N * p.NCB * Kp, Kp};
 }
 
 template <typename T, typename M, int E, int R>
@@ -514,8 +564,8 @@ hipError_t launch_nhwc_cluster(const NhwcClusterArgs<T, M>& ca, int r, int64_t b
 }
 
 template <typename T, typename M>
-hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, int E, void* part,
-                             hipStream_t stream) {
+hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, const NhwcLayout& lay, int E,
+                             void* part, hipStream_t stream) {
     NhwcClusterArgs<T, M> ca;
     ca.X = static_cast<const T*>(a.X);
     ca.skip = static_cast<const T*>(a.skip);
@@ -540,11 +590,19 @@ hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, int E, void
     ca.P = plan.P;
     ca.sw_log = plan.sw_log;
     ca.K = plan.K;
-    ca.units = int(a.N * plan.K);
     ca.skip_bcast = a.skip_broadcast;
     ca.silu = a.activation == 1;
     ca.eps = a.epsilon;
-    const int64_t blocks = (a.N * plan.K + 7) / 8 * 8 * plan.NCB;
+    ca.N = int(a.N);
+    ca.Kp = lay.Kp;
+    ca.G = lay.G;
+    ca.div_G = make_fastdiv(uint32_t(lay.G));
+    ca.div_NCB = make_fastdiv(uint32_t(plan.NCB));
+    ca.div_K = make_fastdiv(uint32_t(plan.K));
+    ca.div_CBv = make_fastdiv(uint32_t(plan.CBv));
+    ca.div_cpg = make_fastdiv(uint32_t(a.C / a.groups));
+    ca.div_P = make_fastdiv(uint32_t(plan.P));
+    const int64_t blocks = lay.grid;
     constexpr int EV = VecWidth<T>::value;
     if (E == EV) return launch_nhwc_cluster<T, M, EV>(ca, plan.R, blocks, stream);
     if (E == EV / 2) return launch_nhwc_cluster<T, M, EV / 2>(ca, plan.R, blocks, stream);
@@ -575,8 +633,12 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
                               : nhwc_kernel_for<float, half_t>(E, plan.R, a.skip_broadcast))
         : (a.param_dtype == 0 ? nhwc_kernel_for<half_t, float>(E, plan.R, a.skip_broadcast)
                               : nhwc_kernel_for<half_t, half_t>(E, plan.R, a.skip_broadcast));
+    // Slice-major where each cluster's span fits in the resident
+    // workgroups, else cluster-major (whose span, at most 64, always does).
     const int64_t resident = resident_workgroups(kernel);
-    if (!kernel || nhwc_cluster_span(a.N, plan) > resident) return false;
+    if (!kernel || resident < 64) return false;
+    NhwcLayout lay = nhwc_layout(a.N, plan, false);
+    if (lay.span > resident) lay = nhwc_layout(a.N, plan, true);
     // Beyond two rounds of resident workgroups the split route measured
     // faster (10-30 %, e.g. 8 x 128 x 128 x 320 float16: 86 against 112 us)
     // where its blocks hold whole pixels; wider pixels stay here (8 x 64 x 64
@@ -584,17 +646,18 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
     const int split_e = a.dtype == 0 ? widest_vector<float>(a.C, {a.X, a.Y, a.S, a.skip, a.bias})
                                      : widest_vector<half_t>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
     const bool split_whole_pixels = split_e > 1 && a.C / split_e <= 256;
-    const int64_t grid = (a.N * plan.K + 7) / 8 * 8 * plan.NCB;
+    const int64_t grid = a.N * plan.NCB * plan.K;  // workgroups that do work
     if (split_whole_pixels && grid > 2 * resident) return false;
-    static const char* const kNames[] = {"sgn.cluster.nhwc.vec4", "sgn.cluster.nhwc.vec8",
-                                         "sgn.cluster.nhwc.vec16"};
-    *route = kNames[E * size == 16 ? 2 : E * size == 8 ? 1 : 0];
+    static const char* const kNames[2][3] = {
+        {"sgn.cluster.nhwc.vec4", "sgn.cluster.nhwc.vec8", "sgn.cluster.nhwc.vec16"},
+        {"sgn.cluster.nhwc.cmajor.vec4", "sgn.cluster.nhwc.cmajor.vec8", "sgn.cluster.nhwc.cmajor.vec16"}};
+    *route = kNames[lay.Kp > 1 ? 1 : 0][E * size == 16 ? 2 : E * size == 8 ? 1 : 0];
     if (a.dtype == 0) {
-        if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, E, part, stream);
-        else *err = launch_nhwc_typed<float, half_t>(a, plan, E, part, stream);
+        if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, lay, E, part, stream);
+        else *err = launch_nhwc_typed<float, half_t>(a, plan, lay, E, part, stream);
     } else {
-        if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, plan, E, part, stream);
-        else *err = launch_nhwc_typed<half_t, half_t>(a, plan, E, part, stream);
+        if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, plan, lay, E, part, stream);
+        else *err = launch_nhwc_typed<half_t, half_t>(a, plan, lay, E, part, stream);
     }
     return true;
 }
