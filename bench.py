@@ -24,6 +24,9 @@ every invocation is preceded by a 1 GiB copy (so it starts from a cold
 cache) and bracketed by HIP events; the oracle is timed on one thread on the
 same inputs (median of 3 runs for the small workloads, one run for the two
 large ones).  It prints one JSON object and a markdown table (stderr).
+
+``--phases`` prints per-workgroup phase timings of the single-launch
+group-norm kernels from the library's phase-trace measurement build.
 """
 from __future__ import annotations
 
@@ -185,6 +188,7 @@ class Op:
                                                   epsilon=a["epsilon"],
                                                   channels_last=a["channels_last"],
                                                   want_sum=want_sum, workspace=ws)
+            self.workspace = ws
         self.tensors = d
 
 
@@ -347,6 +351,70 @@ def config_table(args):
     print(json.dumps(out), flush=True)
 
 
+PHASES = ["loads", "reduce", "publish + S", "exchange + combine", "normalize + Y"]
+
+
+def phase_table(args):
+    """Per-workgroup phase timings of the single-launch SkipGroupNorm routes
+    on the two group-norm workloads, each invocation cold (after a 1 GiB
+    copy), from the measurement build of the library (SN_PHASE_TRACE: each
+    workgroup's leader records the 100 MHz wall clock at six phase
+    boundaries in a tail of the workspace).  Build it first with
+    `python -m group_normalization_amd.build --phase-trace`."""
+    from group_normalization_amd import _lib
+    from group_normalization_amd import build as libbuild
+
+    if not os.path.exists(libbuild.TRACE_LIB_PATH):
+        sys.exit(f"{libbuild.TRACE_LIB_PATH} is missing: run "
+                 "`python -m group_normalization_amd.build --phase-trace` first")
+    _lib.LIB_PATH = libbuild.TRACE_LIB_PATH  # before the first call loads a library
+    import torch
+    import group_normalization_amd as gn
+    import workloads
+
+    trace_bytes = 65536 * 8 * 8  # kTraceBlocks x kTraceStamps x 8 bytes
+    torch.cuda.set_device(0)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    out, lines = {}, ["| workload | route | workgroups | " + " | ".join(f"{p} us" for p in PHASES) +
+                      " | start spread us | first start to last stamp us |",
+                      "|---|---|---|" + "---|" * (len(PHASES) + 2)]
+    for name in ("sgn_f16_nhwc_2x64x64x320", "sgn_f32_nchw_4x1280x32x32"):
+        o = Op(name, torch, gn, workloads)
+        tail = o.workspace[-trace_bytes:]
+        per_call = []
+        for i in range(args.warmup + args.steps):
+            tail.zero_()
+            gn.copy_(dst, src)
+            o.run()
+            route = gn.last_route()
+            torch.cuda.synchronize()
+            if i < args.warmup:
+                continue
+            st = tail.cpu().numpy().view(np.uint64).reshape(-1, 8)[:, :6].astype(np.int64)
+            st = st[st[:, 0] != 0]
+            if st.size == 0 or np.any(st == 0):
+                sys.exit(f"{name}: incomplete phase stamps (route {route})")
+            d = np.diff(st, axis=1) * 0.01  # ticks of 10 ns -> us
+            per_call.append({"wg": len(st), "phases": np.median(d, axis=0),
+                             "spread": (st[:, 0].max() - st[:, 0].min()) * 0.01,
+                             "span": (st[:, 5].max() - st[:, 0].min()) * 0.01})
+        ph = np.median([c["phases"] for c in per_call], axis=0)
+        spread = float(np.median([c["spread"] for c in per_call]))
+        span = float(np.median([c["span"] for c in per_call]))
+        out[name] = {"route": route, "workgroups": per_call[0]["wg"], "invocations": len(per_call),
+                     "median_phase_us": {p: round(float(v), 3) for p, v in zip(PHASES, ph)},
+                     "start_spread_us": round(spread, 3), "first_start_to_last_stamp_us": round(span, 3)}
+        lines.append(f"| {name} | {route} | {per_call[0]['wg']} | " + " | ".join(f"{v:.2f}" for v in ph) +
+                     f" | {spread:.2f} | {span:.2f} |")
+        log(f"{name}: {route}, phases " + ", ".join(f"{p} {v:.2f}" for p, v in zip(PHASES, ph)))
+        del o
+    print("\n".join(lines), file=sys.stderr)
+    print(json.dumps({"phases": out, "clock": "wall clock, 100 MHz", "statistic":
+                      "median over workgroups of each invocation, then median over invocations"}),
+          flush=True)
+
+
 def host_cpu():
     """Logical CPU count and model name of the machine the oracle ran on."""
     model = None
@@ -369,6 +437,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs", action="store_true",
                     help="time each reference workload alone (cold), and the oracle on it")
+    ap.add_argument("--phases", action="store_true",
+                    help="per-phase timings of the single-launch group-norm kernels (needs the "
+                         "phase-trace build of the library)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the operators need no communication and this "
@@ -376,6 +447,9 @@ def main():
         sys.exit(2)
     if args.configs:
         config_table(args)
+        return
+    if args.phases:
+        phase_table(args)
         return
 
     import torch

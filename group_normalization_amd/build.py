@@ -15,6 +15,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libskipnorm.so")
+# Measurement build: the same library with SN_PHASE_TRACE, whose single-launch
+# SkipGroupNorm kernels record per-workgroup phase timestamps in a tail of
+# the workspace (read by `bench.py --phases`).  Never loaded by the package.
+TRACE_BUILD_DIR = os.path.join(PKG, "_build_phase_trace")
+TRACE_LIB_PATH = os.path.join(PKG, "libskipnorm_phase_trace.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -28,9 +33,9 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
          "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the GPU-only feature flag and says so;
     # that line is expected, anything else is shown.
@@ -43,18 +48,21 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    """Compile and link the library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int | None = None, phase_trace: bool = False) -> str:
+    """Compile and link the library (or, with phase_trace, the measurement
+    build); returns its path."""
+    build_dir, lib_path = (TRACE_BUILD_DIR, TRACE_LIB_PATH) if phase_trace else (BUILD_DIR, LIB_PATH)
+    extra = ["-DSN_PHASE_TRACE"] if phase_trace else []
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+    tmp = lib_path + ".tmp"
     subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                    check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(phase_trace="--phase-trace" in sys.argv[1:]))

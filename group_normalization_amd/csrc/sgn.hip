@@ -98,6 +98,7 @@ struct ClusterArgs {
     bool skip_bcast, silu;
     float eps;
     int phase;     // phased route: elements from the 16-byte boundary below the data bases
+    unsigned long long* trace;  // phase timestamps (measurement builds)
 };
 
 
@@ -109,6 +110,7 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
     __shared__ Moments slice_m[kClusterMaxK];
     __shared__ int late[kClusterMaxK];
     const int t = threadIdx.x;
+    SN_PHASE(a.trace, 0);
     const int ng = blockIdx.x / a.K, k = blockIdx.x % a.K;
     const int n = ng / a.groups, g = ng % a.groups;
     const int64_t base = (int64_t(n) * a.C + int64_t(g) * a.cpg) * a.HW / E;  // in vectors
@@ -172,7 +174,9 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
             accumulate(acc, cnt, sv[r]);
         }
     }
+    SN_PHASE(a.trace, 1);
     const Moments mine = block_merge_rcp(acc.moments(cnt), sh);
+    SN_PHASE(a.trace, 2);
 
     // ---- exchange with the other K-1 slices of the group
     Moments tot = mine;
@@ -189,6 +193,7 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
                 if (j < end) store_vec_stream<T, E>(a.S, base + j, sv[r]);
             }
         }
+        SN_PHASE(a.trace, 3);
         if (t < a.K && t != k) {
             const long long t0 = wall_clock64();
             bool ok = false;
@@ -234,13 +239,17 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
             }
             tot = merge_rcp(tot, m);
         }
-    } else if (a.S) {
+    } else {
+        if (a.S) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t j = vec_of(k, r);
-            if (j < end) store_vec_stream<T, E>(a.S, base + j, sv[r]);
+            for (int r = 0; r < R; ++r) {
+                const uint32_t j = vec_of(k, r);
+                if (j < end) store_vec_stream<T, E>(a.S, base + j, sv[r]);
+            }
         }
+        SN_PHASE(a.trace, 3);
     }
+    SN_PHASE(a.trace, 4);
 
     // ---- normalize the held S
     const float2 st = finalize(tot, a.eps);
@@ -260,6 +269,7 @@ sgn_cluster_kernel(ClusterArgs<T, M> a) {
             store_vec_stream<T, E>(a.Y, base + j, out);
         }
     }
+    SN_PHASE(a.trace, 5);
 }
 
 // ------------------------------------------------------------------ group-cluster, phased
@@ -287,6 +297,7 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
     __shared__ int late[kClusterMaxK];
     __shared__ float4 cst[kPhaseMaxCpg];  // per channel: bias, broadcast skip, gamma, beta
     const int t = threadIdx.x;
+    SN_PHASE(a.trace, 0);
     const int ng = blockIdx.x / a.K, k = blockIdx.x % a.K;
     const int n = ng / a.groups, g = ng % a.groups;
     const int64_t span = int64_t(a.cpg) * a.HW;
@@ -390,7 +401,9 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
             accumulate(acc, cnt, sv[r], j);
         }
     }
+    SN_PHASE(a.trace, 1);
     const Moments mine = block_merge_rcp(acc.moments(cnt), sh);
+    SN_PHASE(a.trace, 2);
 
     // ---- exchange with the other K-1 slices of the group (as sgn_cluster_kernel)
     Moments tot = mine;
@@ -404,6 +417,7 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
                 if (j < end) put(sa, j, sv[r]);
             }
         }
+        SN_PHASE(a.trace, 3);
         if (t < a.K && t != k) {
             const long long t0 = wall_clock64();
             bool ok = false;
@@ -447,13 +461,17 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
             }
             tot = merge_rcp(tot, m);
         }
-    } else if (sa) {
+    } else {
+        if (sa) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t j = vec_of(k, r);
-            if (j < end) put(sa, j, sv[r]);
+            for (int r = 0; r < R; ++r) {
+                const uint32_t j = vec_of(k, r);
+                if (j < end) put(sa, j, sv[r]);
+            }
         }
+        SN_PHASE(a.trace, 3);
     }
+    SN_PHASE(a.trace, 4);
 
     // ---- normalize the held S
     const float2 st = finalize(tot, a.eps);
@@ -476,6 +494,7 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
             put(ya, j, out);
         }
     }
+    SN_PHASE(a.trace, 5);
 }
 
 // ------------------------------------------------------------------ split: nhwc
@@ -1118,6 +1137,7 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
             ca.silu = silu;
             ca.eps = a.epsilon;
             ca.phase = phase;
+            ca.trace = a.trace;
             if (nchw_phase) {
                 *route = "sgn.cluster.nchw.phase";
                 return launch_cluster_phase<T, M, EV>(ca, NG * Kc, stream);

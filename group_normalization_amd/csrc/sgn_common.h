@@ -15,6 +15,22 @@ constexpr int kNhwcMaxK = 64;         // slices per (image, channel block), NHWC
 // groups of 2560-5120 elements than several slices and their exchange.
 constexpr int kSingleSliceMaxR = 6;
 
+// Phase k of this workgroup, recorded by its leader in measurement builds:
+// 0 start, 1 own data loaded (leader's wave), 2 slice moments reduced,
+// 3 moments published and S stores issued, 4 statistics combined,
+// 5 Y stores issued.
+#ifdef SN_PHASE_TRACE
+#define SN_PHASE(trace, k)                                                        \
+    do {                                                                          \
+        if ((trace) && threadIdx.x == 0 && blockIdx.x < kTraceBlocks)             \
+            (trace)[size_t(blockIdx.x) * kTraceStamps + (k)] = wall_clock64();    \
+    } while (0)
+#else
+#define SN_PHASE(trace, k) \
+    do {                   \
+    } while (0)
+#endif
+
 // Launches the NHWC channel-block cluster route when the shapes, alignments
 // and `want` allow it (returns false, having launched nothing, otherwise).
 // `part` is the workspace's partial area (the publication slots).

@@ -61,6 +61,7 @@ struct NhwcClusterArgs {
     FastDiv div_G, div_NCB, div_K, div_CBv, div_cpg, div_P;
     bool skip_bcast, silu;
     float eps;
+    unsigned long long* trace;  // phase timestamps (measurement builds)
 };
 
 constexpr int kNhwcMaxCBg = 16;   // groups per channel block: four per wave
@@ -99,6 +100,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
         q = int(r);
     }
     if (q >= a.K || n >= a.N) return;  // padding; not part of any cluster
+    SN_PHASE(a.trace, 0);
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const bool active = t < a.P * a.CBv;
@@ -237,7 +239,9 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
                 form(xs[r], sv[r], sv[r]);
                 accumulate(acc, sv[r], r);
             }
+        SN_PHASE(a.trace, 1);
         reduce_slice(acc, nv_own, own_m);
+        SN_PHASE(a.trace, 2);
     }
 
     // ---- publication: per group, (mean, M2) in its self-tagged slot.
@@ -250,6 +254,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
         for (int r = 0; r < R; ++r)
             if (r < nv_own) store_vec<T, E>(a.S, vidx(q, r), sv[r]);
     }
+    SN_PHASE(a.trace, 3);
     __syncthreads();  // own_m visible to every wave
 
     // ---- statistics: wave w combines groups w, w + 4, ... over the K slices,
@@ -350,6 +355,8 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
         __syncthreads();
     }
 
+    SN_PHASE(a.trace, 4);
+
     // ---- normalize the held S
     if (nv_own > 0) {
         const float2 slo = stat[glo];
@@ -375,6 +382,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
                 store_vec<T, E>(a.Y, vidx(q, r), out);
             }
     }
+    SN_PHASE(a.trace, 5);
 }
 
 // Channel-block cluster plan.  Channel blocks: the fewest (so the most
@@ -602,6 +610,7 @@ hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, const NhwcL
     ca.div_CBv = make_fastdiv(uint32_t(plan.CBv));
     ca.div_cpg = make_fastdiv(uint32_t(a.C / a.groups));
     ca.div_P = make_fastdiv(uint32_t(plan.P));
+    ca.trace = a.trace;
     const int64_t blocks = lay.grid;
     constexpr int EV = VecWidth<T>::value;
     if (E == EV) return launch_nhwc_cluster<T, M, EV>(ca, plan.R, blocks, stream);

@@ -364,6 +364,13 @@ sn_status group_norm(const char* op, const sn_tensor_in* X_d, const sn_tensor_in
     size_t need = 0;
     if (numel > 0)
         need = sn::sgn_workspace_bytes(kernel_dtype(T), d.N, d.C, d.H, d.W, groups, channels_last != 0);
+    size_t trace_at = 0;  // offset of the phase-timestamp area (measurement builds)
+#ifdef SN_PHASE_TRACE
+    if (need > 0 && !noalloc) {
+        trace_at = (need + 255) / 256 * 256;
+        need = trace_at + sn::kTraceBytes;
+    }
+#endif
     if (noalloc) {
         if (need > sn::kStaticScratchBytes)
             return fail(SN_ERR_WORKSPACE,
@@ -409,6 +416,8 @@ sn_status group_norm(const char* op, const sn_tensor_in* X_d, const sn_tensor_in
     a.Y = Y.data;
     a.S = S.present ? S.data : nullptr;
     a.workspace = workspace;
+    a.trace = trace_at ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + trace_at)
+                       : nullptr;
     a.tag = g_tag.fetch_add(2) | 1;  // odd, never 0
     a.exchange_timeout_ticks = g_exchange_timeout_us.load() * 100;
     // A captured graph replays its kernels with the arguments of the
@@ -506,6 +515,9 @@ sn_status skip_group_norm_workspace_size(const sn_tensor_in* X_d, int64_t groups
     *bytes = X.numel == 0 ? 0
                           : sn::sgn_workspace_bytes(kernel_dtype(X.dtype), d.N, d.C, d.H, d.W, groups,
                                                     channels_last != 0);
+#ifdef SN_PHASE_TRACE
+    if (*bytes > 0) *bytes = (*bytes + 255) / 256 * 256 + sn::kTraceBytes;
+#endif
     return ok();
 }
 

@@ -52,7 +52,17 @@ struct SgnArgs {
     // Clear the publication slots before a cluster launch (the call is being
     // captured into a graph, whose replays repeat `tag`).
     bool clear_tags;
+    // Phase timestamps of the single-launch routes (measurement builds with
+    // SN_PHASE_TRACE only; nullptr otherwise).
+    unsigned long long* trace = nullptr;
 };
+// Measurement builds (SN_PHASE_TRACE): the workspace grows by
+// kTraceBytes, where the leader of each of the first kTraceBlocks
+// workgroups of a single-launch SkipGroupNorm route records the 100 MHz
+// wall clock at kTraceStamps phase boundaries.
+constexpr int kTraceStamps = 8;
+constexpr unsigned kTraceBlocks = 65536;
+constexpr size_t kTraceBytes = size_t(kTraceBlocks) * kTraceStamps * 8;
 // Blocks of the statistics pass per (n, group) partial-sum row; a function
 // of the shapes and T only, so that the workspace size does not depend on
 // the route taken.
