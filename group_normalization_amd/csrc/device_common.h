@@ -97,6 +97,55 @@ __device__ __forceinline__ void store_vec_run(T* __restrict__ run, int j, const 
     else store_vec<T, E>(run, j, v);
 }
 
+// Orders a wave's LDS writes before its later LDS reads from other lanes of
+// the same wave: the LDS executes one wave's instructions in issue order, so
+// only the compiler must be kept from moving accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Flat routes (GatedRMSNorm, SkipSimplifiedLayerNormalization): rows as one
+// stream of aligned 16-byte vectors, per-column parameters from an LDS table
+// of kFlatTable float32 slots with E of them ahead of column 0, so rows hold
+// at most kFlatTable - E elements.
+constexpr int kFlatTable = 1024;
+
+// Flat plan for rows of C <= kFlatTable - E elements: rt whole rows per wave
+// such that the vectors they touch (at any offset from the grid) fit the
+// wave's 64 * VPT vector slots, in the smaller tile (VPT = 2 for float16, 4
+// for float32: 1024 element slots) unless `large` allows twice that and the
+// smaller leaves over a quarter of its slots idle while the larger fills
+// more; lpr = the largest power of two with lpr * rt <= 64 (1 beyond 64
+// rows, which the lanes then take in turns).
+struct FlatPlan {
+    int vpt, rt, lpr_log;
+    double fill;  // share of the tile's element slots that carry data
+};
+
+inline bool flat_plan(int64_t C, int vec_elems, bool large, FlatPlan* p) {
+    if (C < 1 || C > kFlatTable - vec_elems) return false;
+    const int small = 16 / vec_elems;
+    p->fill = -1.0;
+    for (int vpt : {small, 2 * small}) {
+        if (vpt != small && !large) break;
+        const int64_t te = int64_t(64) * vpt * vec_elems;
+        const int64_t rt = (te - vec_elems + 1) / C;
+        if (rt < 1) continue;
+        const double fill = double(rt * C) / double(te);
+        if (p->fill >= 0.75 || fill <= p->fill) continue;
+        p->fill = fill;
+        p->vpt = vpt;
+        p->rt = int(rt);
+    }
+    if (p->fill < 0.0) return false;
+    int lpr_log = 0;
+    while ((int64_t(2) << lpr_log) * p->rt <= 64) ++lpr_log;
+    p->lpr_log = lpr_log;
+    return true;
+}
+
 // Host side: whether rows of row_bytes written at these bases (null ones
 // skipped) do not all start on 128-byte lines.
 inline int rows_off_lines(int64_t row_bytes, std::initializer_list<const void*> outs) {

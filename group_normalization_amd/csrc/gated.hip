@@ -139,14 +139,6 @@ gated_segment_kernel(const T* __restrict__ X, const T* __restrict__ scale,
     }
 }
 
-// Orders a wave's LDS writes before its later LDS reads from other lanes of
-// the same wave: the LDS executes one wave's instructions in issue order, so
-// only the compiler must be kept from moving accesses across this point.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Tile route.  Wave w of the grid takes rows [w * rt, w * rt + rt) (fewer at
 // the end), i.e. vectors [0, cnt) from the first of them; lane l holds the
@@ -249,7 +241,6 @@ gated_tile_kernel(const T* __restrict__ X, const T* __restrict__ scale,
 // otherwise a vector spans at most two and the row changes once.  The scale
 // table holds 1024 float32 slots, E of them ahead of column 0, so rows hold
 // at most 1024 - E elements.
-constexpr int kFlatTable = 1024;
 
 template <typename T, int VPT, bool NARROW>
 __global__ void __launch_bounds__(256)
@@ -664,40 +655,6 @@ hipError_t launch_tile_for(const GatedArgs& a, int nvec, const TilePlan& p, hipS
     return hipErrorInvalidValue;  // the plan only picks the widths above
 }
 
-// Flat plan for rows of C <= kFlatTable - E elements: rt whole rows per wave
-// such that the vectors they touch (at any offset from the grid) fit the
-// wave's 64 * VPT vector slots, in the smaller tile (VPT = 2 for float16, 4
-// for float32: 1024 element slots) unless `large` allows twice that and the
-// smaller leaves over a quarter of its slots idle while the larger fills
-// more; lpr = the largest power of two with lpr * rt <= 64 (1 beyond 64
-// rows, which the lanes then take in turns).
-struct FlatPlan {
-    int vpt, rt, lpr_log;
-    double fill;  // share of the tile's element slots that carry data
-};
-
-bool gated_flat_plan(int64_t C, int vec_elems, bool large, FlatPlan* p) {
-    if (C < 1 || C > kFlatTable - vec_elems) return false;
-    const int small = 16 / vec_elems;
-    p->fill = -1.0;
-    for (int vpt : {small, 2 * small}) {
-        if (vpt != small && !large) break;
-        const int64_t te = int64_t(64) * vpt * vec_elems;
-        const int64_t rt = (te - vec_elems + 1) / C;
-        if (rt < 1) continue;
-        const double fill = double(rt * C) / double(te);
-        if (p->fill >= 0.75 || fill <= p->fill) continue;
-        p->fill = fill;
-        p->vpt = vpt;
-        p->rt = int(rt);
-    }
-    if (p->fill < 0.0) return false;
-    int lpr_log = 0;
-    while ((int64_t(2) << lpr_log) * p->rt <= 64) ++lpr_log;
-    p->lpr_log = lpr_log;
-    return true;
-}
-
 // Where the automatic choice takes the flat route, for rows whose widest
 // access (E elements of T) is narrower than 16 bytes, as measured on
 // 2^27-element tensors against the segment and tile routes: tiles at least
@@ -758,7 +715,7 @@ hipError_t launch_gated_t(const GatedArgs& a, Route want, hipStream_t stream, co
         FlatPlan fp;
         if (ph % sizeof(T) == 0 && reinterpret_cast<uintptr_t>(a.gate) % 16 == ph &&
             reinterpret_cast<uintptr_t>(a.Y) % 16 == ph &&
-            gated_flat_plan(a.span, VecWidth<T>::value, want == Route::Flat || sizeof(T) == 4, &fp) &&
+            flat_plan(a.span, VecWidth<T>::value, want == Route::Flat || sizeof(T) == 4, &fp) &&
             (want == Route::Flat || flat_preferred<T>(a.span, E, fp))) {
             *route = "gated.flat.vec16";
             return launch_flat_for<T>(a, fp, int(ph / sizeof(T)), stream);

@@ -195,7 +195,7 @@ sn_status check_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
 }
 
 sn::Route current_route() { return static_cast<sn::Route>(g_force_route.load(std::memory_order_relaxed)); }
-// The flat route is GatedRMSNorm's; the other operators run it as automatic.
+// The flat route is the row norms'; SkipGroupNorm runs it as automatic.
 sn::Route current_route_not_flat() {
     const sn::Route r = current_route();
     return r == sn::Route::Flat ? sn::Route::Auto : r;
@@ -269,7 +269,7 @@ sn_status row_norm(const char* op, bool center, const sn_tensor_in* input_d,
                    static_cast<float*>(inv.present ? inv.data : nullptr),
                    sum.present ? sum.data : nullptr, center};
     const char* route = "";
-    return finish_launch(sn::launch_ssln(a, current_route_not_flat(), stream, &route), route, op);
+    return finish_launch(sn::launch_ssln(a, current_route(), stream, &route), route, op);
 }
 
 // ---------------------------------------------------------------- SkipGroupNorm

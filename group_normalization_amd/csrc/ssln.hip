@@ -604,6 +604,261 @@ ssln_segment_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     }
 }
 
+// ------------------------------------------------------------------ flat route
+// Rows that would otherwise be read with accesses narrower than 16 bytes
+// (odd widths, bases off the 4-byte grid) and hold at most kFlatTable - E
+// elements: the rows as one stream of elements, as in the GatedRMSNorm flat
+// route.  Wave w takes the rt whole rows from r0 = w * rt on, elements
+// [r0 * C, (r0 + rt) * C) (plus the offset `phase` of the data bases from
+// the 16-byte grid, which input, skip, output and S share), and reads the
+// aligned 16-byte vectors that cover them; the first and last may hold a
+// neighbouring wave's elements, which are read and left unused (never
+// outside the 16-byte chunks that hold the tensors' own elements), and they
+// are written element by element, the rest whole (vectors in 128-byte
+// lines shared with the neighbouring tiles through L2).  S is formed per
+// element with its column's bias from a per-workgroup LDS table of (gamma,
+// bias) by column (E slots ahead of column 0 keep the reads of elements
+// before a tile inside it), its square -- with the mean removed, S itself
+// -- goes to the wave's LDS, and each row is summed there by a power-of-two
+// group of lanes (lane k adds elements k, k + lpr, ... into four partial
+// sums, then a butterfly over the group).  The group's first lane writes the row's
+// statistics and leaves them in place of the row's first LDS entries (r;
+// with the mean removed s0, d, r, rows of at least 3 elements), which the
+// elements then read by row.  NARROW (C < elements per vector): a vector
+// spans several rows, so every element finds its own row; otherwise a
+// vector spans at most two and the row changes once.  With the mean
+// removed, the statistics are taken about the row's first element s0 as in
+// the other routes: d = mean(S - s0), then the squares of (S - s0) - d.
+template <typename T, int VPT, bool NARROW, bool CENTER>
+__global__ void __launch_bounds__(256)
+ssln_flat_kernel(const T* __restrict__ input, const T* __restrict__ skip,
+                 const T* __restrict__ gamma, const T* __restrict__ beta,
+                 const T* __restrict__ bias, T* __restrict__ output, float* __restrict__ mean,
+                 float* __restrict__ inv_std_var, T* __restrict__ sum, int64_t rows, int C, int rt,
+                 int lpr_log, int phase, FastDiv cdiv, float hidden_f, float eps) {
+    constexpr int E = VecWidth<T>::value;
+    constexpr int TE = 64 * VPT * E;  // element slots of a wave's tile
+    using V = Vec<T, E>;
+    __shared__ float sq[4][TE];
+    __shared__ float2 gb_tab[kFlatTable];                // (gamma, bias) by column
+    __shared__ float beta_tab[CENTER ? kFlatTable : 1];  // beta by column
+    float2* gb = gb_tab + E;
+    float* bt = beta_tab + (CENTER ? E : 0);
+    const bool has_bias = bias != nullptr;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r0 = (int64_t(blockIdx.x) * 4 + wave) * rt;
+    const int64_t left = rows - r0;
+    const int nr = left <= 0 ? 0 : (left < rt ? int(left) : rt);
+    // A wave past the last row loads the last row (and discards it), so that
+    // every wave reaches the barrier below with nothing out of bounds.
+    const int64_t rl = nr > 0 ? r0 : rows - 1;
+    const int span = (nr > 0 ? nr : 1) * C;
+    const int64_t f0 = phase + rl * C;  // the tile's first element from the aligned base
+    const int64_t v0 = f0 / E;
+    const int off0 = int(f0 - v0 * E);
+    const int nvt = (off0 + span + E - 1) / E;  // vectors the tile touches
+    const T* ia = input - phase;
+    const T* ka = skip - phase;
+    T* oa = output - phase;
+    T* sa = sum ? sum - phase : nullptr;
+
+    V xs[VPT], ss[VPT];  // input; skip, then S
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int i = v * 64 + lane;
+        const int ic = i < nvt ? i : nvt - 1;
+        xs[v] = load_vec_stream<T, E>(ia, v0 + ic);
+        ss[v] = load_vec_stream<T, E>(ka, v0 + ic);
+    }
+    // The tables: each thread's (at most kFlatTable / 256) columns are loaded
+    // at once (indices clamped, no load behind a branch), then stored.
+    constexpr int kFill = kFlatTable / 256;
+    T gv[kFill], bv[kFill], tv[kFill];
+#pragma unroll
+    for (int j = 0; j < kFill; ++j) {
+        const int c = threadIdx.x + j * 256;
+        const int cc = c < C ? c : C - 1;
+        gv[j] = gamma[cc];
+        if (has_bias) bv[j] = bias[cc];
+        if constexpr (CENTER)
+            if (beta) tv[j] = beta[cc];
+    }
+#pragma unroll
+    for (int j = 0; j < kFill; ++j) {
+        const int c = threadIdx.x + j * 256;
+        if (c < C) {
+            gb[c] = make_float2(to_f32(gv[j]), has_bias ? to_f32(bv[j]) : 0.0f);
+            if constexpr (CENTER) bt[c] = beta ? to_f32(tv[j]) : 0.0f;
+        }
+    }
+    __syncthreads();  // the tables
+    if (nr == 0) return;
+
+    // Where vector v's elements fall: row of element 0 (relative to the
+    // tile) and the column of element 0 (1 - E to -1 for the vector that
+    // starts before the tile; clamped for those past it, whose results are
+    // dropped); elements e >= C - column lie in the next row.  Each element
+    // reads its column's parameters at an immediate offset from one of two
+    // table bases (this row's, the next row's).
+    int row_a[VPT], col_a[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int t0 = (v * 64 + lane) * E - off0;
+        const int tc = t0 < 0 ? 0 : (t0 < span ? t0 : span - 1);
+        row_a[v] = int(fastdiv(uint32_t(tc), cdiv));
+        const int c0 = t0 - row_a[v] * C;
+        col_a[v] = c0 > C - 1 ? C - 1 : c0;
+    }
+    // NARROW: element e's row and column from its own position.
+    auto narrow_rc = [&](int v, int e, int& row, int& col) {
+        int t = (v * 64 + lane) * E - off0 + e;
+        t = t < 0 ? 0 : (t < span ? t : span - 1);
+        row = int(fastdiv(uint32_t(t), cdiv));
+        col = t - row * C;
+    };
+
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int i = v * 64 + lane;
+        const float2* pa = gb + col_a[v];
+        const float2* pb = gb + (col_a[v] - C);
+        const int b = C - col_a[v];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float bv;
+            if constexpr (NARROW) {
+                int row, col;
+                narrow_rc(v, e, row, col);
+                bv = gb[col].y;
+            } else {
+                bv = (e >= b ? pb : pa)[e].y;
+            }
+            const float sv = residual_sum<T>(to_f32(xs[v].v[e]), to_f32(ss[v].v[e]), has_bias, bv,
+                                             ss[v].v[e]);
+            sq[wave][i * E + e] = CENTER ? sv : sv * sv;
+        }
+    }
+    wave_lds_sync();
+
+    const int lpr = 1 << lpr_log;
+    const int k = lane & (lpr - 1);
+    // Lane k of a row's group adds f(element) over k, k + lpr, ... into four
+    // partial sums (elements k + 4j lpr, k + (4j + 1) lpr, ...: four LDS reads
+    // in flight), added as ((p0 + p1) + (p2 + p3)); then a butterfly over
+    // the group (every lane ends with the same total).
+    auto row_sum = [&](int first, bool has, auto f) {
+        float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+        if (has) {
+            int c = k;
+            for (; c + 3 * lpr < C; c += 4 * lpr) {
+                const float a0 = sq[wave][first + c], a1 = sq[wave][first + c + lpr];
+                const float a2 = sq[wave][first + c + 2 * lpr], a3 = sq[wave][first + c + 3 * lpr];
+                p0 = f(p0, a0);
+                p1 = f(p1, a1);
+                p2 = f(p2, a2);
+                p3 = f(p3, a3);
+            }
+            if (c < C) p0 = f(p0, sq[wave][first + c]);
+            if (c + lpr < C) p1 = f(p1, sq[wave][first + c + lpr]);
+            if (c + 2 * lpr < C) p2 = f(p2, sq[wave][first + c + 2 * lpr]);
+        }
+        float acc = (p0 + p1) + (p2 + p3);
+        for (int m = 1; m < lpr; m <<= 1) acc += __shfl_xor(acc, m, 64);
+        return acc;
+    };
+    for (int rb = 0; rb < nr; rb += 64 >> lpr_log) {
+        const int rr = rb + (lane >> lpr_log);
+        const bool has = rr < nr;
+        const int first = off0 + (has ? rr : 0) * C;
+        float r, s0 = 0.0f, md = 0.0f;
+        if constexpr (!CENTER) {
+            const float acc = row_sum(first, has, [](float p, float x) { return p + x; });
+            r = inv_sqrt(acc / hidden_f + eps);
+            // The group's reads of this row are done (the butterfly used them).
+            if (has && k == 0) sq[wave][first] = r;
+        } else {
+            s0 = sq[wave][first];
+            md = row_sum(first, has, [&](float p, float x) { return p + (x - s0); }) / hidden_f;
+            const float dev = row_sum(first, has, [&](float p, float x) {
+                const float d = (x - s0) - md;
+                return fmaf_(d, d, p);
+            });
+            r = inv_sqrt(dev / hidden_f + eps);
+            if (has && k == 0) {
+                sq[wave][first + 1] = md;
+                sq[wave][first + 2] = r;
+            }
+        }
+        if (has && k == 0) {
+            if (inv_std_var) inv_std_var[r0 + rr] = r;
+            if (mean) mean[r0 + rr] = CENTER ? s0 + md : 0.0f;
+        }
+    }
+    wave_lds_sync();
+
+    const LineRun orun = line_run<T, E>(oa + v0 * E, nvt);
+    const LineRun srun = line_run<T, E>(sa ? sa + v0 * E : oa + v0 * E, nvt);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int i = v * 64 + lane;
+        const int t0 = i * E - off0;  // the vector's first element, from the tile's first
+        V out;
+        if constexpr (NARROW) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                int row, c;
+                narrow_rc(v, e, row, c);
+                const int at = off0 + row * C;  // the row's first LDS entry
+                const float sv = to_f32(ss[v].v[e]);
+                if constexpr (CENTER)
+                    out.v[e] = from_f32<T>(((sv - sq[wave][at]) - sq[wave][at + 1]) * sq[wave][at + 2] *
+                                           gb[c].x + bt[c]);
+                else
+                    out.v[e] = from_f32<T>(sv * sq[wave][at] * gb[c].x);
+            }
+        } else {
+            // The statistics of this vector's (at most) two rows, once.
+            const int ra = off0 + row_a[v] * C;
+            const int rb = off0 + (row_a[v] + 1 < nr ? row_a[v] + 1 : row_a[v]) * C;
+            const float r_a = sq[wave][CENTER ? ra + 2 : ra], r_b = sq[wave][CENTER ? rb + 2 : rb];
+            float s0_a = 0.0f, s0_b = 0.0f, md_a = 0.0f, md_b = 0.0f;
+            if constexpr (CENTER) {
+                s0_a = sq[wave][ra];
+                s0_b = sq[wave][rb];
+                md_a = sq[wave][ra + 1];
+                md_b = sq[wave][rb + 1];
+            }
+            const float2* pa = gb + col_a[v];
+            const float2* pb = gb + (col_a[v] - C);
+            const float* qa = bt + col_a[v];
+            const float* qb = bt + (col_a[v] - C);
+            const int b = C - col_a[v];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool next = e >= b;
+                const float sv = to_f32(ss[v].v[e]);
+                const float g = (next ? pb : pa)[e].x;
+                if constexpr (CENTER)
+                    out.v[e] = from_f32<T>(((sv - (next ? s0_b : s0_a)) - (next ? md_b : md_a)) *
+                                           (next ? r_b : r_a) * g + (next ? qb : qa)[e]);
+                else
+                    out.v[e] = from_f32<T>(sv * (next ? r_b : r_a) * g);
+            }
+        }
+        if (t0 >= 0 && t0 + E <= span) {
+            store_vec_run<T, E>(oa + v0 * E, i, out, orun);
+            if (sa) store_vec_run<T, E>(sa + v0 * E, i, ss[v], srun);
+        } else if (i < nvt) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (t0 + e >= 0 && t0 + e < span) {
+                    oa[(v0 + i) * E + e] = out.v[e];
+                    if (sa) sa[(v0 + i) * E + e] = ss[v].v[e];
+                }
+        }
+    }
+}
+
 template <typename T, int E, int L>
 hipError_t launch_segment(const SslnArgs& a, int nvec, hipStream_t stream) {
     // About 64 bytes of each input per thread in flight, at most 16 rows.
@@ -810,18 +1065,108 @@ bool launch_ssln_phase(const SslnArgs& a, hipStream_t stream, const char** route
     return true;
 }
 
+// The flat route (see ssln_flat_kernel): rows of at most kFlatTable - E
+// elements whose data tensors (input, skip, output, S) share their offset
+// from a 16-byte boundary; with the mean removed, rows of at least three
+// elements.  Returns false, having launched nothing, when it does not apply.
+template <typename T>
+bool launch_ssln_flat(const SslnArgs& a, bool forced, hipStream_t stream, const char** route,
+                      hipError_t* err) {
+    constexpr int EV = VecWidth<T>::value;
+    const uintptr_t ph = reinterpret_cast<uintptr_t>(a.input) % 16;
+    auto same = [&](const void* q) { return !q || reinterpret_cast<uintptr_t>(q) % 16 == ph; };
+    if (ph % sizeof(T) != 0 || !same(a.skip) || !same(a.output) || !same(a.sum)) return false;
+    if (a.center && a.hidden < 3) return false;
+    FlatPlan fp;
+    if (!flat_plan(a.hidden, EV, forced || sizeof(T) == 4, &fp)) return false;
+    const int C = int(a.hidden);
+    const int phase = int(ph / sizeof(T));
+    const int64_t tiles = (a.rows + fp.rt - 1) / fp.rt;
+    const int64_t blocks = (tiles + 3) / 4;
+    const FastDiv cdiv = make_fastdiv(uint32_t(C));
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                           static_cast<const T*>(a.input), static_cast<const T*>(a.skip),
+                           static_cast<const T*>(a.gamma), static_cast<const T*>(a.beta),
+                           static_cast<const T*>(a.bias), static_cast<T*>(a.output), a.mean,
+                           a.inv_std_var, static_cast<T*>(a.sum), a.rows, C, fp.rt, fp.lpr_log,
+                           phase, cdiv, float(a.hidden), a.epsilon);
+        return hipGetLastError();
+    };
+    auto by_vpt = [&](auto vpt, auto center) {
+        constexpr int VPT = decltype(vpt)::value;
+        constexpr bool CTR = decltype(center)::value;
+        if (C < EV) return go(ssln_flat_kernel<T, VPT, true, CTR>);
+        return go(ssln_flat_kernel<T, VPT, false, CTR>);
+    };
+    auto by_center = [&](auto vpt) {
+        if (a.center) return by_vpt(vpt, std::true_type{});
+        return by_vpt(vpt, std::false_type{});
+    };
+    constexpr int small = 16 / EV;
+    *route = "ssln.flat.vec16";
+    *err = fp.vpt == small ? by_center(std::integral_constant<int, small>{})
+                           : by_center(std::integral_constant<int, 2 * small>{});
+    return true;
+}
+
+// Where the automatic choice takes the flat route, by the access width E the
+// other routes would use, as measured on 2^27-element tensors (outputs Y and
+// S) against them:
+//   element rows: float16 up to 247 elements (the phased route beyond:
+//     f16 255-1015 3.6-3.8 against 3.8-5.3 TB/s), 191 with the mean
+//     removed; float32 up to 255, 1020 with the mean removed.  f16 C = 9 /
+//     33 / 99 / 127 / 247 at 5.7 / 5.5 / 5.5 / 5.8 / 4.0 TB/s against 2.7
+//     / 2.6 / 2.0 / 2.6 / 3.2 (lane groups or one wave of scalars).
+//   float16 pairs (4-byte accesses): rows of 10 to 300 elements (+2 to
+//     +110 %, f16 70 / 130 at 5.7 / 5.1 against 3.7 / 2.4 TB/s); with the
+//     mean removed (two passes over LDS) only where the pairs fill less than
+//     70 % of their lane group's or wave's slots.
+//   float32 pairs (8-byte accesses): rows of 42 elements or more (+3 to +32
+//     %; shorter rows fill their lane groups well and lost up to 17 %).
+//   16-byte rows and float16 8-byte rows keep their routes (mixed, -37 to
+//   +8 %).
+template <typename T>
+bool flat_preferred(const SslnArgs& a, int E) {
+    const int64_t h = a.hidden;
+    const int bytes = E * int(sizeof(T));
+    if (E == 1) {
+        if (sizeof(T) == 2) return h <= (a.center ? 191 : 247);
+        return h <= (a.center ? 1020 : 255);
+    }
+    if (bytes == 4 && sizeof(T) == 2) {
+        if (h < 10 || h > 300) return false;
+        if (!a.center) return true;
+        const int64_t nvec = h / E;
+        int64_t slots = 64 * ((nvec + 63) / 64);  // one wave of up to 64 lanes per pass
+        if (nvec <= 64) {
+            slots = 1;
+            while (slots < nvec) slots <<= 1;  // a power-of-two lane group
+        }
+        return double(nvec) / double(slots) < 0.7;
+    }
+    if (bytes == 8 && sizeof(T) == 4) return h >= 42;
+    return false;
+}
+
 template <typename T>
 hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, const char** route) {
     // Widest access that divides the row and every tensor's base.
     int E = widest_vector<T>(a.hidden, {a.input, a.skip, a.gamma, a.beta, a.bias, a.output, a.sum});
     if (want == Route::Scalar) E = 1;
-    // Rows that would otherwise be read element by element take the phased
-    // route (1.2-2.3x: float16 hidden 4097 / 8193 at 5.3 / 5.1 TB/s against
-    // 3.6 / 3.0); against 4- and 8-byte vectors it measured within -7 / +14 %,
-    // so those keep them.
-    if ((want == Route::Auto || want == Route::Vector) && E == 1) {
-        hipError_t err = hipSuccess;
-        if (launch_ssln_phase<T>(a, stream, route, &err)) return err;
+    hipError_t err = hipSuccess;
+    if (want == Route::Flat) {  // forced where it applies, else automatic
+        if (launch_ssln_flat<T>(a, true, stream, route, &err)) return err;
+        want = Route::Auto;
+    }
+    // The flat route where it measured faster (flat_preferred); rows that
+    // would otherwise be read element by element take the phased route
+    // beyond it (1.2-2.3x: float16 hidden 4097 / 8193 at 5.3 / 5.1 TB/s
+    // against 3.6 / 3.0); against 4- and 8-byte vectors the phased route
+    // measured within -7 / +14 %, so those keep them.
+    if (want == Route::Auto || want == Route::Vector) {
+        if (flat_preferred<T>(a, E) && launch_ssln_flat<T>(a, false, stream, route, &err)) return err;
+        if (E == 1 && launch_ssln_phase<T>(a, stream, route, &err)) return err;
     }
     int64_t max_regs = kMaxRegisterRow<T, 1>;
     if constexpr (sizeof(T) == 2) {

@@ -28,12 +28,13 @@ extern "C" {
  *   4 = skip_group_norm: the three-launch split route (vectorized where the
  *       preconditions hold) even where a single-launch route would apply;
  *       others: automatic.
- *   5 = gated_rms_norm: the flat route (rows read as one stream of aligned
- *       16-byte vectors) wherever it applies -- rows of at most 1016
- *       (float16) or 1020 (float32) elements, X, gate and Y at one offset
- *       from a 16-byte boundary --
+ *   5 = gated_rms_norm, skip_rms_norm, skip_layer_norm: the flat route
+ *       (rows read as one stream of aligned 16-byte vectors) wherever it
+ *       applies -- rows of at most 1016 (float16) or 1020 (float32)
+ *       elements (skip_layer_norm: at least 3), the data tensors (X, gate,
+ *       Y; input, skip, output, S) at one offset from a 16-byte boundary --
  *       where automatic takes it only for the row lengths it measured
- *       faster on; others: automatic.
+ *       faster on; skip_group_norm: automatic.
  * Returns the previous value; an unknown value leaves the setting unchanged
  * and returns the current one. */
 int skipnorm_force_route(int route);

@@ -28,6 +28,8 @@ def make_inputs():
         # route) and GatedRMSNorm rows of 25 (the flat route).
         "xo": rn(24, 4095), "ko": rn(24, 4095), "go": rn(4095),
         "Xf": rn(300, 25), "gf": rn(300, 25), "sf": rn(25),
+        # SSLN rows of 127 (the flat route).
+        "xq": rn(300, 127), "kq": rn(300, 127), "gq": rn(127), "bq": rn(127),
         # SkipGroupNorm shapes whose groups span several workgroups, so that
         # every replay exchanges moments: NHWC 32 slices per channel block,
         # NCHW 16-byte vectors, and NCHW groups off the 16-byte grid (31 x 31
@@ -57,6 +59,8 @@ def run(t):
     route_o = gn.last_route()
     fl = gn.gated_rms_norm(t["Xf"], t["sf"], t["gf"], 1e-5)
     route_f = gn.last_route()
+    q = gn.skip_rms_norm(t["xq"], t["kq"], t["gq"], t["bq"], 1e-6, want_inv_std_var=True, want_sum=True)
+    route_q = gn.last_route()
     d = gn.skip_group_norm(t["Xh"], t["gh"], t["eh"], t["kh"], t["bh"], groups=32, activation=1,
                            channels_last=1, want_sum=True, workspace=t["ws_h"])
     route_h = gn.last_route()
@@ -67,13 +71,14 @@ def run(t):
                            channels_last=0, want_sum=True, workspace=t["ws_p"])
     route_p = gn.last_route()
     outs = [a.output, a.inv_std_var, a.input_skip_bias_sum, b.output, b.mean, b.inv_std_var, c,
-            d.Y, d.S, e.Y, f.Y, f.S, o.output, o.input_skip_bias_sum, fl]
-    return outs, (route_h, route_c, route_p, route_o, route_f)
+            d.Y, d.S, e.Y, f.Y, f.S, o.output, o.input_skip_bias_sum, fl, q.output, q.inv_std_var,
+            q.input_skip_bias_sum]
+    return outs, (route_h, route_c, route_p, route_o, route_f, route_q)
 
 
 def refill(t, seed):
     g = torch.Generator(device="cuda").manual_seed(seed)
-    for name in ("x", "k", "X", "gate", "xo", "ko", "Xf", "gf", "Xh", "kh", "Xc", "kc", "Xp", "kp"):
+    for name in ("x", "k", "X", "gate", "xo", "ko", "Xf", "gf", "xq", "kq", "Xh", "kh", "Xc", "kc", "Xp", "kp"):
         v = t[name]
         v.copy_(torch.randn(v.shape, generator=g, device="cuda", dtype=torch.float32).to(v.dtype))
 
@@ -91,12 +96,13 @@ def test_graph_replays_match_eager():
     with torch.cuda.graph(graph):
         captured, routes = run(t)
     assert routes == ("sgn.cluster.nhwc.vec16", "sgn.cluster.nchw.vec16", "sgn.cluster.nchw.phase",
-                      "ssln.phase.vec16", "gated.flat.vec16"), routes
+                      "ssln.phase.vec16", "gated.flat.vec16", "ssln.flat.vec16"), routes
     torch.cuda.synchronize()
 
     names = ["ssln output", "ssln inv_std_var", "ssln S", "sln output", "sln mean", "sln inv_std_var",
              "gated Y", "sgn nhwc Y", "sgn nhwc S", "sgn nchw Y", "sgn nchw phased Y", "sgn nchw phased S",
-             "ssln phased output", "ssln phased S", "gated flat Y"]
+             "ssln phased output", "ssln phased S", "gated flat Y", "ssln flat output", "ssln flat inv_std_var",
+             "ssln flat S"]
     for rep in range(4):
         refill(t, seed=100 + rep)
         graph.replay()

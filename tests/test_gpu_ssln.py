@@ -102,6 +102,27 @@ SHAPES = [
 ]
 
 
+def flat_expected(dt, hidden, center=False, width=None):
+    """Whether the automatic choice takes the flat route, for a row whose
+    other routes would use `width`-byte accesses (element rows by default):
+    the measured rule of the library, restated."""
+    size = np.dtype(dt).itemsize
+    width = size if width is None else width
+    if width == size:
+        return hidden <= ((191 if center else 247) if size == 2 else (1020 if center else 255))
+    if width == 4 and size == 2:
+        if not 10 <= hidden <= 300:
+            return False
+        if not center:
+            return True
+        nvec = hidden // 2
+        slots = 1 << (nvec - 1).bit_length() if nvec <= 64 else 64 * ((nvec + 63) // 64)
+        return nvec / slots < 0.7
+    if width == 8 and size == 4:
+        return 42 <= hidden <= 1020
+    return False
+
+
 def expected_route(shape, dt):
     size = np.dtype(dt).itemsize
     hidden = shape[-1]
@@ -109,9 +130,12 @@ def expected_route(shape, dt):
     E = width // size
     name = {16: "vec16", 8: "vec8", 4: "vec4"}.get(width) if E > 1 else "scalar"
     nvec = hidden // E
-    # Rows that would be read element by element (all bases here are 16-byte
-    # aligned): the phased route reads whole aligned 16-byte vectors when a
-    # row needs more than 32 and at most 1024 x 4 of them.
+    # All bases here are 16-byte aligned.  The flat route where it measured
+    # faster; rows that would be read element by element beyond it take the
+    # phased route, which reads whole aligned 16-byte vectors when a row
+    # needs more than 32 and at most 1024 x 4 of them.
+    if flat_expected(dt, hidden, width=width):
+        return "ssln.flat.vec16"
     if E == 1 and 32 < hidden // (16 // size) + 2 <= 1024 * 4:
         return "ssln.phase.vec16"
     if nvec <= (64 if width < 16 else 48):
@@ -305,7 +329,8 @@ def test_phased_rows(dt, hidden, offset, center):
                                    desc(inv, (rows, 1)), desc(views["sum"], shp), stream))
             ref = oracle.skip_rms_norm(x["input"], x["skip"], x["gamma"], x["bias"], 1e-5,
                                        want_mean=True, want_inv_std_var=True, want_sum=True)
-        assert gn.last_route() == "ssln.phase.vec16"
+        assert gn.last_route() == ("ssln.flat.vec16" if flat_expected(dt, hidden, center)
+                                   else "ssln.phase.vec16")
         torch.cuda.synchronize()
         assert_close(to_host(views["output"]).reshape(rows, hidden), ref[0], "output")
         assert_close(to_host(mean), ref[1].reshape(-1), "mean")
@@ -314,3 +339,149 @@ def test_phased_rows(dt, hidden, offset, center):
         for k in ("output", "sum"):
             b = to_host(bufs[k])
             assert np.all(b[:pad + offset] == -7.0) and np.all(b[pad + offset + n:] == -7.0), k
+
+
+# ---------------------------------------------------------------- flat route
+def run_rows(x, eps, center, route="auto"):
+    """skip_rms_norm / skip_layer_norm with every output, and the oracle."""
+    with gn.force_route(route):
+        if center:
+            out = gn.skip_layer_norm(to_dev(x["input"]), to_dev(x["skip"]), to_dev(x["gamma"]),
+                                     to_dev(x.get("beta")), to_dev(x.get("bias")), eps, want_mean=True,
+                                     want_inv_std_var=True, want_sum=True)
+        else:
+            out = gn.skip_rms_norm(to_dev(x["input"]), to_dev(x["skip"]), to_dev(x["gamma"]),
+                                   to_dev(x.get("bias")), eps, want_mean=True, want_inv_std_var=True,
+                                   want_sum=True)
+        used = gn.last_route()
+    if center:
+        ref = oracle.skip_layer_norm(x["input"], x["skip"], x["gamma"], x.get("beta"), x.get("bias"), eps,
+                                     want_mean=True, want_inv_std_var=True, want_sum=True)
+    else:
+        ref = oracle.skip_rms_norm(x["input"], x["skip"], x["gamma"], x.get("bias"), eps, want_mean=True,
+                                   want_inv_std_var=True, want_sum=True)
+    torch.cuda.synchronize()
+    assert_close(to_host(out.output), ref[0], "output")
+    assert_close(to_host(out.mean), ref[1], "mean")
+    assert_close(to_host(out.inv_std_var), ref[2], "inv_std_var")
+    assert_bitwise(to_host(out.input_skip_bias_sum), ref[3], "S")
+    return used
+
+
+FLAT_ROWS = [
+    # (rows, hidden, dtype): odd widths through the table's limit, rows that
+    # share vectors (narrow), ragged row counts, several lane-group sizes.
+    (1001, 1, F16), (777, 3, F16), (513, 5, F16), (301, 7, F16), (900, 9, F16), (333, 17, F16),
+    (129, 57, F16), (100, 63, F16), (97, 127, F16), (61, 129, F16), (40, 247, F16), (37, 255, F16),
+    (13, 511, F16), (9, 777, F16), (5, 1015, F16),
+    (1000, 1, F32), (555, 3, F32), (301, 5, F32), (250, 33, F32), (99, 123, F32), (31, 127, F32),
+    (17, 509, F32), (7, 1019, F32),
+]
+
+
+@pytest.mark.parametrize("center", [False, True], ids=["rms", "layer"])
+@pytest.mark.parametrize("rows,hidden,dt", FLAT_ROWS,
+                         ids=[f"{r}x{h}-{np.dtype(d).name}" for r, h, d in FLAT_ROWS])
+def test_flat_rows(rows, hidden, dt, center):
+    """Odd rows read as one stream of aligned 16-byte vectors: the automatic
+    route for the lengths where it measured faster than reading them element
+    by element, and forced (the mean-removed form from 3 elements on); every
+    output against the oracle."""
+    if center:
+        w = workloads.sln("t", (rows, hidden), dt, beta=True, bias=True, epsilon=1e-5)
+    else:
+        w = workloads.ssln("t", (rows, hidden), dt, bias=rows % 2 == 1, epsilon=1e-5)
+    x = workloads.generate(w, seed=rows + hidden)
+    used = run_rows(x, 1e-5, center)
+    if center and hidden < 3:
+        assert used != "ssln.flat.vec16"
+    else:
+        assert (used == "ssln.flat.vec16") == flat_expected(dt, hidden, center)
+    # The same rows forced onto the flat route wherever it applies.
+    used = run_rows(x, 1e-5, center, route="flat")
+    assert (used == "ssln.flat.vec16") == (not center or hidden >= 3)
+
+
+@pytest.mark.parametrize("center", [False, True], ids=["rms", "layer"])
+@pytest.mark.parametrize("rows,hidden,dt", [(500, 4, F16), (300, 30, F16), (200, 100, F16), (64, 1000, F16),
+                                            (400, 6, F32), (100, 250, F32), (30, 1020, F32), (21, 1016, F16),
+                                            (333, 34, F16), (111, 130, F16), (222, 126, F16), (77, 186, F16),
+                                            (90, 42, F32), (60, 750, F32)])
+def test_flat_forced_on_vector_rows(rows, hidden, dt, center):
+    """Forced (route "flat"), rows that otherwise take 4-, 8- or 16-byte
+    vectors on other routes give the same results."""
+    w = (workloads.sln("t", (rows, hidden), dt, beta=False, bias=True, epsilon=1e-5) if center else
+         workloads.ssln("t", (rows, hidden), dt, bias=True, epsilon=1e-5))
+    x = workloads.generate(w, seed=hidden)
+    assert run_rows(x, 1e-5, center, route="flat") == "ssln.flat.vec16"
+    size = np.dtype(dt).itemsize
+    width = next(b for b in (16, 8, 4) if b > size and hidden * size % b == 0)
+    assert (run_rows(x, 1e-5, center) == "ssln.flat.vec16") == flat_expected(dt, hidden, center, width)
+
+
+@pytest.mark.parametrize("dt,hidden,offset,center", [
+    (F16, 7, 1, False), (F16, 127, 3, True), (F16, 1015, 5, False), (F16, 3, 7, True), (F16, 1, 2, False),
+    (F32, 5, 1, True), (F32, 123, 2, False), (F32, 1019, 3, True), (F32, 1, 1, False),
+])
+def test_flat_rows_off_the_grid(dt, hidden, offset, center):
+    """Through the C ABI: input, skip, output and S all `offset` elements
+    past a 16-byte boundary; results match the oracle and nothing outside
+    the outputs is written (canaries around them keep their pattern)."""
+    from group_normalization_amd._lib import lib, check as ck
+    rows, pad = 301, 64
+    if center:
+        w = workloads.sln("t", (rows, hidden), dt, beta=True, bias=True, epsilon=1e-5)
+    else:
+        w = workloads.ssln("t", (rows, hidden), dt, bias=True, epsilon=1e-5)
+    x = workloads.generate(w, seed=hidden + offset)
+    tdt = torch.float16 if dt == F16 else torch.float32
+    n = rows * hidden
+    bufs = {k: torch.full((n + 2 * pad,), -7.0, dtype=tdt, device="cuda") for k in ("input", "skip", "output", "sum")}
+    views = {k: b[pad + offset: pad + offset + n] for k, b in bufs.items()}
+    views["input"].copy_(to_dev(x["input"]).ravel())
+    views["skip"].copy_(to_dev(x["skip"]).ravel())
+    stats = torch.full((4 * pad + 2 * rows,), -7.0, dtype=torch.float32, device="cuda")
+    mean, inv = stats[pad: pad + rows], stats[3 * pad + rows: 3 * pad + 2 * rows]
+    d = {k: to_dev(x[k]) for k in ("gamma", "bias", "beta") if x.get(k) is not None}
+    shp, st = (rows, hidden), (rows, 1)
+    stream = torch.cuda.current_stream().cuda_stream
+    with gn.force_route("flat"):
+        if center:
+            ck(lib().skip_layer_norm(desc(views["input"], shp), desc(views["skip"], shp), desc(d["gamma"]),
+                                     desc(d["beta"]), desc(d["bias"]), 1e-5, desc(views["output"], shp),
+                                     desc(mean, st), desc(inv, st), desc(views["sum"], shp), stream))
+        else:
+            ck(lib().skip_rms_norm(desc(views["input"], shp), desc(views["skip"], shp), desc(d["gamma"]),
+                                   desc(d["bias"]), 1e-5, desc(views["output"], shp), desc(mean, st),
+                                   desc(inv, st), desc(views["sum"], shp), stream))
+    if center:
+        ref = oracle.skip_layer_norm(x["input"], x["skip"], x["gamma"], x["beta"], x["bias"], 1e-5,
+                                     want_mean=True, want_inv_std_var=True, want_sum=True)
+    else:
+        ref = oracle.skip_rms_norm(x["input"], x["skip"], x["gamma"], x["bias"], 1e-5,
+                                   want_mean=True, want_inv_std_var=True, want_sum=True)
+    assert gn.last_route() == "ssln.flat.vec16"
+    torch.cuda.synchronize()
+    assert_close(to_host(views["output"]).reshape(shp), ref[0], "output")
+    assert_close(to_host(mean), ref[1].reshape(-1), "mean")
+    assert_close(to_host(inv), ref[2].reshape(-1), "inv_std_var")
+    assert_bitwise(to_host(views["sum"]).reshape(shp), ref[3], "S")
+    for k in ("output", "sum"):
+        b = to_host(bufs[k])
+        assert np.all(b[:pad + offset] == -7.0) and np.all(b[pad + offset + n:] == -7.0), k
+    s_ = to_host(stats)
+    assert np.all(s_[:pad] == -7.0) and np.all(s_[pad + rows: 3 * pad + rows] == -7.0)
+    assert np.all(s_[3 * pad + 2 * rows:] == -7.0)
+
+
+def test_flat_edge_values_f16():
+    # Ties, overflow to inf, subnormals and -0 in odd rows on the flat route.
+    inp = np.array([[1, 1.0009765625, 65504, 65504, 2 ** -24, 2 ** -14, -0.0],
+                    [3, -0.0, 2 ** -24, 1, 0.5, 0.25, 2.0]], F16)
+    skip = np.array([[2 ** -11, 2 ** -11, 16, 8, 2 ** -24, -(2 ** -24), -0.0],
+                     [-3, -0.0, 2 ** -24, 2 ** -11, 0.5, 0.25, -2.0]], F16)
+    gamma = np.ones(7, F16)
+    ref, out, used = run_both(inp, skip, gamma, None, 1e-6)
+    assert used == "ssln.flat.vec16"
+    assert_bitwise(to_host(out.input_skip_bias_sum), ref[3], "S")
+    assert_close(to_host(out.output), ref[0], "output")
