@@ -27,6 +27,8 @@ large ones).  It prints one JSON object and a markdown table (stderr).
 
 ``--phases`` prints per-workgroup phase timings of the single-launch
 group-norm kernels from the library's phase-trace measurement build.
+``--contention`` times the group-norm ops alone and beside a copy kernel
+running on a second stream.
 """
 from __future__ import annotations
 
@@ -351,6 +353,66 @@ def config_table(args):
     print(json.dumps(out), flush=True)
 
 
+def contention_table(args):
+    """SkipGroupNorm's single-launch routes exchange moments among
+    workgroups that must be resident together; this times each group-norm
+    workload alone and while a 1 GiB copy kernel (2 GiB of traffic, every
+    CU busy) runs on a second stream of the same (default) priority, for
+    the automatic route and the three-launch split route (which waits on
+    nothing), events on the op's own stream."""
+    import torch
+    import group_normalization_amd as gn
+    import workloads
+
+    torch.cuda.set_device(0)
+    hev = HipEvents()
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    flush_a = torch.empty_like(src)
+    rows, lines = {}, ["| workload | route | alone median us | alone p90 us | beside a copy median us | "
+                       "beside a copy p90 us | beside a copy max us |", "|---|---|---|---|---|---|---|"]
+    for name in ("sgn_f16_nhwc_2x64x64x320", "sgn_f32_nchw_4x1280x32x32"):
+        o = Op(name, torch, gn, workloads)
+        for route in ("auto", "split"):
+            res = {}
+            for mode in ("alone", "contended"):
+                with gn.force_route(route):
+                    us = []
+                    for i in range(args.warmup + args.steps):
+                        gn.copy_(flush_a, src)  # cold cache
+                        torch.cuda.synchronize()
+                        a, b = hev.create(), hev.create()
+                        if mode == "contended":
+                            with torch.cuda.stream(side):
+                                gn.copy_(dst, src)
+                            # Let the copy occupy the CUs before the op is enqueued.
+                            time.sleep(20e-6)
+                        hev.record(a, main.cuda_stream)
+                        o.run()
+                        used = gn.last_route()
+                        hev.record(b, main.cuda_stream)
+                        torch.cuda.synchronize()
+                        if i >= args.warmup:
+                            us.append(hev.elapsed_ms(a, b) * 1e3)
+                        hev.destroy(a)
+                        hev.destroy(b)
+                us = np.array(us)
+                res[mode] = {"median_us": round(float(np.median(us)), 2),
+                             "p90_us": round(float(np.percentile(us, 90)), 2),
+                             "max_us": round(float(us.max()), 2)}
+            rows[f"{name} {used}"] = res
+            lines.append(f"| {name} | {used} | {res['alone']['median_us']} | {res['alone']['p90_us']} | "
+                         f"{res['contended']['median_us']} | {res['contended']['p90_us']} | "
+                         f"{res['contended']['max_us']} |")
+            log(f"{name} {used}: alone {res['alone']['median_us']} us, beside a copy "
+                f"{res['contended']['median_us']} us (p90 {res['contended']['p90_us']}, max {res['contended']['max_us']})")
+        del o
+    print("\n".join(lines), file=sys.stderr)
+    print(json.dumps({"contention": rows, "invocations": args.steps}), flush=True)
+
+
 PHASES = ["loads", "reduce", "publish + S", "exchange + combine", "normalize + Y"]
 
 
@@ -437,6 +499,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs", action="store_true",
                     help="time each reference workload alone (cold), and the oracle on it")
+    ap.add_argument("--contention", action="store_true",
+                    help="group-norm ops alone and beside a copy kernel on another stream")
     ap.add_argument("--phases", action="store_true",
                     help="per-phase timings of the single-launch group-norm kernels (needs the "
                          "phase-trace build of the library)")
@@ -450,6 +514,9 @@ def main():
         return
     if args.phases:
         phase_table(args)
+        return
+    if args.contention:
+        contention_table(args)
         return
 
     import torch

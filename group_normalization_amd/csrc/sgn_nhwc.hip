@@ -642,12 +642,19 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
                               : nhwc_kernel_for<float, half_t>(E, plan.R, a.skip_broadcast))
         : (a.param_dtype == 0 ? nhwc_kernel_for<half_t, float>(E, plan.R, a.skip_broadcast)
                               : nhwc_kernel_for<half_t, half_t>(E, plan.R, a.skip_broadcast));
-    // Slice-major where each cluster's span fits in the resident
-    // workgroups, else cluster-major (whose span, at most 64, always does).
+    // Cluster-major where the grid fits in one round of resident
+    // workgroups: when another stream's long-lived workgroups leave only
+    // part of the device free, the first free slots then hold whole clusters
+    // (2 x 64 x 64 x 320 float16 beside LDS-holding spinners on 230 / 240 of
+    // the 256 CUs: 48 / 74 us, against 348 / 951 us slice-major, whose
+    // clusters all wait out their bound and recompute), at 1-3 % alone.
+    // Larger grids slice-major where each cluster's span fits in the
+    // resident workgroups (15 % faster alone), else cluster-major (whose
+    // span, at most 64, always fits).
     const int64_t resident = resident_workgroups(kernel);
     if (!kernel || resident < 64) return false;
     NhwcLayout lay = nhwc_layout(a.N, plan, false);
-    if (lay.span > resident) lay = nhwc_layout(a.N, plan, true);
+    if (plan.K > 1 && (lay.grid <= resident || lay.span > resident)) lay = nhwc_layout(a.N, plan, true);
     // Beyond two rounds of resident workgroups the split route measured
     // faster (10-30 %, e.g. 8 x 128 x 128 x 320 float16: 86 against 112 us)
     // where its blocks hold whole pixels; wider pixels stay here (8 x 64 x 64
@@ -658,9 +665,10 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
     const int64_t grid = a.N * plan.NCB * plan.K;  // workgroups that do work
     if (split_whole_pixels && grid > 2 * resident) return false;
     static const char* const kNames[2][3] = {
-        {"sgn.cluster.nhwc.vec4", "sgn.cluster.nhwc.vec8", "sgn.cluster.nhwc.vec16"},
-        {"sgn.cluster.nhwc.cmajor.vec4", "sgn.cluster.nhwc.cmajor.vec8", "sgn.cluster.nhwc.cmajor.vec16"}};
-    *route = kNames[lay.Kp > 1 ? 1 : 0][E * size == 16 ? 2 : E * size == 8 ? 1 : 0];
+        {"sgn.cluster.nhwc.smajor.vec4", "sgn.cluster.nhwc.smajor.vec8", "sgn.cluster.nhwc.smajor.vec16"},
+        {"sgn.cluster.nhwc.vec4", "sgn.cluster.nhwc.vec8", "sgn.cluster.nhwc.vec16"}};
+    // Named by layout only where slices exchange (K > 1).
+    *route = kNames[lay.Kp > 1 || plan.K == 1 ? 1 : 0][E * size == 16 ? 2 : E * size == 8 ? 1 : 0];
     if (a.dtype == 0) {
         if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, lay, E, part, stream);
         else *err = launch_nhwc_typed<float, half_t>(a, plan, lay, E, part, stream);

@@ -209,15 +209,16 @@ NHWC_LIMIT_CASES = [
     (600, 16, 2, 2, F32, 2, True, "sgn.cluster.nhwc.vec16"),      # one slice per image: no exchange
     # Residency (MI355X: 256 CUs, two workgroups each at 16 pixels per
     # thread): 704 workgroups, more than are resident at once, but each
-    # image's 88 within reach of one another: one launch in two rounds.
-    (8, 640, 64, 64, F16, 32, False, "sgn.cluster.nhwc.vec16"),
+    # image's 88 within reach of one another: one launch in two rounds,
+    # slice-major block order.
+    (8, 640, 64, 64, F16, 32, False, "sgn.cluster.nhwc.smajor.vec16"),
     # One image of 1024 workgroups whose clusters would spread over 904
     # block ids slice-major, more than the device holds at once: the
     # cluster-major order (64 consecutive ids per cluster), two rounds.
-    (1, 512, 256, 256, F16, 32, False, "sgn.cluster.nhwc.cmajor.vec16"),
+    (1, 512, 256, 256, F16, 32, False, "sgn.cluster.nhwc.vec16"),
     # 36 slices of 1024 pixels (16 per thread) x 16 channel blocks: slice-
     # major spans 576 ids > 512 resident; cluster-major pads K to 40.
-    (1, 512, 192, 192, F16, 32, True, "sgn.cluster.nhwc.cmajor.vec16"),
+    (1, 512, 192, 192, F16, 32, True, "sgn.cluster.nhwc.vec16"),
     # 1344 workgroups, more than two rounds of the 512 resident: split.
     (8, 320, 128, 128, F16, 32, False, "sgn.split.nhwc.vec16"),
 ]
