@@ -28,7 +28,8 @@ large ones).  It prints one JSON object and a markdown table (stderr).
 ``--phases`` prints per-workgroup phase timings of the single-launch
 group-norm kernels from the library's phase-trace measurement build.
 ``--contention`` times the group-norm ops alone and beside a copy kernel
-running on a second stream.
+running on a second stream.  ``--summarize DIR`` writes the summaries under
+profiles/ from rocprofv3 output (no GPU needed).
 """
 from __future__ import annotations
 
@@ -50,7 +51,7 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E
 STEP_WORKLOADS = ["ssln_f16_16x2048x4096", "gated_f16_8x4096x4096_c128",
                   "sgn_f16_nhwc_2x64x64x320", "sgn_f32_nchw_4x1280x32x32"]
 DOMINANT = "ssln_f16_16x2048x4096"
-DOMINANT_KERNEL = "ssln_wave_kernel<half, 8 per vector, 4 vectors per lane, 2 waves per row>"
+DOMINANT_KERNEL = "ssln_wave_kernel<T=f16, E=8, NV=4, FULL=1, WPR=2, CENTER=0, WPB=4>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ssln_f16_16x2048x4096.json")
 KERNEL_SOURCES = ["group_normalization_amd/csrc/ssln.hip", "group_normalization_amd/csrc/device_common.h"]
 COPY_BYTES = 1 << 30
@@ -491,6 +492,313 @@ def host_cpu():
     return {"cpu_count": os.cpu_count(), "model": model}
 
 
+# ---------------------------------------------------------------------------
+# Profile summaries: rocprofv3 CSV output -> the text files under profiles/.
+
+PROF_COMMANDS = {
+    "kt": "rocprofv3 --kernel-trace --stats -f csv -d $REPO/gpurun_out/prof/kt -o bench -- "
+          "python3 $REPO/bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "ktc": "rocprofv3 --kernel-trace --stats -f csv -d $REPO/gpurun_out/prof/ktc -o configs -- "
+           "python3 $REPO/bench.py --configs --steps 60 --warmup 5 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/prof/fetch -o bench -- "
+             "python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/prof/write -o bench -- "
+             "python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "configs": "python3 $REPO/bench.py --configs --steps 60 --warmup 5",
+    "bench": "python3 $REPO/bench.py",
+}
+
+# Template parameters of each kernel family, as declared in the sources.
+KERNEL_PARAMS = {
+    "ssln_wave_kernel": "T E NV FULL WPR CENTER WPB",
+    "ssln_phase_kernel": "T E NV WPR CENTER WPB",
+    "ssln_block_kernel": "T E CENTER",
+    "ssln_segment_kernel": "T E L RPT CENTER",
+    "ssln_flat_kernel": "T VPT NARROW CENTER",
+    "gated_segment_kernel": "T E L VPL RPT LINES",
+    "gated_tile_kernel": "T E VPT",
+    "gated_flat_kernel": "T VPT NARROW",
+    "gated_row_kernel": "T E NV TPB",
+    "gated_block_kernel": "T E",
+    "sgn_cluster_kernel": "T M E R BCAST",
+    "sgn_cluster_phase_kernel": "T M E R BCAST",
+    "sgn_nhwc_cluster_kernel": "T M E R BCAST",
+    "sgn_stats_nhwc_kernel": "T E",
+    "sgn_norm_nhwc_kernel": "T M E",
+    "sgn_stats_group_kernel": "T E NCHW",
+    "sgn_norm_group_kernel": "T M E NCHW",
+}
+_TYPE_CODES = {"DF16_": "f16", "f": "f32", "d": "f64"}
+_TYPE_NAMES = {"_Float16": "f16", "__half": "f16", "half": "f16", "float": "f32", "double": "f64"}
+
+
+def _mangled_template_args(rest):
+    """Arguments of an Itanium-mangled template argument list (`I...E`) made
+    of the forms these kernels use: builtin types, int and bool literals."""
+    out, i = [], 1
+    while i < len(rest) and rest[i] != "E":
+        for code, t in _TYPE_CODES.items():
+            if rest.startswith(code, i):
+                out.append(t)
+                i += len(code)
+                break
+        else:
+            if rest[i] != "L":
+                return None
+            j = rest.index("E", i)
+            lit = rest[i + 1:j]  # e.g. "i8", "b1", "in3", "j4"
+            num = lit[1:].replace("n", "-")
+            out.append(("1" if num == "1" else "0") if lit[0] == "b" else num)
+            i = j + 1
+    return out
+
+
+def kernel_family(name):
+    """(family, template arguments or None) of a kernel name as rocprofv3
+    reports it (mangled or demangled)."""
+    import re
+
+    m = re.search(r"(\w+_kernel)<([^()]*)>\(", name)
+    if m:
+        args = [a.strip() for a in m.group(2).split(",")]
+        return m.group(1), [_TYPE_NAMES.get(a, {"true": "1", "false": "0"}.get(a, a)) for a in args]
+    if name.startswith("_ZN"):
+        # Walk the nested-name components by their length prefixes.
+        pos, fam = 3, None
+        while pos < len(name) and name[pos].isdigit():
+            k = pos
+            while name[k].isdigit():
+                k += 1
+            ln = int(name[pos:k])
+            fam, pos = name[k:k + ln], k + ln
+        rest = name[pos:]
+        if fam and fam.endswith("_kernel"):
+            return fam, (_mangled_template_args(rest) if rest.startswith("I") else None)
+    m = re.search(r"(\w+_kernel)\(", name)
+    if m:
+        return m.group(1), None
+    return name, None
+
+
+def kernel_label(name):
+    fam, args = kernel_family(name)
+    if name.startswith("__amd_rocclr_copyBuffer"):
+        return "runtime copyBuffer (host to device set-up)"
+    if "FillFunctor" in name:
+        return "torch fill (set-up)"
+    if args is None:
+        return fam
+    names = KERNEL_PARAMS.get(fam, "").split()
+    if len(names) == len(args):
+        return f"{fam}<" + ", ".join(f"{k}={v}" for k, v in zip(names, args)) + ">"
+    return f"{fam}<" + ", ".join(args) + ">"
+
+
+def step_workload(name):
+    """Workload of a benchmark-step (or next_ops) kernel, from its family:
+    each family serves exactly one workload of that run."""
+    fam, args = kernel_family(name)
+    if fam.startswith("ssln_"):
+        center = args[KERNEL_PARAMS[fam].split().index("CENTER")] if args else "0"
+        return EXTRA_STEP_WORKLOAD if center == "1" else "ssln_f16_16x2048x4096"
+    if fam.startswith("gated_"):
+        return "gated_f16_8x4096x4096_c128"
+    if fam.startswith("sgn_") and ("nhwc" in fam):
+        return "sgn_f16_nhwc_2x64x64x320"
+    if fam.startswith("sgn_"):
+        return "sgn_f32_nchw_4x1280x32x32"
+    return None
+
+
+EXTRA_STEP_WORKLOAD = "sln_f16_16x2048x4096"
+
+
+def _find_csv(d, suffix):
+    import glob
+
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        sys.exit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def _read_csv(path):
+    import csv
+
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _read_json_line(path):
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                return json.loads(line)
+    sys.exit(f"no JSON line in {path}")
+
+
+def _pmc_per_kernel(d, counter):
+    """{kernel name: (dispatches, average counter value per dispatch)} from a
+    rocprofv3 --pmc run (values summed over the rows of one dispatch)."""
+    per_dispatch = {}
+    for r in _read_csv(_find_csv(d, "counter_collection.csv")):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per_dispatch.items():
+        n, tot = out.get(name, (0, 0.0))
+        out[name] = (n + 1, tot + v)
+    return {k: (n, tot / n) for k, (n, tot) in out.items()}
+
+
+def summarize(args):
+    """Write profiles/*.md and the dominant kernel's traffic file from the
+    rocprofv3 output of the commands in PROF_COMMANDS (run on the GPU with
+    this same source tree), collected under one directory."""
+    import workloads
+
+    d = args.summarize
+    io = {n: workloads.io_bytes(w) for n, w in {**workloads.WORKLOADS, **workloads.EXTRA_WORKLOADS}.items()}
+    prof = os.path.join(ROOT, "profiles")
+    cmd = lambda k: f"cd /tmp && export TMPDIR=/tmp && {PROF_COMMANDS[k]}"
+
+    # --- Kernel trace of the benchmark step.
+    stats = _read_csv(_find_csv(os.path.join(d, "kt"), "kernel_stats.csv"))
+    kt_bench = _read_json_line(os.path.join(d, "kt", "bench.json"))
+    lines = ["# Kernel trace of the benchmark step (all hot-path kernels)", "",
+             "Workloads: " + ", ".join(STEP_WORKLOADS) + "; the next_ops leg adds "
+             f"{EXTRA_STEP_WORKLOAD}. One MI355X (gfx950).", "",
+             "Command (from the repository root on the GPU host, `$REPO` = repository root):", "",
+             "```", cmd("kt") + " > $REPO/gpurun_out/prof/kt/bench.json", "```", "",
+             "`rocprofv3 --stats` kernel summary (`bench_kernel_stats.csv`). The GB/s column is the "
+             "workload's algorithmic bytes over the kernel's average duration:", "",
+             "| kernel | workload | calls | avg us | min us | max us | GB/s (avg) |",
+             "|---|---|---|---|---|---|---|"]
+    dom_avg_us = None
+    for r in stats:
+        w = step_workload(r["Name"])
+        avg = float(r["AverageNs"]) / 1e3
+        gbps = f"{io[w] / avg / 1e3:.1f}" if w else ""
+        if w == DOMINANT:
+            dom_avg_us = avg
+        lines.append(f"| {kernel_label(r['Name'])} | {w or ''} | {r['Calls']} | {avg:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {gbps} |")
+    lines += ["", "Same run, bench.py's HIP-event timing (per-op pass, device-scope release events, "
+              "which also span each launch):", "",
+              "| op | avg us (events) | GB/s | fraction of 8 TB/s |", "|---|---|---|---|"]
+    for name, v in {**kt_bench["ops"], **kt_bench["next_ops"]}.items():
+        lines.append(f"| {name} | {v['avg_us']} | {v['gbps']} | {v['frac_of_peak']} |")
+    ev = kt_bench["ops"][DOMINANT]["avg_us"]
+    lines += ["", f"Dominant kernel ({DOMINANT}): rocprofv3 average {dom_avg_us:.2f} us, event "
+              f"average {ev} us. Under the profiler, bench value {kt_bench['value']} GB/s and copy "
+              f"ceiling {kt_bench['copy_ceiling_gbps']} GB/s."]
+    bench_path = os.path.join(d, "bench.json")
+    if os.path.exists(bench_path):
+        b = _read_json_line(bench_path)
+        rf = b["roofline"]
+        lines += ["", "Without the profiler (`" + PROF_COMMANDS["bench"] + "`), the same tree: value "
+                  f"{b['value']} GB/s ({b['ms_per_step']} ms per step); dominant kernel "
+                  f"{rf['achieved']} GB/s by events (frac {rf['frac']}); copy kernel "
+                  f"{b['copy_ceiling_gbps']} GB/s; hipMemcpyDtoD {b['memcpy_dtod_ceiling_gbps']} GB/s."]
+    with open(os.path.join(prof, "kernel_trace_bench_step.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # --- HBM traffic from the two counter passes.
+    fetch = _pmc_per_kernel(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write = _pmc_per_kernel(os.path.join(d, "write"), "WRITE_SIZE")
+    copy_name = next(k for k in fetch if kernel_family(k)[0] == "copy16_kernel")
+    fu, wu = COPY_BYTES / fetch[copy_name][1], COPY_BYTES / write[copy_name][1]
+    lines = ["# HBM traffic from hardware counters (FETCH_SIZE, WRITE_SIZE)", "",
+             "Two counter passes over the benchmark command, one counter each:", "", "```",
+             cmd("fetch"), cmd("write"), "```", "",
+             f"Calibration: the library's copy kernel moves exactly 1 GiB in and 1 GiB out per "
+             f"launch ({fetch[copy_name][0]} launches). It reads FETCH_SIZE = {fetch[copy_name][1]:.1f} "
+             f"and WRITE_SIZE = {write[copy_name][1]:.1f} per dispatch, so one FETCH_SIZE unit is "
+             f"{fu:.2f} bytes and one WRITE_SIZE unit {wu:.2f} bytes on this part.", "",
+             "| kernel | workload | dispatches | FETCH_SIZE | WRITE_SIZE | fetched bytes | written bytes | "
+             "total bytes | algorithmic bytes | total / algorithmic |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    dom = None
+    for name in fetch:
+        w = step_workload(name)
+        fv, wv = fetch[name][1], write.get(name, (0, 0.0))[1]
+        fb, wb = fv * fu, wv * wu
+        alg = io.get(w) if w else (2 * COPY_BYTES if name == copy_name else None)
+        ratio = f"{(fb + wb) / alg:.4f}" if alg else ""
+        lines.append(f"| {kernel_label(name)} | {w or ''} | {fetch[name][0]} | {fv:.1f} | {wv:.1f} | "
+                     f"{fb:,.0f} | {wb:,.0f} | {fb + wb:,.0f} | {f'{alg:,}' if alg else ''} | {ratio} |")
+        if w == DOMINANT:
+            dom = {"kernel": kernel_label(name), "workload": DOMINANT,
+                   "hbm_bytes_per_launch": round(fb + wb), "fetch_bytes_per_launch": round(fb),
+                   "write_bytes_per_launch": round(wb), "algorithmic_bytes_per_launch": io[w],
+                   "fetch_unit_bytes": round(fu, 4), "write_unit_bytes": round(wu, 4),
+                   "source": "profiles/hbm_traffic_pmc_bench_step.md",
+                   "kernel_source_sha256": kernel_source_hash()}
+    lines += ["", "Every input is read once and every output written once when total / algorithmic "
+              "is 1; the remainder is parameter, workspace and counter-granularity traffic."]
+    with open(os.path.join(prof, "hbm_traffic_pmc_bench_step.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if dom is None:
+        sys.exit(f"no {DOMINANT} kernel in the counter runs")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(dom, f, indent=1)
+        f.write("\n")
+
+    # --- The five workloads alone: per-dispatch durations, attributed in order.
+    trace = _read_csv(_find_csv(os.path.join(d, "ktc"), "kernel_trace.csv"))
+    runs = []  # [(kernel name, [durations])] of consecutive non-copy dispatches
+    for r in trace:
+        fam = kernel_family(r["Kernel_Name"])[0]
+        if fam == "copy16_kernel" or "FillFunctor" in r["Kernel_Name"] or "rocclr" in r["Kernel_Name"]:
+            continue
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if runs and runs[-1][0] == r["Kernel_Name"]:
+            runs[-1][1].append(dur)
+        else:
+            runs.append((r["Kernel_Name"], [dur]))
+    if len(runs) != len(workloads.ORDER):
+        sys.exit(f"expected {len(workloads.ORDER)} runs of op kernels in the configs trace, found {len(runs)}")
+    lines = ["# The five reference workloads, each alone and cold: rocprofv3 kernel trace", "",
+             "Command (from the repository root on the GPU host, `$REPO` = repository root):", "", "```",
+             cmd("ktc"), "```", "",
+             "Every invocation follows a 1 GiB copy (the copy kernel), so each starts from a cold cache. "
+             "Durations per dispatch come from `configs_kernel_trace.csv` (5 warm-up and 60 timed "
+             "dispatches per workload, all counted).", "",
+             "| workload | kernel | dispatches | median us | min us | p90 us | GB/s (median) | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|"]
+    for wname, (kname, durs) in zip(workloads.ORDER, runs):
+        a = np.array(durs)
+        med = float(np.median(a))
+        gbps = io[wname] / med / 1e3
+        lines.append(f"| {wname} | {kernel_label(kname)} | {len(a)} | {med:.2f} | {a.min():.2f} | "
+                     f"{np.percentile(a, 90):.2f} | {gbps:.1f} | {100 * gbps / PEAK_GBPS:.1f} |")
+    cfg_path = os.path.join(d, "configs.json")
+    if os.path.exists(cfg_path):
+        c = _read_json_line(cfg_path)
+        h = c.get("host", {})
+        lines += ["", "Same workloads in a separate run without the profiler (`" + PROF_COMMANDS["configs"] +
+                  "`). Times are HIP events per invocation: device-scope release events around the op, "
+                  "spanning the launch. The same-bytes copy is the copy kernel moving the workload's "
+                  "byte count, also cold. The oracle runs on one thread. Copy ceiling "
+                  f"{c['copy_ceiling_gbps']} GB/s, hipMemcpyDtoD {c['memcpy_dtod_ceiling_gbps']} GB/s; host: "
+                  f"{h.get('model', '?')}, {h.get('cpu_count', '?')} logical CPUs, oracle on 1.", "",
+                  "| workload | median us (events) | GB/s | % of 8 TB/s | % of copy | same-bytes copy us | "
+                  "% of same-bytes copy | oracle s | oracle GB/s |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for r in c["configs"]:
+            lines.append(f"| {r['workload']} | {r['median_us']} | {r['gbps']} | {100 * r['frac_of_peak']:.1f} | "
+                         f"{100 * r['frac_of_copy']:.1f} | {r['same_bytes_copy_us']} | "
+                         f"{100 * r['frac_of_same_bytes_copy']:.1f} | {r.get('oracle_s', '')} | "
+                         f"{r.get('oracle_gbps', '')} |")
+    with open(os.path.join(prof, "configs_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"wrote profiles/kernel_trace_bench_step.md, hbm_traffic_pmc_bench_step.md, configs_kernel_trace.md, "
+        f"{os.path.basename(TRAFFIC_FILE)} (dominant kernel {dom['hbm_bytes_per_launch']:,} bytes per launch)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -504,7 +812,12 @@ def main():
     ap.add_argument("--phases", action="store_true",
                     help="per-phase timings of the single-launch group-norm kernels (needs the "
                          "phase-trace build of the library)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write the profiles/ summaries from rocprofv3 output collected under DIR")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the operators need no communication and this "
               "build runs on a single MI355X; use --gpus 1", file=sys.stderr)
