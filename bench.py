@@ -28,7 +28,8 @@ large ones).  It prints one JSON object and a markdown table (stderr).
 ``--phases`` prints per-workgroup phase timings of the single-launch
 group-norm kernels from the library's phase-trace measurement build.
 ``--contention`` times the group-norm ops alone and beside a copy kernel
-running on a second stream.  ``--summarize DIR`` writes the summaries under
+running on a second stream.  ``--shapes`` times general shapes (rows wider
+than the registers hold, ...) on the automatic and on forced routes.  ``--summarize DIR`` writes the summaries under
 profiles/ from rocprofv3 output (no GPU needed).
 """
 from __future__ import annotations
@@ -162,13 +163,17 @@ def copy_ceilings(torch, gn, hev, stream, reps=10):
 class Op:
     """One workload's device tensors and a closure that enqueues the op."""
 
-    def __init__(self, name, torch, gn, workloads):
-        w = workloads.WORKLOADS.get(name) or workloads.EXTRA_WORKLOADS[name]
+    def __init__(self, name, torch, gn, workloads, w=None, d=None):
+        """The named workload with its seeded host inputs, or workload ``w``
+        with the device tensors ``d`` already drawn."""
+        if w is None:
+            w = workloads.WORKLOADS.get(name) or workloads.EXTRA_WORKLOADS[name]
         self.name = name
         self.bytes = workloads.io_bytes(w)
-        host = workloads.generate(w)
-        d = {k: torch.from_numpy(v).cuda() for k, v in host.items()}
-        del host
+        if d is None:
+            host = workloads.generate(w)
+            d = {k: torch.from_numpy(v).cuda() for k, v in host.items()}
+            del host
         a = w.attrs
         if w.op == "skip_rms_norm":
             want_sum = "input_skip_bias_sum" in w.outputs
@@ -412,6 +417,77 @@ def contention_table(args):
         del o
     print("\n".join(lines), file=sys.stderr)
     print(json.dumps({"contention": rows, "invocations": args.steps}), flush=True)
+
+
+def shape_cases(workloads):
+    """General shapes beyond the five workloads, each with the forced
+    routes it is compared against: (label, workload, alternative routes).
+    Tensors of about 2^27 elements (256 MB in float16), so every call
+    starts from a cold last-level cache."""
+    F16, F32 = workloads.F16, workloads.F32
+    out = []
+
+    def add(label, w, alts):
+        out.append((label, w, alts))
+
+    # Rows beyond one workgroup's registers (the wide routes).
+    for h, dt in ((131072, F16), (100000, F16), (139264, F16), (65536, F32), (50004, F32)):
+        rows = (1 << 27) // h
+        n = np.dtype(dt).name
+        add(f"ssln_{n}_{rows}x{h}", workloads.ssln("w", (rows, h), dt, bias=True, epsilon=1e-6,
+                                                   outputs=("output", "input_skip_bias_sum")), ())
+    rows = (1 << 27) // 131072
+    add(f"sln_float16_{rows}x131072", workloads.sln("w", (rows, 131072), F16, beta=True, bias=False,
+                                                    epsilon=1e-5, outputs=("output", "input_skip_bias_sum")),
+        ())
+    for c, dt in ((65536, F16), (131072, F16), (139264, F16), (65536, F32)):
+        rows = (1 << 27) // c
+        add(f"gated_{np.dtype(dt).name}_{rows}x{c}_c{c}", workloads.gated("w", (rows, c), c, dt, epsilon=1e-5),
+            ())
+    return out
+
+
+def shapes_table(args):
+    """Each general shape alone, cold, on the automatic route and on each
+    forced alternative (see shape_cases)."""
+    import torch
+    import group_normalization_amd as gn
+    import workloads
+
+    torch.cuda.set_device(0)
+    hev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    rows, lines = [], ["| shape | route | median us | GB/s | % of 8 TB/s |", "|---|---|---|---|---|"]
+    for label, w, alts in shape_cases(workloads):
+        o = Op(label, torch, gn, workloads, w=w, d=workloads.generate_on_device(w, 0, torch))
+        for route in ("auto",) + tuple(alts):
+            with gn.force_route(route):
+                for _ in range(args.warmup):
+                    gn.copy_(dst, src)
+                    o.run()
+                used = gn.last_route()
+                pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+                for a, b in pairs:
+                    gn.copy_(dst, src)
+                    hev.record(a, stream)
+                    o.run()
+                    hev.record(b, stream)
+                torch.cuda.synchronize()
+            us = float(np.median([hev.elapsed_ms(a, b) * 1e3 for a, b in pairs]))
+            for a, b in pairs:
+                hev.destroy(a)
+                hev.destroy(b)
+            gbps = o.bytes / us / 1e3
+            rows.append({"shape": label, "forced": route, "route": used, "bytes": o.bytes,
+                         "median_us": round(us, 2), "gbps": round(gbps, 1)})
+            lines.append(f"| {label} | {used}{'' if route == 'auto' else ' (forced)'} | {us:.2f} | "
+                         f"{gbps:.1f} | {100 * gbps / PEAK_GBPS:.1f} |")
+            log(f"{label} {used}: {us:.2f} us, {gbps:.1f} GB/s")
+        del o
+    print("\n".join(lines), file=sys.stderr)
+    print(json.dumps({"shapes": rows, "invocations": args.steps}), flush=True)
 
 
 PHASES = ["loads", "reduce", "publish + S", "exchange + combine", "normalize + Y"]
@@ -812,6 +888,8 @@ def main():
     ap.add_argument("--phases", action="store_true",
                     help="per-phase timings of the single-launch group-norm kernels (needs the "
                          "phase-trace build of the library)")
+    ap.add_argument("--shapes", action="store_true",
+                    help="general shapes (wide rows, ...) on the automatic and forced routes")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output collected under DIR")
     args = ap.parse_args()
@@ -830,6 +908,9 @@ def main():
         return
     if args.contention:
         contention_table(args)
+        return
+    if args.shapes:
+        shapes_table(args)
         return
 
     import torch

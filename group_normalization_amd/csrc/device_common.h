@@ -112,6 +112,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 // at most kFlatTable - E elements.
 constexpr int kFlatTable = 1024;
 
+// Wide-row kernels (one 1024-thread workgroup per row): sixteen-byte vectors
+// per lane held in VGPRs and in LDS (9 x 16 KB of gfx950's 160 KB per
+// workgroup), and the vectors per lane of each pipelined LDS chunk.
+constexpr int kWideThreads = 1024;
+constexpr int kWideRegs = 8;
+constexpr int kWideLds = 9;
+constexpr int kWideChunk = 2;
+
 // Flat plan for rows of C <= kFlatTable - E elements: rt whole rows per wave
 // such that the vectors they touch (at any offset from the grid) fit the
 // wave's 64 * VPT vector slots, in the smaller tile (VPT = 2 for float16, 4

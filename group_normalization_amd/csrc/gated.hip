@@ -41,6 +41,10 @@
 //            it in registers (at most four 16-byte vectors or eight
 //            narrower accesses per thread); the waves' sums meet in LDS and
 //            are added as a pairwise tree in wave order.
+//   wide     rows of 16-byte vectors beyond the row route, up to 272 KB of X:
+//            one 1024-thread workgroup per row holding X alone (8 vectors
+//            per lane in VGPRs, up to 9 more in LDS); gate and scale are read
+//            after the statistic (gated_wide_kernel).
 //   block    one 256-thread workgroup per row for wider rows; X is read
 //            twice, four vectors per thread in flight per pass.
 // scale is loaded once per thread and kept in registers as float32 (flat: an
@@ -427,6 +431,122 @@ gated_row_kernel(const T* __restrict__ X, const T* __restrict__ scale,
 // Block route: two passes over X, four vectors per thread per step (the
 // loads of a step go out together; lanes past the row re-read its last
 // vector).  E == 1 is the scalar route.
+// Spans wider than the row route holds (4096 sixteen-byte vectors, 64 KB,
+// with X and gate both in registers), up to kWideRegs + kWideLds vectors
+// per lane (272 KB of X): one 1024-thread workgroup per span keeps X alone
+// -- its first kWideRegs vectors per lane in VGPRs, the rest in LDS -- and
+// reads gate and scale only to form the output, after the statistic, so
+// every tensor is still read once.  Lane t holds vectors t + 1024 v; its
+// LDS vectors t + 1024 (kWideRegs + j) sit at tail[1024 j + t].  Loads of
+// the LDS part (and later of its gate and scale) stream through in chunks of
+// kWideChunk vectors per lane, the next chunk's loads issued before the
+// current one is used, every load unconditional with a clamped index.
+template <typename T>
+__global__ void __launch_bounds__(kWideThreads)
+gated_wide_kernel(const T* __restrict__ X, const T* __restrict__ scale,
+                  const T* __restrict__ gate, T* __restrict__ Y, int nvec, float span_f, float eps) {
+    constexpr int E = VecWidth<T>::value;
+    using V = Vec<T, E>;
+    constexpr int L = kWideThreads, NV = kWideRegs, CH = kWideChunk;
+    __shared__ V tail[kWideLds * L];
+    __shared__ float wave_part[L / 64];
+    const int t = threadIdx.x;
+    const int64_t base = int64_t(blockIdx.x) * nvec;
+    const int ntail = nvec > NV * L ? (nvec - NV * L + L - 1) / L : 0;  // uniform, <= kWideLds
+    const int nch = (ntail + CH - 1) / CH;
+    auto clamp = [&](int idx) { return idx < nvec ? idx : nvec - 1; };
+    auto tail_idx = [&](int j) { return NV * L + j * L + t; };
+
+    V xs[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) xs[v] = load_vec_stream<T, E>(X, base + clamp(v * L + t));
+    V ax[CH], bx[CH];
+    auto load_chunk = [&](int c, V(&x)[CH]) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) x[i] = load_vec_stream<T, E>(X, base + clamp(tail_idx(c * CH + i)));
+    };
+    if (nch > 0) load_chunk(0, ax);
+    float acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        if (v * L + t < nvec) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float x = to_f32(xs[v].v[e]);
+                acc = fmaf_(x, x, acc);
+            }
+        }
+    auto keep_chunk = [&](int c, const V(&x)[CH]) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int j = c * CH + i;
+            if (tail_idx(j) < nvec) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float xv = to_f32(x[i].v[e]);
+                    acc = fmaf_(xv, xv, acc);
+                }
+                tail[j * L + t] = x[i];
+            }
+        }
+    };
+    for (int c = 0; c < nch; c += 2) {
+        load_chunk(c + 1 < nch ? c + 1 : nch - 1, bx);
+        keep_chunk(c, ax);
+        load_chunk(c + 2 < nch ? c + 2 : nch - 1, ax);
+        if (c + 1 < nch) keep_chunk(c + 1, bx);
+    }
+    // Span total: butterfly in each wave, then the 16 wave sums in wave order
+    // (each lane reads back only its own LDS vectors).
+    float total = segment_sum<64>(acc);
+    if ((t & 63) == 0) wave_part[t >> 6] = total;
+    __syncthreads();
+    total = wave_part[0];
+#pragma unroll
+    for (int w = 1; w < L / 64; ++w) total += wave_part[w];
+    const float r = inv_sqrt(total / span_f + eps);
+
+    auto form = [&](const V& xv, const V& gv, const V& sv) {
+        V out;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            out.v[e] = from_f32<T>(to_f32(xv.v[e]) * r * to_f32(sv.v[e]) * silu_f32(to_f32(gv.v[e])));
+        return out;
+    };
+    V ag[CH], as[CH], bg[CH], bs[CH];
+    auto load_par = [&](int c, V(&g)[CH], V(&sc)[CH]) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int idx = clamp(tail_idx(c * CH + i));
+            g[i] = load_vec_stream<T, E>(gate, base + idx);
+            sc[i] = load_vec<T, E>(scale, idx);
+        }
+    };
+    if (nch > 0) load_par(0, ag, as);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int idx = v * L + t;
+        const V gv = load_vec_stream<T, E>(gate, base + clamp(idx));
+        const V sv = load_vec<T, E>(scale, clamp(idx));
+        const V out = form(xs[v], gv, sv);
+        if (idx < nvec) store_vec_stream<T, E>(Y, base + idx, out);
+    }
+    auto out_chunk = [&](int c, const V(&g)[CH], const V(&sc)[CH]) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int j = c * CH + i;
+            const int idx = tail_idx(j);
+            if (idx < nvec) store_vec_stream<T, E>(Y, base + idx, form(tail[j * L + t], g[i], sc[i]));
+        }
+    };
+    for (int c = 0; c < nch; c += 2) {
+        load_par(c + 1 < nch ? c + 1 : nch - 1, bg, bs);
+        out_chunk(c, ag, as);
+        load_par(c + 2 < nch ? c + 2 : nch - 1, ag, as);
+        if (c + 1 < nch) out_chunk(c + 1, bg, bs);
+    }
+}
+
 template <typename T, int E>
 __global__ void __launch_bounds__(256)
 gated_block_kernel(const T* __restrict__ X, const T* __restrict__ scale,
@@ -580,6 +700,19 @@ hipError_t launch_row_for(const GatedArgs& a, int nvec, hipStream_t stream) {
     if (nv512 <= kNvMax && 512 * nv512 <= 1024 * nv1024)
         return launch_row_nv<T, E, 512>(a, nvec, nv512, stream);
     return launch_row_nv<T, E, 1024>(a, nvec, nv1024, stream);
+}
+
+// The wide route (see gated_wide_kernel): spans of 16-byte vectors beyond
+// the row route, one 1024-thread workgroup per span.
+constexpr int64_t kMaxWideVectors = int64_t(kWideThreads) * (kWideRegs + kWideLds);
+
+template <typename T>
+hipError_t launch_wide(const GatedArgs& a, int64_t nvec, hipStream_t stream) {
+    hipLaunchKernelGGL(gated_wide_kernel<T>, dim3(unsigned(a.rows)), dim3(kWideThreads), 0, stream,
+                       static_cast<const T*>(a.X), static_cast<const T*>(a.scale),
+                       static_cast<const T*>(a.gate), static_cast<T*>(a.Y), int(nvec), float(a.span),
+                       a.epsilon);
+    return hipGetLastError();
 }
 
 template <typename T, int E>
@@ -768,6 +901,14 @@ hipError_t launch_gated_t(const GatedArgs& a, Route want, hipStream_t stream, co
         }
         *route = "gated.row.scalar";
         return launch_row_for<T, 1>(a, int(nvec), stream);
+    }
+    // Wider spans of 16-byte vectors: the wide route while a span fits one
+    // workgroup's registers and LDS (one workgroup per span keeps the grid
+    // below 2^32 work-items).
+    if (want != Route::Block && E == VecWidth<T>::value && nvec <= kMaxWideVectors &&
+        a.rows < (int64_t(1) << 22)) {
+        *route = "gated.wide.vec16";
+        return launch_wide<T>(a, nvec, stream);
     }
     // The block route: wider rows, or forced (then with scalar accesses).
     if (want == Route::Block) E = 1;

@@ -30,6 +30,10 @@
 //          row length, or data tensors sharing a base 2 or 6 bytes off a
 //          16-byte boundary): aligned 16-byte vectors read across row
 //          boundaries, boundary elements masked (ssln_phase_kernel).
+//   wide   rows of 16-byte vectors beyond the register routes, up to 272 KB:
+//          one 1024-thread workgroup per row, S held in VGPRs (8 vectors
+//          per lane) and LDS (up to 9 more), so still one read and one write
+//          (ssln_wide_kernel).
 //   block  one 256-thread workgroup per row for any wider row: S is formed
 //          twice (once for the statistic, once for the output; three times
 //          with the mean removed), reading the inputs again each time.
@@ -204,6 +208,208 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
             if (use_lines) store_vec_run<T, E>(output + base * E, idx, out, out_run);
             else store_vec_stream<T, E>(output, base + idx, out);
         }
+    }
+}
+
+// Rows wider than one workgroup's registers hold (more than 1024 lanes x
+// kWideRegs sixteen-byte vectors: 128 KB, 65536 float16 / 32768 float32
+// elements), up to kWideRegs + kWideLds vectors per lane (272 KB): one
+// 1024-thread workgroup per row keeps the row's first kWideRegs vectors per
+// lane in VGPRs, as the widest wave route does, and S of the rest in LDS
+// (gfx950 gives a workgroup up to 160 KB), so the row is still read once and
+// written once.  Lane t holds vectors t + 1024 v; its LDS vectors are
+// t + 1024 (kWideRegs + j), stored at tail[1024 j + t] (consecutive lanes,
+// consecutive 16-byte slots).  The LDS part streams through in chunks of
+// kWideChunk vectors per lane, the next chunk's loads issued before the
+// current one is formed (ping-pong buffers, every load unconditional with
+// its index clamped, so none waits behind a branch); bias (or gamma's
+// address in its place) is fetched with the chunk.  Output and the
+// parameters of the LDS part follow the same pattern.
+template <typename T, bool CENTER>
+__global__ void __launch_bounds__(kWideThreads)
+ssln_wide_kernel(const T* __restrict__ input, const T* __restrict__ skip,
+                 const T* __restrict__ gamma, const T* __restrict__ beta,
+                 const T* __restrict__ biasp, bool has_bias, T* __restrict__ output,
+                 float* __restrict__ mean, float* __restrict__ inv_std_var, T* __restrict__ sum,
+                 int nvec, float hidden_f, float eps, uint32_t beta_mask) {
+    constexpr int E = VecWidth<T>::value;
+    using V = Vec<T, E>;
+    constexpr int L = kWideThreads, NV = kWideRegs, CH = kWideChunk;
+    __shared__ V tail[kWideLds * L];
+    __shared__ float wave_part[L / 64];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int64_t base = row * nvec;
+    // LDS vectors per lane (at most kWideLds: the host checks the width) and
+    // chunks of them; both uniform.
+    const int ntail = nvec > NV * L ? (nvec - NV * L + L - 1) / L : 0;
+    const int nch = (ntail + CH - 1) / CH;
+    auto clamp = [&](int idx) { return idx < nvec ? idx : nvec - 1; };
+    auto tail_idx = [&](int j) { return NV * L + j * L + t; };
+
+    V xs[NV], ks[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int idx = clamp(v * L + t);
+        xs[v] = load_vec_stream<T, E>(input, base + idx);
+        ks[v] = load_vec_stream<T, E>(skip, base + idx);
+    }
+    V ax[CH], ak[CH], ab[CH], bx[CH], bk[CH], bb[CH];
+    auto load_chunk = [&](int c, V(&x)[CH], V(&k)[CH], V(&b)[CH]) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int idx = clamp(tail_idx(c * CH + i));
+            x[i] = load_vec_stream<T, E>(input, base + idx);
+            k[i] = load_vec_stream<T, E>(skip, base + idx);
+            b[i] = load_vec<T, E>(biasp, idx);
+        }
+    };
+    if (nch > 0) load_chunk(0, ax, ak, ab);
+
+    float shift = 0.0f;  // as in ssln_wave_kernel: statistics about S[0]
+    if constexpr (CENTER) {
+        T rounded;
+        shift = residual_sum<T>(to_f32(input[base * E]), to_f32(skip[base * E]), has_bias,
+                                to_f32(biasp[0]), rounded);
+    }
+
+    V ss[NV];
+    float acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int idx = v * L + t;
+        const V bv = load_vec<T, E>(biasp, clamp(idx));
+        if (idx < nvec) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float s = residual_sum<T>(to_f32(xs[v].v[e]), to_f32(ks[v].v[e]), has_bias,
+                                                to_f32(bv.v[e]), ss[v].v[e]);
+                if constexpr (CENTER) acc += s - shift;
+                else acc = fmaf_(s, s, acc);
+            }
+            if (sum) store_vec_stream<T, E>(sum, base + idx, ss[v]);
+        }
+    }
+    auto form_chunk = [&](int c, const V(&x)[CH], const V(&k)[CH], const V(&b)[CH]) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int j = c * CH + i;
+            const int idx = tail_idx(j);
+            if (idx < nvec) {
+                V sv;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float s = residual_sum<T>(to_f32(x[i].v[e]), to_f32(k[i].v[e]), has_bias,
+                                                    to_f32(b[i].v[e]), sv.v[e]);
+                    if constexpr (CENTER) acc += s - shift;
+                    else acc = fmaf_(s, s, acc);
+                }
+                tail[j * L + t] = sv;
+                if (sum) store_vec_stream<T, E>(sum, base + idx, sv);
+            }
+        }
+    };
+    for (int c = 0; c < nch; c += 2) {
+        load_chunk(c + 1 < nch ? c + 1 : nch - 1, bx, bk, bb);
+        form_chunk(c, ax, ak, ab);
+        load_chunk(c + 2 < nch ? c + 2 : nch - 1, ax, ak, ab);
+        if (c + 1 < nch) form_chunk(c + 1, bx, bk, bb);
+    }
+
+    // Row total: butterfly in each wave, then the 16 wave sums in wave order.
+    auto row_total = [&](float part) {
+        float total = segment_sum<64>(part);
+        __syncthreads();  // earlier readers of wave_part are done; tail is complete
+        if ((t & 63) == 0) wave_part[t >> 6] = total;
+        __syncthreads();
+        total = wave_part[0];
+#pragma unroll
+        for (int w = 1; w < L / 64; ++w) total += wave_part[w];
+        return total;
+    };
+    // Each lane reads back only its own LDS vectors, so the barriers in
+    // row_total are for wave_part alone.
+    float md = 0.0f, r;
+    if constexpr (!CENTER) {
+        r = inv_sqrt(row_total(acc) / hidden_f + eps);
+    } else {
+        md = row_total(acc) / hidden_f;
+        float dev = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            if (v * L + t < nvec) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = (to_f32(ss[v].v[e]) - shift) - md;
+                    dev = fmaf_(d, d, dev);
+                }
+            }
+        }
+        for (int j = 0; j < ntail; ++j) {
+            if (tail_idx(j) < nvec) {
+                const V sv = tail[j * L + t];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = (to_f32(sv.v[e]) - shift) - md;
+                    dev = fmaf_(d, d, dev);
+                }
+            }
+        }
+        r = inv_sqrt(row_total(dev) / hidden_f + eps);
+    }
+    if (t == 0) {
+        if (inv_std_var) inv_std_var[row] = r;
+        if (mean) mean[row] = shift + md;
+    }
+
+    auto normalize = [&](const V& sv, const V& gv, const V& bt) {
+        V out;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if constexpr (CENTER) {
+                float y = ((to_f32(sv.v[e]) - shift) - md) * r * to_f32(gv.v[e]);
+                y = y + to_f32(bt.v[e]);
+                out.v[e] = from_f32<T>(y);
+            } else {
+                out.v[e] = from_f32<T>(to_f32(sv.v[e]) * r * to_f32(gv.v[e]));
+            }
+        }
+        return out;
+    };
+    // Parameters of the LDS part: gamma (and beta, masked to +0 without one).
+    V ag[CH], at[CH], bg[CH], bt2[CH];
+    auto load_par = [&](int c, V(&g)[CH], V(&bt)[CH]) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int idx = clamp(tail_idx(c * CH + i));
+            g[i] = load_vec<T, E>(gamma, idx);
+            if constexpr (CENTER) bt[i] = mask_bits(load_vec<T, E>(beta, idx), beta_mask);
+            else bt[i] = V{};
+        }
+    };
+    if (nch > 0) load_par(0, ag, at);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int idx = v * L + t;
+        const V gv = load_vec<T, E>(gamma, clamp(idx));
+        V bt = {};
+        if constexpr (CENTER) bt = mask_bits(load_vec<T, E>(beta, clamp(idx)), beta_mask);
+        const V out = normalize(ss[v], gv, bt);
+        if (idx < nvec) store_vec_stream<T, E>(output, base + idx, out);
+    }
+    auto out_chunk = [&](int c, const V(&g)[CH], const V(&bt)[CH]) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int j = c * CH + i;
+            const int idx = tail_idx(j);
+            if (idx < nvec) store_vec_stream<T, E>(output, base + idx, normalize(tail[j * L + t], g[i], bt[i]));
+        }
+    };
+    for (int c = 0; c < nch; c += 2) {
+        load_par(c + 1 < nch ? c + 1 : nch - 1, bg, bt2);
+        out_chunk(c, ag, at);
+        load_par(c + 2 < nch ? c + 2 : nch - 1, ag, at);
+        if (c + 1 < nch) out_chunk(c + 1, bg, bt2);
     }
 }
 
@@ -1149,6 +1355,28 @@ bool flat_preferred(const SslnArgs& a, int E) {
     return false;
 }
 
+// The wide route (see ssln_wide_kernel): rows of 16-byte vectors beyond
+// the register routes, one 1024-thread workgroup per row.
+template <typename T>
+constexpr int64_t kMaxWideRow = int64_t(kWideThreads) * (kWideRegs + kWideLds) * VecWidth<T>::value;
+
+template <typename T>
+hipError_t launch_ssln_wide(const SslnArgs& a, hipStream_t stream) {
+    constexpr int EV = VecWidth<T>::value;
+    const T* g = static_cast<const T*>(a.gamma);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(unsigned(a.rows)), dim3(kWideThreads), 0, stream,
+                           static_cast<const T*>(a.input), static_cast<const T*>(a.skip), g,
+                           a.beta ? static_cast<const T*>(a.beta) : g,
+                           a.bias ? static_cast<const T*>(a.bias) : g, a.bias != nullptr,
+                           static_cast<T*>(a.output), a.mean, a.inv_std_var, static_cast<T*>(a.sum),
+                           int(a.hidden / EV), float(a.hidden), a.epsilon, a.beta ? ~0u : 0u);
+        return hipGetLastError();
+    };
+    if (a.center) return go(ssln_wide_kernel<T, true>);
+    return go(ssln_wide_kernel<T, false>);
+}
+
 template <typename T>
 hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, const char** route) {
     // Widest access that divides the row and every tensor's base.
@@ -1187,6 +1415,14 @@ hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, cons
             if (E == 2) return launch_ssln_width<T, 2>(a, stream, route);
         }
         return launch_ssln_width<T, 1>(a, stream, route);
+    }
+    // Wider rows of 16-byte vectors: the wide route while a row fits one
+    // workgroup's registers and LDS (a grid of one workgroup per row stays
+    // below 2^32 work-items).
+    if (want != Route::Block && E == VecWidth<T>::value && a.hidden <= kMaxWideRow<T> &&
+        a.rows < (int64_t(1) << 22)) {
+        *route = "ssln.wide.vec16";
+        return launch_ssln_wide<T>(a, stream);
     }
     // Wider rows (or forced, then with scalar accesses): the block route.
     if (want == Route::Block) E = 1;

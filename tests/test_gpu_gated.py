@@ -35,7 +35,13 @@ CASES = [
     ((2, 8200), 4100, F16),      # 1025 eight-byte vectors: row route
     ((3, 24576), 24576, F16),    # 3072 vectors: 16 waves, ragged
     ((2, 32768), 32768, F16),    # 4096 vectors: 16 waves of 4 per thread
-    ((3, 32776), 32776, F16),    # 4097 vectors: two-pass block route, vectorized
+    ((3, 32776), 32776, F16),    # 4097 vectors: wide route, X in VGPRs, gate read after the sum
+    ((2, 65536), 65536, F16),    # 8192 vectors: wide route, VGPRs only
+    ((2, 100000), 100000, F16),  # 12500 vectors: wide route, ragged 5-vector LDS tail
+    ((3, 139264), 139264, F16),  # 17408 vectors: wide route at its widest (9 in LDS)
+    ((2, 139272), 139272, F16),  # one vector more: block route, vectorized
+    ((2, 40000), 40000, F32),    # float32 wide route, 2 LDS vectors per lane
+    ((2, 69632), 69632, F32),    # float32 wide route at its widest
     ((2, 12000), 12000, F16),    # 1500 vectors: 8 waves, ragged
     ((2, 16386), 16386, F32),    # 8193 eight-byte vectors: block route
     ((2, 16382), 16382, F32),    # 8191 eight-byte vectors: 16 waves of 8 per thread
@@ -155,6 +161,8 @@ def expected_route(C, dt, route="auto"):
     if route == "auto" and width < 16 and flat_preferred(C, size, E):
         return "gated.flat.vec16"
     if C // E > (4096 if width == 16 else 8192):  # the row route's widest rows
+        if width == 16 and C // E <= 1024 * 17:  # X in 8 VGPR and up to 9 LDS vectors per lane
+            return "gated.wide.vec16"
         return "gated.block" if E == 1 else f"gated.block.{name}"
     if C // E > 1024:
         return f"gated.row.{name}"

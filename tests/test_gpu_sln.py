@@ -61,6 +61,11 @@ SHAPES = [
     ((2, 8193), F16, False, True),      # odd: phased route
     ((2, 16385), F16, False, True),     # odd: phased route, sixteen waves
     ((2, 32769), F16, True, True),      # block route, scalars
+    ((2, 100000), F16, True, True),     # wide route: 8 vectors per lane in VGPRs, 5 in LDS
+    ((3, 139264), F16, False, False),   # wide route at its widest
+    ((2, 69632), F32, True, False),     # float32 wide route at its widest
+    ((2, 40004), F32, False, True),     # float32 wide route, ragged
+    ((2, 139272), F16, True, False),    # past the wide route: block route
     ((1000, 128), F16, True, True),     # lane groups: 16 lanes per row
     ((64, 6), F32, True, False),        # lane groups of 4
     ((31, 7), F16, True, True),         # scalars in lane groups of 8
@@ -79,11 +84,17 @@ def test_matches_oracle(shape, dt, beta, bias, route):
     if route == "block":
         assert used == "ssln.block"
     elif route == "auto" and shape[-1] * np.dtype(dt).itemsize > 131072:
-        assert used.startswith("ssln.block")  # wider than 1024 lanes x 8 x 16 bytes
+        # Wider than 1024 lanes x 8 x 16 bytes: rows of 16-byte vectors up to
+        # 17 per lane (9 of them in LDS) take the wide route, others the block route.
+        width16 = shape[-1] * np.dtype(dt).itemsize % 16 == 0
+        if width16 and shape[-1] * np.dtype(dt).itemsize <= 1024 * 17 * 16:
+            assert used == "ssln.wide.vec16"
+        else:
+            assert used.startswith("ssln.block")
 
 
 @pytest.mark.parametrize("want", [(), ("sum",), ("mean",), ("inv",), ("mean", "inv", "sum")])
-@pytest.mark.parametrize("dt,hidden", [(F32, 2048), (F16, 4096), (F16, 16384)])
+@pytest.mark.parametrize("dt,hidden", [(F32, 2048), (F16, 4096), (F16, 16384), (F32, 50000)])
 def test_optional_outputs_do_not_change_output(dt, hidden, want):
     w = workloads.sln("t", (21, hidden), dt, beta=True, bias=True, epsilon=1e-5)
     x = workloads.generate(w, seed=7)

@@ -56,12 +56,17 @@ SHAPES = [
     ((2, 16384), F32, True),     # float32 sixteen waves per row
     ((2, 10000), F32, False),    # float32 sixteen waves per row, ragged
     ((2, 40000), F16, True),     # sixteen waves, 5 vectors per lane
-    ((2, 65544), F16, True),     # wider than any register-resident route: block route
-    ((2, 40000), F32, False),    # float32 block route
+    ((2, 65544), F16, True),     # one vector past the register routes: wide route, one LDS vector
+    ((2, 40000), F32, False),    # float32 wide route, 2 LDS vectors per lane
     ((2, 30000), F32, True),     # float32 sixteen waves, 8 vectors per lane, ragged
     ((2, 20004), F16, False),    # 8-byte vectors, sixteen waves
     ((3, 65536), F16, False),    # sixteen waves, 8 vectors per lane (widest register row)
-    ((2, 131072), F16, False),   # block route, 16-byte vectors, whole steps
+    ((2, 131072), F16, False),   # wide route, 8 LDS vectors per lane
+    ((3, 139264), F16, True),    # wide route at its widest: 17 vectors per lane, odd LDS tail
+    ((2, 100000), F16, True),    # wide route, ragged 5-vector LDS tail
+    ((2, 69632), F32, True),     # float32 wide route at its widest
+    ((2, 50004), F32, False),    # float32 wide route, ragged
+    ((2, 139272), F16, False),   # one vector past the wide route: block route, 16-byte vectors
     ((2, 20002), F32, True),     # float32 block route, 8-byte vectors, ragged step
     ((2, 32770), F16, True),     # block route, 4-byte vectors
     ((7, 4100), F16, True),      # 8-byte vectors, 1025 of them: four waves per row
@@ -147,6 +152,8 @@ def expected_route(shape, dt):
         return f"ssln.wave2.{name}"
     widest = 2 * per_lane if width == 16 else per_lane  # accesses per lane of 16-wave rows
     if nvec > 1024 * widest:
+        if width == 16 and nvec <= 1024 * 17:  # 8 vectors per lane in VGPRs, up to 9 in LDS
+            return "ssln.wide.vec16"
         return "ssln.block" if E == 1 else f"ssln.block.{name}"
     if nvec <= 256 * per_lane:
         return f"ssln.rowblock.{name}"
@@ -169,7 +176,7 @@ def test_matches_oracle(shape, dt, with_bias, route):
 
 @pytest.mark.parametrize("want", [(), ("sum",), ("inv",), ("mean",), ("sum", "inv"),
                                   ("mean", "inv", "sum")])
-@pytest.mark.parametrize("dt,hidden", [(F32, 2048), (F16, 2048), (F16, 16384)])
+@pytest.mark.parametrize("dt,hidden", [(F32, 2048), (F16, 2048), (F16, 16384), (F16, 131072)])
 def test_optional_outputs_do_not_change_output(dt, hidden, want):
     w = workloads.ssln("t", (37, hidden), dt, bias=True, epsilon=1e-6)
     x = workloads.generate(w, seed=5)
@@ -227,6 +234,32 @@ def test_edge_values_f16():
         assert_bitwise(to_host(out.input_skip_bias_sum), ref[3], f"S ({route})")
         # The row holds +inf: output is NaN/0 as in the oracle.
         assert_close(to_host(out.output), ref[0], f"output ({route})")
+
+
+@pytest.mark.parametrize("dt,hidden", [(F16, 139264), (F32, 50004)])
+def test_wide_route_edge_values(dt, hidden):
+    """Residual sums that tie, overflow, go subnormal or come out -0, planted
+    in the register part and in the LDS part of wide rows (and in the last
+    vector of the LDS part), against the oracle bit for bit in S."""
+    rng = np.random.default_rng(3)
+    rows = 3
+    inp = rng.standard_normal((rows, hidden)).astype(dt)
+    skip = rng.standard_normal((rows, hidden)).astype(dt)
+    gamma = rng.uniform(0.5, 1.5, hidden).astype(dt)
+    if dt == F16:
+        vals = [(1, 2 ** -11), (1.0009765625, 2 ** -11), (2 ** -24, 2 ** -24), (2 ** -14, -(2 ** -24)),
+                (-0.0, -0.0), (3, -3)]
+    else:
+        vals = [(1, 2 ** -24), (2 ** -149, 2 ** -149), (-0.0, -0.0), (3, -3), (2 ** -126, -(2 ** -149))]
+    E = 16 // np.dtype(dt).itemsize
+    for r in range(rows):
+        for k, (a, b) in enumerate(vals):
+            for vec in (r, 8192 + 1024 * r + 7, hidden // E - 1):  # VGPR part, LDS part, last vector
+                pos = vec * E + (k % E)
+                inp[r, pos], skip[r, pos] = a, b
+    ref, out, used = run_both(inp, skip, gamma, None, 1e-6, "auto")
+    assert used == "ssln.wide.vec16"
+    check(ref, out)
 
 
 def test_zero_rows_and_zero_row():

@@ -66,6 +66,30 @@ def generate(w: Workload, seed: int = 0) -> Dict[str, np.ndarray]:
     return {t.name: _draw(rng, t) for t in w.tensors}
 
 
+def generate_on_device(w: Workload, seed: int, torch):
+    """Device tensors for every input of ``w``, for shapes too large to draw
+    on the host in reasonable time (benchmark shapes of 2^27 elements): a
+    ``torch.Generator(device="cuda")`` seeded with ``seed``, the tensors
+    drawn in order with the same distributions (``torch.randn`` in float32,
+    scaled by 0.1 for ``normal01``; ``torch.rand`` mapped to [0.5, 1.5) for
+    ``uniform``), then one cast to the tensor's dtype.  The values differ
+    from ``generate``'s; they are not compared with the oracle."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    out = {}
+    for t in w.tensors:
+        if t.dist in ("normal", "normal01"):
+            v = torch.randn(t.shape, generator=g, device="cuda", dtype=torch.float32)
+            if t.dist == "normal01":
+                v = v * 0.1
+        elif t.dist == "uniform":
+            v = torch.rand(t.shape, generator=g, device="cuda", dtype=torch.float32) + 0.5
+        else:
+            raise ValueError(f"unknown distribution {t.dist!r}")
+        out[t.name] = v.to({np.float16: torch.float16, np.float32: torch.float32}[t.dtype])
+    return out
+
+
 # ------------------------------------------------------------------ builders
 def ssln(name, shape, dtype, bias: bool, epsilon, outputs=("output",)) -> Workload:
     hidden = shape[-1]
