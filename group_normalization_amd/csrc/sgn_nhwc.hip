@@ -657,8 +657,10 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
     if (plan.K > 1 && (lay.grid <= resident || lay.span > resident)) lay = nhwc_layout(a.N, plan, true);
     // Beyond two rounds of resident workgroups the split route measured
     // faster (10-30 %, e.g. 8 x 128 x 128 x 320 float16: 86 against 112 us)
-    // where its blocks hold whole pixels; wider pixels stay here (8 x 64 x 64
-    // x 1280 float32: 148 us, against 162 us split over channel blocks).
+    // where its blocks hold whole pixels, in either block order (cluster-major
+    // there: 116 us; 4 x 256 x 256 x 256: 158 against 121 us); wider pixels
+    // stay here (8 x 64 x 64 x 1280 float32: 148 us, against 162 us split
+    // over channel blocks).
     const int split_e = a.dtype == 0 ? widest_vector<float>(a.C, {a.X, a.Y, a.S, a.skip, a.bias})
                                      : widest_vector<half_t>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
     const bool split_whole_pixels = split_e > 1 && a.C / split_e <= 256;
