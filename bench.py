@@ -444,6 +444,28 @@ def shape_cases(workloads):
         rows = (1 << 27) // c
         add(f"gated_{np.dtype(dt).name}_{rows}x{c}_c{c}", workloads.gated("w", (rows, c), c, dt, epsilon=1e-5),
             ())
+    # Rows that are not a whole number of 16-byte vectors, and short rows:
+    # phased, flat, segment and narrow-access routes.
+    for h, dt in ((127, F16), (247, F16), (1000, F16), (2046, F16), (4097, F16), (4100, F16), (8193, F16),
+                  (123, F32), (1021, F32), (3001, F32)):
+        rows = (1 << 27) // h
+        add(f"ssln_{np.dtype(dt).name}_{rows}x{h}", workloads.ssln("w", (rows, h), dt, bias=True, epsilon=1e-6,
+                                                                   outputs=("output", "input_skip_bias_sum")), ())
+    for c, dt in ((25, F16), (130, F16), (301, F16), (1025, F16), (2049, F16), (4097, F16), (16385, F16),
+                  (129, F32), (1021, F32), (2049, F32)):
+        rows = (1 << 27) // c
+        add(f"gated_{np.dtype(dt).name}_{rows}x{c}_c{c}", workloads.gated("w", (rows, c), c, dt, epsilon=1e-5),
+            ())
+    # SkipGroupNorm beyond the two workloads: pixels that are not a whole
+    # number of 16-byte vectors, NCHW planes off the grid, large images.
+    for N, C, H, W, dt, cl, g in ((8, 60, 128, 128, F16, 1, 15), (8, 36, 128, 128, F16, 1, 12),
+                                  (8, 15, 128, 128, F16, 1, 5), (16, 3, 256, 256, F16, 1, 1),
+                                  (8, 320, 31, 31, F16, 0, 32), (4, 256, 33, 33, F32, 0, 32),
+                                  (8, 320, 128, 128, F16, 1, 32), (4, 512, 64, 64, F16, 0, 32)):
+        layout = "nhwc" if cl else "nchw"
+        add(f"sgn_{np.dtype(dt).name}_{layout}_{N}x{C}x{H}x{W}_g{g}",
+            workloads.sgn("w", N, C, H, W, dt, F32, channels_last=bool(cl), broadcast_skip=False, bias=True,
+                          groups=g, activation=1, epsilon=1e-5, outputs=("Y", "S")), ())
     return out
 
 

@@ -45,6 +45,10 @@
 //            one 1024-thread workgroup per row holding X alone (8 vectors
 //            per lane in VGPRs, up to 9 more in LDS); gate and scale are read
 //            after the statistic (gated_wide_kernel).
+//   phase    spans read element by element otherwise (odd spans, bases 2 or 6
+//            bytes off the 16-byte grid) beyond the flat route, up to 4096
+//            vectors: aligned 16-byte vectors across span boundaries, scale
+//            funnel-shifted (gated_phase_kernel).
 //   block    one 256-thread workgroup per row for wider rows; X is read
 //            twice, four vectors per thread in flight per pass.
 // scale is loaded once per thread and kept in registers as float32 (flat: an
@@ -431,6 +435,100 @@ gated_row_kernel(const T* __restrict__ X, const T* __restrict__ scale,
 // Block route: two passes over X, four vectors per thread per step (the
 // loads of a step go out together; lanes past the row re-read its last
 // vector).  E == 1 is the scalar route.
+// Spans read element by element otherwise (an odd span, or X, gate and Y
+// sharing a base 2 or 6 bytes off a 16-byte boundary) and too long for the
+// flat route: counted from the boundary at or below X's base, row r holds
+// elements [a, a + C), a = r * C + phase; its lanes read the aligned
+// 16-byte vectors of X and gate that cover them (the first and last may
+// hold a neighbouring row's elements, read and left unused, never outside
+// the 16-byte chunks that hold the tensors' own elements), write the
+// interior vectors of Y whole and the two boundary vectors element by
+// element.  scale is 16-byte aligned: a lane takes its elements' values
+// from the two aligned vectors around them, funnel-shifted by the row's
+// offset p = a mod E (uniform over the row).  WPR waves per row (1, 2 or 4
+// in 256-thread blocks, or 8 and 16 in blocks of WPB = WPR waves), NV
+// vectors per lane; the wave sums meet in LDS and are added in wave order.
+template <typename T, int E, int NV, int WPR, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
+gated_phase_kernel(const T* __restrict__ X, const T* __restrict__ scale,
+                   const T* __restrict__ gate, T* __restrict__ Y, int64_t rows, int span, int phase,
+                   int nvg, float span_f, float eps) {
+    using V = Vec<T, E>;
+    constexpr int LANES = 64 * WPR;
+    static_assert(WPB % WPR == 0, "whole rows per block");
+    __shared__ float wave_part[WPB];
+    const int lane = threadIdx.x % LANES;
+    const int64_t my_row = int64_t(blockIdx.x) * (WPB / WPR) + threadIdx.x / LANES;
+    // With two rows per block the waves of a missing second row stay for the
+    // barrier and store nothing.
+    if (WPR != 2 && my_row >= rows) return;
+    const bool live = my_row < rows;
+    const int64_t row = live ? my_row : rows - 1;
+
+    const int64_t a = row * span + phase;
+    const int64_t v0 = a / E;                            // the row's first vector
+    const int p = int(a - v0 * E);                       // its first element's place in it
+    const int nvr = int((a + span + E - 1) / E - v0);    // vectors the row touches
+    const T* x_a = X - phase;                            // 16-byte aligned bases
+    const T* g_a = gate - phase;
+    T* y_a = Y - phase;
+    const int k_shift = (E - p) % E;
+    const int pv = p > 0 ? 1 : 0;
+    auto clamp = [&](int i) { return i < nvr ? i : nvr - 1; };
+    V xs[NV], gs[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int i = clamp(v * LANES + lane);
+        xs[v] = load_vec_stream<T, E>(x_a, v0 + i);
+        gs[v] = load_vec_stream<T, E>(g_a, v0 + i);
+    }
+    // Element e of vector i lies in the row when lo_e <= e < hi_e.
+    auto in_row = [&](int i, int e) { return i < nvr && e >= p - i * E && e < span + p - i * E; };
+    auto whole = [&](int i) { return i < nvr && p - i * E <= 0 && span + p - i * E >= E; };
+    float acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int i = v * LANES + lane;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float x = to_f32(xs[v].v[e]);
+            acc = in_row(i, e) ? fmaf_(x, x, acc) : acc;
+        }
+    }
+    float total = segment_sum<64>(acc);
+    if constexpr (WPR > 1) {
+        if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = total;
+        __syncthreads();
+        const int w0 = (threadIdx.x / LANES) * WPR;
+        total = wave_part[w0];
+#pragma unroll
+        for (int w = 1; w < WPR; ++w) total += wave_part[w0 + w];
+    }
+    const float r = inv_sqrt(total / span_f + eps);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int i = v * LANES + lane;
+        // scale of vector i's elements (row positions i*E - p + e).
+        int lo = i - pv, hi = i - pv + 1;
+        lo = lo < 0 ? 0 : (lo < nvg ? lo : nvg - 1);
+        hi = hi < 0 ? 0 : (hi < nvg ? hi : nvg - 1);
+        const V sv = funnel16<T, E>(load_vec<T, E>(scale, lo), load_vec<T, E>(scale, hi), k_shift);
+        V out;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            out.v[e] = from_f32<T>(to_f32(xs[v].v[e]) * r * to_f32(sv.v[e]) * silu_f32(to_f32(gs[v].v[e])));
+        if (live) {
+            if (whole(i)) {
+                store_vec_stream<T, E>(y_a, v0 + i, out);
+            } else if (i < nvr) {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (in_row(i, e)) y_a[(v0 + i) * E + e] = out.v[e];
+            }
+        }
+    }
+}
+
 // Spans wider than the row route holds (4096 sixteen-byte vectors, 64 KB,
 // with X and gate both in registers), up to kWideRegs + kWideLds vectors
 // per lane (272 KB of X): one 1024-thread workgroup per span keeps X alone
@@ -702,6 +800,58 @@ hipError_t launch_row_for(const GatedArgs& a, int nvec, hipStream_t stream) {
     return launch_row_nv<T, E, 1024>(a, nvec, nv1024, stream);
 }
 
+template <typename T, int NV, int WPR, int WPB>
+hipError_t launch_phase_nv(const GatedArgs& a, int phase, int nvg, hipStream_t stream) {
+    constexpr int E = VecWidth<T>::value;
+    constexpr int rows_per_block = WPB / WPR;
+    const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL((gated_phase_kernel<T, E, NV, WPR, WPB>), dim3(unsigned(blocks)), dim3(64 * WPB), 0,
+                       stream, static_cast<const T*>(a.X), static_cast<const T*>(a.scale),
+                       static_cast<const T*>(a.gate), static_cast<T*>(a.Y), a.rows, int(a.span), phase, nvg,
+                       float(a.span), a.epsilon);
+    return hipGetLastError();
+}
+
+template <typename T, int WPR, int WPB = 4>
+hipError_t launch_phase_w(const GatedArgs& a, int nmax, int phase, int nvg, hipStream_t stream) {
+    const int need = (nmax + 64 * WPR - 1) / (64 * WPR);
+    if (need <= 1) return launch_phase_nv<T, 1, WPR, WPB>(a, phase, nvg, stream);
+    if (need <= 2) return launch_phase_nv<T, 2, WPR, WPB>(a, phase, nvg, stream);
+    if (need <= 3) return launch_phase_nv<T, 3, WPR, WPB>(a, phase, nvg, stream);
+    return launch_phase_nv<T, 4, WPR, WPB>(a, phase, nvg, stream);
+}
+
+// Vectors per lane of the phased route: four 16-byte vectors of X and of
+// gate (deeper, the scale funnels would crowd the 1024-thread block's
+// 128 VGPRs).
+constexpr int kPhaseNv = 4;
+
+// The phased route (see gated_phase_kernel) for spans that would be read
+// element by element: taken when X, gate and Y share their offset from a
+// 16-byte boundary, scale is 16-byte aligned, and a span touches more than
+// 32 and at most 1024 * kPhaseNv vectors.  Returns false, having launched
+// nothing, otherwise.
+template <typename T>
+bool launch_gated_phase(const GatedArgs& a, hipStream_t stream, const char** route, hipError_t* err) {
+    constexpr int E = VecWidth<T>::value;
+    const uintptr_t ph = reinterpret_cast<uintptr_t>(a.X) % 16;
+    if (ph % sizeof(T) != 0 || reinterpret_cast<uintptr_t>(a.gate) % 16 != ph ||
+        reinterpret_cast<uintptr_t>(a.Y) % 16 != ph || !aligned16(a.scale))
+        return false;
+    const int64_t nmax = a.span / E + 2;  // vectors a span can touch
+    if (nmax <= 32 || nmax > 1024 * kPhaseNv) return false;
+    const int phase = int(ph / sizeof(T));
+    const int nvg = int((a.span + E - 1) / E);
+    const int n = int(nmax);
+    *route = "gated.phase.vec16";
+    if (nmax <= 64 * kPhaseNv) *err = launch_phase_w<T, 1>(a, n, phase, nvg, stream);
+    else if (nmax <= 128 * kPhaseNv) *err = launch_phase_w<T, 2>(a, n, phase, nvg, stream);
+    else if (nmax <= 256 * kPhaseNv) *err = launch_phase_w<T, 4>(a, n, phase, nvg, stream);
+    else if (nmax <= 512 * kPhaseNv) *err = launch_phase_w<T, 8, 8>(a, n, phase, nvg, stream);
+    else *err = launch_phase_w<T, 16, 16>(a, n, phase, nvg, stream);
+    return true;
+}
+
 // The wide route (see gated_wide_kernel): spans of 16-byte vectors beyond
 // the row route, one 1024-thread workgroup per span.
 constexpr int64_t kMaxWideVectors = int64_t(kWideThreads) * (kWideRegs + kWideLds);
@@ -853,6 +1003,12 @@ hipError_t launch_gated_t(const GatedArgs& a, Route want, hipStream_t stream, co
             *route = "gated.flat.vec16";
             return launch_flat_for<T>(a, fp, int(ph / sizeof(T)), stream);
         }
+    }
+    // Spans that would be read element by element beyond the flat route:
+    // aligned 16-byte vectors across span boundaries.
+    if (want != Route::Scalar && want != Route::Block && E == 1) {
+        hipError_t err = hipSuccess;
+        if (launch_gated_phase<T>(a, stream, route, &err)) return err;
     }
     if constexpr (sizeof(T) == 2) {
         TilePlan tp;

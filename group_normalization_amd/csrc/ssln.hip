@@ -413,33 +413,6 @@ ssln_wide_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     }
 }
 
-// Elements k .. k + E - 1 of the 2E-element concatenation [lo, hi] of two
-// 16-byte vectors (0 <= k < E): byte funnel shifts of their eight dwords.
-// The dword offset is applied with value selects, not branches: an
-// if / else-if chain on it, which the compiler could not prove uniform,
-// was lowered into exec-masked blocks that left the last case's values
-// unassigned (seen in the generated code and as wrong rows on the GPU).
-template <typename T, int E>
-__device__ __forceinline__ Vec<T, E> funnel16(const Vec<T, E>& lo, const Vec<T, E>& hi, int k) {
-    static_assert(sizeof(Vec<T, E>) == 16, "16-byte vectors");
-    const u32x4 a = __builtin_bit_cast(u32x4, lo), b = __builtin_bit_cast(u32x4, hi);
-    const uint32_t c[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    const int byte = k * int(sizeof(T));
-    const int q = byte >> 2;
-    const uint32_t r = uint32_t(byte & 3);
-    uint32_t w[5];  // dwords q .. q + 4 of [a, b]
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-        const uint32_t x01 = q == 0 ? c[j] : c[j + 1];
-        const uint32_t x23 = q == 2 ? c[j + 2] : c[j + 3 < 8 ? j + 3 : 7];
-        w[j] = q < 2 ? x01 : x23;
-    }
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], r);
-    return __builtin_bit_cast(Vec<T, E>, o);
-}
-
 // Rows off the 16-byte grid: a row length that is not a whole number of
 // 16-byte vectors, or data tensors (input, skip, output, S) whose common
 // base address sits off a 16-byte boundary.  Counted from the boundary at

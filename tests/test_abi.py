@@ -5,7 +5,19 @@ the operator contracts, attributes, pointers, aliasing and workspace sizes.
 Pointers here are fake addresses that are never dereferenced: each call is
 built to fail validation (or to have zero elements, which launches nothing).
 Skipped when a GPU is visible, so that no bug in validation could ever launch
-a kernel on a fake address."""
+a kernel on a fake address.
+
+Validation accepts tensors at any element-aligned address, and some routes
+then read past a tensor's ends.  For rows, NCHW groups or flat row streams
+off the 16-byte grid, the phased and flat routes read whole aligned 16-byte
+vectors. Those reads can touch up to 15 bytes beside a tensor's first and
+last element, inside the same aligned block. A bounds-checked CPU emulation
+of those kernels would flag the reads. On the GPU they cannot fault,
+because device memory is mapped in pages. The read bytes only ever fill
+lanes that are masked out. That nothing outside the outputs is written is
+checked on the GPU with guard elements around every output (test_phased_rows
+and test_flat_rows_off_the_grid in test_gpu_ssln.py, test_nchw_phased_groups
+in test_gpu_sgn.py, test_flat_route in test_gpu_gated.py)."""
 import ctypes
 import os
 import re

@@ -45,11 +45,15 @@ CASES = [
     ((2, 12000), 12000, F16),    # 1500 vectors: 8 waves, ragged
     ((2, 16386), 16386, F32),    # 8193 eight-byte vectors: block route
     ((2, 16382), 16382, F32),    # 8191 eight-byte vectors: 16 waves of 8 per thread
-    ((3, 4099), 4099, F16),      # 4099 scalars: 16 waves of 8 per thread
-    ((2, 8195), 8195, F16),      # 8195 scalars: scalar block route
-    ((3, 4095), 4095, F16),      # 4095 scalars: 16 waves of 4 per thread
-    ((4, 2049), 2049, F32),      # 2049 scalars: 16 waves, ragged
-    ((2, 5003), 5003, F32),      # 5003 scalars: 16 waves of 8 per thread
+    ((3, 4099), 4099, F16),      # odd span: phased route, four waves
+    ((2, 8195), 8195, F16),      # odd span: phased route, eight waves
+    ((2, 32759), 32759, F16),    # the phased route's longest span (4096 vectors touched)
+    ((2, 32761), 32761, F16),    # one vector more: scalar block route
+    ((2, 32777), 32777, F16),    # longer odd span: scalar block route
+    ((3, 4095), 4095, F16),      # odd span: phased route
+    ((5, 1017), 1017, F16),      # just past the flat route: phased, one wave
+    ((4, 2049), 2049, F32),      # float32 odd span: phased route
+    ((2, 5003), 5003, F32),      # float32 odd span: phased route
     # tile route (float16 rows of 33-128 vectors of 8 or 4 bytes that fill
     # < 60 % of the segment route's lanes, packed back to back): several
     # tiles, a ragged last tile and waves past the last row
@@ -160,6 +164,10 @@ def expected_route(C, dt, route="auto"):
         return "gated.flat.vec16"
     if route == "auto" and width < 16 and flat_preferred(C, size, E):
         return "gated.flat.vec16"
+    # Spans read element by element otherwise: aligned 16-byte vectors across
+    # span boundaries while a span touches 33 to 4096 of them.
+    if route != "scalar" and E == 1 and 32 < C // (16 // size) + 2 <= 4096:
+        return "gated.phase.vec16"
     if C // E > (4096 if width == 16 else 8192):  # the row route's widest rows
         if width == 16 and C // E <= 1024 * 17:  # X in 8 VGPR and up to 9 LDS vectors per lane
             return "gated.wide.vec16"
@@ -266,15 +274,57 @@ def test_flat_route(C, dt, off):
     assert_close(first.reshape(rows, C), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
 
 
+PHASE_CASES = [(1017, F16, 1), (2049, F16, 3), (4097, F16, 5), (8195, F16, 7), (32759, F16, 2),
+               (1021, F32, 1), (2049, F32, 3), (16379, F32, 2)]
+
+
+@pytest.mark.parametrize("C,dt,off", PHASE_CASES, ids=[f"C{c}-{np.dtype(d).name}-off{o}" for c, d, o in PHASE_CASES])
+def test_phased_spans(C, dt, off):
+    """Phased route: X, gate and Y start `off` elements past a 16-byte
+    boundary, spans of odd length, so every span starts and ends inside a
+    vector whose other elements belong to its neighbours (or lie outside the
+    tensors, at the ends).  Guard elements on both sides of Y stay
+    untouched, two runs agree bit for bit, and the spans match the
+    oracle."""
+    from group_normalization_amd._lib import lib, check as ck
+    rows, pad = max(3, 60000 // C), 64
+    w = workloads.gated("t", (rows, C), C, dt, epsilon=1e-5)
+    x = workloads.generate(w, seed=C + off)
+    tdt = torch.float16 if dt == F16 else torch.float32
+
+    def placed(a, fill=None):
+        buf = torch.full((a.size + 2 * pad,), 3.0, dtype=tdt, device="cuda")
+        view = buf[pad + off: pad + off + a.size]  # buf is 256-byte aligned
+        if fill is None:
+            view.copy_(torch.from_numpy(np.ascontiguousarray(a).ravel()))
+        return buf, view
+
+    _, X = placed(x["X"])
+    _, G = placed(x["gate"])
+    arena, Y = placed(x["X"], fill=3.0)
+    S = to_dev(x["scale"])
+    for i in range(2):
+        ck(lib().gated_rms_norm(desc(X, (rows, C)), desc(S), desc(G, (rows, C)), 1e-5, desc(Y, (rows, C)),
+                                torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        assert gn.last_route() == "gated.phase.vec16"
+        if i == 0:
+            first = to_host(Y).copy()
+    assert_bitwise(to_host(Y), first, "second run")
+    a = to_host(arena)
+    assert np.all(a[:pad + off] == 3.0) and np.all(a[pad + off + rows * C:] == 3.0)
+    assert_close(first.reshape(rows, C), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
+
+
 @pytest.mark.parametrize("C,dt", [(1017, F16), (1021, F32)])
 def test_flat_longest_rows(C, dt):
     """One element past the flat route's longest rows: forced flat, the
-    route falls back to the others with the same values."""
+    route falls back to the phased route with the same values."""
     w = workloads.gated("t", (40, C), C, dt, epsilon=1e-5)
     x = workloads.generate(w, seed=C)
     with gn.force_route("flat"):
         y = gn.gated_rms_norm(to_dev(x["X"]), to_dev(x["scale"]), to_dev(x["gate"]), 1e-5)
-    assert gn.last_route() == "gated.segment.scalar"
+    assert gn.last_route() == "gated.phase.vec16"
     assert_close(to_host(y), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
 
 
