@@ -46,9 +46,10 @@
 //            per lane in VGPRs, up to 9 more in LDS); gate and scale are read
 //            after the statistic (gated_wide_kernel).
 //   phase    spans read element by element otherwise (odd spans, bases 2 or 6
-//            bytes off the 16-byte grid) beyond the flat route, up to 4096
-//            vectors: aligned 16-byte vectors across span boundaries, scale
-//            funnel-shifted (gated_phase_kernel).
+//            bytes off the 16-byte grid) beyond the flat route, and longer
+//            spans of 4- or 8-byte accesses, up to 4096 vectors: aligned
+//            16-byte vectors across span boundaries, scale funnel-shifted
+//            (gated_phase_kernel).
 //   block    one 256-thread workgroup per row for wider rows; X is read
 //            twice, four vectors per thread in flight per pass.
 // scale is loaded once per thread and kept in registers as float32 (flat: an
@@ -1004,9 +1005,16 @@ hipError_t launch_gated_t(const GatedArgs& a, Route want, hipStream_t stream, co
             return launch_flat_for<T>(a, fp, int(ph / sizeof(T)), stream);
         }
     }
-    // Spans that would be read element by element beyond the flat route:
-    // aligned 16-byte vectors across span boundaries.
-    if (want != Route::Scalar && want != Route::Block && E == 1) {
+    // The phased route (aligned 16-byte vectors across span boundaries) for
+    // spans read element by element beyond the flat route, and for spans of
+    // more than 300 four-byte or 256 eight-byte vectors, where it measured
+    // faster (f16 C = 766 / 1026 / 2050 / 8194 +17 / +14 / +40 / +26 %,
+    // 1028 / 2052 / 4100 +20 / +21 / +15 %, f32 1026 / 2050 +22 / +6 %;
+    // shorter ones keep the segment route: f16 C = 350 / 514 -5 / -4 %,
+    // 380 / 1012 -10 / -3 %).
+    const int vbytes = E * int(sizeof(T));
+    const bool phase_pref = E == 1 || (vbytes == 4 && nvec > 300) || (vbytes == 8 && nvec > 256);
+    if (want != Route::Scalar && want != Route::Block && phase_pref) {
         hipError_t err = hipSuccess;
         if (launch_gated_phase<T>(a, stream, route, &err)) return err;
     }

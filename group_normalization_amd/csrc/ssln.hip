@@ -28,8 +28,10 @@
 //          wave order.
 //   phase  rows that would otherwise be read element by element (an odd
 //          row length, or data tensors sharing a base 2 or 6 bytes off a
-//          16-byte boundary): aligned 16-byte vectors read across row
-//          boundaries, boundary elements masked (ssln_phase_kernel).
+//          16-byte boundary), and rows of 4- or 8-byte accesses where it
+//          measured faster (phase_preferred): aligned 16-byte vectors read
+//          across row boundaries, boundary elements masked
+//          (ssln_phase_kernel).
 //   wide   rows of 16-byte vectors beyond the register routes, up to 272 KB:
 //          one 1024-thread workgroup per row, S held in VGPRs (8 vectors
 //          per lane) and LDS (up to 9 more), so still one read and one write
@@ -1350,6 +1352,36 @@ hipError_t launch_ssln_wide(const SslnArgs& a, hipStream_t stream) {
     return go(ssln_wide_kernel<T, false>);
 }
 
+// Where the automatic choice takes the phased route (rows that touch 33 to
+// 4096 aligned vectors and that the flat route does not take), by the access
+// width E the other routes would use, as measured on 2^27-element tensors
+// (outputs Y and S) against them:
+//   element rows: always (1.2-2.3x).
+//   float16 pairs (4-byte accesses): always (hidden 302-16382 +7 to +37 %;
+//     with the mean removed +0 to +14 %).
+//   float32 pairs (8-byte accesses): always (1022-8190 +1 to +16 %).
+//   float16 quads (8-byte accesses), the mean not removed: rows of more than
+//     256 of them, or whose lane group or wave leaves more than a fifth of
+//     its slots idle (260 / 380 / 2044 / 4092 / 4100 +9 to +16 %; rows that
+//     fill their slots lose: 252 / 508 / 764 -33 / -11 / -4 %); with the
+//     mean removed, never (2044 +4 %, 4100 -6 %).
+template <typename T>
+bool phase_preferred(const SslnArgs& a, int E) {
+    const int bytes = E * int(sizeof(T));
+    if (E == 1 || bytes == 4 || (bytes == 8 && sizeof(T) == 4)) return true;
+    if (bytes != 8 || a.center) return false;
+    const int64_t nvec = a.hidden / E;
+    if (nvec > 256) return true;
+    int64_t slots = 1;
+    if (nvec <= 64) {
+        while (slots < nvec) slots <<= 1;  // the lane group
+    } else {
+        const int64_t need = (nvec + 63) / 64;  // one wave, as launch_wave picks its depth
+        slots = 64 * (need <= 4 ? need : need <= 6 ? 6 : 8);
+    }
+    return double(nvec) / double(slots) < 0.8;
+}
+
 template <typename T>
 hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, const char** route) {
     // Widest access that divides the row and every tensor's base.
@@ -1360,14 +1392,11 @@ hipError_t launch_ssln_t(const SslnArgs& a, Route want, hipStream_t stream, cons
         if (launch_ssln_flat<T>(a, true, stream, route, &err)) return err;
         want = Route::Auto;
     }
-    // The flat route where it measured faster (flat_preferred); rows that
-    // would otherwise be read element by element take the phased route
-    // beyond it (1.2-2.3x: float16 hidden 4097 / 8193 at 5.3 / 5.1 TB/s
-    // against 3.6 / 3.0); against 4- and 8-byte vectors the phased route
-    // measured within -7 / +14 %, so those keep them.
+    // The flat route where it measured faster (flat_preferred), then the
+    // phased route where it did (phase_preferred).
     if (want == Route::Auto || want == Route::Vector) {
         if (flat_preferred<T>(a, E) && launch_ssln_flat<T>(a, false, stream, route, &err)) return err;
-        if (E == 1 && launch_ssln_phase<T>(a, stream, route, &err)) return err;
+        if (phase_preferred<T>(a, E) && launch_ssln_phase<T>(a, stream, route, &err)) return err;
     }
     int64_t max_regs = kMaxRegisterRow<T, 1>;
     if constexpr (sizeof(T) == 2) {

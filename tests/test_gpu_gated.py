@@ -32,7 +32,12 @@ CASES = [
     ((3, 650), 130, F16),        # 4-byte vectors: 65 per row, two per lane
     ((5, 129), 129, F16),        # odd span: scalars
     ((4, 6), 6, F32),            # float32 8-byte vectors: 3 per row
-    ((2, 8200), 4100, F16),      # 1025 eight-byte vectors: row route
+    ((2, 8200), 4100, F16),      # 1025 eight-byte vectors: phased route
+    ((3, 1012), 1012, F16),      # 253 eight-byte vectors: segment route
+    ((3, 1028), 1028, F16),      # 257 eight-byte vectors: phased route
+    ((3, 602), 602, F16),        # 301 four-byte vectors: phased route
+    ((3, 514), 514, F16),        # 257 four-byte vectors: segment route
+    ((3, 2050), 2050, F32),      # float32 8-byte vectors: phased route
     ((3, 24576), 24576, F16),    # 3072 vectors: 16 waves, ragged
     ((2, 32768), 32768, F16),    # 4096 vectors: 16 waves of 4 per thread
     ((3, 32776), 32776, F16),    # 4097 vectors: wide route, X in VGPRs, gate read after the sum
@@ -164,10 +169,12 @@ def expected_route(C, dt, route="auto"):
         return "gated.flat.vec16"
     if route == "auto" and width < 16 and flat_preferred(C, size, E):
         return "gated.flat.vec16"
-    # Spans read element by element otherwise: aligned 16-byte vectors across
-    # span boundaries while a span touches 33 to 4096 of them.
-    if route != "scalar" and E == 1 and 32 < C // (16 // size) + 2 <= 4096:
-        return "gated.phase.vec16"
+    # Aligned 16-byte vectors across span boundaries while a span touches 33
+    # to 4096 of them: spans read element by element otherwise, and spans of
+    # more than 300 four-byte or 256 eight-byte vectors.
+    if route != "scalar" and 32 < C // (16 // size) + 2 <= 4096:
+        if E == 1 or (width == 4 and C // E > 300) or (width == 8 and C // E > 256):
+            return "gated.phase.vec16"
     if C // E > (4096 if width == 16 else 8192):  # the row route's widest rows
         if width == 16 and C // E <= 1024 * 17:  # X in 8 VGPR and up to 9 LDS vectors per lane
             return "gated.wide.vec16"

@@ -59,7 +59,7 @@ SHAPES = [
     ((2, 65544), F16, True),     # one vector past the register routes: wide route, one LDS vector
     ((2, 40000), F32, False),    # float32 wide route, 2 LDS vectors per lane
     ((2, 30000), F32, True),     # float32 sixteen waves, 8 vectors per lane, ragged
-    ((2, 20004), F16, False),    # 8-byte vectors, sixteen waves
+    ((2, 20004), F16, False),    # 8-byte rows of 5001 vectors: phased route
     ((3, 65536), F16, False),    # sixteen waves, 8 vectors per lane (widest register row)
     ((2, 131072), F16, False),   # wide route, 8 LDS vectors per lane
     ((3, 139264), F16, True),    # wide route at its widest: 17 vectors per lane, odd LDS tail
@@ -69,13 +69,13 @@ SHAPES = [
     ((2, 139272), F16, False),   # one vector past the wide route: block route, 16-byte vectors
     ((2, 20002), F32, True),     # float32 block route, 8-byte vectors, ragged step
     ((2, 32770), F16, True),     # block route, 4-byte vectors
-    ((7, 4100), F16, True),      # 8-byte vectors, 1025 of them: four waves per row
-    ((5, 4092), F16, True),      # 8-byte vectors, two waves per row (odd row count)
-    ((5, 4098), F16, False),     # 4-byte vectors, 2049 of them: four waves per row
-    ((3, 2046), F16, True),      # 4-byte vectors, one wave per row
+    ((7, 4100), F16, True),      # 8-byte rows of 1025 vectors: phased route
+    ((5, 4092), F16, True),      # 8-byte rows of 1023 vectors: phased route (odd row count)
+    ((5, 4098), F16, False),     # 4-byte rows: phased route
+    ((3, 2046), F16, True),      # 4-byte rows: phased route
     ((4, 4097), F16, False),     # odd width: phased route (aligned 16-byte vectors across rows)
     ((3, 6000), F16, True),      # 750 sixteen-byte vectors: four waves per row, ragged
-    ((3, 6002), F32, True),      # float32 8-byte vectors, eight waves per row
+    ((3, 6002), F32, True),      # float32 8-byte rows: phased route
     ((2, 8193), F16, True),      # odd: phased route, eight waves
     ((2, 16385), F16, True),     # odd: phased route, sixteen waves
     ((2, 32769), F16, True),     # odd and wider than the phased route: scalar block route
@@ -104,6 +104,10 @@ SHAPES = [
     ((70, 252), F16, True),      # 63 eight-byte vectors: 64-lane groups
     ((60, 130), F16, False),     # 65 four-byte pairs: one wave per row
     ((80, 102), F32, True),      # 51 eight-byte vectors: 64-lane groups
+    ((40, 252), F16, False),     # 63 eight-byte vectors fill a 64-lane group: segment route
+    ((40, 260), F16, True),      # 65 eight-byte vectors, half a wave's slots idle: phased route
+    ((30, 508), F16, False),     # 127 eight-byte vectors fill a wave of two: wave route
+    ((30, 302), F16, True),      # 151 four-byte vectors: phased route
 ]
 
 
@@ -128,6 +132,28 @@ def flat_expected(dt, hidden, center=False, width=None):
     return False
 
 
+def phase_expected(dt, hidden, width, center=False):
+    """Whether the automatic choice takes the phased route for a row whose
+    other routes would use `width`-byte accesses (the flat route not taking
+    it): the measured rule of the library, restated."""
+    size = np.dtype(dt).itemsize
+    if not 32 < hidden // (16 // size) + 2 <= 1024 * 4:
+        return False
+    if width == size or width == 4 and size == 2 or width == 8 and size == 4:
+        return True
+    if width != 8 or center:
+        return False
+    nvec = hidden // (width // size)
+    if nvec > 256:
+        return True
+    if nvec <= 64:
+        slots = 1 << (nvec - 1).bit_length()
+    else:
+        need = -(-nvec // 64)
+        slots = 64 * (need if need <= 4 else 6 if need <= 6 else 8)
+    return nvec / slots < 0.8
+
+
 def expected_route(shape, dt):
     size = np.dtype(dt).itemsize
     hidden = shape[-1]
@@ -141,7 +167,7 @@ def expected_route(shape, dt):
     # needs more than 32 and at most 1024 x 4 of them.
     if flat_expected(dt, hidden, width=width):
         return "ssln.flat.vec16"
-    if E == 1 and 32 < hidden // (16 // size) + 2 <= 1024 * 4:
+    if phase_expected(dt, hidden, width):
         return "ssln.phase.vec16"
     if nvec <= (64 if width < 16 else 48):
         return f"ssln.segment.{name}"
