@@ -604,6 +604,7 @@ PROF_COMMANDS = {
              "python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
     "configs": "python3 $REPO/bench.py --configs --steps 60 --warmup 5",
     "bench": "python3 $REPO/bench.py",
+    "shapes": "python3 $REPO/bench.py --shapes --steps 10 --warmup 2",
 }
 
 # Template parameters of each kernel family, as declared in the sources.
@@ -893,6 +894,23 @@ def summarize(args):
                          f"{r.get('oracle_gbps', '')} |")
     with open(os.path.join(prof, "configs_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    shapes_path = os.path.join(d, "shapes.json")
+    if os.path.exists(shapes_path):
+        sh = _read_json_line(shapes_path)
+        lines = ["# General shapes: every route family beyond the five workloads", "",
+                 "Command (from the repository root on the GPU host, `$REPO` = repository root):", "", "```",
+                 PROF_COMMANDS["shapes"] + " > $REPO/gpurun_out/prof/shapes.json", "```", "",
+                 "Each shape alone, cold (a 1 GiB copy before every call), HIP events around the op on its "
+                 f"stream, median of {sh['invocations']} calls; inputs drawn on the device "
+                 "(`workloads.generate_on_device`, seed 0). GB/s counts algorithmic bytes: every input read "
+                 "once, every output (Y and S for the skip ops) written once. One MI355X.", "",
+                 "| shape | route | median us | GB/s | % of 8 TB/s |", "|---|---|---|---|---|"]
+        for r in sh["shapes"]:
+            forced = "" if r["forced"] == "auto" else " (forced)"
+            lines.append(f"| {r['shape']} | {r['route']}{forced} | {r['median_us']} | {r['gbps']} | "
+                         f"{100 * r['gbps'] / PEAK_GBPS:.1f} |")
+        with open(os.path.join(prof, "general_shapes.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
     log(f"wrote profiles/kernel_trace_bench_step.md, hbm_traffic_pmc_bench_step.md, configs_kernel_trace.md, "
         f"{os.path.basename(TRAFFIC_FILE)} (dominant kernel {dom['hbm_bytes_per_launch']:,} bytes per launch)")
 
