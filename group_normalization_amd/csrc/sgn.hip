@@ -531,12 +531,27 @@ __device__ __forceinline__ int merge_lanes(int items, int len) {
     return w;
 }
 
+// Packed pixels (kpx > 1): element e of vector cv of a run of kpx pixels is
+// channel (cv * E + e) mod C; bias and a broadcast skip row are read one
+// channel at a time.
+template <typename T, int E>
+__device__ __forceinline__ void load_packed_params(const T* bias, bool has_bias, const T* skip,
+                                                   bool skip_bcast, int n, int cv, int C, float (&bv)[E],
+                                                   float (&kb)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int c = (cv * E + e) % C;
+        if (has_bias) bv[e] = to_f32(bias[c]);
+        if (skip_bcast) kb[e] = to_f32(skip[int64_t(n) * C + c]);
+    }
+}
+
 template <typename T, int E>
 __global__ void __launch_bounds__(256)
 sgn_stats_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
                       const T* __restrict__ bias, T* __restrict__ S, Partial* __restrict__ part,
                       int64_t HW, int Cv, int CBv, int NCB, int P, int cpg, int groups, int B,
-                      int64_t ppb, bool skip_bcast) {
+                      int64_t ppb, bool skip_bcast, int kpx, int C) {
     using V = Vec<T, E>;
     __shared__ float sh_n[256 * E], sh_mean[256 * E], sh_m2[256 * E];
     const NhwcTile tl = nhwc_tile(B, NCB, CBv, P);
@@ -552,8 +567,12 @@ sgn_stats_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
     const bool stream_in = S != nullptr;  // pass 3 reads S, not X and skip
 
     float bv[E] = {}, kb[E] = {};
-    if (active && has_bias) load_param_vec<T, E>(bias, cv, bv);
-    if (active && skip_bcast) load_param_vec<T, E>(skip, int64_t(n) * Cv + cv, kb);
+    if (kpx == 1) {  // uniform
+        if (active && has_bias) load_param_vec<T, E>(bias, cv, bv);
+        if (active && skip_bcast) load_param_vec<T, E>(skip, int64_t(n) * Cv + cv, kb);
+    } else if (active) {
+        load_packed_params<T, E>(bias, has_bias, skip, skip_bcast, n, cv, C, bv, kb);
+    }
 
     ShiftedSums acc[E];
     float cnt = 0.0f;
@@ -617,17 +636,22 @@ sgn_stats_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
         }
     }
     __syncthreads();
-    // Per group of the block over its channels.
+    // Per group of the block over its channels: with packed pixels (kpx > 1,
+    // one block holds all C channels of kpx pixels) a group's channels in
+    // pixel order, then channel order.
     {
-        const int g0 = tl.cv0 * E / cpg, gpb = Cw / cpg;
-        const int w = merge_lanes(gpb, cpg);
+        const int Cp = Cw / kpx;  // channels of the block per pixel
+        const int g0 = tl.cv0 * E / cpg, gpb = Cp / cpg, len = kpx * cpg;
+        const int w = merge_lanes(gpb, len);
         const int lane = t & (w - 1);
         for (int gl0 = 0; gl0 < gpb; gl0 += 256 / w) {
             const int gl = gl0 + t / w;
             Moments m{0.0f, 0.0f, 0.0f};
             if (gl < gpb)
-                for (int c = gl * cpg + lane; c < (gl + 1) * cpg; c += w)
+                for (int i = lane; i < len; i += w) {
+                    const int c = (i / cpg) * Cp + gl * cpg + i % cpg;
                     m = merge(m, Moments{sh_n[c], sh_mean[c], sh_m2[c]});
+                }
             m = segment_merge(m, w);
             if (gl < gpb && lane == 0)
                 part[(int64_t(n) * groups + g0 + gl) * B + b] = Partial{m.n, m.mean, m.m2, 0.0f};
@@ -642,7 +666,7 @@ sgn_norm_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
                      const M* __restrict__ gamma, const M* __restrict__ beta,
                      const float2* __restrict__ stat, T* __restrict__ Y, int64_t HW, int Cv,
                      int CBv, int NCB, int P, int cpg, int groups, int B, int64_t ppb,
-                     bool skip_bcast, bool silu) {
+                     bool skip_bcast, bool silu, int kpx, int C) {
     using V = Vec<T, E>;
     const NhwcTile tl = nhwc_tile(B, NCB, CBv, P);
     if (!tl.active) return;  // no barrier below
@@ -673,15 +697,19 @@ sgn_norm_nhwc_kernel(const T* __restrict__ X, const T* __restrict__ skip,
             first = false;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const int c = cv * E + e;
+                const int c = kpx == 1 ? cv * E + e : (cv * E + e) % C;  // packed: channel of the pixel
                 const float2 st = stat[int64_t(n) * groups + c / cpg];
                 mean[e] = st.x;
                 scl[e] = st.y * to_f32(gamma[c]);
                 sft[e] = to_f32(beta[c]);
             }
             if (!S_in) {
-                if (has_bias) load_param_vec<T, E>(bias, cv, bv);
-                if (skip_bcast) load_param_vec<T, E>(skip, int64_t(n) * Cv + cv, kb);
+                if (kpx == 1) {
+                    if (has_bias) load_param_vec<T, E>(bias, cv, bv);
+                    if (skip_bcast) load_param_vec<T, E>(skip, int64_t(n) * Cv + cv, kb);
+                } else {
+                    load_packed_params<T, E>(bias, has_bias, skip, skip_bcast, n, cv, C, bv, kb);
+                }
             }
         }
 #pragma unroll
@@ -965,6 +993,37 @@ bool nhwc_split_plan(int64_t N, int64_t C, int64_t HW, int64_t groups, int E, Nh
     return true;
 }
 
+// NHWC pixels that are not a whole number of 16-byte vectors: runs of kpx
+// pixels that are (kpx = 16 / gcd(C * size, 16)), one channel block of all
+// C channels per run, element e of vector v the run's channel (v * E + e)
+// mod C.  Applies when H * W holds whole runs and a run is at most 256
+// vectors; the tiling over runs is nhwc_split_plan's.
+struct NhwcPacked {
+    int kpx, SV, P;
+    int64_t runs, ppb, B;
+};
+
+bool nhwc_packed_plan(int64_t N, int64_t C, int64_t HW, int size, NhwcPacked* pk) {
+    int64_t g = C * size, h = 16;
+    while (h) {
+        const int64_t r = g % h;
+        g = h;
+        h = r;
+    }
+    const int64_t kpx = 16 / g, SV = kpx * C * size / 16;
+    if (kpx < 2 || N < 1 || HW < 1 || HW % kpx != 0 || SV > 256) return false;
+    pk->kpx = int(kpx);
+    pk->SV = int(SV);
+    pk->P = int(256 / SV);
+    pk->runs = HW / kpx;
+    int64_t R = (N * pk->runs + pk->P * kSplitTargetBlocks - 1) / (pk->P * kSplitTargetBlocks);
+    if (R < kNhwcRowsPerThread) R = kNhwcRowsPerThread;
+    if (R > kUnroll) R = (R + kUnroll - 1) / kUnroll * kUnroll;
+    pk->ppb = pk->P * R;
+    pk->B = (pk->runs + pk->ppb - 1) / pk->ppb;
+    return true;
+}
+
 // Blocks per image (nhwc: pixel runs) or per (n, group) (group tiling: one
 // unrolled pass of vectors each) of the split route, planned for 16-byte
 // vectors; the partials per (n, group) the workspace holds.
@@ -972,8 +1031,11 @@ int64_t split_blocks(int dtype, int64_t N, int64_t C, int64_t HW, int64_t groups
     const int64_t ev = dtype == 0 ? 4 : 8;
     int64_t B;
     NhwcSplit sp;
+    NhwcPacked pk;
     if (channels_last && nhwc_split_plan(N, C, HW, groups, int(ev), &sp)) {
         B = sp.B;
+    } else if (channels_last && nhwc_packed_plan(N, C, HW, dtype == 0 ? 4 : 2, &pk)) {
+        B = pk.B;
     } else {
         const int64_t per_unit = channels_last ? HW * C : (C / groups) * HW;  // image / group
         B = (per_unit + ev * kVectorsPerBlock - 1) / (ev * kVectorsPerBlock);
@@ -1178,18 +1240,39 @@ hipError_t launch_sgn_tm(const SgnArgs& a, Route want, hipStream_t stream, const
             const int Cv = C / E, CBv = Cv / ncb;
             *route = name;
             hipLaunchKernelGGL((sgn_stats_nhwc_kernel<T, E>), grid, dim3(256), 0, stream, X, skip, bias,
-                               S, part, HW, Cv, CBv, ncb, P, cpg, groups, Bn, ppb, a.skip_broadcast);
+                               S, part, HW, Cv, CBv, ncb, P, cpg, groups, Bn, ppb, a.skip_broadcast, 1, C);
             hipLaunchKernelGGL(sgn_finalize_kernel, fin_grid, dim3(256), 0, stream, part, stat, Bn,
                                a.epsilon);
             hipLaunchKernelGGL((sgn_norm_nhwc_kernel<T, M, E>), grid, dim3(256), 0, stream, X, skip,
                                bias, static_cast<const T*>(S), gamma, beta, stat, Y, HW, Cv, CBv, ncb,
-                               P, cpg, groups, Bn, ppb, a.skip_broadcast, silu);
+                               P, cpg, groups, Bn, ppb, a.skip_broadcast, silu, 1, C);
             return hipGetLastError();
         };
         if (nhwc_e == EV) return launch(std::integral_constant<int, EV>(), "sgn.split.nhwc.vec16");
         if (nhwc_e == EV / 2) return launch(std::integral_constant<int, EV / 2>(), "sgn.split.nhwc.vec8");
         if constexpr (EV >= 8)
             if (nhwc_e == EV / 4) return launch(std::integral_constant<int, EV / 4>(), "sgn.split.nhwc.vec4");
+    }
+
+    // NHWC pixels that are not a whole number of 16-byte vectors: packed runs
+    // of pixels (nhwc_packed_plan), when the data tensors are 16-byte aligned.
+    NhwcPacked pk;
+    if (a.channels_last && nhwc_e == 1 && vec_allowed && data_ok &&
+        nhwc_packed_plan(a.N, C, HW, int(sizeof(T)), &pk)) {
+        if (pk.B > B_ws) {  // within the partials the workspace holds
+            pk.ppb = ((pk.runs + B_ws - 1) / B_ws + pk.P - 1) / pk.P * pk.P;
+            pk.B = (pk.runs + pk.ppb - 1) / pk.ppb;
+        }
+        const int Bn = int(pk.B);
+        const dim3 grid(unsigned(a.N * Bn));
+        *route = "sgn.split.nhwc.packed.vec16";
+        hipLaunchKernelGGL((sgn_stats_nhwc_kernel<T, EV>), grid, dim3(256), 0, stream, X, skip, bias, S, part,
+                           pk.runs, pk.SV, pk.SV, 1, pk.P, cpg, groups, Bn, pk.ppb, a.skip_broadcast, pk.kpx, C);
+        hipLaunchKernelGGL(sgn_finalize_kernel, fin_grid, dim3(256), 0, stream, part, stat, Bn, a.epsilon);
+        hipLaunchKernelGGL((sgn_norm_nhwc_kernel<T, M, EV>), grid, dim3(256), 0, stream, X, skip, bias,
+                           static_cast<const T*>(S), gamma, beta, stat, Y, pk.runs, pk.SV, pk.SV, 1, pk.P, cpg,
+                           groups, Bn, pk.ppb, a.skip_broadcast, silu, pk.kpx, C);
+        return hipGetLastError();
     }
 
     GroupGeom geo;

@@ -51,6 +51,15 @@ CASES = [
     (1, 4096, 2, 2, F16, F16, 1, False, True, 32, 0),     # 512 vectors per pixel: 2 channel blocks
     (3, 8, 1, 1, F32, F16, 1, True, False, 2, 1),         # H = W = 1
     (2, 2560, 8, 8, F32, F32, 1, False, True, 32, 1),     # 640 vectors per pixel: 8 channel blocks
+    # Pixels that are not a whole number of 16-byte vectors: runs of pixels that are.
+    (2, 15, 8, 8, F16, F32, 1, False, True, 5, 1),        # 8 pixels = 15 vectors per run
+    (3, 3, 16, 16, F16, F16, 1, True, True, 1, 0),        # 8 pixels = 3 vectors, broadcast skip
+    (2, 75, 8, 8, F16, F32, 1, False, False, 5, 1),       # 8 pixels = 75 vectors
+    (2, 15, 4, 6, F32, F16, 1, False, True, 3, 1),        # float32: 4 pixels = 15 vectors
+    (1, 5, 40, 40, F32, F32, 1, True, False, 5, 0),       # float32 instance norm, 4 pixels = 5 vectors
+    (4, 15, 64, 64, F16, F32, 1, False, True, 5, 1),      # many pixel runs per image
+    (1, 257, 4, 4, F16, F32, 1, False, True, 1, 0),       # 8 pixels = 257 vectors: scalars
+    (2, 15, 5, 5, F16, F32, 1, False, True, 5, 1),        # 25 pixels, not whole runs of 8: scalars
 ]
 
 
@@ -78,11 +87,13 @@ def split_channel_blocks(C, cpg, e):
     return best
 
 
-def nhwc_route(C, groups, T):
+def nhwc_route(C, groups, T, HW):
     """The NHWC route the library picks for aligned tensors of these
     channels: the channel-block cluster with the widest of 16-, 8- and
     4-byte accesses that divides a pixel and is no wider than a group;
-    otherwise the split route with the widest access (or scalars)."""
+    otherwise the split route with the widest access, or over runs of
+    pixels that make whole 16-byte vectors (at most 256 of them, H*W a
+    whole number of runs), or scalars."""
     size = np.dtype(T).itemsize
     width = next((b for b in (16, 8, 4) if b > size and C * size % b == 0), size)
     names = {16: "vec16", 8: "vec8", 4: "vec4"}
@@ -93,6 +104,9 @@ def nhwc_route(C, groups, T):
         return f"sgn.cluster.nhwc.{names[w]}"
     if width > size and split_channel_blocks(C, C // groups, width // size):
         return f"sgn.split.nhwc.{names[width]}"
+    kpx = 16 // math.gcd(C * size, 16)
+    if kpx > 1 and HW % kpx == 0 and kpx * C * size // 16 <= 256:
+        return "sgn.split.nhwc.packed.vec16"
     return "sgn.split.nhwc.scalar"
 
 
@@ -122,7 +136,7 @@ def test_matches_oracle(case, route):
     if route == "auto" and not cl:
         assert used.startswith("sgn.cluster")  # every NCHW case here fits the cluster route
     if route == "auto" and cl:
-        assert used == nhwc_route(C, groups, T)
+        assert used == nhwc_route(C, groups, T, H * W)
 
 
 # The split route's NHWC tiling over channel blocks: pixels wider than 256
