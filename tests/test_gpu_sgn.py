@@ -60,6 +60,7 @@ CASES = [
     (4, 15, 64, 64, F16, F32, 1, False, True, 5, 1),      # many pixel runs per image
     (1, 257, 4, 4, F16, F32, 1, False, True, 1, 0),       # 8 pixels = 257 vectors: scalars
     (2, 15, 5, 5, F16, F32, 1, False, True, 5, 1),        # 25 pixels, not whole runs of 8: scalars
+    (1, 15, 512, 512, F16, F32, 1, False, True, 5, 1),    # 5 x 964 partials: a finalize launch
 ]
 
 
@@ -87,7 +88,19 @@ def split_channel_blocks(C, cpg, e):
     return best
 
 
-def nhwc_route(C, groups, T, HW):
+def packed_blocks(N, C, HW, size):
+    """Workgroups per image of the packed-pixel split route (runs of pixels
+    that make whole 16-byte vectors), restated from the library's plan."""
+    kpx = 16 // math.gcd(C * size, 16)
+    sv = kpx * C * size // 16
+    runs, P = HW // kpx, 256 // sv
+    R = max(2, -(-N * runs // (P * 2048)))
+    if R > 4:
+        R = -(-R // 4) * 4
+    return -(-runs // (P * R))
+
+
+def nhwc_route(C, groups, T, HW, N=1):
     """The NHWC route the library picks for aligned tensors of these
     channels: the channel-block cluster with the widest of 16-, 8- and
     4-byte accesses that divides a pixel and is no wider than a group;
@@ -106,6 +119,10 @@ def nhwc_route(C, groups, T, HW):
         return f"sgn.split.nhwc.{names[width]}"
     kpx = 16 // math.gcd(C * size, 16)
     if kpx > 1 and HW % kpx == 0 and kpx * C * size // 16 <= 256:
+        # Normalize blocks combine their groups' partials themselves when
+        # there are at most 64 groups and 1024 partials.
+        if groups <= 64 and groups * packed_blocks(N, C, HW, size) <= 1024:
+            return "sgn.split.nhwc.packed.fold.vec16"
         return "sgn.split.nhwc.packed.vec16"
     return "sgn.split.nhwc.scalar"
 
@@ -136,7 +153,7 @@ def test_matches_oracle(case, route):
     if route == "auto" and not cl:
         assert used.startswith("sgn.cluster")  # every NCHW case here fits the cluster route
     if route == "auto" and cl:
-        assert used == nhwc_route(C, groups, T, H * W)
+        assert used == nhwc_route(C, groups, T, H * W, N)
 
 
 # The split route's NHWC tiling over channel blocks: pixels wider than 256
