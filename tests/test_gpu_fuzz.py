@@ -131,3 +131,47 @@ def test_skip_group_norm(case):
     assert_close(to_host(out.Y), ref_y, f"Y ({what})")
     if want_sum:
         assert_bitwise(to_host(out.S), ref_s, f"S ({what})")
+
+
+LARGE_SGN_CASES = 48
+
+
+@pytest.mark.parametrize("case", range(LARGE_SGN_CASES))
+def test_skip_group_norm_large(case):
+    """Larger images (H, W up to 128, up to 4M elements a tensor), so that
+    NHWC and NCHW groups spread over several workgroups (cluster exchanges),
+    the split routes and packed runs of pixels whose channels are not a
+    whole number of vectors (odd C) are drawn; all tensors 16-byte
+    aligned, so the vector and packed routes apply wherever their shapes
+    allow."""
+    rng = np.random.default_rng(4000 + case)
+    T = F16 if rng.random() < 0.6 else F32
+    M = F16 if rng.random() < 0.5 else F32
+    groups = int(rng.choice([1, 3, 5, 8, 16, 32]))
+    cpg = draw_length(rng, [(1, 3, 2), (4, 16, 3), (17, 40, 2)])
+    C = groups * cpg
+    N = int(rng.integers(1, 5))
+    H, W = int(rng.integers(8, 129)), int(rng.integers(8, 129))
+    while N * C * H * W > 2 * MAX_ELEMS:
+        H = max(1, H // 2)
+    cl = int(rng.random() < 0.6)
+    shape = (N, H, W, C) if cl else (N, C, H, W)
+    X = normal(rng, shape, T)
+    bcast = bool(rng.random() < 0.3)
+    skip = normal(rng, (N, C), T) if bcast else normal(rng, shape, T)
+    gamma, beta = uniform(rng, C, M), normal(rng, C, M, 0.1)
+    bias = normal(rng, C, T, 0.1) if rng.random() < 0.5 else None
+    act = int(rng.random() < 0.5)
+    want_sum = bool(rng.random() < 0.6)
+    ref_y, ref_s = oracle.skip_group_norm(X, gamma, beta, skip, bias, groups=groups, activation=act,
+                                          epsilon=1e-5, channels_last=cl, want_sum=True)
+    out = gn.skip_group_norm(dev(X), dev(gamma), dev(beta), dev(skip), dev(bias), groups=groups,
+                             activation=act, epsilon=1e-5, channels_last=cl, want_sum=want_sum)
+    route = gn.last_route()
+    torch.cuda.synchronize()
+    print(f"case {case}: {route}")
+    what = (f"{route} {T.__name__}/{M.__name__} {'nhwc' if cl else 'nchw'} {shape} g={groups} "
+            f"bcast={bcast} bias={bias is not None} act={act}")
+    assert_close(to_host(out.Y), ref_y, f"Y ({what})")
+    if want_sum:
+        assert_bitwise(to_host(out.S), ref_s, f"S ({what})")
