@@ -54,6 +54,8 @@ CASES = [
     (2, 640, 16, 16, np.float16, np.float16, 0, False, True, 32, 1, True),
     (1, 320, 8, 8, np.float32, np.float32, 1, True, False, 16, 0, True),
     (1, 64, 7, 9, np.float16, np.float32, 0, False, True, 8, 1, True),        # odd plane: phased
+    (2, 15, 16, 16, np.float16, np.float32, 1, False, True, 5, 1, True),     # odd C: packed runs, folded finalize
+    (1, 15, 512, 512, np.float16, np.float32, 1, False, True, 5, 1, True),   # packed runs, finalize launch
 ]
 
 
