@@ -1,0 +1,29 @@
+"""The library's host-side tiling rules, restated for tests (no GPU code).
+
+A test that expects a route or a workspace size derives it here, from the
+same rule the library applies, so that a change to either side shows up as
+a mismatch."""
+import math
+
+
+def packed_blocks(N, C, HW, size):
+    """Workgroups per image of the packed-pixel NHWC split route: runs of
+    kpx = 16 / gcd(C * size, 16) pixels (whole 16-byte vectors), P = 256 //
+    vectors-per-run runs in flight per workgroup, R >= 2 runs per thread
+    (as many as keep the grid near 2048 workgroups, whole steps of 4 beyond
+    4)."""
+    kpx = 16 // math.gcd(C * size, 16)
+    sv = kpx * C * size // 16
+    runs, P = HW // kpx, 256 // sv
+    R = max(2, -(-N * runs // (P * 2048)))
+    if R > 4:
+        R = -(-R // 4) * 4
+    return -(-runs // (P * R))
+
+
+def packed_applies(C, HW, size):
+    """Whether an aligned NHWC image of C channels takes packed runs: a run
+    of more than one pixel, H*W a whole number of runs, at most 256 vectors
+    a run."""
+    kpx = 16 // math.gcd(C * size, 16)
+    return kpx > 1 and HW % kpx == 0 and kpx * C * size // 16 <= 256

@@ -276,6 +276,21 @@ def test_workspace_size(lib):
     assert lib.skip_group_norm_workspace_size(x_desc(), 2, 1, None) == NULL
 
 
+@pytest.mark.parametrize("dt,size,N,C,H,W,groups", [
+    (SN_F16, 2, 8, 15, 128, 128, 5), (SN_F16, 2, 1, 15, 512, 512, 5), (SN_F16, 2, 16, 3, 256, 256, 1),
+    (SN_F32, 4, 2, 5, 40, 40, 5), (SN_F16, 2, 4, 75, 1024, 1024, 25)])
+def test_workspace_size_packed_runs(lib, dt, size, N, C, H, W, groups):
+    """NHWC pixels that are not a whole number of 16-byte vectors: the
+    workspace holds the packed-run tiling's partials (at least 64 per
+    (n, group)) of 16 bytes and one (mean, rstd) pair of 8 bytes per
+    (n, group)."""
+    from plans import packed_applies, packed_blocks
+    assert packed_applies(C, H * W, size)
+    B = min(max(packed_blocks(N, C, H * W, size), 64), 16384)
+    st, n = ws_size(lib, dt=dt, N=N, C=C, H=H, W=W, groups=groups, cl=1)
+    assert st == OK and n == N * groups * B * 16 + N * groups * 8
+
+
 SGN_REJECTS = [
     # element types
     (dict(dt=SN_BF16), DTYPE, "X: bfloat16"),

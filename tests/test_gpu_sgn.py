@@ -8,6 +8,7 @@ import torch
 import group_normalization_amd as gn
 import oracle
 import workloads
+from plans import packed_applies, packed_blocks
 from parity import assert_bitwise, assert_close, desc, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -88,18 +89,6 @@ def split_channel_blocks(C, cpg, e):
     return best
 
 
-def packed_blocks(N, C, HW, size):
-    """Workgroups per image of the packed-pixel split route (runs of pixels
-    that make whole 16-byte vectors), restated from the library's plan."""
-    kpx = 16 // math.gcd(C * size, 16)
-    sv = kpx * C * size // 16
-    runs, P = HW // kpx, 256 // sv
-    R = max(2, -(-N * runs // (P * 2048)))
-    if R > 4:
-        R = -(-R // 4) * 4
-    return -(-runs // (P * R))
-
-
 def nhwc_route(C, groups, T, HW, N=1):
     """The NHWC route the library picks for aligned tensors of these
     channels: the channel-block cluster with the widest of 16-, 8- and
@@ -117,8 +106,7 @@ def nhwc_route(C, groups, T, HW, N=1):
         return f"sgn.cluster.nhwc.{names[w]}"
     if width > size and split_channel_blocks(C, C // groups, width // size):
         return f"sgn.split.nhwc.{names[width]}"
-    kpx = 16 // math.gcd(C * size, 16)
-    if kpx > 1 and HW % kpx == 0 and kpx * C * size // 16 <= 256:
+    if packed_applies(C, HW, size):
         # Normalize blocks combine their groups' partials themselves when
         # there are at most 64 groups and 1024 partials.
         if groups <= 64 and groups * packed_blocks(N, C, HW, size) <= 1024:
