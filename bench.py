@@ -594,13 +594,13 @@ def host_cpu():
 # Profile summaries: rocprofv3 CSV output -> the text files under profiles/.
 
 PROF_COMMANDS = {
-    "kt": "rocprofv3 --kernel-trace --stats -f csv -d $REPO/gpurun_out/prof/kt -o bench -- "
+    "kt": "rocprofv3 --kernel-trace --stats -f csv -d $OUT/kt -o bench -- "
           "python3 $REPO/bench.py --steps 20 --warmup 3 --no-cpu-baseline",
-    "ktc": "rocprofv3 --kernel-trace --stats -f csv -d $REPO/gpurun_out/prof/ktc -o configs -- "
+    "ktc": "rocprofv3 --kernel-trace --stats -f csv -d $OUT/ktc -o configs -- "
            "python3 $REPO/bench.py --configs --steps 60 --warmup 5 --no-cpu-baseline",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/prof/fetch -o bench -- "
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/fetch -o bench -- "
              "python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/prof/write -o bench -- "
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/write -o bench -- "
              "python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
     "configs": "python3 $REPO/bench.py --configs --steps 60 --warmup 5",
     "bench": "python3 $REPO/bench.py",
@@ -770,8 +770,9 @@ def summarize(args):
     lines = ["# Kernel trace of the benchmark step (all hot-path kernels)", "",
              "Workloads: " + ", ".join(STEP_WORKLOADS) + "; the next_ops leg adds "
              f"{EXTRA_STEP_WORKLOAD}. One MI355X (gfx950).", "",
-             "Command (from the repository root on the GPU host, `$REPO` = repository root):", "",
-             "```", cmd("kt") + " > $REPO/gpurun_out/prof/kt/bench.json", "```", "",
+             "Command (`$REPO` = repository root, `$OUT` = the directory of rocprofv3 output, the one "
+             "given to `bench.py --summarize`):", "",
+             "```", cmd("kt") + " > $OUT/kt/bench.json", "```", "",
              "`rocprofv3 --stats` kernel summary (`bench_kernel_stats.csv`). The GB/s column is the "
              "workload's algorithmic bytes over the kernel's average duration:", "",
              "| kernel | workload | calls | avg us | min us | max us | GB/s (avg) |",
@@ -861,7 +862,8 @@ def summarize(args):
     if len(runs) != len(workloads.ORDER):
         sys.exit(f"expected {len(workloads.ORDER)} runs of op kernels in the configs trace, found {len(runs)}")
     lines = ["# The five reference workloads, each alone and cold: rocprofv3 kernel trace", "",
-             "Command (from the repository root on the GPU host, `$REPO` = repository root):", "", "```",
+             "Command (`$REPO` = repository root, `$OUT` = the output directory given to "
+             "`bench.py --summarize`):", "", "```",
              cmd("ktc"), "```", "",
              "Every invocation follows a 1 GiB copy (the copy kernel), so each starts from a cold cache. "
              "Durations per dispatch come from `configs_kernel_trace.csv` (5 warm-up and 60 timed "
@@ -898,8 +900,9 @@ def summarize(args):
     if os.path.exists(shapes_path):
         sh = _read_json_line(shapes_path)
         lines = ["# General shapes: every route family beyond the five workloads", "",
-                 "Command (from the repository root on the GPU host, `$REPO` = repository root):", "", "```",
-                 PROF_COMMANDS["shapes"] + " > $REPO/gpurun_out/prof/shapes.json", "```", "",
+                 "Command (`$REPO` = repository root, `$OUT` = the output directory given to "
+                 "`bench.py --summarize`):", "", "```",
+                 PROF_COMMANDS["shapes"] + " > $OUT/shapes.json", "```", "",
                  "Each shape alone, cold (a 1 GiB copy before every call), HIP events around the op on its "
                  f"stream, median of {sh['invocations']} calls; inputs drawn on the device "
                  "(`workloads.generate_on_device`, seed 0). GB/s counts algorithmic bytes: every input read "
