@@ -40,12 +40,21 @@ def make_inputs():
         "gc": rn(640), "ec": rn(640),
         "Xp": rn(2, 640, 31, 31), "kp": rn(2, 640, 31, 31), "bp": rn(640),
         "gp": rn(640, dtype=torch.float32), "ep": rn(640, dtype=torch.float32),
+        # Rows of 100000 float16 (the wide route: VGPRs plus LDS), GatedRMSNorm
+        # spans of 2049 (the phased route), and NHWC pixels of 15 channels
+        # (packed runs of 8 pixels, the split route with its finalize folded).
+        "xw": rn(3, 100000), "kw": rn(3, 100000), "gw": rn(100000),
+        "Xg": rn(24, 2049), "gg": rn(24, 2049), "sg": rn(2049),
+        "Xn": rn(2, 16, 16, 15), "kn": rn(2, 16, 16, 15), "gn": rn(15, dtype=torch.float32),
+        "en": rn(15, dtype=torch.float32),
     }
     t["ws_h"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xh"], 32, 1), dtype=torch.uint8,
                             device="cuda")
     t["ws_c"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xc"], 32, 0), dtype=torch.uint8,
                             device="cuda")
     t["ws_p"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xp"], 32, 0), dtype=torch.uint8,
+                            device="cuda")
+    t["ws_n"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xn"], 5, 1), dtype=torch.uint8,
                             device="cuda")
     return t
 
@@ -70,15 +79,23 @@ def run(t):
     f = gn.skip_group_norm(t["Xp"], t["gp"], t["ep"], t["kp"], t["bp"], groups=32, activation=1,
                            channels_last=0, want_sum=True, workspace=t["ws_p"])
     route_p = gn.last_route()
+    wd = gn.skip_rms_norm(t["xw"], t["kw"], t["gw"], None, 1e-6, want_sum=True)
+    route_w = gn.last_route()
+    gp = gn.gated_rms_norm(t["Xg"], t["sg"], t["gg"], 1e-5)
+    route_g = gn.last_route()
+    pk = gn.skip_group_norm(t["Xn"], t["gn"], t["en"], t["kn"], None, groups=5, activation=1,
+                            channels_last=1, want_sum=True, workspace=t["ws_n"])
+    route_n = gn.last_route()
     outs = [a.output, a.inv_std_var, a.input_skip_bias_sum, b.output, b.mean, b.inv_std_var, c,
             d.Y, d.S, e.Y, f.Y, f.S, o.output, o.input_skip_bias_sum, fl, q.output, q.inv_std_var,
-            q.input_skip_bias_sum]
-    return outs, (route_h, route_c, route_p, route_o, route_f, route_q)
+            q.input_skip_bias_sum, wd.output, wd.input_skip_bias_sum, gp, pk.Y, pk.S]
+    return outs, (route_h, route_c, route_p, route_o, route_f, route_q, route_w, route_g, route_n)
 
 
 def refill(t, seed):
     g = torch.Generator(device="cuda").manual_seed(seed)
-    for name in ("x", "k", "X", "gate", "xo", "ko", "Xf", "gf", "xq", "kq", "Xh", "kh", "Xc", "kc", "Xp", "kp"):
+    for name in ("x", "k", "X", "gate", "xo", "ko", "Xf", "gf", "xq", "kq", "Xh", "kh", "Xc", "kc", "Xp", "kp",
+                 "xw", "kw", "Xg", "gg", "Xn", "kn"):
         v = t[name]
         v.copy_(torch.randn(v.shape, generator=g, device="cuda", dtype=torch.float32).to(v.dtype))
 
@@ -96,13 +113,14 @@ def test_graph_replays_match_eager():
     with torch.cuda.graph(graph):
         captured, routes = run(t)
     assert routes == ("sgn.cluster.nhwc.vec16", "sgn.cluster.nchw.vec16", "sgn.cluster.nchw.phase",
-                      "ssln.phase.vec16", "gated.flat.vec16", "ssln.flat.vec16"), routes
+                      "ssln.phase.vec16", "gated.flat.vec16", "ssln.flat.vec16", "ssln.wide.vec16",
+                      "gated.phase.vec16", "sgn.split.nhwc.packed.fold.vec16"), routes
     torch.cuda.synchronize()
 
     names = ["ssln output", "ssln inv_std_var", "ssln S", "sln output", "sln mean", "sln inv_std_var",
              "gated Y", "sgn nhwc Y", "sgn nhwc S", "sgn nchw Y", "sgn nchw phased Y", "sgn nchw phased S",
              "ssln phased output", "ssln phased S", "gated flat Y", "ssln flat output", "ssln flat inv_std_var",
-             "ssln flat S"]
+             "ssln flat S", "ssln wide output", "ssln wide S", "gated phased Y", "sgn packed Y", "sgn packed S"]
     for rep in range(4):
         refill(t, seed=100 + rep)
         graph.replay()
