@@ -37,17 +37,22 @@
  *   - Pointers need no particular alignment (beyond their element type's):
  *     each call reads and writes in the widest of 16-, 8- and 4-byte vectors
  *     that divides a row (pixel, image plane) and every base address, else
- *     element by element -- except that skip_rms_norm / skip_layer_norm rows
- *     left with element-by-element accesses read aligned 16-byte vectors
- *     across row boundaries when input, skip, output and S share their
- *     offset from a 16-byte boundary and gamma, beta and bias are 16-byte
- *     aligned, and skip_group_norm NCHW groups likewise across group
- *     boundaries when X, skip, Y and S share their offset and H*W holds a
- *     16-byte vector -- with the same results up to float32 summation order.
- *     Such reads touch at most the 15 bytes beside a tensor's first and last
- *     element that lie in the same aligned 16-byte block (GPU memory is
- *     allocated and protected in far larger units, so they never fault);
- *     nothing outside a tensor is written.
+ *     element by element -- except where aligned 16-byte vectors are read
+ *     across the boundaries of rows, spans or groups instead:
+ *     skip_rms_norm / skip_layer_norm rows that would be read with accesses
+ *     narrower than 16 bytes, when input, skip, output and S share their
+ *     offset from a 16-byte boundary (short rows read as one stream take
+ *     gamma, beta and bias at any alignment; longer rows need them 16-byte
+ *     aligned); gated_rms_norm spans likewise when X, gate and Y share their
+ *     offset (longer spans need scale 16-byte aligned); skip_group_norm NCHW groups
+ *     when X, skip, Y and S share their offset and H*W holds a 16-byte
+ *     vector; and NHWC pixels that are not a whole number of 16-byte
+ *     vectors, read as runs of pixels that are, when X, Y, S and a full
+ *     skip are 16-byte aligned.  Results are the same up to float32
+ *     summation order.  Such reads touch at most the 15 bytes beside a
+ *     tensor's first and last element that lie in the same aligned 16-byte
+ *     block (GPU memory is allocated and protected in far larger units, so
+ *     they never fault); nothing outside a tensor is written.
  *   - Zero-sized leading dimensions are valid and launch nothing.  A row
  *     (hidden, span) or one SkipGroupNorm image (C*H*W) may hold at most
  *     2^30 elements.
