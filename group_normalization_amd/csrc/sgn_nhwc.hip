@@ -415,7 +415,11 @@ bool nhwc_cluster_plan(int E, int64_t N, int64_t C, int64_t HW, int64_t groups, 
         y = r;
     }
     const int64_t nb0 = C / (cpg / x * E);  // blocks of lcm(cpg, E) channels
-    for (int pass = 0; pass < 2; ++pass) {  // pass 0: at most one group per wave
+    // Pass 0: at most one group per wave.  Element accesses (E = 1) start
+    // from pass 1, whose whole-pixel blocks read pixels in one piece (f16 8 x
+    // 64 x 64 x 320 with a group per channel: 2.0 against 1.6 TB/s in
+    // one-channel blocks; f32 4 x 128 x 64 x 64: 1.9 against 1.2).
+    for (int pass = E == 1 ? 1 : 0; pass < 2; ++pass) {
         bool found = false;
         int64_t best_grid = 0;
         for (int64_t ncb = 1; ncb <= nb0; ++ncb) {
@@ -502,6 +506,7 @@ const void* nhwc_kernel_for(int E, int r, bool bcast) {
     if (E == EV / 2) return nhwc_kernel<T, M, EV / 2>(r, bcast);
     if constexpr (EV >= 8)
         if (E == EV / 4) return nhwc_kernel<T, M, EV / 4>(r, bcast);
+    if (E == 1) return nhwc_kernel<T, M, 1>(r, bcast);
     return nullptr;
 }
 
@@ -617,6 +622,7 @@ hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, const NhwcL
     if (E == EV / 2) return launch_nhwc_cluster<T, M, EV / 2>(ca, plan.R, blocks, stream);
     if constexpr (EV >= 8)
         if (E == EV / 4) return launch_nhwc_cluster<T, M, EV / 4>(ca, plan.R, blocks, stream);
+    if (E == 1) return launch_nhwc_cluster<T, M, 1>(ca, plan.R, blocks, stream);
     return hipErrorInvalidValue;  // the caller picks E from the same widths
 }
 
@@ -631,12 +637,16 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
     // The widest access that divides a pixel's channels and every base (the
     // broadcast skip's rows are C elements apart, like the pixels) and is
     // no wider than a group: groups narrower than a 16-byte vector take
-    // 8- or 4-byte vectors here rather than three launches.
+    // 8- or 4-byte vectors here rather than three launches, and odd channel
+    // counts or one-channel groups single elements, consecutive threads
+    // still reading consecutive bytes of a pixel (f16 8 x 128 x 128 x 15:
+    // 0.97 against 0.72 TB/s on the split route over packed runs of pixels;
+    // 2 x 64 x 64 x 15: 104 against 55 GB/s).
     int E = a.dtype == 0 ? widest_vector<float>(a.C, {a.X, a.Y, a.S, a.skip, a.bias})
                          : widest_vector<half_t>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
     while (E > 1 && a.C / a.groups < E) E /= 2;
     NhwcPlan plan;
-    if (E == 1 || !nhwc_cluster_plan(E, a.N, a.C, HW, a.groups, &plan)) return false;
+    if (!nhwc_cluster_plan(E, a.N, a.C, HW, a.groups, &plan)) return false;
     const void* kernel = a.dtype == 0
         ? (a.param_dtype == 0 ? nhwc_kernel_for<float, float>(E, plan.R, a.skip_broadcast)
                               : nhwc_kernel_for<float, half_t>(E, plan.R, a.skip_broadcast))
@@ -666,11 +676,12 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
     const bool split_whole_pixels = split_e > 1 && a.C / split_e <= 256;
     const int64_t grid = a.N * plan.NCB * plan.K;  // workgroups that do work
     if (split_whole_pixels && grid > 2 * resident) return false;
-    static const char* const kNames[2][3] = {
-        {"sgn.cluster.nhwc.smajor.vec4", "sgn.cluster.nhwc.smajor.vec8", "sgn.cluster.nhwc.smajor.vec16"},
-        {"sgn.cluster.nhwc.vec4", "sgn.cluster.nhwc.vec8", "sgn.cluster.nhwc.vec16"}};
+    static const char* const kNames[2][4] = {
+        {"sgn.cluster.nhwc.smajor.scalar", "sgn.cluster.nhwc.smajor.vec4", "sgn.cluster.nhwc.smajor.vec8",
+         "sgn.cluster.nhwc.smajor.vec16"},
+        {"sgn.cluster.nhwc.scalar", "sgn.cluster.nhwc.vec4", "sgn.cluster.nhwc.vec8", "sgn.cluster.nhwc.vec16"}};
     // Named by layout only where slices exchange (K > 1).
-    *route = kNames[lay.Kp > 1 || plan.K == 1 ? 1 : 0][E * size == 16 ? 2 : E * size == 8 ? 1 : 0];
+    *route = kNames[lay.Kp > 1 || plan.K == 1 ? 1 : 0][E == 1 ? 0 : E * size == 16 ? 3 : E * size == 8 ? 2 : 1];
     if (a.dtype == 0) {
         if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, lay, E, part, stream);
         else *err = launch_nhwc_typed<float, half_t>(a, plan, lay, E, part, stream);

@@ -27,3 +27,25 @@ def packed_applies(C, HW, size):
     a run."""
     kpx = 16 // math.gcd(C * size, 16)
     return kpx > 1 and HW % kpx == 0 and kpx * C * size // 16 <= 256
+
+
+def nhwc_cluster_fits(C, groups, E, HW):
+    """Whether the NHWC channel-block cluster has a plan for E-element
+    accesses: channel blocks of whole groups and accesses, at most 256
+    accesses and 16 groups each, and an image of at most 64 slices of at most
+    16 pixels per thread."""
+    cpg = C // groups
+    if C % E or cpg < E:
+        return False
+    unit = cpg // math.gcd(cpg, E) * E
+    nb0 = C // unit
+    for ncb in range(1, nb0 + 1):
+        if nb0 % ncb:
+            continue
+        cbv, cbg = C // ncb // E, C // ncb // cpg
+        if cbv > 256 or cbg > 16:
+            continue
+        P = 256 // cbv
+        if -(-HW // (P * 16)) <= 64:
+            return True
+    return False

@@ -42,7 +42,7 @@ def make_inputs():
         "gp": rn(640, dtype=torch.float32), "ep": rn(640, dtype=torch.float32),
         # Rows of 100000 float16 (the wide route: VGPRs plus LDS), GatedRMSNorm
         # spans of 2049 (the phased route), and NHWC pixels of 15 channels
-        # (packed runs of 8 pixels, the split route with its finalize folded).
+        # (the channel-block cluster with element accesses, exchanging moments).
         "xw": rn(3, 100000), "kw": rn(3, 100000), "gw": rn(100000),
         "Xg": rn(24, 2049), "gg": rn(24, 2049), "sg": rn(2049),
         "Xn": rn(2, 16, 16, 15), "kn": rn(2, 16, 16, 15), "gn": rn(15, dtype=torch.float32),
@@ -114,13 +114,13 @@ def test_graph_replays_match_eager():
         captured, routes = run(t)
     assert routes == ("sgn.cluster.nhwc.vec16", "sgn.cluster.nchw.vec16", "sgn.cluster.nchw.phase",
                       "ssln.phase.vec16", "gated.flat.vec16", "ssln.flat.vec16", "ssln.wide.vec16",
-                      "gated.phase.vec16", "sgn.split.nhwc.packed.fold.vec16"), routes
+                      "gated.phase.vec16", "sgn.cluster.nhwc.scalar"), routes
     torch.cuda.synchronize()
 
     names = ["ssln output", "ssln inv_std_var", "ssln S", "sln output", "sln mean", "sln inv_std_var",
              "gated Y", "sgn nhwc Y", "sgn nhwc S", "sgn nchw Y", "sgn nchw phased Y", "sgn nchw phased S",
              "ssln phased output", "ssln phased S", "gated flat Y", "ssln flat output", "ssln flat inv_std_var",
-             "ssln flat S", "ssln wide output", "ssln wide S", "gated phased Y", "sgn packed Y", "sgn packed S"]
+             "ssln flat S", "ssln wide output", "ssln wide S", "gated phased Y", "sgn odd-C Y", "sgn odd-C S"]
     for rep in range(4):
         refill(t, seed=100 + rep)
         graph.replay()

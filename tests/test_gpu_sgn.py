@@ -8,7 +8,7 @@ import torch
 import group_normalization_amd as gn
 import oracle
 import workloads
-from plans import packed_applies, packed_blocks
+from plans import nhwc_cluster_fits, packed_applies, packed_blocks
 from parity import assert_bitwise, assert_close, desc, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -46,7 +46,7 @@ CASES = [
     (3, 64, 7, 9, F16, F16, 1, True, True, 8, 0),
     (2, 96, 5, 5, F32, F32, 0, False, True, 4, 1),        # H*W = 25: not a whole vector
     (1, 40, 13, 11, F16, F32, 1, False, False, 5, 1),
-    (2, 12, 6, 6, F16, F16, 1, False, True, 3, 0),        # C not a whole vector: scalar NHWC
+    (2, 12, 6, 6, F16, F16, 1, False, True, 3, 0),        # 24-byte pixels, 4-channel groups: 8-byte accesses
     (2, 16, 4, 4, F32, F32, 0, True, True, 16, 1),        # groups == C (instance norm)
     (2, 24, 3, 5, F16, F32, 0, False, False, 1, 0),       # one group (layer norm)
     (1, 4096, 2, 2, F16, F16, 1, False, True, 32, 0),     # 512 vectors per pixel: 2 channel blocks
@@ -102,8 +102,8 @@ def nhwc_route(C, groups, T, HW, N=1):
     w = width
     while w > size and C // groups < w // size:
         w //= 2
-    if w > size:
-        return f"sgn.cluster.nhwc.{names[w]}"
+    if nhwc_cluster_fits(C, groups, w // size, HW):
+        return f"sgn.cluster.nhwc.{names[w]}" if w > size else "sgn.cluster.nhwc.scalar"
     if width > size and split_channel_blocks(C, C // groups, width // size):
         return f"sgn.split.nhwc.{names[width]}"
     if packed_applies(C, HW, size):
@@ -219,7 +219,7 @@ NHWC_LIMIT_CASES = [
     (2, 96, 9, 11, F16, 8, False, "sgn.cluster.nhwc.vec16"),      # 12 channels/group, ragged last slice
     (2, 64, 8, 8, F16, 16, False, "sgn.cluster.nhwc.vec8"),       # 4 channels/group: 8-byte vectors
     (2, 64, 8, 8, F16, 32, True, "sgn.cluster.nhwc.vec4"),        # 2 channels/group: 4-byte vectors
-    (2, 64, 8, 8, F16, 64, False, "sgn.split.nhwc.vec16"),        # 1 channel/group: split route
+    (2, 64, 8, 8, F16, 64, False, "sgn.cluster.nhwc.scalar"),     # 1 channel/group: element accesses
     (2, 324, 16, 16, F16, 36, False, "sgn.cluster.nhwc.vec8"),    # 648-byte pixels: 8-byte vectors
     (2, 162, 8, 8, F16, 18, True, "sgn.cluster.nhwc.vec4"),       # 324-byte pixels: 4-byte vectors
     (2, 90, 8, 8, F32, 9, False, "sgn.cluster.nhwc.vec8"),        # float32 360-byte pixels

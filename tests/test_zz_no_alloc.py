@@ -54,7 +54,7 @@ CASES = [
     (2, 640, 16, 16, np.float16, np.float16, 0, False, True, 32, 1, True),
     (1, 320, 8, 8, np.float32, np.float32, 1, True, False, 16, 0, True),
     (1, 64, 7, 9, np.float16, np.float32, 0, False, True, 8, 1, True),        # odd plane: phased
-    (2, 15, 16, 16, np.float16, np.float32, 1, False, True, 5, 1, True),     # odd C: packed runs, folded finalize
+    (2, 15, 16, 16, np.float16, np.float32, 1, False, True, 5, 1, True),     # odd C: element accesses (split: packed runs)
     (1, 15, 512, 512, np.float16, np.float32, 1, False, True, 5, 1, True),   # packed runs, finalize launch
 ]
 
@@ -105,7 +105,10 @@ def test_noalloc_split_routes(route):
     with gn.force_route(route):
         r0 = check_pair(CASES[2], seed=4)
         r1 = check_pair(CASES[4], seed=5)
-    assert r0.startswith("sgn.split") and r1.startswith("sgn.split")
+        r2 = check_pair(CASES[5], seed=6)  # odd C: packed runs with the finalize folded (split)
+    assert r0.startswith("sgn.split") and r1.startswith("sgn.split") and r2.startswith("sgn.split")
+    if route == "split":
+        assert r2 == "sgn.split.nhwc.packed.fold.vec16"
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
