@@ -415,10 +415,11 @@ bool nhwc_cluster_plan(int E, int64_t N, int64_t C, int64_t HW, int64_t groups, 
         y = r;
     }
     const int64_t nb0 = C / (cpg / x * E);  // blocks of lcm(cpg, E) channels
-    // Pass 0: at most one group per wave.  Element accesses (E = 1) start
-    // from pass 1, whose whole-pixel blocks read pixels in one piece (f16 8 x
-    // 64 x 64 x 320 with a group per channel: 2.0 against 1.6 TB/s in
-    // one-channel blocks; f32 4 x 128 x 64 x 64: 1.9 against 1.2).
+    // Pass 0: at most one group per wave; pass 1: up to four.  Element
+    // accesses (E = 1) start from pass 1: its wider blocks give each wave
+    // longer runs of a pixel (f16 8 x 64 x 64 x 320 with a group per channel:
+    // 16-channel blocks 2.0 TB/s against 1.6 in 4-channel ones; f32 4 x 128 x
+    // 64 x 64: 1.9 against 1.2).
     for (int pass = E == 1 ? 1 : 0; pass < 2; ++pass) {
         bool found = false;
         int64_t best_grid = 0;

@@ -226,11 +226,21 @@ NHWC_LIMIT_CASES = [
     (1, 16, 9, 7, F32, 4, True, "sgn.cluster.nhwc.vec16"),        # float32, 4 channels/group, 1 slice
     (2, 2560, 8, 8, F32, 32, False, "sgn.cluster.nhwc.vec16"),    # 640 vectors per pixel, 3 pixel lanes
     (600, 16, 2, 2, F32, 2, True, "sgn.cluster.nhwc.vec16"),      # one slice per image: no exchange
+    # Element accesses: odd C (five blocks of one 3-channel group, 85 pixel
+    # lanes) up to 64 slices of 16 pixels per thread, then packed runs
+    # (split, 5 x 321 partials: a finalize launch).
+    (1, 15, 340, 256, F16, 5, False, "sgn.cluster.nhwc.scalar"),
+    (1, 15, 341, 256, F16, 5, True, "sgn.split.nhwc.packed.vec16"),
+    (2, 15, 64, 64, F32, 5, True, "sgn.cluster.nhwc.scalar"),     # float32 odd C, broadcast skip
     # Residency (MI355X: 256 CUs, two workgroups each at 16 pixels per
     # thread): 704 workgroups, more than are resident at once, but each
     # image's 88 within reach of one another: one launch in two rounds,
     # slice-major block order.
     (8, 640, 64, 64, F16, 32, False, "sgn.cluster.nhwc.smajor.vec16"),
+    # Instance norm (one channel a group): 20 blocks of 16 channels x 16
+    # slices of 16 pixels per thread, 2560 workgroups, more than are resident
+    # at once: slice-major.
+    (8, 320, 64, 64, F16, 320, False, "sgn.cluster.nhwc.smajor.scalar"),
     # One image of 1024 workgroups whose clusters would spread over 904
     # block ids slice-major, more than the device holds at once: the
     # cluster-major order (64 consecutive ids per cluster), two rounds.
@@ -293,6 +303,8 @@ FALLBACK_CASES = [
     (2, 320, 24, 24, F16, F32, 1, False, True, 32, 1),  # NHWC, 11 slices of 51 pixel lanes
     (2, 72, 16, 16, F16, F16, 1, True, False, 8, 0),    # NHWC, 2 groups per wave, 9 slices
     (1, 48, 33, 31, F32, F32, 1, False, True, 4, 1),    # NHWC float32, 32 slices, ragged last
+    (2, 15, 24, 24, F16, F32, 1, False, True, 5, 1),    # NHWC odd C: element accesses, 11 slices
+    (1, 32, 20, 20, F32, F16, 1, True, False, 32, 0),   # NHWC instance norm: element accesses
 ]
 
 
