@@ -323,54 +323,60 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
         return h > l ? float(h - l) : 0.0f;
     };
     auto vec_of = [&](int s, int r) { return slice_begin(s) + uint32_t(t) + uint32_t(r) * kClusterThreads; };
-    // Span position of vector i's element 0 (negative before the span).
-    auto first_pos = [&](uint32_t i) { return int64_t(i) * E - p; };
-    // The two channels (within the group) a vector can hold, and the first
-    // span position of the second.
-    struct Chan {
-        int lo, hi;
-        int64_t edge;
+    // Where vector i lies in the span, in 32-bit positions (a span holds at
+    // most kClusterMaxK * kPhaseMaxR * 256 vectors): its elements [lo, hi)
+    // are the span's, those below nlo belong to channel clo of the group and
+    // the rest to chi (a vector holds at most two channels since H*W >= E).
+    const int span32 = int(span);
+    struct Lay {
+        int lo, hi, nlo, clo, chi;
     };
-    auto chans = [&](uint32_t i) {
-        const int64_t j0 = first_pos(i);
+    auto lay_of = [&](uint32_t i) {
+        const int j0 = int(i) * E - p;
+        Lay l;
+        l.lo = j0 < 0 ? -j0 : 0;
+        const int rem = span32 - j0;
+        l.hi = rem < E ? rem : E;
         const uint32_t c = fastdiv(uint32_t(j0 > 0 ? j0 : 0), a.div);
-        Chan ch;
-        ch.lo = c < uint32_t(a.cpg) ? int(c) : a.cpg - 1;
-        ch.hi = ch.lo + 1 < a.cpg ? ch.lo + 1 : ch.lo;
-        ch.edge = int64_t(c + 1) * HW;
-        return ch;
+        l.clo = c < uint32_t(a.cpg) ? int(c) : a.cpg - 1;
+        l.chi = l.clo + 1 < a.cpg ? l.clo + 1 : l.clo;
+        const int below = int(c + 1) * int(HW) - j0;  // >= 1
+        l.nlo = below < E ? below : E;
+        return l;
     };
-    auto form = [&](const V& x, const V& kv, uint32_t i, V& s) {
-        const Chan ch = chans(i);
-        const float4 c0 = cst[ch.lo], c1 = cst[ch.hi];
-        const int64_t j0 = first_pos(i);
+    auto form = [&](const V& x, const V& kv, const Lay& l, V& s) {
+        const float4 c0 = cst[l.clo], c1 = cst[l.chi];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const bool up = j0 + e >= ch.edge;
+            const bool up = e >= l.nlo;
             const float bb = up ? c1.x : c0.x;
             const float kk = BCAST ? (up ? c1.y : c0.y) : to_f32(kv.v[e]);
             residual_sum<T>(to_f32(x.v[e]), kk, has_bias, bb, s.v[e]);
         }
     };
-    auto accumulate = [&](ShiftedSums& acc, float& cnt, const V& s, uint32_t i) {
-        const int64_t j0 = first_pos(i);
+    // The span's elements in order, shifted by an element of the thread's
+    // first vector: its first, or its last for the span's first vector
+    // (which ends inside the span, as the span holds at least E elements).
+    // Elements outside the span add zero differences.
+    auto accumulate = [&](ShiftedSums& acc, float& cnt, const V& s, const Lay& l) {
+        if (cnt == 0.0f) acc.shift = to_f32(l.lo > 0 ? s.v[E - 1] : s.v[0]);
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (j0 + e >= 0 && j0 + e < span) {
-                acc.add(to_f32(s.v[e]), cnt == 0.0f);
-                cnt += 1.0f;
-            }
+        for (int e = 0; e < E; ++e) {
+            const float d = e >= l.lo && e < l.hi ? to_f32(s.v[e]) - acc.shift : 0.0f;
+            acc.s1 += d;
+            acc.s2 = fmaf_(d, d, acc.s2);
+        }
+        cnt += float(l.hi - l.lo);
     };
     // Vector i of the span into `dst` (aligned base): whole when it lies
     // inside the span, else the span's elements one by one.
-    auto put = [&](T* dst, uint32_t i, const V& v) {
-        const int64_t j0 = first_pos(i);
-        if (j0 >= 0 && j0 + E <= span) {
+    auto put = [&](T* dst, uint32_t i, const Lay& l, const V& v) {
+        if (l.lo == 0 && l.hi == E) {
             store_vec_stream<T, E>(dst, v0 + i, v);
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                if (j0 + e >= 0 && j0 + e < span) dst[(v0 + i) * E + e] = v.v[e];
+                if (e >= l.lo && e < l.hi) dst[(v0 + i) * E + e] = v.v[e];
         }
     };
 
@@ -397,8 +403,9 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
     for (int r = 0; r < R; ++r) {
         const uint32_t j = vec_of(k, r);
         if (j < end) {
-            form(xs[r], sv[r], j, sv[r]);
-            accumulate(acc, cnt, sv[r], j);
+            const Lay l = lay_of(j);
+            form(xs[r], sv[r], l, sv[r]);
+            accumulate(acc, cnt, sv[r], l);
         }
     }
     SN_PHASE(a.trace, 1);
@@ -414,7 +421,7 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const uint32_t j = vec_of(k, r);
-                if (j < end) put(sa, j, sv[r]);
+                if (j < end) put(sa, j, lay_of(j), sv[r]);
             }
         }
         SN_PHASE(a.trace, 3);
@@ -453,8 +460,9 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
                     if (j < qend) {
                         V x = load_vec<T, E>(xa, v0 + j), kv, sq;
                         if constexpr (!BCAST) kv = load_vec<T, E>(ka, v0 + j);
-                        form(x, kv, j, sq);
-                        accumulate(qacc, qcnt, sq, j);
+                        const Lay l = lay_of(j);
+                        form(x, kv, l, sq);
+                        accumulate(qacc, qcnt, sq, l);
                     }
                 }
                 m = block_merge_rcp(qacc.moments(qcnt), sh);
@@ -466,7 +474,7 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const uint32_t j = vec_of(k, r);
-                if (j < end) put(sa, j, sv[r]);
+                if (j < end) put(sa, j, lay_of(j), sv[r]);
             }
         }
         SN_PHASE(a.trace, 3);
@@ -479,19 +487,18 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
     for (int r = 0; r < R; ++r) {
         const uint32_t j = vec_of(k, r);
         if (j < end) {
-            const Chan ch = chans(j);
-            const float4 c0 = cst[ch.lo], c1 = cst[ch.hi];
+            const Lay l = lay_of(j);
+            const float4 c0 = cst[l.clo], c1 = cst[l.chi];
             const float scl0 = st.y * c0.z, scl1 = st.y * c1.z;
-            const int64_t j0 = first_pos(j);
             V out;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const bool up = j0 + e >= ch.edge;
+                const bool up = e >= l.nlo;
                 float y = fmaf_(to_f32(sv[r].v[e]) - st.x, up ? scl1 : scl0, up ? c1.w : c0.w);
                 if (a.silu) y = silu_f32(y);
                 out.v[e] = from_f32<T>(y);
             }
-            put(ya, j, out);
+            put(ya, j, l, out);
         }
     }
     SN_PHASE(a.trace, 5);
