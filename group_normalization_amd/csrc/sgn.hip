@@ -384,15 +384,29 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
     const uint32_t end = slice_end(k);
     auto clamp = [&](uint32_t j) { return j < end ? j : (slice_begin(k) < nvr ? slice_begin(k) : nvr - 1); };
     V sv[R], xs[R];
+    // The table's first entries load before the data (the later rounds of
+    // groups wider than a workgroup after it), by every thread (threads past
+    // the group's channels re-read its first) and with bias read from X when
+    // absent, so that no load sits behind a branch (the data loads would
+    // wait for it).
+    const T* bias_src = has_bias ? a.bias : a.X;  // X holds at least C elements
+    const int ch0 = g * a.cpg + (t < a.cpg ? t : 0);
+    const T tb = bias_src[ch0];
+    T tk = T(0);
+    if constexpr (BCAST) tk = a.skip[int64_t(n) * a.C + ch0];
+    const M tg = a.gamma[ch0], te = a.beta[ch0];
+    __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the data loads
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t j = clamp(vec_of(k, r));
         xs[r] = load_vec_stream<T, E>(xa, v0 + j);
         if constexpr (!BCAST) sv[r] = load_vec_stream<T, E>(ka, v0 + j);
     }
-    for (int c = t; c < a.cpg; c += kClusterThreads) {
+    if (t < a.cpg)
+        cst[t] = make_float4(has_bias ? to_f32(tb) : 0.0f, BCAST ? to_f32(tk) : 0.0f, to_f32(tg), to_f32(te));
+    for (int c = t + kClusterThreads; c < a.cpg; c += kClusterThreads) {
         const int ch = g * a.cpg + c;
-        cst[c] = make_float4(has_bias ? to_f32(a.bias[ch]) : 0.0f,
+        cst[c] = make_float4(has_bias ? to_f32(bias_src[ch]) : 0.0f,
                              BCAST ? to_f32(a.skip[int64_t(n) * a.C + ch]) : 0.0f, to_f32(a.gamma[ch]),
                              to_f32(a.beta[ch]));
     }
