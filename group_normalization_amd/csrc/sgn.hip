@@ -380,7 +380,7 @@ sgn_cluster_phase_kernel(ClusterArgs<T, M> a) {
         }
     };
 
-    // ---- own slice: data loads first, then the group's channel table.
+    // ---- own slice: the group's channel table, then the data loads.
     const uint32_t end = slice_end(k);
     auto clamp = [&](uint32_t j) { return j < end ? j : (slice_begin(k) < nvr ? slice_begin(k) : nvr - 1); };
     V sv[R], xs[R];
