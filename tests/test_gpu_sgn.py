@@ -232,6 +232,10 @@ NHWC_LIMIT_CASES = [
     (1, 15, 340, 256, F16, 5, False, "sgn.cluster.nhwc.scalar"),
     (1, 15, 341, 256, F16, 5, True, "sgn.split.nhwc.packed.vec16"),
     (2, 15, 64, 64, F32, 5, True, "sgn.cluster.nhwc.scalar"),     # float32 odd C, broadcast skip
+    (2, 1, 17, 19, F16, 1, False, "sgn.cluster.nhwc.scalar"),     # one channel
+    (2, 2, 5, 7, F16, 2, True, "sgn.cluster.nhwc.scalar"),        # two one-channel groups
+    (3, 3, 1, 1, F32, 3, False, "sgn.cluster.nhwc.scalar"),       # one pixel: every group one value
+    (2, 2, 3, 3, F16, 1, False, "sgn.cluster.nhwc.vec4"),         # 4-byte pixels, one group
     # Residency (MI355X: 256 CUs, two workgroups each at 16 pixels per
     # thread): 704 workgroups, more than are resident at once, but each
     # image's 88 within reach of one another: one launch in two rounds,
