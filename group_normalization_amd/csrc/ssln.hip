@@ -896,23 +896,30 @@ ssln_flat_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     }
     // The tables: each thread's (at most kFlatTable / 256) columns are loaded
     // at once (indices clamped, no load behind a branch), then stored.
+    // Every table load is unconditional (gamma's address in place of an
+    // absent bias or beta, its values unused) and every value is converted
+    // outside the lane branch that guards the LDS store: a load whose use
+    // sits behind a branch is waited for there, one round trip each.
     constexpr int kFill = kFlatTable / 256;
+    const T* bias_src = has_bias ? bias : gamma;
+    const T* beta_src = beta ? beta : gamma;
     T gv[kFill], bv[kFill], tv[kFill];
 #pragma unroll
     for (int j = 0; j < kFill; ++j) {
         const int c = threadIdx.x + j * 256;
         const int cc = c < C ? c : C - 1;
         gv[j] = gamma[cc];
-        if (has_bias) bv[j] = bias[cc];
-        if constexpr (CENTER)
-            if (beta) tv[j] = beta[cc];
+        bv[j] = bias_src[cc];
+        if constexpr (CENTER) tv[j] = beta_src[cc];
     }
 #pragma unroll
     for (int j = 0; j < kFill; ++j) {
         const int c = threadIdx.x + j * 256;
+        const float2 g_b = make_float2(to_f32(gv[j]), has_bias ? to_f32(bv[j]) : 0.0f);
+        const float t_v = CENTER && beta ? to_f32(tv[j]) : 0.0f;
         if (c < C) {
-            gb[c] = make_float2(to_f32(gv[j]), has_bias ? to_f32(bv[j]) : 0.0f);
-            if constexpr (CENTER) bt[c] = beta ? to_f32(tv[j]) : 0.0f;
+            gb[c] = g_b;
+            if constexpr (CENTER) bt[c] = t_v;
         }
     }
     __syncthreads();  // the tables
