@@ -2,6 +2,7 @@
 // The operator and the other routes are described in sgn.hip.
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "sgn_common.h"
@@ -62,6 +63,8 @@ struct NhwcClusterArgs {
     bool skip_bcast, silu;
     float eps;
     unsigned long long* trace;  // phase timestamps (measurement builds)
+    int C;    // channels per pixel (packed runs: element e of vector v is channel (v * E + e) mod C)
+    int kpx;  // pixels per unit: 1, or the pixels of a packed run
 };
 
 constexpr int kNhwcMaxCBg = 16;   // groups per channel block: four per wave
@@ -69,12 +72,19 @@ constexpr int kNhwcMaxR = 16;     // pixels per thread
 constexpr int kWaves = kClusterThreads / 64;
 constexpr int kGroupsPerWave = kNhwcMaxCBg / kWaves;
 
-template <typename T, typename M, int E, int R, bool BCAST>
+// PACKED: a unit is a run of kpx pixels that is a whole number of 16-byte
+// vectors (pixels of C channels whose bytes are not), one channel block of
+// all kpx * C channels; element e of vector v is channel (v * E + e) mod C,
+// so a vector may touch any number of groups.  Each thread then keeps
+// shifted sums per element (a column per element instead of per group slot),
+// and group g merges its columns in pixel, then channel order.
+template <typename T, typename M, int E, int R, bool BCAST, bool PACKED>
 __global__ void __launch_bounds__(kClusterThreads)
 sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
     using V = Vec<T, E>;
-    __shared__ Moments lane_m[2 * kClusterThreads];  // [pixel lane][column = 2 * vector + slot]
-    __shared__ Moments col_m[2 * kClusterThreads];   // column totals
+    constexpr int kCols = PACKED ? E : 2;  // columns per vector
+    __shared__ Moments lane_m[kCols * kClusterThreads];  // [pixel lane][column = kCols * vector + slot]
+    __shared__ Moments col_m[kCols * kClusterThreads];   // column totals
     __shared__ Moments own_m[kNhwcMaxCBg];           // this slice's group moments
     __shared__ Moments slice_m[kNhwcMaxK][kNhwcMaxCBg];  // recomputed slices
     __shared__ float2 stat[kNhwcMaxCBg];
@@ -109,7 +119,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
     const int cvec = cb * a.CBv + v;  // channel vector within the pixel
     const int glo = int(fastdiv(uint32_t(v * E), a.div_cpg));  // block-local group of the vector's first channel
     const int split = (glo + 1) * a.cpg - v * E;  // channels [0, split) are in glo, the rest in glo + 1
-    const int ncol = 2 * a.CBv;
+    const int ncol = kCols * a.CBv;
     const int SW = 1 << a.sw_log;
     const int64_t img = int64_t(n) * a.HW;
     const bool has_bias = a.bias != nullptr;
@@ -131,15 +141,36 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
         return (img + int64_t(s) * a.pps + pl + int64_t(r) * a.P) * a.Cv + cvec;
     };
     // Per-channel constants: bias and broadcast skip (as T), gamma, beta.
+    // Packed: per element, by its channel.
     V bvec, kvec;
     M gam[E], bet[E];
-    auto load_constants = [&]() {
-        bvec = load_vec<T, E>(has_bias ? a.bias : a.X, cvec);  // X holds at least C elements
-        if constexpr (BCAST) kvec = load_vec<T, E>(a.skip, int64_t(n) * a.Cv + cvec);
+    int ch[PACKED ? E : 1];
+    if constexpr (PACKED) {
+        int c = (cvec * E) % a.C;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            gam[e] = a.gamma[cvec * E + e];
-            bet[e] = a.beta[cvec * E + e];
+            ch[e] = c;
+            c = c + 1 == a.C ? 0 : c + 1;
+        }
+    }
+    auto load_constants = [&]() {
+        if constexpr (PACKED) {
+            const T* bias_src = has_bias ? a.bias : a.X;  // X holds at least C elements
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                bvec.v[e] = bias_src[ch[e]];
+                if constexpr (BCAST) kvec.v[e] = a.skip[int64_t(n) * a.C + ch[e]];
+                gam[e] = a.gamma[ch[e]];
+                bet[e] = a.beta[ch[e]];
+            }
+        } else {
+            bvec = load_vec<T, E>(has_bias ? a.bias : a.X, cvec);  // X holds at least C elements
+            if constexpr (BCAST) kvec = load_vec<T, E>(a.skip, int64_t(n) * a.Cv + cvec);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                gam[e] = a.gamma[cvec * E + e];
+                bet[e] = a.beta[cvec * E + e];
+            }
         }
     };
     auto form = [&](const V& x, const V& kv, V& s) {
@@ -153,34 +184,50 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
     // Shifted sums of the thread's two groups over its pixels of a slice, in
     // pixel then channel order; the shifts are the first pixel's first and
     // last channels (the last channel is in the upper group when it exists).
+    // Packed: one per element, shifted by its value in the first unit.
     struct SlotSums {
         ShiftedSums lo, hi;
     };
-    auto accumulate = [&](SlotSums& acc, const V& s, int r) {
-        if (r == 0) {
-            acc.lo.shift = to_f32(s.v[0]);
-            acc.hi.shift = to_f32(s.v[E - 1]);
-        }
+    struct ElemSums {
+        ShiftedSums el[E];
+    };
+    using Acc = typename std::conditional<PACKED, ElemSums, SlotSums>::type;
+    auto accumulate = [&](Acc& acc, const V& s, int r) {
+        if constexpr (PACKED) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float x = to_f32(s.v[e]);
-            const bool in_lo = e < split;
-            const float d = x - (in_lo ? acc.lo.shift : acc.hi.shift);
-            const float dl = in_lo ? d : 0.0f, dh = in_lo ? 0.0f : d;
-            acc.lo.s1 += dl;
-            acc.lo.s2 = fmaf_(dl, dl, acc.lo.s2);
-            acc.hi.s1 += dh;
-            acc.hi.s2 = fmaf_(dh, dh, acc.hi.s2);
+            for (int e = 0; e < E; ++e) acc.el[e].add(to_f32(s.v[e]), r == 0);
+        } else {
+            if (r == 0) {
+                acc.lo.shift = to_f32(s.v[0]);
+                acc.hi.shift = to_f32(s.v[E - 1]);
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float x = to_f32(s.v[e]);
+                const bool in_lo = e < split;
+                const float d = x - (in_lo ? acc.lo.shift : acc.hi.shift);
+                const float dl = in_lo ? d : 0.0f, dh = in_lo ? 0.0f : d;
+                acc.lo.s1 += dl;
+                acc.lo.s2 = fmaf_(dl, dl, acc.lo.s2);
+                acc.hi.s1 += dh;
+                acc.hi.s2 = fmaf_(dh, dh, acc.hi.s2);
+            }
         }
     };
     // Group moments of a slice from every thread's sums over its nv pixels,
     // into dst[0 .. CBg).  The same code and thread mapping run wherever a
-    // slice is reduced.  Ends with dst written but not yet visible.
-    auto reduce_slice = [&](const SlotSums& acc, int nv, Moments* dst) {
+    // slice is reduced.  Ends with dst written, by thread g for group g
+    // (packed: visible to every thread).
+    auto reduce_slice = [&](const Acc& acc, int nv, Moments* dst) {
         if (active) {
-            const int nlo = split < E ? split : E;
-            lane_m[pl * ncol + 2 * v] = acc.lo.moments(float(nv * nlo));
-            lane_m[pl * ncol + 2 * v + 1] = acc.hi.moments(float(nv * (E - nlo)));
+            if constexpr (PACKED) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) lane_m[pl * ncol + E * v + e] = acc.el[e].moments(float(nv));
+            } else {
+                const int nlo = split < E ? split : E;
+                lane_m[pl * ncol + 2 * v] = acc.lo.moments(float(nv * nlo));
+                lane_m[pl * ncol + 2 * v + 1] = acc.hi.moments(float(nv * (E - nlo)));
+            }
         }
         __syncthreads();
         // Column c, chunk j: pixel lanes j, j + SW, ... in order; then the SW
@@ -207,7 +254,24 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
             if (on && j == 0) col_m[c] = m;
         }
         __syncthreads();
-        if (t < a.CBg) {  // group t over its columns, in channel order
+        if constexpr (PACKED) {
+            // Group g over its kpx * cpg columns (pixel, then channel order):
+            // w lanes per group, lane l merging columns l, l + w, ... in
+            // order, then an ordered butterfly over the w lanes.
+            const int len = a.kpx * a.cpg;
+            int w = 1;
+            while (w < 16 && 2 * w * a.CBg <= kClusterThreads && w < len) w <<= 1;
+            const int gi = t / w, li = t - gi * w;
+            Moments m{0.0f, 0.0f, 0.0f};
+            if (gi < a.CBg)
+                for (int i = li; i < len; i += w) {
+                    const int p = int(fastdiv(uint32_t(i), a.div_cpg));
+                    m = merge_rcp(m, col_m[p * a.C + gi * a.cpg + (i - p * a.cpg)]);
+                }
+            m = segment_merge(m, w);
+            if (gi < a.CBg && li == 0) dst[gi] = m;
+            __syncthreads();  // dst[g] is read by thread g (publication), not its writer
+        } else if (t < a.CBg) {  // group t over its columns, in channel order
             const int vf = (t * a.cpg) / E, vl = ((t + 1) * a.cpg - 1) / E;
             Moments m{0.0f, 0.0f, 0.0f};
             for (int w = vf; w <= vl; ++w)
@@ -237,7 +301,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
             if constexpr (!BCAST) sv[r] = load_vec<T, E>(a.skip, own_idx(r));
         }
         if constexpr (E == 1) load_constants();
-        SlotSums acc;
+        Acc acc;
 #pragma unroll
         for (int r = 0; r < R; ++r)
             if (r < nv_own) {
@@ -267,7 +331,10 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
     // lanes; the lanes beyond K hold empty moments).
     int kw = 1;
     while (kw < a.K) kw <<= 1;
-    auto slice_count = [&](int s) { return float(slice_len(s) * a.cpg); };
+    auto slice_count = [&](int s) {
+        if constexpr (PACKED) return float(slice_len(s) * a.kpx * a.cpg);
+        else return float(slice_len(s) * a.cpg);
+    };
     auto combine = [&](const Moments (&m)[kGroupsPerWave]) {
 #pragma unroll
         for (int i = 0; i < kGroupsPerWave; ++i) {
@@ -327,7 +394,7 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
         for (int s = 0; s < a.K; ++s) {
             if (!late[s]) continue;  // uniform
             const int nv = nvalid(s);
-            SlotSums acc;
+            Acc acc;
 #pragma unroll
             for (int r = 0; r < R; ++r)
                 if (r < nv) {
@@ -364,12 +431,17 @@ sgn_nhwc_cluster_kernel(NhwcClusterArgs<T, M> a) {
 
     // ---- normalize the held S
     if (nv_own > 0) {
-        const float2 slo = stat[glo];
-        const float2 shi = stat[glo + 1 < a.CBg ? glo + 1 : glo];
+        float2 slo, shi;  // the (at most two) groups of the vector (not packed)
+        if constexpr (!PACKED) {
+            slo = stat[glo];
+            shi = stat[glo + 1 < a.CBg ? glo + 1 : glo];
+        }
         float mean[E], scl[E], sft[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const float2 st = e < split ? slo : shi;
+            float2 st;
+            if constexpr (PACKED) st = stat[fastdiv(uint32_t(ch[e]), a.div_cpg)];
+            else st = e < split ? slo : shi;
             mean[e] = st.x;
             scl[e] = st.y * to_f32(gam[e]);
             sft[e] = to_f32(bet[e]);
@@ -471,6 +543,64 @@ bool nhwc_cluster_plan(int E, int64_t N, int64_t C, int64_t HW, int64_t groups, 
     return false;
 }
 
+// Packed runs carry eight times the data of element accesses per thread, so
+// a small image gets few workgroups: below one per CU the element and narrow
+// accesses measured faster (2 x 64 x 64 x 15 float16: 58 workgroups, 13.9
+// against 9.7 us; 2 x 64 x 64 x 100: 16.6 against 11.1), from there the
+// packed runs (8 x 128 x 128 x 15 float32: 16.2 against 20.6 us; 8 x 128 x
+// 128 x 60 float16: 25.5 against 28.0).
+constexpr int64_t kNhwcPackedMinBlocks = 256;
+
+// Packed-run plan for pixels whose C channels are not a whole number of
+// 16-byte vectors: units of kpx = 16 / gcd(C * size, 16) pixels, CBv =
+// kpx * C * size / 16 vectors each, read whole by one channel block that
+// holds every group; slices as in nhwc_cluster_plan.  Needs H * W a whole
+// number of units, a unit of at most 256 vectors and at most kNhwcMaxCBg
+// groups.
+bool nhwc_packed_cluster_plan(int size, int64_t N, int64_t C, int64_t HW, int64_t groups, NhwcPlan* out,
+                              int* kpx_out) {
+    int64_t x = C * size, y = 16;
+    while (y) {
+        const int64_t r = x % y;
+        x = y;
+        y = r;
+    }
+    const int64_t kpx = 16 / x;
+    if (kpx == 1 || N < 1 || HW < 1 || HW % kpx != 0 || groups > kNhwcMaxCBg) return false;
+    const int64_t E = 16 / size;
+    const int64_t cbv = kpx * C * size / 16;
+    if (cbv > kClusterThreads) return false;
+    const int64_t units = HW / kpx;
+    const int64_t P = kClusterThreads / cbv;
+    const int64_t k_fit = (units + P * kNhwcMaxR - 1) / (P * kNhwcMaxR);
+    if (k_fit > kNhwcMaxK) return false;
+    int64_t K = (kNhwcTargetBlocks + N - 1) / N;
+    const int64_t k_work = units * cbv / kClusterThreads;  // at least one vector per thread
+    if (K > k_work) K = k_work;
+    if (K > kNhwcExchangeK) K = kNhwcExchangeK;
+    if (K < k_fit) K = k_fit;
+    if (K > kNhwcMaxK) K = kNhwcMaxK;
+    if (K > units) K = units;
+    if ((units + P - 1) / P <= kSingleSliceMaxR) K = 1;  // one slice, no exchange
+    const int64_t pps = (units + K - 1) / K;
+    K = (units + pps - 1) / pps;  // no empty slices
+    if (N * K < kNhwcPackedMinBlocks) return false;
+    out->CBv = int(cbv);
+    out->NCB = 1;
+    out->CBg = int(groups);
+    out->P = int(P);
+    int sw = 16;  // chunks per column: E columns per vector
+    while (sw > 1 && (E * cbv * sw > kClusterThreads || sw / 2 >= P)) sw >>= 1;
+    int sw_log = 0;
+    while ((1 << sw_log) < sw) ++sw_log;
+    out->sw_log = sw_log;
+    out->K = int(K);
+    out->pps = pps;
+    out->R = int((pps + P - 1) / P);
+    *kpx_out = int(kpx);
+    return true;
+}
+
 // Workgroups of `kernel` (256 threads) that the current device holds at once:
 // its occupancy per CU times the CUs, queried once per device and kernel.
 int resident_workgroups(const void* kernel) {
@@ -489,20 +619,20 @@ int resident_workgroups(const void* kernel) {
     return cache[key] = per_cu * cus;
 }
 
-template <typename T, typename M, int E, int R>
+template <typename T, typename M, int E, int R, bool PACKED = false>
 const void* nhwc_kernel_r(bool bcast) {
-    return bcast ? reinterpret_cast<const void*>(&sgn_nhwc_cluster_kernel<T, M, E, R, true>)
-                 : reinterpret_cast<const void*>(&sgn_nhwc_cluster_kernel<T, M, E, R, false>);
+    return bcast ? reinterpret_cast<const void*>(&sgn_nhwc_cluster_kernel<T, M, E, R, true, PACKED>)
+                 : reinterpret_cast<const void*>(&sgn_nhwc_cluster_kernel<T, M, E, R, false, PACKED>);
 }
 
-// The kernel launch_nhwc_cluster runs for r pixels per thread.
-template <typename T, typename M, int E>
+// The kernel launch_nhwc_cluster runs for r pixels (units) per thread.
+template <typename T, typename M, int E, bool PACKED = false>
 const void* nhwc_kernel(int r, bool bcast) {
-    if (r <= 1) return nhwc_kernel_r<T, M, E, 1>(bcast);
-    if (r <= 2) return nhwc_kernel_r<T, M, E, 2>(bcast);
-    if (r <= 4) return nhwc_kernel_r<T, M, E, 4>(bcast);
-    if (r <= 8) return nhwc_kernel_r<T, M, E, 8>(bcast);
-    return nhwc_kernel_r<T, M, E, kNhwcMaxR>(bcast);
+    if (r <= 1) return nhwc_kernel_r<T, M, E, 1, PACKED>(bcast);
+    if (r <= 2) return nhwc_kernel_r<T, M, E, 2, PACKED>(bcast);
+    if (r <= 4) return nhwc_kernel_r<T, M, E, 4, PACKED>(bcast);
+    if (r <= 8) return nhwc_kernel_r<T, M, E, 8, PACKED>(bcast);
+    return nhwc_kernel_r<T, M, E, kNhwcMaxR, PACKED>(bcast);
 }
 
 template <typename T, typename M>
@@ -561,30 +691,30 @@ NhwcLayout nhwc_layout(int64_t N, const NhwcPlan& p, bool cluster_major) {
     return NhwcLayout{Kp, Kp, N * p.NCB * Kp, Kp};
 }
 
-template <typename T, typename M, int E, int R>
+template <typename T, typename M, int E, int R, bool PACKED>
 hipError_t launch_nhwc_cluster_r(const NhwcClusterArgs<T, M>& ca, int64_t blocks, hipStream_t stream) {
     if (ca.skip_bcast)
-        hipLaunchKernelGGL((sgn_nhwc_cluster_kernel<T, M, E, R, true>), dim3(unsigned(blocks)),
+        hipLaunchKernelGGL((sgn_nhwc_cluster_kernel<T, M, E, R, true, PACKED>), dim3(unsigned(blocks)),
                            dim3(kClusterThreads), 0, stream, ca);
     else
-        hipLaunchKernelGGL((sgn_nhwc_cluster_kernel<T, M, E, R, false>), dim3(unsigned(blocks)),
+        hipLaunchKernelGGL((sgn_nhwc_cluster_kernel<T, M, E, R, false, PACKED>), dim3(unsigned(blocks)),
                            dim3(kClusterThreads), 0, stream, ca);
     return hipGetLastError();
 }
 
-template <typename T, typename M, int E>
+template <typename T, typename M, int E, bool PACKED = false>
 hipError_t launch_nhwc_cluster(const NhwcClusterArgs<T, M>& ca, int r, int64_t blocks,
                                hipStream_t stream) {
-    if (r <= 1) return launch_nhwc_cluster_r<T, M, E, 1>(ca, blocks, stream);
-    if (r <= 2) return launch_nhwc_cluster_r<T, M, E, 2>(ca, blocks, stream);
-    if (r <= 4) return launch_nhwc_cluster_r<T, M, E, 4>(ca, blocks, stream);
-    if (r <= 8) return launch_nhwc_cluster_r<T, M, E, 8>(ca, blocks, stream);
-    return launch_nhwc_cluster_r<T, M, E, kNhwcMaxR>(ca, blocks, stream);
+    if (r <= 1) return launch_nhwc_cluster_r<T, M, E, 1, PACKED>(ca, blocks, stream);
+    if (r <= 2) return launch_nhwc_cluster_r<T, M, E, 2, PACKED>(ca, blocks, stream);
+    if (r <= 4) return launch_nhwc_cluster_r<T, M, E, 4, PACKED>(ca, blocks, stream);
+    if (r <= 8) return launch_nhwc_cluster_r<T, M, E, 8, PACKED>(ca, blocks, stream);
+    return launch_nhwc_cluster_r<T, M, E, kNhwcMaxR, PACKED>(ca, blocks, stream);
 }
 
 template <typename T, typename M>
 hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, const NhwcLayout& lay, int E,
-                             void* part, hipStream_t stream) {
+                             int kpx, void* part, hipStream_t stream) {
     NhwcClusterArgs<T, M> ca;
     ca.X = static_cast<const T*>(a.X);
     ca.skip = static_cast<const T*>(a.skip);
@@ -599,9 +729,11 @@ hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, const NhwcL
             return e;
     ca.tags = publication_tags(a.tag);
     ca.timeout_ticks = a.exchange_timeout_ticks;
-    ca.HW = a.H * a.W;
+    ca.HW = a.H * a.W / kpx;  // units
     ca.pps = plan.pps;
-    ca.Cv = int(a.C / E);
+    ca.Cv = int(a.C * kpx / E);
+    ca.C = int(a.C);
+    ca.kpx = kpx;
     ca.cpg = int(a.C / a.groups);
     ca.CBv = plan.CBv;
     ca.NCB = plan.NCB;
@@ -624,6 +756,8 @@ hipError_t launch_nhwc_typed(const SgnArgs& a, const NhwcPlan& plan, const NhwcL
     ca.trace = a.trace;
     const int64_t blocks = lay.grid;
     constexpr int EV = VecWidth<T>::value;
+    if (kpx > 1) return E == EV ? launch_nhwc_cluster<T, M, EV, true>(ca, plan.R, blocks, stream)
+                                : hipErrorInvalidValue;
     if (E == EV) return launch_nhwc_cluster<T, M, EV>(ca, plan.R, blocks, stream);
     if (E == EV / 2) return launch_nhwc_cluster<T, M, EV / 2>(ca, plan.R, blocks, stream);
     if constexpr (EV >= 8)
@@ -640,6 +774,38 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
         return false;
     const int size = a.dtype == 0 ? 4 : 2;
     const int64_t HW = a.H * a.W;
+    // Pixels that are not a whole number of 16-byte vectors: packed runs of
+    // pixels that are, read with 16-byte accesses (the data tensors 16-byte
+    // aligned; bias and a broadcast skip are read per element).
+    {
+        NhwcPlan plan;
+        int kpx = 1;
+        const bool aligned = aligned16(a.X) && aligned16(a.Y) && (!a.S || aligned16(a.S)) &&
+                             (a.skip_broadcast || aligned16(a.skip));
+        if (aligned && nhwc_packed_cluster_plan(size, a.N, a.C, HW, a.groups, &plan, &kpx)) {
+            const void* kernel = a.dtype == 0
+                ? (a.param_dtype == 0 ? nhwc_kernel<float, float, 4, true>(plan.R, a.skip_broadcast)
+                                      : nhwc_kernel<float, half_t, 4, true>(plan.R, a.skip_broadcast))
+                : (a.param_dtype == 0 ? nhwc_kernel<half_t, float, 8, true>(plan.R, a.skip_broadcast)
+                                      : nhwc_kernel<half_t, half_t, 8, true>(plan.R, a.skip_broadcast));
+            const int64_t resident = resident_workgroups(kernel);
+            if (kernel && resident >= 64) {
+                NhwcLayout lay = nhwc_layout(a.N, plan, false);
+                if (plan.K > 1 && (lay.grid <= resident || lay.span > resident)) lay = nhwc_layout(a.N, plan, true);
+                *route = lay.Kp > 1 || plan.K == 1 ? "sgn.cluster.nhwc.packed.vec16"
+                                                   : "sgn.cluster.nhwc.smajor.packed.vec16";
+                const int E = 16 / size;
+                if (a.dtype == 0) {
+                    if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, lay, E, kpx, part, stream);
+                    else *err = launch_nhwc_typed<float, half_t>(a, plan, lay, E, kpx, part, stream);
+                } else {
+                    if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, plan, lay, E, kpx, part, stream);
+                    else *err = launch_nhwc_typed<half_t, half_t>(a, plan, lay, E, kpx, part, stream);
+                }
+                return true;
+            }
+        }
+    }
     // The widest access that divides a pixel's channels and every base (the
     // broadcast skip's rows are C elements apart, like the pixels) and is
     // no wider than a group: groups narrower than a 16-byte vector take
@@ -689,11 +855,11 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
     // Named by layout only where slices exchange (K > 1).
     *route = kNames[lay.Kp > 1 || plan.K == 1 ? 1 : 0][E == 1 ? 0 : E * size == 16 ? 3 : E * size == 8 ? 2 : 1];
     if (a.dtype == 0) {
-        if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, lay, E, part, stream);
-        else *err = launch_nhwc_typed<float, half_t>(a, plan, lay, E, part, stream);
+        if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, lay, E, 1, part, stream);
+        else *err = launch_nhwc_typed<float, half_t>(a, plan, lay, E, 1, part, stream);
     } else {
-        if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, plan, lay, E, part, stream);
-        else *err = launch_nhwc_typed<half_t, half_t>(a, plan, lay, E, part, stream);
+        if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, plan, lay, E, 1, part, stream);
+        else *err = launch_nhwc_typed<half_t, half_t>(a, plan, lay, E, 1, part, stream);
     }
     return true;
 }

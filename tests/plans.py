@@ -49,3 +49,29 @@ def nhwc_cluster_fits(C, groups, E, HW):
         if -(-HW // (P * 16)) <= 64:
             return True
     return False
+
+
+def nhwc_packed_cluster_fits(N, C, groups, size, HW):
+    """Whether the NHWC cluster takes packed runs for aligned tensors: pixels
+    of C channels that are not a whole number of 16-byte vectors, runs of
+    kpx = 16 / gcd(C * size, 16) pixels (H*W a whole number of them) of at
+    most 256 vectors, at most 16 groups, an image of at most 64 slices of at
+    most 16 runs per thread, and at least 256 workgroups (N * slices; the
+    slices as the library plans them)."""
+    kpx = 16 // math.gcd(C * size, 16)
+    if kpx == 1 or HW % kpx or groups > 16:
+        return False
+    cbv = kpx * C * size // 16
+    if cbv > 256:
+        return False
+    units, P = HW // kpx, 256 // cbv
+    k_fit = -(-units // (P * 16))
+    if k_fit > 64:
+        return False
+    K = min(-(-512 // N), units * cbv // 256, 32)
+    K = min(max(K, k_fit), 64, units)
+    if -(-units // P) <= 6:
+        K = 1
+    pps = -(-units // K)
+    K = -(-units // pps)
+    return N * K >= 256

@@ -8,7 +8,7 @@ import torch
 import group_normalization_amd as gn
 import oracle
 import workloads
-from plans import nhwc_cluster_fits, packed_applies, packed_blocks
+from plans import nhwc_cluster_fits, nhwc_packed_cluster_fits, packed_applies, packed_blocks
 from parity import assert_bitwise, assert_close, desc, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -91,12 +91,16 @@ def split_channel_blocks(C, cpg, e):
 
 def nhwc_route(C, groups, T, HW, N=1):
     """The NHWC route the library picks for aligned tensors of these
-    channels: the channel-block cluster with the widest of 16-, 8- and
+    channels: the cluster over packed runs of pixels where a pixel is not a
+    whole number of 16-byte vectors and the runs fit; else the channel-block
+    cluster with the widest of 16-, 8- and
     4-byte accesses that divides a pixel and is no wider than a group;
     otherwise the split route with the widest access, or over runs of
     pixels that make whole 16-byte vectors (at most 256 of them, H*W a
     whole number of runs), or scalars."""
     size = np.dtype(T).itemsize
+    if nhwc_packed_cluster_fits(N, C, groups, size, HW):
+        return "sgn.cluster.nhwc.packed.vec16"
     width = next((b for b in (16, 8, 4) if b > size and C * size % b == 0), size)
     names = {16: "vec16", 8: "vec8", 4: "vec4"}
     w = width
@@ -232,6 +236,15 @@ NHWC_LIMIT_CASES = [
     (1, 15, 340, 256, F16, 5, False, "sgn.cluster.nhwc.scalar"),
     (1, 15, 341, 256, F16, 5, True, "sgn.split.nhwc.packed.vec16"),
     (2, 15, 64, 64, F32, 5, True, "sgn.cluster.nhwc.scalar"),     # float32 odd C, broadcast skip
+    # Packed runs of pixels (whole 16-byte vectors) where their grid has at
+    # least 256 workgroups; below that, element or narrow accesses.
+    (8, 15, 128, 128, F16, 5, False, "sgn.cluster.nhwc.packed.vec16"),  # runs of 8 pixels, 15 vectors
+    (8, 15, 64, 128, F32, 5, True, "sgn.cluster.nhwc.packed.vec16"),    # float32 runs of 4, broadcast skip
+    (16, 3, 128, 128, F16, 1, False, "sgn.cluster.nhwc.packed.vec16"),  # 3-vector runs, one group
+    (8, 60, 64, 64, F16, 15, False, "sgn.cluster.nhwc.packed.vec16"),   # 15 groups of 4 channels
+    (8, 36, 128, 128, F16, 12, False, "sgn.cluster.nhwc.packed.vec16"), # groups of 3 channels
+    (8, 15, 256, 256, F16, 5, False, "sgn.cluster.nhwc.packed.vec16"),  # 16 runs per thread
+    (4, 12, 128, 128, F16, 3, True, "sgn.cluster.nhwc.vec8"),           # 128 workgroups: 8-byte accesses
     (2, 1, 17, 19, F16, 1, False, "sgn.cluster.nhwc.scalar"),     # one channel
     (2, 2, 5, 7, F16, 2, True, "sgn.cluster.nhwc.scalar"),        # two one-channel groups
     (3, 3, 1, 1, F32, 3, False, "sgn.cluster.nhwc.scalar"),       # one pixel: every group one value
@@ -308,6 +321,7 @@ FALLBACK_CASES = [
     (2, 72, 16, 16, F16, F16, 1, True, False, 8, 0),    # NHWC, 2 groups per wave, 9 slices
     (1, 48, 33, 31, F32, F32, 1, False, True, 4, 1),    # NHWC float32, 32 slices, ragged last
     (2, 15, 24, 24, F16, F32, 1, False, True, 5, 1),    # NHWC odd C: element accesses, 11 slices
+    (8, 15, 64, 128, F16, F32, 1, False, True, 5, 1),   # NHWC odd C: packed runs, 32 slices
     (1, 32, 20, 20, F32, F16, 1, True, False, 32, 0),   # NHWC instance norm: element accesses
 ]
 
