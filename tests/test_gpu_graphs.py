@@ -47,6 +47,10 @@ def make_inputs():
         "Xg": rn(24, 2049), "gg": rn(24, 2049), "sg": rn(2049),
         "Xn": rn(2, 16, 16, 15), "kn": rn(2, 16, 16, 15), "gn": rn(15, dtype=torch.float32),
         "en": rn(15, dtype=torch.float32),
+        # Larger NHWC images of 15 channels: the cluster over packed runs of
+        # 8 pixels (16-byte accesses), 32 slices exchanging moments.
+        "Xr": rn(8, 64, 128, 15), "kr": rn(8, 64, 128, 15), "gr": rn(15, dtype=torch.float32),
+        "er": rn(15, dtype=torch.float32),
     }
     t["ws_h"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xh"], 32, 1), dtype=torch.uint8,
                             device="cuda")
@@ -55,6 +59,8 @@ def make_inputs():
     t["ws_p"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xp"], 32, 0), dtype=torch.uint8,
                             device="cuda")
     t["ws_n"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xn"], 5, 1), dtype=torch.uint8,
+                            device="cuda")
+    t["ws_r"] = torch.empty(gn.skip_group_norm_workspace_size(t["Xr"], 5, 1), dtype=torch.uint8,
                             device="cuda")
     return t
 
@@ -86,16 +92,19 @@ def run(t):
     pk = gn.skip_group_norm(t["Xn"], t["gn"], t["en"], t["kn"], None, groups=5, activation=1,
                             channels_last=1, want_sum=True, workspace=t["ws_n"])
     route_n = gn.last_route()
+    pr = gn.skip_group_norm(t["Xr"], t["gr"], t["er"], t["kr"], None, groups=5, activation=1,
+                            channels_last=1, want_sum=True, workspace=t["ws_r"])
+    route_r = gn.last_route()
     outs = [a.output, a.inv_std_var, a.input_skip_bias_sum, b.output, b.mean, b.inv_std_var, c,
             d.Y, d.S, e.Y, f.Y, f.S, o.output, o.input_skip_bias_sum, fl, q.output, q.inv_std_var,
-            q.input_skip_bias_sum, wd.output, wd.input_skip_bias_sum, gp, pk.Y, pk.S]
-    return outs, (route_h, route_c, route_p, route_o, route_f, route_q, route_w, route_g, route_n)
+            q.input_skip_bias_sum, wd.output, wd.input_skip_bias_sum, gp, pk.Y, pk.S, pr.Y, pr.S]
+    return outs, (route_h, route_c, route_p, route_o, route_f, route_q, route_w, route_g, route_n, route_r)
 
 
 def refill(t, seed):
     g = torch.Generator(device="cuda").manual_seed(seed)
     for name in ("x", "k", "X", "gate", "xo", "ko", "Xf", "gf", "xq", "kq", "Xh", "kh", "Xc", "kc", "Xp", "kp",
-                 "xw", "kw", "Xg", "gg", "Xn", "kn"):
+                 "xw", "kw", "Xg", "gg", "Xn", "kn", "Xr", "kr"):
         v = t[name]
         v.copy_(torch.randn(v.shape, generator=g, device="cuda", dtype=torch.float32).to(v.dtype))
 
@@ -114,13 +123,14 @@ def test_graph_replays_match_eager():
         captured, routes = run(t)
     assert routes == ("sgn.cluster.nhwc.vec16", "sgn.cluster.nchw.vec16", "sgn.cluster.nchw.phase",
                       "ssln.phase.vec16", "gated.flat.vec16", "ssln.flat.vec16", "ssln.wide.vec16",
-                      "gated.phase.vec16", "sgn.cluster.nhwc.scalar"), routes
+                      "gated.phase.vec16", "sgn.cluster.nhwc.scalar", "sgn.cluster.nhwc.packed.vec16"), routes
     torch.cuda.synchronize()
 
     names = ["ssln output", "ssln inv_std_var", "ssln S", "sln output", "sln mean", "sln inv_std_var",
              "gated Y", "sgn nhwc Y", "sgn nhwc S", "sgn nchw Y", "sgn nchw phased Y", "sgn nchw phased S",
              "ssln phased output", "ssln phased S", "gated flat Y", "ssln flat output", "ssln flat inv_std_var",
-             "ssln flat S", "ssln wide output", "ssln wide S", "gated phased Y", "sgn odd-C Y", "sgn odd-C S"]
+             "ssln flat S", "ssln wide output", "ssln wide S", "gated phased Y", "sgn odd-C Y", "sgn odd-C S",
+             "sgn packed Y", "sgn packed S"]
     for rep in range(4):
         refill(t, seed=100 + rep)
         graph.replay()
