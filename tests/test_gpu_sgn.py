@@ -62,6 +62,10 @@ CASES = [
     (1, 257, 4, 4, F16, F32, 1, False, True, 1, 0),       # 8 pixels = 257 vectors: scalars
     (2, 15, 5, 5, F16, F32, 1, False, True, 5, 1),        # 25 pixels, not whole runs of 8: scalars
     (1, 15, 512, 512, F16, F32, 1, False, True, 5, 1),    # 5 x 964 partials: a finalize launch
+    # Packed runs in the cluster (256 workgroups): float16 parameters and a
+    # broadcast skip; float32 data without bias.
+    (8, 15, 64, 128, F16, F16, 1, True, True, 5, 0),
+    (8, 15, 64, 64, F32, F16, 1, False, False, 5, 1),
 ]
 
 
