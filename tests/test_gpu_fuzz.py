@@ -175,3 +175,51 @@ def test_skip_group_norm_large(case):
     assert_close(to_host(out.Y), ref_y, f"Y ({what})")
     if want_sum:
         assert_bitwise(to_host(out.S), ref_s, f"S ({what})")
+
+
+BATCHED_NHWC_CASES = 24
+
+
+@pytest.mark.parametrize("case", range(BATCHED_NHWC_CASES))
+def test_skip_group_norm_batched_nhwc(case):
+    """Batches of 6-16 NHWC images whose pixels are not a whole number of
+    16-byte vectors (C times the element size not a multiple of 16), widths
+    mostly a multiple of 8: grids large enough for the cluster over packed
+    runs of pixels, beside element and narrow accesses and the split route
+    where the plan sends them."""
+    rng = np.random.default_rng(7000 + case)
+    T = F16 if rng.random() < 0.6 else F32
+    size = np.dtype(T).itemsize
+    M = F16 if rng.random() < 0.5 else F32
+    groups = int(rng.choice([1, 3, 5, 7, 12, 15]))
+    cpg = int(rng.integers(1, 9))
+    for _ in range(4):
+        if groups * cpg * size % 16:
+            break
+        cpg += 1
+    C = groups * cpg
+    N = int(rng.integers(6, 17))
+    H = int(rng.integers(24, 97))
+    W = 8 * int(rng.integers(3, 13)) if rng.random() < 0.8 else int(rng.integers(24, 97))
+    while N * C * H * W > 2 * MAX_ELEMS:
+        H = max(1, H // 2)
+    shape = (N, H, W, C)
+    X = normal(rng, shape, T)
+    bcast = bool(rng.random() < 0.3)
+    skip = normal(rng, (N, C), T) if bcast else normal(rng, shape, T)
+    gamma, beta = uniform(rng, C, M), normal(rng, C, M, 0.1)
+    bias = normal(rng, C, T, 0.1) if rng.random() < 0.5 else None
+    act = int(rng.random() < 0.5)
+    want_sum = bool(rng.random() < 0.6)
+    ref_y, ref_s = oracle.skip_group_norm(X, gamma, beta, skip, bias, groups=groups, activation=act,
+                                          epsilon=1e-5, channels_last=1, want_sum=True)
+    out = gn.skip_group_norm(dev(X), dev(gamma), dev(beta), dev(skip), dev(bias), groups=groups,
+                             activation=act, epsilon=1e-5, channels_last=1, want_sum=want_sum)
+    route = gn.last_route()
+    torch.cuda.synchronize()
+    print(f"case {case}: {route}")
+    what = (f"{route} {T.__name__}/{M.__name__} nhwc {shape} g={groups} bcast={bcast} "
+            f"bias={bias is not None} act={act}")
+    assert_close(to_host(out.Y), ref_y, f"Y ({what})")
+    if want_sum:
+        assert_bitwise(to_host(out.S), ref_s, f"S ({what})")
