@@ -248,6 +248,10 @@ NHWC_LIMIT_CASES = [
     (8, 60, 64, 64, F16, 15, False, "sgn.cluster.nhwc.packed.vec16"),   # 15 groups of 4 channels
     (8, 36, 128, 128, F16, 12, False, "sgn.cluster.nhwc.packed.vec16"), # groups of 3 channels
     (8, 15, 256, 256, F16, 5, False, "sgn.cluster.nhwc.packed.vec16"),  # 16 runs per thread
+    # 16 images of 40 slices: 640 workgroups of 16 runs per thread, more than
+    # are resident at once (two a CU), each cluster's 40 ids within reach:
+    # slice-major.
+    (16, 15, 340, 256, F16, 5, False, "sgn.cluster.nhwc.smajor.packed.vec16"),
     (4, 12, 128, 128, F16, 3, True, "sgn.cluster.nhwc.vec8"),           # 128 workgroups: 8-byte accesses
     (2, 1, 17, 19, F16, 1, False, "sgn.cluster.nhwc.scalar"),     # one channel
     (2, 2, 5, 7, F16, 2, True, "sgn.cluster.nhwc.scalar"),        # two one-channel groups
