@@ -56,6 +56,7 @@ CASES = [
     (1, 64, 7, 9, np.float16, np.float32, 0, False, True, 8, 1, True),        # odd plane: phased
     (2, 15, 16, 16, np.float16, np.float32, 1, False, True, 5, 1, True),     # odd C: element accesses (split: packed runs)
     (1, 15, 512, 512, np.float16, np.float32, 1, False, True, 5, 1, True),   # packed runs, finalize launch
+    (8, 15, 64, 128, np.float16, np.float32, 1, False, True, 5, 1, True),    # the cluster over packed runs
 ]
 
 
