@@ -543,13 +543,26 @@ bool nhwc_cluster_plan(int E, int64_t N, int64_t C, int64_t HW, int64_t groups, 
     return false;
 }
 
-// Packed runs carry eight times the data of element accesses per thread, so
-// a small image gets few workgroups: below one per CU the element and narrow
-// accesses measured faster (2 x 64 x 64 x 15 float16: 58 workgroups, 13.9
-// against 9.7 us; 2 x 64 x 64 x 100: 16.6 against 11.1), from there the
-// packed runs (8 x 128 x 128 x 15 float32: 16.2 against 20.6 us; 8 x 128 x
-// 128 x 60 float16: 25.5 against 28.0).
+// When the packed runs are taken over the channel-block form (element or
+// narrow accesses), measured on 19 images: a run carries eight times the data
+// of an element access, so a small image gets few workgroups, and each thread
+// merges per element.  Packed runs won with at least one workgroup per CU
+// (8 x 128 x 128 x 15 float32: 15.5 against 20.5 us; 16 x 256 x 256 x 3
+// float16: 16.0 against 17.9), with at least 12 runs per thread on at least
+// 96 workgroups (4 x 256 x 256 x 15 float32: 20.3 against 32.2 us; 6 x 200
+// x 256 x 15 float16: 20.2 against 23.6), and wherever the channel-block
+// form has no plan (the split route instead: 2 x 512 x 512 x 3 float16: 17.0
+// against 19.7 us); they lost with few runs per thread (4 x 128 x 128 x 15:
+// +10 %) or few workgroups (2 x 256 x 256 x 15, 64 workgroups: +14 %;
+// 1 x 340 x 256 x 15, 40: +39 %).
 constexpr int64_t kNhwcPackedMinBlocks = 256;
+constexpr int64_t kNhwcPackedDeepBlocks = 96;  // with at least kNhwcPackedDeepR runs per thread
+constexpr int kNhwcPackedDeepR = 12;
+bool nhwc_packed_preferred(int64_t N, const NhwcPlan& packed, bool block_fits) {
+    const int64_t grid = N * packed.K;
+    return !block_fits || grid >= kNhwcPackedMinBlocks ||
+           (packed.R >= kNhwcPackedDeepR && grid >= kNhwcPackedDeepBlocks);
+}
 
 // Packed-run plan for pixels whose C channels are not a whole number of
 // 16-byte vectors: units of kpx = 16 / gcd(C * size, 16) pixels, CBv =
@@ -584,7 +597,6 @@ bool nhwc_packed_cluster_plan(int size, int64_t N, int64_t C, int64_t HW, int64_
     if ((units + P - 1) / P <= kSingleSliceMaxR) K = 1;  // one slice, no exchange
     const int64_t pps = (units + K - 1) / K;
     K = (units + pps - 1) / pps;  // no empty slices
-    if (N * K < kNhwcPackedMinBlocks) return false;
     out->CBv = int(cbv);
     out->NCB = 1;
     out->CBg = int(groups);
@@ -774,15 +786,30 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
         return false;
     const int size = a.dtype == 0 ? 4 : 2;
     const int64_t HW = a.H * a.W;
+    // The widest access that divides a pixel's channels and every base (the
+    // broadcast skip's rows are C elements apart, like the pixels) and is
+    // no wider than a group: groups narrower than a 16-byte vector take
+    // 8- or 4-byte vectors here rather than three launches, and odd channel
+    // counts or one-channel groups single elements, consecutive threads
+    // still reading consecutive bytes of a pixel (f16 8 x 128 x 128 x 15:
+    // 0.97 against 0.72 TB/s on the split route over packed runs of pixels;
+    // 2 x 64 x 64 x 15: 104 against 55 GB/s).
+    int E = a.dtype == 0 ? widest_vector<float>(a.C, {a.X, a.Y, a.S, a.skip, a.bias})
+                         : widest_vector<half_t>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
+    while (E > 1 && a.C / a.groups < E) E /= 2;
+    NhwcPlan plan;
+    const bool block_fits = nhwc_cluster_plan(E, a.N, a.C, HW, a.groups, &plan);
     // Pixels that are not a whole number of 16-byte vectors: packed runs of
     // pixels that are, read with 16-byte accesses (the data tensors 16-byte
     // aligned; bias and a broadcast skip are read per element).
     {
-        NhwcPlan plan;
+        NhwcPlan pplan;
         int kpx = 1;
         const bool aligned = aligned16(a.X) && aligned16(a.Y) && (!a.S || aligned16(a.S)) &&
                              (a.skip_broadcast || aligned16(a.skip));
-        if (aligned && nhwc_packed_cluster_plan(size, a.N, a.C, HW, a.groups, &plan, &kpx)) {
+        if (aligned && nhwc_packed_cluster_plan(size, a.N, a.C, HW, a.groups, &pplan, &kpx) &&
+            nhwc_packed_preferred(a.N, pplan, block_fits)) {
+            const NhwcPlan& plan = pplan;
             const void* kernel = a.dtype == 0
                 ? (a.param_dtype == 0 ? nhwc_kernel<float, float, 4, true>(plan.R, a.skip_broadcast)
                                       : nhwc_kernel<float, half_t, 4, true>(plan.R, a.skip_broadcast))
@@ -806,19 +833,7 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
             }
         }
     }
-    // The widest access that divides a pixel's channels and every base (the
-    // broadcast skip's rows are C elements apart, like the pixels) and is
-    // no wider than a group: groups narrower than a 16-byte vector take
-    // 8- or 4-byte vectors here rather than three launches, and odd channel
-    // counts or one-channel groups single elements, consecutive threads
-    // still reading consecutive bytes of a pixel (f16 8 x 128 x 128 x 15:
-    // 0.97 against 0.72 TB/s on the split route over packed runs of pixels;
-    // 2 x 64 x 64 x 15: 104 against 55 GB/s).
-    int E = a.dtype == 0 ? widest_vector<float>(a.C, {a.X, a.Y, a.S, a.skip, a.bias})
-                         : widest_vector<half_t>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
-    while (E > 1 && a.C / a.groups < E) E /= 2;
-    NhwcPlan plan;
-    if (!nhwc_cluster_plan(E, a.N, a.C, HW, a.groups, &plan)) return false;
+    if (!block_fits) return false;
     const void* kernel = a.dtype == 0
         ? (a.param_dtype == 0 ? nhwc_kernel_for<float, float>(E, plan.R, a.skip_broadcast)
                               : nhwc_kernel_for<float, half_t>(E, plan.R, a.skip_broadcast))

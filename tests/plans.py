@@ -51,13 +51,15 @@ def nhwc_cluster_fits(C, groups, E, HW):
     return False
 
 
-def nhwc_packed_cluster_fits(N, C, groups, size, HW):
+def nhwc_packed_cluster_fits(N, C, groups, size, HW, block_fits):
     """Whether the NHWC cluster takes packed runs for aligned tensors: pixels
     of C channels that are not a whole number of 16-byte vectors, runs of
     kpx = 16 / gcd(C * size, 16) pixels (H*W a whole number of them) of at
     most 256 vectors, at most 16 groups, an image of at most 64 slices of at
-    most 16 runs per thread, and at least 256 workgroups (N * slices; the
-    slices as the library plans them)."""
+    most 16 runs per thread (slices as the library plans them); and then
+    preferred when the channel-block form has no plan (block_fits false), or
+    the grid (N * slices) has at least 256 workgroups, or at least 96 with at
+    least 12 runs per thread."""
     kpx = 16 // math.gcd(C * size, 16)
     if kpx == 1 or HW % kpx or groups > 16:
         return False
@@ -74,4 +76,6 @@ def nhwc_packed_cluster_fits(N, C, groups, size, HW):
         K = 1
     pps = -(-units // K)
     K = -(-units // pps)
-    return N * K >= 256
+    R = -(-pps // P)
+    grid = N * K
+    return not block_fits or grid >= 256 or (R >= 12 and grid >= 96)

@@ -103,14 +103,15 @@ def nhwc_route(C, groups, T, HW, N=1):
     pixels that make whole 16-byte vectors (at most 256 of them, H*W a
     whole number of runs), or scalars."""
     size = np.dtype(T).itemsize
-    if nhwc_packed_cluster_fits(N, C, groups, size, HW):
-        return "sgn.cluster.nhwc.packed.vec16"
     width = next((b for b in (16, 8, 4) if b > size and C * size % b == 0), size)
     names = {16: "vec16", 8: "vec8", 4: "vec4"}
     w = width
     while w > size and C // groups < w // size:
         w //= 2
-    if nhwc_cluster_fits(C, groups, w // size, HW):
+    block = nhwc_cluster_fits(C, groups, w // size, HW)
+    if nhwc_packed_cluster_fits(N, C, groups, size, HW, block):
+        return "sgn.cluster.nhwc.packed.vec16"
+    if block:
         return f"sgn.cluster.nhwc.{names[w]}" if w > size else "sgn.cluster.nhwc.scalar"
     if width > size and split_channel_blocks(C, C // groups, width // size):
         return f"sgn.split.nhwc.{names[width]}"
@@ -235,13 +236,18 @@ NHWC_LIMIT_CASES = [
     (2, 2560, 8, 8, F32, 32, False, "sgn.cluster.nhwc.vec16"),    # 640 vectors per pixel, 3 pixel lanes
     (600, 16, 2, 2, F32, 2, True, "sgn.cluster.nhwc.vec16"),      # one slice per image: no exchange
     # Element accesses: odd C (five blocks of one 3-channel group, 85 pixel
-    # lanes) up to 64 slices of 16 pixels per thread, then packed runs
-    # (split, 5 x 321 partials: a finalize launch).
+    # lanes) up to 64 slices of 16 pixels per thread; beyond, the cluster over
+    # packed runs of 8 pixels (17 run lanes) up to 64 slices of 16 runs per
+    # thread, then the split route over the same runs (5 x 513 partials: a
+    # finalize launch).
     (1, 15, 340, 256, F16, 5, False, "sgn.cluster.nhwc.scalar"),
-    (1, 15, 341, 256, F16, 5, True, "sgn.split.nhwc.packed.vec16"),
+    (1, 15, 341, 256, F16, 5, True, "sgn.cluster.nhwc.packed.vec16"),
+    (1, 15, 544, 256, F16, 5, False, "sgn.cluster.nhwc.packed.vec16"),
+    (1, 15, 545, 256, F16, 5, True, "sgn.split.nhwc.packed.vec16"),
     (2, 15, 64, 64, F32, 5, True, "sgn.cluster.nhwc.scalar"),     # float32 odd C, broadcast skip
     # Packed runs of pixels (whole 16-byte vectors) where their grid has at
-    # least 256 workgroups; below that, element or narrow accesses.
+    # least 256 workgroups, or 96 with 12 runs per thread; else element or
+    # narrow accesses.
     (8, 15, 128, 128, F16, 5, False, "sgn.cluster.nhwc.packed.vec16"),  # runs of 8 pixels, 15 vectors
     (8, 15, 64, 128, F32, 5, True, "sgn.cluster.nhwc.packed.vec16"),    # float32 runs of 4, broadcast skip
     (16, 3, 128, 128, F16, 1, False, "sgn.cluster.nhwc.packed.vec16"),  # 3-vector runs, one group
@@ -253,6 +259,8 @@ NHWC_LIMIT_CASES = [
     # slice-major.
     (16, 15, 340, 256, F16, 5, False, "sgn.cluster.nhwc.smajor.packed.vec16"),
     (4, 12, 128, 128, F16, 3, True, "sgn.cluster.nhwc.vec8"),           # 128 workgroups: 8-byte accesses
+    (4, 15, 256, 256, F16, 5, False, "sgn.cluster.nhwc.packed.vec16"),  # 128 workgroups of 16 runs per thread
+    (2, 15, 256, 256, F16, 5, False, "sgn.cluster.nhwc.scalar"),        # 64 of 16: element accesses
     (2, 1, 17, 19, F16, 1, False, "sgn.cluster.nhwc.scalar"),     # one channel
     (2, 2, 5, 7, F16, 2, True, "sgn.cluster.nhwc.scalar"),        # two one-channel groups
     (3, 3, 1, 1, F32, 3, False, "sgn.cluster.nhwc.scalar"),       # one pixel: every group one value
