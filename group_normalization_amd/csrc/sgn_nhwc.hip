@@ -664,7 +664,8 @@ const void* nhwc_kernel_for(int E, int r, bool bcast) {
 // range fits in the workgroups the device holds at once, the lowest
 // unfinished cluster can always become wholly resident and the launch never
 // waits on a workgroup that cannot start; beyond that, waits run into their
-// bound and slices are recomputed (correct, but far slower).
+// bound and slices are recomputed (correct, but far slower: one 512 x 512 x
+// 256 float16 image took 2.5 ms that way).
 // Block-id layout: id = (v / m * NCB + cb) * G + (v % m) * Kp + j with
 // m = G / Kp, for items v with Kp ids each.
 //   slice-major (Kp = 1, G = 8): the items are the N * K (image, slice)
@@ -677,12 +678,7 @@ const void* nhwc_kernel_for(int E, int r, bool bcast) {
 //     images, and a cluster's slices j = q take Kp consecutive ids.  A
 //     cluster spans Kp ids.
 // In both, slice q of image n sits at the same residue mod 8 in every
-// channel block.  Ids with q >= K or n >= N are padding.  The dispatcher starts workgroups in id order, so when a
-// cluster's span fits in the workgroups the device holds at once, the
-// lowest unfinished cluster can always become wholly resident and no
-// workgroup waits on one that cannot start; beyond that, waits would run
-// into their bound and recompute (correct, but far slower: one 512 x 512 x
-// 256 float16 image took 2.5 ms that way).
+// channel block.  Ids with q >= K or n >= N are padding.
 struct NhwcLayout {
     int Kp, G;
     int64_t grid, span;
@@ -803,31 +799,30 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
     // pixels that are, read with 16-byte accesses (the data tensors 16-byte
     // aligned; bias and a broadcast skip are read per element).
     {
-        NhwcPlan pplan;
+        NhwcPlan pp;
         int kpx = 1;
         const bool aligned = aligned16(a.X) && aligned16(a.Y) && (!a.S || aligned16(a.S)) &&
                              (a.skip_broadcast || aligned16(a.skip));
-        if (aligned && nhwc_packed_cluster_plan(size, a.N, a.C, HW, a.groups, &pplan, &kpx) &&
-            nhwc_packed_preferred(a.N, pplan, block_fits)) {
-            const NhwcPlan& plan = pplan;
+        if (aligned && nhwc_packed_cluster_plan(size, a.N, a.C, HW, a.groups, &pp, &kpx) &&
+            nhwc_packed_preferred(a.N, pp, block_fits)) {
             const void* kernel = a.dtype == 0
-                ? (a.param_dtype == 0 ? nhwc_kernel<float, float, 4, true>(plan.R, a.skip_broadcast)
-                                      : nhwc_kernel<float, half_t, 4, true>(plan.R, a.skip_broadcast))
-                : (a.param_dtype == 0 ? nhwc_kernel<half_t, float, 8, true>(plan.R, a.skip_broadcast)
-                                      : nhwc_kernel<half_t, half_t, 8, true>(plan.R, a.skip_broadcast));
+                ? (a.param_dtype == 0 ? nhwc_kernel<float, float, 4, true>(pp.R, a.skip_broadcast)
+                                      : nhwc_kernel<float, half_t, 4, true>(pp.R, a.skip_broadcast))
+                : (a.param_dtype == 0 ? nhwc_kernel<half_t, float, 8, true>(pp.R, a.skip_broadcast)
+                                      : nhwc_kernel<half_t, half_t, 8, true>(pp.R, a.skip_broadcast));
             const int64_t resident = resident_workgroups(kernel);
             if (kernel && resident >= 64) {
-                NhwcLayout lay = nhwc_layout(a.N, plan, false);
-                if (plan.K > 1 && (lay.grid <= resident || lay.span > resident)) lay = nhwc_layout(a.N, plan, true);
-                *route = lay.Kp > 1 || plan.K == 1 ? "sgn.cluster.nhwc.packed.vec16"
-                                                   : "sgn.cluster.nhwc.smajor.packed.vec16";
-                const int E = 16 / size;
+                NhwcLayout lay = nhwc_layout(a.N, pp, false);
+                if (pp.K > 1 && (lay.grid <= resident || lay.span > resident)) lay = nhwc_layout(a.N, pp, true);
+                *route = lay.Kp > 1 || pp.K == 1 ? "sgn.cluster.nhwc.packed.vec16"
+                                                 : "sgn.cluster.nhwc.smajor.packed.vec16";
+                const int ev = 16 / size;  // 16-byte accesses
                 if (a.dtype == 0) {
-                    if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, plan, lay, E, kpx, part, stream);
-                    else *err = launch_nhwc_typed<float, half_t>(a, plan, lay, E, kpx, part, stream);
+                    if (a.param_dtype == 0) *err = launch_nhwc_typed<float, float>(a, pp, lay, ev, kpx, part, stream);
+                    else *err = launch_nhwc_typed<float, half_t>(a, pp, lay, ev, kpx, part, stream);
                 } else {
-                    if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, plan, lay, E, kpx, part, stream);
-                    else *err = launch_nhwc_typed<half_t, half_t>(a, plan, lay, E, kpx, part, stream);
+                    if (a.param_dtype == 0) *err = launch_nhwc_typed<half_t, float>(a, pp, lay, ev, kpx, part, stream);
+                    else *err = launch_nhwc_typed<half_t, half_t>(a, pp, lay, ev, kpx, part, stream);
                 }
                 return true;
             }
