@@ -297,7 +297,10 @@ struct ShiftedSums {
         }
         const float q = s1 / n;
         m.mean = shift + q;
-        m.m2 = fmaxf(fmaf_(-s1, q, s2), 0.0f);
+        // Rounding can leave a tiny negative M2; clamp it, but keep NaN (an
+        // infinite value gives inf - inf here), which fmaxf would turn into 0.
+        const float m2 = fmaf_(-s1, q, s2);
+        m.m2 = m2 < 0.0f ? 0.0f : m2;
         return m;
     }
 };

@@ -129,7 +129,10 @@ __device__ __forceinline__ Moments block_merge(Moments m, Moments* sh) {
 }
 
 __device__ __forceinline__ float2 finalize(const Moments& m, float eps) {
-    const float var = m.n > 0.0f ? fmaxf(m.m2 / m.n, 0.0f) : 0.0f;
+    // Negative rounding residue clamps to 0; NaN (a group holding an
+    // infinity or NaN) stays NaN, so the whole group's output is NaN.
+    const float v = m.m2 / m.n;
+    const float var = m.n > 0.0f ? (v < 0.0f ? 0.0f : v) : 0.0f;
     return make_float2(m.mean, inv_sqrt(var + eps));
 }
 

@@ -476,8 +476,124 @@ def pin_sgn_invariants(orc):
             assert np.allclose(per.var(-1), sv / (sv + eps32), rtol=1e-6)
 
 
+# ----------------------------------------------------------------- non-finite values
+def _plant_rows(x, k, dt):
+    """Row 1 gets +inf, row 2 NaN, row 3 an input pair whose sum overflows dt,
+    row 4 both infinities; the other rows stay finite."""
+    big = 60000.0 if dt == np.float16 else 3e38
+    x[1, 5] = np.inf
+    x[2, 7] = np.nan
+    x[3, 0] = big
+    k[3, 0] = big
+    x[4, 1] = np.inf
+    x[4, 2] = -np.inf
+
+
+def pin_non_finite_matches_torch(orc):
+    """Infinities and NaNs in the inputs, and sums that overflow the data type.
+
+    The pages say nothing about them, so IEEE arithmetic applied to each
+    definition decides the result. The oracle must therefore agree with the
+    float64 library routines on the same S:
+    - the positions of NaN;
+    - the infinities, sign included;
+    - every finite output, within one ulp. This covers the zeros that a row
+      with an infinite mean square gives its finite elements, and every row or
+      group that holds no non-finite value.
+    """
+    rng = np.random.default_rng(41)
+    with np.errstate(all="ignore"):
+        for dt, hidden, with_bias in [(np.float32, 40, True), (np.float16, 24, False)]:
+            x = rng.standard_normal((6, hidden), dtype=np.float32).astype(dt)
+            k = rng.standard_normal((6, hidden), dtype=np.float32).astype(dt)
+            g = rng.uniform(0.5, 1.5, hidden).astype(dt)
+            be = (0.1 * rng.standard_normal(hidden, dtype=np.float32)).astype(dt)
+            b = (0.1 * rng.standard_normal(hidden, dtype=np.float32)).astype(dt) if with_bias else None
+            _plant_rows(x, k, dt)
+            s_ref = residual_sum_numpy(x, k, b, dt)
+            assert np.isinf(s_ref[3, 0]) and np.isnan(s_ref[2, 7]), "planted values not in S"
+            st = torch.from_numpy(s_ref.astype(np.float64))
+            eps = float(np.float32(1e-6))
+            # SSLN: the mean square of rows 1, 3 and 4 is +inf, so their
+            # scale is 0: finite elements give (signed) zeros and the
+            # infinite ones NaN; row 2 is NaN throughout.
+            out, _, inv, s = orc.skip_rms_norm(x, k, g, b, 1e-6, want_inv_std_var=True, want_sum=True)
+            assert np.array_equal(np.isnan(s), np.isnan(s_ref)) and \
+                np.array_equal(s[~np.isnan(s)].view(np.uint8), s_ref[~np.isnan(s_ref)].view(np.uint8)), \
+                "non-finite S differs from numpy's sum"
+            y = F.rms_norm(st, (hidden,), torch.from_numpy(g.astype(np.float64)), eps=eps)
+            assert_within_ulp(out, y.numpy().astype(dt), 1, f"SSLN {np.dtype(dt)} non-finite output")
+            inv_ref = torch.rsqrt(st.pow(2).mean(-1, keepdim=True) + eps)
+            assert_within_ulp(inv, inv_ref.numpy().astype(np.float32), 1, "SSLN non-finite inv_std_var")
+            # Skip layer norm: the mean of rows 1-4 is non-finite, so their
+            # deviations, variance and outputs are NaN.
+            out, mean, inv, _ = orc.skip_layer_norm(x, k, g, be, b, 1e-6, want_mean=True,
+                                                    want_inv_std_var=True, want_sum=True)
+            y = F.layer_norm(st, (hidden,), torch.from_numpy(g.astype(np.float64)),
+                             torch.from_numpy(be.astype(np.float64)), eps=eps)
+            assert_within_ulp(out, y.numpy().astype(dt), 1, f"SLN {np.dtype(dt)} non-finite output")
+            assert_within_ulp(mean, st.mean(-1, keepdim=True).numpy().astype(np.float32), 1,
+                              "SLN non-finite mean")
+            var = st.var(-1, unbiased=False, keepdim=True)
+            assert_within_ulp(inv, torch.rsqrt(var + eps).numpy().astype(np.float32), 1,
+                              "SLN non-finite inv_std_var")
+
+        # GatedRMSNorm: X infinite or NaN in some spans; gate +inf (SiLU = inf),
+        # -inf (SiLU = -inf * 0 = NaN) and NaN in others.
+        for dt in (np.float32, np.float16):
+            C = 8
+            X = rng.standard_normal((5, 3 * C), dtype=np.float32).astype(dt)
+            gate = rng.standard_normal((5, 3 * C), dtype=np.float32).astype(dt)
+            scale = rng.uniform(0.5, 1.5, C).astype(dt)
+            X[0, 1] = np.inf
+            X[1, C + 2] = np.nan
+            X[2, 2 * C] = -np.inf
+            gate[3, 3] = np.inf
+            gate[3, C + 4] = -np.inf
+            gate[4, 2 * C + 5] = np.nan
+            y = orc.gated_rms_norm(X, scale, gate, 1e-5)
+            assert_within_ulp(y, _gated_torch(X, scale, gate, 1e-5, dt), 1, f"gated {np.dtype(dt)} non-finite")
+
+        # SkipGroupNorm: a group's non-finite mean or variance makes the whole
+        # group NaN (SiLU keeps NaN); the other groups of the image and the
+        # other images are untouched.
+        for dt, pdt, cl, bcast, act in [(np.float16, np.float32, 1, False, 1),
+                                        (np.float32, np.float16, 0, True, 0),
+                                        (np.float32, np.float32, 1, False, 1)]:
+            N, C, H, W, groups = 3, 12, 3, 4, 3
+            x, skip, bias, gamma, beta = _sgn_inputs(rng, dt, pdt, N, C, H, W, cl, bcast, True)
+            big = 60000.0 if dt == np.float16 else 3e38
+            at = (lambda n, c, h, w: (n, h, w, c)) if cl else (lambda n, c, h, w: (n, c, h, w))
+            x[at(0, 5, 1, 2)] = np.inf                 # image 0, group 1
+            x[at(1, 0, 2, 3)] = np.nan                 # image 1, group 0
+            x[at(1, 11, 0, 0)] = big                   # image 1, group 2: S overflows
+            if bcast:
+                skip[1, 11] = big
+            else:
+                skip[at(1, 11, 0, 0)] = big
+            x[at(2, 4, 0, 1)] = np.inf                 # image 2, group 1: both infinities
+            x[at(2, 6, 2, 0)] = -np.inf
+            Y, S = orc.skip_group_norm(x, gamma, beta, skip, bias, groups=groups, activation=act,
+                                       epsilon=1e-5, channels_last=cl, want_sum=True)
+            full = _expand_skip(skip, N, C, H, W, cl) if bcast else skip
+            s_ref = residual_sum_numpy(x, full, bias.reshape(1, 1, 1, C) if cl else bias.reshape(1, C, 1, 1), dt)
+            assert np.array_equal(np.isnan(S), np.isnan(s_ref)) and \
+                np.array_equal(S[~np.isnan(S)].view(np.uint8), s_ref[~np.isnan(s_ref)].view(np.uint8)), \
+                "non-finite S differs from numpy's sum"
+            ref = _sgn_torch(s_ref, gamma, beta, groups, 1e-5, act, cl, dt)
+            assert_within_ulp(Y, ref, 1, f"SGN {np.dtype(dt)} cl={cl} non-finite vs group_norm")
+            ys = Y.reshape(N, H * W, C) if cl else np.moveaxis(Y.reshape(N, C, H * W), 1, 2)
+            ys = ys.reshape(N, H * W, groups, C // groups)
+            nan_groups = [(0, 1), (1, 0), (1, 2), (2, 1)]
+            for n in range(N):
+                for gi in range(groups):
+                    blk = ys[n, :, gi]
+                    assert np.isnan(blk).all() == ((n, gi) in nan_groups), f"group ({n}, {gi})"
+                    assert np.isfinite(blk).all() == ((n, gi) not in nan_groups), f"group ({n}, {gi})"
+
+
 PINS = [pin_hand_cases, pin_f16_decode_exhaustive, pin_f32_to_f16_structured,
         pin_f64_to_f16_ties, pin_ssln_matches_torch, pin_ssln_invariants,
         pin_sln_matches_torch, pin_sln_invariants,
         pin_gated_matches_torch, pin_gated_invariants, pin_sgn_matches_torch,
-        pin_sgn_invariants]
+        pin_sgn_invariants, pin_non_finite_matches_torch]

@@ -477,6 +477,48 @@ def test_non_finite_values_stay_in_their_group(cl, route):
     assert nan_groups == {(0, 2), (1, 5)}, nan_groups
 
 
+LONE_INF_SHAPES = [
+    # (N, C, H, W, groups): one 16-byte float16 vector per NCHW group (one
+    # thread holds the whole group), small groups, and the NHWC channel layout.
+    (2, 8, 2, 4, 8),
+    (2, 16, 4, 4, 4),
+    (2, 64, 6, 6, 8),
+    (1, 15, 8, 8, 5),
+]
+
+
+@pytest.mark.parametrize("route", ["auto", "split", "scalar", "block"])
+@pytest.mark.parametrize("cl", [0, 1])
+@pytest.mark.parametrize("dt", [F16, F32])
+@pytest.mark.parametrize("shape", LONE_INF_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_lone_infinity_makes_its_group_nan(shape, dt, cl, route):
+    """A single residual sum that overflows to +inf, without SiLU (which would
+    turn -inf into NaN and hide the difference): the group's mean is +inf and
+    its variance NaN, so IEEE arithmetic on the definition makes every output
+    of the group NaN, as in the oracle, wherever the infinity sits in the
+    group (its first, a middle or its last element) and whichever thread's
+    sums hold it; the other groups match the oracle as usual."""
+    N, C, H, W, groups = shape
+    big = 65504.0 if dt == F16 else 3e38
+    cpg, hw = C // groups, H * W
+    for pos in (0, (cpg * hw) // 2, cpg * hw - 1):  # element of group 1 of image N - 1, in NCHW order
+        w, x = make((N, C, H, W, dt, F32, cl, False, True, groups, 0), seed=17 + pos)
+        X, skip = x["X"].copy(), x["skip"].copy()
+        c, p = cpg * 1 + pos // hw, pos % hw
+        h, wv = divmod(p, W)
+        idx = (N - 1, h, wv, c) if cl else (N - 1, c, h, wv)
+        X[idx] = big
+        skip[idx] = big
+        x = dict(x, X=X, skip=skip)
+        ref, out, used = run(x, w, route)
+        assert np.isinf(ref[1]).sum() == 1
+        check(ref, out)
+        y = to_host(out.Y)
+        y = (y.transpose(0, 3, 1, 2) if cl else y).reshape(N, groups, cpg * hw)
+        nan_groups = {(n, g) for n in range(N) for g in range(groups) if np.isnan(y[n, g]).all()}
+        assert nan_groups == {(N - 1, 1)}, (pos, used, nan_groups)
+
+
 @pytest.mark.parametrize("dt,N,C,H,W,groups,offset,bc", [
     (F16, 2, 64, 8, 8, 8, 1, False),     # whole vectors per plane, bases off the grid
     (F16, 2, 40, 7, 7, 4, 0, True),      # 7 x 7 planes
