@@ -276,6 +276,12 @@ __device__ __forceinline__ Moments merge(const Moments& a, const Moments& b) {
     return r;
 }
 
+// The shift for sums about a row's first element: that element when it is
+// finite, else 0.  With an infinite shift the shift element itself would add
+// inf - inf = NaN, and the mean (shift + mean of the differences) would be
+// NaN where the sum over the row is infinite.
+__device__ __forceinline__ float row_shift(float s0) { return __builtin_isfinite(s0) ? s0 : 0.0f; }
+
 // Per-thread accumulator with the shifted-data method: sums of (x - shift)
 // and (x - shift)^2, shift = the first value seen, so a group whose values
 // are all equal accumulates exact zeros.

@@ -139,6 +139,7 @@ ssln_wave_kernel(const T* __restrict__ input, const T* __restrict__ skip,
             shift = residual_sum<T>(to_f32(input[row * nvec * E]), to_f32(skip[row * nvec * E]), has_bias,
                                     has_bias ? to_f32(bias[0]) : 0.0f, rounded);
         }
+        shift = row_shift(shift);
     }
 
     // S for every lane (lanes past the row's end form their re-read vector
@@ -314,8 +315,8 @@ ssln_wide_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     float shift = 0.0f;  // as in ssln_wave_kernel: statistics about S[0]
     if constexpr (CENTER) {
         T rounded;
-        shift = residual_sum<T>(to_f32(input[base * E]), to_f32(skip[base * E]), has_bias,
-                                to_f32(biasp[0]), rounded);
+        shift = row_shift(residual_sum<T>(to_f32(input[base * E]), to_f32(skip[base * E]), has_bias,
+                                          to_f32(biasp[0]), rounded));
     }
 
     V ss[NV];
@@ -520,8 +521,8 @@ ssln_phase_kernel(const T* __restrict__ input, const T* __restrict__ skip,
     float shift = 0.0f;
     if constexpr (CENTER) {
         T rounded;
-        shift = residual_sum<T>(to_f32(input[row * hidden]), to_f32(skip[row * hidden]), has_bias,
-                                has_bias ? to_f32(bias[0]) : 0.0f, rounded);
+        shift = row_shift(residual_sum<T>(to_f32(input[row * hidden]), to_f32(skip[row * hidden]), has_bias,
+                                          has_bias ? to_f32(bias[0]) : 0.0f, rounded));
     }
     // Element e of vector i lies in the row when lo_e <= e < hi_e.
     auto in_row = [&](int i, int e) { return i < nvr && e >= p - i * E && e < hidden + p - i * E; };
@@ -665,8 +666,8 @@ ssln_block_kernel(const T* __restrict__ input, const T* __restrict__ skip,
         float shift = 0.0f;  // sums about S[0], as in the register routes
         if constexpr (CENTER) {
             T r0;
-            shift = residual_sum<T>(to_f32(input[base * E]), to_f32(skip[base * E]), has_bias,
-                                    to_f32(bias[0]), r0);
+            shift = row_shift(residual_sum<T>(to_f32(input[base * E]), to_f32(skip[base * E]), has_bias,
+                                              to_f32(bias[0]), r0));
         }
         float acc = 0.0f;
         for (int64_t j0 = t; j0 < nvec; j0 += 256 * U) {
@@ -784,7 +785,7 @@ ssln_segment_kernel(const T* __restrict__ input, const T* __restrict__ skip,
         // With the mean removed, sums are taken about the row's first element
         // S[0], which the segment's lane 0 holds.
         float shift = 0.0f, md = 0.0f, r;
-        if constexpr (CENTER) shift = __shfl(to_f32(ss.v[0]), first_lane, 64);
+        if constexpr (CENTER) shift = row_shift(__shfl(to_f32(ss.v[0]), first_lane, 64));
         float part = 0.0f;
         if (l < nvec) {
 #pragma unroll
@@ -1008,7 +1009,7 @@ ssln_flat_kernel(const T* __restrict__ input, const T* __restrict__ skip,
             // The group's reads of this row are done (the butterfly used them).
             if (has && k == 0) sq[wave][first] = r;
         } else {
-            s0 = sq[wave][first];
+            s0 = row_shift(sq[wave][first]);
             md = row_sum(first, has, [&](float p, float x) { return p + (x - s0); }) / hidden_f;
             const float dev = row_sum(first, has, [&](float p, float x) {
                 const float d = (x - s0) - md;

@@ -93,6 +93,47 @@ def test_matches_oracle(shape, dt, beta, bias, route):
             assert used.startswith("ssln.block")
 
 
+NON_FINITE_SHAPES = [
+    # (shape, dtype): one shape for each row route
+    ((64, 768), F32),       # one wave per row
+    ((7, 8192), F16),       # four waves per row
+    ((3, 4100), F16),       # 8-byte vectors
+    ((3, 4097), F16),       # phased route
+    ((1000, 128), F16),     # flat route, lane groups of 16
+    ((31, 7), F16),         # flat route, scalars
+    ((3, 100000), F16),     # wide route
+    ((3, 65544), F16),      # block route
+    ((3, 33), F32),         # short odd float32 rows
+]
+
+
+@pytest.mark.parametrize("route", ["auto", "block"])
+@pytest.mark.parametrize("shape,dt", NON_FINITE_SHAPES, ids=[f"{s}-{np.dtype(d).name}" for s, d in NON_FINITE_SHAPES])
+def test_non_finite_rows(shape, dt, route):
+    """Rows whose sum overflows to +inf at their first element (the element
+    the kernels take their sums about), +inf further in, and a NaN first
+    element: the mean is the row's sum over its count (+inf, or NaN), the
+    variance NaN, so inv_std_var and every output of the row are NaN, as in
+    the oracle; S keeps the infinities bit for bit and the other rows are
+    untouched."""
+    w = workloads.sln("t", shape, dt, beta=True, bias=True, epsilon=1e-5)
+    x = workloads.generate(w, seed=sum(shape) + 3)
+    inp, skp = x["input"].copy(), x["skip"].copy()
+    hidden = shape[-1]
+    a, k = inp.reshape(-1, hidden), skp.reshape(-1, hidden)
+    big = 65504.0 if dt == F16 else 3e38
+    a[0, 0] = k[0, 0] = big                      # S[0] = +inf
+    a[1, hidden // 2] = k[1, hidden // 2] = big  # +inf inside the row
+    a[2, 0] = np.nan                             # S[0] = NaN
+    x = dict(x, input=inp, skip=skp)
+    ref, out, used = run_both(x, 1e-5, route)
+    check(ref, out)
+    mean = to_host(out.mean).reshape(-1)
+    assert mean[0] == np.inf and mean[1] == np.inf and np.isnan(mean[2]), (used, mean[:3])
+    y = to_host(out.output).reshape(-1, hidden)
+    assert np.isnan(y[:3]).all() and np.isfinite(y[3:]).all(), used
+
+
 @pytest.mark.parametrize("want", [(), ("sum",), ("mean",), ("inv",), ("mean", "inv", "sum")])
 @pytest.mark.parametrize("dt,hidden", [(F32, 2048), (F16, 4096), (F16, 16384), (F32, 50000)])
 def test_optional_outputs_do_not_change_output(dt, hidden, want):
