@@ -350,6 +350,52 @@ def test_flat_needs_a_shared_offset():
         assert_close(to_host(y), oracle.gated_rms_norm(x["X"], x["scale"], x["gate"], 1e-5), "Y")
 
 
+NON_FINITE_CASES = [
+    # (X shape, span C, dtype): one shape for each route family
+    ((9, 8), 8, F16),            # one vector per span
+    ((13, 64), 64, F32),         # segment route
+    ((4, 33, 128), 128, F16),    # C = 128, ragged last block
+    ((1000, 25), 25, F16),       # flat route
+    ((1000, 132), 132, F16),     # tile route
+    ((6, 1017), 1017, F16),      # phased route
+    ((6, 2048), 2048, F32),      # row route
+    ((6, 100000), 100000, F16),  # wide route
+    ((6, 139272), 139272, F16),  # block route
+]
+
+
+@pytest.mark.parametrize("route", ["auto", "block"])
+@pytest.mark.parametrize("shape,C,dt", NON_FINITE_CASES, ids=[f"{s}-C{c}-{np.dtype(d).name}"
+                                                                for s, c, d in NON_FINITE_CASES])
+def test_non_finite_spans(shape, C, dt, route):
+    """+inf, NaN and -inf in X (the span's mean square is +inf or NaN: its
+    finite elements give signed zeros, the others NaN) and +inf, -inf and NaN
+    gates (SiLU: +inf, -inf * 0 = NaN, NaN), each in its own span; every
+    output equals the oracle's, NaN positions and infinities included, and
+    the untouched spans are finite."""
+    w = workloads.gated("t", shape, C, dt, epsilon=1e-5)
+    x = workloads.generate(w, seed=C + 5)
+    X, gate = x["X"].copy(), x["gate"].copy()
+    xs, gs = X.reshape(-1, C), gate.reshape(-1, C)
+    e = C // 2
+    xs[0, e] = np.inf
+    xs[1, 0] = np.nan
+    xs[2, C - 1] = -np.inf
+    gs[3, e] = np.inf
+    gs[4, 0] = -np.inf
+    gs[5, C - 1] = np.nan
+    ref = oracle.gated_rms_norm(X, x["scale"], gate, 1e-5)
+    with gn.force_route(route):
+        y = gn.gated_rms_norm(to_dev(X), to_dev(x["scale"]), to_dev(gate), 1e-5)
+        used = gn.last_route()
+    yh = to_host(y)
+    assert_close(yh, ref, f"Y via {used}")
+    ys = yh.reshape(-1, C)
+    assert np.isnan(ys[1]).all() and np.isnan(ys[0, e]) and np.isnan(ys[2, C - 1]), used
+    assert np.isnan(ys[4, 0]) and np.isnan(ys[5, C - 1]), used
+    assert np.isfinite(ys[6:]).all(), used
+
+
 @pytest.mark.parametrize("dt", [F32, F16])
 def test_zero_gate_gives_zero(dt):
     w = workloads.gated("t", (64, 256), 128, dt, epsilon=1e-5)
