@@ -1,0 +1,135 @@
+"""epsilon = 0, which every op accepts (epsilon must be finite and at least
+0), on rows, spans and groups whose variance or mean square is exactly 0:
+the scale 1 / sqrt(0 + 0) is +inf and each output (S - mean) * inf =
+0 * inf is NaN under IEEE arithmetic, in the oracle as on the GPU.  Their
+neighbours, with a non-zero spread, stay finite and match the oracle."""
+import numpy as np
+import pytest
+
+import group_normalization_amd as gn
+import oracle
+import workloads
+from parity import assert_bitwise, assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+F32, F16 = np.float32, np.float16
+
+ROW_SHAPES = [
+    ((64, 768), F32),       # one wave per row
+    ((7, 8192), F16),       # four waves per row
+    ((1000, 128), F16),     # flat route
+    ((3, 4097), F16),       # phased route
+    ((3, 100000), F16),     # wide route
+]
+
+
+@pytest.mark.parametrize("route", ["auto", "block"])
+@pytest.mark.parametrize("shape,dt", ROW_SHAPES, ids=[f"{s}-{np.dtype(d).name}" for s, d in ROW_SHAPES])
+def test_ssln_zero_row(shape, dt, route):
+    w = workloads.ssln("t", shape, dt, bias=False, epsilon=0.0)
+    x = workloads.generate(w, seed=sum(shape))
+    inp, skp = x["input"].copy(), x["skip"].copy()
+    hidden = shape[-1]
+    skp.reshape(-1, hidden)[0] = -inp.reshape(-1, hidden)[0]  # S = 0 exactly: mean square 0
+    ref_y, _, ref_inv, ref_s = oracle.skip_rms_norm(inp, skp, x["gamma"], None, 0.0, want_inv_std_var=True,
+                                                    want_sum=True)
+    with gn.force_route(route):
+        out = gn.skip_rms_norm(to_dev(inp), to_dev(skp), to_dev(x["gamma"]), None, 0.0,
+                               want_inv_std_var=True, want_sum=True)
+        used = gn.last_route()
+    assert_close(to_host(out.output), ref_y, f"output via {used}")
+    assert_close(to_host(out.inv_std_var), ref_inv, "inv_std_var")
+    assert_bitwise(to_host(out.input_skip_bias_sum), ref_s, "S")
+    y = to_host(out.output).reshape(-1, hidden)
+    assert np.isnan(y[0]).all() and np.isfinite(y[1:]).all(), used
+    assert to_host(out.inv_std_var).reshape(-1)[0] == np.inf
+
+
+@pytest.mark.parametrize("route", ["auto", "block"])
+@pytest.mark.parametrize("shape,dt", ROW_SHAPES, ids=[f"{s}-{np.dtype(d).name}" for s, d in ROW_SHAPES])
+def test_sln_constant_row(shape, dt, route):
+    w = workloads.sln("t", shape, dt, beta=True, bias=False, epsilon=0.0)
+    x = workloads.generate(w, seed=sum(shape) + 1)
+    inp, skp = x["input"].copy(), x["skip"].copy()
+    hidden = shape[-1]
+    inp.reshape(-1, hidden)[0] = dt(1.5)
+    skp.reshape(-1, hidden)[0] = dt(-0.25)  # S = 1.25 across the row: variance 0
+    ref = oracle.skip_layer_norm(inp, skp, x["gamma"], x["beta"], None, 0.0, want_mean=True,
+                                 want_inv_std_var=True, want_sum=True)
+    with gn.force_route(route):
+        out = gn.skip_layer_norm(to_dev(inp), to_dev(skp), to_dev(x["gamma"]), to_dev(x["beta"]), None, 0.0,
+                                 want_mean=True, want_inv_std_var=True, want_sum=True)
+        used = gn.last_route()
+    assert_close(to_host(out.output), ref[0], f"output via {used}")
+    assert_close(to_host(out.mean), ref[1], "mean")
+    assert_close(to_host(out.inv_std_var), ref[2], "inv_std_var")
+    assert_bitwise(to_host(out.input_skip_bias_sum), ref[3], "S")
+    y = to_host(out.output).reshape(-1, hidden)
+    assert np.isnan(y[0]).all() and np.isfinite(y[1:]).all(), used
+    assert to_host(out.mean).reshape(-1)[0] == np.float32(1.25)
+
+
+SPAN_CASES = [
+    ((13, 64), 64, F32),        # segment route
+    ((1000, 25), 25, F16),      # flat route
+    ((1000, 132), 132, F16),    # tile route
+    ((6, 2048), 2048, F32),     # row route
+    ((6, 100000), 100000, F16), # wide route
+]
+
+
+@pytest.mark.parametrize("route", ["auto", "block"])
+@pytest.mark.parametrize("shape,C,dt", SPAN_CASES, ids=[f"{s}-C{c}-{np.dtype(d).name}" for s, c, d in SPAN_CASES])
+def test_gated_zero_span(shape, C, dt, route):
+    w = workloads.gated("t", shape, C, dt, epsilon=0.0)
+    x = workloads.generate(w, seed=C + 9)
+    X = x["X"].copy()
+    X.reshape(-1, C)[0] = 0  # mean square 0
+    ref = oracle.gated_rms_norm(X, x["scale"], x["gate"], 0.0)
+    with gn.force_route(route):
+        y = gn.gated_rms_norm(to_dev(X), to_dev(x["scale"]), to_dev(x["gate"]), 0.0)
+        used = gn.last_route()
+    assert_close(to_host(y), ref, f"Y via {used}")
+    ys = to_host(y).reshape(-1, C)
+    assert np.isnan(ys[0]).all() and np.isfinite(ys[1:]).all(), used
+
+
+GROUP_CASES = [
+    # (N, C, H, W, dtype, channels_last, groups)
+    (2, 64, 8, 8, F16, 1, 8),       # NHWC channel-block cluster
+    (2, 64, 8, 8, F32, 0, 8),       # NCHW cluster
+    (2, 64, 7, 9, F16, 0, 8),       # NCHW phased cluster
+    (8, 15, 64, 128, F16, 1, 5),    # NHWC packed runs
+    (2, 15, 16, 16, F16, 1, 5),     # NHWC element accesses
+]
+
+
+@pytest.mark.parametrize("route", ["auto", "split"])
+@pytest.mark.parametrize("case", GROUP_CASES, ids=lambda c: "x".join(map(str, c[:4])) + ("nhwc" if c[5] else "nchw"))
+def test_sgn_constant_group(case, route):
+    N, C, H, W, dt, cl, groups = case
+    w = workloads.sgn("t", N, C, H, W, dt, F32, channels_last=bool(cl), broadcast_skip=False, bias=False,
+                      groups=groups, activation=0, epsilon=0.0)
+    x = workloads.generate(w, seed=N + C + H)
+    X, skip = x["X"].copy(), x["skip"].copy()
+    cpg = C // groups
+    if cl:
+        X[1, :, :, cpg:2 * cpg] = dt(0.75)   # image 1, group 1: S = 0.75 throughout
+        skip[1, :, :, cpg:2 * cpg] = 0
+    else:
+        X[1, cpg:2 * cpg] = dt(0.75)
+        skip[1, cpg:2 * cpg] = 0
+    ref_y, ref_s = oracle.skip_group_norm(X, x["gamma"], x["beta"], skip, None, groups=groups, activation=0,
+                                          epsilon=0.0, channels_last=cl, want_sum=True)
+    with gn.force_route(route):
+        out = gn.skip_group_norm(to_dev(X), to_dev(x["gamma"]), to_dev(x["beta"]), to_dev(skip), None,
+                                 groups=groups, activation=0, epsilon=0.0, channels_last=cl, want_sum=True)
+        used = gn.last_route()
+    assert_close(to_host(out.Y), ref_y, f"Y via {used}")
+    assert_bitwise(to_host(out.S), ref_s, "S")
+    y = to_host(out.Y)
+    y = (y.transpose(0, 3, 1, 2) if cl else y).reshape(N, groups, -1)
+    nan_groups = {(n, g) for n in range(N) for g in range(groups) if np.isnan(y[n, g]).all()}
+    assert nan_groups == {(1, 1)}, (used, nan_groups)
+    assert np.isfinite(np.delete(y.reshape(N * groups, -1), groups + 1, axis=0)).all(), used
