@@ -133,3 +133,54 @@ def test_sgn_constant_group(case, route):
     nan_groups = {(n, g) for n in range(N) for g in range(groups) if np.isnan(y[n, g]).all()}
     assert nan_groups == {(1, 1)}, (used, nan_groups)
     assert np.isfinite(np.delete(y.reshape(N * groups, -1), groups + 1, axis=0)).all(), used
+
+
+LEAK_CASES = [
+    # (op, shape, dtype): rows narrower than a vector or off the 16-byte grid,
+    # so that rows share the vectors at their ends, within a wave's tile and
+    # across tiles
+    ("ssln", (997, 7), F16),
+    ("ssln", (601, 33), F32),
+    ("ssln", (503, 127), F16),
+    ("sln", (997, 7), F16),
+    ("sln", (601, 33), F32),
+    ("gated", (999, 25), F16),
+    ("gated", (700, 301), F32),
+    ("gated", (2000, 3), F16),
+]
+
+
+@pytest.mark.parametrize("op,shape,dt", LEAK_CASES, ids=[f"{o}-{s}-{np.dtype(d).name}" for o, s, d in LEAK_CASES])
+def test_non_finite_values_stay_in_their_row(op, shape, dt):
+    """+inf as the last element of every fifth row and NaN as the first
+    element of every seventh (offset 3): rows that share a vector with them,
+    in the same wave's tile or the next, must stay exactly as the oracle has
+    them (finite), wherever the tiles end."""
+    rows, hidden = shape
+    if op == "gated":
+        w = workloads.gated("t", shape, hidden, dt, epsilon=1e-5)
+        key = "X"
+    else:
+        w = (workloads.ssln("t", shape, dt, bias=True, epsilon=1e-5) if op == "ssln"
+             else workloads.sln("t", shape, dt, beta=True, bias=True, epsilon=1e-5))
+        key = "input"
+    x = workloads.generate(w, seed=rows + hidden)
+    a = x[key].copy()
+    inf_rows, nan_rows = np.arange(0, rows, 5), np.arange(3, rows, 7)
+    a[inf_rows, hidden - 1] = np.inf
+    a[nan_rows, 0] = np.nan
+    if op == "gated":
+        ref = oracle.gated_rms_norm(a, x["scale"], x["gate"], 1e-5)
+        y = to_host(gn.gated_rms_norm(to_dev(a), to_dev(x["scale"]), to_dev(x["gate"]), 1e-5))
+    elif op == "ssln":
+        ref = oracle.skip_rms_norm(a, x["skip"], x["gamma"], x["bias"], 1e-5)[0]
+        y = to_host(gn.skip_rms_norm(to_dev(a), to_dev(x["skip"]), to_dev(x["gamma"]), to_dev(x["bias"]),
+                                     1e-5).output)
+    else:
+        ref = oracle.skip_layer_norm(a, x["skip"], x["gamma"], x["beta"], x["bias"], 1e-5)[0]
+        y = to_host(gn.skip_layer_norm(to_dev(a), to_dev(x["skip"]), to_dev(x["gamma"]), to_dev(x["beta"]),
+                                       to_dev(x["bias"]), 1e-5).output)
+    used = gn.last_route()
+    assert_close(y, ref, f"{op} via {used}")
+    clean = np.setdiff1d(np.arange(rows), np.union1d(inf_rows, nan_rows))
+    assert np.isfinite(y[clean]).all(), used
