@@ -484,6 +484,7 @@ LONE_INF_SHAPES = [
     (2, 16, 4, 4, 4),
     (2, 64, 6, 6, 8),
     (1, 15, 8, 8, 5),
+    (8, 15, 64, 128, 5),  # NHWC: the cluster over packed runs of pixels (vectors holding several groups)
 ]
 
 
