@@ -124,3 +124,29 @@ def test_sgn_beyond_2_31_elements(channels_last):
                                               channels_last=channels_last, want_sum=True)
         assert_close(out.Y[n:n + 1].cpu().numpy(), ref_y, f"Y image {n}")
         assert_bitwise(out.S[n:n + 1].cpu().numpy(), ref_s, f"S image {n}")
+
+
+def test_sgn_packed_runs_beyond_2_31_elements():
+    """NHWC pixels of 15 float16 channels (runs of 8 pixels make 15 whole
+    16-byte vectors): the cluster over packed runs, in many rounds of
+    resident workgroups, past the 2^31-element boundary."""
+    C, H, W, groups = 15, 264, 264, 5
+    per_image = C * H * W
+    N = TWO31 // per_image + 2
+    X = gen((N, H, W, C), torch.float16, 17)
+    skip = gen((N, H, W, C), torch.float16, 18)
+    rng = np.random.default_rng(19)
+    gamma = torch.from_numpy(rng.uniform(0.5, 1.5, C).astype(np.float32)).cuda()
+    beta = torch.from_numpy((0.1 * rng.standard_normal(C)).astype(np.float32)).cuda()
+    bias = torch.from_numpy((0.1 * rng.standard_normal(C)).astype(np.float16)).cuda()
+    out = gn.skip_group_norm(X, gamma, beta, skip, bias, groups=groups, activation=1, channels_last=1,
+                             want_sum=True)
+    assert "packed" in gn.last_route(), gn.last_route()
+    torch.cuda.synchronize()
+    for n in (0, TWO31 // per_image, N - 1):  # the middle one straddles element 2^31
+        ref_y, ref_s = oracle.skip_group_norm(X[n:n + 1].cpu().numpy(), gamma.cpu().numpy(),
+                                              beta.cpu().numpy(), skip[n:n + 1].cpu().numpy(),
+                                              bias.cpu().numpy(), groups=groups, activation=1,
+                                              channels_last=1, want_sum=True)
+        assert_close(out.Y[n:n + 1].cpu().numpy(), ref_y, f"Y image {n}")
+        assert_bitwise(out.S[n:n + 1].cpu().numpy(), ref_s, f"S image {n}")
