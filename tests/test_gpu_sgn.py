@@ -283,6 +283,11 @@ NHWC_LIMIT_CASES = [
     (1, 512, 192, 192, F16, 32, True, "sgn.cluster.nhwc.vec16"),
     # 1344 workgroups, more than two rounds of the 512 resident: split.
     (8, 320, 128, 128, F16, 32, False, "sgn.split.nhwc.vec16"),
+    # One slice per (image, channel block), nothing exchanged: 4096
+    # workgroups of 2 pixels per thread stay in the cluster beyond two rounds;
+    # 1088 of 9 pixels per thread (the 16-pixel form) take the split route.
+    (512, 320, 8, 8, F16, 32, False, "sgn.cluster.nhwc.vec16"),
+    (136, 320, 21, 21, F16, 32, True, "sgn.split.nhwc.vec16"),
 ]
 
 
