@@ -49,6 +49,16 @@ def assert_bitwise(got, ref, what):
                            f"{ref.ravel()[bad[0]]!r}")
 
 
+def assert_bitwise_nan(got, ref, what):
+    """assert_bitwise where NaN positions must agree but NaN payloads (and
+    signs) are not compared: inf - inf and 0 * inf give the host's and the
+    GPU's own default NaN."""
+    got, ref = np.asarray(got), np.asarray(ref)
+    gn, rn = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(gn, rn), f"{what}: NaN positions differ ({gn.sum()} vs {rn.sum()})"
+    assert_bitwise(got[~gn], ref[~rn], what)
+
+
 def assert_close(got, ref, what):
     got, ref = np.asarray(got), np.asarray(ref)
     assert got.dtype == ref.dtype and got.shape == ref.shape, \

@@ -10,7 +10,7 @@ import torch
 
 import group_normalization_amd as gn
 import oracle
-from parity import assert_bitwise, assert_close, to_host
+from parity import assert_bitwise, assert_bitwise_nan, assert_close, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +45,39 @@ def uniform(rng, shape, dtype):
     return rng.uniform(0.5, 1.5, shape).astype(dtype)
 
 
+def plant(rng, a, b, dt, k):
+    """k non-finite values at random positions of a: +inf, -inf, NaN, or a
+    pair of equal large finite values in a and b at the same position (their
+    sum overflows dt).  b may be None (no pair then)."""
+    big = 65504.0 if dt == F16 else 3e38
+    fa, fb = a.reshape(-1), None if b is None else b.reshape(-1)
+    for i in rng.choice(fa.size, size=min(k, fa.size), replace=False):
+        kind = int(rng.integers(0, 4 if fb is not None else 3))
+        if kind == 3:
+            fa[i] = fb[i] = big
+        else:
+            fa[i] = (np.inf, -np.inf, np.nan)[kind]
+
+
+N_NON_FINITE = 24
+
+
 @pytest.mark.parametrize("case", range(N_CASES))
 @pytest.mark.parametrize("center", [False, True], ids=["ssln", "sln"])
 def test_row_norms(center, case):
-    rng = np.random.default_rng(1000 + case + (500 if center else 0))
+    row_norms(center, np.random.default_rng(1000 + case + (500 if center else 0)), False)
+
+
+@pytest.mark.parametrize("case", range(N_NON_FINITE))
+@pytest.mark.parametrize("center", [False, True], ids=["ssln", "sln"])
+def test_row_norms_non_finite(center, case):
+    """As test_row_norms, with a few infinities, NaNs and overflowing sums at
+    random positions: every output (NaN positions and infinities exactly)
+    equals the oracle's."""
+    row_norms(center, np.random.default_rng(4000 + case + (500 if center else 0)), True)
+
+
+def row_norms(center, rng, non_finite):
     dt = F16 if rng.random() < 0.6 else F32
     hidden = draw_length(rng, [(1, 64, 4), (65, 2048, 3), (2049, 12000, 2), (12001, 70000, 1)])
     rows = int(rng.integers(1, max(2, min(300, MAX_ELEMS // hidden)) + 1))
@@ -57,6 +86,8 @@ def test_row_norms(center, case):
     gamma = uniform(rng, hidden, dt)
     bias = normal(rng, hidden, dt, 0.1) if rng.random() < 0.5 else None
     beta = normal(rng, hidden, dt, 0.1) if center and rng.random() < 0.6 else None
+    if non_finite:
+        plant(rng, x, k, dt, int(rng.integers(1, 6)))
     off = int(rng.choice([0, 0, 0, 1, 2, 4]))
     eps = float(rng.choice([1e-6, 1e-5]))
     want = {w: bool(rng.random() < 0.5) for w in ("mean", "inv", "sum")}
@@ -75,7 +106,8 @@ def test_row_norms(center, case):
     what = f"{route} {dt.__name__} {shape} bias={bias is not None} beta={beta is not None} off={off}"
     assert_close(to_host(out.output).reshape(-1, hidden), ref[0], f"output ({what})")
     if want["sum"]:
-        assert_bitwise(to_host(out.input_skip_bias_sum).reshape(-1, hidden), ref[3], f"S ({what})")
+        same = assert_bitwise_nan if non_finite else assert_bitwise
+        same(to_host(out.input_skip_bias_sum).reshape(-1, hidden), ref[3], f"S ({what})")
     if want["inv"]:
         assert_close(to_host(out.inv_std_var).reshape(-1), ref[2].reshape(-1), f"inv_std_var ({what})")
     if want["mean"]:
@@ -84,12 +116,24 @@ def test_row_norms(center, case):
 
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_gated(case):
-    rng = np.random.default_rng(2000 + case)
+    gated(np.random.default_rng(2000 + case), False)
+
+
+@pytest.mark.parametrize("case", range(N_NON_FINITE))
+def test_gated_non_finite(case):
+    """As test_gated, with infinities and NaNs planted in X and in the gate."""
+    gated(np.random.default_rng(5000 + case), True)
+
+
+def gated(rng, non_finite):
     dt = F16 if rng.random() < 0.6 else F32
     C = draw_length(rng, [(1, 64, 3), (65, 1024, 4), (1025, 9000, 2), (9001, 40000, 1)])
     rows = int(rng.integers(1, max(2, min(400, MAX_ELEMS // C)) + 1))
     X, G = normal(rng, (rows, C), dt), normal(rng, (rows, C), dt)
     scale = uniform(rng, C, dt)
+    if non_finite:
+        plant(rng, X, None, dt, int(rng.integers(1, 4)))
+        plant(rng, G, None, dt, int(rng.integers(0, 3)))
     off = int(rng.choice([0, 0, 0, 1, 2, 4]))
     ref = oracle.gated_rms_norm(X, scale, G, 1e-5)
     Y = gn.gated_rms_norm(dev(X, off), dev(scale), dev(G, off), 1e-5)
@@ -100,7 +144,16 @@ def test_gated(case):
 
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_skip_group_norm(case):
-    rng = np.random.default_rng(3000 + case)
+    skip_group_norm(np.random.default_rng(3000 + case), False)
+
+
+@pytest.mark.parametrize("case", range(N_NON_FINITE))
+def test_skip_group_norm_non_finite(case):
+    """As test_skip_group_norm, with infinities, NaNs and overflowing sums planted in X (and skip)."""
+    skip_group_norm(np.random.default_rng(6000 + case), True)
+
+
+def skip_group_norm(rng, non_finite):
     T = F16 if rng.random() < 0.6 else F32
     M = F16 if rng.random() < 0.5 else F32
     groups = int(rng.choice([1, 2, 4, 8, 16, 32]))
@@ -117,6 +170,8 @@ def test_skip_group_norm(case):
     skip = normal(rng, (N, C), T) if bcast else normal(rng, shape, T)
     gamma, beta = uniform(rng, C, M), normal(rng, C, M, 0.1)
     bias = normal(rng, C, T, 0.1) if rng.random() < 0.5 else None
+    if non_finite:
+        plant(rng, X, None if bcast else skip, T, int(rng.integers(1, 5)))
     act = int(rng.random() < 0.5)
     want_sum = bool(rng.random() < 0.5)
     off = int(rng.choice([0, 0, 0, 1, 4]))
@@ -130,7 +185,7 @@ def test_skip_group_norm(case):
             f"bcast={bcast} bias={bias is not None} act={act} off={off}")
     assert_close(to_host(out.Y), ref_y, f"Y ({what})")
     if want_sum:
-        assert_bitwise(to_host(out.S), ref_s, f"S ({what})")
+        (assert_bitwise_nan if non_finite else assert_bitwise)(to_host(out.S), ref_s, f"S ({what})")
 
 
 LARGE_SGN_CASES = 48
