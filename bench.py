@@ -466,6 +466,13 @@ def shape_cases(workloads):
         add(f"sgn_{np.dtype(dt).name}_{layout}_{N}x{C}x{H}x{W}_g{g}",
             workloads.sgn("w", N, C, H, W, dt, F32, channels_last=bool(cl), broadcast_skip=False, bias=True,
                           groups=g, activation=1, epsilon=1e-5, outputs=("Y", "S")), ())
+    # A batch of small images, one workgroup per image's channel block (NHWC)
+    # or group (NCHW) whatever the batch size, beside the split route.
+    for cl in (1, 0):
+        layout = "nhwc" if cl else "nchw"
+        add(f"sgn_float16_{layout}_256x320x16x16_g32",
+            workloads.sgn("w", 256, 320, 16, 16, F16, F32, channels_last=bool(cl), broadcast_skip=False, bias=True,
+                          groups=32, activation=1, epsilon=1e-5, outputs=("Y", "S")), ("split",))
     return out
 
 
