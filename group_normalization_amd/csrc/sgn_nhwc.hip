@@ -854,16 +854,17 @@ bool launch_sgn_nhwc_cluster(const SgnArgs& a, Route want, void* part, hipStream
     // stay here (8 x 64 x 64 x 1280 float32: 148 us, against 162 us split
     // over channel blocks).  Plans of one slice per (image, channel block)
     // exchange nothing, so no workgroup waits and the number of rounds does
-    // not matter: with at most 8 pixels per thread they stay here at any grid
-    // (float16 256 x 16 x 16 x 320: 38.8 against 73.4 us split, 1024 x 8 x 8
-    // x 320 56 against 106, 512 x 16 x 16 x 64 26 against 63, 256 x 20 x 20 x
-    // 320 57 against 91), while the 16-pixel form lost (256 x 24 x 24 x 320
-    // +6 %, 256 x 28 x 28 x 320 +23 %).
+    // not matter: they stay here at any grid (float16 256 x 16 x 16 x 320:
+    // 38.8 against 73.4 us split, 1024 x 8 x 8 x 320 56 against 106, 512 x 16
+    // x 16 x 64 26 against 63, 256 x 20 x 20 x 320 57 against 91; float32
+    // 256 x 16 x 16 x 320 78.5 against 97.5, 256 x 20 x 20 x 320 120 against
+    // 135), except float16 data beyond 8 pixels per thread, which lost (256 x
+    // 24 x 24 x 320 +6 %, 256 x 28 x 28 x 320 +23 %).
     const int split_e = a.dtype == 0 ? widest_vector<float>(a.C, {a.X, a.Y, a.S, a.skip, a.bias})
                                      : widest_vector<half_t>(a.C, {a.X, a.Y, a.S, a.skip, a.bias});
     const bool split_whole_pixels = split_e > 1 && a.C / split_e <= 256;
     const int64_t grid = a.N * plan.NCB * plan.K;  // workgroups that do work
-    const bool split_beyond_two_rounds = plan.K > 1 || plan.R > 8;  // exchanging, or 16 pixels a thread
+    const bool split_beyond_two_rounds = plan.K > 1 || (plan.R > 8 && size == 2);
     if (split_whole_pixels && grid > 2 * resident && split_beyond_two_rounds) return false;
     static const char* const kNames[2][4] = {
         {"sgn.cluster.nhwc.smajor.scalar", "sgn.cluster.nhwc.smajor.vec4", "sgn.cluster.nhwc.smajor.vec8",

@@ -285,9 +285,11 @@ NHWC_LIMIT_CASES = [
     (8, 320, 128, 128, F16, 32, False, "sgn.split.nhwc.vec16"),
     # One slice per (image, channel block), nothing exchanged: 4096
     # workgroups of 2 pixels per thread stay in the cluster beyond two rounds;
-    # 1088 of 9 pixels per thread (the 16-pixel form) take the split route.
+    # float16 with 1088 of 9 pixels per thread (the 16-pixel form) takes the
+    # split route, float32 with 2048 of 11 stays.
     (512, 320, 8, 8, F16, 32, False, "sgn.cluster.nhwc.vec16"),
     (136, 320, 21, 21, F16, 32, True, "sgn.split.nhwc.vec16"),
+    (256, 320, 16, 16, F32, 32, False, "sgn.cluster.nhwc.vec16"),
 ]
 
 
